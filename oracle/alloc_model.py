@@ -1,0 +1,192 @@
+"""Reference model of the block allocator -- TEST INFRASTRUCTURE ONLY.
+
+A plain Python model of the host-side block pool, written independently of
+the library's C++ allocator so that block tables, slot mappings and
+refcounts can be checked bit for bit.  Only tests, the smoke check and the
+benchmark's CPU-baseline leg use it.
+
+What it models (sources, by page title and section):
+  * dev.to, "Why LLMs Run Out of VRAM: KV Cache Fragmentation and How
+    PagedAttention Fixes It":
+      - §4 "How PagedAttention Solves Fragmentation": a pool of fixed-size
+        physical blocks made once at startup; one block table per sequence
+        mapping logical block i (tokens i*bs .. i*bs+bs-1) to a physical id;
+        on-demand allocation -- a sequence takes a new block exactly when its
+        length reaches a multiple of the block size.
+      - §5 "Zero-Copy Forking": several block tables may point at the same
+        physical block, whose reference count is the number of tables that
+        map it; a block returns to the pool when that count reaches zero.
+  * hyperinfer.ai, "KV cache & paged attention deep dive", "PagedAttention:
+    virtual memory for attention state" and "What 16-token blocks buy you":
+    new blocks come from a free pool; evicting a sequence frees its blocks.
+  * dev.to §2 "The Concrete Math of KV Cache Growth": bytes per token
+    = 2 x layers x kv_heads x head_dim x bytes per element.
+
+The pages give no placement policy, so the library fixes one and this model
+restates it (it is what makes the tables reproducible):
+  * The free list starts as [0, 1, ..., N-1].  If the shuffle seed is
+    non-zero it is permuted by a Fisher-Yates pass, i from N-1 down to 1,
+    swapping entry i with entry (splitmix64() mod (i+1)), where splitmix64
+    is the generator of Steele, Lea and Flood (OOPSLA 2014) seeded with the
+    shuffle seed.
+  * Allocation pops from the end of the free list; freeing pushes a
+    sequence's blocks in table order onto the end.
+  * Sequence ids count up from 0 and are never reused.
+  * Writing into a block whose refcount is above one is refused (copy on
+    write is not modelled).
+"""
+
+MASK64 = (1 << 64) - 1
+
+OK = 0
+ERR_INVALID_ARG = 1
+ERR_OUT_OF_BLOCKS = 2
+ERR_CAPACITY = 3
+ERR_UNSUPPORTED = 4
+
+
+class SplitMix64:
+    """splitmix64 as published by Steele, Lea and Flood (2014)."""
+
+    def __init__(self, seed):
+        self.state = seed & MASK64
+
+    def next(self):
+        self.state = (self.state + 0x9E3779B97F4A7C15) & MASK64
+        z = self.state
+        z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & MASK64
+        z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & MASK64
+        return z ^ (z >> 31)
+
+
+def kv_bytes_per_token(layers, kv_heads, head_dim, elem_bytes):
+    """dev.to §2: 2 (K and V) x layers x kv_heads x head_dim x bytes."""
+    return 2 * layers * kv_heads * head_dim * elem_bytes
+
+
+class PoolModel:
+    def __init__(self, num_blocks, block_size, shuffle_seed):
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+        free = list(range(num_blocks))
+        if shuffle_seed != 0:
+            rng = SplitMix64(shuffle_seed)
+            for i in range(num_blocks - 1, 0, -1):
+                j = rng.next() % (i + 1)
+                free[i], free[j] = free[j], free[i]
+        self.free = free
+        self.refcount = [0] * num_blocks
+        self.tables = {}  # seq id -> list of physical block ids
+        self.lens = {}    # seq id -> tokens stored
+        self.next_id = 0
+
+    # -- sequences -------------------------------------------------------
+    def seq_create(self):
+        sid = self.next_id
+        self.next_id += 1
+        self.tables[sid] = []
+        self.lens[sid] = 0
+        return sid
+
+    def _blocks_for(self, ntokens):
+        return -(-ntokens // self.block_size)
+
+    def _check_append(self, sid, ntok):
+        if sid not in self.tables or ntok < 0:
+            return ERR_INVALID_ARG, 0
+        n = self.lens[sid]
+        table = self.tables[sid]
+        if ntok > 0 and n % self.block_size != 0 and self.refcount[table[-1]] > 1:
+            return ERR_UNSUPPORTED, 0
+        return OK, self._blocks_for(n + ntok) - len(table)
+
+    def _do_append(self, sid, ntok):
+        n = self.lens[sid]
+        table = self.tables[sid]
+        need = self._blocks_for(n + ntok) - len(table)
+        for _ in range(need):
+            blk = self.free.pop()
+            self.refcount[blk] = 1
+            table.append(blk)
+        slots = []
+        for pos in range(n, n + ntok):
+            slots.append(table[pos // self.block_size] * self.block_size
+                         + pos % self.block_size)
+        self.lens[sid] = n + ntok
+        return slots
+
+    def append_slots(self, sid, ntok):
+        """Returns (status, slots); on error nothing changes."""
+        st, need = self._check_append(sid, ntok)
+        if st != OK:
+            return st, []
+        if need > len(self.free):
+            return ERR_OUT_OF_BLOCKS, []
+        return OK, self._do_append(sid, ntok)
+
+    def append_slots_batch(self, sids, ntok):
+        """ntok tokens to each sequence, in list order; all or nothing."""
+        if len(set(sids)) != len(sids):
+            return ERR_INVALID_ARG, []
+        total = 0
+        for sid in sids:
+            st, need = self._check_append(sid, ntok)
+            if st != OK:
+                return st, []
+            total += need
+        if total > len(self.free):
+            return ERR_OUT_OF_BLOCKS, []
+        out = []
+        for sid in sids:
+            out.extend(self._do_append(sid, ntok))
+        return OK, out
+
+    def fork(self, parent):
+        if parent not in self.tables:
+            return ERR_INVALID_ARG, -1
+        child = self.seq_create()
+        self.tables[child] = list(self.tables[parent])
+        self.lens[child] = self.lens[parent]
+        for blk in self.tables[child]:
+            self.refcount[blk] += 1
+        return OK, child
+
+    def free_seq(self, sid):
+        if sid not in self.tables:
+            return ERR_INVALID_ARG
+        for blk in self.tables[sid]:
+            self.refcount[blk] -= 1
+            if self.refcount[blk] == 0:
+                self.free.append(blk)
+        del self.tables[sid]
+        del self.lens[sid]
+        return OK
+
+    # -- export ----------------------------------------------------------
+    def export(self, sids, max_blocks):
+        """(status, tables[nseq][max_blocks] padded with -1, lens)."""
+        tables, lens = [], []
+        for sid in sids:
+            if sid not in self.tables:
+                return ERR_INVALID_ARG, None, None
+            t = self.tables[sid]
+            if len(t) > max_blocks:
+                return ERR_CAPACITY, None, None
+            tables.append(t + [-1] * (max_blocks - len(t)))
+            lens.append(self.lens[sid])
+        return OK, tables, lens
+
+    def stats(self):
+        used = self.num_blocks - len(self.free)
+        mapped = sum(len(t) for t in self.tables.values())
+        return {
+            "num_blocks": self.num_blocks,
+            "free_blocks": len(self.free),
+            "used_blocks": used,
+            "shared_blocks": sum(1 for r in self.refcount if r > 1),
+            "live_seqs": len(self.tables),
+            "logical_tokens": sum(self.lens.values()),
+            "mapped_blocks": mapped,
+            "tail_slack_tokens": sum(len(self.tables[s]) * self.block_size - self.lens[s]
+                                     for s in self.tables),
+        }

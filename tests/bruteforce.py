@@ -1,0 +1,59 @@
+"""Brute-force contiguous attention in numpy, used to pin the oracle.
+
+Written separately from the oracle: stored values are decoded with library
+routines (numpy float16, torch bfloat16 / float8_e4m3fn views), each
+sequence's K and V are gathered into contiguous [n][D] arrays with
+np.concatenate over its block table, and softmax(q K^T * scale) V is then
+evaluated with whole-array numpy operations (dev.to, "Why LLMs Run Out of
+VRAM...", §1 attention formula; §4 block table).
+"""
+import numpy as np
+import torch
+
+
+def decode_storage(a, dtype):
+    """Stored values -> float64, via library conversions."""
+    if dtype == "f32":
+        return np.asarray(a, dtype=np.float32).astype(np.float64)
+    if dtype == "f16":
+        return np.asarray(a, dtype=np.uint16).view(np.float16).astype(np.float64)
+    if dtype == "bf16":
+        t = torch.from_numpy(np.asarray(a, dtype=np.uint16).view(np.int16).copy())
+        return t.view(torch.bfloat16).to(torch.float64).numpy()
+    if dtype == "e4m3":
+        t = torch.from_numpy(np.asarray(a, dtype=np.uint8).copy())
+        return t.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    raise ValueError(dtype)
+
+
+def gather(cache_vals, table, n, bs, layout):
+    """Contiguous [n][Hkv][D] rows of one sequence from a paged cache given as
+    float64 [blocks][Hkv][bs][D] ("k") or [blocks][Hkv][D][bs] ("v")."""
+    nblk = -(-n // bs)
+    if layout == "k":
+        parts = [cache_vals[table[j]].transpose(1, 0, 2) for j in range(nblk)]
+    else:
+        parts = [cache_vals[table[j]].transpose(2, 0, 1) for j in range(nblk)]
+    return np.concatenate(parts, axis=0)[:n]
+
+
+def attention(q, k_cache, v_cache, tables, lens, *, num_q_heads, num_kv_heads, head_dim,
+              block_size, q_dtype, kv_dtype, scale, k_scale=1.0, v_scale=1.0):
+    B = len(lens)
+    G = num_q_heads // num_kv_heads
+    qv = decode_storage(q, q_dtype).reshape(B, num_q_heads, head_dim)
+    kv = decode_storage(k_cache, kv_dtype).reshape(-1, num_kv_heads, block_size, head_dim)
+    vv = decode_storage(v_cache, kv_dtype).reshape(-1, num_kv_heads, head_dim, block_size)
+    out = np.zeros((B, num_q_heads, head_dim))
+    for b in range(B):
+        n = int(lens[b])
+        if n == 0:
+            continue
+        K = gather(kv, tables[b], n, block_size, "k") * k_scale  # [n][Hkv][D]
+        V = gather(vv, tables[b], n, block_size, "v") * v_scale
+        for h in range(num_q_heads):
+            g = h // G
+            s = K[:, g, :] @ qv[b, h] * scale
+            w = np.exp(s - s.max())
+            out[b, h] = (w[:, None] * V[:, g, :]).sum(0) / w.sum()
+    return out

@@ -1,0 +1,168 @@
+"""Pins of the allocator model (oracle/alloc_model.py) against the pages'
+worked examples, published generator outputs and policy-free invariants."""
+import json
+import os
+
+import numpy as np
+
+from oracle import alloc_model as am
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def test_splitmix64_published_outputs():
+    g = _golden("splitmix64_vectors.json")
+    for vec in g["vectors"]:
+        r = am.SplitMix64(vec["seed"])
+        for want in vec["first_outputs"]:
+            assert r.next() == int(want, 0)
+
+
+def test_shuffled_free_list_is_a_permutation():
+    for seed in [0, 1, 77, 2**63 + 5]:
+        p = am.PoolModel(1000, 16, seed)
+        assert sorted(p.free) == list(range(1000))
+    assert am.PoolModel(50, 16, 0).free == list(range(50))
+    assert am.PoolModel(50, 16, 3).free != list(range(50))
+
+
+def test_on_demand_allocation_at_multiples_of_block_size():
+    """dev.to §4 'On-Demand Allocation': one block at the start, tokens
+    1..15 write into it, token 16 takes the next block."""
+    p = am.PoolModel(10, 16, 0)
+    s = p.seq_create()
+    used = []
+    for t in range(40):
+        st, _ = p.append_slots(s, 1)
+        assert st == am.OK
+        used.append(p.stats()["used_blocks"])
+    assert used[0] == 1 and used[15] == 1 and used[16] == 2 and used[31] == 2 and used[32] == 3
+
+
+def test_page_addressing_example():
+    """dev.to §4 figure: logical blocks 0/1/2 -> physical 84/12/903."""
+    ex = _golden("devto_block_table_example.json")
+    phys = [e["physical"] for e in ex["logical_blocks"]]
+    p = am.PoolModel(1000, ex["block_size"], 0)
+    p.free = [b for b in range(1000) if b not in phys] + phys[::-1]  # pops 84, 12, 903
+    s = p.seq_create()
+    st, slots = p.append_slots(s, 48)
+    assert st == am.OK
+    assert p.tables[s] == phys
+    for e in ex["logical_blocks"]:
+        for t in range(e["first_token"], e["last_token"] + 1):
+            assert slots[t] == e["physical"] * 16 + (t - e["first_token"])
+    assert slots[20] == 196 and slots[47] == 14463
+
+
+def test_fork_example_and_sharing_saving():
+    """dev.to §5: two prompt blocks mapped by both branches (refcount 2),
+    each branch's first new token goes to its own private block."""
+    ex = _golden("devto_fork_example.json")
+    p = am.PoolModel(200, 16, 0)
+    prompt_blocks = ex["prompt_physical_blocks"]
+    priv = [b["private_block"] for b in ex["branches"]]
+    order = prompt_blocks + priv  # pop order
+    p.free = [b for b in range(200) if b not in order] + order[::-1]
+    root = p.seq_create()
+    assert p.append_slots(root, 32)[0] == am.OK
+    st, a = p.fork(root)
+    assert st == am.OK
+    st, b = p.fork(root)
+    p.free_seq(root)
+    assert all(p.refcount[x] == ex["sharers_in_example"] for x in prompt_blocks)
+    st, sa = p.append_slots(a, 16)
+    st, sb = p.append_slots(b, 16)
+    assert p.tables[a] == prompt_blocks + [priv[0]]
+    assert p.tables[b] == prompt_blocks + [priv[1]]
+    assert sa[0] == priv[0] * 16 and sb[-1] == priv[1] * 16 + 15
+    # k sharers of a prompt use 1/k of the duplicated memory: 75% saved at k = 4
+    k = ex["samples_sharing_prompt"]
+    q = am.PoolModel(100, 16, 9)
+    r = q.seq_create()
+    q.append_slots(r, 32)
+    kids = [q.fork(r)[1] for _ in range(k)]
+    q.free_seq(r)
+    st = q.stats()
+    assert 1 - st["used_blocks"] / st["mapped_blocks"] == ex["prompt_memory_saving_with_4_sharers"]
+    assert len(kids) == k
+
+
+def test_out_of_blocks_changes_nothing():
+    p = am.PoolModel(5, 16, 4)
+    s = p.seq_create()
+    assert p.append_slots(s, 60)[0] == am.OK  # 4 blocks
+    before = (list(p.free), dict(p.lens), {k: list(v) for k, v in p.tables.items()})
+    assert p.append_slots(s, 40)[0] == am.ERR_OUT_OF_BLOCKS  # needs 3 more
+    t = p.seq_create()
+    assert p.append_slots_batch([s, t], 20)[0] == am.ERR_OUT_OF_BLOCKS
+    assert p.free == before[0] and p.lens[s] == before[1][s] and p.tables[s] == before[2][s]
+    assert p.lens[t] == 0
+
+
+def test_write_into_shared_partial_block_is_refused():
+    p = am.PoolModel(8, 16, 0)
+    s = p.seq_create()
+    p.append_slots(s, 10)
+    _, c = p.fork(s)
+    assert p.append_slots(c, 1)[0] == am.ERR_UNSUPPORTED
+    assert p.append_slots(s, 1)[0] == am.ERR_UNSUPPORTED
+
+
+def test_random_operations_keep_invariants():
+    rng = np.random.default_rng(1)
+    p = am.PoolModel(300, 16, 12345)
+    live = []
+    for _ in range(2000):
+        op = rng.integers(0, 10)
+        if op < 2 or not live:
+            live.append(p.seq_create())
+        elif op < 7:
+            s = live[rng.integers(len(live))]
+            p.append_slots(s, int(rng.integers(1, 40)))
+        elif op < 8:
+            s = live[rng.integers(len(live))]
+            if p.lens[s] % 16 == 0:
+                live.append(p.fork(s)[1])
+        else:
+            s = live.pop(rng.integers(len(live)))
+            assert p.free_seq(s) == am.OK
+        # invariants
+        counts = {}
+        for sid, t in p.tables.items():
+            assert len(t) == -(-p.lens[sid] // 16)
+            assert len(set(t)) == len(t)
+            for b in t:
+                counts[b] = counts.get(b, 0) + 1
+        for b in range(300):
+            assert p.refcount[b] == counts.get(b, 0)
+        assert len(p.free) + len(counts) == 300
+        assert set(p.free).isdisjoint(counts)
+
+
+def test_average_tail_slack_is_about_half_a_block():
+    """hyperinfer.ai 'What 16-token blocks buy you': across many sequences of
+    varying length the unused tail averages about 8 tokens; for lengths spread
+    evenly over residues it is (16 - 1) / 2 = 7.5."""
+    rng = np.random.default_rng(2)
+    p = am.PoolModel(200000, 16, 1)
+    lens = rng.integers(1, 1500, size=3000)
+    for n in lens:
+        s = p.seq_create()
+        assert p.append_slots(s, int(n))[0] == am.OK
+    st = p.stats()
+    avg = st["tail_slack_tokens"] / st["live_seqs"]
+    assert abs(avg - 7.5) < 0.3
+    assert all(len(p.tables[s]) * 16 - p.lens[s] <= 15 for s in p.tables)
+
+
+def test_bytes_per_token_closed_form():
+    g = _golden("devto_kv_sizes.json")
+    for ex in g["examples"]:
+        assert am.kv_bytes_per_token(ex["layers"], ex["kv_heads"], ex["head_dim"],
+                                     ex["elem_bytes"]) == ex["bytes_per_token"]
