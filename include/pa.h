@@ -1,0 +1,244 @@
+/*
+ * pa.h -- C ABI of libpa: paged KV cache and PagedAttention decode on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What the calls compute is fixed by three pages (cited by title and
+ * section):
+ *   [devto] dev.to, "Why LLMs Run Out of VRAM: KV Cache Fragmentation and
+ *           How PagedAttention Fixes It"
+ *   [hi]    hyperinfer.ai, "KV cache & paged attention deep dive"
+ *   [vk]    vaibhawkumar.in, "Why LLMs run out of VRAM: KV cache
+ *           fragmentation and the PagedAttention fix"
+ *
+ * Conventions shared by every call:
+ *   - Every function returns a pa_status; on failure pa_last_error() gives a
+ *     message (thread-local, valid until the next failing call on the thread).
+ *   - The library never allocates or frees device memory.  Device buffers
+ *     (caches, q, out, tables, workspace) belong to the caller and are
+ *     borrowed until the launched work completes on `stream`.
+ *   - `stream` is a hipStream_t passed as void*; NULL is the default stream.
+ *     Kernel calls are asynchronous: argument errors that the host can see are
+ *     returned at once, device-side faults appear at the caller's next
+ *     synchronisation.
+ *   - All arrays are dense, row-major, without padding.
+ *
+ * Cache layout (per layer, one K and one V tensor, both [num_blocks][Hkv]
+ * tiles of one block of one KV head):
+ *   k_cache[block][kv_head][token_in_block][dim]     token-major K tile
+ *   v_cache[block][kv_head][dim][token_in_block]     dimension-major V tile
+ * The pages fix only that a block holds a fixed number of consecutive tokens
+ * ([devto] §4); the tile orders are this library's choice: K rows and V
+ * columns are then contiguous in the order the decode kernels consume them.
+ *
+ * A token's slot is block * block_size + offset; token t of a sequence lives
+ * in block block_tables[seq][t / block_size] at offset t % block_size
+ * ([devto] §4, the logical-to-physical block figure).
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PA_OK = 0,
+    PA_ERR_INVALID_ARG = 1,   /* bad pointer, shape, id or size */
+    PA_ERR_OUT_OF_BLOCKS = 2, /* the pool cannot supply the blocks asked for */
+    PA_ERR_CAPACITY = 3,      /* a caller-sized buffer is too small */
+    PA_ERR_UNSUPPORTED = 4,   /* valid request this build does not implement */
+    PA_ERR_HIP = 5            /* a HIP runtime call or launch failed */
+} pa_status;
+
+typedef enum {
+    PA_F32 = 0,
+    PA_F16 = 1,
+    PA_BF16 = 2,
+    PA_FP8_E4M3 = 3 /* OCP E4M3FN: bias 7, max 448, no infinities */
+} pa_dtype;
+
+/* ------------------------------------------------------------------------ */
+/* Block pool (host only).                                                  */
+/* ------------------------------------------------------------------------ */
+
+typedef struct pa_pool pa_pool;
+
+typedef struct {
+    int32_t num_blocks;    /* physical blocks, fixed at init */
+    int32_t block_size;    /* tokens per block; this build supports 16 */
+    int32_t num_layers;    /* used only for the byte counts below */
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    pa_dtype kv_dtype;
+    uint64_t shuffle_seed; /* 0: free list in id order; else a seeded permutation */
+} pa_pool_config;
+
+typedef struct {
+    int32_t num_blocks;
+    int32_t free_blocks;
+    int32_t used_blocks;       /* blocks with refcount > 0 */
+    int32_t shared_blocks;     /* blocks with refcount > 1 */
+    int32_t live_seqs;
+    int32_t reserved;
+    int64_t logical_tokens;    /* sum of live sequence lengths */
+    int64_t mapped_blocks;     /* sum of block-table lengths (a shared block counts per table) */
+    int64_t tail_slack_tokens; /* sum over live sequences of unused slots in their blocks */
+} pa_pool_stats;
+
+/* Creates the pool: every block of the fixed-size physical pool exists from
+ * the start and sits on the free list ([devto] §4 "Centralized Physical Block
+ * Pool"; [hi] "PagedAttention: virtual memory for attention state").
+ * Placement policy: the free list starts as ids 0..N-1; a non-zero
+ * shuffle_seed permutes it by a Fisher-Yates pass (i from N-1 down to 1,
+ * swap with splitmix64() mod (i+1), splitmix64 of Steele, Lea and Flood
+ * seeded with shuffle_seed).  Blocks are taken from the end of the list and
+ * returned to the end.  *out receives the pool; the caller frees it with
+ * pa_block_pool_destroy.  Errors: PA_ERR_INVALID_ARG for non-positive sizes
+ * or an unknown dtype, PA_ERR_UNSUPPORTED for block_size != 16. */
+pa_status pa_block_pool_init(const pa_pool_config *cfg, pa_pool **out);
+
+/* Frees the pool object (NULL is ignored). */
+void pa_block_pool_destroy(pa_pool *pool);
+
+/* KV bytes one token occupies over all layers: 2 x layers x kv_heads x
+ * head_dim x bytes per element ([devto] §2 "The Concrete Math of KV Cache
+ * Growth"; [hi] "What the KV cache is").  Page size is counted in tokens and
+ * bytes follow from the dtype ([vk] "Practical pitfalls", item 3).
+ * Returns 0 for a NULL pool. */
+uint64_t pa_kv_bytes_per_token(const pa_pool *pool);
+
+/* Bytes of one block of one layer in one of the two tensors (K or V):
+ * block_size x kv_heads x head_dim x bytes per element.  The caller sizes
+ * each cache tensor as num_blocks times this.  0 for a NULL pool. */
+uint64_t pa_block_bytes(const pa_pool *pool);
+
+/* New empty sequence; ids count up from 0 and are never reused. */
+pa_status pa_seq_create(pa_pool *pool, int32_t *seq_out);
+
+/* Reserves slots for ntok more tokens of `seq` and writes their slot ids
+ * (block * block_size + offset) to slots_out[0..ntok).  A block is taken
+ * from the free list exactly when the sequence length reaches a multiple of
+ * block_size ([devto] §4 "On-Demand Allocation").  All or nothing: on
+ * PA_ERR_OUT_OF_BLOCKS nothing changes.  Writing into a block shared with
+ * another sequence (refcount > 1) returns PA_ERR_UNSUPPORTED (copy on write
+ * is not implemented). */
+pa_status pa_seq_append_slots(pa_pool *pool, int32_t seq, int32_t ntok, int32_t *slots_out);
+
+/* pa_seq_append_slots for nseq distinct sequences, ntok tokens each, in the
+ * given order; slots_out receives nseq*ntok slots, sequence-major.  All or
+ * nothing over the whole batch.  This is the per-step host work of a decode
+ * step (ntok = 1). */
+pa_status pa_seq_append_slots_batch(pa_pool *pool, const int32_t *seqs, int32_t nseq,
+                                    int32_t ntok, int32_t *slots_out);
+
+/* New sequence whose table maps the same physical blocks as `parent`, each
+ * block's reference count incremented ([devto] §5 "Parallel Sampling & Tree
+ * Search": tables point at the same prompt blocks; [hi] "Prefix caching").
+ * The child has the parent's length. */
+pa_status pa_seq_fork(pa_pool *pool, int32_t parent, int32_t *child_out);
+
+/* Drops the sequence; each of its blocks loses one reference and returns to
+ * the free list (in table order) when the count reaches zero ([hi] "What
+ * 16-token blocks buy you": evicting a sequence frees its blocks). */
+pa_status pa_seq_free(pa_pool *pool, int32_t seq);
+
+/* Current length (tokens) of a live sequence. */
+pa_status pa_seq_length(const pa_pool *pool, int32_t seq, int32_t *len_out);
+
+/* Reference count of one physical block. */
+pa_status pa_block_refcount(const pa_pool *pool, int32_t block, int32_t *refcount_out);
+
+/* Writes the block tables of nseq sequences into tables_out
+ * [nseq][max_blocks] (int32, entries past a table's end set to -1) and their
+ * lengths into lens_out[nseq] (either output may be NULL).
+ * PA_ERR_CAPACITY if a table has more than max_blocks entries. */
+pa_status pa_export_block_tables(const pa_pool *pool, const int32_t *seqs, int32_t nseq,
+                                 int32_t max_blocks, int32_t *tables_out, int32_t *lens_out);
+
+pa_status pa_pool_get_stats(const pa_pool *pool, pa_pool_stats *out);
+
+/* ------------------------------------------------------------------------ */
+/* Kernels (device, asynchronous on `stream`).                              */
+/* ------------------------------------------------------------------------ */
+
+/* Kernel choice for pa_decode. */
+enum {
+    PA_KERNEL_AUTO = 0, /* library picks by dtype, head_dim and group size */
+    PA_KERNEL_VALU = 1, /* vector-ALU kernel (fp32 math); every dtype */
+    PA_KERNEL_MFMA = 2  /* matrix-core kernel; 16-bit q, 16-bit or FP8 KV */
+};
+
+typedef struct {
+    int32_t num_q_heads;
+    int32_t num_kv_heads;  /* must divide num_q_heads; group G = Hq / Hkv */
+    int32_t head_dim;      /* 64 or 128 */
+    int32_t block_size;    /* 16 */
+    int32_t num_blocks;    /* blocks in each cache tensor (bounds for ids/slots) */
+    pa_dtype q_dtype;      /* q, out and the new tokens' K/V */
+    pa_dtype kv_dtype;     /* cache storage: equal to q_dtype, or FP8 with 16-bit q */
+    int32_t kernel;        /* PA_KERNEL_* */
+} pa_kv_desc;
+
+/* Writes the K and V of num_tokens new tokens into their cache slots:
+ *   k_cache[s / bs][g][s % bs][d] = cvt(k[t][g][d])
+ *   v_cache[s / bs][g][d][s % bs] = cvt(v[t][g][d]),   s = slot_mapping[t]
+ * for every KV head g and dim d ([devto] §1: the new token's K and V are
+ * appended to the cache; §4: a slot is a place in a physical block).
+ * k, v: device [num_tokens][Hkv][D] in desc->q_dtype.  slot_mapping: device
+ * int32 [num_tokens]; a negative slot skips the token; slots must be
+ * distinct.  cvt is a bit copy when kv_dtype == q_dtype; for FP8 it is
+ * e4m3(x * fl32(1/k_scale)) (resp. v_scale) rounded to nearest, ties to even,
+ * saturating at +-448 ([devto] §6 "Enable FP8 KV Cache"; [hi] "KV
+ * quantization cuts memory in half"); k_scale and v_scale are the
+ * dequantisation factors and are ignored for other dtypes.  A slot outside
+ * [0, num_blocks * block_size) is skipped by the kernel. */
+pa_status pa_cache_append(const void *k, const void *v, void *k_cache, void *v_cache,
+                          const int32_t *slot_mapping, int32_t num_tokens,
+                          const pa_kv_desc *desc, float k_scale, float v_scale, void *stream);
+
+/* partition_size for pa_decode. */
+#define PA_PARTITION_NONE 0       /* one pass per (sequence, KV head), no workspace */
+#define PA_PARTITION_BALANCED (-1) /* tokens split evenly over the GPU's waves */
+
+/* Workspace bytes pa_decode needs for this shape and partitioning (0 for
+ * PA_PARTITION_NONE).  partition_size > 0 must be a multiple of block_size. */
+size_t pa_decode_workspace_bytes(const pa_kv_desc *desc, int32_t num_seqs, int32_t max_seq_len,
+                                 int32_t partition_size);
+
+/* Single-query attention for each sequence b and query head h
+ * ([devto] §1, Attention(Q,K,V) = softmax(QK^T / sqrt(d_k)) V; §4 "The
+ * PagedAttention CUDA Kernel": the query reads K and V through the block
+ * table):
+ *   out[b][h][:] = sum_t w_t * v_scale * V_t / sum_t w_t,
+ *   w_t = exp(scale * k_scale * <q[b][h], K_t> - max),  t in [0, seq_lens[b]),
+ * with K_t, V_t the rows of KV head h / (Hq / Hkv) found through
+ * block_tables[b][t / bs].  A zero-length sequence gives a zero row.
+ *   q, out: device [num_seqs][Hq][D] in desc->q_dtype (out may not alias q).
+ *   block_tables: device int32 [num_seqs][max_blocks_per_seq].
+ *   seq_lens: device int32 [num_seqs], each in [0, max_seq_len] and
+ *     <= max_blocks_per_seq * block_size; a row whose length or block ids are
+ *     out of range is written as NaN instead of being read.
+ *   partition_size: PA_PARTITION_NONE, PA_PARTITION_BALANCED, or a positive
+ *     multiple of block_size: each (sequence, KV head) is split into chunks
+ *     of that many tokens whose partial softmax states are merged by a second
+ *     kernel.  The partitioned modes need `workspace` (device, at least
+ *     pa_decode_workspace_bytes(...) bytes, no initial contents required).
+ * Accumulation is fp32; out is rounded to nearest even. */
+pa_status pa_decode(const void *q, const void *k_cache, const void *v_cache,
+                    const int32_t *block_tables, int32_t max_blocks_per_seq,
+                    const int32_t *seq_lens, int32_t num_seqs, int32_t max_seq_len, float scale,
+                    float k_scale, float v_scale, void *out, void *workspace,
+                    size_t workspace_bytes, int32_t partition_size, const pa_kv_desc *desc,
+                    void *stream);
+
+/* Message describing the last failure on this thread ("" if none). */
+const char *pa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

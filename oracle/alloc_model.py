@@ -190,3 +190,27 @@ class PoolModel:
             "tail_slack_tokens": sum(len(self.tables[s]) * self.block_size - self.lens[s]
                                      for s in self.tables),
         }
+
+
+def execute_plan(model, ops):
+    """Runs a workload plan (see workloads) on the model.  Returns
+    (ids, prefill_slots): the model's id for each plan sequence, and the slots
+    of every prefill token in plan order."""
+    ids = []
+    slots = []
+    for op in ops:
+        if op[0] == "create":
+            ids.append(model.seq_create())
+        elif op[0] == "fork":
+            st, c = model.fork(ids[op[1]])
+            assert st == OK, st
+            ids.append(c)
+        elif op[0] == "free":
+            assert model.free_seq(ids[op[1]]) == OK
+        elif op[0] == "prefill":
+            st, s = model.append_slots(ids[op[1]], op[2])
+            assert st == OK, st
+            slots.extend(s)
+        else:
+            raise ValueError(op)
+    return ids, slots

@@ -238,10 +238,42 @@ static void store_elem(const orc_cache_desc *c, void *cache, size_t idx, const v
     dst[idx] = orc_e4m3_from_float(y);
 }
 
+typedef struct {
+    const orc_cache_desc *c;
+    const void *k_new, *v_new;
+    void *k_cache, *v_cache;
+    const int32_t *slots;
+    int32_t t0, t1;
+    float k_scale, v_scale;
+} append_job;
+
+/* Writes tokens [t0, t1) of one job; slots were checked by the caller. */
+static void *append_worker(void *arg)
+{
+    const append_job *J = (const append_job *)arg;
+    const orc_cache_desc *c = J->c;
+    for (int32_t t = J->t0; t < J->t1; ++t) {
+        int64_t slot = J->slots[t];
+        if (slot < 0)
+            continue;
+        int64_t blk = slot / c->block_size;
+        int o = (int)(slot % c->block_size);
+        for (int g = 0; g < c->num_kv_heads; ++g) {
+            for (int d = 0; d < c->head_dim; ++d) {
+                size_t src = ((size_t)t * c->num_kv_heads + g) * c->head_dim + d;
+                store_elem(c, J->k_cache, k_index(c, blk, g, o, d), J->k_new, src, J->k_scale);
+                store_elem(c, J->v_cache, v_index(c, blk, g, o, d), J->v_new, src, J->v_scale);
+            }
+        }
+    }
+    return NULL;
+}
+
 /* k_new, v_new: [num_tokens][Hkv][D] in in_dtype.  slot_mapping[t] is
- * block * block_size + offset, or negative to skip the token.
- * Returns 0, or -1 if a slot lies outside the pool or the dtype pair is not
- * one the path defines. */
+ * block * block_size + offset, or negative to skip the token.  Tokens are
+ * independent (their slots are distinct), so ranges of them are written by
+ * separate threads.  Returns 0, or -1 if a slot lies outside the pool or the
+ * dtype pair is not one the path defines. */
 int orc_cache_append(const orc_cache_desc *c, const void *k_new, const void *v_new,
                      void *k_cache, void *v_cache, const int32_t *slot_mapping,
                      int32_t num_tokens, float k_scale, float v_scale)
@@ -249,21 +281,33 @@ int orc_cache_append(const orc_cache_desc *c, const void *k_new, const void *v_n
     if (!(c->kv_dtype == c->in_dtype ||
           (c->kv_dtype == ORC_E4M3 && (c->in_dtype == ORC_BF16 || c->in_dtype == ORC_F16))))
         return -1;
-    for (int32_t t = 0; t < num_tokens; ++t) {
-        int64_t slot = slot_mapping[t];
-        if (slot < 0)
-            continue;
-        if (slot >= (int64_t)c->num_blocks * c->block_size)
+    for (int32_t t = 0; t < num_tokens; ++t)
+        if (slot_mapping[t] >= (int64_t)c->num_blocks * c->block_size)
             return -1;
-        int64_t blk = slot / c->block_size;
-        int o = (int)(slot % c->block_size);
-        for (int g = 0; g < c->num_kv_heads; ++g) {
-            for (int d = 0; d < c->head_dim; ++d) {
-                size_t src = ((size_t)t * c->num_kv_heads + g) * c->head_dim + d;
-                store_elem(c, k_cache, k_index(c, blk, g, o, d), k_new, src, k_scale);
-                store_elem(c, v_cache, v_index(c, blk, g, o, d), v_new, src, v_scale);
-            }
-        }
+    int nthreads = (int)sysconf(_SC_NPROCESSORS_ONLN);
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > 64)
+        nthreads = 64;
+    if (num_tokens < 1024)
+        nthreads = 1;
+    append_job jobs[64];
+    pthread_t th[64];
+    int started[64] = {0};
+    for (int i = 0; i < nthreads; ++i) {
+        append_job j = {c, k_new, v_new, k_cache, v_cache, slot_mapping,
+                        (int32_t)((int64_t)num_tokens * i / nthreads),
+                        (int32_t)((int64_t)num_tokens * (i + 1) / nthreads), k_scale, v_scale};
+        jobs[i] = j;
+    }
+    for (int i = 1; i < nthreads; ++i)
+        started[i] = pthread_create(&th[i], NULL, append_worker, &jobs[i]) == 0;
+    append_worker(&jobs[0]);
+    for (int i = 1; i < nthreads; ++i) {
+        if (started[i])
+            pthread_join(th[i], NULL);
+        else
+            append_worker(&jobs[i]);
     }
     return 0;
 }

@@ -1,0 +1,281 @@
+"""Python binding of libpa (paged KV cache + PagedAttention decode on MI355X).
+
+Argument marshalling only: every function forwards to the C entry point of
+the same name in libpa.so (declared in include/pa.h), passing tensor data
+pointers, sizes and the current HIP stream.  All computation happens in the
+library's HIP kernels and host allocator.  Importing this package fails if
+libpa.so has not been built (python -m paged_kv_cache_255_amd.build).
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with "
+                      "`python -m paged_kv_cache_255_amd.build`")
+_lib = ctypes.CDLL(LIB_PATH)
+
+# pa_status
+OK, ERR_INVALID_ARG, ERR_OUT_OF_BLOCKS, ERR_CAPACITY, ERR_UNSUPPORTED, ERR_HIP = range(6)
+STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_OUT_OF_BLOCKS",
+                3: "PA_ERR_CAPACITY", 4: "PA_ERR_UNSUPPORTED", 5: "PA_ERR_HIP"}
+# pa_dtype
+F32, F16, BF16, FP8_E4M3 = 0, 1, 2, 3
+DTYPE_CODES = {"f32": F32, "f16": F16, "bf16": BF16, "e4m3": FP8_E4M3}
+DTYPE_BYTES = {F32: 4, F16: 2, BF16: 2, FP8_E4M3: 1}
+# kernel choice and partitioning
+KERNEL_AUTO, KERNEL_VALU, KERNEL_MFMA = 0, 1, 2
+PARTITION_NONE, PARTITION_BALANCED = 0, -1
+
+
+class PaError(RuntimeError):
+    def __init__(self, status, where):
+        msg = _lib.pa_last_error().decode()
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+class PoolConfig(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("num_layers", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("kv_dtype", ctypes.c_int),
+                ("shuffle_seed", ctypes.c_uint64)]
+
+
+class PoolStats(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("free_blocks", ctypes.c_int32),
+                ("used_blocks", ctypes.c_int32), ("shared_blocks", ctypes.c_int32),
+                ("live_seqs", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("logical_tokens", ctypes.c_int64), ("mapped_blocks", ctypes.c_int64),
+                ("tail_slack_tokens", ctypes.c_int64)]
+
+
+class KvDesc(ctypes.Structure):
+    _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("num_blocks", ctypes.c_int32), ("q_dtype", ctypes.c_int),
+                ("kv_dtype", ctypes.c_int), ("kernel", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_PI32 = ctypes.POINTER(ctypes.c_int32)
+_SIGS = {
+    "pa_block_pool_init": (ctypes.c_int, [ctypes.POINTER(PoolConfig), ctypes.POINTER(_P)]),
+    "pa_block_pool_destroy": (None, [_P]),
+    "pa_kv_bytes_per_token": (ctypes.c_uint64, [_P]),
+    "pa_block_bytes": (ctypes.c_uint64, [_P]),
+    "pa_seq_create": (ctypes.c_int, [_P, _PI32]),
+    "pa_seq_append_slots": (ctypes.c_int, [_P, _I32, _I32, _P]),
+    "pa_seq_append_slots_batch": (ctypes.c_int, [_P, _P, _I32, _I32, _P]),
+    "pa_seq_fork": (ctypes.c_int, [_P, _I32, _PI32]),
+    "pa_seq_free": (ctypes.c_int, [_P, _I32]),
+    "pa_seq_length": (ctypes.c_int, [_P, _I32, _PI32]),
+    "pa_block_refcount": (ctypes.c_int, [_P, _I32, _PI32]),
+    "pa_export_block_tables": (ctypes.c_int, [_P, _P, _I32, _I32, _P, _P]),
+    "pa_pool_get_stats": (ctypes.c_int, [_P, ctypes.POINTER(PoolStats)]),
+    "pa_cache_append": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, ctypes.POINTER(KvDesc),
+                                       ctypes.c_float, ctypes.c_float, _P]),
+    "pa_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(KvDesc), _I32, _I32, _I32]),
+    "pa_decode": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _I32, _I32, ctypes.c_float,
+                                 ctypes.c_float, ctypes.c_float, _P, _P, ctypes.c_size_t, _I32,
+                                 ctypes.POINTER(KvDesc), _P]),
+    "pa_last_error": (ctypes.c_char_p, []),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+def _check(status, where):
+    if status != OK:
+        raise PaError(status, where)
+
+
+def _addr(x):
+    """Data address of a torch tensor, a numpy array, an int or None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if isinstance(x, np.ndarray):
+        return x.ctypes.data
+    return x.data_ptr()
+
+
+def _i32_array(x):
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+# ---- block pool ------------------------------------------------------------
+class Pool:
+    """Owns a pa_pool handle; destroyed with the object."""
+
+    def __init__(self, handle, config):
+        self.handle = handle
+        self.config = config
+
+    def __del__(self):
+        if getattr(self, "handle", None):
+            _lib.pa_block_pool_destroy(self.handle)
+            self.handle = None
+
+
+def pa_block_pool_init(num_blocks, num_kv_heads, head_dim, kv_dtype, num_layers=1,
+                       block_size=16, shuffle_seed=0):
+    cfg = PoolConfig(num_blocks, block_size, num_layers, num_kv_heads, head_dim,
+                     DTYPE_CODES.get(kv_dtype, kv_dtype), shuffle_seed)
+    h = _P()
+    _check(_lib.pa_block_pool_init(ctypes.byref(cfg), ctypes.byref(h)), "pa_block_pool_init")
+    return Pool(h.value, cfg)
+
+
+def pa_block_pool_destroy(pool):
+    if pool.handle:
+        _lib.pa_block_pool_destroy(pool.handle)
+        pool.handle = None
+
+
+def pa_kv_bytes_per_token(pool):
+    return int(_lib.pa_kv_bytes_per_token(pool.handle))
+
+
+def pa_block_bytes(pool):
+    return int(_lib.pa_block_bytes(pool.handle))
+
+
+def pa_seq_create(pool):
+    sid = _I32()
+    _check(_lib.pa_seq_create(pool.handle, ctypes.byref(sid)), "pa_seq_create")
+    return sid.value
+
+
+def pa_seq_append_slots(pool, seq, ntok):
+    slots = np.empty(max(ntok, 1), dtype=np.int32)
+    _check(_lib.pa_seq_append_slots(pool.handle, seq, ntok, slots.ctypes.data),
+           "pa_seq_append_slots")
+    return slots[:ntok]
+
+
+def pa_seq_append_slots_batch(pool, seqs, ntok, slots_out=None):
+    """slots_out: optional int32 buffer (numpy / pinned tensor) of len(seqs)*ntok."""
+    seqs = _i32_array(seqs)
+    out = slots_out if slots_out is not None else np.empty(max(len(seqs) * ntok, 1), np.int32)
+    _check(_lib.pa_seq_append_slots_batch(pool.handle, seqs.ctypes.data, len(seqs), ntok,
+                                          _addr(out)), "pa_seq_append_slots_batch")
+    return out if slots_out is not None else out[:len(seqs) * ntok]
+
+
+def pa_seq_fork(pool, parent):
+    c = _I32()
+    _check(_lib.pa_seq_fork(pool.handle, parent, ctypes.byref(c)), "pa_seq_fork")
+    return c.value
+
+
+def pa_seq_free(pool, seq):
+    _check(_lib.pa_seq_free(pool.handle, seq), "pa_seq_free")
+
+
+def pa_seq_length(pool, seq):
+    n = _I32()
+    _check(_lib.pa_seq_length(pool.handle, seq, ctypes.byref(n)), "pa_seq_length")
+    return n.value
+
+
+def pa_block_refcount(pool, block):
+    r = _I32()
+    _check(_lib.pa_block_refcount(pool.handle, block, ctypes.byref(r)), "pa_block_refcount")
+    return r.value
+
+
+def pa_export_block_tables(pool, seqs, max_blocks, tables_out=None, lens_out=None):
+    """Returns (tables [nseq][max_blocks] int32, lens [nseq] int32); pass
+    preallocated buffers (numpy or pinned tensors) to fill them in place."""
+    seqs = _i32_array(seqs)
+    t = tables_out if tables_out is not None else np.empty((len(seqs), max_blocks), np.int32)
+    n = lens_out if lens_out is not None else np.empty(len(seqs), np.int32)
+    _check(_lib.pa_export_block_tables(pool.handle, seqs.ctypes.data, len(seqs), max_blocks,
+                                       _addr(t), _addr(n)), "pa_export_block_tables")
+    return t, n
+
+
+def pa_pool_get_stats(pool):
+    st = PoolStats()
+    _check(_lib.pa_pool_get_stats(pool.handle, ctypes.byref(st)), "pa_pool_get_stats")
+    return {f: getattr(st, f) for f, _ in PoolStats._fields_ if f != "reserved"}
+
+
+# ---- kernels ---------------------------------------------------------------
+def kv_desc(num_q_heads, num_kv_heads, head_dim, num_blocks, q_dtype, kv_dtype,
+            block_size=16, kernel=KERNEL_AUTO):
+    return KvDesc(num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                  DTYPE_CODES.get(q_dtype, q_dtype), DTYPE_CODES.get(kv_dtype, kv_dtype), kernel)
+
+
+def _check_tensor(t, name, nbytes=None):
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+    if nbytes is not None and t.numel() * t.element_size() != nbytes:
+        raise ValueError(f"{name}: expected {nbytes} bytes, got {t.numel() * t.element_size()}")
+
+
+def pa_cache_append(k, v, k_cache, v_cache, slot_mapping, desc, k_scale=1.0, v_scale=1.0,
+                    stream=None):
+    T = slot_mapping.numel()
+    qb, kb = DTYPE_BYTES[desc.q_dtype], DTYPE_BYTES[desc.kv_dtype]
+    row = desc.num_kv_heads * desc.head_dim
+    cache_bytes = desc.num_blocks * desc.block_size * row * kb
+    for t, nm in [(k, "k"), (v, "v")]:
+        _check_tensor(t, nm, T * row * qb)
+    for t, nm in [(k_cache, "k_cache"), (v_cache, "v_cache")]:
+        _check_tensor(t, nm, cache_bytes)
+    _check_tensor(slot_mapping, "slot_mapping", T * 4)
+    _check(_lib.pa_cache_append(_addr(k), _addr(v), _addr(k_cache), _addr(v_cache),
+                                _addr(slot_mapping), T, ctypes.byref(desc), k_scale, v_scale,
+                                _stream(stream)), "pa_cache_append")
+
+
+def pa_decode_workspace_bytes(desc, num_seqs, max_seq_len, partition_size):
+    return int(_lib.pa_decode_workspace_bytes(ctypes.byref(desc), num_seqs, max_seq_len,
+                                              partition_size))
+
+
+def pa_decode(q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale, out, desc,
+              k_scale=1.0, v_scale=1.0, workspace=None, partition_size=PARTITION_NONE,
+              stream=None):
+    B = seq_lens.numel()
+    qb, kb = DTYPE_BYTES[desc.q_dtype], DTYPE_BYTES[desc.kv_dtype]
+    qrow = desc.num_q_heads * desc.head_dim
+    cache_bytes = desc.num_blocks * desc.block_size * desc.num_kv_heads * desc.head_dim * kb
+    _check_tensor(q, "q", B * qrow * qb)
+    _check_tensor(out, "out", B * qrow * qb)
+    for t, nm in [(k_cache, "k_cache"), (v_cache, "v_cache")]:
+        _check_tensor(t, nm, cache_bytes)
+    _check_tensor(seq_lens, "seq_lens", B * 4)
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [num_seqs][max_blocks_per_seq]")
+    _check_tensor(block_tables, "block_tables")
+    ws_bytes = 0
+    if workspace is not None:
+        _check_tensor(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(_lib.pa_decode(_addr(q), _addr(k_cache), _addr(v_cache), _addr(block_tables),
+                          block_tables.shape[1], _addr(seq_lens), B, max_seq_len, scale,
+                          k_scale, v_scale, _addr(out), _addr(workspace), ws_bytes,
+                          partition_size, ctypes.byref(desc), _stream(stream)), "pa_decode")
+
+
+def pa_last_error():
+    return _lib.pa_last_error().decode()

@@ -1,0 +1,200 @@
+// C ABI of the device calls: argument checks, kernel choice, launches.
+// The block pool calls live in pool.cpp; pa.h documents every entry point.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "pa.h"
+#include "pa_internal.hpp"
+#include "work.hpp"
+
+namespace pa {
+
+hipError_t launch_decode_valu(const DecodeArgs &a, pa_dtype qt, pa_dtype kt, int D,
+                              int32_t num_items, hipStream_t s);
+bool valu_supports(pa_dtype qt, pa_dtype kt, int D, int G);
+hipError_t launch_merge(const DecodeArgs &a, pa_dtype qt, int D, hipStream_t s);
+hipError_t launch_append(const void *k, const void *v, void *kc, void *vc, const int32_t *slots,
+                         int32_t T, int32_t H, int32_t NB, int D, pa_dtype qt, pa_dtype kt,
+                         float k_inv, float v_inv, hipStream_t s);
+
+namespace {
+
+pa_status hip_fail(hipError_t e, const char *what)
+{
+    std::string m = std::string(what) + ": " + hipGetErrorString(e);
+    return fail(PA_ERR_HIP, m.c_str());
+}
+
+bool valid_dtype(pa_dtype t) { return dtype_bytes(t) != 0; }
+
+// The (q, kv) storage pairs the path defines: matching 16/32-bit types, or
+// FP8 storage under 16-bit activations.
+bool valid_pair(pa_dtype q, pa_dtype kv)
+{
+    if (q == kv)
+        return q != PA_FP8_E4M3;
+    return kv == PA_FP8_E4M3 && (q == PA_BF16 || q == PA_F16);
+}
+
+pa_status check_desc(const pa_kv_desc *d)
+{
+    if (!d)
+        return fail(PA_ERR_INVALID_ARG, "null desc");
+    if (d->num_q_heads <= 0 || d->num_kv_heads <= 0 || d->num_q_heads % d->num_kv_heads != 0)
+        return fail(PA_ERR_INVALID_ARG, "num_q_heads must be a positive multiple of num_kv_heads");
+    if (d->num_blocks <= 0)
+        return fail(PA_ERR_INVALID_ARG, "num_blocks must be positive");
+    if (!valid_dtype(d->q_dtype) || !valid_dtype(d->kv_dtype))
+        return fail(PA_ERR_INVALID_ARG, "unknown dtype");
+    if (!valid_pair(d->q_dtype, d->kv_dtype))
+        return fail(PA_ERR_UNSUPPORTED, "unsupported (q, kv) dtype pair");
+    if (d->block_size != kBlockSize)
+        return fail(PA_ERR_UNSUPPORTED, "block_size must be 16");
+    if (d->head_dim != 64 && d->head_dim != 128)
+        return fail(PA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+    if ((int64_t)d->num_blocks * d->num_kv_heads * kBlockSize * d->head_dim > (int64_t)1 << 40)
+        return fail(PA_ERR_INVALID_ARG, "cache too large");
+    return PA_OK;
+}
+
+int32_t parts_for(int32_t max_seq_len, int32_t partition)
+{
+    if (partition <= 0)
+        return 1;
+    int32_t p = (max_seq_len + partition - 1) / partition;
+    return p < 1 ? 1 : p;
+}
+
+} // namespace
+
+} // namespace pa
+
+using namespace pa;
+
+extern "C" {
+
+pa_status pa_cache_append(const void *k, const void *v, void *k_cache, void *v_cache,
+                          const int32_t *slot_mapping, int32_t num_tokens, const pa_kv_desc *desc,
+                          float k_scale, float v_scale, void *stream)
+{
+    pa_status st = check_desc(desc);
+    if (st != PA_OK)
+        return st;
+    if (num_tokens < 0)
+        return fail(PA_ERR_INVALID_ARG, "num_tokens must be >= 0");
+    if (num_tokens == 0)
+        return PA_OK;
+    if (!k || !v || !k_cache || !v_cache || !slot_mapping)
+        return fail(PA_ERR_INVALID_ARG, "null pointer");
+    float k_inv = 1.f, v_inv = 1.f;
+    if (desc->kv_dtype == PA_FP8_E4M3) {
+        if (!(k_scale > 0.f) || !(v_scale > 0.f) || k_scale == INFINITY || v_scale == INFINITY)
+            return fail(PA_ERR_INVALID_ARG, "FP8 scales must be positive and finite");
+        k_inv = 1.0f / k_scale;
+        v_inv = 1.0f / v_scale;
+    }
+    hipError_t e = launch_append(k, v, k_cache, v_cache, slot_mapping, num_tokens,
+                                 desc->num_kv_heads, desc->num_blocks, desc->head_dim,
+                                 desc->q_dtype, desc->kv_dtype, k_inv, v_inv,
+                                 static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "cache append launch");
+    return PA_OK;
+}
+
+size_t pa_decode_workspace_bytes(const pa_kv_desc *desc, int32_t num_seqs, int32_t max_seq_len,
+                                 int32_t partition_size)
+{
+    if (!desc || num_seqs <= 0 || max_seq_len < 0 || partition_size <= 0 ||
+        desc->num_kv_heads <= 0 || desc->num_q_heads <= 0 || desc->head_dim <= 0)
+        return 0;
+    const int64_t G = desc->num_q_heads / desc->num_kv_heads;
+    const int64_t W = (int64_t)num_seqs * desc->num_kv_heads * parts_for(max_seq_len, partition_size);
+    return (size_t)(W * G * (2 + desc->head_dim) * (int64_t)sizeof(float));
+}
+
+pa_status pa_decode(const void *q, const void *k_cache, const void *v_cache,
+                    const int32_t *block_tables, int32_t max_blocks_per_seq,
+                    const int32_t *seq_lens, int32_t num_seqs, int32_t max_seq_len, float scale,
+                    float k_scale, float v_scale, void *out, void *workspace,
+                    size_t workspace_bytes, int32_t partition_size, const pa_kv_desc *desc,
+                    void *stream)
+{
+    pa_status st = check_desc(desc);
+    if (st != PA_OK)
+        return st;
+    if (num_seqs < 0 || max_seq_len < 0 || max_blocks_per_seq < 0)
+        return fail(PA_ERR_INVALID_ARG, "negative size");
+    if (num_seqs == 0)
+        return PA_OK;
+    if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !out)
+        return fail(PA_ERR_INVALID_ARG, "null pointer");
+    if (q == out)
+        return fail(PA_ERR_INVALID_ARG, "out may not alias q");
+    if (!(scale > 0.f) || !(k_scale > 0.f) || !(v_scale > 0.f))
+        return fail(PA_ERR_INVALID_ARG, "scales must be positive");
+    if (partition_size == PA_PARTITION_BALANCED)
+        return fail(PA_ERR_UNSUPPORTED, "balanced partitioning is not built yet");
+    if (partition_size < 0 || partition_size % kBlockSize != 0)
+        return fail(PA_ERR_INVALID_ARG, "partition_size must be 0 or a positive multiple of 16");
+    if ((int64_t)max_blocks_per_seq * kBlockSize < (int64_t)max_seq_len)
+        return fail(PA_ERR_INVALID_ARG, "max_seq_len exceeds max_blocks_per_seq * block_size");
+
+    const int D = desc->head_dim;
+    const int G = desc->num_q_heads / desc->num_kv_heads;
+    DecodeArgs a{};
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.seq_lens = seq_lens;
+    a.out = out;
+    a.ws = static_cast<float *>(workspace);
+    a.num_seqs = num_seqs;
+    a.num_q_heads = desc->num_q_heads;
+    a.num_kv_heads = desc->num_kv_heads;
+    a.group = G;
+    a.num_blocks = desc->num_blocks;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.max_seq_len = max_seq_len;
+    a.partition = partition_size;
+    a.max_parts = parts_for(max_seq_len, partition_size);
+    a.score_scale = scale * k_scale * kLog2e;
+    a.v_scale = v_scale;
+
+    if (partition_size > 0) {
+        const size_t need = pa_decode_workspace_bytes(desc, num_seqs, max_seq_len, partition_size);
+        if (!workspace || workspace_bytes < need)
+            return fail(PA_ERR_CAPACITY, "workspace smaller than pa_decode_workspace_bytes()");
+    }
+    const int64_t items64 = (int64_t)num_seqs * desc->num_kv_heads * a.max_parts;
+    if (items64 > (int64_t)1 << 30)
+        return fail(PA_ERR_INVALID_ARG, "too many work items");
+    const int32_t items = (int32_t)items64;
+
+    int kernel = desc->kernel;
+    if (kernel == PA_KERNEL_AUTO)
+        kernel = PA_KERNEL_VALU;
+    if (kernel == PA_KERNEL_MFMA)
+        return fail(PA_ERR_UNSUPPORTED, "MFMA kernel is not built yet");
+    if (kernel != PA_KERNEL_VALU)
+        return fail(PA_ERR_INVALID_ARG, "unknown kernel choice");
+    if (!valu_supports(desc->q_dtype, desc->kv_dtype, D, G))
+        return fail(PA_ERR_UNSUPPORTED, "VALU kernel: unsupported (dtype, head_dim, group)");
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_decode_valu(a, desc->q_dtype, desc->kv_dtype, D, items, s);
+    if (e != hipSuccess)
+        return hip_fail(e, "decode launch");
+    if (partition_size > 0) {
+        e = launch_merge(a, desc->q_dtype, D, s);
+        if (e != hipSuccess)
+            return hip_fail(e, "merge launch");
+    }
+    return PA_OK;
+}
+
+} // extern "C"

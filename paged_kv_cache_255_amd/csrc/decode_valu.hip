@@ -1,0 +1,294 @@
+// PagedAttention decode on the vector ALU: one wave per work item (sequence,
+// KV head, token range), fp32 arithmetic for every storage dtype.
+//
+// What it computes: dev.to, "Why LLMs Run Out of VRAM: KV Cache Fragmentation
+// and How PagedAttention Fixes It", §1 (attention formula, decode of one new
+// query against the cached K/V) and §4 "The PagedAttention CUDA Kernel" (the
+// query walks its block table and reads K/V from scattered physical blocks).
+// The softmax is evaluated online (running max m, running sum l, rescaled
+// accumulator), one 16-token block at a time, in log2 units.
+//
+// Lane layout inside a wave, per 16-token block:
+//   K tile [16][D]: lane = 4 * token + c; lane c of a quad reads 16-byte
+//     chunks c, c+4, c+8, ... of its token's row, so each load instruction
+//     covers 64 contiguous bytes of every row.  Partial dot products are
+//     summed over the quad.
+//   V tile [D][16]: the tile is read as one contiguous run, 16 bytes per lane
+//     per instruction; a lane holds 16/bytes consecutive tokens of one
+//     dimension row and accumulates them, partial sums are combined over the
+//     lanes of a row at the end.
+//   The probabilities move from the K layout to the V layout through LDS.
+#include "device.hpp"
+#include "work.hpp"
+
+namespace pa {
+
+template <int QT, int KT, int D, int G>
+struct ValuShape {
+    using TQ = typename Store<QT>::T;
+    static constexpr int KE = Store<KT>::bytes;
+    static constexpr int ROW_BYTES = D * KE;          // one K row
+    static constexpr int CHUNKS = ROW_BYTES / 16;     // 16-byte chunks in a K row
+    static constexpr int CH_PER_LANE = CHUNKS / 4;
+    static constexpr int EPC = 16 / KE;               // elements per chunk
+    static constexpr int V_ROW_BYTES = kBlockSize * KE; // one V^T row (16 tokens)
+    static constexpr int V_LPR = V_ROW_BYTES / 16;    // lanes per V^T row
+    static constexpr int V_TPL = kBlockSize / V_LPR;  // tokens per lane
+    static constexpr int V_RPI = kWave / V_LPR;       // rows per load instruction
+    static constexpr int V_INSTR = D / V_RPI;
+    static constexpr int TILE_BYTES = kBlockSize * D * KE;
+    static_assert(CH_PER_LANE >= 1 && CHUNKS % 4 == 0, "K row too short for quad layout");
+    static_assert(V_INSTR >= 1 && D % V_RPI == 0, "V tile layout");
+};
+
+template <int QT, int KT, int D, int G>
+__global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a, int32_t num_items)
+{
+    using S = ValuShape<QT, KT, D, G>;
+    using TQ = typename S::TQ;
+    __shared__ float p_lds[4][G][kBlockSize];
+
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int32_t w = blockIdx.x * 4 + wid;
+    if (w >= num_items)
+        return;
+    const Item it = item_of(a, w);
+    if (it.valid_len && it.n > 0 && it.t0 >= it.t1)
+        return; // part beyond the end of this sequence
+    if (it.valid_len && it.n == 0 && it.p > 0)
+        return;
+
+    const int tq = lane >> 2;    // token of this lane in the K layout
+    const int cq = lane & 3;     // quad lane
+    const int vrow = lane / S::V_LPR;
+    const int vtok0 = (lane % S::V_LPR) * S::V_TPL;
+
+    // q of the G heads, the slice matching this lane's K chunks, in fp32.
+    float qv[G][S::CH_PER_LANE][S::EPC];
+    {
+        const TQ *qp = static_cast<const TQ *>(a.q) +
+                       ((size_t)it.b * a.num_q_heads + (size_t)it.g * G) * D;
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int j = 0; j < S::CH_PER_LANE; ++j)
+#pragma unroll
+                for (int e = 0; e < S::EPC; ++e)
+                    qv[h][j][e] = to_f32<QT>(qp[h * D + (cq + 4 * j) * S::EPC + e]) * a.score_scale;
+    }
+
+    float m[G], l[G], acc[G][S::V_INSTR];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        m[h] = -INFINITY;
+        l[h] = 0.f;
+#pragma unroll
+        for (int i = 0; i < S::V_INSTR; ++i)
+            acc[h][i] = 0.f;
+    }
+
+    bool bad = !it.valid_len;
+    const int32_t *table = a.block_tables + (size_t)it.b * a.max_blocks_per_seq;
+    const char *kbase = static_cast<const char *>(a.k_cache);
+    const char *vbase = static_cast<const char *>(a.v_cache);
+    const int32_t jb0 = it.t0 / kBlockSize;
+    const int32_t jb1 = bad ? jb0 : (it.t1 + kBlockSize - 1) / kBlockSize;
+
+    for (int32_t jb = jb0; jb < jb1; ++jb) {
+        const int32_t phys = __builtin_amdgcn_readfirstlane(table[jb]);
+        if (phys < 0 || phys >= a.num_blocks) {
+            bad = true;
+            break;
+        }
+        const size_t tile = ((size_t)phys * a.num_kv_heads + it.g) * S::TILE_BYTES;
+        const int32_t tok_base = jb * kBlockSize;
+        const bool tail = tok_base + kBlockSize > it.t1;
+
+        // K tile: this lane's chunks of token tq.
+        float kv[S::CH_PER_LANE][S::EPC];
+#pragma unroll
+        for (int j = 0; j < S::CH_PER_LANE; ++j) {
+            const u32x4 c = load16(kbase + tile + tq * S::ROW_BYTES + (cq + 4 * j) * 16);
+            Chunk<KT>::unpack(c, kv[j]);
+        }
+        // V tile: this lane's rows.
+        float vv[S::V_INSTR][S::V_TPL];
+#pragma unroll
+        for (int i = 0; i < S::V_INSTR; ++i) {
+            const u32x4 c = load16(vbase + tile + i * 1024 + lane * 16);
+            Chunk<KT>::unpack(c, vv[i]);
+        }
+
+        // scores of token tq for the G heads (log2 units)
+        const bool tok_ok = tok_base + tq < it.t1;
+        float s[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float d = 0.f;
+#pragma unroll
+            for (int j = 0; j < S::CH_PER_LANE; ++j)
+#pragma unroll
+                for (int e = 0; e < S::EPC; ++e)
+                    d = fmaf(qv[h][j][e], kv[j][e], d);
+            d += shfl_xor(d, 1);
+            d += shfl_xor(d, 2);
+            s[h] = tok_ok ? d : -INFINITY;
+        }
+        // online softmax update, block max over the whole wave
+        float pr[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float bm = s[h];
+            bm = fmaxf(bm, shfl_xor(bm, 4));
+            bm = fmaxf(bm, shfl_xor(bm, 8));
+            bm = fmaxf(bm, shfl_xor(bm, 16));
+            bm = fmaxf(bm, shfl_xor(bm, 32));
+            const float mn = fmaxf(m[h], bm);
+            const float alpha = __builtin_amdgcn_exp2f(m[h] - mn);
+            m[h] = mn;
+            pr[h] = __builtin_amdgcn_exp2f(s[h] - mn);
+            l[h] = fmaf(l[h], alpha, pr[h]);
+#pragma unroll
+            for (int i = 0; i < S::V_INSTR; ++i)
+                acc[h][i] *= alpha;
+        }
+        // K layout -> V layout for the probabilities
+#pragma unroll
+        for (int h = cq; h < G; h += 4)
+            p_lds[wid][h][tq] = pr[h];
+        wave_lds_sync();
+        if (tail) {
+#pragma unroll
+            for (int i = 0; i < S::V_INSTR; ++i)
+#pragma unroll
+                for (int e = 0; e < S::V_TPL; ++e)
+                    if (tok_base + vtok0 + e >= it.t1)
+                        vv[i][e] = 0.f; // slots past the end may hold anything
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float pv[S::V_TPL];
+#pragma unroll
+            for (int e = 0; e < S::V_TPL; ++e)
+                pv[e] = p_lds[wid][h][vtok0 + e];
+#pragma unroll
+            for (int i = 0; i < S::V_INSTR; ++i) {
+                float t = acc[h][i];
+#pragma unroll
+                for (int e = 0; e < S::V_TPL; ++e)
+                    t = fmaf(pv[e], vv[i][e], t);
+                acc[h][i] = t;
+            }
+        }
+        wave_lds_sync();
+    }
+
+    // combine lane partials: l over the 16 token quads, acc over a row's lanes
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        l[h] += shfl_xor(l[h], 4);
+        l[h] += shfl_xor(l[h], 8);
+        l[h] += shfl_xor(l[h], 16);
+        l[h] += shfl_xor(l[h], 32);
+#pragma unroll
+        for (int i = 0; i < S::V_INSTR; ++i) {
+#pragma unroll
+            for (int x = 1; x < S::V_LPR; x <<= 1)
+                acc[h][i] += shfl_xor(acc[h][i], x);
+        }
+    }
+
+    const bool writer = (lane % S::V_LPR) == 0;
+    if (a.partition == 0) {
+        TQ *o = static_cast<TQ *>(a.out) + ((size_t)it.b * a.num_q_heads + (size_t)it.g * G) * D;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float inv = (it.n > 0) ? a.v_scale / l[h] : 0.f;
+#pragma unroll
+            for (int i = 0; i < S::V_INSTR; ++i) {
+                float r = bad ? NAN : acc[h][i] * inv;
+                if (writer)
+                    o[h * D + i * S::V_RPI + vrow] = from_f32<QT>(r);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            if (lane == 0) {
+                float *ml = ws_ml(a, w, h);
+                ml[0] = bad ? NAN : m[h];
+                ml[1] = bad ? NAN : l[h];
+            }
+            float *accp = ws_acc(a, w, h, D);
+#pragma unroll
+            for (int i = 0; i < S::V_INSTR; ++i)
+                if (writer)
+                    accp[i * S::V_RPI + vrow] = bad ? NAN : acc[h][i] * a.v_scale;
+        }
+    }
+}
+
+// Host-side launcher, instantiated per supported (q, kv, D, G).
+template <int QT, int KT, int D, int G>
+hipError_t launch_valu(const DecodeArgs &a, int32_t num_items, hipStream_t stream)
+{
+    const int grid = (num_items + 3) / 4;
+    hipLaunchKernelGGL((decode_valu_kernel<QT, KT, D, G>), dim3(grid), dim3(256), 0, stream, a,
+                       num_items);
+    return hipGetLastError();
+}
+
+// Dispatch on the runtime shape; returns hipErrorInvalidValue if the shape has
+// no instantiation.
+template <int QT, int KT, int D>
+hipError_t valu_by_group(const DecodeArgs &a, int32_t n, hipStream_t s)
+{
+    switch (a.group) {
+    case 1: return launch_valu<QT, KT, D, 1>(a, n, s);
+    case 2: return launch_valu<QT, KT, D, 2>(a, n, s);
+    case 4: return launch_valu<QT, KT, D, 4>(a, n, s);
+    case 8:
+        if constexpr (D == 64)
+            return launch_valu<QT, KT, D, 8>(a, n, s);
+        else
+            return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int QT, int KT>
+hipError_t valu_by_dim(const DecodeArgs &a, int D, int32_t n, hipStream_t s)
+{
+    if (D == 64)
+        return valu_by_group<QT, KT, 64>(a, n, s);
+    if (D == 128)
+        return valu_by_group<QT, KT, 128>(a, n, s);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_valu(const DecodeArgs &a, pa_dtype qt, pa_dtype kt, int D,
+                              int32_t num_items, hipStream_t s)
+{
+    if (qt == PA_F32 && kt == PA_F32)
+        return valu_by_dim<PA_F32, PA_F32>(a, D, num_items, s);
+    if (qt == PA_F16 && kt == PA_F16)
+        return valu_by_dim<PA_F16, PA_F16>(a, D, num_items, s);
+    if (qt == PA_BF16 && kt == PA_BF16)
+        return valu_by_dim<PA_BF16, PA_BF16>(a, D, num_items, s);
+    if (qt == PA_BF16 && kt == PA_FP8_E4M3)
+        return valu_by_dim<PA_BF16, PA_FP8_E4M3>(a, D, num_items, s);
+    if (qt == PA_F16 && kt == PA_FP8_E4M3)
+        return valu_by_dim<PA_F16, PA_FP8_E4M3>(a, D, num_items, s);
+    return hipErrorInvalidValue;
+}
+
+bool valu_supports(pa_dtype qt, pa_dtype kt, int D, int G)
+{
+    const bool dt = (qt == kt && qt != PA_FP8_E4M3) ||
+                    (kt == PA_FP8_E4M3 && (qt == PA_BF16 || qt == PA_F16));
+    const bool g = G == 1 || G == 2 || G == 4 || (G == 8 && D == 64);
+    return dt && (D == 64 || D == 128) && g;
+}
+
+} // namespace pa

@@ -1,0 +1,155 @@
+// Device-side helpers for the gfx950 kernels: storage types, conversions,
+// cross-lane reductions.  Everything here runs on the GPU only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa.h"
+
+namespace pa {
+
+constexpr int kWave = 64;     // CDNA wavefront width
+constexpr int kBlockSize = 16; // tokens per KV block (the only size built)
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---- storage types ---------------------------------------------------------
+template <int DT> struct Store;
+template <> struct Store<PA_F32> { using T = float; static constexpr int bytes = 4; };
+template <> struct Store<PA_F16> { using T = _Float16; static constexpr int bytes = 2; };
+template <> struct Store<PA_BF16> { using T = __bf16; static constexpr int bytes = 2; };
+template <> struct Store<PA_FP8_E4M3> { using T = uint8_t; static constexpr int bytes = 1; };
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ float f16_lo(uint32_t w)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// Two E4M3 bytes (word `hi` of w) -> two floats, hardware conversion.
+__device__ __forceinline__ f32x2 fp8x2_to_f32(uint32_t w, bool hi)
+{
+    return hi ? __builtin_amdgcn_cvt_pk_f32_fp8(w, true) : __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+}
+
+// Unpacks one 16-byte chunk of stored values into floats (16/bytes values).
+template <int DT> struct Chunk;
+template <> struct Chunk<PA_F32> {
+    static constexpr int N = 4;
+    __device__ static void unpack(const u32x4 c, float *o)
+    {
+        o[0] = __uint_as_float(c.x); o[1] = __uint_as_float(c.y);
+        o[2] = __uint_as_float(c.z); o[3] = __uint_as_float(c.w);
+    }
+};
+template <> struct Chunk<PA_BF16> {
+    static constexpr int N = 8;
+    __device__ static void unpack(const u32x4 c, float *o)
+    {
+        const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { o[2 * i] = bf16_lo(w[i]); o[2 * i + 1] = bf16_hi(w[i]); }
+    }
+};
+template <> struct Chunk<PA_F16> {
+    static constexpr int N = 8;
+    __device__ static void unpack(const u32x4 c, float *o)
+    {
+        const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { o[2 * i] = f16_lo(w[i]); o[2 * i + 1] = f16_hi(w[i]); }
+    }
+};
+template <> struct Chunk<PA_FP8_E4M3> {
+    static constexpr int N = 16;
+    __device__ static void unpack(const u32x4 c, float *o)
+    {
+        const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f32x2 a = fp8x2_to_f32(w[i], false);
+            f32x2 b = fp8x2_to_f32(w[i], true);
+            o[4 * i] = a.x; o[4 * i + 1] = a.y; o[4 * i + 2] = b.x; o[4 * i + 3] = b.y;
+        }
+    }
+};
+
+// ---- scalar conversions ----------------------------------------------------
+template <int DT> __device__ __forceinline__ float to_f32(typename Store<DT>::T x);
+template <> __device__ __forceinline__ float to_f32<PA_F32>(float x) { return x; }
+template <> __device__ __forceinline__ float to_f32<PA_F16>(_Float16 x) { return (float)x; }
+template <> __device__ __forceinline__ float to_f32<PA_BF16>(__bf16 x) { return (float)x; }
+
+// Round to nearest even (the compiler lowers these to v_cvt_*_f32, RNE).
+template <int DT> __device__ __forceinline__ typename Store<DT>::T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<PA_F32>(float x) { return x; }
+template <> __device__ __forceinline__ _Float16 from_f32<PA_F16>(float x) { return (_Float16)x; }
+template <> __device__ __forceinline__ __bf16 from_f32<PA_BF16>(float x) { return (__bf16)x; }
+
+// fp32 -> E4M3FN, nearest value with ties to the even code, saturating at
+// +-448, NaN -> 0x7F with the sign kept.  Works on the fp32 bit pattern: the
+// normal range keeps the top 3 mantissa bits with round-half-even on the
+// dropped 20, and the exponent carry of a round-up falls into place because
+// (exponent, mantissa) are adjacent fields; below 2^-6 the value is scaled
+// by 2^9 (exact) and rounded to an integer count of the 2^-9 quantum.
+__device__ __forceinline__ uint8_t f32_to_e4m3(float x)
+{
+    const uint32_t u = __float_as_uint(x);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    if (a > 0x7F800000u)
+        return (uint8_t)(sign | 0x7Fu);
+    if (a >= 0x43E00000u) // 448.0f and above (including inf)
+        return (uint8_t)(sign | 0x7Eu);
+    if (a < 0x3C800000u) { // below 2^-6: subnormal E4M3 (or zero)
+        const float q = __builtin_rintf(__uint_as_float(a) * 512.0f); // 0..8
+        return (uint8_t)(sign | (uint32_t)q);
+    }
+    uint32_t r = a >> 20;           // biased fp32 exponent : top 3 mantissa bits
+    const uint32_t rest = a & 0xFFFFFu;
+    if (rest > 0x80000u || (rest == 0x80000u && (r & 1u)))
+        ++r;
+    r -= (127u - 7u) << 3;          // rebias exponent 127 -> 7
+    if (r > 0x7Eu)
+        r = 0x7Eu;
+    return (uint8_t)(sign | r);
+}
+
+// ---- cross-lane ------------------------------------------------------------
+__device__ __forceinline__ float shfl_xor(float v, int mask)
+{
+    return __shfl_xor(v, mask, kWave);
+}
+
+// Orders this wave's LDS accesses in program order for the compiler; the
+// hardware already executes one wave's LDS instructions in order.
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ u32x4 load16(const void *p)
+{
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+
+} // namespace pa

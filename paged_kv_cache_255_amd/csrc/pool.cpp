@@ -1,0 +1,305 @@
+// Host-side block pool: free list, per-sequence block tables, reference
+// counts.  Pure C++17, no HIP; it is what a serving scheduler calls once per
+// decode step to get each new token's slot (pa.h documents every call).
+//
+// [devto] dev.to, "Why LLMs Run Out of VRAM: KV Cache Fragmentation and How
+//         PagedAttention Fixes It", §4 (block pool, block tables, on-demand
+//         allocation) and §5 (shared blocks with reference counts).
+// [hi]    hyperinfer.ai, "KV cache & paged attention deep dive" (free pool,
+//         eviction frees a sequence's blocks).
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "pa.h"
+#include "pa_internal.hpp"
+
+struct pa_pool {
+    pa_pool_config cfg{};
+    std::vector<int32_t> free_list; // taken from and returned to the back
+    std::vector<int32_t> refcount;  // per physical block
+    struct Seq {
+        bool live = false;
+        int32_t len = 0;
+        std::vector<int32_t> blocks;
+    };
+    std::vector<Seq> seqs; // index = sequence id
+};
+
+namespace {
+
+// splitmix64 (Steele, Lea, Flood, OOPSLA 2014).
+struct SplitMix64 {
+    uint64_t s;
+    uint64_t next()
+    {
+        s += 0x9E3779B97F4A7C15ull;
+        uint64_t z = s;
+        z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+        z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+        return z ^ (z >> 31);
+    }
+};
+
+int32_t blocks_for(int64_t tokens, int32_t bs) { return (int32_t)((tokens + bs - 1) / bs); }
+
+pa_pool::Seq *live_seq(pa_pool *p, int32_t id)
+{
+    if (!p || id < 0 || (size_t)id >= p->seqs.size() || !p->seqs[id].live)
+        return nullptr;
+    return &p->seqs[id];
+}
+
+const pa_pool::Seq *live_seq(const pa_pool *p, int32_t id)
+{
+    return live_seq(const_cast<pa_pool *>(p), id);
+}
+
+// New blocks `s` needs for ntok more tokens, or an error if the write would
+// land in a block some other table also maps.
+pa_status check_append(const pa_pool *p, const pa_pool::Seq &s, int32_t ntok, int32_t *need)
+{
+    const int32_t bs = p->cfg.block_size;
+    if (ntok > 0 && s.len % bs != 0 && p->refcount[s.blocks.back()] > 1)
+        return pa::fail(PA_ERR_UNSUPPORTED,
+                        "append would write into a block shared with another sequence "
+                        "(copy on write is not implemented)");
+    int64_t total = (int64_t)s.len + ntok;
+    if (total > INT32_MAX)
+        return pa::fail(PA_ERR_INVALID_ARG, "sequence length overflows int32");
+    *need = blocks_for(total, bs) - (int32_t)s.blocks.size();
+    return PA_OK;
+}
+
+void do_append(pa_pool *p, pa_pool::Seq &s, int32_t ntok, int32_t *slots)
+{
+    const int32_t bs = p->cfg.block_size;
+    const int32_t need = blocks_for((int64_t)s.len + ntok, bs) - (int32_t)s.blocks.size();
+    for (int32_t i = 0; i < need; ++i) {
+        int32_t b = p->free_list.back();
+        p->free_list.pop_back();
+        p->refcount[b] = 1;
+        s.blocks.push_back(b);
+    }
+    for (int32_t i = 0; i < ntok; ++i) {
+        int32_t pos = s.len + i;
+        if (slots)
+            slots[i] = s.blocks[pos / bs] * bs + pos % bs;
+    }
+    s.len += ntok;
+}
+
+} // namespace
+
+extern "C" {
+
+pa_status pa_block_pool_init(const pa_pool_config *cfg, pa_pool **out)
+{
+    if (!cfg || !out)
+        return pa::fail(PA_ERR_INVALID_ARG, "null argument");
+    *out = nullptr;
+    if (cfg->num_blocks <= 0 || cfg->block_size <= 0 || cfg->num_layers <= 0 ||
+        cfg->num_kv_heads <= 0 || cfg->head_dim <= 0)
+        return pa::fail(PA_ERR_INVALID_ARG, "pool sizes must be positive");
+    if (pa::dtype_bytes(cfg->kv_dtype) == 0)
+        return pa::fail(PA_ERR_INVALID_ARG, "unknown kv dtype");
+    if (cfg->block_size != 16)
+        return pa::fail(PA_ERR_UNSUPPORTED, "block_size must be 16");
+    if ((int64_t)cfg->num_blocks * cfg->block_size > INT32_MAX)
+        return pa::fail(PA_ERR_INVALID_ARG, "num_blocks * block_size overflows int32 slots");
+    pa_pool *p = new (std::nothrow) pa_pool();
+    if (!p)
+        return pa::fail(PA_ERR_INVALID_ARG, "out of host memory");
+    p->cfg = *cfg;
+    p->free_list.resize(cfg->num_blocks);
+    for (int32_t i = 0; i < cfg->num_blocks; ++i)
+        p->free_list[i] = i;
+    if (cfg->shuffle_seed != 0) {
+        SplitMix64 rng{cfg->shuffle_seed};
+        for (int64_t i = cfg->num_blocks - 1; i > 0; --i) {
+            uint64_t j = rng.next() % (uint64_t)(i + 1);
+            std::swap(p->free_list[i], p->free_list[j]);
+        }
+    }
+    p->refcount.assign(cfg->num_blocks, 0);
+    *out = p;
+    return PA_OK;
+}
+
+void pa_block_pool_destroy(pa_pool *pool) { delete pool; }
+
+uint64_t pa_kv_bytes_per_token(const pa_pool *p)
+{
+    if (!p)
+        return 0;
+    return 2ull * (uint64_t)p->cfg.num_layers * (uint64_t)p->cfg.num_kv_heads *
+           (uint64_t)p->cfg.head_dim * (uint64_t)pa::dtype_bytes(p->cfg.kv_dtype);
+}
+
+uint64_t pa_block_bytes(const pa_pool *p)
+{
+    if (!p)
+        return 0;
+    return (uint64_t)p->cfg.block_size * (uint64_t)p->cfg.num_kv_heads *
+           (uint64_t)p->cfg.head_dim * (uint64_t)pa::dtype_bytes(p->cfg.kv_dtype);
+}
+
+pa_status pa_seq_create(pa_pool *p, int32_t *seq_out)
+{
+    if (!p || !seq_out)
+        return pa::fail(PA_ERR_INVALID_ARG, "null argument");
+    if (p->seqs.size() >= (size_t)INT32_MAX)
+        return pa::fail(PA_ERR_CAPACITY, "sequence ids exhausted");
+    p->seqs.emplace_back();
+    p->seqs.back().live = true;
+    *seq_out = (int32_t)(p->seqs.size() - 1);
+    return PA_OK;
+}
+
+pa_status pa_seq_append_slots(pa_pool *p, int32_t seq, int32_t ntok, int32_t *slots_out)
+{
+    pa_pool::Seq *s = live_seq(p, seq);
+    if (!s)
+        return pa::fail(PA_ERR_INVALID_ARG, "unknown or freed sequence id");
+    if (ntok < 0 || (ntok > 0 && !slots_out))
+        return pa::fail(PA_ERR_INVALID_ARG, "bad token count or null slots_out");
+    int32_t need = 0;
+    pa_status st = check_append(p, *s, ntok, &need);
+    if (st != PA_OK)
+        return st;
+    if ((size_t)need > p->free_list.size())
+        return pa::fail(PA_ERR_OUT_OF_BLOCKS, "block pool exhausted");
+    do_append(p, *s, ntok, slots_out);
+    return PA_OK;
+}
+
+pa_status pa_seq_append_slots_batch(pa_pool *p, const int32_t *seqs, int32_t nseq, int32_t ntok,
+                                    int32_t *slots_out)
+{
+    if (!p || nseq < 0 || ntok < 0 || (nseq > 0 && !seqs) || (nseq > 0 && ntok > 0 && !slots_out))
+        return pa::fail(PA_ERR_INVALID_ARG, "bad batch arguments");
+    std::vector<int32_t> sorted(seqs, seqs + nseq);
+    std::sort(sorted.begin(), sorted.end());
+    if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end())
+        return pa::fail(PA_ERR_INVALID_ARG, "sequence repeated in batch");
+    int64_t total = 0;
+    for (int32_t i = 0; i < nseq; ++i) {
+        pa_pool::Seq *s = live_seq(p, seqs[i]);
+        if (!s)
+            return pa::fail(PA_ERR_INVALID_ARG, "unknown or freed sequence id in batch");
+        int32_t need = 0;
+        pa_status st = check_append(p, *s, ntok, &need);
+        if (st != PA_OK)
+            return st;
+        total += need;
+    }
+    if ((size_t)total > p->free_list.size())
+        return pa::fail(PA_ERR_OUT_OF_BLOCKS, "block pool exhausted");
+    for (int32_t i = 0; i < nseq; ++i)
+        do_append(p, p->seqs[seqs[i]], ntok, slots_out ? slots_out + (size_t)i * ntok : nullptr);
+    return PA_OK;
+}
+
+pa_status pa_seq_fork(pa_pool *p, int32_t parent, int32_t *child_out)
+{
+    if (!child_out || !live_seq(p, parent))
+        return pa::fail(PA_ERR_INVALID_ARG, "unknown parent or null child_out");
+    int32_t child;
+    pa_status st = pa_seq_create(p, &child);
+    if (st != PA_OK)
+        return st;
+    pa_pool::Seq &par = p->seqs[parent];
+    pa_pool::Seq &c = p->seqs[child];
+    c.blocks = par.blocks;
+    c.len = par.len;
+    for (int32_t b : c.blocks)
+        ++p->refcount[b];
+    *child_out = child;
+    return PA_OK;
+}
+
+pa_status pa_seq_free(pa_pool *p, int32_t seq)
+{
+    pa_pool::Seq *s = live_seq(p, seq);
+    if (!s)
+        return pa::fail(PA_ERR_INVALID_ARG, "unknown or already freed sequence id");
+    for (int32_t b : s->blocks) {
+        if (--p->refcount[b] == 0)
+            p->free_list.push_back(b);
+    }
+    s->blocks.clear();
+    s->blocks.shrink_to_fit();
+    s->len = 0;
+    s->live = false;
+    return PA_OK;
+}
+
+pa_status pa_seq_length(const pa_pool *p, int32_t seq, int32_t *len_out)
+{
+    const pa_pool::Seq *s = live_seq(p, seq);
+    if (!s || !len_out)
+        return pa::fail(PA_ERR_INVALID_ARG, "unknown sequence or null len_out");
+    *len_out = s->len;
+    return PA_OK;
+}
+
+pa_status pa_block_refcount(const pa_pool *p, int32_t block, int32_t *refcount_out)
+{
+    if (!p || !refcount_out || block < 0 || block >= p->cfg.num_blocks)
+        return pa::fail(PA_ERR_INVALID_ARG, "bad block id or null output");
+    *refcount_out = p->refcount[block];
+    return PA_OK;
+}
+
+pa_status pa_export_block_tables(const pa_pool *p, const int32_t *seqs, int32_t nseq,
+                                 int32_t max_blocks, int32_t *tables_out, int32_t *lens_out)
+{
+    if (!p || nseq < 0 || max_blocks < 0 || (nseq > 0 && !seqs))
+        return pa::fail(PA_ERR_INVALID_ARG, "bad export arguments");
+    for (int32_t i = 0; i < nseq; ++i) {
+        const pa_pool::Seq *s = live_seq(p, seqs[i]);
+        if (!s)
+            return pa::fail(PA_ERR_INVALID_ARG, "unknown sequence id in export");
+        if (tables_out && s->blocks.size() > (size_t)max_blocks)
+            return pa::fail(PA_ERR_CAPACITY, "block table longer than max_blocks");
+    }
+    for (int32_t i = 0; i < nseq; ++i) {
+        const pa_pool::Seq &s = p->seqs[seqs[i]];
+        if (tables_out) {
+            int32_t *row = tables_out + (size_t)i * max_blocks;
+            const size_t n = s.blocks.size();
+            if (n)
+                std::memcpy(row, s.blocks.data(), n * sizeof(int32_t));
+            std::fill(row + n, row + max_blocks, -1);
+        }
+        if (lens_out)
+            lens_out[i] = s.len;
+    }
+    return PA_OK;
+}
+
+pa_status pa_pool_get_stats(const pa_pool *p, pa_pool_stats *out)
+{
+    if (!p || !out)
+        return pa::fail(PA_ERR_INVALID_ARG, "null argument");
+    pa_pool_stats st{};
+    st.num_blocks = p->cfg.num_blocks;
+    st.free_blocks = (int32_t)p->free_list.size();
+    st.used_blocks = st.num_blocks - st.free_blocks;
+    for (int32_t r : p->refcount)
+        st.shared_blocks += (r > 1);
+    for (const auto &s : p->seqs) {
+        if (!s.live)
+            continue;
+        ++st.live_seqs;
+        st.logical_tokens += s.len;
+        st.mapped_blocks += (int64_t)s.blocks.size();
+        st.tail_slack_tokens += (int64_t)s.blocks.size() * p->cfg.block_size - s.len;
+    }
+    *out = st;
+    return PA_OK;
+}
+
+} // extern "C"

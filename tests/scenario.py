@@ -1,0 +1,227 @@
+"""Runs one decode step of a workload on both sides.
+
+GPU side: the library's block pool, cache append and decode (through the C
+ABI).  Oracle side: the allocator model, the oracle's append and decode.  The
+two meet only in the seeded inputs from `workloads` and in the comparisons
+the tests make.
+"""
+import numpy as np
+import torch
+
+import oracle
+import paged_kv_cache_255_amd as pa
+import workloads
+from oracle import alloc_model as am
+from paged_kv_cache_255_amd.plan import execute_plan
+
+TORCH_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
+            "e4m3": torch.uint8}
+EB = {"f32": 4, "f16": 2, "bf16": 2, "e4m3": 1}
+TOL = {"f32": ("rowrel", 1e-5), "f16": ("abs", 1e-2), "bf16": ("abs", 1e-2),
+       "e4m3": ("abs", 2e-2)}
+
+
+def cache_bytes(w):
+    return w.num_blocks * w.num_kv_heads * 16 * w.head_dim * EB[w.kv_dtype]
+
+
+def poisoned_device_cache(w, device="cuda"):
+    """Cache tensor filled with 0xFF bytes: NaN in every float format, so a
+    read of a slot that holds no token shows up in the output."""
+    t = torch.full((cache_bytes(w),), 0xFF, dtype=torch.uint8, device=device)
+    return t if w.kv_dtype == "e4m3" else t.view(TORCH_DT[w.kv_dtype])
+
+
+def poisoned_host_cache(w):
+    dt = {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16, "e4m3": np.uint8}[w.kv_dtype]
+    a = np.empty(cache_bytes(w) // EB[w.kv_dtype], dtype=dt)
+    a.view(np.uint8)[:] = 0xFF
+    return a
+
+
+def as_bytes(t):
+    return t.contiguous().view(torch.uint8).cpu().numpy()
+
+
+class Inputs:
+    """Seeded tensors of one layer, on the device."""
+
+    def __init__(self, w, layer=0, device="cuda"):
+        self.k_pre, self.v_pre = workloads.prefill_tensors(w, layer, device)
+        self.q, self.k_new, self.v_new = workloads.step_tensors(w, layer, device)
+        if w.kv_dtype == "e4m3":
+            self.k_scale = workloads.fp8_scale(self.k_pre)
+            self.v_scale = workloads.fp8_scale(self.v_pre)
+        else:
+            self.k_scale = self.v_scale = 1.0
+
+
+class GpuStep:
+    """The library path for one layer: pool, append of the prefill and of the
+    new token, decode."""
+
+    def __init__(self, w, layer, inputs, partition=None, kernel=pa.KERNEL_AUTO):
+        self.w = w
+        self.partition = w.partition_size if partition is None else partition
+        self.pool = pa.pa_block_pool_init(w.num_blocks, w.num_kv_heads, w.head_dim, w.kv_dtype,
+                                          shuffle_seed=w.shuffle_seeds[layer])
+        ids, pre = execute_plan(self.pool, w.ops)
+        self.dec = [ids[s] for s in w.decode_seqs]
+        self.pre_slots = pre
+        self.step_slots = pa.pa_seq_append_slots_batch(self.pool, self.dec, 1)
+        self.tables, self.lens = pa.pa_export_block_tables(self.pool, self.dec,
+                                                           w.max_blocks_per_seq())
+        self.desc = pa.kv_desc(w.num_q_heads, w.num_kv_heads, w.head_dim, w.num_blocks,
+                               w.q_dtype, w.kv_dtype, kernel=kernel)
+        self.inputs = inputs
+        self.k_cache = poisoned_device_cache(w)
+        self.v_cache = poisoned_device_cache(w)
+        self.d_tables = torch.from_numpy(self.tables).cuda()
+        self.d_lens = torch.from_numpy(self.lens).cuda()
+        self.out = torch.empty_like(inputs.q)
+        self.workspace = None
+        if self.partition > 0:
+            nb = pa.pa_decode_workspace_bytes(self.desc, w.num_seqs, w.max_seq_len(),
+                                              self.partition)
+            self.workspace = torch.empty(nb, dtype=torch.uint8, device="cuda")
+
+    def append_prefill(self):
+        i = self.inputs
+        slots = torch.from_numpy(self.pre_slots).cuda()
+        pa.pa_cache_append(i.k_pre, i.v_pre, self.k_cache, self.v_cache, slots, self.desc,
+                           i.k_scale, i.v_scale)
+
+    def append_step(self):
+        i = self.inputs
+        slots = torch.from_numpy(np.ascontiguousarray(self.step_slots)).cuda()
+        pa.pa_cache_append(i.k_new, i.v_new, self.k_cache, self.v_cache, slots, self.desc,
+                           i.k_scale, i.v_scale)
+
+    def decode(self, out=None):
+        i = self.inputs
+        out = self.out if out is None else out
+        pa.pa_decode(i.q, self.k_cache, self.v_cache, self.d_tables, self.d_lens,
+                     self.w.max_seq_len(), self.w.scale, out, self.desc, i.k_scale, i.v_scale,
+                     workspace=self.workspace, partition_size=self.partition)
+        return out
+
+
+def _ancestors(ops):
+    """plan seq -> the plan seqs whose prefill tokens its table maps."""
+    parent = {}
+    n = 0
+    for op in ops:
+        if op[0] == "create":
+            parent[n] = None
+            n += 1
+        elif op[0] == "fork":
+            parent[n] = op[1]
+            n += 1
+    out = {}
+    for s in parent:
+        chain, p = [s], parent[s]
+        while p is not None:
+            chain.append(p)
+            p = parent[p]
+        out[s] = set(chain)
+    return out
+
+
+class OracleStep:
+    """The oracle path for one layer.  `only` restricts the work to some
+    decode positions (their prefill tokens and output rows)."""
+
+    def __init__(self, w, layer, inputs, only=None):
+        self.w = w
+        m = am.PoolModel(w.num_blocks, 16, w.shuffle_seeds[layer])
+        mids, mpre = am.execute_plan(m, w.ops)
+        self.pre_slots = np.array(mpre, dtype=np.int32)
+        mdec = [mids[s] for s in w.decode_seqs]
+        st, mstep = m.append_slots_batch(mdec, 1)
+        assert st == am.OK
+        self.step_slots = np.array(mstep, dtype=np.int32)
+        st, mt, ml = m.export(mdec, w.max_blocks_per_seq())
+        assert st == am.OK
+        self.tables = np.array(mt, dtype=np.int32).reshape(len(mdec), -1)
+        self.lens = np.array(ml, dtype=np.int32)
+        self.only = None if only is None else sorted(only)
+        self.k_cache = poisoned_host_cache(w)
+        self.v_cache = poisoned_host_cache(w)
+        i = inputs
+        kp, vp = i.k_pre, i.v_pre
+        pre_slots = self.pre_slots
+        if self.only is not None:
+            anc = _ancestors(w.ops)
+            need = set()
+            for pos in self.only:
+                need |= anc[w.decode_seqs[pos]]
+            keep = []
+            start = 0
+            for op in w.ops:
+                if op[0] == "prefill":
+                    if op[1] in need:
+                        keep.append(np.arange(start, start + op[2]))
+                    start += op[2]
+            idx = np.concatenate(keep) if keep else np.zeros(0, np.int64)
+            pre_slots = pre_slots[idx]
+            tidx = torch.from_numpy(idx).to(kp.device)
+            kp, vp = kp.index_select(0, tidx), vp.index_select(0, tidx)
+        common = dict(num_kv_heads=w.num_kv_heads, head_dim=w.head_dim, block_size=16,
+                      num_blocks=w.num_blocks, kv_dtype=w.kv_dtype, in_dtype=w.q_dtype,
+                      k_scale=i.k_scale, v_scale=i.v_scale)
+        oracle.cache_append(workloads.storage(kp), workloads.storage(vp), self.k_cache,
+                            self.v_cache, pre_slots, **common)
+        oracle.cache_append(workloads.storage(i.k_new), workloads.storage(i.v_new), self.k_cache,
+                            self.v_cache, self.step_slots, **common)
+        self.inputs = inputs
+
+    def decode(self, rows=None):
+        w, i = self.w, self.inputs
+        if rows is None and self.only is not None:
+            rows = [(b, h) for b in self.only for h in range(w.num_q_heads)]
+        return oracle.decode(workloads.storage(i.q), self.k_cache, self.v_cache, self.tables,
+                             self.lens, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+                             head_dim=w.head_dim, block_size=16, num_blocks=w.num_blocks,
+                             q_dtype=w.q_dtype, kv_dtype=w.kv_dtype, scale=w.scale,
+                             k_scale=i.k_scale, v_scale=i.v_scale, rows=rows)
+
+    def block_ids(self):
+        """Physical blocks the selected decode positions map."""
+        pos = range(self.w.num_seqs) if self.only is None else self.only
+        ids = set()
+        for b in pos:
+            n = -(-int(self.lens[b]) // 16)
+            ids.update(int(x) for x in self.tables[b][:n])
+        return sorted(ids)
+
+
+def to_f64(t):
+    return t.detach().float().cpu().double().numpy()
+
+
+def check_close(got, ref, kv_dtype, q_dtype):
+    """Asserts the tolerance for the dtype; returns the measured error."""
+    kind, tol = TOL["e4m3" if kv_dtype == "e4m3" else q_dtype]
+    assert got.shape == ref.shape
+    assert np.all(np.isfinite(got)), "non-finite output"
+    if kind == "rowrel":
+        g = got.reshape(-1, got.shape[-1])
+        r = ref.reshape(-1, ref.shape[-1])
+        err = float(np.max(np.max(np.abs(g - r), axis=1) / np.maximum(np.max(np.abs(r), axis=1),
+                                                                       1e-30)))
+    else:
+        err = float(np.max(np.abs(got - ref)))
+    assert err <= tol, f"max {kind} error {err:.3g} > {tol}"
+    return err
+
+
+def compare_cache_blocks(gpu_cache, host_cache, w, blocks):
+    """Byte-exact comparison of the given physical blocks."""
+    per_block = w.num_kv_heads * 16 * w.head_dim * EB[w.kv_dtype]
+    g = as_bytes(gpu_cache).reshape(w.num_blocks, per_block)
+    h = host_cache.view(np.uint8).reshape(w.num_blocks, per_block)
+    if blocks is None:
+        np.testing.assert_array_equal(g, h)
+    else:
+        idx = np.asarray(blocks)
+        np.testing.assert_array_equal(g[idx], h[idx])

@@ -1,0 +1,247 @@
+"""GPU parity: the library (through its C ABI) against the CPU oracle.
+
+Cache append is compared byte for byte, block tables bit for bit, decode
+outputs within the tolerance of their dtype:
+  fp32: max over rows of max|x - r| / max|r| <= 1e-5
+  fp16 / bf16: max |x - r| <= 1e-2 (fp32 accumulation, output rounded)
+  FP8 KV: max |x - r| <= 2e-2 against the oracle on the same stored bytes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_255_amd as pa
+import workloads
+from tests.scenario import (GpuStep, Inputs, OracleStep, check_close, compare_cache_blocks,
+                            to_f64)
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def run_and_check(w, layer=0, partition=None, kernel=pa.KERNEL_AUTO, only=None, rows=None):
+    say(f"[case] {w.name} cfg{w.config_id} layer={layer} partition={partition} kernel={kernel}")
+    inp = Inputs(w, layer)
+    g = GpuStep(w, layer, inp, partition=partition, kernel=kernel)
+    o = OracleStep(w, layer, inp, only=only)
+    np.testing.assert_array_equal(g.tables, o.tables)
+    np.testing.assert_array_equal(g.lens, o.lens)
+    np.testing.assert_array_equal(g.step_slots, o.step_slots)
+    g.append_prefill()
+    g.append_step()
+    torch.cuda.synchronize()
+    compare_cache_blocks(g.k_cache, o.k_cache, w, None if only is None else o.block_ids())
+    compare_cache_blocks(g.v_cache, o.v_cache, w, None if only is None else o.block_ids())
+    out = to_f64(g.decode())
+    torch.cuda.synchronize()
+    if rows is not None:
+        ref = o.decode(rows=rows)
+        got = np.stack([out[b, h] for (b, h) in rows])
+    elif only is not None:
+        ref = o.decode().reshape(len(only), w.num_q_heads, w.head_dim)
+        got = out[sorted(only)]
+    else:
+        ref = o.decode()
+        got = out
+    err = check_close(got, ref, w.kv_dtype, w.q_dtype)
+    say(f"[ok] {w.name} err={err:.3g}")
+    return g, out
+
+
+# -- small shapes: every config, every partition mode -------------------------
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("partition", [0, 64, 512])
+def test_parity_small(cid, partition):
+    w = workloads.config(cid, "full" if cid == 1 else "small")
+    for layer in range(w.num_layers):
+        run_and_check(w, layer, partition=partition, kernel=pa.KERNEL_VALU)
+
+
+def test_parity_config1_tiny_fp32():
+    """The tiny fp32 MHA step exactly as specified (lengths 17/33/64/100 plus
+    one appended token, 64-block permuted pool, single pass)."""
+    w = workloads.config(1)
+    run_and_check(w)
+
+
+# -- full sizes, in the launch configuration the benchmark times --------------
+def test_parity_config2_full():
+    w = workloads.config(2)
+    run_and_check(w)
+
+
+def test_parity_config4_full_sampled():
+    w = workloads.config(4)
+    rng = np.random.default_rng(4)
+    only = sorted(set(rng.choice(w.num_seqs, size=6, replace=False).tolist()) | {0, w.num_seqs - 1})
+    run_and_check(w, only=only)
+
+
+def test_parity_config5_full_sampled():
+    w = workloads.config(5)
+    rows = [(b, h) for b in (1, 3) for h in (0, 7, 8, 33, 63)]
+    run_and_check(w, only=[1, 3], rows=rows)
+
+
+def test_parity_config3_full_sampled_layers():
+    w = workloads.config(3)
+    for layer in (0, w.num_layers - 1):
+        rows = [(b, h) for b in (0, 5) for h in (0, 19, 39)]
+        run_and_check(w, layer, only=[0, 5], rows=rows)
+
+
+# -- exhaustive FP8 decode through the decode path ----------------------------
+@pytest.mark.parametrize("kernel", [pa.KERNEL_VALU])
+def test_fp8_value_decode_all_codes(kernel):
+    """Two one-token sequences whose V rows hold all 256 E4M3 codes: with one
+    token the softmax weight is exactly 1, so out = v_scale * V_0, which
+    bf16 holds exactly for every finite E4M3 value."""
+    say(f"[case] fp8 all codes kernel={kernel}")
+    D, NB = 128, 4
+    k = torch.zeros(NB * 16 * D, dtype=torch.uint8, device="cuda")
+    v = torch.zeros(NB * D * 16, dtype=torch.uint8, device="cuda")
+    vv = v.view(NB, 1, D, 16)
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    vv[2, 0, :, 0] = codes[:128].cuda()
+    vv[1, 0, :, 0] = codes[128:].cuda()
+    tables = torch.tensor([[2], [1]], dtype=torch.int32, device="cuda")
+    lens = torch.tensor([1, 1], dtype=torch.int32, device="cuda")
+    q = torch.randn(2, 1, D, device="cuda").to(torch.bfloat16)
+    out = torch.empty_like(q)
+    desc = pa.kv_desc(1, 1, D, NB, "bf16", "e4m3", kernel=kernel)
+    pa.pa_decode(q, k, v, tables, lens, 1, 0.1, out, desc, 1.0, 1.0)
+    torch.cuda.synchronize()
+    got = to_f64(out).reshape(256)
+    want = np.array([oracle.e4m3_to_double(c) for c in range(256)])
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    np.testing.assert_array_equal(got[ok], want[ok])
+
+
+def test_fp8_append_encoder_rounding():
+    """Append of bf16 values at every E4M3 rounding midpoint (and beyond the
+    saturation point), scale 1: byte-exact against the oracle's encoder."""
+    say("[case] fp8 append midpoints")
+    vals = np.array([oracle.e4m3_to_double(c) for c in range(0x7F)])
+    mids = (vals[:-1] + vals[1:]) / 2
+    x = np.concatenate([vals, mids, -mids, [448.0, 460.0, 464.0, 500.0, 1e4, -1e4, 0.0]])
+    xb = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16)
+    assert np.array_equal(xb.double().numpy(), x)  # all exactly representable in bf16
+    D = 128
+    T = -(-len(x) // D)
+    pad = torch.zeros(T * D, dtype=torch.bfloat16)
+    pad[:len(x)] = xb
+    kin = pad.reshape(T, 1, D).cuda()
+    vin = (-pad).reshape(T, 1, D).cuda()
+    NB = T
+    kc = torch.full((NB * 16 * D,), 0xFF, dtype=torch.uint8, device="cuda")
+    vc = torch.full((NB * 16 * D,), 0xFF, dtype=torch.uint8, device="cuda")
+    slots = torch.tensor([16 * i + 3 for i in range(T)], dtype=torch.int32, device="cuda")
+    desc = pa.kv_desc(1, 1, D, NB, "bf16", "e4m3")
+    pa.pa_cache_append(kin, vin, kc, vc, slots, desc, 1.0, 1.0)
+    torch.cuda.synchronize()
+    hk = np.full(NB * 16 * D, 0xFF, dtype=np.uint8)
+    hv = np.full(NB * 16 * D, 0xFF, dtype=np.uint8)
+    oracle.cache_append(workloads.storage(kin), workloads.storage(vin), hk, hv,
+                        slots.cpu().numpy(), num_kv_heads=1, head_dim=D, block_size=16,
+                        num_blocks=NB, kv_dtype="e4m3", in_dtype="bf16")
+    np.testing.assert_array_equal(kc.cpu().numpy(), hk)
+    np.testing.assert_array_equal(vc.cpu().numpy(), hv)
+
+
+# -- invariances on the GPU (bitwise) -------------------------------------------
+def test_block_placement_does_not_change_output_bits():
+    """Two pools with different shuffle seeds place the same logical blocks
+    differently; the outputs must be bit-identical."""
+    w = workloads.config(2, "small")
+    inp = Inputs(w)
+    outs, tables = [], []
+    for seed in (11, 12345):
+        w.shuffle_seeds = [seed]
+        g = GpuStep(w, 0, inp, partition=64, kernel=pa.KERNEL_VALU)
+        g.append_prefill()
+        g.append_step()
+        outs.append(g.decode().clone())
+        tables.append(g.tables.copy())
+    torch.cuda.synchronize()
+    assert not np.array_equal(tables[0], tables[1])  # the placements differ
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+
+
+def test_shared_prefix_equals_duplicated_prefix_bits():
+    """dev.to §5: sequences mapping the same prefix blocks give the same bits
+    as sequences holding private copies of that prefix."""
+    w = workloads.config(4, "small")
+    inp = Inputs(w)
+    g = GpuStep(w, 0, inp, partition=0, kernel=pa.KERNEL_VALU)
+    g.append_prefill()
+    g.append_step()
+    shared = g.decode().clone()
+    # private copies: every child gets its own prefix blocks holding the same data
+    P = w.ops[1][2]
+    ops = []
+    kp, vp = [], []
+    start = P
+    for c, op in enumerate([o for o in w.ops if o[0] == "prefill"][1:]):
+        ops += [("create",), ("prefill", c, P + op[2])]
+        kp += [inp.k_pre[:P], inp.k_pre[start:start + op[2]]]
+        vp += [inp.v_pre[:P], inp.v_pre[start:start + op[2]]]
+        start += op[2]
+    w2 = workloads.Workload(name="dup", config_id=4, num_q_heads=w.num_q_heads,
+                            num_kv_heads=w.num_kv_heads, head_dim=w.head_dim, q_dtype=w.q_dtype,
+                            kv_dtype=w.kv_dtype, num_blocks=w.num_blocks * 4, ops=ops,
+                            decode_seqs=list(range(w.num_seqs)), seed=w.seed,
+                            shuffle_seeds=[77])
+    inp2 = Inputs.__new__(Inputs)
+    inp2.k_pre, inp2.v_pre = torch.cat(kp), torch.cat(vp)
+    inp2.q, inp2.k_new, inp2.v_new = inp.q, inp.k_new, inp.v_new
+    inp2.k_scale, inp2.v_scale = inp.k_scale, inp.v_scale
+    g2 = GpuStep(w2, 0, inp2, partition=0, kernel=pa.KERNEL_VALU)
+    assert set(g2.tables[0][:P // 16]).isdisjoint(g2.tables[1][:P // 16])
+    g2.append_prefill()
+    g2.append_step()
+    dup = g2.decode().clone()
+    torch.cuda.synchronize()
+    assert torch.equal(shared.view(torch.int16), dup.view(torch.int16))
+
+
+def test_partitioned_matches_single_pass():
+    w = workloads.config(2, "small")
+    inp = Inputs(w)
+    outs = {}
+    for part in (0, 16, 128):
+        g = GpuStep(w, 0, inp, partition=part, kernel=pa.KERNEL_VALU)
+        g.append_prefill()
+        g.append_step()
+        outs[part] = to_f64(g.decode())
+    assert np.max(np.abs(outs[0] - outs[16])) < 1e-2
+    assert np.max(np.abs(outs[0] - outs[128])) < 1e-2
+
+
+def test_zero_length_sequence_gives_zero_row():
+    D, NB = 64, 3
+    k = torch.randn(NB * 16 * D, device="cuda")
+    v = torch.randn(NB * 16 * D, device="cuda")
+    tables = torch.tensor([[0, -1], [2, 1]], dtype=torch.int32, device="cuda")
+    lens = torch.tensor([0, 20], dtype=torch.int32, device="cuda")
+    q = torch.randn(2, 2, D, device="cuda")
+    for part in (0, 16):
+        desc = pa.kv_desc(2, 1, D, NB, "f32", "f32", kernel=pa.KERNEL_VALU)
+        ws = None
+        if part:
+            ws = torch.empty(pa.pa_decode_workspace_bytes(desc, 2, 32, part), dtype=torch.uint8,
+                             device="cuda")
+        out = torch.full_like(q, 7.0)
+        pa.pa_decode(q, k, v, tables, lens, 32, 0.125, out, desc, workspace=ws,
+                     partition_size=part)
+        torch.cuda.synchronize()
+        assert torch.all(out[0] == 0) and torch.all(torch.isfinite(out[1]))
+        ref = oracle.decode(workloads.storage(q), k.cpu().numpy(), v.cpu().numpy(),
+                            tables.cpu().numpy(), lens.cpu().numpy(), num_q_heads=2,
+                            num_kv_heads=1, head_dim=D, block_size=16, num_blocks=NB,
+                            q_dtype="f32", kv_dtype="f32", scale=0.125)
+        check_close(to_f64(out), ref, "f32", "f32")

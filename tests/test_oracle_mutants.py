@@ -41,7 +41,7 @@ MUTANTS = {
                            "if (a >= 464.0)\n        return sign | 0x7F;"),
     "f16_bias": ("mag = ldexp(1.0 + (double)m / 1024.0, e - 15);",
                  "mag = ldexp(1.0 + (double)m / 1024.0, e - 14);"),
-    "append_v_with_k_layout": ("store_elem(c, v_cache, v_index(", "store_elem(c, v_cache, k_index("),
+    "append_v_with_k_layout": ("store_elem(c, J->v_cache, v_index(", "store_elem(c, J->v_cache, k_index("),
     "bytes_per_token_no_factor_2": ("return (uint64_t)(2 * layers", "return (uint64_t)(1 * layers"),
 }
 

@@ -52,7 +52,7 @@ class Workload:
     num_layers: int = 1
     block_size: int = BLOCK_SIZE
     seed: int = 0
-    partition_size: int = -1   # launch configuration that bench.py times
+    partition_size: int = 256  # launch configuration that bench.py times
     shuffle_seeds: list = field(default_factory=list)  # one per layer
 
     @property
