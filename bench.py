@@ -1,0 +1,304 @@
+#!/usr/bin/env python3
+"""PagedAttention decode benchmark on one MI355X.
+
+Default workload: one decode step of a Llama-3-8B-shaped attention layer
+(32 query heads on 8 KV heads, head_dim 128, bf16, 16-token blocks) for a
+batch of 32 sequences with lengths uniform in [512, 4096], blocks scattered
+over a pool 1.25x the size they need (dev.to, "Why LLMs Run Out of VRAM...",
+§2 Example 2 and §4).
+
+A timed step is the whole hot path for the batch:
+  host:   pa_seq_append_slots_batch (one new slot per sequence, a new block
+          at every 16th token) and pa_export_block_tables into pinned memory,
+          then an async copy to the device;
+  device: pa_cache_append of the new token's K/V, then pa_decode (partials +
+          merge kernels, or one kernel in single-pass mode).
+Inputs are resident in HBM before timing starts.  The caches are rotated
+over R replicas (one per step, like the layers of a model) so that the
+working set exceeds the 256 MB Infinity Cache and reads come from HBM.
+
+Printed: one JSON line.  `value` is KV-read GB/s over whole steps
+(algorithmic bytes: every valid token's K and V row of each KV head once);
+`roofline` is for the decode kernel alone, timed with HIP events around each
+of its launches; `cpu_baseline` times the CPU oracle on a bounded sample.
+"""
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor peak
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--config", type=int, default=2, help="workload 2..5 (2 = headline)")
+    ap.add_argument("--partition", type=int, default=None,
+                    help="tokens per work item (0 = single pass, -1 = balanced)")
+    ap.add_argument("--kernel", choices=["auto", "valu", "mfma"], default="auto")
+    ap.add_argument("--replicas", type=int, default=None, help="cache replicas rotated per step")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode path "
+              "shards by sequence or KV head with no collective, see the design notes.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_255_amd as pa
+    import workloads
+    from paged_kv_cache_255_amd.plan import execute_plan
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    w = workloads.config(args.config)
+    partition = w.partition_size if args.partition is None else args.partition
+    kernel = {"auto": pa.KERNEL_AUTO, "valu": pa.KERNEL_VALU, "mfma": pa.KERNEL_MFMA}[args.kernel]
+    B, Hq, Hkv, D, L = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.num_layers
+    eb = {"f32": 4, "f16": 2, "bf16": 2, "e4m3": 1}[w.kv_dtype]
+    K, W = args.steps, args.warmup
+    total_steps = K + W
+
+    # pool with room for every token the steps append
+    grow_blocks = B * (math.ceil((total_steps + 1) / 16) + 1)
+    nblocks = w.num_blocks + grow_blocks
+    pool = pa.pa_block_pool_init(nblocks, Hkv, D, w.kv_dtype, shuffle_seed=w.shuffle_seeds[0])
+    ids, pre_slots = execute_plan(pool, w.ops)
+    dec = np.array([ids[s] for s in w.decode_seqs], dtype=np.int32)
+    lens0 = np.array(w.decode_lengths(), dtype=np.int64) - 1  # before the first step
+    max_len = int(lens0.max()) + total_steps
+    maxb = math.ceil(max_len / 16)
+
+    step_bytes_1 = Hkv * D * 2 * eb * L  # per token
+    per_replica = nblocks * Hkv * 16 * D * eb * 2 * L
+    R = args.replicas or max(1, math.ceil(1.2e9 / max(1, int(lens0.sum()) * step_bytes_1)))
+    log(f"[bench] {w.name}: B={B} Hq={Hq} Hkv={Hkv} D={D} layers={L} kv={w.kv_dtype} "
+        f"pool={nblocks} blocks, replicas={R} ({R * per_replica / 1e9:.2f} GB of cache), "
+        f"partition={partition} kernel={args.kernel}")
+
+    # caches: every replica and layer gets the same prefill through the append kernel
+    desc = pa.kv_desc(Hq, Hkv, D, nblocks, w.q_dtype, w.kv_dtype, kernel=kernel)
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
+           "e4m3": torch.uint8}[w.kv_dtype]
+    nelem = nblocks * Hkv * 16 * D
+    caches = []  # index layer * R + replica
+    d_pre = torch.from_numpy(pre_slots).to(dev)
+    ks = vs = 1.0
+    for layer in range(L):
+        k_pre, v_pre = workloads.prefill_tensors(w, layer, dev)
+        if w.kv_dtype == "e4m3" and layer == 0:
+            ks, vs = workloads.fp8_scale(k_pre), workloads.fp8_scale(v_pre)
+        kc = torch.zeros(nelem, dtype=tdt, device=dev)
+        vc = torch.zeros(nelem, dtype=tdt, device=dev)
+        pa.pa_cache_append(k_pre, v_pre, kc, vc, d_pre, desc, ks, vs)
+        caches.append((kc, vc))
+        for _ in range(1, R):
+            caches.append((kc.clone(), vc.clone()))
+        del k_pre, v_pre
+    torch.cuda.synchronize()
+    q, k_new, v_new = workloads.step_tensors(w, 0, dev)
+    out = torch.empty_like(q)
+    ws = None
+    ws_bytes = 0
+    if partition != 0:
+        ws_bytes = pa.pa_decode_workspace_bytes(desc, B, max_len, partition)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+    # host staging ring (pinned) and the device copy of per-step metadata
+    NBUF = 8
+    meta_words = B + B * maxb + B  # slots, tables, lens
+    staging = torch.empty((NBUF, meta_words), dtype=torch.int32, pin_memory=True)
+    staged = [torch.cuda.Event() for _ in range(NBUF)]
+    d_meta = torch.empty(meta_words, dtype=torch.int32, device=dev)
+    d_slots = d_meta[:B]
+    d_tables = d_meta[B:B + B * maxb].view(B, maxb)
+    d_lens = d_meta[B + B * maxb:]
+
+    lib = pa._lib
+    pool_h = pool.handle
+    dec_p = dec.ctypes.data
+    stream = torch.cuda.current_stream()
+    s_h = stream.cuda_stream
+    dref = ctypes.byref(desc)
+    kc_p = [(c[0].data_ptr(), c[1].data_ptr()) for c in caches]
+    qp, kn, vn, op = q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), out.data_ptr()
+    ws_p = ws.data_ptr() if ws is not None else None
+    scale = w.scale
+    stage_ptrs = [staging[i].data_ptr() for i in range(NBUF)]
+    slots_p, tables_p, lens_p = d_slots.data_ptr(), d_tables.data_ptr(), d_lens.data_ptr()
+
+    # HIP events around every launch of the decode kernel (one per layer and step)
+    ev_k = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(K * L)]
+
+    def step(i, timed):
+        buf = i % NBUF
+        if i >= NBUF:
+            staged[buf].synchronize()  # the copy that last read this buffer is done
+        sp = stage_ptrs[buf]
+        rc = lib.pa_seq_append_slots_batch(pool_h, dec_p, B, 1, sp)
+        rc |= lib.pa_export_block_tables(pool_h, dec_p, B, maxb, sp + 4 * B,
+                                         sp + 4 * (B + B * maxb))
+        if rc:
+            raise RuntimeError("host step failed: " + pa.pa_last_error())
+        d_meta.copy_(staging[buf], non_blocking=True)
+        staged[buf].record()
+        r = i % R
+        for layer in range(L):
+            kcp, vcp = kc_p[layer * R + r]
+            rc = lib.pa_cache_append(kn, vn, kcp, vcp, slots_p, B, dref, ks, vs, s_h)
+            ev = ev_k[(i - W) * L + layer] if timed else None
+            if ev:
+                ev[0].record()
+            if partition == 0:
+                rc |= lib.pa_decode(qp, kcp, vcp, tables_p, maxb, lens_p,
+                                    B, max_len, scale, ks, vs, op, None, 0, 0, dref, s_h)
+                if ev:
+                    ev[1].record()
+            else:
+                rc |= lib.pa_decode_partials(qp, kcp, vcp, tables_p, maxb,
+                                             lens_p, B, max_len, scale, ks, vs, ws_p,
+                                             ws_bytes, partition, dref, s_h)
+                if ev:
+                    ev[1].record()
+                rc |= lib.pa_decode_merge(lens_p, B, maxb, max_len, op, ws_p, ws_bytes,
+                                          partition, dref, s_h)
+            if rc:
+                raise RuntimeError("launch failed: " + pa.pa_last_error())
+
+    for i in range(W):
+        step(i, False)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(W, W + K):
+        step(i, True)
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t_start.elapsed_time(t_end)
+    ms_per_step = ms_total / K
+
+    # algorithmic KV bytes: step i decodes lens0 + i + 1 tokens per sequence
+    tokens = np.array([int((lens0 + i + 1).sum()) for i in range(W, W + K)], dtype=np.float64)
+    bytes_steps = tokens * step_bytes_1
+    gbs = bytes_steps.sum() / (ms_total * 1e-3) / 1e9
+    kern_ms = np.array([a.elapsed_time(b) for a, b in ev_k])  # per launch
+    kern_gbs = bytes_steps.sum() / (kern_ms.sum() * 1e-3) / 1e9
+    log(f"[bench] {K} steps: {ms_per_step * 1e3:.2f} us/step (wall {wall / K * 1e6:.2f} us), "
+        f"{gbs:.1f} GB/s over whole steps; decode kernel {kern_ms.mean() * 1e3:.2f} us/launch "
+        f"(p10 {np.percentile(kern_ms, 10) * 1e3:.2f}, p90 {np.percentile(kern_ms, 90) * 1e3:.2f}),"
+        f" {kern_gbs:.1f} GB/s = {kern_gbs / HBM_PEAK_GBS * 100:.1f}% of HBM peak")
+    final_tables = staging[(W + K - 1) % NBUF][B:B + B * maxb].numpy().reshape(B, maxb).copy()
+    final_lens = staging[(W + K - 1) % NBUF][B + B * maxb:].numpy().copy()
+    last_r = (W + K - 1) % R
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, caches[last_r][0], caches[last_r][1], q, final_tables,
+                           final_lens, nblocks, ks, vs, args.cpu_seconds)
+
+    kname = {0: "auto", 1: "valu", 2: "mfma"}[kernel]
+    if kernel == pa.KERNEL_AUTO:
+        kname = "auto(mfma)" if w.q_dtype in ("bf16", "f16") else "auto(valu)"
+    result = {
+        "metric": "achieved KV-read HBM GB/s (% of peak) + µs/decode step, "
+                  "Llama-3-8B GQA batch 32",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "steps_per_s": round(1e3 / ms_per_step, 1),
+        "pct_of_peak": round(gbs / HBM_PEAK_GBS * 100, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.kv_dtype if w.kv_dtype == w.q_dtype else f"{w.q_dtype}+{w.kv_dtype}",
+        "data": "synthetic (seeded N(0,1) K/V/q, seeded lengths and block placement)",
+        "config": {
+            "workload": f"{w.name}: decode step of {L} layer(s), {B} seqs, {Hq} q / {Hkv} kv "
+                        f"heads, head_dim {D}, block 16, lengths {int(lens0.min()) + 1}.."
+                        f"{int(lens0.max()) + 1} at the first timed step",
+            "global_batch": B,
+            "kv_tokens_first_step": int(tokens[0]),
+            "kv_bytes_per_step_avg": int(bytes_steps.mean()),
+            "partition": partition,
+            "kernel": kname,
+            "cache_replicas": R,
+            "parallelism": "none (1 GPU)",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(kern_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "decode_mfma_kernel" if "mfma" in kname else "decode_valu_kernel",
+            "kernel_us_avg": round(float(kern_ms.mean()) * 1e3, 2),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(w, k_cache, v_cache, q, tables, lens, nblocks, ks, vs, target_s):
+    """The CPU oracle (fp64 C, all host threads up to 16) on the first sequences
+    of the last timed step, sized to about `target_s` seconds."""
+    import oracle
+    import workloads
+    threads = min(16, len(os.sched_getaffinity(0)))
+    kh = workloads.storage(k_cache)
+    vh = workloads.storage(v_cache)
+    qh = workloads.storage(q)
+    eb = {"f32": 4, "f16": 2, "bf16": 2, "e4m3": 1}[w.kv_dtype]
+    args = dict(num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+                block_size=16, num_blocks=nblocks, q_dtype=w.q_dtype, kv_dtype=w.kv_dtype,
+                scale=w.scale, k_scale=ks, v_scale=vs, nthreads=threads)
+
+    def run(nseq):
+        rows = [(b, h) for b in range(nseq) for h in range(w.num_q_heads)]
+        t0 = time.perf_counter()
+        oracle.decode(qh, kh, vh, tables, lens, rows=rows, **args)
+        return time.perf_counter() - t0
+
+    t1 = run(1)
+    nseq = int(max(1, min(len(lens), target_s / max(t1, 1e-6))))
+    t = run(nseq)
+    nbytes = int(lens[:nseq].sum()) * w.num_kv_heads * w.head_dim * 2 * eb
+    return {"value": round(nbytes / t / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{nseq} of {len(lens)} sequences ({int(lens[:nseq].sum())} tokens, all "
+                      f"{w.num_q_heads} q heads) of the last timed step, fp64 C oracle, "
+                      f"{t:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

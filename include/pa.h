@@ -234,6 +234,24 @@ pa_status pa_decode(const void *q, const void *k_cache, const void *v_cache,
                     size_t workspace_bytes, int32_t partition_size, const pa_kv_desc *desc,
                     void *stream);
 
+/* The two launches of a partitioned pa_decode, callable one at a time (same
+ * arguments as pa_decode; partition_size must be > 0 and `workspace` as for
+ * pa_decode).  pa_decode_partials runs the per-partition kernel and leaves
+ * each partition's softmax state (running max, sum, unnormalised output) in
+ * the workspace; pa_decode_merge combines them into `out`.  Issued in this
+ * order on one stream they compute exactly what pa_decode computes; a caller
+ * may time or schedule the two separately. */
+pa_status pa_decode_partials(const void *q, const void *k_cache, const void *v_cache,
+                             const int32_t *block_tables, int32_t max_blocks_per_seq,
+                             const int32_t *seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                             float scale, float k_scale, float v_scale, void *workspace,
+                             size_t workspace_bytes, int32_t partition_size,
+                             const pa_kv_desc *desc, void *stream);
+pa_status pa_decode_merge(const int32_t *seq_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
+                          int32_t max_seq_len, void *out, const void *workspace,
+                          size_t workspace_bytes, int32_t partition_size, const pa_kv_desc *desc,
+                          void *stream);
+
 /* Message describing the last failure on this thread ("" if none). */
 const char *pa_last_error(void);
 

@@ -4,7 +4,7 @@ Argument marshalling only: every function forwards to the C entry point of
 the same name in libpa.so (declared in include/pa.h), passing tensor data
 pointers, sizes and the current HIP stream.  All computation happens in the
 library's HIP kernels and host allocator.  Importing this package fails if
-libpa.so has not been built (python -m paged_kv_cache_255_amd.build).
+libpa.so has not been built (python paged_kv_cache_255_amd/build.py).
 """
 import ctypes
 import os
@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libpa.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with "
-                      "`python -m paged_kv_cache_255_amd.build`")
+                      "`python paged_kv_cache_255_amd/build.py`")
 _lib = ctypes.CDLL(LIB_PATH)
 
 # pa_status
@@ -84,6 +84,11 @@ _SIGS = {
     "pa_decode": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _I32, _I32, ctypes.c_float,
                                  ctypes.c_float, ctypes.c_float, _P, _P, ctypes.c_size_t, _I32,
                                  ctypes.POINTER(KvDesc), _P]),
+    "pa_decode_partials": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _I32, _I32, ctypes.c_float,
+                                          ctypes.c_float, ctypes.c_float, _P, ctypes.c_size_t,
+                                          _I32, ctypes.POINTER(KvDesc), _P]),
+    "pa_decode_merge": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _P, ctypes.c_size_t, _I32,
+                                       ctypes.POINTER(KvDesc), _P]),
     "pa_last_error": (ctypes.c_char_p, []),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -275,6 +280,28 @@ def pa_decode(q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale, o
                           block_tables.shape[1], _addr(seq_lens), B, max_seq_len, scale,
                           k_scale, v_scale, _addr(out), _addr(workspace), ws_bytes,
                           partition_size, ctypes.byref(desc), _stream(stream)), "pa_decode")
+
+
+def pa_decode_partials(q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale, desc,
+                       workspace, partition_size, k_scale=1.0, v_scale=1.0, stream=None):
+    B = seq_lens.numel()
+    _check_tensor(workspace, "workspace")
+    _check(_lib.pa_decode_partials(_addr(q), _addr(k_cache), _addr(v_cache), _addr(block_tables),
+                                   block_tables.shape[1], _addr(seq_lens), B, max_seq_len, scale,
+                                   k_scale, v_scale, _addr(workspace),
+                                   workspace.numel() * workspace.element_size(), partition_size,
+                                   ctypes.byref(desc), _stream(stream)), "pa_decode_partials")
+
+
+def pa_decode_merge(seq_lens, max_blocks_per_seq, max_seq_len, out, desc, workspace,
+                    partition_size, stream=None):
+    B = seq_lens.numel()
+    _check_tensor(workspace, "workspace")
+    _check_tensor(out, "out")
+    _check(_lib.pa_decode_merge(_addr(seq_lens), B, max_blocks_per_seq, max_seq_len, _addr(out),
+                                _addr(workspace), workspace.numel() * workspace.element_size(),
+                                partition_size, ctypes.byref(desc), _stream(stream)),
+           "pa_decode_merge")
 
 
 def pa_last_error():

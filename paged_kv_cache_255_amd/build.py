@@ -1,6 +1,8 @@
 """Builds libpa.so (HIP kernels for gfx950 plus the host block pool) in place.
 
-    python -m paged_kv_cache_255_amd.build
+    python paged_kv_cache_255_amd/build.py
+
+(run as a script: importing the package needs the library this builds).
 
 hipcc compiles the device sources for gfx950 only; the host-only sources are
 compiled as plain C++.  Objects go to _build/ at the repository root, the
@@ -19,7 +21,7 @@ OBJDIR = os.path.join(ROOT, "_build", "libpa")
 LIB = os.path.join(HERE, "libpa.so")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["append.hip", "decode_valu.hip", "merge.hip"]
+HIP_SOURCES = ["append.hip", "decode_valu.hip", "decode_mfma.hip", "merge.hip"]
 HOST_HIP_API = ["api.cpp"]           # host code that calls the HIP runtime
 HOST_ONLY = ["pool.cpp", "errors.cpp"]
 

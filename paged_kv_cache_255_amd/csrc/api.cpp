@@ -15,6 +15,9 @@ namespace pa {
 hipError_t launch_decode_valu(const DecodeArgs &a, pa_dtype qt, pa_dtype kt, int D,
                               int32_t num_items, hipStream_t s);
 bool valu_supports(pa_dtype qt, pa_dtype kt, int D, int G);
+hipError_t launch_decode_mfma(const DecodeArgs &a, pa_dtype qt, pa_dtype kt, int D,
+                              int32_t num_items, hipStream_t s);
+bool mfma_supports(pa_dtype qt, pa_dtype kt, int D, int G);
 hipError_t launch_merge(const DecodeArgs &a, pa_dtype qt, int D, hipStream_t s);
 hipError_t launch_append(const void *k, const void *v, void *kc, void *vc, const int32_t *slots,
                          int32_t T, int32_t H, int32_t NB, int D, pa_dtype qt, pa_dtype kt,
@@ -116,12 +119,18 @@ size_t pa_decode_workspace_bytes(const pa_kv_desc *desc, int32_t num_seqs, int32
     return (size_t)(W * G * (2 + desc->head_dim) * (int64_t)sizeof(float));
 }
 
-pa_status pa_decode(const void *q, const void *k_cache, const void *v_cache,
-                    const int32_t *block_tables, int32_t max_blocks_per_seq,
-                    const int32_t *seq_lens, int32_t num_seqs, int32_t max_seq_len, float scale,
-                    float k_scale, float v_scale, void *out, void *workspace,
-                    size_t workspace_bytes, int32_t partition_size, const pa_kv_desc *desc,
-                    void *stream)
+} // extern "C"
+
+namespace {
+
+enum Phase { kAll, kPartials, kMerge };
+
+pa_status decode_impl(Phase phase, const void *q, const void *k_cache, const void *v_cache,
+                      const int32_t *block_tables, int32_t max_blocks_per_seq,
+                      const int32_t *seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                      float scale, float k_scale, float v_scale, void *out, void *workspace,
+                      size_t workspace_bytes, int32_t partition_size, const pa_kv_desc *desc,
+                      void *stream)
 {
     pa_status st = check_desc(desc);
     if (st != PA_OK)
@@ -130,16 +139,22 @@ pa_status pa_decode(const void *q, const void *k_cache, const void *v_cache,
         return fail(PA_ERR_INVALID_ARG, "negative size");
     if (num_seqs == 0)
         return PA_OK;
-    if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !out)
+    if (!seq_lens || (phase != kPartials && !out))
         return fail(PA_ERR_INVALID_ARG, "null pointer");
-    if (q == out)
-        return fail(PA_ERR_INVALID_ARG, "out may not alias q");
-    if (!(scale > 0.f) || !(k_scale > 0.f) || !(v_scale > 0.f))
-        return fail(PA_ERR_INVALID_ARG, "scales must be positive");
+    if (phase != kMerge) {
+        if (!q || !k_cache || !v_cache || !block_tables)
+            return fail(PA_ERR_INVALID_ARG, "null pointer");
+        if (q == out)
+            return fail(PA_ERR_INVALID_ARG, "out may not alias q");
+        if (!(scale > 0.f) || !(k_scale > 0.f) || !(v_scale > 0.f))
+            return fail(PA_ERR_INVALID_ARG, "scales must be positive");
+    }
     if (partition_size == PA_PARTITION_BALANCED)
         return fail(PA_ERR_UNSUPPORTED, "balanced partitioning is not built yet");
     if (partition_size < 0 || partition_size % kBlockSize != 0)
         return fail(PA_ERR_INVALID_ARG, "partition_size must be 0 or a positive multiple of 16");
+    if (phase != kAll && partition_size == 0)
+        return fail(PA_ERR_INVALID_ARG, "partials/merge need partition_size > 0");
     if ((int64_t)max_blocks_per_seq * kBlockSize < (int64_t)max_seq_len)
         return fail(PA_ERR_INVALID_ARG, "max_seq_len exceeds max_blocks_per_seq * block_size");
 
@@ -175,26 +190,72 @@ pa_status pa_decode(const void *q, const void *k_cache, const void *v_cache,
         return fail(PA_ERR_INVALID_ARG, "too many work items");
     const int32_t items = (int32_t)items64;
 
-    int kernel = desc->kernel;
-    if (kernel == PA_KERNEL_AUTO)
-        kernel = PA_KERNEL_VALU;
-    if (kernel == PA_KERNEL_MFMA)
-        return fail(PA_ERR_UNSUPPORTED, "MFMA kernel is not built yet");
-    if (kernel != PA_KERNEL_VALU)
-        return fail(PA_ERR_INVALID_ARG, "unknown kernel choice");
-    if (!valu_supports(desc->q_dtype, desc->kv_dtype, D, G))
-        return fail(PA_ERR_UNSUPPORTED, "VALU kernel: unsupported (dtype, head_dim, group)");
-
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = launch_decode_valu(a, desc->q_dtype, desc->kv_dtype, D, items, s);
-    if (e != hipSuccess)
-        return hip_fail(e, "decode launch");
-    if (partition_size > 0) {
+    hipError_t e;
+    if (phase != kMerge) {
+        int kernel = desc->kernel;
+        if (kernel == PA_KERNEL_AUTO)
+            kernel = mfma_supports(desc->q_dtype, desc->kv_dtype, D, G) ? PA_KERNEL_MFMA
+                                                                          : PA_KERNEL_VALU;
+        if (kernel == PA_KERNEL_MFMA) {
+            if (!mfma_supports(desc->q_dtype, desc->kv_dtype, D, G))
+                return fail(PA_ERR_UNSUPPORTED, "MFMA kernel: needs 16-bit q and a group of <= 16");
+            e = launch_decode_mfma(a, desc->q_dtype, desc->kv_dtype, D, items, s);
+        } else if (kernel == PA_KERNEL_VALU) {
+            if (!valu_supports(desc->q_dtype, desc->kv_dtype, D, G))
+                return fail(PA_ERR_UNSUPPORTED,
+                            "VALU kernel: unsupported (dtype, head_dim, group)");
+            e = launch_decode_valu(a, desc->q_dtype, desc->kv_dtype, D, items, s);
+        } else {
+            return fail(PA_ERR_INVALID_ARG, "unknown kernel choice");
+        }
+        if (e != hipSuccess)
+            return hip_fail(e, "decode launch");
+    }
+    if (phase != kPartials && partition_size > 0) {
         e = launch_merge(a, desc->q_dtype, D, s);
         if (e != hipSuccess)
             return hip_fail(e, "merge launch");
     }
     return PA_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+pa_status pa_decode(const void *q, const void *k_cache, const void *v_cache,
+                    const int32_t *block_tables, int32_t max_blocks_per_seq,
+                    const int32_t *seq_lens, int32_t num_seqs, int32_t max_seq_len, float scale,
+                    float k_scale, float v_scale, void *out, void *workspace,
+                    size_t workspace_bytes, int32_t partition_size, const pa_kv_desc *desc,
+                    void *stream)
+{
+    return decode_impl(kAll, q, k_cache, v_cache, block_tables, max_blocks_per_seq, seq_lens,
+                       num_seqs, max_seq_len, scale, k_scale, v_scale, out, workspace,
+                       workspace_bytes, partition_size, desc, stream);
+}
+
+pa_status pa_decode_partials(const void *q, const void *k_cache, const void *v_cache,
+                             const int32_t *block_tables, int32_t max_blocks_per_seq,
+                             const int32_t *seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                             float scale, float k_scale, float v_scale, void *workspace,
+                             size_t workspace_bytes, int32_t partition_size,
+                             const pa_kv_desc *desc, void *stream)
+{
+    return decode_impl(kPartials, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                       seq_lens, num_seqs, max_seq_len, scale, k_scale, v_scale, nullptr,
+                       workspace, workspace_bytes, partition_size, desc, stream);
+}
+
+pa_status pa_decode_merge(const int32_t *seq_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
+                          int32_t max_seq_len, void *out, const void *workspace,
+                          size_t workspace_bytes, int32_t partition_size, const pa_kv_desc *desc,
+                          void *stream)
+{
+    return decode_impl(kMerge, nullptr, nullptr, nullptr, nullptr, max_blocks_per_seq, seq_lens,
+                       num_seqs, max_seq_len, 1.f, 1.f, 1.f, out, const_cast<void *>(workspace),
+                       workspace_bytes, partition_size, desc, stream);
 }
 
 } // extern "C"
