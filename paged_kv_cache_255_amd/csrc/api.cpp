@@ -4,7 +4,10 @@
 
 #include <cstdio>
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <string>
+#include <tuple>
 
 #include "pa.h"
 #include "pa_internal.hpp"
@@ -18,6 +21,7 @@ bool valu_supports(pa_dtype qt, pa_dtype kt, int D, int G);
 hipError_t launch_decode_mfma(const DecodeArgs &a, pa_dtype qt, pa_dtype kt, int D,
                               int32_t num_items, hipStream_t s);
 bool mfma_supports(pa_dtype qt, pa_dtype kt, int D, int G);
+int mfma_waves_per_cu(pa_dtype qt, pa_dtype kt, int D);
 hipError_t launch_merge(const DecodeArgs &a, pa_dtype qt, int D, hipStream_t s);
 hipError_t launch_append(const void *k, const void *v, void *kc, void *vc, const int32_t *slots,
                          int32_t T, int32_t H, int32_t NB, int D, pa_dtype qt, pa_dtype kt,
@@ -61,6 +65,29 @@ pa_status check_desc(const pa_kv_desc *d)
     if ((int64_t)d->num_blocks * d->num_kv_heads * kBlockSize * d->head_dim > (int64_t)1 << 40)
         return fail(PA_ERR_INVALID_ARG, "cache too large");
     return PA_OK;
+}
+
+// Waves the balanced split uses on the current device: all the waves of the
+// balanced kernel that the GPU holds at once (CUs x resident waves per CU),
+// so every run starts at launch and they finish together.  0 if unknown.
+int32_t balanced_waves(const pa_kv_desc *d)
+{
+    static std::mutex mu;
+    static std::map<std::tuple<int, int, int, int>, int32_t> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return 0;
+    const auto key = std::make_tuple(dev, (int)d->q_dtype, (int)d->kv_dtype, d->head_dim);
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(key);
+    if (it != cache.end())
+        return it->second;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    const int32_t w = cus * mfma_waves_per_cu(d->q_dtype, d->kv_dtype, d->head_dim);
+    cache[key] = w;
+    return w;
 }
 
 int32_t parts_for(int32_t max_seq_len, int32_t partition)
@@ -111,12 +138,17 @@ pa_status pa_cache_append(const void *k, const void *v, void *k_cache, void *v_c
 size_t pa_decode_workspace_bytes(const pa_kv_desc *desc, int32_t num_seqs, int32_t max_seq_len,
                                  int32_t partition_size)
 {
-    if (!desc || num_seqs <= 0 || max_seq_len < 0 || partition_size <= 0 ||
-        desc->num_kv_heads <= 0 || desc->num_q_heads <= 0 || desc->head_dim <= 0)
+    if (!desc || num_seqs <= 0 || max_seq_len < 0 || partition_size == 0 ||
+        partition_size < PA_PARTITION_BALANCED || desc->num_kv_heads <= 0 ||
+        desc->num_q_heads <= 0 || desc->head_dim <= 0)
         return 0;
     const int64_t G = desc->num_q_heads / desc->num_kv_heads;
-    const int64_t W = (int64_t)num_seqs * desc->num_kv_heads * parts_for(max_seq_len, partition_size);
-    return (size_t)(W * G * (2 + desc->head_dim) * (int64_t)sizeof(float));
+    int64_t slots;
+    if (partition_size == PA_PARTITION_BALANCED)
+        slots = (int64_t)balanced_waves(desc) + (int64_t)num_seqs * desc->num_kv_heads;
+    else
+        slots = (int64_t)num_seqs * desc->num_kv_heads * parts_for(max_seq_len, partition_size);
+    return (size_t)(slots * G * (2 + desc->head_dim) * (int64_t)sizeof(float));
 }
 
 } // extern "C"
@@ -149,12 +181,12 @@ pa_status decode_impl(Phase phase, const void *q, const void *k_cache, const voi
         if (!(scale > 0.f) || !(k_scale > 0.f) || !(v_scale > 0.f))
             return fail(PA_ERR_INVALID_ARG, "scales must be positive");
     }
-    if (partition_size == PA_PARTITION_BALANCED)
-        return fail(PA_ERR_UNSUPPORTED, "balanced partitioning is not built yet");
-    if (partition_size < 0 || partition_size % kBlockSize != 0)
-        return fail(PA_ERR_INVALID_ARG, "partition_size must be 0 or a positive multiple of 16");
+    const bool balanced = partition_size == PA_PARTITION_BALANCED;
+    if (!balanced && (partition_size < 0 || partition_size % kBlockSize != 0))
+        return fail(PA_ERR_INVALID_ARG,
+                    "partition_size must be 0, PA_PARTITION_BALANCED or a positive multiple of 16");
     if (phase != kAll && partition_size == 0)
-        return fail(PA_ERR_INVALID_ARG, "partials/merge need partition_size > 0");
+        return fail(PA_ERR_INVALID_ARG, "partials/merge need a partitioned mode");
     if ((int64_t)max_blocks_per_seq * kBlockSize < (int64_t)max_seq_len)
         return fail(PA_ERR_INVALID_ARG, "max_seq_len exceeds max_blocks_per_seq * block_size");
 
@@ -176,27 +208,40 @@ pa_status decode_impl(Phase phase, const void *q, const void *k_cache, const voi
     a.max_blocks_per_seq = max_blocks_per_seq;
     a.max_seq_len = max_seq_len;
     a.partition = partition_size;
-    a.max_parts = parts_for(max_seq_len, partition_size);
+    a.max_parts = balanced ? 1 : parts_for(max_seq_len, partition_size);
     a.score_scale = scale * k_scale * kLog2e;
     a.v_scale = v_scale;
 
-    if (partition_size > 0) {
-        const size_t need = pa_decode_workspace_bytes(desc, num_seqs, max_seq_len, partition_size);
-        if (!workspace || workspace_bytes < need)
-            return fail(PA_ERR_CAPACITY, "workspace smaller than pa_decode_workspace_bytes()");
+    int kernel = desc->kernel;
+    if (kernel == PA_KERNEL_AUTO)
+        kernel = mfma_supports(desc->q_dtype, desc->kv_dtype, D, G) ? PA_KERNEL_MFMA
+                                                                      : PA_KERNEL_VALU;
+    int64_t items64;
+    if (balanced) {
+        if (kernel != PA_KERNEL_MFMA)
+            return fail(PA_ERR_UNSUPPORTED, "balanced partitioning needs the MFMA kernel");
+        a.waves = balanced_waves(desc);
+        if (a.waves <= 0)
+            return fail(PA_ERR_HIP, "could not query the device for the balanced split");
+        items64 = a.waves;
+        a.num_slots = (int64_t)a.waves + (int64_t)num_seqs * desc->num_kv_heads;
+    } else {
+        items64 = (int64_t)num_seqs * desc->num_kv_heads * a.max_parts;
+        a.waves = 0;
+        a.num_slots = items64;
     }
-    const int64_t items64 = (int64_t)num_seqs * desc->num_kv_heads * a.max_parts;
     if (items64 > (int64_t)1 << 30)
         return fail(PA_ERR_INVALID_ARG, "too many work items");
     const int32_t items = (int32_t)items64;
+    if (partition_size != 0) {
+        const size_t need = pa_decode_workspace_bytes(desc, num_seqs, max_seq_len, partition_size);
+        if (!workspace || need == 0 || workspace_bytes < need)
+            return fail(PA_ERR_CAPACITY, "workspace smaller than pa_decode_workspace_bytes()");
+    }
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (phase != kMerge) {
-        int kernel = desc->kernel;
-        if (kernel == PA_KERNEL_AUTO)
-            kernel = mfma_supports(desc->q_dtype, desc->kv_dtype, D, G) ? PA_KERNEL_MFMA
-                                                                          : PA_KERNEL_VALU;
         if (kernel == PA_KERNEL_MFMA) {
             if (!mfma_supports(desc->q_dtype, desc->kv_dtype, D, G))
                 return fail(PA_ERR_UNSUPPORTED, "MFMA kernel: needs 16-bit q and a group of <= 16");
@@ -212,7 +257,7 @@ pa_status decode_impl(Phase phase, const void *q, const void *k_cache, const voi
         if (e != hipSuccess)
             return hip_fail(e, "decode launch");
     }
-    if (phase != kPartials && partition_size > 0) {
+    if (phase != kPartials && partition_size != 0) {
         e = launch_merge(a, desc->q_dtype, D, s);
         if (e != hipSuccess)
             return hip_fail(e, "merge launch");

@@ -6,17 +6,30 @@
 // (the query walks its block table and reads K/V from scattered physical
 // blocks); §2 "Example 2" (query heads of a group share one KV head).
 //
-// One wave per work item (sequence, KV head, token range).  The G query heads
-// of the KV head sit in the 16 columns of the MFMA tiles (G <= 16; unused
-// columns carry q = 0 and are discarded), so each K and V tile is read from
-// HBM once for the whole group.  Per 16-token block:
+// A wave processes a run of 16-token blocks of one (sequence, KV head).  The
+// G query heads of the KV head sit in the 16 columns of the MFMA tiles
+// (G <= 16; unused columns carry q = 0 and are discarded), so each K and V
+// tile is read from HBM once for the whole group.  Per block:
 //   S^T[16 tokens][16 heads] = K_tile[16][D] * Q^T[D][16]     (D/32 MFMA 16x16x32)
 //   online softmax on S^T, 4 tokens x 1 head per lane
 //   O^T[D][16 heads] += V^T_tile[D][16] * P^T[16][16 heads]   (D/16 MFMA 16x16x16)
-// The MFMA output layout of S^T (lane l: tokens 4*(l/16)+r, head l%16) is the
+// The output layout of S^T (lane l: tokens 4*(l/16)+r, head l%16) is the
 // B-operand layout of the second product, so P never leaves the registers.
 // FP8 tiles are widened to the q type with the hardware converter (exact:
 // every E4M3 value is a bf16 and an fp16 value).
+//
+// The next block's K/V loads are issued before the current block's math, and
+// the block-table entries of a run are read with one vector load, so a wave
+// keeps two tiles of HBM reads in flight.
+//
+// Work split (DecodeArgs::partition):
+//   0   one wave per (sequence, KV head), output written directly;
+//   > 0 one wave per (sequence, KV head, partition of that many tokens),
+//       partial states merged by merge.hip;
+//   balanced: the tiles of all (sequence, KV head) pairs, in order, are cut
+//       into W equal runs, one per wave (W = the waves the GPU holds at
+//       once); a run that covers a whole segment writes the output, the
+//       others leave partial states that merge.hip combines.
 #include "device.hpp"
 #include "work.hpp"
 
@@ -73,120 +86,95 @@ template <> struct Mma<PA_F16> {
     }
 };
 
-// Static shape of one kernel instance.
+// One wave's state and per-block work for one (sequence, KV head).
 template <int QT, int KT, int D>
-struct MfmaShape {
-    static constexpr int KE = Store<KT>::bytes;              // 2 or 1
-    static constexpr int ROW_BYTES = D * KE;                  // one K row
-    static constexpr int CHUNKS = ROW_BYTES / 16;             // 16-byte chunks per K row
-    static constexpr int CH_PER_LANE = CHUNKS / 4;            // chunks per lane per tile
-    static constexpr int QK_MMAS = D / 32;
-    static constexpr int PV_TILES = D / 16;
-    static constexpr int V_ROW_BYTES = kBlockSize * KE;       // one V^T row (16 tokens)
-    static constexpr int TILE_BYTES = kBlockSize * D * KE;
-    static_assert(CHUNKS % 4 == 0, "row must split into 4 lane groups");
-};
-
-template <int QT, int KT, int D>
-__global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a, int32_t num_items)
-{
-    using S = MfmaShape<QT, KT, D>;
+struct MfmaWave {
     using M = Mma<QT>;
     using TQ = typename Store<QT>::T;
     using A8 = typename M::A8;
     using A4 = typename M::A4;
+    static constexpr int KE = Store<KT>::bytes;        // 2 or 1
+    static constexpr int ROW_BYTES = D * KE;            // one K row
+    static constexpr int CHUNKS = ROW_BYTES / 16;       // 16-byte chunks per K row
+    static constexpr int CH_PER_LANE = CHUNKS / 4;      // chunks per lane per tile
+    static constexpr int QK_MMAS = D / 32;
+    static constexpr int PV_TILES = D / 16;
+    static constexpr int V_ROW_BYTES = kBlockSize * KE; // one V^T row (16 tokens)
+    static constexpr int TILE_BYTES = kBlockSize * D * KE;
+    static_assert(CHUNKS % 4 == 0, "row must split into 4 lane groups");
 
-    const int lane = threadIdx.x & 63;
-    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int32_t w = blockIdx.x * 4 + wid;
-    if (w >= num_items)
-        return;
-    const Item it = item_of(a, w);
-    if (it.valid_len && it.n > 0 && it.t0 >= it.t1)
-        return;
-    if (it.valid_len && it.n == 0 && it.p > 0)
-        return;
+    struct Tile {
+        u32x4 k[CH_PER_LANE];
+        uint32_t v[PV_TILES][KE];
+    };
 
-    const int col = lane & 15; // MFMA column: query head within the group
-    const int grp = lane >> 4; // lane group: 4 tokens of S^T, 4 dims of O^T
-    const int G = a.group;
+    int col; // MFMA column: query head within the group
+    int grp; // lane group: 4 tokens of S^T, 4 dims of O^T
+    A8 qop[QK_MMAS];
+    f32x4 acc[PV_TILES];
+    float m_run; // running max of head `col` (log2 units)
+    float l_run; // this lane's share of the running sum
 
-    // q of head `col` as the B operand of the D/32 QK products; chunk
-    // mapping identical to the K operand below.
-    A8 qop[S::QK_MMAS];
+    __device__ MfmaWave(int lane) : col(lane & 15), grp(lane >> 4) {}
+
+    // q of head `col` as the B operand of the QK products; the dim mapping
+    // matches the K operand loaded by load_tile.
+    __device__ void start(const DecodeArgs &a, int32_t b, int32_t g)
     {
         const TQ *qp = static_cast<const TQ *>(a.q) +
-                       ((size_t)it.b * a.num_q_heads + (size_t)it.g * G + col) * D;
+                       ((size_t)b * a.num_q_heads + (size_t)g * a.group + col) * D;
+        const bool real = col < a.group;
 #pragma unroll
-        for (int m = 0; m < S::QK_MMAS; ++m) {
+        for (int m = 0; m < QK_MMAS; ++m) {
             int d0;
-            if constexpr (S::KE == 2)
+            if constexpr (KE == 2)
                 d0 = (grp + 4 * m) * 8;
             else
                 d0 = (grp + 4 * (m / 2)) * 16 + 8 * (m % 2);
-            A8 v;
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (real)
+                v = load16(qp + d0); // 8 consecutive q values, 16-byte aligned
+            qop[m] = __builtin_bit_cast(A8, v);
+        }
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                v[i] = col < G ? qp[d0 + i] : (TQ)0.f;
-            qop[m] = v;
+        for (int t = 0; t < PV_TILES; ++t)
+            acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m_run = -INFINITY;
+        l_run = 0.f;
+    }
+
+    // K: token `col`, chunks grp, grp+4, ... (64 contiguous bytes of every row
+    // per load instruction).  V^T: dims 16t + col, tokens 4*grp .. 4*grp+3
+    // (512 contiguous bytes per load instruction).
+    __device__ static void load_tile(const char *kt, const char *vt, int col, int grp, Tile &T)
+    {
+#pragma unroll
+        for (int j = 0; j < CH_PER_LANE; ++j)
+            T.k[j] = load16(kt + col * ROW_BYTES + (grp + 4 * j) * 16);
+#pragma unroll
+        for (int t = 0; t < PV_TILES; ++t) {
+            const char *p = vt + (16 * t + col) * V_ROW_BYTES + grp * 4 * KE;
+            if constexpr (KE == 2) {
+                const u32x2 x = *reinterpret_cast<const u32x2 *>(p);
+                T.v[t][0] = x.x;
+                T.v[t][1] = x.y;
+            } else {
+                T.v[t][0] = *reinterpret_cast<const uint32_t *>(p);
+            }
         }
     }
 
-    f32x4 acc[S::PV_TILES];
-#pragma unroll
-    for (int t = 0; t < S::PV_TILES; ++t)
-        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY; // running max of head `col` (log2 units)
-    float l_run = 0.f;       // this lane's share of the running sum
-
-    bool bad = !it.valid_len;
-    const int32_t *table = a.block_tables + (size_t)it.b * a.max_blocks_per_seq;
-    const char *kbase = static_cast<const char *>(a.k_cache);
-    const char *vbase = static_cast<const char *>(a.v_cache);
-    const int32_t jb0 = it.t0 / kBlockSize;
-    const int32_t jb1 = bad ? jb0 : (it.t1 + kBlockSize - 1) / kBlockSize;
-    const float sc = a.score_scale;
-
-    for (int32_t jb = jb0; jb < jb1; ++jb) {
-        const int32_t phys = __builtin_amdgcn_readfirstlane(table[jb]);
-        if (phys < 0 || phys >= a.num_blocks) {
-            bad = true;
-            break;
-        }
-        const size_t tile = ((size_t)phys * a.num_kv_heads + it.g) * S::TILE_BYTES;
-        const int32_t tok_base = jb * kBlockSize;
-        const int32_t valid = it.t1 - tok_base; // tokens of this block in range (>= 1)
-
-        // K: token `col`, chunks grp, grp+4, ... (64 contiguous bytes of every
-        // row per load instruction)
-        u32x4 kr[S::CH_PER_LANE];
-#pragma unroll
-        for (int j = 0; j < S::CH_PER_LANE; ++j)
-            kr[j] = load16(kbase + tile + col * S::ROW_BYTES + (grp + 4 * j) * 16);
-        // V^T: dims 16t + col, tokens 4*grp .. 4*grp+3 (512 contiguous bytes
-        // per load instruction)
-        uint32_t vr[S::PV_TILES][S::KE];
-#pragma unroll
-        for (int t = 0; t < S::PV_TILES; ++t) {
-            const char *p = vbase + tile + (16 * t + col) * S::V_ROW_BYTES + grp * 4 * S::KE;
-            if constexpr (S::KE == 2) {
-                const u32x2 x = *reinterpret_cast<const u32x2 *>(p);
-                vr[t][0] = x.x;
-                vr[t][1] = x.y;
-            } else {
-                vr[t][0] = *reinterpret_cast<const uint32_t *>(p);
-            }
-        }
-
-        // S^T = K * Q^T
+    // One block: `valid` tokens of it (1..16) belong to the range.
+    __device__ void compute(const Tile &T, int valid, float sc)
+    {
         f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int m = 0; m < S::QK_MMAS; ++m) {
+        for (int m = 0; m < QK_MMAS; ++m) {
             A8 kop;
-            if constexpr (S::KE == 2) {
-                kop = __builtin_bit_cast(A8, kr[m]);
+            if constexpr (KE == 2) {
+                kop = __builtin_bit_cast(A8, T.k[m]);
             } else {
-                const u32x4 c = kr[m / 2];
+                const u32x4 c = T.k[m / 2];
                 const uint32_t w0 = (m % 2) ? c.z : c.x;
                 const uint32_t w1 = (m % 2) ? c.w : c.y;
                 u32x4 e = {M::fp8x2(w0, false), M::fp8x2(w0, true), M::fp8x2(w1, false),
@@ -195,8 +183,6 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a, int32_t 
             }
             s = M::qk(kop, qop[m], s);
         }
-
-        // online softmax for head `col`; this lane holds tokens 4*grp + r
         float x[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r)
@@ -214,17 +200,14 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a, int32_t 
         l_run = fmaf(l_run, alpha, (p[0] + p[1]) + (p[2] + p[3]));
         const u32x2 pp = {M::pack2(p[0], p[1]), M::pack2(p[2], p[3])};
         const A4 pop = __builtin_bit_cast(A4, pp);
-
-        // O^T += V^T * P^T
         const bool tail = valid < kBlockSize;
 #pragma unroll
-        for (int t = 0; t < S::PV_TILES; ++t) {
+        for (int t = 0; t < PV_TILES; ++t) {
             u32x2 vw;
-            if constexpr (S::KE == 2) {
-                vw = u32x2{vr[t][0], vr[t][1]};
-            } else {
-                vw = u32x2{M::fp8x2(vr[t][0], false), M::fp8x2(vr[t][0], true)};
-            }
+            if constexpr (KE == 2)
+                vw = u32x2{T.v[t][0], T.v[t][1]};
+            else
+                vw = u32x2{M::fp8x2(T.v[t][0], false), M::fp8x2(T.v[t][0], true)};
             if (tail) {
                 // slots past the end may hold anything (NaN included): zero them
 #pragma unroll
@@ -243,34 +226,176 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a, int32_t 
         }
     }
 
-    // the lane groups hold disjoint tokens: sum their shares of l
-    l_run += shfl_xor(l_run, 16);
-    l_run += shfl_xor(l_run, 32);
+    // Tokens [t0, t1) of (b, g); t0 is a multiple of 16.  Returns false if a
+    // block-table entry is outside the pool (nothing is read then).
+    __device__ bool run(const DecodeArgs &a, int lane, int32_t b, int32_t g, int32_t t0,
+                        int32_t t1)
+    {
+        const int32_t *table = a.block_tables + (size_t)b * a.max_blocks_per_seq;
+        const char *kbase = static_cast<const char *>(a.k_cache) + (size_t)g * TILE_BYTES;
+        const char *vbase = static_cast<const char *>(a.v_cache) + (size_t)g * TILE_BYTES;
+        const size_t bstride = (size_t)a.num_kv_heads * TILE_BYTES;
+        const int32_t jb0 = uniform(t0 / kBlockSize);
+        const int32_t jb1 = uniform((t1 + kBlockSize - 1) / kBlockSize);
+        t1 = uniform(t1);
+        const float sc = a.score_scale;
 
-    if (col >= G)
-        return;
-    if (a.partition == 0) {
+        // block ids of up to 64 blocks, one per lane
+        int32_t cb = jb0;
+        int32_t tv = 0;
+        auto fetch_ids = [&](int32_t base) -> bool {
+            cb = base;
+            const bool in = base + lane < jb1;
+            tv = in ? table[base + lane] : 0;
+            // Keep the ids in this register: re-reading an id from memory per
+            // block would wait for every load in flight, the next tile's too.
+            asm volatile("" : "+v"(tv));
+            return !__any(in && (tv < 0 || tv >= a.num_blocks));
+        };
+        if (!fetch_ids(jb0))
+            return false;
+        auto tile_ptrs = [&](int32_t jb, const char *&kt, const char *&vt) -> bool {
+            if (jb - cb >= kWave && !fetch_ids(jb))
+                return false;
+            const int32_t phys = __builtin_amdgcn_readlane(tv, uniform(jb - cb));
+            kt = kbase + (size_t)phys * bstride;
+            vt = vbase + (size_t)phys * bstride;
+            return true;
+        };
+        auto valid_of = [&](int32_t jb) { return min(kBlockSize, t1 - jb * kBlockSize); };
+
+        Tile A, B;
+        const char *kt, *vt;
+        int32_t jb = jb0;
+        if (!tile_ptrs(jb, kt, vt))
+            return false;
+        load_tile(kt, vt, col, grp, A);
+        for (;;) {
+            const bool hasB = jb + 1 < jb1;
+            if (hasB) {
+                if (!tile_ptrs(jb + 1, kt, vt))
+                    return false;
+                load_tile(kt, vt, col, grp, B);
+            }
+            compute(A, valid_of(jb), sc);
+            if (!hasB)
+                break;
+            const bool hasA = jb + 2 < jb1;
+            if (hasA) {
+                if (!tile_ptrs(jb + 2, kt, vt))
+                    return false;
+                load_tile(kt, vt, col, grp, A);
+            }
+            compute(B, valid_of(jb + 1), sc);
+            if (!hasA)
+                break;
+            jb += 2;
+        }
+        return true;
+    }
+
+    // The lane groups hold disjoint tokens: sum their shares of l.
+    __device__ void finish() { l_run += shfl_xor(l_run, 16), l_run += shfl_xor(l_run, 32); }
+
+    __device__ void write_out(const DecodeArgs &a, int32_t b, int32_t g, int32_t n, bool ok)
+    {
+        if (col >= a.group)
+            return;
         TQ *o = static_cast<TQ *>(a.out) +
-                ((size_t)it.b * a.num_q_heads + (size_t)it.g * G + col) * D;
-        const float inv = bad ? NAN : (it.n > 0 ? a.v_scale / l_run : 0.f);
+                ((size_t)b * a.num_q_heads + (size_t)g * a.group + col) * D;
+        const float inv = !ok ? NAN : (n > 0 ? a.v_scale / l_run : 0.f);
 #pragma unroll
-        for (int t = 0; t < S::PV_TILES; ++t)
+        for (int t = 0; t < PV_TILES; ++t)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 o[16 * t + 4 * grp + r] = from_f32<QT>(acc[t][r] * inv);
-    } else {
+    }
+
+    __device__ void write_partial(const DecodeArgs &a, int64_t slot, bool ok)
+    {
+        if (col >= a.group)
+            return;
         if (grp == 0) {
-            float *ml = ws_ml(a, w, col);
-            ml[0] = bad ? NAN : m_run;
-            ml[1] = bad ? NAN : l_run;
+            float *ml = ws_ml(a, slot, col);
+            ml[0] = ok ? m_run : NAN;
+            ml[1] = ok ? l_run : NAN;
         }
-        float *accp = ws_acc(a, w, col, D);
-        const float f = bad ? NAN : a.v_scale;
+        float *accp = ws_acc(a, slot, col, D);
+        const float f = ok ? a.v_scale : NAN;
 #pragma unroll
-        for (int t = 0; t < S::PV_TILES; ++t)
+        for (int t = 0; t < PV_TILES; ++t)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 accp[16 * t + 4 * grp + r] = acc[t][r] * f;
+    }
+};
+
+// partition == 0 or > 0: one wave per work item (see work.hpp).
+template <int QT, int KT, int D>
+__global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a, int32_t num_items)
+{
+    const int lane = threadIdx.x & 63;
+    const int32_t w = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (w >= num_items)
+        return;
+    const Item it = item_of(a, w);
+    if (it.valid_len && it.n > 0 && it.t0 >= it.t1)
+        return;
+    if (it.valid_len && it.n == 0 && it.p > 0)
+        return;
+    MfmaWave<QT, KT, D> wv(lane);
+    wv.start(a, it.b, it.g);
+    bool ok = it.valid_len;
+    if (ok && it.t1 > it.t0)
+        ok = wv.run(a, lane, it.b, it.g, it.t0, it.t1);
+    wv.finish();
+    if (a.partition == 0)
+        wv.write_out(a, it.b, it.g, it.n, ok);
+    else
+        wv.write_partial(a, w, ok);
+}
+
+// Balanced split: wave i of W takes tiles [i*T/W, (i+1)*T/W) of the list of
+// all (sequence, KV head, block) tiles in that order, T tiles in total.
+template <int QT, int KT, int D>
+__global__ __launch_bounds__(256) void decode_mfma_balanced_kernel(DecodeArgs a, int32_t W)
+{
+    const int lane = threadIdx.x & 63;
+    const int32_t i = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (i >= W)
+        return;
+    const int32_t H = a.num_kv_heads;
+
+    // T, the number of runs (never more than tiles, so no run is empty), and
+    // the first segment of this wave's run
+    const int64_t T = tiles_before(a, lane, a.num_seqs);
+    const int32_t runs = effective_runs(T, W);
+    if (i >= runs)
+        return;
+    const int64_t x0 = (int64_t)i * T / runs;
+    const int64_t x1 = (int64_t)(i + 1) * T / runs;
+    SeqPos pos = locate_tile(a, lane, x0);
+
+    MfmaWave<QT, KT, D> wv(lane);
+    int64_t x = x0;
+    while (x < x1) {
+        const int32_t nb = blocks_of(pos.n);
+        const int64_t local = x - pos.first_tile;
+        const int32_t g = (int32_t)(local / nb);
+        const int32_t j = (int32_t)(local % nb);
+        const int64_t seg_end = pos.first_tile + (int64_t)(g + 1) * nb;
+        const int64_t stop = min(x1, seg_end);
+        const int32_t je = j + (int32_t)(stop - x);
+        wv.start(a, pos.b, g);
+        const bool ok = wv.run(a, lane, pos.b, g, j * kBlockSize, min(je * kBlockSize, pos.n));
+        wv.finish();
+        if (j == 0 && je == nb)
+            wv.write_out(a, pos.b, g, pos.n, ok);
+        else
+            wv.write_partial(a, (int64_t)i + (int64_t)pos.b * H + g, ok);
+        x = stop;
+        if (x < x1 && g == H - 1)
+            pos = next_sequence(a, pos);
     }
 }
 
@@ -278,9 +403,25 @@ template <int QT, int KT, int D>
 hipError_t launch_mfma(const DecodeArgs &a, int32_t num_items, hipStream_t stream)
 {
     const int grid = (num_items + 3) / 4;
-    hipLaunchKernelGGL((decode_mfma_kernel<QT, KT, D>), dim3(grid), dim3(256), 0, stream, a,
-                       num_items);
+    if (a.partition == kPartitionBalanced)
+        hipLaunchKernelGGL((decode_mfma_balanced_kernel<QT, KT, D>), dim3(grid), dim3(256), 0,
+                           stream, a, num_items);
+    else
+        hipLaunchKernelGGL((decode_mfma_kernel<QT, KT, D>), dim3(grid), dim3(256), 0, stream, a,
+                           num_items);
     return hipGetLastError();
+}
+
+// Waves of the balanced kernel one CU holds at once.
+template <int QT, int KT, int D>
+int mfma_balanced_waves_per_cu()
+{
+    int blocks = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &blocks, reinterpret_cast<const void *>(&decode_mfma_balanced_kernel<QT, KT, D>), 256,
+            0) != hipSuccess)
+        return 0;
+    return blocks * 4;
 }
 
 template <int QT, int KT>
@@ -305,6 +446,20 @@ hipError_t launch_decode_mfma(const DecodeArgs &a, pa_dtype qt, pa_dtype kt, int
     if (qt == PA_F16 && kt == PA_FP8_E4M3)
         return mfma_by_dim<PA_F16, PA_FP8_E4M3>(a, D, num_items, s);
     return hipErrorInvalidValue;
+}
+
+int mfma_waves_per_cu(pa_dtype qt, pa_dtype kt, int D)
+{
+#define PA_W(Q, K)                                                                                 \
+    if (qt == Q && kt == K)                                                                        \
+        return D == 64 ? mfma_balanced_waves_per_cu<Q, K, 64>()                                    \
+                       : mfma_balanced_waves_per_cu<Q, K, 128>();
+    PA_W(PA_BF16, PA_BF16)
+    PA_W(PA_F16, PA_F16)
+    PA_W(PA_BF16, PA_FP8_E4M3)
+    PA_W(PA_F16, PA_FP8_E4M3)
+#undef PA_W
+    return 0;
 }
 
 bool mfma_supports(pa_dtype qt, pa_dtype kt, int D, int G)

@@ -147,6 +147,15 @@ __device__ __forceinline__ void wave_lds_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// A value every lane of the wave reads from the same address, marked
+// wave-uniform so control flow that depends on it stays scalar.
+__device__ __forceinline__ int32_t uniform_load(const int32_t *p)
+{
+    return __builtin_amdgcn_readfirstlane(*p);
+}
+
+__device__ __forceinline__ int32_t uniform(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
 __device__ __forceinline__ u32x4 load16(const void *p)
 {
     return *reinterpret_cast<const u32x4 *>(p);

@@ -24,19 +24,33 @@ __global__ __launch_bounds__(64) void merge_kernel(DecodeArgs a)
     const int32_t n = a.seq_lens[b];
     TQ *o = static_cast<TQ *>(a.out) + (size_t)row * D;
 
-    const bool valid = n >= 0 && n <= a.max_seq_len &&
-                       (int64_t)n <= (int64_t)a.max_blocks_per_seq * kBlockSize;
+    const bool valid = len_ok(a, n);
     if (!valid || n == 0) {
 #pragma unroll
         for (int i = 0; i < PER_LANE; ++i)
             o[i * kWave + lane] = from_f32<QT>(valid ? 0.f : NAN);
         return;
     }
-    const int32_t nparts = (n + a.partition - 1) / a.partition;
-    const int64_t w0 = ((int64_t)b * a.num_kv_heads + g) * a.max_parts;
+    // slots w0 .. w0 + nparts - 1 hold this segment's partial states
+    int64_t w0, nparts;
+    if (a.partition == kPartitionBalanced) {
+        const int64_t T = tiles_before(a, lane, a.num_seqs);
+        const int32_t R = effective_runs(T, a.waves);
+        const int64_t S0 = tiles_before(a, lane, b) + (int64_t)g * blocks_of(n);
+        const int64_t S1 = S0 + blocks_of(n);
+        const int64_t i0 = run_of_tile(S0, T, R);
+        const int64_t i1 = run_of_tile(S1 - 1, T, R);
+        if (i0 == i1)
+            return; // one run held the whole segment and wrote the row itself
+        w0 = i0 + (int64_t)b * a.num_kv_heads + g;
+        nparts = i1 - i0 + 1;
+    } else {
+        w0 = ((int64_t)b * a.num_kv_heads + g) * a.max_parts;
+        nparts = (n + a.partition - 1) / a.partition;
+    }
 
     float M = -INFINITY;
-    for (int32_t p = lane; p < nparts; p += kWave)
+    for (int64_t p = lane; p < nparts; p += kWave)
         M = fmaxf(M, ws_ml(a, w0 + p, h)[0]);
 #pragma unroll
     for (int x = 1; x < kWave; x <<= 1)
@@ -48,7 +62,7 @@ __global__ __launch_bounds__(64) void merge_kernel(DecodeArgs a)
     for (int i = 0; i < PER_LANE; ++i)
         acc[i] = 0.f;
     bool nan_seen = false;
-    for (int32_t p = 0; p < nparts; ++p) {
+    for (int64_t p = 0; p < nparts; ++p) {
         const float *ml = ws_ml(a, w0 + p, h);
         const float mp = ml[0];
         nan_seen |= (mp != mp);

@@ -22,11 +22,123 @@ struct DecodeArgs {
     int32_t num_blocks;
     int32_t max_blocks_per_seq;
     int32_t max_seq_len;
-    int32_t partition;         // tokens per work item; 0 = whole sequence
-    int32_t max_parts;         // work items per (sequence, KV head)
+    int32_t partition;         // tokens per work item; 0 = whole sequence; -1 = balanced
+    int32_t max_parts;         // work items per (sequence, KV head) (fixed partitions)
+    int32_t waves;             // W, the number of runs (balanced)
+    int64_t num_slots;         // partial-state slots in the workspace
     float score_scale;         // scale * k_scale * log2(e): scores in log2 units
     float v_scale;
 };
+
+constexpr int32_t kPartitionBalanced = -1; // PA_PARTITION_BALANCED
+
+__device__ __forceinline__ bool len_ok(const DecodeArgs &a, int32_t n)
+{
+    return n >= 0 && n <= a.max_seq_len &&
+           (int64_t)n <= (int64_t)a.max_blocks_per_seq * kBlockSize;
+}
+
+__device__ __forceinline__ int32_t blocks_of(int32_t n) { return (n + kBlockSize - 1) / kBlockSize; }
+
+// Blocks a sequence contributes to the balanced split; a length out of range
+// contributes none (the merge kernel writes that row as NaN).
+__device__ __forceinline__ int32_t split_blocks(const DecodeArgs &a, int32_t n)
+{
+    return len_ok(a, n) ? blocks_of(n) : 0;
+}
+
+__device__ __forceinline__ int64_t wave_sum(int64_t v)
+{
+#pragma unroll
+    for (int x = 1; x < kWave; x <<= 1)
+        v += __shfl_xor(v, x, kWave);
+    return v;
+}
+
+__device__ __forceinline__ int64_t wave_incl_scan(int64_t v, int lane)
+{
+#pragma unroll
+    for (int x = 1; x < kWave; x <<= 1) {
+        const int64_t o = __shfl_up(v, x, kWave);
+        if (lane >= x)
+            v += o;
+    }
+    return v;
+}
+
+__device__ __forceinline__ int64_t readlane64(int64_t v, int l)
+{
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, l);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)v >> 32), l);
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Tiles (KV head x block) of sequences [0, upto), summed by one wave.
+__device__ __forceinline__ int64_t tiles_before(const DecodeArgs &a, int lane, int32_t upto)
+{
+    int64_t t = 0;
+    for (int32_t c = 0; c < upto; c += kWave) {
+        const int32_t b = c + lane;
+        t += (b < upto) ? split_blocks(a, a.seq_lens[b]) : 0;
+    }
+    return wave_sum(t) * a.num_kv_heads;
+}
+
+struct SeqPos {
+    int32_t b;          // sequence
+    int32_t n;          // its length
+    int64_t first_tile; // index of its first tile in the balanced order
+};
+
+// The sequence holding tile x (x < total tiles), found one 64-sequence chunk
+// at a time with a wave scan and a ballot.
+__device__ __forceinline__ SeqPos locate_tile(const DecodeArgs &a, int lane, int64_t x)
+{
+    int64_t carry = 0;
+    for (int32_t c = 0; c < a.num_seqs; c += kWave) {
+        const int32_t b = c + lane;
+        const int64_t tiles =
+            (b < a.num_seqs) ? (int64_t)split_blocks(a, a.seq_lens[b]) * a.num_kv_heads : 0;
+        const int64_t incl = wave_incl_scan(tiles, lane);
+        const uint64_t hit = __ballot(b < a.num_seqs && carry + incl > x);
+        if (hit) {
+            const int k = __ffsll((unsigned long long)hit) - 1;
+            SeqPos p;
+            p.b = c + k;
+            p.n = uniform_load(a.seq_lens + p.b);
+            p.first_tile = carry + readlane64(incl - tiles, k);
+            return p;
+        }
+        carry += readlane64(incl, kWave - 1);
+    }
+    return SeqPos{a.num_seqs, 0, carry};
+}
+
+// The next sequence after p that has tiles.
+__device__ __forceinline__ SeqPos next_sequence(const DecodeArgs &a, SeqPos p)
+{
+    SeqPos q;
+    q.first_tile = p.first_tile + (int64_t)blocks_of(p.n) * a.num_kv_heads;
+    q.b = p.b + 1;
+    while (q.b < a.num_seqs && split_blocks(a, uniform_load(a.seq_lens + q.b)) == 0)
+        ++q.b;
+    q.n = q.b < a.num_seqs ? uniform_load(a.seq_lens + q.b) : 0;
+    return q;
+}
+
+// Runs the balanced split cuts T tiles into: the launch's W waves, but no
+// more than T so that every run holds at least one tile.
+__device__ __forceinline__ int32_t effective_runs(int64_t T, int32_t W)
+{
+    return (int32_t)(T < (int64_t)W ? T : (int64_t)W);
+}
+
+// Run holding tile x when T tiles are cut into R runs [i*T/R, (i+1)*T/R)
+// (R <= T, so runs are never empty and consecutive runs are adjacent).
+__device__ __forceinline__ int64_t run_of_tile(int64_t x, int64_t T, int32_t R)
+{
+    return ((x + 1) * R - 1) / T;
+}
 
 // Work item w covers (sequence b, KV head g, part p) with
 //   w = (b * num_kv_heads + g) * max_parts + p
@@ -44,9 +156,8 @@ __device__ __forceinline__ Item item_of(const DecodeArgs &a, int32_t w)
     const int32_t s = w / a.max_parts;
     it.b = s / a.num_kv_heads;
     it.g = s % a.num_kv_heads;
-    it.n = a.seq_lens[it.b];
-    it.valid_len = it.n >= 0 && it.n <= a.max_seq_len &&
-                   (int64_t)it.n <= (int64_t)a.max_blocks_per_seq * kBlockSize;
+    it.n = uniform_load(a.seq_lens + it.b);
+    it.valid_len = len_ok(a, it.n);
     if (a.partition == 0) {
         it.t0 = 0;
         it.t1 = it.n;
@@ -57,10 +168,11 @@ __device__ __forceinline__ Item item_of(const DecodeArgs &a, int32_t w)
     return it;
 }
 
-// Partial state layout in the workspace, per work item and query head of its
-// group: (m, l) pairs first, then the unnormalised accumulators.
+// Partial state layout in the workspace, per slot w (a work item, or in the
+// balanced split a (run, segment) pair) and query head h of the group: (m, l)
+// pairs first, then the unnormalised accumulators.  S = num_slots.
 //   ws[(w * G + h) * 2 + {0, 1}]                     m (log2 units), l
-//   ws[2 * W * G + (w * G + h) * D + d]              acc
+//   ws[2 * S * G + (w * G + h) * D + d]              acc
 __device__ __forceinline__ float *ws_ml(const DecodeArgs &a, int64_t w, int h)
 {
     return a.ws + (w * a.group + h) * 2;
@@ -68,8 +180,7 @@ __device__ __forceinline__ float *ws_ml(const DecodeArgs &a, int64_t w, int h)
 
 __device__ __forceinline__ float *ws_acc(const DecodeArgs &a, int64_t w, int h, int D)
 {
-    const int64_t W = (int64_t)a.num_seqs * a.num_kv_heads * a.max_parts;
-    return a.ws + 2 * W * a.group + (w * a.group + h) * (int64_t)D;
+    return a.ws + 2 * a.num_slots * a.group + (w * a.group + h) * (int64_t)D;
 }
 
 } // namespace pa

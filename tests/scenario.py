@@ -80,7 +80,7 @@ class GpuStep:
         self.d_lens = torch.from_numpy(self.lens).cuda()
         self.out = torch.empty_like(inputs.q)
         self.workspace = None
-        if self.partition > 0:
+        if self.partition != 0:
             nb = pa.pa_decode_workspace_bytes(self.desc, w.num_seqs, w.max_seq_len(),
                                               self.partition)
             self.workspace = torch.empty(nb, dtype=torch.uint8, device="cuda")

@@ -65,11 +65,13 @@ KERNELS = [pa.KERNEL_VALU, pa.KERNEL_MFMA]
 
 @pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
-@pytest.mark.parametrize("partition", [0, 64, 512])
+@pytest.mark.parametrize("partition", [0, 64, 512, pa.PARTITION_BALANCED])
 def test_parity_small(cid, partition, kernel):
     w = workloads.config(cid, "full" if cid == 1 else "small")
     if not kernel_supports(kernel, w):
         pytest.skip("shape not built for this kernel")
+    if partition == pa.PARTITION_BALANCED and kernel != pa.KERNEL_MFMA:
+        pytest.skip("the balanced split is built for the MFMA kernel")
     for layer in range(w.num_layers):
         run_and_check(w, layer, partition=partition, kernel=kernel)
 
@@ -167,7 +169,9 @@ def test_fp8_append_encoder_rounding():
 
 
 # -- invariances on the GPU (bitwise) -------------------------------------------
-def test_block_placement_does_not_change_output_bits():
+@pytest.mark.parametrize("kernel,partition", [(pa.KERNEL_VALU, 64), (pa.KERNEL_MFMA, 64),
+                                              (pa.KERNEL_MFMA, pa.PARTITION_BALANCED)])
+def test_block_placement_does_not_change_output_bits(kernel, partition):
     """Two pools with different shuffle seeds place the same logical blocks
     differently; the outputs must be bit-identical."""
     w = workloads.config(2, "small")
@@ -175,7 +179,7 @@ def test_block_placement_does_not_change_output_bits():
     outs, tables = [], []
     for seed in (11, 12345):
         w.shuffle_seeds = [seed]
-        g = GpuStep(w, 0, inp, partition=64, kernel=pa.KERNEL_VALU)
+        g = GpuStep(w, 0, inp, partition=partition, kernel=kernel)
         g.append_prefill()
         g.append_step()
         outs.append(g.decode().clone())
@@ -185,12 +189,13 @@ def test_block_placement_does_not_change_output_bits():
     assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
 
 
-def test_shared_prefix_equals_duplicated_prefix_bits():
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_shared_prefix_equals_duplicated_prefix_bits(kernel):
     """dev.to §5: sequences mapping the same prefix blocks give the same bits
     as sequences holding private copies of that prefix."""
     w = workloads.config(4, "small")
     inp = Inputs(w)
-    g = GpuStep(w, 0, inp, partition=0, kernel=pa.KERNEL_VALU)
+    g = GpuStep(w, 0, inp, partition=0, kernel=kernel)
     g.append_prefill()
     g.append_step()
     shared = g.decode().clone()
@@ -213,7 +218,7 @@ def test_shared_prefix_equals_duplicated_prefix_bits():
     inp2.k_pre, inp2.v_pre = torch.cat(kp), torch.cat(vp)
     inp2.q, inp2.k_new, inp2.v_new = inp.q, inp.k_new, inp.v_new
     inp2.k_scale, inp2.v_scale = inp.k_scale, inp.v_scale
-    g2 = GpuStep(w2, 0, inp2, partition=0, kernel=pa.KERNEL_VALU)
+    g2 = GpuStep(w2, 0, inp2, partition=0, kernel=kernel)
     assert set(g2.tables[0][:P // 16]).isdisjoint(g2.tables[1][:P // 16])
     g2.append_prefill()
     g2.append_step()
@@ -222,17 +227,19 @@ def test_shared_prefix_equals_duplicated_prefix_bits():
     assert torch.equal(shared.view(torch.int16), dup.view(torch.int16))
 
 
-def test_partitioned_matches_single_pass():
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_partitioned_matches_single_pass(kernel):
     w = workloads.config(2, "small")
     inp = Inputs(w)
     outs = {}
-    for part in (0, 16, 128):
-        g = GpuStep(w, 0, inp, partition=part, kernel=pa.KERNEL_VALU)
+    parts = (0, 16, 128) + ((pa.PARTITION_BALANCED,) if kernel == pa.KERNEL_MFMA else ())
+    for part in parts:
+        g = GpuStep(w, 0, inp, partition=part, kernel=kernel)
         g.append_prefill()
         g.append_step()
         outs[part] = to_f64(g.decode())
-    assert np.max(np.abs(outs[0] - outs[16])) < 1e-2
-    assert np.max(np.abs(outs[0] - outs[128])) < 1e-2
+    for part in parts[1:]:
+        assert np.max(np.abs(outs[0] - outs[part])) < 1e-2
 
 
 def test_zero_length_sequence_gives_zero_row():
@@ -258,3 +265,30 @@ def test_zero_length_sequence_gives_zero_row():
                             num_kv_heads=1, head_dim=D, block_size=16, num_blocks=NB,
                             q_dtype="f32", kv_dtype="f32", scale=0.125)
         check_close(to_f64(out), ref, "f32", "f32")
+
+
+@pytest.mark.parametrize("part", [0, 16, pa.PARTITION_BALANCED])
+def test_zero_length_rows_mfma(part):
+    """bf16 GQA batch with empty sequences between non-empty ones."""
+    say(f"[case] zero-length rows mfma partition={part}")
+    D, NB, Hq, Hkv = 128, 6, 8, 2
+    g = torch.Generator().manual_seed(3)
+    k = torch.randn(NB * Hkv * 16 * D, generator=g).to(torch.bfloat16).cuda()
+    v = torch.randn(NB * Hkv * 16 * D, generator=g).to(torch.bfloat16).cuda()
+    tables = torch.tensor([[0, -1], [2, 1], [-1, -1], [5, -1]], dtype=torch.int32, device="cuda")
+    lens = torch.tensor([0, 20, 0, 5], dtype=torch.int32, device="cuda")
+    q = torch.randn(4, Hq, D, generator=g).to(torch.bfloat16).cuda()
+    desc = pa.kv_desc(Hq, Hkv, D, NB, "bf16", "bf16", kernel=pa.KERNEL_MFMA)
+    ws = None
+    if part:
+        ws = torch.empty(pa.pa_decode_workspace_bytes(desc, 4, 32, part), dtype=torch.uint8,
+                         device="cuda")
+    out = torch.full_like(q, 7.0)
+    pa.pa_decode(q, k, v, tables, lens, 32, 0.088, out, desc, workspace=ws, partition_size=part)
+    torch.cuda.synchronize()
+    assert torch.all(out[0] == 0) and torch.all(out[2] == 0)
+    ref = oracle.decode(workloads.storage(q), workloads.storage(k), workloads.storage(v),
+                        tables.cpu().numpy(), lens.cpu().numpy(), num_q_heads=Hq,
+                        num_kv_heads=Hkv, head_dim=D, block_size=16, num_blocks=NB,
+                        q_dtype="bf16", kv_dtype="bf16", scale=float(np.float32(0.088)))
+    check_close(to_f64(out), ref, "bf16", "bf16")
