@@ -86,6 +86,11 @@ template <> struct Mma<PA_F16> {
     }
 };
 
+// Largest gap (log2 units) between a block's scores and the reference max
+// before the accumulators are rescaled: weights stay <= 2^8, exact in bf16/fp16
+// range and harmless to fp32 sums.
+constexpr float kLazyRescale = 8.0f;
+
 // One wave's state and per-block work for one (sequence, KV head).
 template <int QT, int KT, int D>
 struct MfmaWave {
@@ -190,14 +195,24 @@ struct MfmaWave {
         float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
         bm = fmaxf(bm, shfl_xor(bm, 16));
         bm = fmaxf(bm, shfl_xor(bm, 32));
-        const float mn = fmaxf(m_run, bm);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
-        m_run = mn;
+        // The reference max m_run moves only when a block's max exceeds it by
+        // more than kLazyRescale (log2 units); until then the weights
+        // 2^(s - m_run) stay below 2^kLazyRescale and acc, l need no rescale.
+        // Any reference gives the same softmax: acc and l share it.
+        if (__any(bm > m_run + kLazyRescale)) {
+            const float mn = fmaxf(m_run, bm);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+            m_run = mn;
+            l_run *= alpha;
+#pragma unroll
+            for (int t = 0; t < PV_TILES; ++t)
+                acc[t] *= alpha;
+        }
         float p[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            p[r] = __builtin_amdgcn_exp2f(x[r] - mn);
-        l_run = fmaf(l_run, alpha, (p[0] + p[1]) + (p[2] + p[3]));
+            p[r] = __builtin_amdgcn_exp2f(x[r] - m_run);
+        l_run += (p[0] + p[1]) + (p[2] + p[3]);
         const u32x2 pp = {M::pack2(p[0], p[1]), M::pack2(p[2], p[3])};
         const A4 pop = __builtin_bit_cast(A4, pp);
         const bool tail = valid < kBlockSize;
@@ -221,7 +236,6 @@ struct MfmaWave {
                     }
                 }
             }
-            acc[t] *= alpha;
             acc[t] = M::pv(__builtin_bit_cast(A4, vw), pop, acc[t]);
         }
     }
@@ -264,6 +278,7 @@ struct MfmaWave {
         };
         auto valid_of = [&](int32_t jb) { return min(kBlockSize, t1 - jb * kBlockSize); };
 
+        // Two tiles alternate: while one is computed, the next is in flight.
         Tile A, B;
         const char *kt, *vt;
         int32_t jb = jb0;
