@@ -7,20 +7,24 @@ batch of 32 sequences with lengths uniform in [512, 4096], blocks scattered
 over a pool 1.25x the size they need (dev.to, "Why LLMs Run Out of VRAM...",
 §2 Example 2 and §4).
 
-A timed step is the whole hot path for the batch:
-  host:   pa_seq_append_slots_batch (one new slot per sequence, a new block
-          at every 16th token) and pa_export_block_tables into pinned memory,
-          then an async copy to the device;
-  device: pa_cache_append of the new token's K/V, then pa_decode (partials +
-          merge kernels, or one kernel in single-pass mode).
-Inputs are resident in HBM before timing starts.  The caches are rotated
-over R replicas (one per step, like the layers of a model) so that the
-working set exceeds the 256 MB Infinity Cache and reads come from HBM.
+A timed step is the whole device-side hot path for the batch:
+pa_cache_append of the new token's K/V, then pa_decode (decode kernel, then
+the merge kernel in the partitioned modes).  Inputs are resident in HBM when
+timing starts, the per-step metadata included: the host allocator
+(pa_seq_append_slots_batch: one new slot per sequence, a new block at every
+16th token; pa_export_block_tables) runs for every step first and the
+tables, lengths and slots of all steps go to the device in one copy.
+--upload-per-step instead runs the allocator and a pinned-memory copy of that
+step's metadata inside every timed step (the host-inclusive rate).  The
+caches are rotated over R replicas (one per step, like the layers of a
+model) so that the working set exceeds the 256 MB Infinity Cache and reads
+come from HBM.
 
 Printed: one JSON line.  `value` is KV-read GB/s over whole steps
 (algorithmic bytes: every valid token's K and V row of each KV head once);
-`roofline` is for the decode kernel alone, timed with HIP events around each
-of its launches; `cpu_baseline` times the CPU oracle on a bounded sample.
+`roofline` is for the decode kernel alone: K launches of it back to back on
+the last step's inputs, between two events; `cpu_baseline` times the CPU
+oracle on a bounded sample.
 """
 import argparse
 import ctypes
@@ -55,6 +59,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--upload-per-step", action="store_true",
+                    help="run the host allocator and copy the step's metadata inside each "
+                         "timed step")
     return ap.parse_args()
 
 
@@ -79,7 +86,7 @@ def main():
     B, Hq, Hkv, D, L = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.num_layers
     eb = {"f32": 4, "f16": 2, "bf16": 2, "e4m3": 1}[w.kv_dtype]
     K, W = args.steps, args.warmup
-    total_steps = W + 2 * K  # warm-up, timed pass, kernel-event pass
+    total_steps = W + K
 
     # pool with room for every token the steps append
     grow_blocks = B * (math.ceil((total_steps + 1) / 16) + 1)
@@ -126,18 +133,35 @@ def main():
         ws_bytes = pa.pa_decode_workspace_bytes(desc, B, max_len, partition)
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
 
-    # Per-step metadata (slots, tables, lengths): the host writes it into a
-    # pinned staging ring, then one async copy on the compute stream moves it
-    # to the device buffer the kernels read.
-    NBUF = 8
+    # Per-step metadata (slots, tables, lengths), one row per step.
     meta_words = B + B * maxb + B  # slots, tables, lens
-    staging = torch.empty((NBUF, meta_words), dtype=torch.int32, pin_memory=True)
-    staged = [torch.cuda.Event() for _ in range(NBUF)]      # copy out of staging[buf] done
-    d_meta = torch.empty(meta_words, dtype=torch.int32, device=dev)
-
     lib = pa._lib
     pool_h = pool.handle
     dec_p = dec.ctypes.data
+
+    def host_step(dst_ptr):
+        rc = lib.pa_seq_append_slots_batch(pool_h, dec_p, B, 1, dst_ptr)
+        rc |= lib.pa_export_block_tables(pool_h, dec_p, B, maxb, dst_ptr + 4 * B,
+                                         dst_ptr + 4 * (B + B * maxb))
+        if rc:
+            raise RuntimeError("host step failed: " + pa.pa_last_error())
+
+    upload = args.upload_per_step
+    if upload:
+        # a pinned staging ring; each step copies its row to the device buffer
+        NBUF = 8
+        staging = torch.empty((NBUF, meta_words), dtype=torch.int32, pin_memory=True)
+        staged = [torch.cuda.Event() for _ in range(NBUF)]  # copy out of staging[buf] done
+        d_meta = torch.empty((1, meta_words), dtype=torch.int32, device=dev)
+        stage_ptrs = [staging[i].data_ptr() for i in range(NBUF)]
+    else:
+        # every step's metadata, made by the host allocator up front
+        h_meta = torch.empty((total_steps, meta_words), dtype=torch.int32, pin_memory=True)
+        for i in range(total_steps):
+            host_step(h_meta[i].data_ptr())
+        d_meta = h_meta.to(dev)
+    meta_row = d_meta.stride(0) * 4
+
     stream = torch.cuda.current_stream()
     s_h = stream.cuda_stream
     dref = ctypes.byref(desc)
@@ -145,86 +169,90 @@ def main():
     qp, kn, vn, op = q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), out.data_ptr()
     ws_p = ws.data_ptr() if ws is not None else None
     scale = w.scale
-    stage_ptrs = [staging[i].data_ptr() for i in range(NBUF)]
-    slots_p = d_meta.data_ptr()
-    tables_p = slots_p + 4 * B
-    lens_p = slots_p + 4 * (B + B * maxb)
+    meta_base = d_meta.data_ptr()
 
-    # HIP events around every launch of the decode kernel (one per layer and step)
-    ev_k = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(K * L)]
-
-    def step(i, timed):
-        buf = i % NBUF
-        if i >= NBUF:
-            staged[buf].synchronize()  # the copy that last read this buffer is done
-        sp = stage_ptrs[buf]
-        rc = lib.pa_seq_append_slots_batch(pool_h, dec_p, B, 1, sp)
-        rc |= lib.pa_export_block_tables(pool_h, dec_p, B, maxb, sp + 4 * B,
-                                         sp + 4 * (B + B * maxb))
-        if rc:
-            raise RuntimeError("host step failed: " + pa.pa_last_error())
-        d_meta.copy_(staging[buf], non_blocking=True)
-        staged[buf].record(stream)
+    def step(i):
+        if upload:
+            buf = i % NBUF
+            if i >= NBUF:
+                staged[buf].synchronize()  # the copy that last read this buffer is done
+            host_step(stage_ptrs[buf])
+            d_meta[0].copy_(staging[buf], non_blocking=True)
+            staged[buf].record(stream)
+            row = meta_base
+        else:
+            row = meta_base + i * meta_row
+        slots_p, tables_p, lens_p = row, row + 4 * B, row + 4 * (B + B * maxb)
         r = i % R
         for layer in range(L):
             kcp, vcp = kc_p[layer * R + r]
             rc = lib.pa_cache_append(kn, vn, kcp, vcp, slots_p, B, dref, ks, vs, s_h)
-            ev = ev_k[(i - W - K) * L + layer] if timed else None
-            if ev:
-                ev[0].record()
-            if partition == 0:
-                rc |= lib.pa_decode(qp, kcp, vcp, tables_p, maxb, lens_p,
-                                    B, max_len, scale, ks, vs, op, None, 0, 0, dref, s_h)
-                if ev:
-                    ev[1].record()
-            else:
-                rc |= lib.pa_decode_partials(qp, kcp, vcp, tables_p, maxb,
-                                             lens_p, B, max_len, scale, ks, vs, ws_p,
-                                             ws_bytes, partition, dref, s_h)
-                if ev:
-                    ev[1].record()
-                rc |= lib.pa_decode_merge(lens_p, B, maxb, max_len, op, ws_p, ws_bytes,
-                                          partition, dref, s_h)
+            rc |= lib.pa_decode(qp, kcp, vcp, tables_p, maxb, lens_p, B, max_len, scale, ks,
+                                vs, op, ws_p, ws_bytes, partition, dref, s_h)
             if rc:
                 raise RuntimeError("launch failed: " + pa.pa_last_error())
 
     # pass 1 (the headline): K whole steps, nothing recorded between kernels
     for i in range(W):
-        step(i, False)
+        step(i)
     torch.cuda.synchronize()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     t_start.record()
     for i in range(W, W + K):
-        step(i, False)
+        step(i)
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_total = t_start.elapsed_time(t_end)
     ms_per_step = ms_total / K
-    # pass 2: the same steps again with HIP events around every decode-kernel launch
-    for i in range(W + K, W + 2 * K):
-        step(i, True)
+    last = W + K - 1
+
+    # pass 2: the decode kernel alone (no append, no merge), K * L launches back
+    # to back on the last step's metadata, rotating over the replicas, between
+    # two events: an event pair around each single launch would add the
+    # queue's dispatch latency to every sample.
+    row = meta_base if upload else meta_base + last * meta_row
+    tables_p, lens_p = row + 4 * B, row + 4 * (B + B * maxb)
+
+    def decode_kernel(r, layer):
+        kcp, vcp = kc_p[layer * R + r]
+        if partition == 0:
+            rc = lib.pa_decode(qp, kcp, vcp, tables_p, maxb, lens_p, B, max_len, scale, ks, vs,
+                               op, None, 0, 0, dref, s_h)
+        else:
+            rc = lib.pa_decode_partials(qp, kcp, vcp, tables_p, maxb, lens_p, B, max_len, scale,
+                                        ks, vs, ws_p, ws_bytes, partition, dref, s_h)
+        if rc:
+            raise RuntimeError("launch failed: " + pa.pa_last_error())
+
+    for j in range(min(K, 10)):
+        decode_kernel(j % R, 0)
     torch.cuda.synchronize()
+    k_start = torch.cuda.Event(enable_timing=True)
+    k_end = torch.cuda.Event(enable_timing=True)
+    k_start.record()
+    for j in range(K):
+        for layer in range(L):
+            decode_kernel(j % R, layer)
+    k_end.record()
+    torch.cuda.synchronize()
+    kern_us = k_start.elapsed_time(k_end) * 1e3 / (K * L)
 
     # algorithmic KV bytes: step i decodes lens0 + i + 1 tokens per sequence
     tokens = np.array([int((lens0 + i + 1).sum()) for i in range(W, W + K)], dtype=np.float64)
     bytes_steps = tokens * step_bytes_1
     gbs = bytes_steps.sum() / (ms_total * 1e-3) / 1e9
-    tokens2 = np.array([int((lens0 + i + 1).sum()) for i in range(W + K, W + 2 * K)],
-                       dtype=np.float64)
-    bytes_steps2 = tokens2 * step_bytes_1
-    kern_ms = np.array([a.elapsed_time(b) for a, b in ev_k])  # per launch
-    kern_gbs = bytes_steps2.sum() / (kern_ms.sum() * 1e-3) / 1e9
+    launch_bytes = int((lens0 + last + 1).sum()) * step_bytes_1 / L  # one layer, last step
+    kern_gbs = launch_bytes / (kern_us * 1e-6) / 1e9
     log(f"[bench] {K} steps: {ms_per_step * 1e3:.2f} us/step (wall {wall / K * 1e6:.2f} us), "
-        f"{gbs:.1f} GB/s over whole steps; decode kernel {kern_ms.mean() * 1e3:.2f} us/launch "
-        f"(p10 {np.percentile(kern_ms, 10) * 1e3:.2f}, p90 {np.percentile(kern_ms, 90) * 1e3:.2f}),"
-        f" {kern_gbs:.1f} GB/s = {kern_gbs / HBM_PEAK_GBS * 100:.1f}% of HBM peak")
-    last = W + 2 * K - 1
-    final_tables = staging[last % NBUF][B:B + B * maxb].numpy().reshape(B, maxb).copy()
-    final_lens = staging[last % NBUF][B + B * maxb:].numpy().copy()
+        f"{gbs:.1f} GB/s over whole steps; decode kernel {kern_us:.2f} us per launch "
+        f"({K * L} back to back), {kern_gbs:.1f} GB/s = {kern_gbs / HBM_PEAK_GBS * 100:.1f}% "
+        f"of HBM peak")
+    final_meta = (staging[last % NBUF] if upload else h_meta[last]).numpy()
+    final_tables = final_meta[B:B + B * maxb].reshape(B, maxb).copy()
+    final_lens = final_meta[B + B * maxb:].copy()
     last_r = last % R
 
     cpu = None
@@ -262,6 +290,7 @@ def main():
             "partition": partition,
             "kernel": kname,
             "cache_replicas": R,
+            "metadata": "uploaded per step" if upload else "resident (all steps)",
             "parallelism": "none (1 GPU)",
         },
         "roofline": {
@@ -271,8 +300,10 @@ def main():
             "unit": "GB/s",
             "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
             "traffic": None,
-            "kernel": "decode_mfma_kernel" if "mfma" in kname else "decode_valu_kernel",
-            "kernel_us_avg": round(float(kern_ms.mean()) * 1e3, 2),
+            "kernel": ("decode_valu_kernel" if "valu" in kname else
+                       "decode_mfma_balanced_kernel" if partition == -1 else
+                       "decode_mfma_kernel"),
+            "kernel_us_avg": round(kern_us, 2),
         },
         "cpu_baseline": cpu,
     }
@@ -299,15 +330,21 @@ def cpu_baseline(w, k_cache, v_cache, q, tables, lens, nblocks, ks, vs, target_s
         oracle.decode(qh, kh, vh, tables, lens, rows=rows, **args)
         return time.perf_counter() - t0
 
+    # as many sequences as fit in target_s; if the whole batch is faster than
+    # that, the whole batch repeated until about target_s have passed
     t1 = run(1)
     nseq = int(max(1, min(len(lens), target_s / max(t1, 1e-6))))
     t = run(nseq)
-    nbytes = int(lens[:nseq].sum()) * w.num_kv_heads * w.head_dim * 2 * eb
+    reps = 1
+    while t < 0.8 * target_s:
+        t += run(nseq)
+        reps += 1
+    nbytes = reps * int(lens[:nseq].sum()) * w.num_kv_heads * w.head_dim * 2 * eb
     return {"value": round(nbytes / t / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{nseq} of {len(lens)} sequences ({int(lens[:nseq].sum())} tokens, all "
-                      f"{w.num_q_heads} q heads) of the last timed step, fp64 C oracle, "
-                      f"{t:.1f} s"}
+                      f"{w.num_q_heads} q heads) of the last timed step, {reps} pass(es), fp64 C "
+                      f"oracle, {t:.1f} s"}
 
 
 if __name__ == "__main__":

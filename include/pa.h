@@ -225,7 +225,8 @@ size_t pa_decode_workspace_bytes(const pa_kv_desc *desc, int32_t num_seqs, int32
  *     multiple of block_size: each (sequence, KV head) is split into chunks
  *     of that many tokens whose partial softmax states are merged by a second
  *     kernel.  The partitioned modes need `workspace` (device, at least
- *     pa_decode_workspace_bytes(...) bytes, no initial contents required).
+ *     pa_decode_workspace_bytes(...) bytes, no initial contents required;
+ *     two launches that may run at the same time must not share one).
  * Accumulation is fp32; out is rounded to nearest even. */
 pa_status pa_decode(const void *q, const void *k_cache, const void *v_cache,
                     const int32_t *block_tables, int32_t max_blocks_per_seq,
@@ -234,13 +235,14 @@ pa_status pa_decode(const void *q, const void *k_cache, const void *v_cache,
                     size_t workspace_bytes, int32_t partition_size, const pa_kv_desc *desc,
                     void *stream);
 
-/* The two launches of a partitioned pa_decode, callable one at a time (same
- * arguments as pa_decode; partition_size must be > 0 and `workspace` as for
+/* A partitioned pa_decode as two launches (same arguments as pa_decode;
+ * partition_size must not be PA_PARTITION_NONE and `workspace` as for
  * pa_decode).  pa_decode_partials runs the per-partition kernel and leaves
  * each partition's softmax state (running max, sum, unnormalised output) in
  * the workspace; pa_decode_merge combines them into `out`.  Issued in this
- * order on one stream they compute exactly what pa_decode computes; a caller
- * may time or schedule the two separately. */
+ * order on one stream they compute what pa_decode computes, bit for bit (it
+ * launches the same two kernels); a caller may time or schedule the two
+ * separately. */
 pa_status pa_decode_partials(const void *q, const void *k_cache, const void *v_cache,
                              const int32_t *block_tables, int32_t max_blocks_per_seq,
                              const int32_t *seq_lens, int32_t num_seqs, int32_t max_seq_len,

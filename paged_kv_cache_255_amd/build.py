@@ -26,9 +26,12 @@ HOST_HIP_API = ["api.cpp"]           # host code that calls the HIP runtime
 HOST_ONLY = ["pool.cpp", "errors.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC, "-Wall"]
-# Packed-fp32 VALU instructions are kept out of the device code.
+# Packed-fp32 VALU instructions are kept out of the device code.  MFMA
+# accumulators stay in ordinary VGPRs: the decode loop rescales them with
+# VALU ops, which cannot read AGPRs, so AGPR accumulators cost a copy of
+# every accumulator per block.
 DEVICE_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
-                "-packed-fp32-ops", "-munsafe-fp-atomics"]
+                "-packed-fp32-ops", "-munsafe-fp-atomics", "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def _hipcc():

@@ -193,8 +193,7 @@ struct MfmaWave {
         for (int r = 0; r < 4; ++r)
             x[r] = (4 * grp + r < valid) ? s[r] * sc : -INFINITY;
         float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-        bm = fmaxf(bm, shfl_xor(bm, 16));
-        bm = fmaxf(bm, shfl_xor(bm, 32));
+        bm = max_xor32(max_xor16(bm));
         // The reference max m_run moves only when a block's max exceeds it by
         // more than kLazyRescale (log2 units); until then the weights
         // 2^(s - m_run) stay below 2^kLazyRescale and acc, l need no rescale.
@@ -215,7 +214,11 @@ struct MfmaWave {
         l_run += (p[0] + p[1]) + (p[2] + p[3]);
         const u32x2 pp = {M::pack2(p[0], p[1]), M::pack2(p[2], p[3])};
         const A4 pop = __builtin_bit_cast(A4, pp);
-        const bool tail = valid < kBlockSize;
+        // Slots past the end may hold anything (NaN included): their V
+        // values are zeroed, without a branch, so 0 * garbage never reaches acc.
+        const int k = valid - 4 * grp; // tokens of this lane's 4 that are valid
+        const uint32_t keep_x = k >= 2 ? 0xFFFFFFFFu : (k == 1 ? 0x0000FFFFu : 0u);
+        const uint32_t keep_y = k >= 4 ? 0xFFFFFFFFu : (k == 3 ? 0x0000FFFFu : 0u);
 #pragma unroll
         for (int t = 0; t < PV_TILES; ++t) {
             u32x2 vw;
@@ -223,94 +226,79 @@ struct MfmaWave {
                 vw = u32x2{T.v[t][0], T.v[t][1]};
             else
                 vw = u32x2{M::fp8x2(T.v[t][0], false), M::fp8x2(T.v[t][0], true)};
-            if (tail) {
-                // slots past the end may hold anything (NaN included): zero them
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    if (4 * grp + r >= valid) {
-                        const uint32_t keep = (r & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-                        if (r < 2)
-                            vw.x &= keep;
-                        else
-                            vw.y &= keep;
-                    }
-                }
-            }
+            vw.x &= keep_x;
+            vw.y &= keep_y;
             acc[t] = M::pv(__builtin_bit_cast(A4, vw), pop, acc[t]);
         }
     }
 
     // Tokens [t0, t1) of (b, g); t0 is a multiple of 16.  Returns false if a
-    // block-table entry is outside the pool (nothing is read then).
-    __device__ bool run(const DecodeArgs &a, int lane, int32_t b, int32_t g, int32_t t0,
-                        int32_t t1)
+    // block-table entry is outside the pool (that block is not read).
+    __device__ bool run(const DecodeArgs &a, int32_t b, int32_t g, int32_t t0, int32_t t1)
     {
-        const int32_t *table = a.block_tables + (size_t)b * a.max_blocks_per_seq;
+        // The block table does not change while the kernel runs: its entries
+        // are read with scalar loads (one wave-uniform id per block, fetched
+        // two blocks ahead), which keeps them out of the vector-load queue
+        // the tiles stream through.
+        using CI32 = __attribute__((address_space(4))) const int32_t;
+        b = uniform(b);
+        g = uniform(g);
+        const CI32 *table = (const CI32 *)(a.block_tables + (size_t)b * a.max_blocks_per_seq);
         const char *kbase = static_cast<const char *>(a.k_cache) + (size_t)g * TILE_BYTES;
         const char *vbase = static_cast<const char *>(a.v_cache) + (size_t)g * TILE_BYTES;
         const size_t bstride = (size_t)a.num_kv_heads * TILE_BYTES;
         const int32_t jb0 = uniform(t0 / kBlockSize);
-        const int32_t jb1 = uniform((t1 + kBlockSize - 1) / kBlockSize);
+        const int32_t last = uniform((t1 + kBlockSize - 1) / kBlockSize) - 1;
         t1 = uniform(t1);
         const float sc = a.score_scale;
+        const uint32_t nblocks = (uint32_t)a.num_blocks;
 
-        // block ids of up to 64 blocks, one per lane
-        int32_t cb = jb0;
-        int32_t tv = 0;
-        auto fetch_ids = [&](int32_t base) -> bool {
-            cb = base;
-            const bool in = base + lane < jb1;
-            tv = in ? table[base + lane] : 0;
-            // Keep the ids in this register: re-reading an id from memory per
-            // block would wait for every load in flight, the next tile's too.
-            asm volatile("" : "+v"(tv));
-            return !__any(in && (tv < 0 || tv >= a.num_blocks));
-        };
-        if (!fetch_ids(jb0))
-            return false;
-        auto tile_ptrs = [&](int32_t jb, const char *&kt, const char *&vt) -> bool {
-            if (jb - cb >= kWave && !fetch_ids(jb))
-                return false;
-            const int32_t phys = __builtin_amdgcn_readlane(tv, uniform(jb - cb));
-            kt = kbase + (size_t)phys * bstride;
-            vt = vbase + (size_t)phys * bstride;
-            return true;
-        };
+        auto id_of = [&](int32_t jb) -> int32_t { return uniform(table[uniform(min(jb, last))]); };
         auto valid_of = [&](int32_t jb) { return min(kBlockSize, t1 - jb * kBlockSize); };
+        auto load = [&](int32_t phys, Tile &T) {
+            load_tile(kbase + (size_t)phys * bstride, vbase + (size_t)phys * bstride, col, grp, T);
+        };
 
         // Two tiles alternate: while one is computed, the next is in flight.
+        // The loop runs over pairs of blocks and has one exit, at the
+        // bottom; the next load is issued on every path (past the end it
+        // re-reads the last block, an L2 hit).  A load issued on one path
+        // only, or an exit that shares a block with the back edge, would make
+        // the compiler's wait counts assume a shorter queue and wait for the
+        // next tile before the current one is done.  An entry outside the
+        // pool is recorded and block 0 read in its place (the caller turns
+        // the result into NaN), so no early exit is needed either.
         Tile A, B;
-        const char *kt, *vt;
-        int32_t jb = jb0;
-        if (!tile_ptrs(jb, kt, vt))
-            return false;
-        load_tile(kt, vt, col, grp, A);
-        for (;;) {
-            const bool hasB = jb + 1 < jb1;
-            if (hasB) {
-                if (!tile_ptrs(jb + 1, kt, vt))
-                    return false;
-                load_tile(kt, vt, col, grp, B);
-            }
+        const int32_t n = last - jb0 + 1; // blocks in the range, >= 1
+        bool bad = false;
+        auto checked = [&](int32_t id) {
+            const bool out = (uint32_t)id >= nblocks;
+            bad |= out;
+            return out ? 0 : id;
+        };
+        load(checked(id_of(jb0)), A);
+        int32_t idB = id_of(jb0 + 1);
+        for (int32_t i = 0; i + 1 < n; i = uniform(i + 2)) {
+            const int32_t jb = jb0 + i;
+            const int32_t idA = id_of(jb + 2);
+            load(checked(idB), B);
+            __builtin_amdgcn_sched_barrier(0); // B's loads go out before A is waited for
             compute(A, valid_of(jb), sc);
-            if (!hasB)
-                break;
-            const bool hasA = jb + 2 < jb1;
-            if (hasA) {
-                if (!tile_ptrs(jb + 2, kt, vt))
-                    return false;
-                load_tile(kt, vt, col, grp, A);
-            }
+            idB = id_of(jb + 3);
+            load(checked(idA), A);
+            __builtin_amdgcn_sched_barrier(0);
             compute(B, valid_of(jb + 1), sc);
-            if (!hasA)
-                break;
-            jb += 2;
         }
-        return true;
+        if (n & 1)
+            compute(A, valid_of(last), sc); // A holds the last block
+        // Drain the re-read issued past the end (n even), so no load into
+        // these registers is in flight when the next range starts.
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        return !bad;
     }
 
     // The lane groups hold disjoint tokens: sum their shares of l.
-    __device__ void finish() { l_run += shfl_xor(l_run, 16), l_run += shfl_xor(l_run, 32); }
+    __device__ void finish() { l_run = sum_xor32(sum_xor16(l_run)); }
 
     __device__ void write_out(const DecodeArgs &a, int32_t b, int32_t g, int32_t n, bool ok)
     {
@@ -356,13 +344,13 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a, int32_t 
     const Item it = item_of(a, w);
     if (it.valid_len && it.n > 0 && it.t0 >= it.t1)
         return;
-    if (it.valid_len && it.n == 0 && it.p > 0)
-        return;
+    if ((!it.valid_len || it.n == 0) && it.p > 0)
+        return; // the merge writes such rows without reading partial states
     MfmaWave<QT, KT, D> wv(lane);
     wv.start(a, it.b, it.g);
     bool ok = it.valid_len;
     if (ok && it.t1 > it.t0)
-        ok = wv.run(a, lane, it.b, it.g, it.t0, it.t1);
+        ok = wv.run(a, it.b, it.g, it.t0, it.t1);
     wv.finish();
     if (a.partition == 0)
         wv.write_out(a, it.b, it.g, it.n, ok);
@@ -373,7 +361,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a, int32_t 
 // Balanced split: wave i of W takes tiles [i*T/W, (i+1)*T/W) of the list of
 // all (sequence, KV head, block) tiles in that order, T tiles in total.
 template <int QT, int KT, int D>
-__global__ __launch_bounds__(256) void decode_mfma_balanced_kernel(DecodeArgs a, int32_t W)
+__global__ __launch_bounds__(256)
+void decode_mfma_balanced_kernel(DecodeArgs a, int32_t W)
 {
     const int lane = threadIdx.x & 63;
     const int32_t i = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -402,12 +391,13 @@ __global__ __launch_bounds__(256) void decode_mfma_balanced_kernel(DecodeArgs a,
         const int64_t stop = min(x1, seg_end);
         const int32_t je = j + (int32_t)(stop - x);
         wv.start(a, pos.b, g);
-        const bool ok = wv.run(a, lane, pos.b, g, j * kBlockSize, min(je * kBlockSize, pos.n));
+        const bool ok = wv.run(a, pos.b, g, j * kBlockSize, min(je * kBlockSize, pos.n));
         wv.finish();
-        if (j == 0 && je == nb)
+        if (j == 0 && je == nb) {
             wv.write_out(a, pos.b, g, pos.n, ok);
-        else
+        } else {
             wv.write_partial(a, (int64_t)i + (int64_t)pos.b * H + g, ok);
+        }
         x = stop;
         if (x < x1 && g == H - 1)
             pos = next_sequence(a, pos);
@@ -418,12 +408,9 @@ template <int QT, int KT, int D>
 hipError_t launch_mfma(const DecodeArgs &a, int32_t num_items, hipStream_t stream)
 {
     const int grid = (num_items + 3) / 4;
-    if (a.partition == kPartitionBalanced)
-        hipLaunchKernelGGL((decode_mfma_balanced_kernel<QT, KT, D>), dim3(grid), dim3(256), 0,
-                           stream, a, num_items);
-    else
-        hipLaunchKernelGGL((decode_mfma_kernel<QT, KT, D>), dim3(grid), dim3(256), 0, stream, a,
-                           num_items);
+    auto k = a.partition == kPartitionBalanced ? decode_mfma_balanced_kernel<QT, KT, D>
+                                               : decode_mfma_kernel<QT, KT, D>;
+    hipLaunchKernelGGL(k, dim3(grid), dim3(256), 0, stream, a, num_items);
     return hipGetLastError();
 }
 

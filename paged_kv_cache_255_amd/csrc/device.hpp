@@ -132,11 +132,36 @@ __device__ __forceinline__ uint8_t f32_to_e4m3(float x)
     return (uint8_t)(sign | r);
 }
 
+// s_waitcnt operand that waits for vmcnt == 0 and leaves the expcnt and
+// lgkmcnt fields at their maxima (no wait): gfx9 encoding.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 // ---- cross-lane ------------------------------------------------------------
 __device__ __forceinline__ float shfl_xor(float v, int mask)
 {
     return __shfl_xor(v, mask, kWave);
 }
+
+// Max / sum of v over the lane pairs (l, l^16) and (l, l^32), with the
+// gfx950 permlane swaps (plain VALU: no LDS queue, nothing for a wait
+// counter).  Passing v as both operands, one result holds each lane's own row
+// (or half) and the other its partner's, so combining them is the reduction.
+__device__ __forceinline__ f32x2 pair_xor16(float v)
+{
+    const uint32_t u = __float_as_uint(v);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return f32x2{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ f32x2 pair_xor32(float v)
+{
+    const uint32_t u = __float_as_uint(v);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return f32x2{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ float max_xor16(float v) { const f32x2 p = pair_xor16(v); return fmaxf(p.x, p.y); }
+__device__ __forceinline__ float max_xor32(float v) { const f32x2 p = pair_xor32(v); return fmaxf(p.x, p.y); }
+__device__ __forceinline__ float sum_xor16(float v) { const f32x2 p = pair_xor16(v); return p.x + p.y; }
+__device__ __forceinline__ float sum_xor32(float v) { const f32x2 p = pair_xor32(v); return p.x + p.y; }
 
 // Orders this wave's LDS accesses in program order for the compiler; the
 // hardware already executes one wave's LDS instructions in order.

@@ -242,6 +242,31 @@ def test_partitioned_matches_single_pass(kernel):
         assert np.max(np.abs(outs[0] - outs[part])) < 1e-2
 
 
+@pytest.mark.parametrize("cid,kernel,part", [(2, pa.KERNEL_MFMA, pa.PARTITION_BALANCED),
+                                              (2, pa.KERNEL_MFMA, 64),
+                                              (5, pa.KERNEL_MFMA, 16),
+                                              (3, pa.KERNEL_MFMA, 64),
+                                              (2, pa.KERNEL_VALU, 64)])
+def test_two_phase_matches_pa_decode_bits(cid, kernel, part):
+    """pa_decode_partials then pa_decode_merge give pa_decode's bits; covers
+    the per-segment merge (G*D a multiple of 256, configs 2 and 5, up to 94
+    parts per segment) and the per-row merge (config 3, G = 1)."""
+    say(f"[case] two-phase config {cid} kernel {kernel} partition {part}")
+    w = workloads.config(cid, "small")
+    inp = Inputs(w)
+    g = GpuStep(w, 0, inp, partition=part, kernel=kernel)
+    g.append_prefill()
+    g.append_step()
+    one = g.decode().clone()
+    two = torch.full_like(one, 7.0)
+    pa.pa_decode_partials(inp.q, g.k_cache, g.v_cache, g.d_tables, g.d_lens, w.max_seq_len(),
+                          w.scale, g.desc, g.workspace, part, inp.k_scale, inp.v_scale)
+    pa.pa_decode_merge(g.d_lens, g.d_tables.shape[1], w.max_seq_len(), two, g.desc, g.workspace,
+                       part)
+    torch.cuda.synchronize()
+    assert torch.equal(one.view(torch.int16), two.view(torch.int16))
+
+
 def test_zero_length_sequence_gives_zero_row():
     D, NB = 64, 3
     k = torch.randn(NB * 16 * D, device="cuda")

@@ -52,7 +52,7 @@ class Workload:
     num_layers: int = 1
     block_size: int = BLOCK_SIZE
     seed: int = 0
-    partition_size: int = 256  # launch configuration that bench.py times
+    partition_size: int = -1  # launch configuration bench.py times (-1: balanced split)
     shuffle_seeds: list = field(default_factory=list)  # one per layer
 
     @property
@@ -180,11 +180,11 @@ def config(cid, size="full"):
     elif cid == 5:
         # Long context (hyperinfer.ai "Why this matters for long context"):
         # 70B-shaped layer, 64 q heads on 8 KV heads, FP8 E4M3 KV, bf16 q,
-        # 4 sequences at exactly 131072 tokens, 512-token partitions.
+        # 4 sequences at exactly 131072 tokens.
         B, n = (4, 131072) if size == "full" else (2, 1500)
         w = _independent("long-context-fp8-70b", 5, [n - 1] * B, 1.0, num_q_heads=64,
                          num_kv_heads=8, head_dim=128, q_dtype="bf16", kv_dtype="e4m3",
-                         seed=seed, partition_size=512)
+                         seed=seed)
     else:
         raise ValueError(cid)
     w.shuffle_seeds = [seed * 7919 + layer + 1 for layer in range(w.num_layers)]
