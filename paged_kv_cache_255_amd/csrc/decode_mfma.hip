@@ -372,16 +372,14 @@ void decode_mfma_balanced_kernel(DecodeArgs a, int32_t W)
 
     // T, the number of runs (never more than tiles, so no run is empty), and
     // the first segment of this wave's run
-    const int64_t T = tiles_before(a, lane, a.num_seqs);
-    const int32_t runs = effective_runs(T, W);
-    if (i >= runs)
+    const RunStart rs = run_start(a, lane, i, W);
+    if (i >= rs.runs)
         return;
-    const int64_t x0 = (int64_t)i * T / runs;
-    const int64_t x1 = (int64_t)(i + 1) * T / runs;
-    SeqPos pos = locate_tile(a, lane, x0);
+    const int64_t x1 = rs.x1;
+    SeqPos pos = rs.pos;
 
     MfmaWave<QT, KT, D> wv(lane);
-    int64_t x = x0;
+    int64_t x = rs.x0;
     while (x < x1) {
         const int32_t nb = blocks_of(pos.n);
         const int64_t local = x - pos.first_tile;

@@ -68,7 +68,7 @@ __device__ __forceinline__ void merge_segment_s(const DecodeArgs &a, int32_t b, 
                                                 int64_t w0, int64_t nparts, int lane)
 {
     using TQ = typename Store<QT>::T;
-    constexpr int CH = 16 / S; // parts per batch: 16 x 3 loads in flight per lane
+    constexpr int CH = 32 / S; // parts per batch: 32 x 3 loads in flight per lane
     int hs[S];
     float M[S], L[S];
     f32x4 acc[S];
@@ -178,9 +178,10 @@ __global__ __launch_bounds__(64) void merge_kernel(DecodeArgs a)
     // slots w0 .. w0 + nparts - 1 hold this segment's partial states
     int64_t w0, nparts;
     if (a.partition == kPartitionBalanced) {
-        const int64_t T = tiles_before(a, lane, a.num_seqs);
+        const TileCounts tc = tile_counts(a, lane, b);
+        const int64_t T = tc.total;
         const int32_t R = effective_runs(T, a.waves);
-        const int64_t S0 = tiles_before(a, lane, b) + (int64_t)g * blocks_of(n);
+        const int64_t S0 = tc.before + (int64_t)g * blocks_of(n);
         const int64_t S1 = S0 + blocks_of(n);
         const int64_t i0 = run_of_tile(S0, T, R);
         const int64_t i1 = run_of_tile(S1 - 1, T, R);
@@ -214,9 +215,10 @@ __global__ __launch_bounds__(64) void merge_segment_kernel(DecodeArgs a)
     }
     int64_t w0, nparts;
     if (a.partition == kPartitionBalanced) {
-        const int64_t T = tiles_before(a, lane, a.num_seqs);
+        const TileCounts tc = tile_counts(a, lane, b);
+        const int64_t T = tc.total;
         const int32_t R = effective_runs(T, a.waves);
-        const int64_t S0 = tiles_before(a, lane, b) + (int64_t)g * blocks_of(n);
+        const int64_t S0 = tc.before + (int64_t)g * blocks_of(n);
         const int64_t i0 = run_of_tile(S0, T, R);
         const int64_t i1 = run_of_tile(S0 + blocks_of(n) - 1, T, R);
         if (i0 == i1)

@@ -84,6 +84,26 @@ __device__ __forceinline__ int64_t tiles_before(const DecodeArgs &a, int lane, i
     return wave_sum(t) * a.num_kv_heads;
 }
 
+// Tiles of sequences [0, b) and of all sequences, from one pass over the
+// lengths (each lane sums its own sequences; the two sums are wave
+// reductions).
+struct TileCounts {
+    int64_t before; // tiles of sequences [0, b)
+    int64_t total;  // T
+};
+
+__device__ __forceinline__ TileCounts tile_counts(const DecodeArgs &a, int lane, int32_t b)
+{
+    int64_t before = 0, total = 0;
+    for (int32_t c = 0; c < a.num_seqs; c += kWave) {
+        const int32_t s = c + lane;
+        const int64_t t = (s < a.num_seqs) ? split_blocks(a, a.seq_lens[s]) : 0;
+        total += t;
+        before += (s < b) ? t : 0;
+    }
+    return TileCounts{wave_sum(before) * a.num_kv_heads, wave_sum(total) * a.num_kv_heads};
+}
+
 struct SeqPos {
     int32_t b;          // sequence
     int32_t n;          // its length
@@ -114,6 +134,56 @@ __device__ __forceinline__ SeqPos locate_tile(const DecodeArgs &a, int lane, int
     return SeqPos{a.num_seqs, 0, carry};
 }
 
+// Runs the balanced split cuts T tiles into: the launch's W waves, but no
+// more than T so that every run holds at least one tile.
+__device__ __forceinline__ int32_t effective_runs(int64_t T, int32_t W)
+{
+    return (int32_t)(T < (int64_t)W ? T : (int64_t)W);
+}
+
+// Where run i of the balanced split starts: T, the number of runs, the run's
+// tiles [x0, x1) and the sequence holding x0.  Up to 64 sequences this is one
+// pass over the lengths (one load per lane, one scan, one ballot); beyond,
+// the chunked count and search above.
+struct RunStart {
+    int64_t T;
+    int32_t runs;
+    int64_t x0, x1;
+    SeqPos pos;
+};
+
+__device__ __forceinline__ RunStart run_start(const DecodeArgs &a, int lane, int32_t i,
+                                              int32_t W)
+{
+    RunStart r;
+    if (a.num_seqs <= kWave) {
+        const bool in = lane < a.num_seqs;
+        const int32_t n = in ? a.seq_lens[lane] : 0;
+        const int64_t tiles = in ? (int64_t)split_blocks(a, n) * a.num_kv_heads : 0;
+        const int64_t incl = wave_incl_scan(tiles, lane);
+        r.T = readlane64(incl, kWave - 1);
+        r.runs = effective_runs(r.T, W);
+        if (i >= r.runs)
+            return r;
+        r.x0 = (int64_t)i * r.T / r.runs;
+        r.x1 = (int64_t)(i + 1) * r.T / r.runs;
+        const uint64_t hit = __ballot(in && incl > r.x0);
+        const int k = __ffsll((unsigned long long)hit) - 1; // x0 < T: some lane hits
+        r.pos.b = k;
+        r.pos.n = __builtin_amdgcn_readlane(n, k);
+        r.pos.first_tile = readlane64(incl - tiles, k);
+        return r;
+    }
+    r.T = tiles_before(a, lane, a.num_seqs);
+    r.runs = effective_runs(r.T, W);
+    if (i >= r.runs)
+        return r;
+    r.x0 = (int64_t)i * r.T / r.runs;
+    r.x1 = (int64_t)(i + 1) * r.T / r.runs;
+    r.pos = locate_tile(a, lane, r.x0);
+    return r;
+}
+
 // The next sequence after p that has tiles.
 __device__ __forceinline__ SeqPos next_sequence(const DecodeArgs &a, SeqPos p)
 {
@@ -124,13 +194,6 @@ __device__ __forceinline__ SeqPos next_sequence(const DecodeArgs &a, SeqPos p)
         ++q.b;
     q.n = q.b < a.num_seqs ? uniform_load(a.seq_lens + q.b) : 0;
     return q;
-}
-
-// Runs the balanced split cuts T tiles into: the launch's W waves, but no
-// more than T so that every run holds at least one tile.
-__device__ __forceinline__ int32_t effective_runs(int64_t T, int32_t W)
-{
-    return (int32_t)(T < (int64_t)W ? T : (int64_t)W);
 }
 
 // Run holding tile x when T tiles are cut into R runs [i*T/R, (i+1)*T/R)
