@@ -8,8 +8,9 @@ over a pool 1.25x the size they need (dev.to, "Why LLMs Run Out of VRAM...",
 §2 Example 2 and §4).
 
 A timed step is the whole device-side hot path for the batch:
-pa_cache_append of the new token's K/V, then pa_decode (decode kernel, then
-the merge kernel in the partitioned modes).  Inputs are resident in HBM when
+pa_decode_append, which appends the new token's K/V and decodes in one
+kernel (then the merge kernel in the partitioned modes); --separate-append
+times pa_cache_append + pa_decode instead.  Inputs are resident in HBM when
 timing starts, the per-step metadata included: the host allocator
 (pa_seq_append_slots_batch: one new slot per sequence, a new block at every
 16th token; pa_export_block_tables) runs for every step first and the
@@ -62,6 +63,9 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain device-to-device copies of 1 GiB (calibrates the HBM "
                          "byte counters a profiler reports) and exit")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="a step calls pa_cache_append then pa_decode instead of "
+                         "pa_decode_append")
     ap.add_argument("--upload-per-step", action="store_true",
                     help="run the host allocator and copy the step's metadata inside each "
                          "timed step")
@@ -178,6 +182,8 @@ def main():
     scale = w.scale
     meta_base = d_meta.data_ptr()
 
+    separate = args.separate_append
+
     def step(i):
         if upload:
             buf = i % NBUF
@@ -193,9 +199,14 @@ def main():
         r = i % R
         for layer in range(L):
             kcp, vcp = kc_p[layer * R + r]
-            rc = lib.pa_cache_append(kn, vn, kcp, vcp, slots_p, B, dref, ks, vs, s_h)
-            rc |= lib.pa_decode(qp, kcp, vcp, tables_p, maxb, lens_p, B, max_len, scale, ks,
-                                vs, op, ws_p, ws_bytes, partition, dref, s_h)
+            if separate:
+                rc = lib.pa_cache_append(kn, vn, kcp, vcp, slots_p, B, dref, ks, vs, s_h)
+                rc |= lib.pa_decode(qp, kcp, vcp, tables_p, maxb, lens_p, B, max_len, scale,
+                                    ks, vs, op, ws_p, ws_bytes, partition, dref, s_h)
+            else:
+                rc = lib.pa_decode_append(qp, kn, vn, slots_p, kcp, vcp, tables_p, maxb, lens_p,
+                                          B, max_len, scale, ks, vs, op, ws_p, ws_bytes,
+                                          partition, dref, s_h)
             if rc:
                 raise RuntimeError("launch failed: " + pa.pa_last_error())
 
@@ -298,6 +309,7 @@ def main():
             "kernel": kname,
             "cache_replicas": R,
             "metadata": "uploaded per step" if upload else "resident (all steps)",
+            "step_calls": ("pa_cache_append + pa_decode" if separate else "pa_decode_append"),
             "parallelism": "none (1 GPU)",
         },
         "roofline": {

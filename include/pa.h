@@ -235,6 +235,30 @@ pa_status pa_decode(const void *q, const void *k_cache, const void *v_cache,
                     size_t workspace_bytes, int32_t partition_size, const pa_kv_desc *desc,
                     void *stream);
 
+/* One decode step with the step's append folded in: the same result, cache
+ * bytes and output bits as
+ *   pa_cache_append(k_new, v_new, k_cache, v_cache, slot_mapping, num_seqs, ...)
+ *   pa_decode(q, k_cache, v_cache, ...)
+ * issued in that order, with one launch fewer ([devto] §1: each step appends
+ * the new token's K and V, then attends over all cached tokens, itself
+ * included).  Token b of k_new / v_new ([num_seqs][Hkv][D], q's dtype) is
+ * sequence b's token at position seq_lens[b] - 1; slot_mapping[b] must be
+ * that position's cache slot (what pa_seq_append_slots returned for it) or
+ * negative (nothing is written and the cache slot is read as it is).  With
+ * the MFMA kernel the wave that reads a sequence's last block writes the
+ * token there first; a row whose slot is neither negative nor that slot is
+ * written as NaN, and its token is not stored; a sequence whose length is out
+ * of range stores nothing.  With the VALU kernel the append is a separate
+ * launch.  Other arguments and errors as for pa_decode; k_scale / v_scale
+ * are also the FP8 quantisation scales as in pa_cache_append. */
+pa_status pa_decode_append(const void *q, const void *k_new, const void *v_new,
+                           const int32_t *slot_mapping, void *k_cache, void *v_cache,
+                           const int32_t *block_tables, int32_t max_blocks_per_seq,
+                           const int32_t *seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                           float scale, float k_scale, float v_scale, void *out, void *workspace,
+                           size_t workspace_bytes, int32_t partition_size,
+                           const pa_kv_desc *desc, void *stream);
+
 /* A partitioned pa_decode as two launches (same arguments as pa_decode;
  * partition_size must not be PA_PARTITION_NONE and `workspace` as for
  * pa_decode).  pa_decode_partials runs the per-partition kernel and leaves

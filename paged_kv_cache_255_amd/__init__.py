@@ -89,6 +89,9 @@ _SIGS = {
                                           _I32, ctypes.POINTER(KvDesc), _P]),
     "pa_decode_merge": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _P, ctypes.c_size_t, _I32,
                                        ctypes.POINTER(KvDesc), _P]),
+    "pa_decode_append": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _P, _I32, _I32,
+                                        ctypes.c_float, ctypes.c_float, ctypes.c_float, _P, _P,
+                                        ctypes.c_size_t, _I32, _P, _P]),
     "pa_last_error": (ctypes.c_char_p, []),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -280,6 +283,37 @@ def pa_decode(q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale, o
                           block_tables.shape[1], _addr(seq_lens), B, max_seq_len, scale,
                           k_scale, v_scale, _addr(out), _addr(workspace), ws_bytes,
                           partition_size, ctypes.byref(desc), _stream(stream)), "pa_decode")
+
+
+def pa_decode_append(q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables, seq_lens,
+                     max_seq_len, scale, out, desc, k_scale=1.0, v_scale=1.0, workspace=None,
+                     partition_size=PARTITION_NONE, stream=None):
+    B = seq_lens.numel()
+    qb, kb = DTYPE_BYTES[desc.q_dtype], DTYPE_BYTES[desc.kv_dtype]
+    qrow = desc.num_q_heads * desc.head_dim
+    krow = desc.num_kv_heads * desc.head_dim
+    cache_bytes = desc.num_blocks * desc.block_size * desc.num_kv_heads * desc.head_dim * kb
+    _check_tensor(q, "q", B * qrow * qb)
+    _check_tensor(out, "out", B * qrow * qb)
+    _check_tensor(k_new, "k_new", B * krow * qb)
+    _check_tensor(v_new, "v_new", B * krow * qb)
+    _check_tensor(slot_mapping, "slot_mapping", B * 4)
+    for t, nm in [(k_cache, "k_cache"), (v_cache, "v_cache")]:
+        _check_tensor(t, nm, cache_bytes)
+    _check_tensor(seq_lens, "seq_lens", B * 4)
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [num_seqs][max_blocks_per_seq]")
+    _check_tensor(block_tables, "block_tables")
+    ws_bytes = 0
+    if workspace is not None:
+        _check_tensor(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(_lib.pa_decode_append(_addr(q), _addr(k_new), _addr(v_new), _addr(slot_mapping),
+                                 _addr(k_cache), _addr(v_cache), _addr(block_tables),
+                                 block_tables.shape[1], _addr(seq_lens), B, max_seq_len, scale,
+                                 k_scale, v_scale, _addr(out), _addr(workspace), ws_bytes,
+                                 partition_size, ctypes.byref(desc), _stream(stream)),
+           "pa_decode_append")
 
 
 def pa_decode_partials(q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale, desc,

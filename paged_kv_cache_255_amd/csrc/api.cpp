@@ -157,12 +157,19 @@ namespace {
 
 enum Phase { kAll, kPartials, kMerge };
 
+// The step's new tokens when pa_decode_append is the caller (else all null).
+struct NewTokens {
+    const void *k = nullptr;
+    const void *v = nullptr;
+    const int32_t *slots = nullptr;
+};
+
 pa_status decode_impl(Phase phase, const void *q, const void *k_cache, const void *v_cache,
                       const int32_t *block_tables, int32_t max_blocks_per_seq,
                       const int32_t *seq_lens, int32_t num_seqs, int32_t max_seq_len,
                       float scale, float k_scale, float v_scale, void *out, void *workspace,
                       size_t workspace_bytes, int32_t partition_size, const pa_kv_desc *desc,
-                      void *stream)
+                      void *stream, const NewTokens &nt = NewTokens{})
 {
     pa_status st = check_desc(desc);
     if (st != PA_OK)
@@ -211,6 +218,18 @@ pa_status decode_impl(Phase phase, const void *q, const void *k_cache, const voi
     a.max_parts = balanced ? 1 : parts_for(max_seq_len, partition_size);
     a.score_scale = scale * k_scale * kLog2e;
     a.v_scale = v_scale;
+    const bool appending = nt.slots != nullptr;
+    if (appending) {
+        if (!nt.k || !nt.v)
+            return fail(PA_ERR_INVALID_ARG, "null pointer");
+        if (nt.k == out || nt.v == out)
+            return fail(PA_ERR_INVALID_ARG, "out may not alias the new tokens");
+        a.k_new = nt.k;
+        a.v_new = nt.v;
+        a.slots = nt.slots;
+        a.k_inv = desc->kv_dtype == PA_FP8_E4M3 ? 1.0f / k_scale : 1.f;
+        a.v_inv = desc->kv_dtype == PA_FP8_E4M3 ? 1.0f / v_scale : 1.f;
+    }
 
     int kernel = desc->kernel;
     if (kernel == PA_KERNEL_AUTO)
@@ -241,6 +260,19 @@ pa_status decode_impl(Phase phase, const void *q, const void *k_cache, const voi
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
+    if (appending) {
+        if (desc->kv_dtype == PA_FP8_E4M3 && (k_scale == INFINITY || v_scale == INFINITY))
+            return fail(PA_ERR_INVALID_ARG, "FP8 scales must be positive and finite");
+        if (kernel == PA_KERNEL_MFMA) {
+            a.append = 1; // the decode kernel writes the tokens itself
+        } else {
+            e = launch_append(nt.k, nt.v, const_cast<void *>(k_cache), const_cast<void *>(v_cache),
+                              nt.slots, num_seqs, desc->num_kv_heads, desc->num_blocks, D,
+                              desc->q_dtype, desc->kv_dtype, a.k_inv, a.v_inv, s);
+            if (e != hipSuccess)
+                return hip_fail(e, "cache append launch");
+        }
+    }
     if (phase != kMerge) {
         if (kernel == PA_KERNEL_MFMA) {
             if (!mfma_supports(desc->q_dtype, desc->kv_dtype, D, G))
@@ -279,6 +311,25 @@ pa_status pa_decode(const void *q, const void *k_cache, const void *v_cache,
     return decode_impl(kAll, q, k_cache, v_cache, block_tables, max_blocks_per_seq, seq_lens,
                        num_seqs, max_seq_len, scale, k_scale, v_scale, out, workspace,
                        workspace_bytes, partition_size, desc, stream);
+}
+
+pa_status pa_decode_append(const void *q, const void *k_new, const void *v_new,
+                           const int32_t *slot_mapping, void *k_cache, void *v_cache,
+                           const int32_t *block_tables, int32_t max_blocks_per_seq,
+                           const int32_t *seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                           float scale, float k_scale, float v_scale, void *out, void *workspace,
+                           size_t workspace_bytes, int32_t partition_size,
+                           const pa_kv_desc *desc, void *stream)
+{
+    if (num_seqs > 0 && !slot_mapping)
+        return fail(PA_ERR_INVALID_ARG, "null pointer");
+    NewTokens nt;
+    nt.k = k_new;
+    nt.v = v_new;
+    nt.slots = slot_mapping;
+    return decode_impl(kAll, q, k_cache, v_cache, block_tables, max_blocks_per_seq, seq_lens,
+                       num_seqs, max_seq_len, scale, k_scale, v_scale, out, workspace,
+                       workspace_bytes, partition_size, desc, stream, nt);
 }
 
 pa_status pa_decode_partials(const void *q, const void *k_cache, const void *v_cache,

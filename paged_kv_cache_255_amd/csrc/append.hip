@@ -1,15 +1,7 @@
-// Cache append: scatter each new token's K and V into its slot.
-//
-// dev.to, "Why LLMs Run Out of VRAM: KV Cache Fragmentation and How
-// PagedAttention Fixes It", §1: every step appends the new token's K and V to
-// the cache; §4: the slot is a place inside a physical block; §6 "Enable FP8
-// KV Cache": the cache may hold 1-byte FP8 values.  hyperinfer.ai, "KV cache &
-// paged attention deep dive", "KV quantization cuts memory in half".
-//
-// One wave per (token, KV head); lane d writes dims d, d + 64, ...  The K row
-// of a slot is contiguous ([block][head][token][dim]); the V column is strided
-// by the block size ([block][head][dim][token]).
-#include "device.hpp"
+// Cache append kernel: one wave per (token, KV head) writes that token's K
+// row and V column into its slot (store_token, append.hpp).  A slot outside
+// [0, num_blocks * block_size) is skipped.
+#include "append.hpp"
 
 namespace pa {
 
@@ -20,7 +12,6 @@ __global__ __launch_bounds__(256) void append_kernel(const void *k, const void *
                                                      int32_t num_blocks, float k_inv, float v_inv)
 {
     using TQ = typename Store<QT>::T;
-    using TK = typename Store<KT>::T;
     const int lane = threadIdx.x & 63;
     const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (w >= (int64_t)num_tokens * num_kv_heads)
@@ -30,23 +21,10 @@ __global__ __launch_bounds__(256) void append_kernel(const void *k, const void *
     const int32_t slot = slots[t];
     if (slot < 0 || (int64_t)slot >= (int64_t)num_blocks * kBlockSize)
         return;
-    const int32_t blk = slot / kBlockSize;
-    const int32_t off = slot % kBlockSize;
     const TQ *ks = static_cast<const TQ *>(k) + ((size_t)t * num_kv_heads + g) * D;
     const TQ *vs = static_cast<const TQ *>(v) + ((size_t)t * num_kv_heads + g) * D;
-    TK *kd = static_cast<TK *>(k_cache) + (((size_t)blk * num_kv_heads + g) * kBlockSize + off) * D;
-    TK *vd = static_cast<TK *>(v_cache) + ((size_t)blk * num_kv_heads + g) * D * kBlockSize + off;
-#pragma unroll
-    for (int i = 0; i < D / kWave; ++i) {
-        const int d = i * kWave + lane;
-        if constexpr (KT == PA_FP8_E4M3) {
-            kd[d] = f32_to_e4m3(to_f32<QT>(ks[d]) * k_inv);
-            vd[(size_t)d * kBlockSize] = f32_to_e4m3(to_f32<QT>(vs[d]) * v_inv);
-        } else {
-            kd[d] = ks[d];
-            vd[(size_t)d * kBlockSize] = vs[d];
-        }
-    }
+    store_token<QT, KT, D>(ks, vs, k_cache, v_cache, slot / kBlockSize, slot % kBlockSize, g,
+                           num_kv_heads, k_inv, v_inv, lane);
 }
 
 template <int QT, int KT>

@@ -1,0 +1,45 @@
+// One token's K row and V column for one KV head, written into its cache slot
+// by one wave: the cache append, shared by the append kernel and the decode
+// launch that appends the step's token itself (so both write the same bytes).
+//
+// dev.to, "Why LLMs Run Out of VRAM: KV Cache Fragmentation and How
+// PagedAttention Fixes It", §1: every step appends the new token's K and V to
+// the cache; §4: the slot is a place inside a physical block; §6 "Enable FP8
+// KV Cache": the cache may hold 1-byte FP8 values.  hyperinfer.ai, "KV cache &
+// paged attention deep dive", "KV quantization cuts memory in half".
+//
+// Lane d writes dims d, d + 64, ...  The K row of a slot is contiguous
+// ([block][head][token][dim]); the V column is strided by the block size
+// ([block][head][dim][token]).  FP8: the E4M3 code of x * inv (inv = 1/scale
+// in fp32), nearest even, saturating.
+#pragma once
+
+#include "device.hpp"
+
+namespace pa {
+
+template <int QT, int KT, int D>
+__device__ __forceinline__ void store_token(const typename Store<QT>::T *ks,
+                                            const typename Store<QT>::T *vs, void *k_cache,
+                                            void *v_cache, int32_t blk, int32_t off, int32_t g,
+                                            int32_t num_kv_heads, float k_inv, float v_inv,
+                                            int lane)
+{
+    using TK = typename Store<KT>::T;
+    TK *kd = static_cast<TK *>(k_cache) +
+             (((size_t)blk * num_kv_heads + g) * kBlockSize + off) * D;
+    TK *vd = static_cast<TK *>(v_cache) + ((size_t)blk * num_kv_heads + g) * D * kBlockSize + off;
+#pragma unroll
+    for (int i = 0; i < D / kWave; ++i) {
+        const int d = i * kWave + lane;
+        if constexpr (KT == PA_FP8_E4M3) {
+            kd[d] = f32_to_e4m3(to_f32<QT>(ks[d]) * k_inv);
+            vd[(size_t)d * kBlockSize] = f32_to_e4m3(to_f32<QT>(vs[d]) * v_inv);
+        } else {
+            kd[d] = ks[d];
+            vd[(size_t)d * kBlockSize] = vs[d];
+        }
+    }
+}
+
+} // namespace pa

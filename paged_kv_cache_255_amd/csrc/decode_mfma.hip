@@ -30,6 +30,7 @@
 //       into W equal runs, one per wave (W = the waves the GPU holds at
 //       once); a run that covers a whole segment writes the output, the
 //       others leave partial states that merge.hip combines.
+#include "append.hpp"
 #include "device.hpp"
 #include "work.hpp"
 
@@ -233,8 +234,11 @@ struct MfmaWave {
     }
 
     // Tokens [t0, t1) of (b, g); t0 is a multiple of 16.  Returns false if a
-    // block-table entry is outside the pool (that block is not read).
-    __device__ bool run(const DecodeArgs &a, int32_t b, int32_t g, int32_t t0, int32_t t1)
+    // block-table entry is outside the pool (that block is not read), or if
+    // the step's token is to be appended here (t1 is the sequence's length)
+    // and its slot is not the cache slot of position t1 - 1.
+    __device__ bool run(const DecodeArgs &a, int32_t b, int32_t g, int32_t t0, int32_t t1,
+                        bool append_here)
     {
         // The block table does not change while the kernel runs: its entries
         // are read with scalar loads (one wave-uniform id per block, fetched
@@ -276,6 +280,29 @@ struct MfmaWave {
             bad |= out;
             return out ? 0 : id;
         };
+        if (append_here) {
+            // The step's token (position t1 - 1) goes into the last block
+            // before any of the range is read.  The last block's loads are
+            // issued only after an earlier block's wait, which covers these
+            // older stores; a range of one or two blocks waits here instead.
+            const int32_t slot = uniform_load(a.slots + b);
+            const int32_t id_last = id_of(last);
+            const int32_t off = (t1 - 1) % kBlockSize;
+            if (slot >= 0) {
+                if ((uint32_t)id_last >= nblocks || slot != id_last * kBlockSize + off) {
+                    bad = true;
+                } else {
+                    const size_t row = ((size_t)b * a.num_kv_heads + g) * D;
+                    store_token<QT, KT, D>(static_cast<const TQ *>(a.k_new) + row,
+                                           static_cast<const TQ *>(a.v_new) + row,
+                                           const_cast<void *>(a.k_cache),
+                                           const_cast<void *>(a.v_cache), id_last, off, g,
+                                           a.num_kv_heads, a.k_inv, a.v_inv, col + 16 * grp);
+                    if (n < 3)
+                        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+                }
+            }
+        }
         load(checked(id_of(jb0)), A);
         int32_t idB = id_of(jb0 + 1);
         for (int32_t i = 0; i + 1 < n; i = uniform(i + 2)) {
@@ -350,7 +377,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a, int32_t 
     wv.start(a, it.b, it.g);
     bool ok = it.valid_len;
     if (ok && it.t1 > it.t0)
-        ok = wv.run(a, it.b, it.g, it.t0, it.t1);
+        ok = wv.run(a, it.b, it.g, it.t0, it.t1, a.append && it.t1 == it.n);
     wv.finish();
     if (a.partition == 0)
         wv.write_out(a, it.b, it.g, it.n, ok);
@@ -389,7 +416,8 @@ void decode_mfma_balanced_kernel(DecodeArgs a, int32_t W)
         const int64_t stop = min(x1, seg_end);
         const int32_t je = j + (int32_t)(stop - x);
         wv.start(a, pos.b, g);
-        const bool ok = wv.run(a, pos.b, g, j * kBlockSize, min(je * kBlockSize, pos.n));
+        const bool ok = wv.run(a, pos.b, g, j * kBlockSize, min(je * kBlockSize, pos.n),
+                               a.append && je == nb);
         wv.finish();
         if (j == 0 && je == nb) {
             wv.write_out(a, pos.b, g, pos.n, ok);

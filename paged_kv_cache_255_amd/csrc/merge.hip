@@ -68,7 +68,7 @@ __device__ __forceinline__ void merge_segment_s(const DecodeArgs &a, int32_t b, 
                                                 int64_t w0, int64_t nparts, int lane)
 {
     using TQ = typename Store<QT>::T;
-    constexpr int CH = 32 / S; // parts per batch: 32 x 3 loads in flight per lane
+    constexpr int CH = 16 / S; // parts per batch: 16 x 3 loads in flight per lane
     int hs[S];
     float M[S], L[S];
     f32x4 acc[S];

@@ -28,6 +28,14 @@ struct DecodeArgs {
     int64_t num_slots;         // partial-state slots in the workspace
     float score_scale;         // scale * k_scale * log2(e): scores in log2 units
     float v_scale;
+    // Appending decode: the step's new token of sequence b (k_new, v_new:
+    // [num_seqs][Hkv][D] in the q dtype) goes to slot slots[b], written by
+    // the wave whose range holds the sequence's last block.
+    int32_t append;
+    const void *k_new;
+    const void *v_new;
+    const int32_t *slots;
+    float k_inv, v_inv;        // FP8 cache: 1 / k_scale, 1 / v_scale
 };
 
 constexpr int32_t kPartitionBalanced = -1; // PA_PARTITION_BALANCED

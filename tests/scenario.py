@@ -97,6 +97,18 @@ class GpuStep:
         pa.pa_cache_append(i.k_new, i.v_new, self.k_cache, self.v_cache, slots, self.desc,
                            i.k_scale, i.v_scale)
 
+    def decode_append(self, out=None, slots=None):
+        """pa_decode_append with the step's token: append and decode in one call."""
+        i = self.inputs
+        out = self.out if out is None else out
+        if slots is None:
+            slots = torch.from_numpy(np.ascontiguousarray(self.step_slots)).cuda()
+        pa.pa_decode_append(i.q, i.k_new, i.v_new, slots, self.k_cache, self.v_cache,
+                            self.d_tables, self.d_lens, self.w.max_seq_len(), self.w.scale, out,
+                            self.desc, i.k_scale, i.v_scale, workspace=self.workspace,
+                            partition_size=self.partition)
+        return out
+
     def decode(self, out=None):
         i = self.inputs
         out = self.out if out is None else out

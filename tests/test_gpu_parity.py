@@ -267,6 +267,66 @@ def test_two_phase_matches_pa_decode_bits(cid, kernel, part):
     assert torch.equal(one.view(torch.int16), two.view(torch.int16))
 
 
+APPEND_CASES = [(2, pa.KERNEL_MFMA, pa.PARTITION_BALANCED), (2, pa.KERNEL_MFMA, 64),
+                (2, pa.KERNEL_MFMA, 0), (2, pa.KERNEL_VALU, 64), (4, pa.KERNEL_MFMA, 16),
+                (5, pa.KERNEL_MFMA, pa.PARTITION_BALANCED), (3, pa.KERNEL_MFMA, 64)]
+
+
+@pytest.mark.parametrize("cid,kernel,part", APPEND_CASES)
+def test_decode_append_matches_append_then_decode(cid, kernel, part):
+    """pa_decode_append writes the same cache bytes and gives the same output
+    bits as pa_cache_append followed by pa_decode (bf16, fp16 and FP8 caches;
+    both kernels; single pass, fixed partitions and the balanced split)."""
+    say(f"[case] decode_append config {cid} kernel {kernel} partition {part}")
+    w = workloads.config(cid, "small")
+    inp = Inputs(w)
+    ref = GpuStep(w, 0, inp, partition=part, kernel=kernel)
+    ref.append_prefill()
+    ref.append_step()
+    want = ref.decode().clone()
+    got_step = GpuStep(w, 0, inp, partition=part, kernel=kernel)
+    got_step.append_prefill()
+    got = got_step.decode_append(out=torch.full_like(want, 7.0))
+    torch.cuda.synchronize()
+    assert torch.equal(want.view(torch.int16), got.view(torch.int16))
+    assert torch.equal(ref.k_cache.view(torch.uint8), got_step.k_cache.view(torch.uint8))
+    assert torch.equal(ref.v_cache.view(torch.uint8), got_step.v_cache.view(torch.uint8))
+
+
+@pytest.mark.parametrize("kernel,part", [(pa.KERNEL_MFMA, pa.PARTITION_BALANCED),
+                                         (pa.KERNEL_MFMA, 0)])
+def test_decode_append_slot_checks(kernel, part):
+    """A negative slot stores nothing and the row reads the cache as it is; a
+    slot that is not the sequence's last position gives a NaN row and stores
+    nothing; the other rows are unaffected."""
+    say(f"[case] decode_append slot checks kernel {kernel} partition {part}")
+    w = workloads.config(2, "small")
+    inp = Inputs(w)
+    slots = np.ascontiguousarray(GpuStep(w, 0, inp, partition=part).step_slots).copy()
+    skip, wrong = 0, 1
+    slots[skip] = -1
+    slots[wrong] = slots[wrong] + 1 if slots[wrong] % 16 != 15 else slots[wrong] - 1
+    ref = GpuStep(w, 0, inp, partition=part, kernel=kernel)
+    ref.append_prefill()
+    keep = np.ascontiguousarray(ref.step_slots).copy()
+    keep[skip] = -1
+    keep[wrong] = -1
+    i = inp
+    pa.pa_cache_append(i.k_new, i.v_new, ref.k_cache, ref.v_cache,
+                       torch.from_numpy(keep).cuda(), ref.desc, i.k_scale, i.v_scale)
+    want = ref.decode().clone()
+    got_step = GpuStep(w, 0, inp, partition=part, kernel=kernel)
+    got_step.append_prefill()
+    got = got_step.decode_append(out=torch.full_like(want, 7.0),
+                                 slots=torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    assert torch.all(torch.isnan(got[wrong].float()))
+    others = [b for b in range(w.num_seqs) if b != wrong]
+    assert torch.equal(want[others].view(torch.int16), got[others].view(torch.int16))
+    assert torch.equal(ref.k_cache.view(torch.uint8), got_step.k_cache.view(torch.uint8))
+    assert torch.equal(ref.v_cache.view(torch.uint8), got_step.v_cache.view(torch.uint8))
+
+
 def test_zero_length_sequence_gives_zero_row():
     D, NB = 64, 3
     k = torch.randn(NB * 16 * D, device="cuda")
