@@ -30,6 +30,9 @@
 //       into W equal runs, one per wave (W = the waves the GPU holds at
 //       once); a run that covers a whole segment writes the output, the
 //       others leave partial states that merge.hip combines.
+#include <map>
+#include <mutex>
+
 #include "append.hpp"
 #include "device.hpp"
 #include "work.hpp"
@@ -114,6 +117,17 @@ struct MfmaWave {
         uint32_t v[PV_TILES][KE];
     };
 
+    // The step's new token (pa_decode_append), in the cache's storage format
+    // and in tile layout: the K chunks a lane would hold if its column were
+    // the token's row, and the V value of dim 16 t + col.  It replaces the
+    // token's slot in the registers of the last block, so that block's loads
+    // need not wait for the token's own store.
+    struct NewToken {
+        u32x4 k[CH_PER_LANE];
+        uint32_t v[PV_TILES];
+        int tok; // the token's offset inside its block
+    };
+
     int col; // MFMA column: query head within the group
     int grp; // lane group: 4 tokens of S^T, 4 dims of O^T
     A8 qop[QK_MMAS];
@@ -147,6 +161,75 @@ struct MfmaWave {
             acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
         m_run = -INFINITY;
         l_run = 0.f;
+    }
+
+    // Row (b, g) of k_new / v_new into `nt`, converted as the append does.
+    __device__ void load_new_token(const DecodeArgs &a, int32_t b, int32_t g, int tok,
+                                   NewToken &nt) const
+    {
+        const size_t row = ((size_t)b * a.num_kv_heads + g) * D;
+        const TQ *kr = static_cast<const TQ *>(a.k_new) + row;
+        const TQ *vr = static_cast<const TQ *>(a.v_new) + row;
+        nt.tok = tok;
+#pragma unroll
+        for (int j = 0; j < CH_PER_LANE; ++j) {
+            const int c = grp + 4 * j; // chunk of the K row this lane holds
+            if constexpr (KE == 2) {
+                nt.k[j] = load16(kr + c * 8);
+            } else {
+                const u32x4 lo = load16(kr + c * 16);
+                const u32x4 hi = load16(kr + c * 16 + 8);
+                const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+                uint32_t q[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    uint32_t word = 0;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t src = w[(4 * i + e) / 2];
+                        const uint16_t h = (uint16_t)((e & 1) ? (src >> 16) : (src & 0xFFFFu));
+                        const float x = to_f32<QT>(__builtin_bit_cast(TQ, h));
+                        word |= (uint32_t)f32_to_e4m3(x * a.k_inv) << (8 * e);
+                    }
+                    q[i] = word;
+                }
+                nt.k[j] = u32x4{q[0], q[1], q[2], q[3]};
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < PV_TILES; ++t) {
+            const TQ x = vr[16 * t + col];
+            if constexpr (KE == 2)
+                nt.v[t] = __builtin_bit_cast(uint16_t, x);
+            else
+                nt.v[t] = f32_to_e4m3(to_f32<QT>(x) * a.v_inv);
+        }
+    }
+
+    // Puts the new token into tile T (the sequence's last block).
+    __device__ void apply_new_token(Tile &T, const NewToken &nt) const
+    {
+#pragma unroll
+        for (int j = 0; j < CH_PER_LANE; ++j)
+            if (col == nt.tok)
+                T.k[j] = nt.k[j];
+        if (grp != nt.tok / 4)
+            return;
+        const int r = nt.tok % 4; // the token's place among this lane's 4
+#pragma unroll
+        for (int t = 0; t < PV_TILES; ++t) {
+            if constexpr (KE == 2) {
+                const int w = r / 2, sh = 16 * (r % 2);
+                const uint32_t keep = ~(0xFFFFu << sh);
+                if (w == 0)
+                    T.v[t][0] = (T.v[t][0] & keep) | (nt.v[t] << sh);
+                else
+                    T.v[t][1] = (T.v[t][1] & keep) | (nt.v[t] << sh);
+            } else {
+                const int sh = 8 * r;
+                T.v[t][0] = (T.v[t][0] & ~(0xFFu << sh)) | (nt.v[t] << sh);
+            }
+        }
     }
 
     // K: token `col`, chunks grp, grp+4, ... (64 contiguous bytes of every row
@@ -280,28 +363,24 @@ struct MfmaWave {
             bad |= out;
             return out ? 0 : id;
         };
+        // The step's token (position t1 - 1) when this range ends the
+        // sequence: checked against its slot, put into the last block's
+        // registers when that block is computed, stored after the loop.
+        bool put = false;
+        NewToken nt;
+        int32_t id_last = 0;
         if (append_here) {
-            // The step's token (position t1 - 1) goes into the last block
-            // before any of the range is read.  The last block's loads are
-            // issued only after an earlier block's wait, which covers these
-            // older stores; a range of one or two blocks waits here instead.
-            const int32_t slot = uniform_load(a.slots + b);
-            const int32_t id_last = id_of(last);
+            const int32_t slot = uniform(((const CI32 *)a.slots)[b]);
+            id_last = id_of(last);
             const int32_t off = (t1 - 1) % kBlockSize;
             if (slot >= 0) {
-                if ((uint32_t)id_last >= nblocks || slot != id_last * kBlockSize + off) {
+                if ((uint32_t)id_last >= nblocks || slot != id_last * kBlockSize + off)
                     bad = true;
-                } else {
-                    const size_t row = ((size_t)b * a.num_kv_heads + g) * D;
-                    store_token<QT, KT, D>(static_cast<const TQ *>(a.k_new) + row,
-                                           static_cast<const TQ *>(a.v_new) + row,
-                                           const_cast<void *>(a.k_cache),
-                                           const_cast<void *>(a.v_cache), id_last, off, g,
-                                           a.num_kv_heads, a.k_inv, a.v_inv, col + 16 * grp);
-                    if (n < 3)
-                        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-                }
+                else
+                    put = true;
             }
+            if (put)
+                load_new_token(a, b, g, off, nt);
         }
         load(checked(id_of(jb0)), A);
         int32_t idB = id_of(jb0 + 1);
@@ -314,13 +393,26 @@ struct MfmaWave {
             idB = id_of(jb + 3);
             load(checked(idA), A);
             __builtin_amdgcn_sched_barrier(0);
+            if (put && jb + 1 == last)
+                apply_new_token(B, nt);
             compute(B, valid_of(jb + 1), sc);
         }
-        if (n & 1)
+        if (n & 1) {
+            if (put)
+                apply_new_token(A, nt);
             compute(A, valid_of(last), sc); // A holds the last block
+        }
         // Drain the re-read issued past the end (n even), so no load into
         // these registers is in flight when the next range starts.
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        if (put) {
+            const size_t row = ((size_t)b * a.num_kv_heads + g) * D;
+            store_token<QT, KT, D>(static_cast<const TQ *>(a.k_new) + row,
+                                   static_cast<const TQ *>(a.v_new) + row,
+                                   const_cast<void *>(a.k_cache), const_cast<void *>(a.v_cache),
+                                   id_last, (t1 - 1) % kBlockSize, g, a.num_kv_heads, a.k_inv,
+                                   a.v_inv, col + 16 * grp);
+        }
         return !bad;
     }
 
@@ -430,24 +522,60 @@ void decode_mfma_balanced_kernel(DecodeArgs a, int32_t W)
     }
 }
 
+// LDS bytes the balanced kernel's launch asks for and never uses: just over
+// half of a CU's LDS, so that a CU holds one 256-thread workgroup, one wave
+// per SIMD (0 if the device cannot grant that much to one workgroup).
+// Measured on MI355X: a CU's memory requests are served oldest wave first, so
+// a second or third wave per SIMD adds no bandwidth; it only waits, then
+// runs as a later generation, which lengthens the tail and cuts the tiles
+// into more runs (more partial states to merge).  With one wave per SIMD the
+// config-2 step went from 72.0 to 69.9 us, the config-5 one from 236.7 to
+// 219.1 us.
+static int balanced_lds_bytes()
+{
+    static std::mutex mu;
+    static std::map<int, int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(dev);
+    if (it != cache.end())
+        return it->second;
+    int per_cu = 0, per_block = 0;
+    if (hipDeviceGetAttribute(&per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+            hipSuccess ||
+        hipDeviceGetAttribute(&per_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
+            hipSuccess)
+        return 0;
+    int want = per_cu / 2 + 1024;
+    if (want > per_block)
+        want = 0;
+    cache[dev] = want;
+    return want;
+}
+
 template <int QT, int KT, int D>
 hipError_t launch_mfma(const DecodeArgs &a, int32_t num_items, hipStream_t stream)
 {
     const int grid = (num_items + 3) / 4;
-    auto k = a.partition == kPartitionBalanced ? decode_mfma_balanced_kernel<QT, KT, D>
-                                               : decode_mfma_kernel<QT, KT, D>;
-    hipLaunchKernelGGL(k, dim3(grid), dim3(256), 0, stream, a, num_items);
+    if (a.partition == kPartitionBalanced)
+        hipLaunchKernelGGL((decode_mfma_balanced_kernel<QT, KT, D>), dim3(grid), dim3(256),
+                           balanced_lds_bytes(), stream, a, num_items);
+    else
+        hipLaunchKernelGGL((decode_mfma_kernel<QT, KT, D>), dim3(grid), dim3(256), 0, stream, a,
+                           num_items);
     return hipGetLastError();
 }
 
-// Waves of the balanced kernel one CU holds at once.
+// Waves of the balanced kernel one CU holds at once (with its LDS request).
 template <int QT, int KT, int D>
 int mfma_balanced_waves_per_cu()
 {
     int blocks = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
             &blocks, reinterpret_cast<const void *>(&decode_mfma_balanced_kernel<QT, KT, D>), 256,
-            0) != hipSuccess)
+            balanced_lds_bytes()) != hipSuccess)
         return 0;
     return blocks * 4;
 }
