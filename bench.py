@@ -331,16 +331,15 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_mfma_balanced_llama3-8b-gqa-bf16.traffic.json")
-
-
 def measured_traffic(workload, partition, steps, warmup):
-    """HBM bytes per decode launch from the committed rocprofv3 counter runs,
-    if they were taken for this launch configuration and the kernel's sources
-    have not changed since; else None."""
+    """HBM bytes per decode launch from the committed rocprofv3 counter runs
+    (profiles/decode_mfma_balanced_<workload>.traffic.json), if they were taken
+    for this launch configuration and the kernel's sources have not changed
+    since; else None."""
     import hashlib
+    path = os.path.join(ROOT, "profiles", f"decode_mfma_balanced_{workload}.traffic.json")
     try:
-        rec = json.load(open(TRAFFIC_RECORD))
+        rec = json.load(open(path))
         h = hashlib.sha256()
         for f in rec["kernel_sources"]:
             h.update(open(os.path.join(ROOT, f), "rb").read())
