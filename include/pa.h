@@ -121,10 +121,16 @@ pa_status pa_seq_create(pa_pool *pool, int32_t *seq_out);
 /* Reserves slots for ntok more tokens of `seq` and writes their slot ids
  * (block * block_size + offset) to slots_out[0..ntok).  A block is taken
  * from the free list exactly when the sequence length reaches a multiple of
- * block_size ([devto] §4 "On-Demand Allocation").  All or nothing: on
- * PA_ERR_OUT_OF_BLOCKS nothing changes.  Writing into a block shared with
- * another sequence (refcount > 1) returns PA_ERR_UNSUPPORTED (copy on write
- * is not implemented). */
+ * block_size ([devto] §4 "On-Demand Allocation").  Copy on write ([devto]
+ * §5 "Parallel Sampling & Tree Search": a branch's first new token goes to a
+ * private block): if the sequence's last block is partly filled and another
+ * table also maps it (refcount > 1), a free block is taken first, replaces
+ * the shared one in this table (which loses one reference), and the copy
+ * (shared -> private) is queued for pa_pool_take_copies; the slots then lie
+ * in the private block.  The caller must make the queued copies on the device
+ * (pa_copy_blocks) before writing these slots.  All or nothing: on
+ * PA_ERR_OUT_OF_BLOCKS nothing changes (a needed private copy counts as one
+ * block). */
 pa_status pa_seq_append_slots(pa_pool *pool, int32_t seq, int32_t ntok, int32_t *slots_out);
 
 /* pa_seq_append_slots for nseq distinct sequences, ntok tokens each, in the
@@ -142,7 +148,9 @@ pa_status pa_seq_fork(pa_pool *pool, int32_t parent, int32_t *child_out);
 
 /* Drops the sequence; each of its blocks loses one reference and returns to
  * the free list (in table order) when the count reaches zero ([hi] "What
- * 16-token blocks buy you": evicting a sequence frees its blocks). */
+ * 16-token blocks buy you": evicting a sequence frees its blocks).  A block
+ * that a queued copy still reads is held back and joins the free list when
+ * the copies are taken; a queued copy into a freed block is dropped. */
 pa_status pa_seq_free(pa_pool *pool, int32_t seq);
 
 /* Current length (tokens) of a live sequence. */
@@ -159,6 +167,17 @@ pa_status pa_export_block_tables(const pa_pool *pool, const int32_t *seqs, int32
                                  int32_t max_blocks, int32_t *tables_out, int32_t *lens_out);
 
 pa_status pa_pool_get_stats(const pa_pool *pool, pa_pool_stats *out);
+
+/* Hands out the block copies the appends since the last call queued (copy on
+ * write, see pa_seq_append_slots), in the order they were made, as int32
+ * pairs pairs_out[i][0] = source block, pairs_out[i][1] = destination block,
+ * and clears the queue; held blocks then join the free list.  *count_out is
+ * the number of queued copies; if it exceeds max_pairs (or pairs_out is
+ * NULL) nothing is written or cleared and PA_ERR_CAPACITY is returned, so a
+ * call with max_pairs = 0 asks for the count.  No block is both a source and
+ * a destination in one set of copies. */
+pa_status pa_pool_take_copies(pa_pool *pool, int32_t *pairs_out, int32_t max_pairs,
+                              int32_t *count_out);
 
 /* ------------------------------------------------------------------------ */
 /* Kernels (device, asynchronous on `stream`).                              */
@@ -234,6 +253,15 @@ pa_status pa_decode(const void *q, const void *k_cache, const void *v_cache,
                     float k_scale, float v_scale, void *out, void *workspace,
                     size_t workspace_bytes, int32_t partition_size, const pa_kv_desc *desc,
                     void *stream);
+
+/* Makes the copies pa_pool_take_copies handed out, for one layer's caches:
+ * for each pair (src, dst) of the device int32 array pairs[num_pairs][2], the
+ * K and V of block dst (all KV heads) become those of block src ([devto] §5:
+ * the private block of a branch starts as a copy of the shared one).  Ids
+ * outside [0, num_blocks) and src == dst are skipped.  num_pairs in
+ * [0, 65535]. */
+pa_status pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *pairs, int32_t num_pairs,
+                         const pa_kv_desc *desc, void *stream);
 
 /* One decode step with the step's append folded in: the same result, cache
  * bytes and output bits as

@@ -16,6 +16,7 @@ What it models (sources, by page title and section):
       - §5 "Zero-Copy Forking": several block tables may point at the same
         physical block, whose reference count is the number of tables that
         map it; a block returns to the pool when that count reaches zero.
+        A branch's first new token goes to a private block (copy on write).
   * hyperinfer.ai, "KV cache & paged attention deep dive", "PagedAttention:
     virtual memory for attention state" and "What 16-token blocks buy you":
     new blocks come from a free pool; evicting a sequence frees its blocks.
@@ -32,8 +33,14 @@ restates it (it is what makes the tables reproducible):
   * Allocation pops from the end of the free list; freeing pushes a
     sequence's blocks in table order onto the end.
   * Sequence ids count up from 0 and are never reused.
-  * Writing into a block whose refcount is above one is refused (copy on
-    write is not modelled).
+  * Copy on write.  An append that would write into a partly filled last
+    block mapped by more than one table first pops a block for the appending
+    sequence, puts it in place of the shared one (which loses a reference)
+    and queues the copy (shared, private); the OUT_OF_BLOCKS check counts
+    that block.  Queued copies are handed out in order by take_copies.  A
+    block whose count reaches zero while a queued copy reads it waits in a
+    held list and joins the free list (in order) when the copies are handed
+    out; a queued copy into a block whose count reaches zero is dropped.
 """
 
 MASK64 = (1 << 64) - 1
@@ -79,6 +86,8 @@ class PoolModel:
         self.tables = {}  # seq id -> list of physical block ids
         self.lens = {}    # seq id -> tokens stored
         self.next_id = 0
+        self.copies = []  # queued (source, destination) block copies
+        self.held = []    # unreferenced blocks a queued copy still reads
 
     # -- sequences -------------------------------------------------------
     def seq_create(self):
@@ -91,18 +100,40 @@ class PoolModel:
     def _blocks_for(self, ntokens):
         return -(-ntokens // self.block_size)
 
+    def _shared_tail(self, sid, ntok):
+        """Would this append write into a partly filled block another table maps?"""
+        table = self.tables[sid]
+        return (ntok > 0 and self.lens[sid] % self.block_size != 0
+                and self.refcount[table[-1]] > 1)
+
     def _check_append(self, sid, ntok):
         if sid not in self.tables or ntok < 0:
             return ERR_INVALID_ARG, 0
         n = self.lens[sid]
-        table = self.tables[sid]
-        if ntok > 0 and n % self.block_size != 0 and self.refcount[table[-1]] > 1:
-            return ERR_UNSUPPORTED, 0
-        return OK, self._blocks_for(n + ntok) - len(table)
+        extra = 1 if self._shared_tail(sid, ntok) else 0
+        return OK, self._blocks_for(n + ntok) - len(self.tables[sid]) + extra
+
+    def _drop(self, blk):
+        """One table stops mapping blk."""
+        self.refcount[blk] -= 1
+        if self.refcount[blk] > 0:
+            return
+        self.copies = [c for c in self.copies if c[1] != blk]
+        if any(c[0] == blk for c in self.copies):
+            self.held.append(blk)
+        else:
+            self.free.append(blk)
 
     def _do_append(self, sid, ntok):
         n = self.lens[sid]
         table = self.tables[sid]
+        if self._shared_tail(sid, ntok):
+            shared = table[-1]
+            mine = self.free.pop()
+            self.refcount[mine] = 1
+            table[-1] = mine
+            self.copies.append((shared, mine))
+            self._drop(shared)
         need = self._blocks_for(n + ntok) - len(table)
         for _ in range(need):
             blk = self.free.pop()
@@ -155,12 +186,18 @@ class PoolModel:
         if sid not in self.tables:
             return ERR_INVALID_ARG
         for blk in self.tables[sid]:
-            self.refcount[blk] -= 1
-            if self.refcount[blk] == 0:
-                self.free.append(blk)
+            self._drop(blk)
         del self.tables[sid]
         del self.lens[sid]
         return OK
+
+    def take_copies(self):
+        """The queued copies, in order; clears them and frees held blocks."""
+        out = list(self.copies)
+        self.copies = []
+        self.free.extend(self.held)
+        self.held = []
+        return out
 
     # -- export ----------------------------------------------------------
     def export(self, sids, max_blocks):

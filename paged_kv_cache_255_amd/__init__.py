@@ -92,6 +92,8 @@ _SIGS = {
     "pa_decode_append": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _P, _I32, _I32,
                                         ctypes.c_float, ctypes.c_float, ctypes.c_float, _P, _P,
                                         ctypes.c_size_t, _I32, _P, _P]),
+    "pa_pool_take_copies": (ctypes.c_int, [_P, _P, _I32, _P]),
+    "pa_copy_blocks": (ctypes.c_int, [_P, _P, _P, _I32, _P, _P]),
     "pa_last_error": (ctypes.c_char_p, []),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -225,6 +227,20 @@ def pa_pool_get_stats(pool):
     return {f: getattr(st, f) for f, _ in PoolStats._fields_ if f != "reserved"}
 
 
+def pa_pool_take_copies(pool):
+    """The queued copy-on-write block copies as an int32 array [n][2] of
+    (source, destination); clears the queue."""
+    n = _I32()
+    st = _lib.pa_pool_take_copies(pool.handle, None, 0, ctypes.byref(n))
+    if n.value == 0:
+        _check(st, "pa_pool_take_copies")
+        return np.zeros((0, 2), dtype=np.int32)
+    pairs = np.empty((n.value, 2), dtype=np.int32)
+    _check(_lib.pa_pool_take_copies(pool.handle, pairs.ctypes.data, n.value, ctypes.byref(n)),
+           "pa_pool_take_copies")
+    return pairs
+
+
 # ---- kernels ---------------------------------------------------------------
 def kv_desc(num_q_heads, num_kv_heads, head_dim, num_blocks, q_dtype, kv_dtype,
             block_size=16, kernel=KERNEL_AUTO):
@@ -253,6 +269,19 @@ def pa_cache_append(k, v, k_cache, v_cache, slot_mapping, desc, k_scale=1.0, v_s
     _check(_lib.pa_cache_append(_addr(k), _addr(v), _addr(k_cache), _addr(v_cache),
                                 _addr(slot_mapping), T, ctypes.byref(desc), k_scale, v_scale,
                                 _stream(stream)), "pa_cache_append")
+
+
+def pa_copy_blocks(k_cache, v_cache, pairs, desc, stream=None):
+    """pairs: device int32 tensor [n][2] of (source, destination) blocks."""
+    kb = DTYPE_BYTES[desc.kv_dtype]
+    cache_bytes = desc.num_blocks * desc.block_size * desc.num_kv_heads * desc.head_dim * kb
+    for t, nm in [(k_cache, "k_cache"), (v_cache, "v_cache")]:
+        _check_tensor(t, nm, cache_bytes)
+    n = pairs.shape[0] if pairs.dim() == 2 else 0
+    if n:
+        _check_tensor(pairs, "pairs", n * 8)
+    _check(_lib.pa_copy_blocks(_addr(k_cache), _addr(v_cache), _addr(pairs) if n else None, n,
+                               ctypes.byref(desc), _stream(stream)), "pa_copy_blocks")
 
 
 def pa_decode_workspace_bytes(desc, num_seqs, max_seq_len, partition_size):

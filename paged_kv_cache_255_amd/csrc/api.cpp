@@ -26,6 +26,9 @@ hipError_t launch_merge(const DecodeArgs &a, pa_dtype qt, int D, hipStream_t s);
 hipError_t launch_append(const void *k, const void *v, void *kc, void *vc, const int32_t *slots,
                          int32_t T, int32_t H, int32_t NB, int D, pa_dtype qt, pa_dtype kt,
                          float k_inv, float v_inv, hipStream_t s);
+hipError_t launch_copy_blocks(void *k_cache, void *v_cache, const int32_t *pairs,
+                              int32_t num_pairs, int64_t block_bytes, int32_t num_blocks,
+                              hipStream_t s);
 
 namespace {
 
@@ -132,6 +135,27 @@ pa_status pa_cache_append(const void *k, const void *v, void *k_cache, void *v_c
                                  static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return hip_fail(e, "cache append launch");
+    return PA_OK;
+}
+
+pa_status pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *pairs, int32_t num_pairs,
+                         const pa_kv_desc *desc, void *stream)
+{
+    pa_status st = check_desc(desc);
+    if (st != PA_OK)
+        return st;
+    if (num_pairs < 0 || num_pairs > 65535)
+        return fail(PA_ERR_INVALID_ARG, "num_pairs must be in [0, 65535]");
+    if (num_pairs == 0)
+        return PA_OK;
+    if (!k_cache || !v_cache || !pairs)
+        return fail(PA_ERR_INVALID_ARG, "null pointer");
+    const int64_t block_bytes = (int64_t)kBlockSize * desc->num_kv_heads * desc->head_dim *
+                                dtype_bytes(desc->kv_dtype);
+    hipError_t e = launch_copy_blocks(k_cache, v_cache, pairs, num_pairs, block_bytes,
+                                      desc->num_blocks, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "block copy launch");
     return PA_OK;
 }
 

@@ -1,6 +1,8 @@
 // Cache append kernel: one wave per (token, KV head) writes that token's K
 // row and V column into its slot (store_token, append.hpp).  A slot outside
 // [0, num_blocks * block_size) is skipped.
+#include <algorithm>
+
 #include "append.hpp"
 
 namespace pa {
@@ -25,6 +27,44 @@ __global__ __launch_bounds__(256) void append_kernel(const void *k, const void *
     const TQ *vs = static_cast<const TQ *>(v) + ((size_t)t * num_kv_heads + g) * D;
     store_token<QT, KT, D>(ks, vs, k_cache, v_cache, slot / kBlockSize, slot % kBlockSize, g,
                            num_kv_heads, k_inv, v_inv, lane);
+}
+
+// Block copies for copy on write: for each pair (src, dst), the K and V of
+// block dst (all KV heads, block_bytes each) become those of block src.
+// blockIdx.y picks the pair; the threads of a row of workgroups stride over
+// the block 16 bytes at a time.  A pair with an id outside [0, num_blocks)
+// is skipped.  No block of a call is both a source and a destination (the
+// pool holds a block whose copy is pending), so the order of pairs is free.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(char *k_cache, char *v_cache,
+                                                          const int32_t *pairs,
+                                                          int64_t block_bytes, int32_t num_blocks)
+{
+    const int32_t src = pairs[2 * blockIdx.y];
+    const int32_t dst = pairs[2 * blockIdx.y + 1];
+    if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks || src == dst)
+        return;
+    const int64_t step = (int64_t)gridDim.x * blockDim.x * 16;
+    for (int64_t off = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 16; off < block_bytes;
+         off += step) {
+        const u32x4 k = load16(k_cache + src * block_bytes + off);
+        const u32x4 v = load16(v_cache + src * block_bytes + off);
+        *reinterpret_cast<u32x4 *>(k_cache + dst * block_bytes + off) = k;
+        *reinterpret_cast<u32x4 *>(v_cache + dst * block_bytes + off) = v;
+    }
+}
+
+hipError_t launch_copy_blocks(void *k_cache, void *v_cache, const int32_t *pairs,
+                              int32_t num_pairs, int64_t block_bytes, int32_t num_blocks,
+                              hipStream_t s)
+{
+    if (num_pairs == 0)
+        return hipSuccess;
+    const int64_t threads = (block_bytes + 15) / 16;
+    const int gx = (int)std::min<int64_t>((threads + 255) / 256, 64);
+    hipLaunchKernelGGL(copy_blocks_kernel, dim3(gx, num_pairs), dim3(256), 0, s,
+                       static_cast<char *>(k_cache), static_cast<char *>(v_cache), pairs,
+                       block_bytes, num_blocks);
+    return hipGetLastError();
 }
 
 template <int QT, int KT>

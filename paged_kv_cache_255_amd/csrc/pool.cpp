@@ -4,7 +4,8 @@
 //
 // [devto] dev.to, "Why LLMs Run Out of VRAM: KV Cache Fragmentation and How
 //         PagedAttention Fixes It", §4 (block pool, block tables, on-demand
-//         allocation) and §5 (shared blocks with reference counts).
+//         allocation) and §5 (shared blocks with reference counts; a
+//         branch's first write goes to a private block: copy on write).
 // [hi]    hyperinfer.ai, "KV cache & paged attention deep dive" (free pool,
 //         eviction frees a sequence's blocks).
 #include <algorithm>
@@ -26,6 +27,12 @@ struct pa_pool {
         std::vector<int32_t> blocks;
     };
     std::vector<Seq> seqs; // index = sequence id
+    // Copy on write: (src, dst) block copies made by appends and not yet
+    // handed out (pa_pool_take_copies), in the order they were made; and
+    // blocks whose last reference went while a pending copy still reads them
+    // (they join the free list when the copies are handed out).
+    std::vector<std::pair<int32_t, int32_t>> copies;
+    std::vector<int32_t> held;
 };
 
 namespace {
@@ -57,25 +64,60 @@ const pa_pool::Seq *live_seq(const pa_pool *p, int32_t id)
     return live_seq(const_cast<pa_pool *>(p), id);
 }
 
-// New blocks `s` needs for ntok more tokens, or an error if the write would
-// land in a block some other table also maps.
+// Whether an append of ntok tokens to `s` writes into a partly filled last
+// block that another table also maps ([devto] §5 "Zero-Copy Forking": a
+// branch's first new token goes to a private block; copy on write).
+bool needs_copy(const pa_pool *p, const pa_pool::Seq &s, int32_t ntok)
+{
+    return ntok > 0 && s.len % p->cfg.block_size != 0 && p->refcount[s.blocks.back()] > 1;
+}
+
+// New blocks `s` needs for ntok more tokens (a private copy of a shared last
+// block counts as one).
 pa_status check_append(const pa_pool *p, const pa_pool::Seq &s, int32_t ntok, int32_t *need)
 {
     const int32_t bs = p->cfg.block_size;
-    if (ntok > 0 && s.len % bs != 0 && p->refcount[s.blocks.back()] > 1)
-        return pa::fail(PA_ERR_UNSUPPORTED,
-                        "append would write into a block shared with another sequence "
-                        "(copy on write is not implemented)");
     int64_t total = (int64_t)s.len + ntok;
     if (total > INT32_MAX)
         return pa::fail(PA_ERR_INVALID_ARG, "sequence length overflows int32");
-    *need = blocks_for(total, bs) - (int32_t)s.blocks.size();
+    *need = blocks_for(total, bs) - (int32_t)s.blocks.size() + (needs_copy(p, s, ntok) ? 1 : 0);
     return PA_OK;
+}
+
+// Drops one reference to block b; at zero it goes back to the free list, or
+// is held while a pending copy still reads it.  A pending copy into b is
+// dropped (nothing maps b any more).
+void release_block(pa_pool *p, int32_t b)
+{
+    if (--p->refcount[b] != 0)
+        return;
+    auto &c = p->copies;
+    c.erase(std::remove_if(c.begin(), c.end(), [b](const std::pair<int32_t, int32_t> &e) {
+                return e.second == b;
+            }),
+            c.end());
+    for (const auto &e : c)
+        if (e.first == b) {
+            p->held.push_back(b);
+            return;
+        }
+    p->free_list.push_back(b);
 }
 
 void do_append(pa_pool *p, pa_pool::Seq &s, int32_t ntok, int32_t *slots)
 {
     const int32_t bs = p->cfg.block_size;
+    if (needs_copy(p, s, ntok)) {
+        // the private copy is taken first: pop, map it in place of the
+        // shared block, remember the copy the device must make
+        const int32_t shared = s.blocks.back();
+        const int32_t mine = p->free_list.back();
+        p->free_list.pop_back();
+        p->refcount[mine] = 1;
+        s.blocks.back() = mine;
+        p->copies.emplace_back(shared, mine);
+        release_block(p, shared); // refcount > 1: never reaches zero here
+    }
     const int32_t need = blocks_for((int64_t)s.len + ntok, bs) - (int32_t)s.blocks.size();
     for (int32_t i = 0; i < need; ++i) {
         int32_t b = p->free_list.back();
@@ -225,10 +267,8 @@ pa_status pa_seq_free(pa_pool *p, int32_t seq)
     pa_pool::Seq *s = live_seq(p, seq);
     if (!s)
         return pa::fail(PA_ERR_INVALID_ARG, "unknown or already freed sequence id");
-    for (int32_t b : s->blocks) {
-        if (--p->refcount[b] == 0)
-            p->free_list.push_back(b);
-    }
+    for (int32_t b : s->blocks)
+        release_block(p, b);
     s->blocks.clear();
     s->blocks.shrink_to_fit();
     s->len = 0;
@@ -277,6 +317,28 @@ pa_status pa_export_block_tables(const pa_pool *p, const int32_t *seqs, int32_t 
         if (lens_out)
             lens_out[i] = s.len;
     }
+    return PA_OK;
+}
+
+pa_status pa_pool_take_copies(pa_pool *p, int32_t *pairs_out, int32_t max_pairs,
+                              int32_t *count_out)
+{
+    if (!p || !count_out || max_pairs < 0)
+        return pa::fail(PA_ERR_INVALID_ARG, "bad arguments");
+    const size_t n = p->copies.size();
+    *count_out = (int32_t)n;
+    if (n == 0)
+        return PA_OK;
+    if (!pairs_out || (size_t)max_pairs < n)
+        return pa::fail(PA_ERR_CAPACITY, "more pending copies than max_pairs");
+    for (size_t i = 0; i < n; ++i) {
+        pairs_out[2 * i] = p->copies[i].first;
+        pairs_out[2 * i + 1] = p->copies[i].second;
+    }
+    p->copies.clear();
+    for (int32_t b : p->held)
+        p->free_list.push_back(b);
+    p->held.clear();
     return PA_OK;
 }
 

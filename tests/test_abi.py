@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 22, names
     lib = ctypes.CDLL(pa.LIB_PATH)
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing, missing
@@ -64,8 +64,10 @@ def test_error_codes():
     assert e.value.status == pa.ERR_CAPACITY
     c = pa.pa_seq_fork(p, s)
     with pytest.raises(pa.PaError) as e:
-        pa.pa_seq_append_slots(p, c, 1)  # tail block shared
-    assert e.value.status == pa.ERR_UNSUPPORTED
+        pa.pa_seq_append_slots(p, c, 1)  # needs a private copy of the shared tail: none free
+    assert e.value.status == pa.ERR_OUT_OF_BLOCKS
+    assert pa.pa_seq_length(p, c) == 60  # all or nothing
+    assert pa.pa_pool_take_copies(p).shape == (0, 2)
     pa.pa_seq_free(p, c)
     with pytest.raises(pa.PaError) as e:
         pa.pa_seq_free(p, c)
@@ -95,6 +97,7 @@ def test_pool_matches_model_on_random_operations():
     pool = pa.pa_block_pool_init(NB, 2, 64, "bf16", shuffle_seed=987654321)
     model = am.PoolModel(NB, 16, 987654321)
     live = []  # (lib id, model id)
+    copies_seen = 0
     for it in range(1500):
         op = rng.integers(0, 10)
         if op < 2 or not live:
@@ -124,6 +127,11 @@ def test_pool_matches_model_on_random_operations():
             i = rng.integers(len(live))
             st, mc = model.fork(live[i][1])
             live.append((pa.pa_seq_fork(pool, live[i][0]), mc))
+        elif op < 9:
+            got = pa.pa_pool_take_copies(pool)
+            want = np.array(model.take_copies(), dtype=np.int32).reshape(-1, 2)
+            np.testing.assert_array_equal(got, want)
+            copies_seen += len(want)
         else:
             l, m = live.pop(rng.integers(len(live)))
             pa.pa_seq_free(pool, l)
@@ -131,6 +139,7 @@ def test_pool_matches_model_on_random_operations():
         if it % 50 == 0 and live:
             _compare(pool, model, [l for l, _ in live], [m for _, m in live], 64)
     _compare(pool, model, [l for l, _ in live], [m for _, m in live], 64)
+    assert copies_seen > 20  # forks at any length: copy on write was exercised
 
 
 @pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])

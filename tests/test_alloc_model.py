@@ -105,13 +105,102 @@ def test_out_of_blocks_changes_nothing():
     assert p.lens[t] == 0
 
 
-def test_write_into_shared_partial_block_is_refused():
+def test_copy_on_write_of_a_shared_partial_block():
+    """dev.to §5: a branch's first new token goes to a private block.  With a
+    20-token prompt the second block is partly filled and shared after the
+    fork, so the first branch to write gets a private block that starts as a
+    copy of it; the last table still mapping it then writes in place."""
+    p = am.PoolModel(8, 16, 0)  # pops 7, 6, 5, ...
+    s = p.seq_create()
+    assert p.append_slots(s, 20) == (am.OK, list(range(7 * 16, 7 * 16 + 16))
+                                     + list(range(6 * 16, 6 * 16 + 4)))
+    _, c = p.fork(s)
+    assert p.refcount[6] == 2 and p.refcount[7] == 2
+    assert p.append_slots(s, 1) == (am.OK, [5 * 16 + 4])     # private block 5
+    assert p.tables[s] == [7, 5] and p.tables[c] == [7, 6]
+    assert p.refcount[6] == 1 and p.refcount[5] == 1
+    assert p.append_slots(c, 1) == (am.OK, [6 * 16 + 4])     # in place: only c maps 6
+    assert p.take_copies() == [(6, 5)]
+    assert p.take_copies() == []
+
+
+def test_copy_on_write_holds_a_freed_source_and_drops_a_freed_destination():
     p = am.PoolModel(8, 16, 0)
     s = p.seq_create()
-    p.append_slots(s, 10)
+    p.append_slots(s, 20)                 # blocks 7, 6
     _, c = p.fork(s)
-    assert p.append_slots(c, 1)[0] == am.ERR_UNSUPPORTED
-    assert p.append_slots(s, 1)[0] == am.ERR_UNSUPPORTED
+    p.append_slots(s, 1)                  # copy (6 -> 5) queued
+    p.free_seq(c)                         # 6 loses its last reference ...
+    assert 6 not in p.free and p.held == [6]   # ... but the queued copy reads it
+    assert p.take_copies() == [(6, 5)]
+    assert p.free[-1] == 6 and p.held == []
+    # a copy into a block nobody maps any more is dropped
+    _, d = p.fork(s)                      # s: [7, 5], 21 tokens
+    p.append_slots(d, 1)                  # copy (5 -> 6) queued, d: [7, 6]
+    p.free_seq(d)
+    assert p.take_copies() == []
+    assert p.free[-1] == 6
+
+
+def test_copy_on_write_needs_a_free_block():
+    p = am.PoolModel(2, 16, 0)
+    s = p.seq_create()
+    p.append_slots(s, 20)                 # both blocks
+    _, c = p.fork(s)
+    assert p.append_slots(c, 1)[0] == am.ERR_OUT_OF_BLOCKS
+    assert p.tables[c] == p.tables[s] and p.take_copies() == []
+
+
+def test_forked_sequences_read_their_own_tokens():
+    """Content check, independent of how the pool places blocks: every token
+    appended gets a unique value; a step's queued copies are applied, then
+    its writes; each live sequence must read exactly its own history through
+    its table, whatever forks (at any length), appends and frees came before."""
+    rng = np.random.default_rng(5)
+    p = am.PoolModel(160, 16, 77)
+    content = {}
+    history = {}
+    live = []
+    val = 0
+    for step in range(400):
+        writes = []
+        for _ in range(int(rng.integers(1, 6))):
+            op = rng.integers(0, 10)
+            if op < 2 or not live:
+                sid = p.seq_create()
+                live.append(sid)
+                history[sid] = []
+            elif op < 6:
+                sid = live[rng.integers(len(live))]
+                n = int(rng.integers(1, 25))
+                st, slots = p.append_slots(sid, n)
+                if st != am.OK:
+                    continue
+                vals = list(range(val, val + n))
+                val += n
+                writes += list(zip(slots, vals))
+                history[sid] += vals
+            elif op < 8:
+                par = live[rng.integers(len(live))]
+                st, c = p.fork(par)
+                live.append(c)
+                history[c] = list(history[par])
+            else:
+                sid = live.pop(rng.integers(len(live)))
+                p.free_seq(sid)
+                del history[sid]
+        for src, dst in p.take_copies():
+            for o in range(16):
+                if src * 16 + o in content:
+                    content[dst * 16 + o] = content[src * 16 + o]
+                else:
+                    content.pop(dst * 16 + o, None)
+        for slot, v in writes:
+            content[slot] = v
+        for sid in live:
+            t = p.tables[sid]
+            got = [content.get(t[i // 16] * 16 + i % 16) for i in range(p.lens[sid])]
+            assert got == history[sid], (step, sid)
 
 
 def test_random_operations_keep_invariants():
@@ -127,8 +216,9 @@ def test_random_operations_keep_invariants():
             p.append_slots(s, int(rng.integers(1, 40)))
         elif op < 8:
             s = live[rng.integers(len(live))]
-            if p.lens[s] % 16 == 0:
-                live.append(p.fork(s)[1])
+            live.append(p.fork(s)[1])
+        elif op < 9:
+            p.take_copies()
         else:
             s = live.pop(rng.integers(len(live)))
             assert p.free_seq(s) == am.OK
@@ -141,8 +231,10 @@ def test_random_operations_keep_invariants():
                 counts[b] = counts.get(b, 0) + 1
         for b in range(300):
             assert p.refcount[b] == counts.get(b, 0)
-        assert len(p.free) + len(counts) == 300
-        assert set(p.free).isdisjoint(counts)
+        assert len(p.free) + len(p.held) + len(counts) == 300
+        assert set(p.free).isdisjoint(counts) and set(p.held).isdisjoint(counts)
+        assert set(p.held) <= {src for src, _ in p.copies}
+        assert all(p.refcount[dst] >= 1 for _, dst in p.copies)
 
 
 def test_average_tail_slack_is_about_half_a_block():
