@@ -69,11 +69,21 @@ def parse():
     ap.add_argument("--upload-per-step", action="store_true",
                     help="run the host allocator and copy the step's metadata inside each "
                          "timed step")
+    ap.add_argument("--traffic-record", nargs=5, default=None,
+                    metavar=("BENCH_LINE", "FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
+                             "COPY_WRITE_CSV"),
+                    help="write profiles/decode_mfma_balanced_<workload>.traffic.json from "
+                         "the JSON line of a bench run and the rocprofv3 --pmc FETCH_SIZE and "
+                         "WRITE_SIZE counter CSVs of that same command and of "
+                         "--copy-calibration, then exit (no GPU needed)")
     return ap.parse_args()
 
 
 def main():
     args = parse()
+    if args.traffic_record:
+        write_traffic_record(*args.traffic_record)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode path "
               "shards by sequence or KV head with no collective, see the design notes.",
@@ -302,6 +312,7 @@ def main():
             "workload": f"{w.name}: decode step of {L} layer(s), {B} seqs, {Hq} q / {Hkv} kv "
                         f"heads, head_dim {D}, block 16, lengths {int(lens0.min()) + 1}.."
                         f"{int(lens0.max()) + 1} at the first timed step",
+            "workload_name": w.name,
             "global_batch": B,
             "kv_tokens_first_step": int(tokens[0]),
             "kv_bytes_per_step_avg": int(bytes_steps.mean()),
@@ -341,6 +352,8 @@ def measured_traffic(workload, partition, steps, warmup):
     try:
         rec = json.load(open(path))
         h = hashlib.sha256()
+        if rec["kernel_sources"] != TRAFFIC_SOURCES:
+            return None
         for f in rec["kernel_sources"]:
             h.update(open(os.path.join(ROOT, f), "rb").read())
     except (OSError, ValueError, KeyError):
@@ -349,6 +362,88 @@ def measured_traffic(workload, partition, steps, warmup):
             rec.get("steps") == steps and rec.get("warmup") == warmup and
             rec.get("kernel_sources_sha256") == h.hexdigest())
     return rec["hbm_bytes_per_launch"] if same else None
+
+
+TRAFFIC_SOURCES = [
+    "paged_kv_cache_255_amd/csrc/decode_mfma.hip",
+    "paged_kv_cache_255_amd/csrc/work.hpp",
+    "paged_kv_cache_255_amd/csrc/device.hpp",
+    "paged_kv_cache_255_amd/csrc/append.hpp",
+    "paged_kv_cache_255_amd/build.py",
+]
+
+
+def _counter_values(path, counter, kernel_substr):
+    import csv
+    with open(path, newline="") as f:
+        return [float(r["Counter_Value"]) for r in csv.DictReader(f)
+                if r["Counter_Name"] == counter and kernel_substr in r["Kernel_Name"]]
+
+
+def write_traffic_record(bench_line, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+    """Turns two rocprofv3 counter runs of one bench command into HBM bytes per
+    decode launch.  The counters read KiB per dispatch; each is scaled by
+    what it reads for a plain device-to-device copy of known size (bench.py
+    --copy-calibration: three copies of 2^30 bytes).  The last `steps`
+    dispatches of the decode kernel are the back-to-back launches that the
+    roofline times."""
+    import hashlib
+    line = None
+    for ln in open(bench_line):
+        if ln.startswith("{") and '"roofline"' in ln:
+            line = json.loads(ln)
+    if line is None:
+        sys.exit(f"no bench JSON line in {bench_line}")
+    roof, cfg = line["roofline"], line["config"]
+    steps, warmup = line["steps"], line["warmup"]
+    if roof["kernel"] != "decode_mfma_balanced_kernel":
+        sys.exit("traffic records are kept for the balanced MFMA decode kernel only")
+
+    def mean_last(path, counter):
+        v = _counter_values(path, counter, "decode_mfma_balanced_kernel")
+        if len(v) < steps:
+            sys.exit(f"{path}: {len(v)} decode dispatches with {counter}, need {steps}")
+        return sum(v[-steps:]) / steps
+
+    def copy_mean(path, counter):
+        v = _counter_values(path, counter, "copyBuffer")
+        if len(v) != 3:
+            sys.exit(f"{path}: expected 3 copy dispatches with {counter}, found {len(v)}")
+        return sum(v) / 3
+
+    gib_kib = (1 << 30) / 1024
+    cf, cw = copy_mean(copy_fetch_csv, "FETCH_SIZE"), copy_mean(copy_write_csv, "WRITE_SIZE")
+    fetch_scale, write_scale = round(gib_kib / cf, 2), round(gib_kib / cw, 2)
+    fk, wk = mean_last(fetch_csv, "FETCH_SIZE"), mean_last(write_csv, "WRITE_SIZE")
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    rec = {
+        "kernel": roof["kernel"],
+        "workload": cfg["workload_name"],
+        "partition": cfg["partition"],
+        "steps": steps,
+        "warmup": warmup,
+        "launches": f"the {steps} back-to-back decode launches bench.py times "
+                    "(last step's metadata)",
+        "kernel_sources": TRAFFIC_SOURCES,
+        "kernel_sources_sha256": h.hexdigest(),
+        "fetch_size_kib_per_launch_raw": round(fk, 2),
+        "fetch_scale": fetch_scale,
+        "write_size_kib_per_launch_raw": round(wk, 2),
+        "write_scale": write_scale,
+        "copy_calibration": {"bytes_read_and_written": 1 << 30,
+                             "fetch_size_kib": round(cf, 1), "write_size_kib": round(cw, 1)},
+        "hbm_bytes_per_launch": int(round(fk * 1024 * fetch_scale + wk * 1024 * write_scale)),
+        "algorithmic_bytes_per_launch": roof["algorithmic_bytes"],
+    }
+    path = os.path.join(ROOT, "profiles",
+                        f"decode_mfma_balanced_{cfg['workload_name']}.traffic.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(f"{path}: {rec['hbm_bytes_per_launch']} HBM bytes per launch, "
+          f"{rec['hbm_bytes_per_launch'] / rec['algorithmic_bytes_per_launch']:.4f}x algorithmic")
 
 
 def copy_calibration(torch):

@@ -82,7 +82,7 @@ typedef struct {
     int32_t used_blocks;       /* blocks with refcount > 0 */
     int32_t shared_blocks;     /* blocks with refcount > 1 */
     int32_t live_seqs;
-    int32_t reserved;
+    int32_t cached_blocks; /* blocks the prefix cache holds */
     int64_t logical_tokens;    /* sum of live sequence lengths */
     int64_t mapped_blocks;     /* sum of block-table lengths (a shared block counts per table) */
     int64_t tail_slack_tokens; /* sum over live sequences of unused slots in their blocks */
@@ -179,6 +179,37 @@ pa_status pa_pool_get_stats(const pa_pool *pool, pa_pool_stats *out);
 pa_status pa_pool_take_copies(pa_pool *pool, int32_t *pairs_out, int32_t max_pairs,
                               int32_t *count_out);
 
+/* Prefix caching ([devto] §5 "Automatic Prefix Caching": a request whose
+ * prompt matches computed blocks maps those physical blocks and skips their
+ * prefill; [hi] "Prefix caching: share the system prompt": one copy of the
+ * prefix KV, mapped by every request).  A cached block is identified by its
+ * 16 token ids and the cached block holding the 16 tokens before it (none for
+ * a first block), so a match means the whole prefix up to it is equal; the
+ * cache holds one reference on each of its blocks.
+ *
+ * pa_prefix_register: puts the full blocks of `seq`'s first ntok tokens
+ * (token ids `tokens`, ntok <= its length) into the cache, block by block from
+ * the start; a block whose key is already cached is skipped (its cached block
+ * continues the chain), and registration stops at a block cached under other
+ * tokens.  *added_out (may be NULL): blocks newly cached.  Call it once the
+ * K/V of those tokens are in the cache. */
+pa_status pa_prefix_register(pa_pool *pool, int32_t seq, const int32_t *tokens, int32_t ntok,
+                             int32_t *added_out);
+
+/* For an empty sequence (new request, length 0): maps the longest run of
+ * cached full blocks matching tokens[0..ntok) from the start into its table
+ * (each gains a reference) and sets its length to the tokens they hold,
+ * written to *matched_out (a multiple of block_size).  The caller prefills
+ * the remaining tokens with pa_seq_append_slots as usual. */
+pa_status pa_prefix_match(pa_pool *pool, int32_t seq, const int32_t *tokens, int32_t ntok,
+                          int32_t *matched_out);
+
+/* Drops up to max_blocks cached blocks that no table maps, least recently
+ * registered or matched first (ties: lower block id), only blocks no other
+ * cached block names as its parent; each returns to the free list.
+ * *evicted_out (may be NULL): blocks dropped. */
+pa_status pa_prefix_evict(pa_pool *pool, int32_t max_blocks, int32_t *evicted_out);
+
 /* ------------------------------------------------------------------------ */
 /* Kernels (device, asynchronous on `stream`).                              */
 /* ------------------------------------------------------------------------ */
@@ -186,8 +217,10 @@ pa_status pa_pool_take_copies(pa_pool *pool, int32_t *pairs_out, int32_t max_pai
 /* Kernel choice for pa_decode. */
 enum {
     PA_KERNEL_AUTO = 0, /* library picks by dtype, head_dim and group size */
-    PA_KERNEL_VALU = 1, /* vector-ALU kernel (fp32 math); every dtype */
-    PA_KERNEL_MFMA = 2  /* matrix-core kernel; 16-bit q, 16-bit or FP8 KV */
+    PA_KERNEL_VALU = 1, /* vector-ALU kernel (fp32 math); every dtype;
+                           group 1, 2 or 4 (8 at head_dim 64) */
+    PA_KERNEL_MFMA = 2  /* matrix-core kernel; 16-bit q, 16-bit or FP8 KV;
+                           group 1..16 */
 };
 
 typedef struct {

@@ -41,6 +41,18 @@ restates it (it is what makes the tables reproducible):
     block whose count reaches zero while a queued copy reads it waits in a
     held list and joins the free list (in order) when the copies are handed
     out; a queued copy into a block whose count reaches zero is dropped.
+  * Prefix caching (dev.to §5 "Automatic Prefix Caching"; hyperinfer.ai
+    "Prefix caching: share the system prompt").  A cached full block is keyed
+    by (the cached block before it, or -1 for a first block; its 16 token
+    ids), so equal keys mean equal whole prefixes.  The cache holds one
+    reference per block.  register walks a sequence's full blocks from the
+    start: a key already cached continues the chain through the cached block;
+    otherwise the sequence's block is cached, until a block that is cached
+    under other tokens.  match maps the longest chain of cached blocks into an
+    empty sequence.  Every registration or match of a block stamps it with
+    the next value of a counter; evict drops, one at a time, the block with
+    the lowest stamp (ties: lower id) among cached blocks that only the cache
+    maps and that no cached key names as parent.
 """
 
 MASK64 = (1 << 64) - 1
@@ -88,6 +100,9 @@ class PoolModel:
         self.next_id = 0
         self.copies = []  # queued (source, destination) block copies
         self.held = []    # unreferenced blocks a queued copy still reads
+        self.prefix = {}  # (parent block, 16 tokens) -> cached block
+        self.cache = {}   # cached block -> [key, stamp, cached children]
+        self.clock = 0
 
     # -- sequences -------------------------------------------------------
     def seq_create(self):
@@ -199,6 +214,71 @@ class PoolModel:
         self.held = []
         return out
 
+    # -- prefix cache -----------------------------------------------------
+    def _stamp(self, blk):
+        self.clock += 1
+        self.cache[blk][1] = self.clock
+
+    def prefix_register(self, sid, tokens):
+        """Caches the full blocks of sid's first len(tokens) tokens; returns
+        (status, blocks newly cached)."""
+        if sid not in self.tables or len(tokens) > self.lens[sid]:
+            return ERR_INVALID_ARG, 0
+        added, parent = 0, -1
+        bs = self.block_size
+        for i in range(len(tokens) // bs):
+            key = (parent, tuple(int(t) for t in tokens[i * bs:(i + 1) * bs]))
+            if key in self.prefix:
+                parent = self.prefix[key]
+                self._stamp(parent)
+                continue
+            blk = self.tables[sid][i]
+            if blk in self.cache:
+                break
+            self.prefix[key] = blk
+            self.cache[blk] = [key, 0, 0]
+            self._stamp(blk)
+            self.refcount[blk] += 1
+            if parent >= 0:
+                self.cache[parent][2] += 1
+            parent = blk
+            added += 1
+        return OK, added
+
+    def prefix_match(self, sid, tokens):
+        """Maps the cached chain matching tokens into the empty sid; returns
+        (status, tokens matched)."""
+        if sid not in self.tables or self.lens[sid] != 0:
+            return ERR_INVALID_ARG, 0
+        parent = -1
+        bs = self.block_size
+        for i in range(len(tokens) // bs):
+            key = (parent, tuple(int(t) for t in tokens[i * bs:(i + 1) * bs]))
+            if key not in self.prefix:
+                break
+            parent = self.prefix[key]
+            self._stamp(parent)
+            self.refcount[parent] += 1
+            self.tables[sid].append(parent)
+        self.lens[sid] = len(self.tables[sid]) * bs
+        return OK, self.lens[sid]
+
+    def prefix_evict(self, max_blocks):
+        n = 0
+        while n < max_blocks:
+            cand = [(e[1], b) for b, e in self.cache.items()
+                    if self.refcount[b] == 1 and e[2] == 0]
+            if not cand:
+                break
+            _, blk = min(cand)
+            key = self.cache.pop(blk)[0]
+            del self.prefix[key]
+            if key[0] >= 0:
+                self.cache[key[0]][2] -= 1
+            self._drop(blk)
+            n += 1
+        return n
+
     # -- export ----------------------------------------------------------
     def export(self, sids, max_blocks):
         """(status, tables[nseq][max_blocks] padded with -1, lens)."""
@@ -221,6 +301,7 @@ class PoolModel:
             "free_blocks": len(self.free),
             "used_blocks": used,
             "shared_blocks": sum(1 for r in self.refcount if r > 1),
+            "cached_blocks": len(self.cache),
             "live_seqs": len(self.tables),
             "logical_tokens": sum(self.lens.values()),
             "mapped_blocks": mapped,

@@ -17,6 +17,15 @@ LIB_PATH = os.path.join(_HERE, "libpa.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with "
                       "`python paged_kv_cache_255_amd/build.py`")
+
+# The callers hand the library device pointers and streams of torch's HIP
+# runtime, so the library must run on that same runtime.  torch ships its own
+# libamdhip64.so.7; once torch is loaded, the dynamic loader resolves libpa's
+# dependency of that name to it.  Loading libpa first would bring in a second
+# HIP runtime (the system one), which then finds no free device and knows none
+# of torch's allocations.
+import torch  # noqa: E402,F401  (must precede the CDLL below)
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 # pa_status
@@ -49,7 +58,7 @@ class PoolConfig(ctypes.Structure):
 class PoolStats(ctypes.Structure):
     _fields_ = [("num_blocks", ctypes.c_int32), ("free_blocks", ctypes.c_int32),
                 ("used_blocks", ctypes.c_int32), ("shared_blocks", ctypes.c_int32),
-                ("live_seqs", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("live_seqs", ctypes.c_int32), ("cached_blocks", ctypes.c_int32),
                 ("logical_tokens", ctypes.c_int64), ("mapped_blocks", ctypes.c_int64),
                 ("tail_slack_tokens", ctypes.c_int64)]
 
@@ -93,6 +102,9 @@ _SIGS = {
                                         ctypes.c_float, ctypes.c_float, ctypes.c_float, _P, _P,
                                         ctypes.c_size_t, _I32, _P, _P]),
     "pa_pool_take_copies": (ctypes.c_int, [_P, _P, _I32, _P]),
+    "pa_prefix_register": (ctypes.c_int, [_P, _I32, _P, _I32, _P]),
+    "pa_prefix_match": (ctypes.c_int, [_P, _I32, _P, _I32, _P]),
+    "pa_prefix_evict": (ctypes.c_int, [_P, _I32, _P]),
     "pa_copy_blocks": (ctypes.c_int, [_P, _P, _P, _I32, _P, _P]),
     "pa_last_error": (ctypes.c_char_p, []),
 }
@@ -224,7 +236,7 @@ def pa_export_block_tables(pool, seqs, max_blocks, tables_out=None, lens_out=Non
 def pa_pool_get_stats(pool):
     st = PoolStats()
     _check(_lib.pa_pool_get_stats(pool.handle, ctypes.byref(st)), "pa_pool_get_stats")
-    return {f: getattr(st, f) for f, _ in PoolStats._fields_ if f != "reserved"}
+    return {f: getattr(st, f) for f, _ in PoolStats._fields_}
 
 
 def pa_pool_take_copies(pool):
@@ -239,6 +251,37 @@ def pa_pool_take_copies(pool):
     _check(_lib.pa_pool_take_copies(pool.handle, pairs.ctypes.data, n.value, ctypes.byref(n)),
            "pa_pool_take_copies")
     return pairs
+
+
+def _tokens(tokens):
+    t = np.ascontiguousarray(tokens, dtype=np.int32)
+    return t, (t.ctypes.data if t.size else None)
+
+
+def pa_prefix_register(pool, seq, tokens):
+    """Caches the full blocks of seq's first len(tokens) tokens; returns the
+    number of blocks newly cached."""
+    t, ptr = _tokens(tokens)
+    n = _I32()
+    _check(_lib.pa_prefix_register(pool.handle, seq, ptr, t.size, ctypes.byref(n)),
+           "pa_prefix_register")
+    return n.value
+
+
+def pa_prefix_match(pool, seq, tokens):
+    """Maps the cached full blocks matching tokens into the empty seq;
+    returns the tokens they hold."""
+    t, ptr = _tokens(tokens)
+    n = _I32()
+    _check(_lib.pa_prefix_match(pool.handle, seq, ptr, t.size, ctypes.byref(n)),
+           "pa_prefix_match")
+    return n.value
+
+
+def pa_prefix_evict(pool, max_blocks):
+    n = _I32()
+    _check(_lib.pa_prefix_evict(pool.handle, max_blocks, ctypes.byref(n)), "pa_prefix_evict")
+    return n.value
 
 
 # ---- kernels ---------------------------------------------------------------

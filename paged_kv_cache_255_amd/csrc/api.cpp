@@ -38,6 +38,11 @@ pa_status hip_fail(hipError_t e, const char *what)
     return fail(PA_ERR_HIP, m.c_str());
 }
 
+// hipGetLastError reports the thread's last failed HIP call of any caller in
+// the process (a framework probing devices may leave one behind), so the
+// launchers clear it first: the check after a launch then sees that launch.
+void clear_stale_hip_error() { (void)hipGetLastError(); }
+
 bool valid_dtype(pa_dtype t) { return dtype_bytes(t) != 0; }
 
 // The (q, kv) storage pairs the path defines: matching 16/32-bit types, or
@@ -129,6 +134,7 @@ pa_status pa_cache_append(const void *k, const void *v, void *k_cache, void *v_c
         k_inv = 1.0f / k_scale;
         v_inv = 1.0f / v_scale;
     }
+    clear_stale_hip_error();
     hipError_t e = launch_append(k, v, k_cache, v_cache, slot_mapping, num_tokens,
                                  desc->num_kv_heads, desc->num_blocks, desc->head_dim,
                                  desc->q_dtype, desc->kv_dtype, k_inv, v_inv,
@@ -152,6 +158,7 @@ pa_status pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *pairs, int
         return fail(PA_ERR_INVALID_ARG, "null pointer");
     const int64_t block_bytes = (int64_t)kBlockSize * desc->num_kv_heads * desc->head_dim *
                                 dtype_bytes(desc->kv_dtype);
+    clear_stale_hip_error();
     hipError_t e = launch_copy_blocks(k_cache, v_cache, pairs, num_pairs, block_bytes,
                                       desc->num_blocks, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
@@ -284,6 +291,7 @@ pa_status decode_impl(Phase phase, const void *q, const void *k_cache, const voi
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
+    clear_stale_hip_error();
     if (appending) {
         if (desc->kv_dtype == PA_FP8_E4M3 && (k_scale == INFINITY || v_scale == INFINITY))
             return fail(PA_ERR_INVALID_ARG, "FP8 scales must be positive and finite");

@@ -12,10 +12,38 @@
 #include <cstdint>
 #include <cstring>
 #include <new>
+#include <unordered_map>
 #include <vector>
 
 #include "pa.h"
 #include "pa_internal.hpp"
+
+// Identity of a cached full block ([devto] §5 "Automatic Prefix Caching":
+// a table of physical blocks looked up by their tokens): the cached block
+// that holds the 16 tokens before it (-1 for a sequence's first block) and
+// its own 16 token ids.  Chaining by the parent's physical id makes equal
+// keys mean equal whole prefixes, and equality is exact (no lossy hash).
+struct BlockKey {
+    int32_t parent;
+    int32_t tokens[16];
+    bool operator==(const BlockKey &o) const
+    {
+        return parent == o.parent && std::memcmp(tokens, o.tokens, sizeof(tokens)) == 0;
+    }
+};
+
+struct BlockKeyHash {
+    size_t operator()(const BlockKey &k) const
+    {
+        uint64_t h = 0x243F6A8885A308D3ull ^ (uint32_t)k.parent;
+        for (int32_t t : k.tokens) {
+            h ^= (uint32_t)t;
+            h *= 0x9E3779B97F4A7C15ull;
+            h ^= h >> 29;
+        }
+        return (size_t)h;
+    }
+};
 
 struct pa_pool {
     pa_pool_config cfg{};
@@ -33,6 +61,17 @@ struct pa_pool {
     // (they join the free list when the copies are handed out).
     std::vector<std::pair<int32_t, int32_t>> copies;
     std::vector<int32_t> held;
+    // Prefix cache: key -> block, and per cached block its key, when it was
+    // last registered or matched, and how many cached keys name it as parent.
+    // The cache holds one reference on each of its blocks.
+    struct Cached {
+        BlockKey key;
+        uint64_t last_use;
+        int32_t children;
+    };
+    std::unordered_map<BlockKey, int32_t, BlockKeyHash> prefix;
+    std::unordered_map<int32_t, Cached> cached;
+    uint64_t tick = 0;
 };
 
 namespace {
@@ -342,6 +381,106 @@ pa_status pa_pool_take_copies(pa_pool *p, int32_t *pairs_out, int32_t max_pairs,
     return PA_OK;
 }
 
+pa_status pa_prefix_register(pa_pool *p, int32_t seq, const int32_t *tokens, int32_t ntok,
+                             int32_t *added_out)
+{
+    pa_pool::Seq *s = live_seq(p, seq);
+    if (!s)
+        return pa::fail(PA_ERR_INVALID_ARG, "unknown or freed sequence id");
+    if (ntok < 0 || ntok > s->len || (ntok > 0 && !tokens))
+        return pa::fail(PA_ERR_INVALID_ARG, "ntok must be in [0, sequence length]");
+    const int32_t bs = p->cfg.block_size;
+    int32_t added = 0, prev = -1;
+    for (int32_t i = 0; i < ntok / bs; ++i) {
+        BlockKey key;
+        key.parent = prev;
+        std::memcpy(key.tokens, tokens + (size_t)i * bs, sizeof(key.tokens));
+        auto it = p->prefix.find(key);
+        if (it != p->prefix.end()) {
+            prev = it->second;
+            p->cached[prev].last_use = ++p->tick;
+            continue;
+        }
+        const int32_t b = s->blocks[i];
+        if (p->cached.count(b))
+            break; // cached under other tokens: not this prefix's block
+        p->prefix.emplace(key, b);
+        p->cached[b] = pa_pool::Cached{key, ++p->tick, 0};
+        ++p->refcount[b];
+        if (prev >= 0)
+            ++p->cached[prev].children;
+        prev = b;
+        ++added;
+    }
+    if (added_out)
+        *added_out = added;
+    return PA_OK;
+}
+
+pa_status pa_prefix_match(pa_pool *p, int32_t seq, const int32_t *tokens, int32_t ntok,
+                          int32_t *matched_out)
+{
+    pa_pool::Seq *s = live_seq(p, seq);
+    if (!s || !matched_out)
+        return pa::fail(PA_ERR_INVALID_ARG, "unknown sequence or null matched_out");
+    if (s->len != 0)
+        return pa::fail(PA_ERR_INVALID_ARG, "prefix matching needs an empty sequence");
+    if (ntok < 0 || (ntok > 0 && !tokens))
+        return pa::fail(PA_ERR_INVALID_ARG, "bad tokens");
+    const int32_t bs = p->cfg.block_size;
+    int32_t prev = -1, n = 0;
+    for (int32_t i = 0; i < ntok / bs; ++i) {
+        BlockKey key;
+        key.parent = prev;
+        std::memcpy(key.tokens, tokens + (size_t)i * bs, sizeof(key.tokens));
+        auto it = p->prefix.find(key);
+        if (it == p->prefix.end())
+            break;
+        prev = it->second;
+        p->cached[prev].last_use = ++p->tick;
+        ++p->refcount[prev];
+        s->blocks.push_back(prev);
+        ++n;
+    }
+    s->len = n * bs;
+    *matched_out = n * bs;
+    return PA_OK;
+}
+
+pa_status pa_prefix_evict(pa_pool *p, int32_t max_blocks, int32_t *evicted_out)
+{
+    if (!p || max_blocks < 0)
+        return pa::fail(PA_ERR_INVALID_ARG, "bad arguments");
+    int32_t n = 0;
+    while (n < max_blocks) {
+        // the least recently used cached block that only the cache maps and
+        // that no cached key names as parent (ties: lower block id)
+        int32_t best = -1;
+        uint64_t best_use = 0;
+        for (const auto &e : p->cached) {
+            if (p->refcount[e.first] != 1 || e.second.children != 0)
+                continue;
+            if (best < 0 || e.second.last_use < best_use ||
+                (e.second.last_use == best_use && e.first < best)) {
+                best = e.first;
+                best_use = e.second.last_use;
+            }
+        }
+        if (best < 0)
+            break;
+        const BlockKey key = p->cached[best].key;
+        p->prefix.erase(key);
+        if (key.parent >= 0)
+            --p->cached[key.parent].children;
+        p->cached.erase(best);
+        release_block(p, best);
+        ++n;
+    }
+    if (evicted_out)
+        *evicted_out = n;
+    return PA_OK;
+}
+
 pa_status pa_pool_get_stats(const pa_pool *p, pa_pool_stats *out)
 {
     if (!p || !out)
@@ -352,6 +491,7 @@ pa_status pa_pool_get_stats(const pa_pool *p, pa_pool_stats *out)
     st.used_blocks = st.num_blocks - st.free_blocks;
     for (int32_t r : p->refcount)
         st.shared_blocks += (r > 1);
+    st.cached_blocks = (int32_t)p->cached.size();
     for (const auto &s : p->seqs) {
         if (!s.live)
             continue;

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 22, names
+    assert len(names) == 25, names
     lib = ctypes.CDLL(pa.LIB_PATH)
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing, missing
@@ -142,6 +142,61 @@ def test_pool_matches_model_on_random_operations():
     assert copies_seen > 20  # forks at any length: copy on write was exercised
 
 
+def test_pool_matches_model_with_prefix_cache():
+    """Register, match and evict (with appends, forks, frees and copies)
+    give the same tables, refcounts, stats and copies in the library and in
+    the model."""
+    rng = np.random.default_rng(13)
+    NB = 200
+    pool = pa.pa_block_pool_init(NB, 2, 64, "bf16", shuffle_seed=55)
+    model = am.PoolModel(NB, 16, 55)
+    systems = [[int(x) for x in rng.integers(0, 30, size=n)] for n in (16, 40, 70)]
+    live = []  # (lib id, model id, tokens)
+    hits = 0
+    for it in range(1200):
+        op = rng.integers(0, 10)
+        if op < 3 or not live:
+            prompt = systems[rng.integers(3)] + [int(x) for x in rng.integers(0, 30, size=int(rng.integers(0, 25)))]
+            l, m = pa.pa_seq_create(pool), model.seq_create()
+            got = pa.pa_prefix_match(pool, l, prompt)
+            st, want = model.prefix_match(m, prompt)
+            assert got == want
+            hits += got
+            st, ms = model.append_slots(m, len(prompt) - want)
+            if st == am.OK:
+                np.testing.assert_array_equal(
+                    pa.pa_seq_append_slots(pool, l, len(prompt) - got), ms)
+                assert pa.pa_prefix_register(pool, l, prompt) == model.prefix_register(m, prompt)[1]
+            else:
+                with pytest.raises(pa.PaError) as e:
+                    pa.pa_seq_append_slots(pool, l, len(prompt) - got)
+                assert e.value.status == st
+            live.append((l, m, prompt))
+        elif op < 5:
+            l, m, _ = live[rng.integers(len(live))]
+            st, ms = model.append_slots(m, 1)
+            if st == am.OK:
+                np.testing.assert_array_equal(pa.pa_seq_append_slots(pool, l, 1), ms)
+        elif op < 6:
+            l, m, t = live[rng.integers(len(live))]
+            live.append((pa.pa_seq_fork(pool, l), model.fork(m)[1], t))
+        elif op < 8:
+            l, m, _ = live.pop(rng.integers(len(live)))
+            pa.pa_seq_free(pool, l)
+            model.free_seq(m)
+        elif op < 9:
+            k = int(rng.integers(1, 8))
+            assert pa.pa_prefix_evict(pool, k) == model.prefix_evict(k)
+        else:
+            np.testing.assert_array_equal(
+                pa.pa_pool_take_copies(pool),
+                np.array(model.take_copies(), dtype=np.int32).reshape(-1, 2))
+        if it % 40 == 0 and live:
+            _compare(pool, model, [l for l, _, _ in live], [m for _, m, _ in live], 64)
+    _compare(pool, model, [l for l, _, _ in live], [m for _, m, _ in live], 64)
+    assert hits > 300
+
+
 @pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
 def test_pool_matches_model_on_workload_plans(cid):
     w = workloads.config(cid, "full" if cid in (1, 2, 4) else "small")
@@ -165,3 +220,17 @@ def test_pool_matches_model_on_workload_plans(cid):
         if cid == 4:
             s = pa.pa_pool_get_stats(pool)
             assert s["shared_blocks"] == 4 if w.num_seqs == 6 else 128
+
+
+def test_one_hip_runtime_whatever_the_import_order():
+    """Importing the package before torch must not load a second HIP runtime:
+    torch's tensors and streams belong to the runtime torch loaded."""
+    import subprocess
+    import sys
+    code = ("import paged_kv_cache_255_amd, torch\n"
+            "libs = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}\n"
+            "print(len(libs), sorted(libs))\n")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                         timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.startswith("1 "), out.stdout

@@ -258,3 +258,101 @@ def test_bytes_per_token_closed_form():
     for ex in g["examples"]:
         assert am.kv_bytes_per_token(ex["layers"], ex["kv_heads"], ex["head_dim"],
                                      ex["elem_bytes"]) == ex["bytes_per_token"]
+
+
+def test_prefix_cache_maps_a_shared_system_prompt():
+    """dev.to §5 "Automatic Prefix Caching" / hyperinfer.ai "Prefix caching":
+    a request whose prompt starts with cached blocks maps them (no prefill for
+    those tokens); a prompt that differs inside the second block maps only the
+    first; eviction takes unreferenced leaves, least recently used first."""
+    p = am.PoolModel(16, 16, 0)       # pops 15, 14, ...
+    system = list(range(100, 132))    # two full blocks of system prompt
+    a = p.seq_create()
+    prompt_a = system + [7] * 8
+    assert p.append_slots(a, 40)[0] == am.OK
+    assert p.tables[a] == [15, 14, 13]
+    assert p.prefix_register(a, prompt_a) == (am.OK, 2)     # the partial block is not cached
+    assert p.refcount[15] == 2 and p.refcount[14] == 2 and p.stats()["cached_blocks"] == 2
+    b = p.seq_create()
+    assert p.prefix_match(b, system + [9] * 5) == (am.OK, 32)
+    assert p.tables[b] == [15, 14] and p.refcount[15] == 3
+    assert p.append_slots(b, 5) == (am.OK, [12 * 16 + i for i in range(5)])  # no copy: full blocks
+    c = p.seq_create()
+    other = system[:16] + [0] * 16
+    assert p.prefix_match(c, other) == (am.OK, 16)
+    assert p.tables[c] == [15]
+    assert p.prefix_register(a, prompt_a) == (am.OK, 0)     # already cached: stamps only
+    for s in (a, b, c):
+        p.free_seq(s)
+    assert p.refcount[15] == 1 and p.refcount[14] == 1      # the cache's own references
+    assert 15 not in p.free and 14 not in p.free
+    assert p.prefix_evict(1) == 1 and p.free[-1] == 14      # the leaf goes first
+    assert p.prefix_evict(5) == 1 and p.free[-1] == 15
+    assert p.stats()["cached_blocks"] == 0 and p.take_copies() == []
+
+
+def test_prefix_cached_sequences_read_their_own_tokens():
+    """Content check with prefix caching: prompts share a few system prompts;
+    each request matches what it can, prefills the rest, registers its
+    prompt, decodes a few tokens (forks too); blocks are evicted at random.
+    Every live sequence must read back exactly its own tokens."""
+    rng = np.random.default_rng(9)
+    p = am.PoolModel(120, 16, 31)
+    systems = [[int(x) for x in rng.integers(0, 50, size=n)] for n in (16, 37, 64)]
+    content, history, live = {}, {}, []
+    matched_total = 0
+    for step in range(300):
+        writes = []
+        op = rng.integers(0, 10)
+        if op < 3 or not live:
+            prompt = systems[rng.integers(3)] + [int(x) for x in rng.integers(0, 50, size=int(rng.integers(0, 20)))]
+            s = p.seq_create()
+            st, m = p.prefix_match(s, prompt)
+            matched_total += m
+            rest = len(prompt) - m
+            st, slots = p.append_slots(s, rest)
+            if st != am.OK:
+                p.free_seq(s)
+                p.prefix_evict(8)
+                continue
+            writes += list(zip(slots, prompt[m:]))
+            live.append(s)
+            history[s] = list(prompt)
+            p.prefix_register(s, prompt)  # its K/V are written below, before any reader
+        elif op < 6:
+            s = live[rng.integers(len(live))]
+            tok = int(rng.integers(0, 50))
+            st, slots = p.append_slots(s, 1)
+            if st == am.OK:
+                writes.append((slots[0], tok))
+                history[s].append(tok)
+        elif op < 7:
+            par = live[rng.integers(len(live))]
+            c = p.fork(par)[1]
+            live.append(c)
+            history[c] = list(history[par])
+        elif op < 9:
+            s = live.pop(rng.integers(len(live)))
+            p.free_seq(s)
+            del history[s]
+        else:
+            p.prefix_evict(int(rng.integers(1, 6)))
+        for src, dst in p.take_copies():
+            for o in range(16):
+                if src * 16 + o in content:
+                    content[dst * 16 + o] = content[src * 16 + o]
+                else:
+                    content.pop(dst * 16 + o, None)
+        for slot, v in writes:
+            content[slot] = v
+        for s in live:
+            t = p.tables[s]
+            got = [content.get(t[i // 16] * 16 + i % 16) for i in range(p.lens[s])]
+            assert got == history[s], (step, s)
+        counts = {}
+        for t in p.tables.values():
+            for b in t:
+                counts[b] = counts.get(b, 0) + 1
+        for b in range(120):
+            assert p.refcount[b] == counts.get(b, 0) + (1 if b in p.cache else 0)
+    assert matched_total > 500  # the cache was actually used
