@@ -19,9 +19,11 @@
  * notes):
  *   - Query head h reads KV head h / (Hq/Hkv) (consecutive grouping of GQA,
  *     [devto] §2 "Example 2").
- *   - Within one physical block the K tile is stored token-major
- *     ([bs][D]) and the V tile dimension-major ([D][bs]); the pages fix only
- *     that a block holds a fixed number of tokens ([devto] §4).
+ *   - Within one physical block and KV head, K is stored token-major
+ *     ([bs][D]) and V as bs/16 dimension-major tiles of 16 consecutive
+ *     tokens each ([bs/16][D][16]; one [D][16] tile when bs = 16); bs is a
+ *     multiple of 16.  The pages fix only that a block holds a fixed number
+ *     of consecutive tokens ([devto] §4).
  *   - The decoded token attends to every cached token including the one just
  *     appended ([devto] §1: append, then attend over the stored history).
  *   - FP8 is OCP E4M3FN (bias 7, max 448, no infinities); the pages only say
@@ -217,7 +219,8 @@ static size_t k_index(const orc_cache_desc *c, int64_t blk, int g, int o, int d)
 
 static size_t v_index(const orc_cache_desc *c, int64_t blk, int g, int o, int d)
 {
-    return (((size_t)blk * c->num_kv_heads + g) * c->head_dim + d) * c->block_size + o;
+    const size_t tile = ((size_t)blk * c->num_kv_heads + g) * (c->block_size / 16) + o / 16;
+    return (tile * c->head_dim + d) * 16 + o % 16;
 }
 
 /* Store one value of the new token into the cache slot. */
@@ -272,14 +275,16 @@ static void *append_worker(void *arg)
 /* k_new, v_new: [num_tokens][Hkv][D] in in_dtype.  slot_mapping[t] is
  * block * block_size + offset, or negative to skip the token.  Tokens are
  * independent (their slots are distinct), so ranges of them are written by
- * separate threads.  Returns 0, or -1 if a slot lies outside the pool or the
- * dtype pair is not one the path defines. */
+ * separate threads.  Returns 0, or -1 if a slot lies outside the pool, the
+ * dtype pair is not one the path defines or block_size is not a positive
+ * multiple of 16. */
 int orc_cache_append(const orc_cache_desc *c, const void *k_new, const void *v_new,
                      void *k_cache, void *v_cache, const int32_t *slot_mapping,
                      int32_t num_tokens, float k_scale, float v_scale)
 {
     if (!(c->kv_dtype == c->in_dtype ||
-          (c->kv_dtype == ORC_E4M3 && (c->in_dtype == ORC_BF16 || c->in_dtype == ORC_F16))))
+          (c->kv_dtype == ORC_E4M3 && (c->in_dtype == ORC_BF16 || c->in_dtype == ORC_F16))) ||
+        c->block_size <= 0 || c->block_size % 16 != 0)
         return -1;
     for (int32_t t = 0; t < num_tokens; ++t)
         if (slot_mapping[t] >= (int64_t)c->num_blocks * c->block_size)
@@ -450,7 +455,7 @@ int orc_decode(const orc_decode_desc *d, const void *q, const void *k_cache,
                int64_t num_rows, double *out, int nthreads)
 {
     if (d->num_kv_heads <= 0 || d->num_q_heads % d->num_kv_heads != 0 || d->head_dim <= 0 ||
-        d->block_size <= 0)
+        d->block_size <= 0 || d->block_size % 16 != 0)
         return -3;
     decode_job J;
     J.d = d;

@@ -26,15 +26,19 @@ def decode_storage(a, dtype):
     raise ValueError(dtype)
 
 
-def gather(cache_vals, table, n, bs, layout):
+def gather(cache_vals, table, n, bs):
     """Contiguous [n][Hkv][D] rows of one sequence from a paged cache given as
-    float64 [blocks][Hkv][bs][D] ("k") or [blocks][Hkv][D][bs] ("v")."""
+    float64 [blocks][Hkv][bs][D]."""
     nblk = -(-n // bs)
-    if layout == "k":
-        parts = [cache_vals[table[j]].transpose(1, 0, 2) for j in range(nblk)]
-    else:
-        parts = [cache_vals[table[j]].transpose(2, 0, 1) for j in range(nblk)]
+    parts = [cache_vals[table[j]].transpose(1, 0, 2) for j in range(nblk)]
     return np.concatenate(parts, axis=0)[:n]
+
+
+def v_token_major(v_vals, num_kv_heads, head_dim, bs):
+    """The V cache, stored per block and KV head as bs/16 dimension-major
+    tiles of 16 tokens ([bs/16][D][16]), as [blocks][Hkv][bs][D]."""
+    t = v_vals.reshape(-1, num_kv_heads, bs // 16, head_dim, 16)
+    return t.transpose(0, 1, 2, 4, 3).reshape(-1, num_kv_heads, bs, head_dim)
 
 
 def attention(q, k_cache, v_cache, tables, lens, *, num_q_heads, num_kv_heads, head_dim,
@@ -43,14 +47,14 @@ def attention(q, k_cache, v_cache, tables, lens, *, num_q_heads, num_kv_heads, h
     G = num_q_heads // num_kv_heads
     qv = decode_storage(q, q_dtype).reshape(B, num_q_heads, head_dim)
     kv = decode_storage(k_cache, kv_dtype).reshape(-1, num_kv_heads, block_size, head_dim)
-    vv = decode_storage(v_cache, kv_dtype).reshape(-1, num_kv_heads, head_dim, block_size)
+    vv = v_token_major(decode_storage(v_cache, kv_dtype), num_kv_heads, head_dim, block_size)
     out = np.zeros((B, num_q_heads, head_dim))
     for b in range(B):
         n = int(lens[b])
         if n == 0:
             continue
-        K = gather(kv, tables[b], n, block_size, "k") * k_scale  # [n][Hkv][D]
-        V = gather(vv, tables[b], n, block_size, "v") * v_scale
+        K = gather(kv, tables[b], n, block_size) * k_scale  # [n][Hkv][D]
+        V = gather(vv, tables[b], n, block_size) * v_scale
         for h in range(num_q_heads):
             g = h // G
             s = K[:, g, :] @ qv[b, h] * scale

@@ -2,7 +2,9 @@
 
 Builds storage arrays, block tables (random injective placement of each
 sequence's blocks in the pool) and lengths from a numpy seed.  It contains
-no attention arithmetic.
+no attention arithmetic.  Cache shapes: K [blocks][Hkv][bs][D]; V
+[blocks][Hkv][D][16] for bs = 16, else [blocks][Hkv][bs/16][D][16] (16-token
+dimension-major tiles).
 """
 import numpy as np
 import torch
@@ -26,13 +28,17 @@ def random_storage(rng, shape, dtype, scale=1.0):
     raise ValueError(dtype)
 
 
+def v_shape(NB, Hkv, D, bs):
+    return (NB, Hkv, D, 16) if bs == 16 else (NB, Hkv, bs // 16, D, 16)
+
+
 def random_case(seed, *, B=3, Hq=4, Hkv=2, D=32, q_dtype="f32", kv_dtype="f32",
-                lens=None, extra_blocks=5, max_len=90):
+                lens=None, extra_blocks=5, max_len=90, bs=BS):
     rng = np.random.default_rng(seed)
     if lens is None:
         lens = rng.integers(1, max_len, size=B)
     lens = np.asarray(lens, dtype=np.int32)
-    nblk = [-(-int(n) // BS) for n in lens]
+    nblk = [-(-int(n) // bs) for n in lens]
     NB = sum(nblk) + extra_blocks
     perm = rng.permutation(NB)
     maxb = max(max(nblk), 1)
@@ -42,7 +48,7 @@ def random_case(seed, *, B=3, Hq=4, Hkv=2, D=32, q_dtype="f32", kv_dtype="f32",
         tables[b, :k] = perm[pos:pos + k]
         pos += k
     q = random_storage(rng, (len(lens), Hq, D), q_dtype)
-    k = random_storage(rng, (NB, Hkv, BS, D), kv_dtype)
-    v = random_storage(rng, (NB, Hkv, D, BS), kv_dtype)
-    return dict(q=q, k=k, v=v, tables=tables, lens=lens, NB=NB, Hq=Hq, Hkv=Hkv, D=D,
+    k = random_storage(rng, (NB, Hkv, bs, D), kv_dtype)
+    v = random_storage(rng, v_shape(NB, Hkv, D, bs), kv_dtype)
+    return dict(q=q, k=k, v=v, tables=tables, lens=lens, NB=NB, Hq=Hq, Hkv=Hkv, D=D, bs=bs,
                 q_dtype=q_dtype, kv_dtype=kv_dtype, scale=float(np.float32(1 / np.sqrt(D))))

@@ -18,8 +18,11 @@ MUTANTS = {
     "gqa_head_mapping": ("int g = h / G;", "int g = h % d->num_kv_heads;"),
     "k_tile_transposed": ("* c->block_size + o) * c->head_dim + d;\n}\n\nstatic size_t v_index",
                           "* c->head_dim + d) * c->block_size + o;\n}\n\nstatic size_t v_index"),
-    "v_tile_token_major": ("* c->head_dim + d) * c->block_size + o;\n}\n\n/* Store",
-                           "* c->block_size + o) * c->head_dim + d;\n}\n\n/* Store"),
+    "v_tile_token_major": ("return (tile * c->head_dim + d) * 16 + o % 16;",
+                           "return (tile * 16 + o % 16) * c->head_dim + d;"),
+    # the same at 16-token blocks: only the larger-block pins can catch it
+    "v_subtile_order": ("* (c->block_size / 16) + o / 16;",
+                        "* (c->block_size / 16) + (o / 16 + 1) % (c->block_size / 16);"),
     "scale_dropped": ("s[t] = J->scale * dot;", "s[t] = dot;"),
     "softmax_sign": ("s[t] = exp(s[t] - m);", "s[t] = exp(m - s[t]);"),
     "normaliser_dropped": ("out_row[i] /= Z;", "out_row[i] /= 1.0;"),

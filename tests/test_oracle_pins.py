@@ -15,7 +15,7 @@ import torch
 
 import oracle
 from tests import bruteforce
-from tests.cases import BS, random_case, random_storage
+from tests.cases import BS, random_case, random_storage, v_shape
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -26,7 +26,7 @@ def _golden(name):
 
 
 def run_oracle(c, **over):
-    args = dict(num_q_heads=c["Hq"], num_kv_heads=c["Hkv"], head_dim=c["D"], block_size=BS,
+    args = dict(num_q_heads=c["Hq"], num_kv_heads=c["Hkv"], head_dim=c["D"], block_size=c["bs"],
                 num_blocks=c["NB"], q_dtype=c["q_dtype"], kv_dtype=c["kv_dtype"],
                 scale=c["scale"])
     args.update(over)
@@ -34,7 +34,7 @@ def run_oracle(c, **over):
 
 
 def run_brute(c, **over):
-    args = dict(num_q_heads=c["Hq"], num_kv_heads=c["Hkv"], head_dim=c["D"], block_size=BS,
+    args = dict(num_q_heads=c["Hq"], num_kv_heads=c["Hkv"], head_dim=c["D"], block_size=c["bs"],
                 q_dtype=c["q_dtype"], kv_dtype=c["kv_dtype"], scale=c["scale"])
     args.update(over)
     return bruteforce.attention(c["q"], c["k"], c["v"], c["tables"], c["lens"], **args)
@@ -278,18 +278,28 @@ def test_f16_and_bf16_decoders_against_library():
 @pytest.mark.parametrize("kv_dtype,in_dtype", [("f32", "f32"), ("bf16", "bf16"),
                                                ("f16", "f16"), ("e4m3", "bf16"),
                                                ("e4m3", "f16")])
-def test_append_writes_exact_slots_only(kv_dtype, in_dtype):
+@pytest.mark.parametrize("bs", [16, 64])
+def test_append_writes_exact_slots_only(kv_dtype, in_dtype, bs):
+    """Each token lands in its slot and nowhere else.  The V column of offset
+    o is read back as v[blk, :, :, o] (bs = 16) or v[blk, :, o // 16, :, o % 16]
+    (16-token dimension-major tiles)."""
     rng = np.random.default_rng(21)
-    NB, Hkv, D, T = 12, 3, 16, 7
+    NB, Hkv, D = 12, 3, 16
+    slots = np.array([5, bs * 11 + bs - 1, -1, 33, bs * 4, 2, 100, bs * 7 + bs // 2 + 13],
+                     dtype=np.int32)
+    T = len(slots)
     eb = oracle.ELEM_BYTES[kv_dtype]
     sentinel = {1: np.uint8(0xFF), 2: np.uint16(0xFFFF), 4: np.float32(np.nan)}[eb]
-    k = np.full((NB, Hkv, BS, D), sentinel)
-    v = np.full((NB, Hkv, D, BS), sentinel)
+    k = np.full((NB, Hkv, bs, D), sentinel)
+    v = np.full(v_shape(NB, Hkv, D, bs), sentinel)
+
+    def vcol(a, blk, off):
+        return a[blk, :, :, off] if bs == 16 else a[blk, :, off // 16, :, off % 16]
+
     k_new = random_storage(rng, (T, Hkv, D), in_dtype)
     v_new = random_storage(rng, (T, Hkv, D), in_dtype)
-    slots = np.array([5, 16 * 11 + 15, -1, 33, 16 * 4, 2, 100], dtype=np.int32)
     ks, vs = 0.011, 0.007
-    oracle.cache_append(k_new, v_new, k, v, slots, num_kv_heads=Hkv, head_dim=D, block_size=BS,
+    oracle.cache_append(k_new, v_new, k, v, slots, num_kv_heads=Hkv, head_dim=D, block_size=bs,
                         num_blocks=NB, kv_dtype=kv_dtype, in_dtype=in_dtype,
                         k_scale=ks, v_scale=vs)
     written_k = np.zeros(k.shape, bool)
@@ -299,12 +309,12 @@ def test_append_writes_exact_slots_only(kv_dtype, in_dtype):
     for t, s in enumerate(slots):
         if s < 0:
             continue
-        blk, off = divmod(int(s), BS)
+        blk, off = divmod(int(s), bs)
         written_k[blk, :, off, :] = True
-        written_v[blk, :, :, off] = True
+        vcol(written_v, blk, off)[...] = True
         if kv_dtype == in_dtype:
             np.testing.assert_array_equal(k[blk, :, off, :], k_new[t])
-            np.testing.assert_array_equal(v[blk, :, :, off], v_new[t])
+            np.testing.assert_array_equal(vcol(v, blk, off), v_new[t])
         else:
             # torch's cast agrees with the saturating RNE encoder below 464
             xk = torch.from_numpy((kin[t] .astype(np.float32) * np.float32(1.0 / np.float32(ks)))
@@ -315,7 +325,7 @@ def test_append_writes_exact_slots_only(kv_dtype, in_dtype):
             xv = xv.clamp(-448, 448)
             np.testing.assert_array_equal(k[blk, :, off, :],
                                           xk.to(torch.float8_e4m3fn).view(torch.uint8).numpy())
-            np.testing.assert_array_equal(v[blk, :, :, off],
+            np.testing.assert_array_equal(vcol(v, blk, off),
                                           xv.to(torch.float8_e4m3fn).view(torch.uint8).numpy())
     k_bytes = k.view(np.uint8).reshape(k.shape + (eb,))
     v_bytes = v.view(np.uint8).reshape(v.shape + (eb,))
@@ -337,3 +347,59 @@ def test_append_then_decode_reads_new_token():
                         kv_dtype="f32", in_dtype="f32")
     o = run_oracle(c)
     np.testing.assert_allclose(o[0, 0], np.arange(16), atol=1e-6)
+
+
+# -- block sizes -----------------------------------------------------------------
+@pytest.mark.parametrize("bs", [32, 64, 256])
+@pytest.mark.parametrize("q_dtype,kv_dtype,Hq,Hkv,D", [("f32", "f32", 4, 2, 32),
+                                                     ("bf16", "e4m3", 8, 2, 64)])
+def test_block_size_variants_match_bruteforce(bs, q_dtype, kv_dtype, Hq, Hkv, D):
+    """Blocks of more than 16 tokens (the pages also name 32, and 256 or more
+    per page): the oracle against the brute force, which restates the cache
+    layout with its own numpy reshapes.  Lengths span several blocks and end
+    inside one."""
+    for seed in range(2):
+        c = random_case(200 + seed, bs=bs, B=3, Hq=Hq, Hkv=Hkv, D=D, q_dtype=q_dtype,
+                        kv_dtype=kv_dtype, max_len=3 * bs + 7)
+        ks, vs = (0.037, 0.021) if kv_dtype == "e4m3" else (1.0, 1.0)
+        np.testing.assert_allclose(run_oracle(c, k_scale=ks, v_scale=vs),
+                                   run_brute(c, k_scale=ks, v_scale=vs), rtol=1e-12, atol=1e-13)
+
+
+def test_block_size_is_storage_only():
+    """The same token rows, appended into pools of 16-, 32-, 64- and 256-token
+    blocks under random placements, decode to the same bits: the block size
+    changes where a row is stored, not what is computed."""
+    rng = np.random.default_rng(41)
+    Hq, Hkv, D = 4, 2, 32
+    lens = np.array([1, 17, 300, 64], dtype=np.int32)
+    rows_k = [random_storage(rng, (n, Hkv, D), "bf16") for n in lens]
+    rows_v = [random_storage(rng, (n, Hkv, D), "bf16") for n in lens]
+    q = random_storage(rng, (len(lens), Hq, D), "bf16")
+    outs = []
+    for bs in (16, 32, 64, 256):
+        nblk = [-(-int(n) // bs) for n in lens]
+        NB = sum(nblk) + 3
+        perm = rng.permutation(NB)
+        tables = np.full((len(lens), max(nblk)), -1, dtype=np.int32)
+        k = np.zeros((NB, Hkv, bs, D), np.uint16)
+        v = np.zeros(v_shape(NB, Hkv, D, bs), np.uint16)
+        pos = 0
+        for b, n in enumerate(lens):
+            tables[b, :nblk[b]] = perm[pos:pos + nblk[b]]
+            pos += nblk[b]
+            t = np.arange(n)
+            slots = (tables[b][t // bs] * bs + t % bs).astype(np.int32)
+            oracle.cache_append(rows_k[b], rows_v[b], k, v, slots, num_kv_heads=Hkv, head_dim=D,
+                                block_size=bs, num_blocks=NB, kv_dtype="bf16", in_dtype="bf16")
+        outs.append(oracle.decode(q, k, v, tables, lens, num_q_heads=Hq, num_kv_heads=Hkv,
+                                  head_dim=D, block_size=bs, num_blocks=NB, q_dtype="bf16",
+                                  kv_dtype="bf16", scale=0.125))
+    for o in outs[1:]:
+        np.testing.assert_array_equal(o, outs[0])
+
+
+def test_block_size_must_be_a_multiple_of_16():
+    c = random_case(3, B=1, lens=[5])
+    with pytest.raises(ValueError, match=r"\(-3\)"):
+        run_oracle(c, block_size=8)
