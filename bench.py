@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--partition", type=int, default=None,
                     help="tokens per work item (0 = single pass, -1 = balanced)")
     ap.add_argument("--kernel", choices=["auto", "valu", "mfma"], default="auto")
+    ap.add_argument("--block-size", type=int, default=16, choices=[16, 32, 64, 128, 256],
+                    help="tokens per physical block (the workloads use 16)")
     ap.add_argument("--replicas", type=int, default=None, help="cache replicas rotated per step")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
@@ -101,7 +103,8 @@ def main():
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
-    w = workloads.config(args.config)
+    w = workloads.config(args.config, block_size=args.block_size)
+    bs = w.block_size
     partition = w.partition_size if args.partition is None else args.partition
     kernel = {"auto": pa.KERNEL_AUTO, "valu": pa.KERNEL_VALU, "mfma": pa.KERNEL_MFMA}[args.kernel]
     B, Hq, Hkv, D, L = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.num_layers
@@ -110,27 +113,28 @@ def main():
     total_steps = W + K
 
     # pool with room for every token the steps append
-    grow_blocks = B * (math.ceil((total_steps + 1) / 16) + 1)
+    grow_blocks = B * (math.ceil((total_steps + 1) / bs) + 1)
     nblocks = w.num_blocks + grow_blocks
-    pool = pa.pa_block_pool_init(nblocks, Hkv, D, w.kv_dtype, shuffle_seed=w.shuffle_seeds[0])
+    pool = pa.pa_block_pool_init(nblocks, Hkv, D, w.kv_dtype, block_size=bs,
+                                 shuffle_seed=w.shuffle_seeds[0])
     ids, pre_slots = execute_plan(pool, w.ops)
     dec = np.array([ids[s] for s in w.decode_seqs], dtype=np.int32)
     lens0 = np.array(w.decode_lengths(), dtype=np.int64) - 1  # before the first step
     max_len = int(lens0.max()) + total_steps
-    maxb = math.ceil(max_len / 16)
+    maxb = math.ceil(max_len / bs)
 
     step_bytes_1 = Hkv * D * 2 * eb * L  # per token
-    per_replica = nblocks * Hkv * 16 * D * eb * 2 * L
+    per_replica = nblocks * Hkv * bs * D * eb * 2 * L
     R = args.replicas or max(1, math.ceil(1.2e9 / max(1, int(lens0.sum()) * step_bytes_1)))
     log(f"[bench] {w.name}: B={B} Hq={Hq} Hkv={Hkv} D={D} layers={L} kv={w.kv_dtype} "
         f"pool={nblocks} blocks, replicas={R} ({R * per_replica / 1e9:.2f} GB of cache), "
-        f"partition={partition} kernel={args.kernel}")
+        f"partition={partition} kernel={args.kernel} block_size={bs}")
 
     # caches: every replica and layer gets the same prefill through the append kernel
-    desc = pa.kv_desc(Hq, Hkv, D, nblocks, w.q_dtype, w.kv_dtype, kernel=kernel)
+    desc = pa.kv_desc(Hq, Hkv, D, nblocks, w.q_dtype, w.kv_dtype, block_size=bs, kernel=kernel)
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
            "e4m3": torch.uint8}[w.kv_dtype]
-    nelem = nblocks * Hkv * 16 * D
+    nelem = nblocks * Hkv * bs * D
     caches = []  # index layer * R + replica
     d_pre = torch.from_numpy(pre_slots).to(dev)
     ks = vs = 1.0
@@ -310,13 +314,14 @@ def main():
         "data": "synthetic (seeded N(0,1) K/V/q, seeded lengths and block placement)",
         "config": {
             "workload": f"{w.name}: decode step of {L} layer(s), {B} seqs, {Hq} q / {Hkv} kv "
-                        f"heads, head_dim {D}, block 16, lengths {int(lens0.min()) + 1}.."
+                        f"heads, head_dim {D}, block {bs}, lengths {int(lens0.min()) + 1}.."
                         f"{int(lens0.max()) + 1} at the first timed step",
             "workload_name": w.name,
             "global_batch": B,
             "kv_tokens_first_step": int(tokens[0]),
             "kv_bytes_per_step_avg": int(bytes_steps.mean()),
             "partition": partition,
+            "block_size": bs,
             "kernel": kname,
             "cache_replicas": R,
             "metadata": "uploaded per step" if upload else "resident (all steps)",
@@ -329,7 +334,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(w.name, partition, K, W),
+            "traffic": measured_traffic(w.name, partition, K, W) if bs == 16 else None,
             "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE x1)",
             "algorithmic_bytes": int(launch_bytes),
             "kernel": ("decode_valu_kernel" if "valu" in kname else
@@ -396,8 +401,9 @@ def write_traffic_record(bench_line, fetch_csv, write_csv, copy_fetch_csv, copy_
         sys.exit(f"no bench JSON line in {bench_line}")
     roof, cfg = line["roofline"], line["config"]
     steps, warmup = line["steps"], line["warmup"]
-    if roof["kernel"] != "decode_mfma_balanced_kernel":
-        sys.exit("traffic records are kept for the balanced MFMA decode kernel only")
+    if roof["kernel"] != "decode_mfma_balanced_kernel" or cfg.get("block_size", 16) != 16:
+        sys.exit("traffic records are kept for the balanced MFMA decode kernel at 16-token "
+                 "blocks only")
 
     def mean_last(path, counter):
         v = _counter_values(path, counter, "decode_mfma_balanced_kernel")
@@ -471,8 +477,8 @@ def cpu_baseline(w, k_cache, v_cache, q, tables, lens, nblocks, ks, vs, target_s
     qh = workloads.storage(q)
     eb = {"f32": 4, "f16": 2, "bf16": 2, "e4m3": 1}[w.kv_dtype]
     args = dict(num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
-                block_size=16, num_blocks=nblocks, q_dtype=w.q_dtype, kv_dtype=w.kv_dtype,
-                scale=w.scale, k_scale=ks, v_scale=vs, nthreads=threads)
+                block_size=w.block_size, num_blocks=nblocks, q_dtype=w.q_dtype,
+                kv_dtype=w.kv_dtype, scale=w.scale, k_scale=ks, v_scale=vs, nthreads=threads)
 
     def run(nseq):
         rows = [(b, h) for b in range(nseq) for h in range(w.num_q_heads)]

@@ -23,12 +23,14 @@
  *   - All arrays are dense, row-major, without padding.
  *
  * Cache layout (per layer, one K and one V tensor, both [num_blocks][Hkv]
- * tiles of one block of one KV head):
- *   k_cache[block][kv_head][token_in_block][dim]     token-major K tile
- *   v_cache[block][kv_head][dim][token_in_block]     dimension-major V tile
- * The pages fix only that a block holds a fixed number of consecutive tokens
- * ([devto] §4); the tile orders are this library's choice: K rows and V
- * columns are then contiguous in the order the decode kernels consume them.
+ * pieces of one block of one KV head; bs = block_size, o = offset in block):
+ *   k_cache[block][kv_head][o][dim]                   token-major K
+ *   v_cache[block][kv_head][o / 16][dim][o % 16]      V as bs/16 dimension-
+ *                                                      major tiles of 16 tokens
+ * (at bs = 16: v_cache[block][kv_head][dim][o]).  The pages fix only that a
+ * block holds a fixed number of consecutive tokens ([devto] §4); the orders
+ * are this library's choice: every 16-token tile of any block size has the
+ * layout the decode kernels consume, K rows and V columns contiguous.
  *
  * A token's slot is block * block_size + offset; token t of a sequence lives
  * in block block_tables[seq][t / block_size] at offset t % block_size
@@ -68,7 +70,7 @@ typedef struct pa_pool pa_pool;
 
 typedef struct {
     int32_t num_blocks;    /* physical blocks, fixed at init */
-    int32_t block_size;    /* tokens per block; this build supports 16 */
+    int32_t block_size;    /* tokens per block: 16, 32, 64, 128 or 256 */
     int32_t num_layers;    /* used only for the byte counts below */
     int32_t num_kv_heads;
     int32_t head_dim;
@@ -97,7 +99,9 @@ typedef struct {
  * seeded with shuffle_seed).  Blocks are taken from the end of the list and
  * returned to the end.  *out receives the pool; the caller frees it with
  * pa_block_pool_destroy.  Errors: PA_ERR_INVALID_ARG for non-positive sizes
- * or an unknown dtype, PA_ERR_UNSUPPORTED for block_size != 16. */
+ * or an unknown dtype, PA_ERR_UNSUPPORTED for another block_size.  The pages
+ * use 16-token blocks and also name 32 and pages of 256 or more ([devto] §4
+ * and §6; [vk] paged-cache sketch). */
 pa_status pa_block_pool_init(const pa_pool_config *cfg, pa_pool **out);
 
 /* Frees the pool object (NULL is ignored). */
@@ -183,9 +187,9 @@ pa_status pa_pool_take_copies(pa_pool *pool, int32_t *pairs_out, int32_t max_pai
  * prompt matches computed blocks maps those physical blocks and skips their
  * prefill; [hi] "Prefix caching: share the system prompt": one copy of the
  * prefix KV, mapped by every request).  A cached block is identified by its
- * 16 token ids and the cached block holding the 16 tokens before it (none for
- * a first block), so a match means the whole prefix up to it is equal; the
- * cache holds one reference on each of its blocks.
+ * block_size token ids and the cached block holding the block_size tokens
+ * before it (none for a first block), so a match means the whole prefix up to
+ * it is equal; the cache holds one reference on each of its blocks.
  *
  * pa_prefix_register: puts the full blocks of `seq`'s first ntok tokens
  * (token ids `tokens`, ntok <= its length) into the cache, block by block from
@@ -227,16 +231,17 @@ typedef struct {
     int32_t num_q_heads;
     int32_t num_kv_heads;  /* must divide num_q_heads; group G = Hq / Hkv */
     int32_t head_dim;      /* 64 or 128 */
-    int32_t block_size;    /* 16 */
+    int32_t block_size;    /* 16, 32, 64, 128 or 256; as the pool's */
     int32_t num_blocks;    /* blocks in each cache tensor (bounds for ids/slots) */
     pa_dtype q_dtype;      /* q, out and the new tokens' K/V */
     pa_dtype kv_dtype;     /* cache storage: equal to q_dtype, or FP8 with 16-bit q */
     int32_t kernel;        /* PA_KERNEL_* */
 } pa_kv_desc;
 
-/* Writes the K and V of num_tokens new tokens into their cache slots:
- *   k_cache[s / bs][g][s % bs][d] = cvt(k[t][g][d])
- *   v_cache[s / bs][g][d][s % bs] = cvt(v[t][g][d]),   s = slot_mapping[t]
+/* Writes the K and V of num_tokens new tokens into their cache slots
+ * (s = slot_mapping[t], o = s % bs, in the layout above):
+ *   k_cache[s / bs][g][o][d] = cvt(k[t][g][d])
+ *   v_cache[s / bs][g][o / 16][d][o % 16] = cvt(v[t][g][d])
  * for every KV head g and dim d ([devto] §1: the new token's K and V are
  * appended to the cache; §4: a slot is a place in a physical block).
  * k, v: device [num_tokens][Hkv][D] in desc->q_dtype.  slot_mapping: device
@@ -256,7 +261,7 @@ pa_status pa_cache_append(const void *k, const void *v, void *k_cache, void *v_c
 #define PA_PARTITION_BALANCED (-1) /* tokens split evenly over the GPU's waves */
 
 /* Workspace bytes pa_decode needs for this shape and partitioning (0 for
- * PA_PARTITION_NONE).  partition_size > 0 must be a multiple of block_size. */
+ * PA_PARTITION_NONE).  partition_size > 0 must be a multiple of 16. */
 size_t pa_decode_workspace_bytes(const pa_kv_desc *desc, int32_t num_seqs, int32_t max_seq_len,
                                  int32_t partition_size);
 

@@ -2,6 +2,7 @@
 // The block pool calls live in pool.cpp; pa.h documents every entry point.
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cstdio>
 #include <cstring>
 #include <map>
@@ -24,8 +25,8 @@ bool mfma_supports(pa_dtype qt, pa_dtype kt, int D, int G);
 int mfma_waves_per_cu(pa_dtype qt, pa_dtype kt, int D);
 hipError_t launch_merge(const DecodeArgs &a, pa_dtype qt, int D, hipStream_t s);
 hipError_t launch_append(const void *k, const void *v, void *kc, void *vc, const int32_t *slots,
-                         int32_t T, int32_t H, int32_t NB, int D, pa_dtype qt, pa_dtype kt,
-                         float k_inv, float v_inv, hipStream_t s);
+                         int32_t T, int32_t H, int32_t NB, int32_t TS, int D, pa_dtype qt,
+                         pa_dtype kt, float k_inv, float v_inv, hipStream_t s);
 hipError_t launch_copy_blocks(void *k_cache, void *v_cache, const int32_t *pairs,
                               int32_t num_pairs, int64_t block_bytes, int32_t num_blocks,
                               hipStream_t s);
@@ -44,6 +45,15 @@ pa_status hip_fail(hipError_t e, const char *what)
 void clear_stale_hip_error() { (void)hipGetLastError(); }
 
 bool valid_dtype(pa_dtype t) { return dtype_bytes(t) != 0; }
+
+// log2(block_size / 16) for the block sizes the kernels take, else -1.
+int tile_shift_of(int32_t block_size)
+{
+    for (int sh = 0; sh <= 4; ++sh)
+        if (block_size == (kTile << sh))
+            return sh;
+    return -1;
+}
 
 // The (q, kv) storage pairs the path defines: matching 16/32-bit types, or
 // FP8 storage under 16-bit activations.
@@ -66,11 +76,13 @@ pa_status check_desc(const pa_kv_desc *d)
         return fail(PA_ERR_INVALID_ARG, "unknown dtype");
     if (!valid_pair(d->q_dtype, d->kv_dtype))
         return fail(PA_ERR_UNSUPPORTED, "unsupported (q, kv) dtype pair");
-    if (d->block_size != kBlockSize)
-        return fail(PA_ERR_UNSUPPORTED, "block_size must be 16");
+    if (tile_shift_of(d->block_size) < 0)
+        return fail(PA_ERR_UNSUPPORTED, "block_size must be 16, 32, 64, 128 or 256");
     if (d->head_dim != 64 && d->head_dim != 128)
         return fail(PA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
-    if ((int64_t)d->num_blocks * d->num_kv_heads * kBlockSize * d->head_dim > (int64_t)1 << 40)
+    if ((int64_t)d->num_blocks * d->block_size > INT32_MAX)
+        return fail(PA_ERR_INVALID_ARG, "num_blocks * block_size overflows int32 slots");
+    if ((int64_t)d->num_blocks * d->num_kv_heads * d->block_size * d->head_dim > (int64_t)1 << 40)
         return fail(PA_ERR_INVALID_ARG, "cache too large");
     return PA_OK;
 }
@@ -136,7 +148,8 @@ pa_status pa_cache_append(const void *k, const void *v, void *k_cache, void *v_c
     }
     clear_stale_hip_error();
     hipError_t e = launch_append(k, v, k_cache, v_cache, slot_mapping, num_tokens,
-                                 desc->num_kv_heads, desc->num_blocks, desc->head_dim,
+                                 desc->num_kv_heads, desc->num_blocks,
+                                 tile_shift_of(desc->block_size), desc->head_dim,
                                  desc->q_dtype, desc->kv_dtype, k_inv, v_inv,
                                  static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
@@ -156,7 +169,7 @@ pa_status pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *pairs, int
         return PA_OK;
     if (!k_cache || !v_cache || !pairs)
         return fail(PA_ERR_INVALID_ARG, "null pointer");
-    const int64_t block_bytes = (int64_t)kBlockSize * desc->num_kv_heads * desc->head_dim *
+    const int64_t block_bytes = (int64_t)desc->block_size * desc->num_kv_heads * desc->head_dim *
                                 dtype_bytes(desc->kv_dtype);
     clear_stale_hip_error();
     hipError_t e = launch_copy_blocks(k_cache, v_cache, pairs, num_pairs, block_bytes,
@@ -220,12 +233,12 @@ pa_status decode_impl(Phase phase, const void *q, const void *k_cache, const voi
             return fail(PA_ERR_INVALID_ARG, "scales must be positive");
     }
     const bool balanced = partition_size == PA_PARTITION_BALANCED;
-    if (!balanced && (partition_size < 0 || partition_size % kBlockSize != 0))
+    if (!balanced && (partition_size < 0 || partition_size % kTile != 0))
         return fail(PA_ERR_INVALID_ARG,
                     "partition_size must be 0, PA_PARTITION_BALANCED or a positive multiple of 16");
     if (phase != kAll && partition_size == 0)
         return fail(PA_ERR_INVALID_ARG, "partials/merge need a partitioned mode");
-    if ((int64_t)max_blocks_per_seq * kBlockSize < (int64_t)max_seq_len)
+    if ((int64_t)max_blocks_per_seq * desc->block_size < (int64_t)max_seq_len)
         return fail(PA_ERR_INVALID_ARG, "max_seq_len exceeds max_blocks_per_seq * block_size");
 
     const int D = desc->head_dim;
@@ -243,6 +256,7 @@ pa_status decode_impl(Phase phase, const void *q, const void *k_cache, const voi
     a.num_kv_heads = desc->num_kv_heads;
     a.group = G;
     a.num_blocks = desc->num_blocks;
+    a.tile_shift = tile_shift_of(desc->block_size);
     a.max_blocks_per_seq = max_blocks_per_seq;
     a.max_seq_len = max_seq_len;
     a.partition = partition_size;
@@ -299,8 +313,9 @@ pa_status decode_impl(Phase phase, const void *q, const void *k_cache, const voi
             a.append = 1; // the decode kernel writes the tokens itself
         } else {
             e = launch_append(nt.k, nt.v, const_cast<void *>(k_cache), const_cast<void *>(v_cache),
-                              nt.slots, num_seqs, desc->num_kv_heads, desc->num_blocks, D,
-                              desc->q_dtype, desc->kv_dtype, a.k_inv, a.v_inv, s);
+                              nt.slots, num_seqs, desc->num_kv_heads, desc->num_blocks,
+                              a.tile_shift, D, desc->q_dtype, desc->kv_dtype, a.k_inv, a.v_inv,
+                              s);
             if (e != hipSuccess)
                 return hip_fail(e, "cache append launch");
         }

@@ -11,7 +11,8 @@ template <int QT, int KT, int D>
 __global__ __launch_bounds__(256) void append_kernel(const void *k, const void *v, void *k_cache,
                                                      void *v_cache, const int32_t *slots,
                                                      int32_t num_tokens, int32_t num_kv_heads,
-                                                     int32_t num_blocks, float k_inv, float v_inv)
+                                                     int32_t num_blocks, int32_t tile_shift,
+                                                     float k_inv, float v_inv)
 {
     using TQ = typename Store<QT>::T;
     const int lane = threadIdx.x & 63;
@@ -21,11 +22,12 @@ __global__ __launch_bounds__(256) void append_kernel(const void *k, const void *
     const int32_t t = (int32_t)(w / num_kv_heads);
     const int32_t g = (int32_t)(w % num_kv_heads);
     const int32_t slot = slots[t];
-    if (slot < 0 || (int64_t)slot >= (int64_t)num_blocks * kBlockSize)
+    const int32_t bs = kTile << tile_shift;
+    if (slot < 0 || (int64_t)slot >= (int64_t)num_blocks * bs)
         return;
     const TQ *ks = static_cast<const TQ *>(k) + ((size_t)t * num_kv_heads + g) * D;
     const TQ *vs = static_cast<const TQ *>(v) + ((size_t)t * num_kv_heads + g) * D;
-    store_token<QT, KT, D>(ks, vs, k_cache, v_cache, slot / kBlockSize, slot % kBlockSize, g,
+    store_token<QT, KT, D>(ks, vs, k_cache, v_cache, slot / bs, slot % bs, tile_shift, g,
                            num_kv_heads, k_inv, v_inv, lane);
 }
 
@@ -69,38 +71,41 @@ hipError_t launch_copy_blocks(void *k_cache, void *v_cache, const int32_t *pairs
 
 template <int QT, int KT>
 hipError_t append_by_dim(const void *k, const void *v, void *kc, void *vc, const int32_t *slots,
-                         int32_t T, int32_t H, int32_t NB, int D, float ki, float vi,
-                         hipStream_t s)
+                         int32_t T, int32_t H, int32_t NB, int32_t TS, int D, float ki,
+                         float vi, hipStream_t s)
 {
     const int64_t waves = (int64_t)T * H;
     const int grid = (int)((waves + 3) / 4);
     if (D == 64)
         hipLaunchKernelGGL((append_kernel<QT, KT, 64>), dim3(grid), dim3(256), 0, s, k, v, kc, vc,
-                           slots, T, H, NB, ki, vi);
+                           slots, T, H, NB, TS, ki, vi);
     else if (D == 128)
         hipLaunchKernelGGL((append_kernel<QT, KT, 128>), dim3(grid), dim3(256), 0, s, k, v, kc,
-                           vc, slots, T, H, NB, ki, vi);
+                           vc, slots, T, H, NB, TS, ki, vi);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
 hipError_t launch_append(const void *k, const void *v, void *kc, void *vc, const int32_t *slots,
-                         int32_t T, int32_t H, int32_t NB, int D, pa_dtype qt, pa_dtype kt,
-                         float k_inv, float v_inv, hipStream_t s)
+                         int32_t T, int32_t H, int32_t NB, int32_t TS, int D, pa_dtype qt,
+                         pa_dtype kt, float k_inv, float v_inv, hipStream_t s)
 {
     if (qt == PA_F32 && kt == PA_F32)
-        return append_by_dim<PA_F32, PA_F32>(k, v, kc, vc, slots, T, H, NB, D, k_inv, v_inv, s);
+        return append_by_dim<PA_F32, PA_F32>(k, v, kc, vc, slots, T, H, NB, TS, D, k_inv, v_inv,
+                                             s);
     if (qt == PA_F16 && kt == PA_F16)
-        return append_by_dim<PA_F16, PA_F16>(k, v, kc, vc, slots, T, H, NB, D, k_inv, v_inv, s);
+        return append_by_dim<PA_F16, PA_F16>(k, v, kc, vc, slots, T, H, NB, TS, D, k_inv, v_inv,
+                                             s);
     if (qt == PA_BF16 && kt == PA_BF16)
-        return append_by_dim<PA_BF16, PA_BF16>(k, v, kc, vc, slots, T, H, NB, D, k_inv, v_inv, s);
+        return append_by_dim<PA_BF16, PA_BF16>(k, v, kc, vc, slots, T, H, NB, TS, D, k_inv,
+                                               v_inv, s);
     if (qt == PA_BF16 && kt == PA_FP8_E4M3)
-        return append_by_dim<PA_BF16, PA_FP8_E4M3>(k, v, kc, vc, slots, T, H, NB, D, k_inv, v_inv,
-                                                   s);
+        return append_by_dim<PA_BF16, PA_FP8_E4M3>(k, v, kc, vc, slots, T, H, NB, TS, D, k_inv,
+                                                   v_inv, s);
     if (qt == PA_F16 && kt == PA_FP8_E4M3)
-        return append_by_dim<PA_F16, PA_FP8_E4M3>(k, v, kc, vc, slots, T, H, NB, D, k_inv, v_inv,
-                                                  s);
+        return append_by_dim<PA_F16, PA_FP8_E4M3>(k, v, kc, vc, slots, T, H, NB, TS, D, k_inv,
+                                                  v_inv, s);
     return hipErrorInvalidValue;
 }
 

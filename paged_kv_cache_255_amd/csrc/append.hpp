@@ -9,9 +9,10 @@
 // paged attention deep dive", "KV quantization cuts memory in half".
 //
 // Lane d writes dims d, d + 64, ...  The K row of a slot is contiguous
-// ([block][head][token][dim]); the V column is strided by the block size
-// ([block][head][dim][token]).  FP8: the E4M3 code of x * inv (inv = 1/scale
-// in fp32), nearest even, saturating.
+// ([block][head][token][dim]); V is stored per block and head as 16-token
+// dimension-major tiles ([block][head][token / 16][dim][token % 16]), so the
+// V column of a slot is strided by 16.  FP8: the E4M3 code of x * inv
+// (inv = 1/scale in fp32), nearest even, saturating.
 #pragma once
 
 #include "device.hpp"
@@ -21,23 +22,24 @@ namespace pa {
 template <int QT, int KT, int D>
 __device__ __forceinline__ void store_token(const typename Store<QT>::T *ks,
                                             const typename Store<QT>::T *vs, void *k_cache,
-                                            void *v_cache, int32_t blk, int32_t off, int32_t g,
-                                            int32_t num_kv_heads, float k_inv, float v_inv,
-                                            int lane)
+                                            void *v_cache, int32_t blk, int32_t off,
+                                            int32_t tile_shift, int32_t g, int32_t num_kv_heads,
+                                            float k_inv, float v_inv, int lane)
 {
     using TK = typename Store<KT>::T;
-    TK *kd = static_cast<TK *>(k_cache) +
-             (((size_t)blk * num_kv_heads + g) * kBlockSize + off) * D;
-    TK *vd = static_cast<TK *>(v_cache) + ((size_t)blk * num_kv_heads + g) * D * kBlockSize + off;
+    // first tile of (blk, g); `off` (0 .. block_size - 1) is in tile off / 16
+    const size_t tile0 = ((size_t)blk * num_kv_heads + g) << tile_shift;
+    TK *kd = static_cast<TK *>(k_cache) + (tile0 * kTile + off) * D;
+    TK *vd = static_cast<TK *>(v_cache) + (tile0 + off / kTile) * D * kTile + off % kTile;
 #pragma unroll
     for (int i = 0; i < D / kWave; ++i) {
         const int d = i * kWave + lane;
         if constexpr (KT == PA_FP8_E4M3) {
             kd[d] = f32_to_e4m3(to_f32<QT>(ks[d]) * k_inv);
-            vd[(size_t)d * kBlockSize] = f32_to_e4m3(to_f32<QT>(vs[d]) * v_inv);
+            vd[(size_t)d * kTile] = f32_to_e4m3(to_f32<QT>(vs[d]) * v_inv);
         } else {
             kd[d] = ks[d];
-            vd[(size_t)d * kBlockSize] = vs[d];
+            vd[(size_t)d * kTile] = vs[d];
         }
     }
 }

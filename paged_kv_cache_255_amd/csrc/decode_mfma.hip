@@ -6,10 +6,11 @@
 // (the query walks its block table and reads K/V from scattered physical
 // blocks); §2 "Example 2" (query heads of a group share one KV head).
 //
-// A wave processes a run of 16-token blocks of one (sequence, KV head).  The
-// G query heads of the KV head sit in the 16 columns of the MFMA tiles
-// (G <= 16; unused columns carry q = 0 and are discarded), so each K and V
-// tile is read from HBM once for the whole group.  Per block:
+// A wave processes a run of 16-token tiles of one (sequence, KV head); a cache
+// block of 16, 32, ... 256 tokens is 1, 2, ... 16 consecutive tiles.  The G
+// query heads of the KV head sit in the 16 columns of the MFMA tiles (G <= 16;
+// unused columns carry q = 0 and are discarded), so each K and V tile is read
+// from HBM once for the whole group.  Per tile:
 //   S^T[16 tokens][16 heads] = K_tile[16][D] * Q^T[D][16]     (D/32 MFMA 16x16x32)
 //   online softmax on S^T, 4 tokens x 1 head per lane
 //   O^T[D][16 heads] += V^T_tile[D][16] * P^T[16][16 heads]   (D/16 MFMA 16x16x16)
@@ -18,9 +19,9 @@
 // FP8 tiles are widened to the q type with the hardware converter (exact:
 // every E4M3 value is a bf16 and an fp16 value).
 //
-// The next block's K/V loads are issued before the current block's math, and
-// the block-table entries of a run are read with one vector load, so a wave
-// keeps two tiles of HBM reads in flight.
+// The next tile's K/V loads are issued before the current tile's math, and
+// the block-table entries are read with scalar loads two tiles ahead, so a
+// wave keeps two tiles of HBM reads in flight.
 //
 // Work split (DecodeArgs::partition):
 //   0   one wave per (sequence, KV head), output written directly;
@@ -90,12 +91,12 @@ template <> struct Mma<PA_F16> {
     }
 };
 
-// Largest gap (log2 units) between a block's scores and the reference max
+// Largest gap (log2 units) between a tile's scores and the reference max
 // before the accumulators are rescaled: weights stay <= 2^8, exact in bf16/fp16
 // range and harmless to fp32 sums.
 constexpr float kLazyRescale = 8.0f;
 
-// One wave's state and per-block work for one (sequence, KV head).
+// One wave's state and per-tile work for one (sequence, KV head).
 template <int QT, int KT, int D>
 struct MfmaWave {
     using M = Mma<QT>;
@@ -108,8 +109,8 @@ struct MfmaWave {
     static constexpr int CH_PER_LANE = CHUNKS / 4;      // chunks per lane per tile
     static constexpr int QK_MMAS = D / 32;
     static constexpr int PV_TILES = D / 16;
-    static constexpr int V_ROW_BYTES = kBlockSize * KE; // one V^T row (16 tokens)
-    static constexpr int TILE_BYTES = kBlockSize * D * KE;
+    static constexpr int V_ROW_BYTES = kTile * KE; // one V^T row (16 tokens)
+    static constexpr int TILE_BYTES = kTile * D * KE;
     static_assert(CHUNKS % 4 == 0, "row must split into 4 lane groups");
 
     struct Tile {
@@ -120,12 +121,12 @@ struct MfmaWave {
     // The step's new token (pa_decode_append), in the cache's storage format
     // and in tile layout: the K chunks a lane would hold if its column were
     // the token's row, and the V value of dim 16 t + col.  It replaces the
-    // token's slot in the registers of the last block, so that block's loads
+    // token's slot in the registers of the last tile, so that tile's loads
     // need not wait for the token's own store.
     struct NewToken {
         u32x4 k[CH_PER_LANE];
         uint32_t v[PV_TILES];
-        int tok; // the token's offset inside its block
+        int tok; // the token's offset inside its tile
     };
 
     int col; // MFMA column: query head within the group
@@ -206,7 +207,7 @@ struct MfmaWave {
         }
     }
 
-    // Puts the new token into tile T (the sequence's last block).
+    // Puts the new token into tile T (the sequence's last tile).
     __device__ void apply_new_token(Tile &T, const NewToken &nt) const
     {
 #pragma unroll
@@ -253,7 +254,7 @@ struct MfmaWave {
         }
     }
 
-    // One block: `valid` tokens of it (1..16) belong to the range.
+    // One tile: `valid` tokens of it (1..16) belong to the range.
     __device__ void compute(const Tile &T, int valid, float sc)
     {
         f32x4 s = {0.f, 0.f, 0.f, 0.f};
@@ -278,7 +279,7 @@ struct MfmaWave {
             x[r] = (4 * grp + r < valid) ? s[r] * sc : -INFINITY;
         float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
         bm = max_xor32(max_xor16(bm));
-        // The reference max m_run moves only when a block's max exceeds it by
+        // The reference max m_run moves only when a tile's max exceeds it by
         // more than kLazyRescale (log2 units); until then the weights
         // 2^(s - m_run) stay below 2^kLazyRescale and acc, l need no rescale.
         // Any reference gives the same softmax: acc and l share it.
@@ -324,39 +325,49 @@ struct MfmaWave {
                         bool append_here)
     {
         // The block table does not change while the kernel runs: its entries
-        // are read with scalar loads (one wave-uniform id per block, fetched
-        // two blocks ahead), which keeps them out of the vector-load queue
+        // are read with scalar loads (one wave-uniform id per tile, fetched
+        // two tiles ahead), which keeps them out of the vector-load queue
         // the tiles stream through.
         using CI32 = __attribute__((address_space(4))) const int32_t;
         b = uniform(b);
         g = uniform(g);
+        // A block of 16 << sh tokens is 1 << sh tiles: tile jb of the
+        // sequence is tile jb & mask of block table[jb >> sh].
         const CI32 *table = (const CI32 *)(a.block_tables + (size_t)b * a.max_blocks_per_seq);
-        const char *kbase = static_cast<const char *>(a.k_cache) + (size_t)g * TILE_BYTES;
-        const char *vbase = static_cast<const char *>(a.v_cache) + (size_t)g * TILE_BYTES;
-        const size_t bstride = (size_t)a.num_kv_heads * TILE_BYTES;
-        const int32_t jb0 = uniform(t0 / kBlockSize);
-        const int32_t last = uniform((t1 + kBlockSize - 1) / kBlockSize) - 1;
+        const int32_t sh = a.tile_shift;
+        const int32_t mask = (1 << sh) - 1;
+        const char *kbase = static_cast<const char *>(a.k_cache) + ((size_t)g << sh) * TILE_BYTES;
+        const char *vbase = static_cast<const char *>(a.v_cache) + ((size_t)g << sh) * TILE_BYTES;
+        const size_t bstride = ((size_t)a.num_kv_heads << sh) * TILE_BYTES;
+        const int32_t jb0 = uniform(t0 / kTile);
+        const int32_t last = uniform((t1 + kTile - 1) / kTile) - 1;
         t1 = uniform(t1);
         const float sc = a.score_scale;
         const uint32_t nblocks = (uint32_t)a.num_blocks;
 
-        auto id_of = [&](int32_t jb) -> int32_t { return uniform(table[uniform(min(jb, last))]); };
-        auto valid_of = [&](int32_t jb) { return min(kBlockSize, t1 - jb * kBlockSize); };
-        auto load = [&](int32_t phys, Tile &T) {
-            load_tile(kbase + (size_t)phys * bstride, vbase + (size_t)phys * bstride, col, grp, T);
+        auto id_of = [&](int32_t jb) -> int32_t {
+            return uniform(table[uniform(min(jb, last) >> sh)]);
+        };
+        auto sub_of = [&](int32_t jb) -> size_t {
+            return (size_t)(min(jb, last) & mask) * TILE_BYTES;
+        };
+        auto valid_of = [&](int32_t jb) { return min(kTile, t1 - jb * kTile); };
+        auto load = [&](int32_t phys, size_t sub, Tile &T) {
+            const size_t o = (size_t)phys * bstride + sub;
+            load_tile(kbase + o, vbase + o, col, grp, T);
         };
 
         // Two tiles alternate: while one is computed, the next is in flight.
-        // The loop runs over pairs of blocks and has one exit, at the
+        // The loop runs over pairs of tiles and has one exit, at the
         // bottom; the next load is issued on every path (past the end it
-        // re-reads the last block, an L2 hit).  A load issued on one path
+        // re-reads the last tile, an L2 hit).  A load issued on one path
         // only, or an exit that shares a block with the back edge, would make
         // the compiler's wait counts assume a shorter queue and wait for the
         // next tile before the current one is done.  An entry outside the
         // pool is recorded and block 0 read in its place (the caller turns
         // the result into NaN), so no early exit is needed either.
         Tile A, B;
-        const int32_t n = last - jb0 + 1; // blocks in the range, >= 1
+        const int32_t n = last - jb0 + 1; // tiles in the range, >= 1
         bool bad = false;
         auto checked = [&](int32_t id) {
             const bool out = (uint32_t)id >= nblocks;
@@ -364,34 +375,34 @@ struct MfmaWave {
             return out ? 0 : id;
         };
         // The step's token (position t1 - 1) when this range ends the
-        // sequence: checked against its slot, put into the last block's
-        // registers when that block is computed, stored after the loop.
+        // sequence: checked against its slot, put into the last tile's
+        // registers when that tile is computed, stored after the loop.
         bool put = false;
         NewToken nt;
         int32_t id_last = 0;
+        const int32_t off_last = (t1 - 1) & ((kTile << sh) - 1); // in its block
         if (append_here) {
             const int32_t slot = uniform(((const CI32 *)a.slots)[b]);
             id_last = id_of(last);
-            const int32_t off = (t1 - 1) % kBlockSize;
             if (slot >= 0) {
-                if ((uint32_t)id_last >= nblocks || slot != id_last * kBlockSize + off)
+                if ((uint32_t)id_last >= nblocks || slot != (id_last << sh) * kTile + off_last)
                     bad = true;
                 else
                     put = true;
             }
             if (put)
-                load_new_token(a, b, g, off, nt);
+                load_new_token(a, b, g, (t1 - 1) % kTile, nt);
         }
-        load(checked(id_of(jb0)), A);
+        load(checked(id_of(jb0)), sub_of(jb0), A);
         int32_t idB = id_of(jb0 + 1);
         for (int32_t i = 0; i + 1 < n; i = uniform(i + 2)) {
             const int32_t jb = jb0 + i;
             const int32_t idA = id_of(jb + 2);
-            load(checked(idB), B);
+            load(checked(idB), sub_of(jb + 1), B);
             __builtin_amdgcn_sched_barrier(0); // B's loads go out before A is waited for
             compute(A, valid_of(jb), sc);
             idB = id_of(jb + 3);
-            load(checked(idA), A);
+            load(checked(idA), sub_of(jb + 2), A);
             __builtin_amdgcn_sched_barrier(0);
             if (put && jb + 1 == last)
                 apply_new_token(B, nt);
@@ -400,7 +411,7 @@ struct MfmaWave {
         if (n & 1) {
             if (put)
                 apply_new_token(A, nt);
-            compute(A, valid_of(last), sc); // A holds the last block
+            compute(A, valid_of(last), sc); // A holds the last tile
         }
         // Drain the re-read issued past the end (n even), so no load into
         // these registers is in flight when the next range starts.
@@ -410,8 +421,8 @@ struct MfmaWave {
             store_token<QT, KT, D>(static_cast<const TQ *>(a.k_new) + row,
                                    static_cast<const TQ *>(a.v_new) + row,
                                    const_cast<void *>(a.k_cache), const_cast<void *>(a.v_cache),
-                                   id_last, (t1 - 1) % kBlockSize, g, a.num_kv_heads, a.k_inv,
-                                   a.v_inv, col + 16 * grp);
+                                   id_last, off_last, sh, g, a.num_kv_heads, a.k_inv, a.v_inv,
+                                   col + 16 * grp);
         }
         return !bad;
     }
@@ -478,7 +489,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a, int32_t 
 }
 
 // Balanced split: wave i of W takes tiles [i*T/W, (i+1)*T/W) of the list of
-// all (sequence, KV head, block) tiles in that order, T tiles in total.
+// all (sequence, KV head, 16-token tile) tiles in that order, T tiles in total.
 template <int QT, int KT, int D>
 __global__ __launch_bounds__(256)
 void decode_mfma_balanced_kernel(DecodeArgs a, int32_t W)
@@ -500,7 +511,7 @@ void decode_mfma_balanced_kernel(DecodeArgs a, int32_t W)
     MfmaWave<QT, KT, D> wv(lane);
     int64_t x = rs.x0;
     while (x < x1) {
-        const int32_t nb = blocks_of(pos.n);
+        const int32_t nb = tiles_of(pos.n);
         const int64_t local = x - pos.first_tile;
         const int32_t g = (int32_t)(local / nb);
         const int32_t j = (int32_t)(local % nb);
@@ -508,7 +519,7 @@ void decode_mfma_balanced_kernel(DecodeArgs a, int32_t W)
         const int64_t stop = min(x1, seg_end);
         const int32_t je = j + (int32_t)(stop - x);
         wv.start(a, pos.b, g);
-        const bool ok = wv.run(a, pos.b, g, j * kBlockSize, min(je * kBlockSize, pos.n),
+        const bool ok = wv.run(a, pos.b, g, j * kTile, min(je * kTile, pos.n),
                                a.append && je == nb);
         wv.finish();
         if (j == 0 && je == nb) {

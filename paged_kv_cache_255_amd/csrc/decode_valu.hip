@@ -6,9 +6,10 @@
 // query against the cached K/V) and §4 "The PagedAttention CUDA Kernel" (the
 // query walks its block table and reads K/V from scattered physical blocks).
 // The softmax is evaluated online (running max m, running sum l, rescaled
-// accumulator), one 16-token block at a time, in log2 units.
+// accumulator), one 16-token tile at a time, in log2 units.  A cache block of
+// 16 << k tokens is 1 << k consecutive tiles of the layout below.
 //
-// Lane layout inside a wave, per 16-token block:
+// Lane layout inside a wave, per 16-token tile:
 //   K tile [16][D]: lane = 4 * token + c; lane c of a quad reads 16-byte
 //     chunks c, c+4, c+8, ... of its token's row, so each load instruction
 //     covers 64 contiguous bytes of every row.  Partial dot products are
@@ -31,12 +32,12 @@ struct ValuShape {
     static constexpr int CHUNKS = ROW_BYTES / 16;     // 16-byte chunks in a K row
     static constexpr int CH_PER_LANE = CHUNKS / 4;
     static constexpr int EPC = 16 / KE;               // elements per chunk
-    static constexpr int V_ROW_BYTES = kBlockSize * KE; // one V^T row (16 tokens)
+    static constexpr int V_ROW_BYTES = kTile * KE; // one V^T row (16 tokens)
     static constexpr int V_LPR = V_ROW_BYTES / 16;    // lanes per V^T row
-    static constexpr int V_TPL = kBlockSize / V_LPR;  // tokens per lane
+    static constexpr int V_TPL = kTile / V_LPR;  // tokens per lane
     static constexpr int V_RPI = kWave / V_LPR;       // rows per load instruction
     static constexpr int V_INSTR = D / V_RPI;
-    static constexpr int TILE_BYTES = kBlockSize * D * KE;
+    static constexpr int TILE_BYTES = kTile * D * KE;
     static_assert(CH_PER_LANE >= 1 && CHUNKS % 4 == 0, "K row too short for quad layout");
     static_assert(V_INSTR >= 1 && D % V_RPI == 0, "V tile layout");
 };
@@ -46,7 +47,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a, int32_t 
 {
     using S = ValuShape<QT, KT, D, G>;
     using TQ = typename S::TQ;
-    __shared__ float p_lds[4][G][kBlockSize];
+    __shared__ float p_lds[4][G][kTile];
 
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -92,18 +93,21 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a, int32_t 
     const int32_t *table = a.block_tables + (size_t)it.b * a.max_blocks_per_seq;
     const char *kbase = static_cast<const char *>(a.k_cache);
     const char *vbase = static_cast<const char *>(a.v_cache);
-    const int32_t jb0 = it.t0 / kBlockSize;
-    const int32_t jb1 = bad ? jb0 : (it.t1 + kBlockSize - 1) / kBlockSize;
+    const int32_t sh = a.tile_shift; // a block is 1 << sh tiles
+    const int32_t jb0 = it.t0 / kTile;
+    const int32_t jb1 = bad ? jb0 : (it.t1 + kTile - 1) / kTile;
 
     for (int32_t jb = jb0; jb < jb1; ++jb) {
-        const int32_t phys = __builtin_amdgcn_readfirstlane(table[jb]);
+        const int32_t phys = __builtin_amdgcn_readfirstlane(table[jb >> sh]);
         if (phys < 0 || phys >= a.num_blocks) {
             bad = true;
             break;
         }
-        const size_t tile = ((size_t)phys * a.num_kv_heads + it.g) * S::TILE_BYTES;
-        const int32_t tok_base = jb * kBlockSize;
-        const bool tail = tok_base + kBlockSize > it.t1;
+        const size_t tile =
+            ((((size_t)phys * a.num_kv_heads + it.g) << sh) + (jb & ((1 << sh) - 1))) *
+            S::TILE_BYTES;
+        const int32_t tok_base = jb * kTile;
+        const bool tail = tok_base + kTile > it.t1;
 
         // K tile: this lane's chunks of token tq.
         float kv[S::CH_PER_LANE][S::EPC];
@@ -135,7 +139,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a, int32_t 
             d += shfl_xor(d, 2);
             s[h] = tok_ok ? d : -INFINITY;
         }
-        // online softmax update, block max over the whole wave
+        // online softmax update, tile max over the whole wave
         float pr[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) {

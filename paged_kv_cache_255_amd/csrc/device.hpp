@@ -10,7 +10,10 @@
 namespace pa {
 
 constexpr int kWave = 64;     // CDNA wavefront width
-constexpr int kBlockSize = 16; // tokens per KV block (the only size built)
+// Tokens per tile, the kernels' unit of work.  A cache block of block_size
+// tokens (16, 32, 64, 128 or 256) is block_size / 16 consecutive tiles, each
+// with the same layout as a 16-token block.
+constexpr int kTile = 16;
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));

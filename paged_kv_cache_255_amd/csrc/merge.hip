@@ -181,8 +181,8 @@ __global__ __launch_bounds__(64) void merge_kernel(DecodeArgs a)
         const TileCounts tc = tile_counts(a, lane, b);
         const int64_t T = tc.total;
         const int32_t R = effective_runs(T, a.waves);
-        const int64_t S0 = tc.before + (int64_t)g * blocks_of(n);
-        const int64_t S1 = S0 + blocks_of(n);
+        const int64_t S0 = tc.before + (int64_t)g * tiles_of(n);
+        const int64_t S1 = S0 + tiles_of(n);
         const int64_t i0 = run_of_tile(S0, T, R);
         const int64_t i1 = run_of_tile(S1 - 1, T, R);
         if (i0 == i1)
@@ -218,9 +218,9 @@ __global__ __launch_bounds__(64) void merge_segment_kernel(DecodeArgs a)
         const TileCounts tc = tile_counts(a, lane, b);
         const int64_t T = tc.total;
         const int32_t R = effective_runs(T, a.waves);
-        const int64_t S0 = tc.before + (int64_t)g * blocks_of(n);
+        const int64_t S0 = tc.before + (int64_t)g * tiles_of(n);
         const int64_t i0 = run_of_tile(S0, T, R);
-        const int64_t i1 = run_of_tile(S0 + blocks_of(n) - 1, T, R);
+        const int64_t i1 = run_of_tile(S0 + tiles_of(n) - 1, T, R);
         if (i0 == i1)
             return; // one run held the whole segment and wrote the rows itself
         w0 = i0 + (int64_t)b * a.num_kv_heads + g;

@@ -20,16 +20,14 @@
 
 // Identity of a cached full block ([devto] §5 "Automatic Prefix Caching":
 // a table of physical blocks looked up by their tokens): the cached block
-// that holds the 16 tokens before it (-1 for a sequence's first block) and
-// its own 16 token ids.  Chaining by the parent's physical id makes equal
-// keys mean equal whole prefixes, and equality is exact (no lossy hash).
+// that holds the block_size tokens before it (-1 for a sequence's first
+// block) and its own block_size token ids.  Chaining by the parent's physical
+// id makes equal keys mean equal whole prefixes, and equality is exact (no
+// lossy hash).
 struct BlockKey {
     int32_t parent;
-    int32_t tokens[16];
-    bool operator==(const BlockKey &o) const
-    {
-        return parent == o.parent && std::memcmp(tokens, o.tokens, sizeof(tokens)) == 0;
-    }
+    std::vector<int32_t> tokens;
+    bool operator==(const BlockKey &o) const { return parent == o.parent && tokens == o.tokens; }
 };
 
 struct BlockKeyHash {
@@ -186,8 +184,9 @@ pa_status pa_block_pool_init(const pa_pool_config *cfg, pa_pool **out)
         return pa::fail(PA_ERR_INVALID_ARG, "pool sizes must be positive");
     if (pa::dtype_bytes(cfg->kv_dtype) == 0)
         return pa::fail(PA_ERR_INVALID_ARG, "unknown kv dtype");
-    if (cfg->block_size != 16)
-        return pa::fail(PA_ERR_UNSUPPORTED, "block_size must be 16");
+    if (cfg->block_size != 16 && cfg->block_size != 32 && cfg->block_size != 64 &&
+        cfg->block_size != 128 && cfg->block_size != 256)
+        return pa::fail(PA_ERR_UNSUPPORTED, "block_size must be 16, 32, 64, 128 or 256");
     if ((int64_t)cfg->num_blocks * cfg->block_size > INT32_MAX)
         return pa::fail(PA_ERR_INVALID_ARG, "num_blocks * block_size overflows int32 slots");
     pa_pool *p = new (std::nothrow) pa_pool();
@@ -394,7 +393,7 @@ pa_status pa_prefix_register(pa_pool *p, int32_t seq, const int32_t *tokens, int
     for (int32_t i = 0; i < ntok / bs; ++i) {
         BlockKey key;
         key.parent = prev;
-        std::memcpy(key.tokens, tokens + (size_t)i * bs, sizeof(key.tokens));
+        key.tokens.assign(tokens + (size_t)i * bs, tokens + (size_t)(i + 1) * bs);
         auto it = p->prefix.find(key);
         if (it != p->prefix.end()) {
             prev = it->second;
@@ -432,7 +431,7 @@ pa_status pa_prefix_match(pa_pool *p, int32_t seq, const int32_t *tokens, int32_
     for (int32_t i = 0; i < ntok / bs; ++i) {
         BlockKey key;
         key.parent = prev;
-        std::memcpy(key.tokens, tokens + (size_t)i * bs, sizeof(key.tokens));
+        key.tokens.assign(tokens + (size_t)i * bs, tokens + (size_t)(i + 1) * bs);
         auto it = p->prefix.find(key);
         if (it == p->prefix.end())
             break;

@@ -20,6 +20,7 @@ struct DecodeArgs {
     int32_t num_kv_heads;
     int32_t group;             // num_q_heads / num_kv_heads
     int32_t num_blocks;
+    int32_t tile_shift;        // log2(block_size / 16): a block is 1 << tile_shift tiles
     int32_t max_blocks_per_seq;
     int32_t max_seq_len;
     int32_t partition;         // tokens per work item; 0 = whole sequence; -1 = balanced
@@ -30,7 +31,7 @@ struct DecodeArgs {
     float v_scale;
     // Appending decode: the step's new token of sequence b (k_new, v_new:
     // [num_seqs][Hkv][D] in the q dtype) goes to slot slots[b], written by
-    // the wave whose range holds the sequence's last block.
+    // the wave whose range holds the sequence's last tile.
     int32_t append;
     const void *k_new;
     const void *v_new;
@@ -43,16 +44,16 @@ constexpr int32_t kPartitionBalanced = -1; // PA_PARTITION_BALANCED
 __device__ __forceinline__ bool len_ok(const DecodeArgs &a, int32_t n)
 {
     return n >= 0 && n <= a.max_seq_len &&
-           (int64_t)n <= (int64_t)a.max_blocks_per_seq * kBlockSize;
+           (int64_t)n <= ((int64_t)a.max_blocks_per_seq << a.tile_shift) * kTile;
 }
 
-__device__ __forceinline__ int32_t blocks_of(int32_t n) { return (n + kBlockSize - 1) / kBlockSize; }
+__device__ __forceinline__ int32_t tiles_of(int32_t n) { return (n + kTile - 1) / kTile; }
 
-// Blocks a sequence contributes to the balanced split; a length out of range
+// Tiles a sequence contributes to the balanced split; a length out of range
 // contributes none (the merge kernel writes that row as NaN).
-__device__ __forceinline__ int32_t split_blocks(const DecodeArgs &a, int32_t n)
+__device__ __forceinline__ int32_t split_tiles(const DecodeArgs &a, int32_t n)
 {
-    return len_ok(a, n) ? blocks_of(n) : 0;
+    return len_ok(a, n) ? tiles_of(n) : 0;
 }
 
 __device__ __forceinline__ int64_t wave_sum(int64_t v)
@@ -81,13 +82,13 @@ __device__ __forceinline__ int64_t readlane64(int64_t v, int l)
     return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-// Tiles (KV head x block) of sequences [0, upto), summed by one wave.
+// Tiles (KV head x 16-token tile) of sequences [0, upto), summed by one wave.
 __device__ __forceinline__ int64_t tiles_before(const DecodeArgs &a, int lane, int32_t upto)
 {
     int64_t t = 0;
     for (int32_t c = 0; c < upto; c += kWave) {
         const int32_t b = c + lane;
-        t += (b < upto) ? split_blocks(a, a.seq_lens[b]) : 0;
+        t += (b < upto) ? split_tiles(a, a.seq_lens[b]) : 0;
     }
     return wave_sum(t) * a.num_kv_heads;
 }
@@ -105,7 +106,7 @@ __device__ __forceinline__ TileCounts tile_counts(const DecodeArgs &a, int lane,
     int64_t before = 0, total = 0;
     for (int32_t c = 0; c < a.num_seqs; c += kWave) {
         const int32_t s = c + lane;
-        const int64_t t = (s < a.num_seqs) ? split_blocks(a, a.seq_lens[s]) : 0;
+        const int64_t t = (s < a.num_seqs) ? split_tiles(a, a.seq_lens[s]) : 0;
         total += t;
         before += (s < b) ? t : 0;
     }
@@ -126,7 +127,7 @@ __device__ __forceinline__ SeqPos locate_tile(const DecodeArgs &a, int lane, int
     for (int32_t c = 0; c < a.num_seqs; c += kWave) {
         const int32_t b = c + lane;
         const int64_t tiles =
-            (b < a.num_seqs) ? (int64_t)split_blocks(a, a.seq_lens[b]) * a.num_kv_heads : 0;
+            (b < a.num_seqs) ? (int64_t)split_tiles(a, a.seq_lens[b]) * a.num_kv_heads : 0;
         const int64_t incl = wave_incl_scan(tiles, lane);
         const uint64_t hit = __ballot(b < a.num_seqs && carry + incl > x);
         if (hit) {
@@ -167,7 +168,7 @@ __device__ __forceinline__ RunStart run_start(const DecodeArgs &a, int lane, int
     if (a.num_seqs <= kWave) {
         const bool in = lane < a.num_seqs;
         const int32_t n = in ? a.seq_lens[lane] : 0;
-        const int64_t tiles = in ? (int64_t)split_blocks(a, n) * a.num_kv_heads : 0;
+        const int64_t tiles = in ? (int64_t)split_tiles(a, n) * a.num_kv_heads : 0;
         const int64_t incl = wave_incl_scan(tiles, lane);
         r.T = readlane64(incl, kWave - 1);
         r.runs = effective_runs(r.T, W);
@@ -196,9 +197,9 @@ __device__ __forceinline__ RunStart run_start(const DecodeArgs &a, int lane, int
 __device__ __forceinline__ SeqPos next_sequence(const DecodeArgs &a, SeqPos p)
 {
     SeqPos q;
-    q.first_tile = p.first_tile + (int64_t)blocks_of(p.n) * a.num_kv_heads;
+    q.first_tile = p.first_tile + (int64_t)tiles_of(p.n) * a.num_kv_heads;
     q.b = p.b + 1;
-    while (q.b < a.num_seqs && split_blocks(a, uniform_load(a.seq_lens + q.b)) == 0)
+    while (q.b < a.num_seqs && split_tiles(a, uniform_load(a.seq_lens + q.b)) == 0)
         ++q.b;
     q.n = q.b < a.num_seqs ? uniform_load(a.seq_lens + q.b) : 0;
     return q;

@@ -22,7 +22,7 @@ TOL = {"f32": ("rowrel", 1e-5), "f16": ("abs", 1e-2), "bf16": ("abs", 1e-2),
 
 
 def cache_bytes(w):
-    return w.num_blocks * w.num_kv_heads * 16 * w.head_dim * EB[w.kv_dtype]
+    return w.num_blocks * w.num_kv_heads * w.block_size * w.head_dim * EB[w.kv_dtype]
 
 
 def poisoned_device_cache(w, device="cuda"):
@@ -64,6 +64,7 @@ class GpuStep:
         self.w = w
         self.partition = w.partition_size if partition is None else partition
         self.pool = pa.pa_block_pool_init(w.num_blocks, w.num_kv_heads, w.head_dim, w.kv_dtype,
+                                          block_size=w.block_size,
                                           shuffle_seed=w.shuffle_seeds[layer])
         ids, pre = execute_plan(self.pool, w.ops)
         self.dec = [ids[s] for s in w.decode_seqs]
@@ -72,7 +73,7 @@ class GpuStep:
         self.tables, self.lens = pa.pa_export_block_tables(self.pool, self.dec,
                                                            w.max_blocks_per_seq())
         self.desc = pa.kv_desc(w.num_q_heads, w.num_kv_heads, w.head_dim, w.num_blocks,
-                               w.q_dtype, w.kv_dtype, kernel=kernel)
+                               w.q_dtype, w.kv_dtype, block_size=w.block_size, kernel=kernel)
         self.inputs = inputs
         self.k_cache = poisoned_device_cache(w)
         self.v_cache = poisoned_device_cache(w)
@@ -145,7 +146,7 @@ class OracleStep:
 
     def __init__(self, w, layer, inputs, only=None):
         self.w = w
-        m = am.PoolModel(w.num_blocks, 16, w.shuffle_seeds[layer])
+        m = am.PoolModel(w.num_blocks, w.block_size, w.shuffle_seeds[layer])
         mids, mpre = am.execute_plan(m, w.ops)
         self.pre_slots = np.array(mpre, dtype=np.int32)
         mdec = [mids[s] for s in w.decode_seqs]
@@ -178,7 +179,7 @@ class OracleStep:
             pre_slots = pre_slots[idx]
             tidx = torch.from_numpy(idx).to(kp.device)
             kp, vp = kp.index_select(0, tidx), vp.index_select(0, tidx)
-        common = dict(num_kv_heads=w.num_kv_heads, head_dim=w.head_dim, block_size=16,
+        common = dict(num_kv_heads=w.num_kv_heads, head_dim=w.head_dim, block_size=w.block_size,
                       num_blocks=w.num_blocks, kv_dtype=w.kv_dtype, in_dtype=w.q_dtype,
                       k_scale=i.k_scale, v_scale=i.v_scale)
         oracle.cache_append(workloads.storage(kp), workloads.storage(vp), self.k_cache,
@@ -193,7 +194,7 @@ class OracleStep:
             rows = [(b, h) for b in self.only for h in range(w.num_q_heads)]
         return oracle.decode(workloads.storage(i.q), self.k_cache, self.v_cache, self.tables,
                              self.lens, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
-                             head_dim=w.head_dim, block_size=16, num_blocks=w.num_blocks,
+                             head_dim=w.head_dim, block_size=w.block_size, num_blocks=w.num_blocks,
                              q_dtype=w.q_dtype, kv_dtype=w.kv_dtype, scale=w.scale,
                              k_scale=i.k_scale, v_scale=i.v_scale, rows=rows)
 
@@ -202,7 +203,7 @@ class OracleStep:
         pos = range(self.w.num_seqs) if self.only is None else self.only
         ids = set()
         for b in pos:
-            n = -(-int(self.lens[b]) // 16)
+            n = -(-int(self.lens[b]) // self.w.block_size)
             ids.update(int(x) for x in self.tables[b][:n])
         return sorted(ids)
 
@@ -229,7 +230,7 @@ def check_close(got, ref, kv_dtype, q_dtype):
 
 def compare_cache_blocks(gpu_cache, host_cache, w, blocks):
     """Byte-exact comparison of the given physical blocks."""
-    per_block = w.num_kv_heads * 16 * w.head_dim * EB[w.kv_dtype]
+    per_block = w.num_kv_heads * w.block_size * w.head_dim * EB[w.kv_dtype]
     g = as_bytes(gpu_cache).reshape(w.num_blocks, per_block)
     h = host_cache.view(np.uint8).reshape(w.num_blocks, per_block)
     if blocks is None:

@@ -49,9 +49,13 @@ def test_error_codes():
     with pytest.raises(pa.PaError) as e:
         pa.pa_block_pool_init(0, 8, 128, "bf16")
     assert e.value.status == pa.ERR_INVALID_ARG
-    with pytest.raises(pa.PaError) as e:
-        pa.pa_block_pool_init(16, 8, 128, "bf16", block_size=32)
-    assert e.value.status == pa.ERR_UNSUPPORTED
+    for bs in (8, 48, 512):
+        with pytest.raises(pa.PaError) as e:
+            pa.pa_block_pool_init(16, 8, 128, "bf16", block_size=bs)
+        assert e.value.status == pa.ERR_UNSUPPORTED
+    for bs in (16, 32, 64, 128, 256):
+        p = pa.pa_block_pool_init(16, 8, 128, "bf16", block_size=bs)
+        assert pa.pa_block_bytes(p) == bs * 8 * 128 * 2
     p = pa.pa_block_pool_init(4, 1, 64, "f32", shuffle_seed=3)
     s = pa.pa_seq_create(p)
     pa.pa_seq_append_slots(p, s, 60)
@@ -91,11 +95,12 @@ def _compare(pool, model, ids, mids, max_blocks):
         assert pa.pa_block_refcount(pool, b) == model.refcount[b]
 
 
-def test_pool_matches_model_on_random_operations():
+@pytest.mark.parametrize("bs", [16, 64])
+def test_pool_matches_model_on_random_operations(bs):
     rng = np.random.default_rng(7)
     NB = 400
-    pool = pa.pa_block_pool_init(NB, 2, 64, "bf16", shuffle_seed=987654321)
-    model = am.PoolModel(NB, 16, 987654321)
+    pool = pa.pa_block_pool_init(NB, 2, 64, "bf16", block_size=bs, shuffle_seed=987654321)
+    model = am.PoolModel(NB, bs, 987654321)
     live = []  # (lib id, model id)
     copies_seen = 0
     for it in range(1500):
@@ -142,14 +147,15 @@ def test_pool_matches_model_on_random_operations():
     assert copies_seen > 20  # forks at any length: copy on write was exercised
 
 
-def test_pool_matches_model_with_prefix_cache():
+@pytest.mark.parametrize("bs", [16, 32])
+def test_pool_matches_model_with_prefix_cache(bs):
     """Register, match and evict (with appends, forks, frees and copies)
     give the same tables, refcounts, stats and copies in the library and in
     the model."""
     rng = np.random.default_rng(13)
     NB = 200
-    pool = pa.pa_block_pool_init(NB, 2, 64, "bf16", shuffle_seed=55)
-    model = am.PoolModel(NB, 16, 55)
+    pool = pa.pa_block_pool_init(NB, 2, 64, "bf16", block_size=bs, shuffle_seed=55)
+    model = am.PoolModel(NB, bs, 55)
     systems = [[int(x) for x in rng.integers(0, 30, size=n)] for n in (16, 40, 70)]
     live = []  # (lib id, model id, tokens)
     hits = 0

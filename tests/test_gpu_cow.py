@@ -25,13 +25,13 @@ def say(*a):
     print(*a, flush=True)
 
 
-@pytest.mark.parametrize("kv", ["bf16", "e4m3"])
-def test_copy_blocks_kernel(kv):
-    say(f"[case] copy_blocks kv={kv}")
+@pytest.mark.parametrize("kv,bs", [("bf16", 16), ("e4m3", 16), ("bf16", 256)])
+def test_copy_blocks_kernel(kv, bs):
+    say(f"[case] copy_blocks kv={kv} block_size={bs}")
     NB, Hkv, D = 40, 4, 128
-    desc = pa.kv_desc(8, Hkv, D, NB, "bf16", kv)
+    desc = pa.kv_desc(8, Hkv, D, NB, "bf16", kv, block_size=bs)
     eb = 1 if kv == "e4m3" else 2
-    nbytes = NB * Hkv * 16 * D * eb
+    nbytes = NB * Hkv * bs * D * eb
     g = torch.Generator().manual_seed(11)
     k = torch.randint(0, 256, (nbytes,), generator=g, dtype=torch.uint8)
     v = torch.randint(0, 256, (nbytes,), generator=g, dtype=torch.uint8)
@@ -40,7 +40,7 @@ def test_copy_blocks_kernel(kv):
     pairs = np.array([[3, 10], [3, 11], [17, 2], [39, 0], [5, 40]], dtype=np.int32)
     pa.pa_copy_blocks(kd, vd, torch.from_numpy(pairs).cuda(), desc)
     torch.cuda.synchronize()
-    blk = Hkv * 16 * D * eb
+    blk = Hkv * bs * D * eb
     wk, wv = k.numpy().reshape(NB, blk).copy(), v.numpy().reshape(NB, blk).copy()
     for s, d in pairs:
         if 0 <= s < NB and 0 <= d < NB:
@@ -49,29 +49,32 @@ def test_copy_blocks_kernel(kv):
     np.testing.assert_array_equal(vd.cpu().numpy().reshape(NB, blk), wv)
 
 
-@pytest.mark.parametrize("kv,kernel,part", [("bf16", pa.KERNEL_MFMA, pa.PARTITION_BALANCED),
-                                            ("bf16", pa.KERNEL_VALU, 0),
-                                            ("e4m3", pa.KERNEL_MFMA, 0)])
-def test_branches_append_into_a_shared_partial_block(kv, kernel, part):
+@pytest.mark.parametrize("kv,kernel,part,bs", [("bf16", pa.KERNEL_MFMA, pa.PARTITION_BALANCED, 16),
+                                               ("bf16", pa.KERNEL_VALU, 0, 16),
+                                               ("e4m3", pa.KERNEL_MFMA, 0, 16),
+                                               ("bf16", pa.KERNEL_MFMA, pa.PARTITION_BALANCED, 64),
+                                               ("e4m3", pa.KERNEL_VALU, 64, 64)])
+def test_branches_append_into_a_shared_partial_block(kv, kernel, part, bs):
     """A 20-token prompt (second block partly filled) forked into three
     branches; each step appends one token to every sequence.  The pool's
     tables, slots and copies match the model's; after the copies and appends
     the caches match the oracle's byte for byte and the decode matches the
     oracle's output."""
-    say(f"[case] copy-on-write branches kv={kv} kernel={kernel} partition={part}")
+    say(f"[case] copy-on-write branches kv={kv} kernel={kernel} partition={part} bs={bs}")
     Hq, Hkv, D, NB = 8, 2, 128, 24
     qd = "bf16"
-    pool = pa.pa_block_pool_init(NB, Hkv, D, kv, shuffle_seed=4242)
-    model = am.PoolModel(NB, 16, 4242)
-    desc = pa.kv_desc(Hq, Hkv, D, NB, qd, kv, kernel=kernel)
+    pool = pa.pa_block_pool_init(NB, Hkv, D, kv, block_size=bs, shuffle_seed=4242)
+    model = am.PoolModel(NB, bs, 4242)
+    desc = pa.kv_desc(Hq, Hkv, D, NB, qd, kv, block_size=bs, kernel=kernel)
 
     def tensor(shape, seed):
         return workloads.normal(shape, seed, qd, "cuda")
 
-    kc, vc = poisoned_device_cache(_W(NB, Hkv, D, kv)), poisoned_device_cache(_W(NB, Hkv, D, kv))
-    hk, hv = poisoned_host_cache(_W(NB, Hkv, D, kv)), poisoned_host_cache(_W(NB, Hkv, D, kv))
+    shape = _W(NB, Hkv, D, kv, bs)
+    kc, vc = poisoned_device_cache(shape), poisoned_device_cache(shape)
+    hk, hv = poisoned_host_cache(shape), poisoned_host_cache(shape)
     k_scale = v_scale = (1.0 / 64 if kv == "e4m3" else 1.0)
-    common = dict(num_kv_heads=Hkv, head_dim=D, block_size=16, num_blocks=NB, kv_dtype=kv,
+    common = dict(num_kv_heads=Hkv, head_dim=D, block_size=bs, num_blocks=NB, kv_dtype=kv,
                   in_dtype=qd, k_scale=k_scale, v_scale=v_scale)
 
     def write(slots, k, v):
@@ -129,7 +132,7 @@ def test_branches_append_into_a_shared_partial_block(kv, kernel, part):
                  scale, out, desc, k_scale, v_scale, workspace=ws, partition_size=part)
     torch.cuda.synchronize()
     ref = oracle.decode(workloads.storage(q), hk, hv, tables, lens, num_q_heads=Hq,
-                        num_kv_heads=Hkv, head_dim=D, block_size=16, num_blocks=NB,
+                        num_kv_heads=Hkv, head_dim=D, block_size=bs, num_blocks=NB,
                         q_dtype=qd, kv_dtype=kv, scale=scale, k_scale=k_scale, v_scale=v_scale)
     check_close(to_f64(out), ref, kv, qd)
 
@@ -137,5 +140,6 @@ def test_branches_append_into_a_shared_partial_block(kv, kernel, part):
 class _W:
     """The cache shape fields poisoned_*_cache read."""
 
-    def __init__(self, nb, hkv, d, kv):
+    def __init__(self, nb, hkv, d, kv, bs=16):
         self.num_blocks, self.num_kv_heads, self.head_dim, self.kv_dtype = nb, hkv, d, kv
+        self.block_size = bs

@@ -31,8 +31,9 @@ def say(*a):
 
 
 class _W:
-    def __init__(self, nb, hkv, d, kv):
+    def __init__(self, nb, hkv, d, kv, bs):
         self.num_blocks, self.num_kv_heads, self.head_dim, self.kv_dtype = nb, hkv, d, kv
+        self.block_size = bs
 
 
 def _prefix_seed(tokens, i, which):
@@ -46,11 +47,12 @@ def _kv_rows(tokens, lo, hi, Hkv, D, qd):
     return torch.stack(k).cuda(), torch.stack(v).cuda()
 
 
-@pytest.mark.parametrize("kv,kernel,part", [("bf16", pa.KERNEL_MFMA, pa.PARTITION_BALANCED),
-                                            ("bf16", pa.KERNEL_VALU, 0),
-                                            ("e4m3", pa.KERNEL_MFMA, pa.PARTITION_BALANCED)])
-def test_prefix_matched_requests_decode_like_fully_written_ones(kv, kernel, part):
-    say(f"[case] prefix cache kv={kv} kernel={kernel} partition={part}")
+@pytest.mark.parametrize("kv,kernel,part,bs", [("bf16", pa.KERNEL_MFMA, pa.PARTITION_BALANCED, 16),
+                                               ("bf16", pa.KERNEL_VALU, 0, 16),
+                                               ("e4m3", pa.KERNEL_MFMA, pa.PARTITION_BALANCED, 16),
+                                               ("bf16", pa.KERNEL_MFMA, pa.PARTITION_BALANCED, 32)])
+def test_prefix_matched_requests_decode_like_fully_written_ones(kv, kernel, part, bs):
+    say(f"[case] prefix cache kv={kv} kernel={kernel} partition={part} block_size={bs}")
     Hq, Hkv, D, NB = 8, 2, 128, 48  # group 4: both kernels
     qd = "bf16"
     rng = np.random.default_rng(77)
@@ -59,13 +61,14 @@ def test_prefix_matched_requests_decode_like_fully_written_ones(kv, kernel, part
     prompt_b = system + [int(x) for x in rng.integers(0, 1000, size=13)]  # 53 tokens
     prompt_d = prompt_a[:48]                                               # only full cached blocks
 
-    pool = pa.pa_block_pool_init(NB, Hkv, D, kv, shuffle_seed=99)
-    model = am.PoolModel(NB, 16, 99)
-    desc = pa.kv_desc(Hq, Hkv, D, NB, qd, kv, kernel=kernel)
-    kc, vc = poisoned_device_cache(_W(NB, Hkv, D, kv)), poisoned_device_cache(_W(NB, Hkv, D, kv))
-    hk, hv = poisoned_host_cache(_W(NB, Hkv, D, kv)), poisoned_host_cache(_W(NB, Hkv, D, kv))
+    pool = pa.pa_block_pool_init(NB, Hkv, D, kv, block_size=bs, shuffle_seed=99)
+    model = am.PoolModel(NB, bs, 99)
+    desc = pa.kv_desc(Hq, Hkv, D, NB, qd, kv, block_size=bs, kernel=kernel)
+    shape = _W(NB, Hkv, D, kv, bs)
+    kc, vc = poisoned_device_cache(shape), poisoned_device_cache(shape)
+    hk, hv = poisoned_host_cache(shape), poisoned_host_cache(shape)
     k_scale = v_scale = (1.0 / 64 if kv == "e4m3" else 1.0)
-    common = dict(num_kv_heads=Hkv, head_dim=D, block_size=16, num_blocks=NB, kv_dtype=kv,
+    common = dict(num_kv_heads=Hkv, head_dim=D, block_size=bs, num_blocks=NB, kv_dtype=kv,
                   in_dtype=qd, k_scale=k_scale, v_scale=v_scale)
     written = []
 
@@ -94,9 +97,12 @@ def test_prefix_matched_requests_decode_like_fully_written_ones(kv, kernel, part
     b, mb, hit_b = admit(prompt_b)
     c, mc, _ = admit(prompt_b, use_cache=False)
     d, md, hit_d = admit(prompt_d)
-    assert (hit_a, hit_b, hit_d) == (0, 32, 48)
-    assert written == [50, 21, 53, 0]
-    assert pa.pa_pool_get_stats(pool)["cached_blocks"] == model.stats()["cached_blocks"] == 4
+    # full blocks inside the 40 shared tokens; d's 48 tokens are all a's
+    hb, hd = (40 // bs) * bs, (48 // bs) * bs
+    assert (hit_a, hit_b, hit_d) == (0, hb, hd)
+    assert written == [50, 53 - hb, 53, 48 - hd]
+    n_cached = 50 // bs + 53 // bs - hb // bs  # a's full blocks, then b's beyond the match
+    assert pa.pa_pool_get_stats(pool)["cached_blocks"] == model.stats()["cached_blocks"] == n_cached
     assert len(pa.pa_pool_take_copies(pool)) == 0
 
     # every request takes one more token (decode with the fused append)
@@ -106,15 +112,16 @@ def test_prefix_matched_requests_decode_like_fully_written_ones(kv, kernel, part
     slots_c = pa.pa_seq_append_slots(pool, c, 1)
     assert list(slots_c) == model.append_slots(mc, 1)[1]
     assert len(pa.pa_pool_take_copies(pool)) == 0  # matched blocks are full: no copy
-    maxb = 4
+    maxb = -(-54 // bs)
     tables, lens = pa.pa_export_block_tables(pool, seqs, maxb)
     np.testing.assert_array_equal(tables, np.array(model.export(mseqs, maxb)[1], dtype=np.int32))
     tables_c, lens_c = pa.pa_export_block_tables(pool, [a, c, d], maxb)
     assert list(lens) == list(lens_c) == [51, 54, 49]
     np.testing.assert_array_equal(tables_c, np.array(model.export([ma, mc, md], maxb)[1],
                                                      dtype=np.int32))
-    assert list(tables[1][:2]) == list(tables[0][:2]) and list(tables[2][:3]) == list(tables[0][:3])
-    assert not set(tables[1][:3]) & set(tables_c[1][:3])  # c shares nothing with b
+    assert list(tables[1][:hb // bs]) == list(tables[0][:hb // bs])
+    assert list(tables[2][:hd // bs]) == list(tables[0][:hd // bs])
+    assert not (set(tables[1]) & set(tables_c[1])) - {-1}  # c shares nothing with b
 
     B = 3
     q = workloads.normal((B, Hq, D), 501, qd, "cuda")
@@ -144,18 +151,18 @@ def test_prefix_matched_requests_decode_like_fully_written_ones(kv, kernel, part
     np.testing.assert_array_equal(kc.view(torch.uint8).cpu().numpy(), hk.view(np.uint8))
     np.testing.assert_array_equal(vc.view(torch.uint8).cpu().numpy(), hv.view(np.uint8))
     ref = oracle.decode(workloads.storage(q), hk, hv, tables, lens, num_q_heads=Hq,
-                        num_kv_heads=Hkv, head_dim=D, block_size=16, num_blocks=NB,
+                        num_kv_heads=Hkv, head_dim=D, block_size=bs, num_blocks=NB,
                         q_dtype=qd, kv_dtype=kv, scale=scale, k_scale=k_scale, v_scale=v_scale)
     check_close(to_f64(outs[0]), ref, kv, qd)
 
-    # eviction leaves mapped blocks alone: all four cached blocks are still in tables
+    # eviction leaves mapped blocks alone: every cached block is still in a table
     assert pa.pa_prefix_evict(pool, NB) == model.prefix_evict(NB) == 0
     for s, m in ((a, ma), (b, mb), (c, mc), (d, md)):
         pa.pa_seq_free(pool, s)
         model.free_seq(m)
     st = pa.pa_pool_get_stats(pool)
-    assert st["cached_blocks"] == 4 and st["free_blocks"] == NB - 4
+    assert st["cached_blocks"] == n_cached and st["free_blocks"] == NB - n_cached
     # once no table maps them they go, leaves first
-    assert pa.pa_prefix_evict(pool, NB) == model.prefix_evict(NB) == 4
+    assert pa.pa_prefix_evict(pool, NB) == model.prefix_evict(NB) == n_cached
     st = pa.pa_pool_get_stats(pool)
     assert st["cached_blocks"] == 0 and st["free_blocks"] == NB == model.stats()["free_blocks"]

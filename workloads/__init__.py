@@ -110,8 +110,8 @@ class Workload:
         return (self.seed * 1000 + layer * 10 + tags[what]) & 0x7FFFFFFF
 
 
-def _pool_blocks(lengths, slack):
-    need = sum(-(-n // BLOCK_SIZE) for n in lengths)
+def _pool_blocks(lengths, slack, bs):
+    need = sum(-(-n // bs) for n in lengths)
     return int(math.ceil(slack * need))
 
 
@@ -121,7 +121,7 @@ def _independent(name, cid, lens_pre, nblocks_slack, **kw):
         ops.append(("create",))
         ops.append(("prefill", i, int(n)))
     lens_dec = [int(n) + 1 for n in lens_pre]
-    nb = kw.pop("num_blocks", None) or _pool_blocks(lens_dec, nblocks_slack)
+    nb = kw.pop("num_blocks", None) or _pool_blocks(lens_dec, nblocks_slack, kw["block_size"])
     return Workload(name=name, config_id=cid, num_blocks=nb, ops=ops,
                     decode_seqs=list(range(len(lens_pre))), **kw)
 
@@ -135,31 +135,38 @@ def _shared_prefix(name, cid, prefix_len, suffixes, slack, **kw):
     ops.append(("free", 0))
     for c, s in zip(children, suffixes):
         ops.append(("prefill", c, int(s)))
-    need = -(-prefix_len // BLOCK_SIZE) + sum(
-        -(-(prefix_len + int(s) + 1) // BLOCK_SIZE) - prefix_len // BLOCK_SIZE for s in suffixes)
+    bs = kw["block_size"]
+    need = -(-prefix_len // bs) + sum(
+        -(-(prefix_len + int(s) + 1) // bs) - prefix_len // bs for s in suffixes)
     nb = int(math.ceil(slack * need))
     return Workload(name=name, config_id=cid, num_blocks=nb, ops=ops, decode_seqs=children,
                     **kw)
 
 
-def config(cid, size="full"):
+def config(cid, size="full", block_size=BLOCK_SIZE):
     """The five workloads; size="small" gives a reduced variant of the same
-    shape that the oracle finishes in seconds (several tiles, ragged tails)."""
+    shape that the oracle finishes in seconds (several tiles, ragged tails).
+    block_size (16 by default, as in the pages' workloads) changes only how
+    many tokens a physical block holds; lengths and tensors stay the same."""
     seed = 1000 + cid + (0 if size == "full" else 500)
     rng = np.random.default_rng(seed)
+    bs = block_size
     if cid == 1:
         # Tiny fp32 MHA step: 4 heads, head_dim 64, lengths {17,33,64,100}
-        # before the append, blocks permuted in a 64-block pool.
-        w = _independent("tiny-fp32-mha", 1, [17, 33, 64, 100], 1.0, num_blocks=64,
+        # before the append, blocks permuted in a 64-block pool (the same
+        # 1024 slots at other block sizes, at least 4 spare blocks).
+        nb = max(64 * 16 // bs, _pool_blocks([18, 34, 65, 101], 1.0, bs) + 4)
+        w = _independent("tiny-fp32-mha", 1, [17, 33, 64, 100], 1.0, num_blocks=nb,
                          num_q_heads=4, num_kv_heads=4, head_dim=64, q_dtype="f32",
-                         kv_dtype="f32", seed=seed, partition_size=0)
+                         kv_dtype="f32", seed=seed, partition_size=0, block_size=bs)
     elif cid == 2:
         # Llama-3-8B layer (dev.to §2 Example 2): 32 q heads on 8 KV heads,
         # head_dim 128, bf16; lengths uniform in [512, 4096], pool 1.25x.
         B, lo, hi = (32, 512, 4096) if size == "full" else (5, 20, 700)
         lens = rng.integers(lo, hi + 1, size=B)
         w = _independent("llama3-8b-gqa-bf16", 2, lens, 1.25, num_q_heads=32, num_kv_heads=8,
-                         head_dim=128, q_dtype="bf16", kv_dtype="bf16", seed=seed)
+                         head_dim=128, q_dtype="bf16", kv_dtype="bf16", seed=seed,
+                         block_size=bs)
     elif cid == 3:
         # Llama-2-13B MHA (dev.to §2 Example 1): 40 heads, head_dim 128, fp16,
         # 8 sequences at exactly 4096 tokens, all 40 layers, a pool per layer
@@ -167,7 +174,7 @@ def config(cid, size="full"):
         B, n, L = (8, 4096, 40) if size == "full" else (3, 300, 2)
         w = _independent("llama2-13b-mha-fp16", 3, [n - 1] * B, 1.0, num_q_heads=40,
                          num_kv_heads=40, head_dim=128, q_dtype="f16", kv_dtype="f16",
-                         seed=seed, num_layers=L)
+                         seed=seed, num_layers=L, block_size=bs)
     elif cid == 4:
         # 256 sequences sharing a 2048-token prefix by reference count
         # (dev.to §5), each with its own suffix, geometric with mean 350
@@ -176,7 +183,7 @@ def config(cid, size="full"):
         suf = np.minimum(rng.geometric(1.0 / mean, size=B), 2048)
         w = _shared_prefix("prefix-sharing-bf16", 4, P, suf, 1.25, num_q_heads=32,
                            num_kv_heads=8, head_dim=128, q_dtype="bf16", kv_dtype="bf16",
-                           seed=seed)
+                           seed=seed, block_size=bs)
     elif cid == 5:
         # Long context (hyperinfer.ai "Why this matters for long context"):
         # 70B-shaped layer, 64 q heads on 8 KV heads, FP8 E4M3 KV, bf16 q,
@@ -184,7 +191,7 @@ def config(cid, size="full"):
         B, n = (4, 131072) if size == "full" else (2, 1500)
         w = _independent("long-context-fp8-70b", 5, [n - 1] * B, 1.0, num_q_heads=64,
                          num_kv_heads=8, head_dim=128, q_dtype="bf16", kv_dtype="e4m3",
-                         seed=seed)
+                         seed=seed, block_size=bs)
     else:
         raise ValueError(cid)
     w.shuffle_seeds = [seed * 7919 + layer + 1 for layer in range(w.num_layers)]
