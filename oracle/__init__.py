@@ -79,7 +79,7 @@ def _load():
         lib.orc_cache_append.argtypes = [ctypes.POINTER(_CacheDesc), P, P, P, P, P,
                                          ctypes.c_int32, ctypes.c_float, ctypes.c_float]
         lib.orc_decode.restype = ctypes.c_int
-        lib.orc_decode.argtypes = [ctypes.POINTER(_DecodeDesc), P, P, P, P, P,
+        lib.orc_decode.argtypes = [ctypes.POINTER(_DecodeDesc), P, P, P, P, P, P,
                                    ctypes.c_double, ctypes.c_double, ctypes.c_double,
                                    P, ctypes.c_int64, P, ctypes.c_int]
         _lib = lib
@@ -143,10 +143,12 @@ def cache_append(k_new, v_new, k_cache, v_cache, slot_mapping, *, num_kv_heads, 
 # -- decode --------------------------------------------------------------
 def decode(q, k_cache, v_cache, block_tables, seq_lens, *, num_q_heads, num_kv_heads,
            head_dim, block_size, num_blocks, q_dtype, kv_dtype, scale, k_scale=1.0,
-           v_scale=1.0, rows=None, nthreads=0):
+           v_scale=1.0, rows=None, nthreads=0, seq_starts=None):
     """fp64 attention output, [B][Hq][D] (or [len(rows)][D] for a row list).
 
-    rows: optional iterable of (b, h) pairs to compute."""
+    rows: optional iterable of (b, h) pairs to compute.  seq_starts: optional
+    [B] window starts (tokens before them are left out; start = length gives
+    a zero row)."""
     _check_storage(q, q_dtype)
     _check_storage(k_cache, kv_dtype)
     _check_storage(v_cache, kv_dtype)
@@ -155,6 +157,10 @@ def decode(q, k_cache, v_cache, block_tables, seq_lens, *, num_q_heads, num_kv_h
     B = lens.shape[0]
     assert tables.ndim == 2 and tables.shape[0] == B
     assert q.size == B * num_q_heads * head_dim
+    starts = None
+    if seq_starts is not None:
+        starts = np.ascontiguousarray(seq_starts, dtype=np.int32)
+        assert starts.shape == (B,)
     desc = _DecodeDesc(B, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                        tables.shape[1], DTYPES[q_dtype], DTYPES[kv_dtype])
     if rows is None:
@@ -166,7 +172,8 @@ def decode(q, k_cache, v_cache, block_tables, seq_lens, *, num_q_heads, num_kv_h
         nrows = row_ids.shape[0]
         out = np.zeros((nrows, head_dim), dtype=np.float64)
     rc = _load().orc_decode(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
-                            _ptr(tables), _ptr(lens), float(scale), float(k_scale),
+                            _ptr(tables), _ptr(lens), None if starts is None else _ptr(starts),
+                            float(scale), float(k_scale),
                             float(v_scale), None if row_ids is None else _ptr(row_ids),
                             nrows, _ptr(out), int(nthreads))
     if rc != 0:

@@ -53,6 +53,26 @@ restates it (it is what makes the tables reproducible):
     the next value of a counter; evict drops, one at a time, the block with
     the lowest stamp (ties: lower id) among cached blocks that only the cache
     maps and that no cached key names as parent.
+  * Sliding window (vaibhawkumar.in, "Why LLMs run out of VRAM: KV cache
+    fragmentation and the PagedAttention fix", "PagedAttention: the idea"
+    and its truncate sketch: sliding the window releases whole leading
+    pages; the cut inside the first kept page only moves its start).  A
+    sequence keeps its length (the positions it has seen), a window start
+    and a count of released leading blocks; its table maps the blocks from
+    the first kept one.  slide_window(w) moves the start to length - w (never
+    backwards) and releases, in order, every leading block that lies wholly
+    before the start.  The export gives lengths and starts relative to the
+    first kept block.  A sequence with a moved window can no longer register
+    its prefix.
+  * Swapping (hyperinfer.ai "What 16-token blocks buy you": swapping to CPU
+    memory goes block by block).  A second pool of host blocks, ids 0..H-1,
+    free list [0, ..., H-1], allocation from the end, frees appended in table
+    order.  swap_out takes a host block for every block of the table, in
+    table order, gives the pairs (device, host), then drops the device
+    blocks in table order; it needs an empty copy queue (the copies are made
+    first).  swap_in takes device blocks from the free list, in table order,
+    gives the pairs (host, device), then frees the host blocks in table
+    order.  A swapped-out sequence can only be swapped in or freed.
 """
 
 MASK64 = (1 << 64) - 1
@@ -84,7 +104,7 @@ def kv_bytes_per_token(layers, kv_heads, head_dim, elem_bytes):
 
 
 class PoolModel:
-    def __init__(self, num_blocks, block_size, shuffle_seed):
+    def __init__(self, num_blocks, block_size, shuffle_seed, num_host_blocks=0):
         self.num_blocks = num_blocks
         self.block_size = block_size
         free = list(range(num_blocks))
@@ -100,9 +120,14 @@ class PoolModel:
         self.next_id = 0
         self.copies = []  # queued (source, destination) block copies
         self.held = []    # unreferenced blocks a queued copy still reads
-        self.prefix = {}  # (parent block, 16 tokens) -> cached block
+        self.prefix = {}  # (parent block, block_size tokens) -> cached block
         self.cache = {}   # cached block -> [key, stamp, cached children]
         self.clock = 0
+        self.starts = {}  # seq id -> window start (a position)
+        self.dropped = {}  # seq id -> leading blocks released by the window
+        self.swapped = set()  # seq ids whose tables hold host block ids
+        self.num_host_blocks = num_host_blocks
+        self.host_free = list(range(num_host_blocks))
 
     # -- sequences -------------------------------------------------------
     def seq_create(self):
@@ -110,7 +135,12 @@ class PoolModel:
         self.next_id += 1
         self.tables[sid] = []
         self.lens[sid] = 0
+        self.starts[sid] = 0
+        self.dropped[sid] = 0
         return sid
+
+    def _resident(self, sid):
+        return sid in self.tables and sid not in self.swapped
 
     def _blocks_for(self, ntokens):
         return -(-ntokens // self.block_size)
@@ -122,11 +152,12 @@ class PoolModel:
                 and self.refcount[table[-1]] > 1)
 
     def _check_append(self, sid, ntok):
-        if sid not in self.tables or ntok < 0:
+        if not self._resident(sid) or ntok < 0:
             return ERR_INVALID_ARG, 0
         n = self.lens[sid]
         extra = 1 if self._shared_tail(sid, ntok) else 0
-        return OK, self._blocks_for(n + ntok) - len(self.tables[sid]) + extra
+        return OK, (self._blocks_for(n + ntok) - self.dropped[sid] - len(self.tables[sid])
+                    + extra)
 
     def _drop(self, blk):
         """One table stops mapping blk."""
@@ -149,14 +180,15 @@ class PoolModel:
             table[-1] = mine
             self.copies.append((shared, mine))
             self._drop(shared)
-        need = self._blocks_for(n + ntok) - len(table)
+        first = self.dropped[sid]  # logical block of table[0]
+        need = self._blocks_for(n + ntok) - first - len(table)
         for _ in range(need):
             blk = self.free.pop()
             self.refcount[blk] = 1
             table.append(blk)
         slots = []
         for pos in range(n, n + ntok):
-            slots.append(table[pos // self.block_size] * self.block_size
+            slots.append(table[pos // self.block_size - first] * self.block_size
                          + pos % self.block_size)
         self.lens[sid] = n + ntok
         return slots
@@ -188,11 +220,13 @@ class PoolModel:
         return OK, out
 
     def fork(self, parent):
-        if parent not in self.tables:
+        if not self._resident(parent):
             return ERR_INVALID_ARG, -1
         child = self.seq_create()
         self.tables[child] = list(self.tables[parent])
         self.lens[child] = self.lens[parent]
+        self.starts[child] = self.starts[parent]
+        self.dropped[child] = self.dropped[parent]
         for blk in self.tables[child]:
             self.refcount[blk] += 1
         return OK, child
@@ -200,11 +234,64 @@ class PoolModel:
     def free_seq(self, sid):
         if sid not in self.tables:
             return ERR_INVALID_ARG
-        for blk in self.tables[sid]:
-            self._drop(blk)
+        if sid in self.swapped:
+            self.host_free.extend(self.tables[sid])
+            self.swapped.discard(sid)
+        else:
+            for blk in self.tables[sid]:
+                self._drop(blk)
         del self.tables[sid]
         del self.lens[sid]
+        del self.starts[sid]
+        del self.dropped[sid]
         return OK
+
+    # -- sliding window and swapping ---------------------------------------
+    def slide_window(self, sid, window):
+        """Keeps the last `window` positions in the window; returns (status,
+        blocks released)."""
+        if not self._resident(sid) or window < 0:
+            return ERR_INVALID_ARG, 0
+        bs = self.block_size
+        self.starts[sid] = max(self.starts[sid], self.lens[sid] - window)
+        released = 0
+        table = self.tables[sid]
+        while table and self.starts[sid] - self.dropped[sid] * bs >= bs:
+            self._drop(table.pop(0))
+            self.dropped[sid] += 1
+            released += 1
+        return OK, released
+
+    def swap_out(self, sid):
+        """Returns (status, [(device block, host block)]) in table order."""
+        if not self._resident(sid) or self.copies:
+            return ERR_INVALID_ARG, []
+        table = self.tables[sid]
+        if len(table) > len(self.host_free):
+            return ERR_OUT_OF_BLOCKS, []
+        pairs = [(blk, self.host_free.pop()) for blk in table]
+        for blk in table:
+            self._drop(blk)
+        self.tables[sid] = [h for _, h in pairs]
+        self.swapped.add(sid)
+        return OK, pairs
+
+    def swap_in(self, sid):
+        """Returns (status, [(host block, device block)]) in table order."""
+        if sid not in self.swapped:
+            return ERR_INVALID_ARG, []
+        hosts = self.tables[sid]
+        if len(hosts) > len(self.free):
+            return ERR_OUT_OF_BLOCKS, []
+        pairs = []
+        for h in hosts:
+            blk = self.free.pop()
+            self.refcount[blk] = 1
+            pairs.append((h, blk))
+        self.host_free.extend(hosts)
+        self.tables[sid] = [d for _, d in pairs]
+        self.swapped.discard(sid)
+        return OK, pairs
 
     def take_copies(self):
         """The queued copies, in order; clears them and frees held blocks."""
@@ -222,7 +309,8 @@ class PoolModel:
     def prefix_register(self, sid, tokens):
         """Caches the full blocks of sid's first len(tokens) tokens; returns
         (status, blocks newly cached)."""
-        if sid not in self.tables or len(tokens) > self.lens[sid]:
+        if (not self._resident(sid) or len(tokens) > self.lens[sid] or self.starts[sid] != 0
+                or self.dropped[sid] != 0):
             return ERR_INVALID_ARG, 0
         added, parent = 0, -1
         bs = self.block_size
@@ -248,7 +336,7 @@ class PoolModel:
     def prefix_match(self, sid, tokens):
         """Maps the cached chain matching tokens into the empty sid; returns
         (status, tokens matched)."""
-        if sid not in self.tables or self.lens[sid] != 0:
+        if not self._resident(sid) or self.lens[sid] != 0:
             return ERR_INVALID_ARG, 0
         parent = -1
         bs = self.block_size
@@ -280,33 +368,40 @@ class PoolModel:
         return n
 
     # -- export ----------------------------------------------------------
-    def export(self, sids, max_blocks):
-        """(status, tables[nseq][max_blocks] padded with -1, lens)."""
-        tables, lens = [], []
+    def export(self, sids, max_blocks, with_starts=False):
+        """(status, tables[nseq][max_blocks] padded with -1, lens) and, with
+        with_starts, the window starts as a fourth item; lengths and starts
+        count from the first kept block."""
+        tables, lens, starts = [], [], []
         for sid in sids:
-            if sid not in self.tables:
-                return ERR_INVALID_ARG, None, None
+            if not self._resident(sid):
+                return (ERR_INVALID_ARG, None, None) + ((None,) if with_starts else ())
             t = self.tables[sid]
             if len(t) > max_blocks:
-                return ERR_CAPACITY, None, None
+                return (ERR_CAPACITY, None, None) + ((None,) if with_starts else ())
             tables.append(t + [-1] * (max_blocks - len(t)))
-            lens.append(self.lens[sid])
-        return OK, tables, lens
+            base = self.dropped[sid] * self.block_size
+            lens.append(self.lens[sid] - base)
+            starts.append(self.starts[sid] - base)
+        return (OK, tables, lens) + ((starts,) if with_starts else ())
 
     def stats(self):
         used = self.num_blocks - len(self.free)
-        mapped = sum(len(t) for t in self.tables.values())
+        res = [s for s in self.tables if s not in self.swapped]
+        bs = self.block_size
         return {
             "num_blocks": self.num_blocks,
             "free_blocks": len(self.free),
             "used_blocks": used,
             "shared_blocks": sum(1 for r in self.refcount if r > 1),
-            "cached_blocks": len(self.cache),
             "live_seqs": len(self.tables),
-            "logical_tokens": sum(self.lens.values()),
-            "mapped_blocks": mapped,
-            "tail_slack_tokens": sum(len(self.tables[s]) * self.block_size - self.lens[s]
-                                     for s in self.tables),
+            "cached_blocks": len(self.cache),
+            "swapped_seqs": len(self.swapped),
+            "free_host_blocks": len(self.host_free),
+            "logical_tokens": sum(self.lens[s] - self.starts[s] for s in self.tables),
+            "mapped_blocks": sum(len(self.tables[s]) for s in res),
+            "tail_slack_tokens": sum((self.dropped[s] + len(self.tables[s])) * bs - self.lens[s]
+                                     for s in res),
         }
 
 

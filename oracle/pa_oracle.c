@@ -322,6 +322,10 @@ int orc_cache_append(const orc_cache_desc *c, const void *k_new, const void *v_n
 /*   out = softmax(q K^T * scale) V          ([devto] §1, attention eq.)    */
 /*   token t of sequence b lives in physical block table[b][t / bs] at      */
 /*   offset t % bs                           ([devto] §4, block table)      */
+/*   With a window start w (optional), only tokens w..n-1 take part: the    */
+/*   sliding window keeps the most recent tokens; the earlier ones of the   */
+/*   first kept block stay stored but are left out ([vk] "PagedAttention:   */
+/*   the idea" and its truncate sketch).  w = n gives a zero row.           */
 /* ---------------------------------------------------------------------- */
 
 typedef struct {
@@ -339,7 +343,7 @@ typedef struct {
 typedef struct {
     const orc_decode_desc *d;
     const void *q, *k_cache, *v_cache;
-    const int32_t *block_tables, *seq_lens;
+    const int32_t *block_tables, *seq_lens, *seq_starts;
     double scale, k_scale, v_scale;
     const int32_t *rows; /* NULL: all rows b*Hq+h; else list of row ids */
     int64_t num_rows;
@@ -360,15 +364,16 @@ static int decode_row(const decode_job *J, int64_t row, double *out_row, double 
     int g = h / G;
     int D = d->head_dim;
     int64_t n = J->seq_lens[b];
+    int64_t w = J->seq_starts ? J->seq_starts[b] : 0; /* first token of the window */
     orc_cache_desc c = {d->num_blocks, d->block_size, d->num_kv_heads, D, d->kv_dtype,
                         d->q_dtype};
 
     for (int i = 0; i < D; ++i)
         out_row[i] = 0.0;
-    if (n == 0)
-        return 0;
-    if (n < 0 || n > (int64_t)d->max_blocks_per_seq * d->block_size)
+    if (n < 0 || n > (int64_t)d->max_blocks_per_seq * d->block_size || w < 0 || w > n)
         return -1;
+    if (w == n)
+        return 0;
 
     const int32_t *table = J->block_tables + (size_t)b * d->max_blocks_per_seq;
     size_t qbase = ((size_t)b * d->num_q_heads + h) * D;
@@ -379,7 +384,7 @@ static int decode_row(const decode_job *J, int64_t row, double *out_row, double 
         qv[i] = orc_load(d->q_dtype, J->q, qbase + i);
 
     /* scores s_t = scale * sum_d q[d] * (k_scale * K_t[d]) */
-    for (int64_t t = 0; t < n; ++t) {
+    for (int64_t t = w; t < n; ++t) {
         int64_t blk = table[t / d->block_size];
         int o = (int)(t % d->block_size);
         if (blk < 0 || blk >= d->num_blocks)
@@ -393,16 +398,16 @@ static int decode_row(const decode_job *J, int64_t row, double *out_row, double 
     }
     /* softmax weights w_t = exp(s_t - max s) / sum */
     double m = -INFINITY;
-    for (int64_t t = 0; t < n; ++t)
+    for (int64_t t = w; t < n; ++t)
         if (s[t] > m)
             m = s[t];
     double Z = 0.0;
-    for (int64_t t = 0; t < n; ++t) {
+    for (int64_t t = w; t < n; ++t) {
         s[t] = exp(s[t] - m);
         Z += s[t];
     }
     /* out = sum_t w_t * (v_scale * V_t) / Z */
-    for (int64_t t = 0; t < n; ++t) {
+    for (int64_t t = w; t < n; ++t) {
         int64_t blk = table[t / d->block_size];
         int o = (int)(t % d->block_size);
         for (int i = 0; i < D; ++i) {
@@ -445,13 +450,15 @@ static void *decode_worker(void *arg)
 }
 
 /* q: [B][Hq][D] in q_dtype; caches as described above; block_tables:
- * [B][max_blocks_per_seq]; seq_lens: [B].  rows: optional list of row ids
+ * [B][max_blocks_per_seq]; seq_lens: [B]; seq_starts: [B] window starts, or
+ * NULL for windows that start at token 0.  rows: optional list of row ids
  * (b * Hq + h) to compute, or NULL for all B*Hq rows; out: [rows][D] fp64.
  * nthreads <= 0 uses every online CPU.  Returns 0, or -1 on a bad table
  * entry / length, -2 on allocation failure, -3 on a bad shape. */
 int orc_decode(const orc_decode_desc *d, const void *q, const void *k_cache,
                const void *v_cache, const int32_t *block_tables, const int32_t *seq_lens,
-               double scale, double k_scale, double v_scale, const int32_t *rows,
+               const int32_t *seq_starts, double scale, double k_scale, double v_scale,
+               const int32_t *rows,
                int64_t num_rows, double *out, int nthreads)
 {
     if (d->num_kv_heads <= 0 || d->num_q_heads % d->num_kv_heads != 0 || d->head_dim <= 0 ||
@@ -464,6 +471,7 @@ int orc_decode(const orc_decode_desc *d, const void *q, const void *k_cache,
     J.v_cache = v_cache;
     J.block_tables = block_tables;
     J.seq_lens = seq_lens;
+    J.seq_starts = seq_starts;
     J.scale = scale;
     J.k_scale = k_scale;
     J.v_scale = v_scale;

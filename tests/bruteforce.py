@@ -42,7 +42,9 @@ def v_token_major(v_vals, num_kv_heads, head_dim, bs):
 
 
 def attention(q, k_cache, v_cache, tables, lens, *, num_q_heads, num_kv_heads, head_dim,
-              block_size, q_dtype, kv_dtype, scale, k_scale=1.0, v_scale=1.0):
+              block_size, q_dtype, kv_dtype, scale, k_scale=1.0, v_scale=1.0, seq_starts=None):
+    """seq_starts: optional window starts; the rows before them are cut off
+    the gathered K and V before the softmax."""
     B = len(lens)
     G = num_q_heads // num_kv_heads
     qv = decode_storage(q, q_dtype).reshape(B, num_q_heads, head_dim)
@@ -51,10 +53,11 @@ def attention(q, k_cache, v_cache, tables, lens, *, num_q_heads, num_kv_heads, h
     out = np.zeros((B, num_q_heads, head_dim))
     for b in range(B):
         n = int(lens[b])
-        if n == 0:
+        w = 0 if seq_starts is None else int(seq_starts[b])
+        if n == w:
             continue
-        K = gather(kv, tables[b], n, block_size) * k_scale  # [n][Hkv][D]
-        V = gather(vv, tables[b], n, block_size) * v_scale
+        K = gather(kv, tables[b], n, block_size)[w:] * k_scale  # [n - w][Hkv][D]
+        V = gather(vv, tables[b], n, block_size)[w:] * v_scale
         for h in range(num_q_heads):
             g = h // G
             s = K[:, g, :] @ qv[b, h] * scale

@@ -356,3 +356,138 @@ def test_prefix_cached_sequences_read_their_own_tokens():
         for b in range(120):
             assert p.refcount[b] == counts.get(b, 0) + (1 if b in p.cache else 0)
     assert matched_total > 500  # the cache was actually used
+
+
+def test_sliding_window_releases_whole_leading_blocks():
+    """vaibhawkumar.in, "PagedAttention: the idea": sliding the window hands
+    the oldest whole pages back to the allocator; a cut inside the first kept
+    page only moves its start."""
+    p = am.PoolModel(20, 16, 0)  # free list 0..19, taken from the end
+    s = p.seq_create()
+    assert p.append_slots(s, 100)[0] == am.OK
+    assert p.tables[s] == [19, 18, 17, 16, 15, 14, 13]
+    assert p.slide_window(s, 200) == (am.OK, 0)  # a window longer than the sequence
+    assert p.slide_window(s, 40) == (am.OK, 3)   # start 60: blocks of 0..47 go
+    assert p.tables[s] == [16, 15, 14, 13]
+    assert p.free[-3:] == [19, 18, 17]
+    st, t, n, w = p.export([s], 4, with_starts=True)
+    assert (n, w) == ([52], [12])  # from the first kept block (positions 48..)
+    assert p.append_slots(s, 1) == (am.OK, [13 * 16 + 100 % 16])
+    assert p.slide_window(s, 50) == (am.OK, 0)  # never moves the start back
+    assert p.starts[s] == 60
+    assert p.slide_window(s, 0) == (am.OK, 3)   # start 101: blocks of 48..95 go
+    st, t, n, w = p.export([s], 4, with_starts=True)
+    assert t == [[13, -1, -1, -1]] and (n, w) == ([5], [5])  # an empty window
+    st = p.stats()
+    assert st["logical_tokens"] == 0 and st["tail_slack_tokens"] == 11
+    assert p.prefix_register(s, list(range(101)))[0] == am.ERR_INVALID_ARG
+
+
+def test_swap_out_and_in_block_by_block():
+    """hyperinfer.ai, "What 16-token blocks buy you": swapping to CPU memory
+    goes block by block.  The pairs name every block once, in table order."""
+    p = am.PoolModel(10, 16, 0, num_host_blocks=4)
+    s, o = p.seq_create(), p.seq_create()
+    p.append_slots(s, 40)  # blocks 9, 8, 7
+    p.append_slots(o, 1)   # block 6
+    c = p.fork(s)[1]
+    assert p.append_slots(c, 1)[0] == am.OK  # copy on write of block 7 queued
+    assert p.swap_out(s) == (am.ERR_INVALID_ARG, [])  # copies first
+    assert p.take_copies() == [(7, 5)]
+    st, pairs = p.swap_out(s)
+    assert st == am.OK and pairs == [(9, 3), (8, 2), (7, 1)]
+    assert p.refcount[9] == p.refcount[8] == 1  # still mapped by the fork
+    assert p.refcount[7] == 0 and p.free[-1] == 7
+    assert p.append_slots(s, 1)[0] == am.ERR_INVALID_ARG
+    assert p.fork(s)[0] == am.ERR_INVALID_ARG
+    assert p.export([s], 4)[0] == am.ERR_INVALID_ARG
+    st = p.stats()
+    assert st["swapped_seqs"] == 1 and st["free_host_blocks"] == 1 and st["live_seqs"] == 3
+    assert p.swap_out(o) == (am.OK, [(6, 0)])
+    assert p.swap_out(c) == (am.ERR_OUT_OF_BLOCKS, [])  # no host block left
+    free_before = list(p.free)
+    st, pairs = p.swap_in(s)
+    assert st == am.OK and pairs == [(3, free_before[-1]), (2, free_before[-2]),
+                                     (1, free_before[-3])]
+    assert p.host_free == [3, 2, 1]
+    assert p.swap_in(s)[0] == am.ERR_INVALID_ARG
+    assert p.free_seq(o) == am.OK and p.host_free == [3, 2, 1, 0]
+
+
+def test_windows_and_swaps_keep_every_sequence_s_tokens():
+    """Content check: appends, forks (copy on write), frees, window slides,
+    swaps out and in, with the copies and swap transfers applied to a model
+    of device and host memory.  Every resident sequence must read back
+    exactly the tokens of its window."""
+    rng = np.random.default_rng(17)
+    bs = 16
+    p = am.PoolModel(60, bs, 5, num_host_blocks=40)
+    dev, host = {}, {}
+    hist, live = {}, []
+    slides = swaps = 0
+    for step in range(600):
+        writes = []
+        op = rng.integers(0, 12)
+        if op < 2 or not live:
+            s = p.seq_create()
+            live.append(s)
+            hist[s] = []
+        elif op < 6:
+            s = live[rng.integers(len(live))]
+            k = int(rng.integers(1, 30))
+            st, slots = p.append_slots(s, k)
+            if st == am.OK:
+                toks = [int(x) for x in rng.integers(0, 1000, size=k)]
+                writes += list(zip(slots, toks))
+                hist[s] += toks
+        elif op < 7:
+            par = live[rng.integers(len(live))]
+            st, c = p.fork(par)
+            if st == am.OK:
+                live.append(c)
+                hist[c] = list(hist[par])
+        elif op < 8:
+            s = live.pop(rng.integers(len(live)))
+            p.free_seq(s)
+            del hist[s]
+        elif op < 10:
+            s = live[rng.integers(len(live))]
+            if p.slide_window(s, int(rng.integers(0, 60)))[0] == am.OK:
+                slides += 1
+        else:
+            for src, dst in p.take_copies():  # swapping needs the copies made
+                for o in range(bs):
+                    dev[dst * bs + o] = dev.get(src * bs + o)
+            s = live[rng.integers(len(live))]
+            if s in p.swapped:
+                st, pairs = p.swap_in(s)
+                src_mem, dst_mem = host, dev
+            else:
+                st, pairs = p.swap_out(s)
+                src_mem, dst_mem = dev, host
+            if st == am.OK:
+                swaps += 1
+                for a, b in pairs:
+                    for o in range(bs):
+                        dst_mem[b * bs + o] = src_mem.get(a * bs + o)
+        for src, dst in p.take_copies():
+            for o in range(bs):
+                dev[dst * bs + o] = dev.get(src * bs + o)
+        for slot, v in writes:
+            dev[slot] = v
+        for s in live:
+            if s in p.swapped:
+                continue
+            t, first = p.tables[s], p.dropped[s]
+            got = [dev.get(t[i // bs - first] * bs + i % bs)
+                   for i in range(p.starts[s], p.lens[s])]
+            assert got == hist[s][p.starts[s]:], (step, s)
+        counts = {}
+        for s, t in p.tables.items():
+            if s not in p.swapped:
+                for b in t:
+                    counts[b] = counts.get(b, 0) + 1
+        for b in range(p.num_blocks):
+            assert p.refcount[b] == counts.get(b, 0)
+        assert len(p.free) + len(p.held) + len(counts) == p.num_blocks
+    assert slides > 50 and swaps > 50

@@ -30,8 +30,12 @@ MUTANTS = {
                         "int64_t blk = table[(t / d->block_size) / 2];"),
     "offset_in_block": ("int o = (int)(t % d->block_size);",
                         "int o = (int)((t + 1) % d->block_size);"),
-    "last_token_skipped": ("for (int64_t t = 0; t < n; ++t) {\n        int64_t blk",
-                           "for (int64_t t = 0; t < n - 1; ++t) {\n        int64_t blk"),
+    "last_token_skipped": ("for (int64_t t = w; t < n; ++t) {\n        int64_t blk",
+                           "for (int64_t t = w; t < n - 1; ++t) {\n        int64_t blk"),
+    "window_start_ignored": ("int64_t w = J->seq_starts ? J->seq_starts[b] : 0;",
+                             "int64_t w = 0;"),
+    "window_start_off_by_one": ("int64_t w = J->seq_starts ? J->seq_starts[b] : 0;",
+                                "int64_t w = J->seq_starts ? J->seq_starts[b] - (b > 0) : 0;"),
     "k_scale_dropped": ("k_index(&c, blk, g, o, i)) * J->k_scale;", "k_index(&c, blk, g, o, i));"),
     "v_scale_dropped": ("v_index(&c, blk, g, o, i)) * J->v_scale;", "v_index(&c, blk, g, o, i));"),
     "q_decoded_as_kv": ("qv[i] = orc_load(d->q_dtype", "qv[i] = orc_load(d->kv_dtype"),

@@ -403,3 +403,67 @@ def test_block_size_must_be_a_multiple_of_16():
     c = random_case(3, B=1, lens=[5])
     with pytest.raises(ValueError, match=r"\(-3\)"):
         run_oracle(c, block_size=8)
+
+
+# -- sliding window ----------------------------------------------------------------
+@pytest.mark.parametrize("bs", [16, 64])
+@pytest.mark.parametrize("q_dtype,kv_dtype", [("f32", "f32"), ("bf16", "e4m3")])
+def test_window_matches_bruteforce(bs, q_dtype, kv_dtype):
+    """Window starts anywhere in [0, n] (the first kept block partly cut,
+    whole blocks cut, one token left, nothing left): the oracle against the
+    brute force, which slices the gathered rows."""
+    for seed in range(3):
+        c = random_case(300 + seed, bs=bs, B=6, Hq=4, Hkv=2, D=32, q_dtype=q_dtype,
+                        kv_dtype=kv_dtype, max_len=4 * bs)
+        n = c["lens"]
+        rng = np.random.default_rng(seed)
+        starts = np.array([0, n[1], n[2] - 1, n[3] // 2, rng.integers(0, n[4] + 1),
+                           min(bs + 3, n[5])], dtype=np.int32)
+        ks, vs = (0.037, 0.021) if kv_dtype == "e4m3" else (1.0, 1.0)
+        np.testing.assert_allclose(run_oracle(c, k_scale=ks, v_scale=vs, seq_starts=starts),
+                                   run_brute(c, k_scale=ks, v_scale=vs, seq_starts=starts),
+                                   rtol=1e-12, atol=1e-13)
+
+
+def test_window_equals_a_sequence_holding_only_the_window():
+    """Leaving tokens 0..w-1 out gives the same bits as a table whose blocks
+    hold only tokens w..n-1 (appended from offset 0 in new blocks)."""
+    bs, Hq, Hkv, D = 16, 4, 2, 32
+    rng = np.random.default_rng(51)
+    n, w = 150, 37
+    rows_k = random_storage(rng, (n, Hkv, D), "bf16")
+    rows_v = random_storage(rng, (n, Hkv, D), "bf16")
+    q = random_storage(rng, (1, Hq, D), "bf16")
+    NB = 40
+    k = np.zeros((NB, Hkv, bs, D), np.uint16)
+    v = np.zeros(v_shape(NB, Hkv, D, bs), np.uint16)
+    perm = rng.permutation(NB)
+    full = perm[:-(-n // bs)]
+    part = perm[20:20 + -(-(n - w) // bs)]
+    common = dict(num_kv_heads=Hkv, head_dim=D, block_size=bs, num_blocks=NB, kv_dtype="bf16",
+                  in_dtype="bf16")
+    t = np.arange(n)
+    oracle.cache_append(rows_k, rows_v, k, v, (full[t // bs] * bs + t % bs).astype(np.int32),
+                        **common)
+    t = np.arange(n - w)
+    oracle.cache_append(np.ascontiguousarray(rows_k[w:]), np.ascontiguousarray(rows_v[w:]), k, v,
+                        (part[t // bs] * bs + t % bs).astype(np.int32), **common)
+    args = dict(num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=bs, num_blocks=NB,
+                q_dtype="bf16", kv_dtype="bf16", scale=0.125)
+    a = oracle.decode(q, k, v, full[None, :].astype(np.int32), [n], seq_starts=[w], **args)
+    b = oracle.decode(q, k, v, part[None, :].astype(np.int32), [n - w], **args)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_window_closed_forms():
+    """One token in the window: its V row exactly.  An empty window: zeros.
+    A start outside [0, n]: an error."""
+    c = random_case(61, B=2, Hq=2, Hkv=1, D=16, lens=[40, 40])
+    vv = bruteforce.v_token_major(bruteforce.decode_storage(c["v"], "f32"), 1, 16, BS)
+    o = run_oracle(c, seq_starts=[39, 40])
+    t = 39
+    np.testing.assert_allclose(o[0, 0], vv[c["tables"][0][t // BS], 0, t % BS], rtol=0, atol=0)
+    np.testing.assert_array_equal(o[1], 0.0)
+    for bad in ([41, 0], [-1, 0]):
+        with pytest.raises(ValueError, match=r"\(-1\)"):
+            run_oracle(c, seq_starts=bad)
