@@ -167,7 +167,7 @@ def main():
     def host_step(dst_ptr):
         rc = lib.pa_seq_append_slots_batch(pool_h, dec_p, B, 1, dst_ptr)
         rc |= lib.pa_export_block_tables(pool_h, dec_p, B, maxb, dst_ptr + 4 * B,
-                                         dst_ptr + 4 * (B + B * maxb))
+                                         dst_ptr + 4 * (B + B * maxb), None)
         if rc:
             raise RuntimeError("host step failed: " + pa.pa_last_error())
 
@@ -215,11 +215,11 @@ def main():
             kcp, vcp = kc_p[layer * R + r]
             if separate:
                 rc = lib.pa_cache_append(kn, vn, kcp, vcp, slots_p, B, dref, ks, vs, s_h)
-                rc |= lib.pa_decode(qp, kcp, vcp, tables_p, maxb, lens_p, B, max_len, scale,
-                                    ks, vs, op, ws_p, ws_bytes, partition, dref, s_h)
+                rc |= lib.pa_decode(qp, kcp, vcp, tables_p, maxb, lens_p, None, B, max_len,
+                                    scale, ks, vs, op, ws_p, ws_bytes, partition, dref, s_h)
             else:
                 rc = lib.pa_decode_append(qp, kn, vn, slots_p, kcp, vcp, tables_p, maxb, lens_p,
-                                          B, max_len, scale, ks, vs, op, ws_p, ws_bytes,
+                                          None, B, max_len, scale, ks, vs, op, ws_p, ws_bytes,
                                           partition, dref, s_h)
             if rc:
                 raise RuntimeError("launch failed: " + pa.pa_last_error())
@@ -251,11 +251,11 @@ def main():
     def decode_kernel(r, layer):
         kcp, vcp = kc_p[layer * R + r]
         if partition == 0:
-            rc = lib.pa_decode(qp, kcp, vcp, tables_p, maxb, lens_p, B, max_len, scale, ks, vs,
-                               op, None, 0, 0, dref, s_h)
+            rc = lib.pa_decode(qp, kcp, vcp, tables_p, maxb, lens_p, None, B, max_len, scale, ks,
+                               vs, op, None, 0, 0, dref, s_h)
         else:
-            rc = lib.pa_decode_partials(qp, kcp, vcp, tables_p, maxb, lens_p, B, max_len, scale,
-                                        ks, vs, ws_p, ws_bytes, partition, dref, s_h)
+            rc = lib.pa_decode_partials(qp, kcp, vcp, tables_p, maxb, lens_p, None, B, max_len,
+                                        scale, ks, vs, ws_p, ws_bytes, partition, dref, s_h)
         if rc:
             raise RuntimeError("launch failed: " + pa.pa_last_error())
 

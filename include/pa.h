@@ -76,6 +76,7 @@ typedef struct {
     int32_t head_dim;
     pa_dtype kv_dtype;
     uint64_t shuffle_seed; /* 0: free list in id order; else a seeded permutation */
+    int32_t num_host_blocks; /* host swap space in blocks (0: no swapping) */
 } pa_pool_config;
 
 typedef struct {
@@ -83,11 +84,15 @@ typedef struct {
     int32_t free_blocks;
     int32_t used_blocks;       /* blocks with refcount > 0 */
     int32_t shared_blocks;     /* blocks with refcount > 1 */
-    int32_t live_seqs;
-    int32_t cached_blocks; /* blocks the prefix cache holds */
-    int64_t logical_tokens;    /* sum of live sequence lengths */
-    int64_t mapped_blocks;     /* sum of block-table lengths (a shared block counts per table) */
-    int64_t tail_slack_tokens; /* sum over live sequences of unused slots in their blocks */
+    int32_t live_seqs;         /* swapped-out ones included */
+    int32_t cached_blocks;     /* blocks the prefix cache holds */
+    int32_t swapped_seqs;      /* live sequences whose blocks are in host swap space */
+    int32_t free_host_blocks;
+    int64_t logical_tokens;    /* sum over live sequences of the tokens in their windows */
+    int64_t mapped_blocks;     /* sum of device block-table lengths (a shared block counts per
+                                  table) */
+    int64_t tail_slack_tokens; /* sum over resident sequences of unused slots after their last
+                                  token */
 } pa_pool_stats;
 
 /* Creates the pool: every block of the fixed-size physical pool exists from
@@ -157,18 +162,61 @@ pa_status pa_seq_fork(pa_pool *pool, int32_t parent, int32_t *child_out);
  * the copies are taken; a queued copy into a freed block is dropped. */
 pa_status pa_seq_free(pa_pool *pool, int32_t seq);
 
-/* Current length (tokens) of a live sequence. */
+/* Sliding window ([vk] "PagedAttention: the idea": sliding the window
+ * releases the oldest whole pages to the allocator; a cut inside the first
+ * kept page only moves its start, nothing is copied).  Moves the window start
+ * of `seq` to length - window (never backwards) and drops, in table order,
+ * every leading block that lies wholly before the start; each loses one
+ * reference and is freed at zero like a freed sequence's blocks.  Later
+ * appends continue at the sequence's length; pa_export_block_tables gives
+ * the kept blocks with lengths and window starts counted from the first kept
+ * block, and the decode calls take those starts.  A sequence whose window
+ * has moved can no longer register its prefix.  *released_out (may be NULL):
+ * blocks dropped from the table. */
+pa_status pa_seq_slide_window(pa_pool *pool, int32_t seq, int32_t window,
+                              int32_t *released_out);
+
+/* Swapping a sequence out to host memory and back, block by block ([hi]
+ * "What 16-token blocks buy you": swapping to CPU RAM goes one block at a
+ * time, with no contiguous reorganisation).  The pool manages host block ids
+ * 0..num_host_blocks-1 (a free list in id order, taken from and returned to
+ * the end); the caller owns the host memory (pinned, laid out like a cache
+ * of num_host_blocks blocks) and moves the bytes with pa_swap_blocks.
+ *
+ * pa_seq_swap_out: for each block of the table, in order, takes a host block
+ * and writes the pair (device block, host block) to pairs_out; then every
+ * device block loses the table's reference (freed at zero).  The caller must
+ * copy the pairs (pa_swap_blocks, to host) before any later write to those
+ * device blocks (launch it next on the same stream).  Needs an empty
+ * copy-on-write queue (take and make those copies first).  A swapped-out
+ * sequence can only be swapped in or freed.
+ * pa_seq_swap_in: takes a device block for each host block, in table order,
+ * writes the pairs (host block, device block), and frees the host blocks; the
+ * caller copies the pairs (pa_swap_blocks, to device) before the next decode
+ * of the sequence.  The sequence keeps its length and window.
+ * Both: *count_out = blocks of the table; PA_ERR_OUT_OF_BLOCKS if the other
+ * side has too few free blocks, then PA_ERR_CAPACITY if max_pairs is smaller
+ * (or pairs_out NULL); nothing changes on an error. */
+pa_status pa_seq_swap_out(pa_pool *pool, int32_t seq, int32_t *pairs_out, int32_t max_pairs,
+                          int32_t *count_out);
+pa_status pa_seq_swap_in(pa_pool *pool, int32_t seq, int32_t *pairs_out, int32_t max_pairs,
+                         int32_t *count_out);
+
+/* Current length (positions appended so far) of a live sequence. */
 pa_status pa_seq_length(const pa_pool *pool, int32_t seq, int32_t *len_out);
 
 /* Reference count of one physical block. */
 pa_status pa_block_refcount(const pa_pool *pool, int32_t block, int32_t *refcount_out);
 
-/* Writes the block tables of nseq sequences into tables_out
- * [nseq][max_blocks] (int32, entries past a table's end set to -1) and their
- * lengths into lens_out[nseq] (either output may be NULL).
- * PA_ERR_CAPACITY if a table has more than max_blocks entries. */
+/* Writes the block tables of nseq resident sequences into tables_out
+ * [nseq][max_blocks] (int32, entries past a table's end set to -1), their
+ * lengths into lens_out[nseq] and their window starts into starts_out[nseq]
+ * (any output may be NULL).  Lengths and starts count from the first kept
+ * block (see pa_seq_slide_window); without a window they are the length and
+ * 0.  PA_ERR_CAPACITY if a table has more than max_blocks entries. */
 pa_status pa_export_block_tables(const pa_pool *pool, const int32_t *seqs, int32_t nseq,
-                                 int32_t max_blocks, int32_t *tables_out, int32_t *lens_out);
+                                 int32_t max_blocks, int32_t *tables_out, int32_t *lens_out,
+                                 int32_t *starts_out);
 
 pa_status pa_pool_get_stats(const pa_pool *pool, pa_pool_stats *out);
 
@@ -270,14 +318,19 @@ size_t pa_decode_workspace_bytes(const pa_kv_desc *desc, int32_t num_seqs, int32
  * PagedAttention CUDA Kernel": the query reads K and V through the block
  * table):
  *   out[b][h][:] = sum_t w_t * v_scale * V_t / sum_t w_t,
- *   w_t = exp(scale * k_scale * <q[b][h], K_t> - max),  t in [0, seq_lens[b]),
+ *   w_t = exp(scale * k_scale * <q[b][h], K_t> - max),  t in [w_b, seq_lens[b]),
  * with K_t, V_t the rows of KV head h / (Hq / Hkv) found through
- * block_tables[b][t / bs].  A zero-length sequence gives a zero row.
+ * block_tables[b][t / bs], and w_b = seq_starts[b] the window start (0 when
+ * seq_starts is NULL; [vk] "PagedAttention: the idea": a slid window leaves
+ * the earlier tokens of its first kept page out).  A zero-length sequence or
+ * an empty window (w_b = seq_lens[b]) gives a zero row.
  *   q, out: device [num_seqs][Hq][D] in desc->q_dtype (out may not alias q).
  *   block_tables: device int32 [num_seqs][max_blocks_per_seq].
  *   seq_lens: device int32 [num_seqs], each in [0, max_seq_len] and
- *     <= max_blocks_per_seq * block_size; a row whose length or block ids are
- *     out of range is written as NaN instead of being read.
+ *     <= max_blocks_per_seq * block_size; a row whose length, window start or
+ *     block ids are out of range is written as NaN instead of being read.
+ *   seq_starts: device int32 [num_seqs] or NULL; each in [0, seq_lens[b]]
+ *     (not read for zero-length rows).  pa_export_block_tables gives them.
  *   partition_size: PA_PARTITION_NONE, PA_PARTITION_BALANCED, or a positive
  *     multiple of block_size: each (sequence, KV head) is split into chunks
  *     of that many tokens whose partial softmax states are merged by a second
@@ -287,10 +340,10 @@ size_t pa_decode_workspace_bytes(const pa_kv_desc *desc, int32_t num_seqs, int32
  * Accumulation is fp32; out is rounded to nearest even. */
 pa_status pa_decode(const void *q, const void *k_cache, const void *v_cache,
                     const int32_t *block_tables, int32_t max_blocks_per_seq,
-                    const int32_t *seq_lens, int32_t num_seqs, int32_t max_seq_len, float scale,
-                    float k_scale, float v_scale, void *out, void *workspace,
-                    size_t workspace_bytes, int32_t partition_size, const pa_kv_desc *desc,
-                    void *stream);
+                    const int32_t *seq_lens, const int32_t *seq_starts, int32_t num_seqs,
+                    int32_t max_seq_len, float scale, float k_scale, float v_scale, void *out,
+                    void *workspace, size_t workspace_bytes, int32_t partition_size,
+                    const pa_kv_desc *desc, void *stream);
 
 /* Makes the copies pa_pool_take_copies handed out, for one layer's caches:
  * for each pair (src, dst) of the device int32 array pairs[num_pairs][2], the
@@ -300,6 +353,22 @@ pa_status pa_decode(const void *q, const void *k_cache, const void *v_cache,
  * [0, 65535]. */
 pa_status pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *pairs, int32_t num_pairs,
                          const pa_kv_desc *desc, void *stream);
+
+/* Moves the bytes of pa_seq_swap_out / pa_seq_swap_in for one layer's
+ * caches ([hi] "What 16-token blocks buy you": swapping to CPU RAM is block
+ * by block).  host_k, host_v: pinned host memory (hipHostMalloc, e.g. a
+ * pinned torch tensor), each num_host_blocks blocks laid out like the device
+ * caches.  pairs: device int32 [num_pairs][2].  to_host != 0: pairs are
+ * (device block, host block) and each host block's K and V become the device
+ * block's; to_host == 0: pairs are (host block, device block) and the other
+ * way round.  Pairs with ids out of range are skipped.  The kernel reads and
+ * writes the host memory through its device mapping, asynchronously on
+ * `stream`: the host buffers must stay alive and untouched until the stream
+ * has passed it.  PA_ERR_INVALID_ARG if a host buffer is not pinned memory the
+ * device can address; num_pairs in [0, 65535]. */
+pa_status pa_swap_blocks(void *k_cache, void *v_cache, void *host_k, void *host_v,
+                         int32_t num_host_blocks, const int32_t *pairs, int32_t num_pairs,
+                         int32_t to_host, const pa_kv_desc *desc, void *stream);
 
 /* One decode step with the step's append folded in: the same result, cache
  * bytes and output bits as
@@ -320,10 +389,10 @@ pa_status pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *pairs, int
 pa_status pa_decode_append(const void *q, const void *k_new, const void *v_new,
                            const int32_t *slot_mapping, void *k_cache, void *v_cache,
                            const int32_t *block_tables, int32_t max_blocks_per_seq,
-                           const int32_t *seq_lens, int32_t num_seqs, int32_t max_seq_len,
-                           float scale, float k_scale, float v_scale, void *out, void *workspace,
-                           size_t workspace_bytes, int32_t partition_size,
-                           const pa_kv_desc *desc, void *stream);
+                           const int32_t *seq_lens, const int32_t *seq_starts, int32_t num_seqs,
+                           int32_t max_seq_len, float scale, float k_scale, float v_scale,
+                           void *out, void *workspace, size_t workspace_bytes,
+                           int32_t partition_size, const pa_kv_desc *desc, void *stream);
 
 /* A partitioned pa_decode as two launches (same arguments as pa_decode;
  * partition_size must not be PA_PARTITION_NONE and `workspace` as for
@@ -335,10 +404,10 @@ pa_status pa_decode_append(const void *q, const void *k_new, const void *v_new,
  * separately. */
 pa_status pa_decode_partials(const void *q, const void *k_cache, const void *v_cache,
                              const int32_t *block_tables, int32_t max_blocks_per_seq,
-                             const int32_t *seq_lens, int32_t num_seqs, int32_t max_seq_len,
-                             float scale, float k_scale, float v_scale, void *workspace,
-                             size_t workspace_bytes, int32_t partition_size,
-                             const pa_kv_desc *desc, void *stream);
+                             const int32_t *seq_lens, const int32_t *seq_starts,
+                             int32_t num_seqs, int32_t max_seq_len, float scale, float k_scale,
+                             float v_scale, void *workspace, size_t workspace_bytes,
+                             int32_t partition_size, const pa_kv_desc *desc, void *stream);
 pa_status pa_decode_merge(const int32_t *seq_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
                           int32_t max_seq_len, void *out, const void *workspace,
                           size_t workspace_bytes, int32_t partition_size, const pa_kv_desc *desc,

@@ -52,13 +52,14 @@ class PoolConfig(ctypes.Structure):
     _fields_ = [("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("num_layers", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("kv_dtype", ctypes.c_int),
-                ("shuffle_seed", ctypes.c_uint64)]
+                ("shuffle_seed", ctypes.c_uint64), ("num_host_blocks", ctypes.c_int32)]
 
 
 class PoolStats(ctypes.Structure):
     _fields_ = [("num_blocks", ctypes.c_int32), ("free_blocks", ctypes.c_int32),
                 ("used_blocks", ctypes.c_int32), ("shared_blocks", ctypes.c_int32),
                 ("live_seqs", ctypes.c_int32), ("cached_blocks", ctypes.c_int32),
+                ("swapped_seqs", ctypes.c_int32), ("free_host_blocks", ctypes.c_int32),
                 ("logical_tokens", ctypes.c_int64), ("mapped_blocks", ctypes.c_int64),
                 ("tail_slack_tokens", ctypes.c_int64)]
 
@@ -85,20 +86,25 @@ _SIGS = {
     "pa_seq_free": (ctypes.c_int, [_P, _I32]),
     "pa_seq_length": (ctypes.c_int, [_P, _I32, _PI32]),
     "pa_block_refcount": (ctypes.c_int, [_P, _I32, _PI32]),
-    "pa_export_block_tables": (ctypes.c_int, [_P, _P, _I32, _I32, _P, _P]),
+    "pa_export_block_tables": (ctypes.c_int, [_P, _P, _I32, _I32, _P, _P, _P]),
+    "pa_seq_slide_window": (ctypes.c_int, [_P, _I32, _I32, _P]),
+    "pa_seq_swap_out": (ctypes.c_int, [_P, _I32, _P, _I32, _P]),
+    "pa_seq_swap_in": (ctypes.c_int, [_P, _I32, _P, _I32, _P]),
+    "pa_swap_blocks": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _I32, _I32,
+                                      ctypes.POINTER(KvDesc), _P]),
     "pa_pool_get_stats": (ctypes.c_int, [_P, ctypes.POINTER(PoolStats)]),
     "pa_cache_append": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, ctypes.POINTER(KvDesc),
                                        ctypes.c_float, ctypes.c_float, _P]),
     "pa_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(KvDesc), _I32, _I32, _I32]),
-    "pa_decode": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _I32, _I32, ctypes.c_float,
+    "pa_decode": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _P, _I32, _I32, ctypes.c_float,
                                  ctypes.c_float, ctypes.c_float, _P, _P, ctypes.c_size_t, _I32,
                                  ctypes.POINTER(KvDesc), _P]),
-    "pa_decode_partials": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _I32, _I32, ctypes.c_float,
-                                          ctypes.c_float, ctypes.c_float, _P, ctypes.c_size_t,
-                                          _I32, ctypes.POINTER(KvDesc), _P]),
+    "pa_decode_partials": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _P, _I32, _I32,
+                                          ctypes.c_float, ctypes.c_float, ctypes.c_float, _P,
+                                          ctypes.c_size_t, _I32, ctypes.POINTER(KvDesc), _P]),
     "pa_decode_merge": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _P, ctypes.c_size_t, _I32,
                                        ctypes.POINTER(KvDesc), _P]),
-    "pa_decode_append": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _P, _I32, _I32,
+    "pa_decode_append": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _I32, _I32,
                                         ctypes.c_float, ctypes.c_float, ctypes.c_float, _P, _P,
                                         ctypes.c_size_t, _I32, _P, _P]),
     "pa_pool_take_copies": (ctypes.c_int, [_P, _P, _I32, _P]),
@@ -156,9 +162,9 @@ class Pool:
 
 
 def pa_block_pool_init(num_blocks, num_kv_heads, head_dim, kv_dtype, num_layers=1,
-                       block_size=16, shuffle_seed=0):
+                       block_size=16, shuffle_seed=0, num_host_blocks=0):
     cfg = PoolConfig(num_blocks, block_size, num_layers, num_kv_heads, head_dim,
-                     DTYPE_CODES.get(kv_dtype, kv_dtype), shuffle_seed)
+                     DTYPE_CODES.get(kv_dtype, kv_dtype), shuffle_seed, num_host_blocks)
     h = _P()
     _check(_lib.pa_block_pool_init(ctypes.byref(cfg), ctypes.byref(h)), "pa_block_pool_init")
     return Pool(h.value, cfg)
@@ -222,15 +228,50 @@ def pa_block_refcount(pool, block):
     return r.value
 
 
-def pa_export_block_tables(pool, seqs, max_blocks, tables_out=None, lens_out=None):
-    """Returns (tables [nseq][max_blocks] int32, lens [nseq] int32); pass
-    preallocated buffers (numpy or pinned tensors) to fill them in place."""
+def pa_export_block_tables(pool, seqs, max_blocks, tables_out=None, lens_out=None,
+                           starts_out=None, with_starts=False):
+    """Returns (tables [nseq][max_blocks] int32, lens [nseq] int32), and the
+    window starts [nseq] as a third item with with_starts (or starts_out);
+    pass preallocated buffers (numpy or pinned tensors) to fill them in place."""
     seqs = _i32_array(seqs)
     t = tables_out if tables_out is not None else np.empty((len(seqs), max_blocks), np.int32)
     n = lens_out if lens_out is not None else np.empty(len(seqs), np.int32)
+    w = starts_out
+    if w is None and with_starts:
+        w = np.empty(len(seqs), np.int32)
     _check(_lib.pa_export_block_tables(pool.handle, seqs.ctypes.data, len(seqs), max_blocks,
-                                       _addr(t), _addr(n)), "pa_export_block_tables")
-    return t, n
+                                       _addr(t), _addr(n), _addr(w)), "pa_export_block_tables")
+    return (t, n, w) if w is not None else (t, n)
+
+
+def pa_seq_slide_window(pool, seq, window):
+    """Keeps the last `window` positions in the window; returns the blocks
+    released."""
+    n = _I32()
+    _check(_lib.pa_seq_slide_window(pool.handle, seq, window, ctypes.byref(n)),
+           "pa_seq_slide_window")
+    return n.value
+
+
+def _swap(fn, name, pool, seq):
+    n = _I32()
+    st = fn(pool.handle, seq, None, 0, ctypes.byref(n))
+    if st != ERR_CAPACITY or n.value == 0:
+        _check(st, name)
+        return np.zeros((0, 2), dtype=np.int32)
+    pairs = np.empty((n.value, 2), dtype=np.int32)
+    _check(fn(pool.handle, seq, pairs.ctypes.data, n.value, ctypes.byref(n)), name)
+    return pairs
+
+
+def pa_seq_swap_out(pool, seq):
+    """Swaps seq out; returns int32 [n][2] pairs (device block, host block)."""
+    return _swap(_lib.pa_seq_swap_out, "pa_seq_swap_out", pool, seq)
+
+
+def pa_seq_swap_in(pool, seq):
+    """Swaps seq back in; returns int32 [n][2] pairs (host block, device block)."""
+    return _swap(_lib.pa_seq_swap_in, "pa_seq_swap_in", pool, seq)
 
 
 def pa_pool_get_stats(pool):
@@ -327,14 +368,40 @@ def pa_copy_blocks(k_cache, v_cache, pairs, desc, stream=None):
                                ctypes.byref(desc), _stream(stream)), "pa_copy_blocks")
 
 
+def pa_swap_blocks(k_cache, v_cache, host_k, host_v, pairs, desc, to_host, stream=None):
+    """host_k, host_v: pinned host tensors of whole blocks laid out like the
+    caches; pairs: device int32 tensor [n][2] as pa_seq_swap_out / _in gave."""
+    kb = DTYPE_BYTES[desc.kv_dtype]
+    block = desc.block_size * desc.num_kv_heads * desc.head_dim * kb
+    for t, nm in [(k_cache, "k_cache"), (v_cache, "v_cache")]:
+        _check_tensor(t, nm, desc.num_blocks * block)
+    hb = host_k.numel() * host_k.element_size()
+    if (host_k.is_cuda or host_v.is_cuda or not host_k.is_pinned() or not host_v.is_pinned()
+            or hb % block or host_v.numel() * host_v.element_size() != hb):
+        raise ValueError("host_k / host_v must be pinned host tensors of whole blocks")
+    n = pairs.shape[0] if pairs.dim() == 2 else 0
+    if n:
+        _check_tensor(pairs, "pairs", n * 8)
+    _check(_lib.pa_swap_blocks(_addr(k_cache), _addr(v_cache), _addr(host_k), _addr(host_v),
+                               hb // block, _addr(pairs) if n else None, n, int(bool(to_host)),
+                               ctypes.byref(desc), _stream(stream)), "pa_swap_blocks")
+
+
 def pa_decode_workspace_bytes(desc, num_seqs, max_seq_len, partition_size):
     return int(_lib.pa_decode_workspace_bytes(ctypes.byref(desc), num_seqs, max_seq_len,
                                               partition_size))
 
 
+def _starts(seq_starts, B):
+    if seq_starts is None:
+        return None
+    _check_tensor(seq_starts, "seq_starts", B * 4)
+    return _addr(seq_starts)
+
+
 def pa_decode(q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale, out, desc,
               k_scale=1.0, v_scale=1.0, workspace=None, partition_size=PARTITION_NONE,
-              stream=None):
+              stream=None, seq_starts=None):
     B = seq_lens.numel()
     qb, kb = DTYPE_BYTES[desc.q_dtype], DTYPE_BYTES[desc.kv_dtype]
     qrow = desc.num_q_heads * desc.head_dim
@@ -352,14 +419,15 @@ def pa_decode(q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale, o
         _check_tensor(workspace, "workspace")
         ws_bytes = workspace.numel() * workspace.element_size()
     _check(_lib.pa_decode(_addr(q), _addr(k_cache), _addr(v_cache), _addr(block_tables),
-                          block_tables.shape[1], _addr(seq_lens), B, max_seq_len, scale,
-                          k_scale, v_scale, _addr(out), _addr(workspace), ws_bytes,
-                          partition_size, ctypes.byref(desc), _stream(stream)), "pa_decode")
+                          block_tables.shape[1], _addr(seq_lens), _starts(seq_starts, B), B,
+                          max_seq_len, scale, k_scale, v_scale, _addr(out), _addr(workspace),
+                          ws_bytes, partition_size, ctypes.byref(desc), _stream(stream)),
+           "pa_decode")
 
 
 def pa_decode_append(q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables, seq_lens,
                      max_seq_len, scale, out, desc, k_scale=1.0, v_scale=1.0, workspace=None,
-                     partition_size=PARTITION_NONE, stream=None):
+                     partition_size=PARTITION_NONE, stream=None, seq_starts=None):
     B = seq_lens.numel()
     qb, kb = DTYPE_BYTES[desc.q_dtype], DTYPE_BYTES[desc.kv_dtype]
     qrow = desc.num_q_heads * desc.head_dim
@@ -382,18 +450,20 @@ def pa_decode_append(q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tabl
         ws_bytes = workspace.numel() * workspace.element_size()
     _check(_lib.pa_decode_append(_addr(q), _addr(k_new), _addr(v_new), _addr(slot_mapping),
                                  _addr(k_cache), _addr(v_cache), _addr(block_tables),
-                                 block_tables.shape[1], _addr(seq_lens), B, max_seq_len, scale,
-                                 k_scale, v_scale, _addr(out), _addr(workspace), ws_bytes,
-                                 partition_size, ctypes.byref(desc), _stream(stream)),
-           "pa_decode_append")
+                                 block_tables.shape[1], _addr(seq_lens), _starts(seq_starts, B),
+                                 B, max_seq_len, scale, k_scale, v_scale, _addr(out),
+                                 _addr(workspace), ws_bytes, partition_size, ctypes.byref(desc),
+                                 _stream(stream)), "pa_decode_append")
 
 
 def pa_decode_partials(q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale, desc,
-                       workspace, partition_size, k_scale=1.0, v_scale=1.0, stream=None):
+                       workspace, partition_size, k_scale=1.0, v_scale=1.0, stream=None,
+                       seq_starts=None):
     B = seq_lens.numel()
     _check_tensor(workspace, "workspace")
     _check(_lib.pa_decode_partials(_addr(q), _addr(k_cache), _addr(v_cache), _addr(block_tables),
-                                   block_tables.shape[1], _addr(seq_lens), B, max_seq_len, scale,
+                                   block_tables.shape[1], _addr(seq_lens),
+                                   _starts(seq_starts, B), B, max_seq_len, scale,
                                    k_scale, v_scale, _addr(workspace),
                                    workspace.numel() * workspace.element_size(), partition_size,
                                    ctypes.byref(desc), _stream(stream)), "pa_decode_partials")

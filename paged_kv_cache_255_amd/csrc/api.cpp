@@ -27,6 +27,9 @@ hipError_t launch_merge(const DecodeArgs &a, pa_dtype qt, int D, hipStream_t s);
 hipError_t launch_append(const void *k, const void *v, void *kc, void *vc, const int32_t *slots,
                          int32_t T, int32_t H, int32_t NB, int32_t TS, int D, pa_dtype qt,
                          pa_dtype kt, float k_inv, float v_inv, hipStream_t s);
+hipError_t launch_swap_blocks(const void *src_k, const void *src_v, void *dst_k, void *dst_v,
+                              const int32_t *pairs, int32_t num_pairs, int64_t block_bytes,
+                              int32_t n_src, int32_t n_dst, hipStream_t s);
 hipError_t launch_copy_blocks(void *k_cache, void *v_cache, const int32_t *pairs,
                               int32_t num_pairs, int64_t block_bytes, int32_t num_blocks,
                               hipStream_t s);
@@ -179,6 +182,40 @@ pa_status pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *pairs, int
     return PA_OK;
 }
 
+pa_status pa_swap_blocks(void *k_cache, void *v_cache, void *host_k, void *host_v,
+                         int32_t num_host_blocks, const int32_t *pairs, int32_t num_pairs,
+                         int32_t to_host, const pa_kv_desc *desc, void *stream)
+{
+    pa_status st = check_desc(desc);
+    if (st != PA_OK)
+        return st;
+    if (num_pairs < 0 || num_pairs > 65535 || num_host_blocks < 0)
+        return fail(PA_ERR_INVALID_ARG, "num_pairs must be in [0, 65535]");
+    if (num_pairs == 0)
+        return PA_OK;
+    if (!k_cache || !v_cache || !host_k || !host_v || !pairs)
+        return fail(PA_ERR_INVALID_ARG, "null pointer");
+    // the host buffers must be pinned memory the device can address
+    void *dk = nullptr, *dv = nullptr;
+    if (hipHostGetDevicePointer(&dk, host_k, 0) != hipSuccess ||
+        hipHostGetDevicePointer(&dv, host_v, 0) != hipSuccess || !dk || !dv) {
+        (void)hipGetLastError();
+        return fail(PA_ERR_INVALID_ARG, "host swap buffers must be pinned (hipHostMalloc) memory");
+    }
+    const int64_t block_bytes = (int64_t)desc->block_size * desc->num_kv_heads * desc->head_dim *
+                                dtype_bytes(desc->kv_dtype);
+    clear_stale_hip_error();
+    hipError_t e = to_host ? launch_swap_blocks(k_cache, v_cache, dk, dv, pairs, num_pairs,
+                                                block_bytes, desc->num_blocks, num_host_blocks,
+                                                static_cast<hipStream_t>(stream))
+                           : launch_swap_blocks(dk, dv, k_cache, v_cache, pairs, num_pairs,
+                                                block_bytes, num_host_blocks, desc->num_blocks,
+                                                static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "swap launch");
+    return PA_OK;
+}
+
 size_t pa_decode_workspace_bytes(const pa_kv_desc *desc, int32_t num_seqs, int32_t max_seq_len,
                                  int32_t partition_size)
 {
@@ -210,10 +247,10 @@ struct NewTokens {
 
 pa_status decode_impl(Phase phase, const void *q, const void *k_cache, const void *v_cache,
                       const int32_t *block_tables, int32_t max_blocks_per_seq,
-                      const int32_t *seq_lens, int32_t num_seqs, int32_t max_seq_len,
-                      float scale, float k_scale, float v_scale, void *out, void *workspace,
-                      size_t workspace_bytes, int32_t partition_size, const pa_kv_desc *desc,
-                      void *stream, const NewTokens &nt = NewTokens{})
+                      const int32_t *seq_lens, const int32_t *seq_starts, int32_t num_seqs,
+                      int32_t max_seq_len, float scale, float k_scale, float v_scale, void *out,
+                      void *workspace, size_t workspace_bytes, int32_t partition_size,
+                      const pa_kv_desc *desc, void *stream, const NewTokens &nt = NewTokens{})
 {
     pa_status st = check_desc(desc);
     if (st != PA_OK)
@@ -249,6 +286,7 @@ pa_status decode_impl(Phase phase, const void *q, const void *k_cache, const voi
     a.v_cache = v_cache;
     a.block_tables = block_tables;
     a.seq_lens = seq_lens;
+    a.seq_starts = seq_starts;
     a.out = out;
     a.ws = static_cast<float *>(workspace);
     a.num_seqs = num_seqs;
@@ -350,23 +388,23 @@ extern "C" {
 
 pa_status pa_decode(const void *q, const void *k_cache, const void *v_cache,
                     const int32_t *block_tables, int32_t max_blocks_per_seq,
-                    const int32_t *seq_lens, int32_t num_seqs, int32_t max_seq_len, float scale,
-                    float k_scale, float v_scale, void *out, void *workspace,
-                    size_t workspace_bytes, int32_t partition_size, const pa_kv_desc *desc,
-                    void *stream)
+                    const int32_t *seq_lens, const int32_t *seq_starts, int32_t num_seqs,
+                    int32_t max_seq_len, float scale, float k_scale, float v_scale, void *out,
+                    void *workspace, size_t workspace_bytes, int32_t partition_size,
+                    const pa_kv_desc *desc, void *stream)
 {
     return decode_impl(kAll, q, k_cache, v_cache, block_tables, max_blocks_per_seq, seq_lens,
-                       num_seqs, max_seq_len, scale, k_scale, v_scale, out, workspace,
-                       workspace_bytes, partition_size, desc, stream);
+                       seq_starts, num_seqs, max_seq_len, scale, k_scale, v_scale, out,
+                       workspace, workspace_bytes, partition_size, desc, stream);
 }
 
 pa_status pa_decode_append(const void *q, const void *k_new, const void *v_new,
                            const int32_t *slot_mapping, void *k_cache, void *v_cache,
                            const int32_t *block_tables, int32_t max_blocks_per_seq,
-                           const int32_t *seq_lens, int32_t num_seqs, int32_t max_seq_len,
-                           float scale, float k_scale, float v_scale, void *out, void *workspace,
-                           size_t workspace_bytes, int32_t partition_size,
-                           const pa_kv_desc *desc, void *stream)
+                           const int32_t *seq_lens, const int32_t *seq_starts, int32_t num_seqs,
+                           int32_t max_seq_len, float scale, float k_scale, float v_scale,
+                           void *out, void *workspace, size_t workspace_bytes,
+                           int32_t partition_size, const pa_kv_desc *desc, void *stream)
 {
     if (num_seqs > 0 && !slot_mapping)
         return fail(PA_ERR_INVALID_ARG, "null pointer");
@@ -375,20 +413,20 @@ pa_status pa_decode_append(const void *q, const void *k_new, const void *v_new,
     nt.v = v_new;
     nt.slots = slot_mapping;
     return decode_impl(kAll, q, k_cache, v_cache, block_tables, max_blocks_per_seq, seq_lens,
-                       num_seqs, max_seq_len, scale, k_scale, v_scale, out, workspace,
-                       workspace_bytes, partition_size, desc, stream, nt);
+                       seq_starts, num_seqs, max_seq_len, scale, k_scale, v_scale, out,
+                       workspace, workspace_bytes, partition_size, desc, stream, nt);
 }
 
 pa_status pa_decode_partials(const void *q, const void *k_cache, const void *v_cache,
                              const int32_t *block_tables, int32_t max_blocks_per_seq,
-                             const int32_t *seq_lens, int32_t num_seqs, int32_t max_seq_len,
-                             float scale, float k_scale, float v_scale, void *workspace,
-                             size_t workspace_bytes, int32_t partition_size,
-                             const pa_kv_desc *desc, void *stream)
+                             const int32_t *seq_lens, const int32_t *seq_starts,
+                             int32_t num_seqs, int32_t max_seq_len, float scale, float k_scale,
+                             float v_scale, void *workspace, size_t workspace_bytes,
+                             int32_t partition_size, const pa_kv_desc *desc, void *stream)
 {
     return decode_impl(kPartials, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
-                       seq_lens, num_seqs, max_seq_len, scale, k_scale, v_scale, nullptr,
-                       workspace, workspace_bytes, partition_size, desc, stream);
+                       seq_lens, seq_starts, num_seqs, max_seq_len, scale, k_scale, v_scale,
+                       nullptr, workspace, workspace_bytes, partition_size, desc, stream);
 }
 
 pa_status pa_decode_merge(const int32_t *seq_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
@@ -397,8 +435,9 @@ pa_status pa_decode_merge(const int32_t *seq_lens, int32_t num_seqs, int32_t max
                           void *stream)
 {
     return decode_impl(kMerge, nullptr, nullptr, nullptr, nullptr, max_blocks_per_seq, seq_lens,
-                       num_seqs, max_seq_len, 1.f, 1.f, 1.f, out, const_cast<void *>(workspace),
-                       workspace_bytes, partition_size, desc, stream);
+                       nullptr, num_seqs, max_seq_len, 1.f, 1.f, 1.f, out,
+                       const_cast<void *>(workspace), workspace_bytes, partition_size, desc,
+                       stream);
 }
 
 } // extern "C"

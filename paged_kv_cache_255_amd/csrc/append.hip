@@ -69,6 +69,47 @@ hipError_t launch_copy_blocks(void *k_cache, void *v_cache, const int32_t *pairs
     return hipGetLastError();
 }
 
+// Swap transfers: for each pair (src, dst), block dst of the destination
+// caches (K and V, block_bytes each) becomes block src of the source caches.
+// One side is device memory, the other the device mapping of pinned host
+// memory, so the transfer is a plain load/store stream over the host link;
+// blockIdx.y picks the pair.  Ids outside [0, n_src) or [0, n_dst) skip the
+// pair.
+__global__ __launch_bounds__(256) void swap_blocks_kernel(const char *src_k, const char *src_v,
+                                                          char *dst_k, char *dst_v,
+                                                          const int32_t *pairs,
+                                                          int64_t block_bytes, int32_t n_src,
+                                                          int32_t n_dst)
+{
+    const int32_t src = pairs[2 * blockIdx.y];
+    const int32_t dst = pairs[2 * blockIdx.y + 1];
+    if (src < 0 || src >= n_src || dst < 0 || dst >= n_dst)
+        return;
+    const int64_t step = (int64_t)gridDim.x * blockDim.x * 16;
+    for (int64_t off = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 16; off < block_bytes;
+         off += step) {
+        const u32x4 k = load16(src_k + src * block_bytes + off);
+        const u32x4 v = load16(src_v + src * block_bytes + off);
+        *reinterpret_cast<u32x4 *>(dst_k + dst * block_bytes + off) = k;
+        *reinterpret_cast<u32x4 *>(dst_v + dst * block_bytes + off) = v;
+    }
+}
+
+hipError_t launch_swap_blocks(const void *src_k, const void *src_v, void *dst_k, void *dst_v,
+                              const int32_t *pairs, int32_t num_pairs, int64_t block_bytes,
+                              int32_t n_src, int32_t n_dst, hipStream_t s)
+{
+    if (num_pairs == 0)
+        return hipSuccess;
+    const int64_t threads = (block_bytes + 15) / 16;
+    const int gx = (int)std::min<int64_t>((threads + 255) / 256, 64);
+    hipLaunchKernelGGL(swap_blocks_kernel, dim3(gx, num_pairs), dim3(256), 0, s,
+                       static_cast<const char *>(src_k), static_cast<const char *>(src_v),
+                       static_cast<char *>(dst_k), static_cast<char *>(dst_v), pairs,
+                       block_bytes, n_src, n_dst);
+    return hipGetLastError();
+}
+
 template <int QT, int KT>
 hipError_t append_by_dim(const void *k, const void *v, void *kc, void *vc, const int32_t *slots,
                          int32_t T, int32_t H, int32_t NB, int32_t TS, int D, float ki,

@@ -160,7 +160,7 @@ struct MfmaWave {
 #pragma unroll
         for (int t = 0; t < PV_TILES; ++t)
             acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        m_run = -INFINITY;
+        m_run = kMaxStart;
         l_run = 0.f;
     }
 
@@ -254,8 +254,9 @@ struct MfmaWave {
         }
     }
 
-    // One tile: `valid` tokens of it (1..16) belong to the range.
-    __device__ void compute(const Tile &T, int valid, float sc)
+    // One tile: its tokens lo .. valid - 1 (0 <= lo, valid <= 16) belong to
+    // the range; lo > 0 only in a tile that holds the window start.
+    __device__ void compute(const Tile &T, int lo, int valid, float sc)
     {
         f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -276,7 +277,7 @@ struct MfmaWave {
         float x[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            x[r] = (4 * grp + r < valid) ? s[r] * sc : -INFINITY;
+            x[r] = (4 * grp + r < valid && 4 * grp + r >= lo) ? s[r] * sc : -INFINITY;
         float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
         bm = max_xor32(max_xor16(bm));
         // The reference max m_run moves only when a tile's max exceeds it by
@@ -299,11 +300,15 @@ struct MfmaWave {
         l_run += (p[0] + p[1]) + (p[2] + p[3]);
         const u32x2 pp = {M::pack2(p[0], p[1]), M::pack2(p[2], p[3])};
         const A4 pop = __builtin_bit_cast(A4, pp);
-        // Slots past the end may hold anything (NaN included): their V
-        // values are zeroed, without a branch, so 0 * garbage never reaches acc.
-        const int k = valid - 4 * grp; // tokens of this lane's 4 that are valid
-        const uint32_t keep_x = k >= 2 ? 0xFFFFFFFFu : (k == 1 ? 0x0000FFFFu : 0u);
-        const uint32_t keep_y = k >= 4 ? 0xFFFFFFFFu : (k == 3 ? 0x0000FFFFu : 0u);
+        // Slots past the end or before the window start may hold anything
+        // (NaN included): their V values are zeroed, without a branch, so
+        // 0 * garbage never reaches acc.  This lane's tokens r = 0..3 are in
+        // the range when khi > r >= klo.
+        const int khi = valid - 4 * grp, klo = lo - 4 * grp;
+        const uint32_t keep_x = (klo <= 0 && khi > 0 ? 0x0000FFFFu : 0u) |
+                                (klo <= 1 && khi > 1 ? 0xFFFF0000u : 0u);
+        const uint32_t keep_y = (klo <= 2 && khi > 2 ? 0x0000FFFFu : 0u) |
+                                (klo <= 3 && khi > 3 ? 0xFFFF0000u : 0u);
 #pragma unroll
         for (int t = 0; t < PV_TILES; ++t) {
             u32x2 vw;
@@ -317,12 +322,14 @@ struct MfmaWave {
         }
     }
 
-    // Tokens [t0, t1) of (b, g); t0 is a multiple of 16.  Returns false if a
-    // block-table entry is outside the pool (that block is not read), or if
-    // the step's token is to be appended here (t1 is the sequence's length)
-    // and its slot is not the cache slot of position t1 - 1.
+    // Tokens [t0, t1) of (b, g), of a sequence of n tokens; t0 is a multiple
+    // of 16.  Tokens before the window start (seq_starts[b]) are left out.
+    // Returns false if a block-table entry is outside the pool (that block is
+    // not read), if the window start is outside [0, n], or if the step's
+    // token is to be appended here (a.append and t1 == n) and its slot is not
+    // the cache slot of position n - 1.
     __device__ bool run(const DecodeArgs &a, int32_t b, int32_t g, int32_t t0, int32_t t1,
-                        bool append_here)
+                        int32_t n_seq)
     {
         // The block table does not change while the kernel runs: its entries
         // are read with scalar loads (one wave-uniform id per tile, fetched
@@ -352,6 +359,9 @@ struct MfmaWave {
             return (size_t)(min(jb, last) & mask) * TILE_BYTES;
         };
         auto valid_of = [&](int32_t jb) { return min(kTile, t1 - jb * kTile); };
+        const int32_t w0 = a.seq_starts ? uniform(((const CI32 *)a.seq_starts)[b]) : 0;
+        auto lo_of = [&](int32_t jb) { return min(kTile, max(0, w0 - jb * kTile)); };
+        const bool append_here = a.append && t1 == uniform(n_seq);
         auto load = [&](int32_t phys, size_t sub, Tile &T) {
             const size_t o = (size_t)phys * bstride + sub;
             load_tile(kbase + o, vbase + o, col, grp, T);
@@ -368,7 +378,7 @@ struct MfmaWave {
         // the result into NaN), so no early exit is needed either.
         Tile A, B;
         const int32_t n = last - jb0 + 1; // tiles in the range, >= 1
-        bool bad = false;
+        bool bad = w0 < 0 || w0 > n_seq;
         auto checked = [&](int32_t id) {
             const bool out = (uint32_t)id >= nblocks;
             bad |= out;
@@ -400,18 +410,18 @@ struct MfmaWave {
             const int32_t idA = id_of(jb + 2);
             load(checked(idB), sub_of(jb + 1), B);
             __builtin_amdgcn_sched_barrier(0); // B's loads go out before A is waited for
-            compute(A, valid_of(jb), sc);
+            compute(A, lo_of(jb), valid_of(jb), sc);
             idB = id_of(jb + 3);
             load(checked(idA), sub_of(jb + 2), A);
             __builtin_amdgcn_sched_barrier(0);
             if (put && jb + 1 == last)
                 apply_new_token(B, nt);
-            compute(B, valid_of(jb + 1), sc);
+            compute(B, lo_of(jb + 1), valid_of(jb + 1), sc);
         }
         if (n & 1) {
             if (put)
                 apply_new_token(A, nt);
-            compute(A, valid_of(last), sc); // A holds the last tile
+            compute(A, lo_of(last), valid_of(last), sc); // A holds the last tile
         }
         // Drain the re-read issued past the end (n even), so no load into
         // these registers is in flight when the next range starts.
@@ -436,7 +446,8 @@ struct MfmaWave {
             return;
         TQ *o = static_cast<TQ *>(a.out) +
                 ((size_t)b * a.num_q_heads + (size_t)g * a.group + col) * D;
-        const float inv = !ok ? NAN : (n > 0 ? a.v_scale / l_run : 0.f);
+        // l = 0: no token in the range (n = 0 or an empty window)
+        const float inv = !ok ? NAN : (l_run == 0.f ? 0.f : a.v_scale / l_run);
 #pragma unroll
         for (int t = 0; t < PV_TILES; ++t)
 #pragma unroll
@@ -480,7 +491,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a, int32_t 
     wv.start(a, it.b, it.g);
     bool ok = it.valid_len;
     if (ok && it.t1 > it.t0)
-        ok = wv.run(a, it.b, it.g, it.t0, it.t1, a.append && it.t1 == it.n);
+        ok = wv.run(a, it.b, it.g, it.t0, it.t1, it.n);
     wv.finish();
     if (a.partition == 0)
         wv.write_out(a, it.b, it.g, it.n, ok);
@@ -519,8 +530,7 @@ void decode_mfma_balanced_kernel(DecodeArgs a, int32_t W)
         const int64_t stop = min(x1, seg_end);
         const int32_t je = j + (int32_t)(stop - x);
         wv.start(a, pos.b, g);
-        const bool ok = wv.run(a, pos.b, g, j * kTile, min(je * kTile, pos.n),
-                               a.append && je == nb);
+        const bool ok = wv.run(a, pos.b, g, j * kTile, min(je * kTile, pos.n), pos.n);
         wv.finish();
         if (j == 0 && je == nb) {
             wv.write_out(a, pos.b, g, pos.n, ok);

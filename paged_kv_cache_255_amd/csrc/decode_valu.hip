@@ -82,14 +82,17 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a, int32_t 
     float m[G], l[G], acc[G][S::V_INSTR];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-        m[h] = -INFINITY;
+        m[h] = kMaxStart;
         l[h] = 0.f;
 #pragma unroll
         for (int i = 0; i < S::V_INSTR; ++i)
             acc[h][i] = 0.f;
     }
 
-    bool bad = !it.valid_len;
+    // window start: tokens before it are left out (n = 0 rows are not read)
+    const bool windowed = a.seq_starts && it.valid_len && it.n > 0;
+    const int32_t w0 = windowed ? __builtin_amdgcn_readfirstlane(a.seq_starts[it.b]) : 0;
+    bool bad = !it.valid_len || w0 < 0 || w0 > it.n;
     const int32_t *table = a.block_tables + (size_t)it.b * a.max_blocks_per_seq;
     const char *kbase = static_cast<const char *>(a.k_cache);
     const char *vbase = static_cast<const char *>(a.v_cache);
@@ -107,7 +110,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a, int32_t 
             ((((size_t)phys * a.num_kv_heads + it.g) << sh) + (jb & ((1 << sh) - 1))) *
             S::TILE_BYTES;
         const int32_t tok_base = jb * kTile;
-        const bool tail = tok_base + kTile > it.t1;
+        const bool tail = tok_base + kTile > it.t1 || tok_base < w0;
 
         // K tile: this lane's chunks of token tq.
         float kv[S::CH_PER_LANE][S::EPC];
@@ -125,7 +128,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a, int32_t 
         }
 
         // scores of token tq for the G heads (log2 units)
-        const bool tok_ok = tok_base + tq < it.t1;
+        const bool tok_ok = tok_base + tq < it.t1 && tok_base + tq >= w0;
         float s[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) {
@@ -167,8 +170,8 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a, int32_t 
             for (int i = 0; i < S::V_INSTR; ++i)
 #pragma unroll
                 for (int e = 0; e < S::V_TPL; ++e)
-                    if (tok_base + vtok0 + e >= it.t1)
-                        vv[i][e] = 0.f; // slots past the end may hold anything
+                    if (tok_base + vtok0 + e >= it.t1 || tok_base + vtok0 + e < w0)
+                        vv[i][e] = 0.f; // slots outside the range may hold anything
         }
 #pragma unroll
         for (int h = 0; h < G; ++h) {
@@ -208,7 +211,8 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a, int32_t 
         TQ *o = static_cast<TQ *>(a.out) + ((size_t)it.b * a.num_q_heads + (size_t)it.g * G) * D;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            const float inv = (it.n > 0) ? a.v_scale / l[h] : 0.f;
+            // l = 0: no token in the range (n = 0 or an empty window)
+            const float inv = (l[h] == 0.f) ? 0.f : a.v_scale / l[h];
 #pragma unroll
             for (int i = 0; i < S::V_INSTR; ++i) {
                 float r = bad ? NAN : acc[h][i] * inv;

@@ -47,7 +47,7 @@ __device__ __forceinline__ void merge_row(const DecodeArgs &a, int32_t b, int32_
         for (int i = 0; i < PER_LANE; ++i)
             acc[i] = fmaf(ap[i * kWave + lane], wgt, acc[i]);
     }
-    const float inv = nan_seen ? NAN : 1.f / L;
+    const float inv = nan_seen ? NAN : (L == 0.f ? 0.f : 1.f / L); // L = 0: empty window
 #pragma unroll
     for (int i = 0; i < PER_LANE; ++i)
         o[i * kWave + lane] = from_f32<QT>(acc[i] * inv);
@@ -106,7 +106,8 @@ __device__ __forceinline__ void merge_segment_s(const DecodeArgs &a, int32_t b, 
                 nan_seen |= mp[c][s] != mp[c][s];
                 mb = fmaxf(mb, mp[c][s]);
             }
-            // every part holds a finite max (at least one token), so mb is finite
+            // every part holds a finite max (a real score, or the finite start
+            // value when all its tokens lie before the window), so mb is finite
             const float alpha = __builtin_amdgcn_exp2f(M[s] - mb); // 0 on the first batch
             L[s] *= alpha;
             acc[s] *= alpha;
@@ -122,7 +123,7 @@ __device__ __forceinline__ void merge_segment_s(const DecodeArgs &a, int32_t b, 
     TQ *o = static_cast<TQ *>(a.out) + ((size_t)b * a.num_q_heads + (size_t)g * a.group) * D;
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-        const float inv = nan_seen ? NAN : 1.f / L[s];
+        const float inv = nan_seen ? NAN : (L[s] == 0.f ? 0.f : 1.f / L[s]); // 0: empty window
         TQ *r = o + 256 * s + 4 * lane; // row hs[s], dims (256 s + 4 lane) % D ..
 #pragma unroll
         for (int j = 0; j < 4; ++j)

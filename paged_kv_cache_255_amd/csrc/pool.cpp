@@ -49,7 +49,11 @@ struct pa_pool {
     std::vector<int32_t> refcount;  // per physical block
     struct Seq {
         bool live = false;
-        int32_t len = 0;
+        bool swapped = false; // blocks holds host block ids
+        int32_t len = 0;      // positions appended so far
+        int32_t start = 0;    // first position of the window
+        int32_t dropped = 0;  // leading blocks the window released; blocks[0] is
+                              // logical block `dropped`
         std::vector<int32_t> blocks;
     };
     std::vector<Seq> seqs; // index = sequence id
@@ -70,6 +74,8 @@ struct pa_pool {
     std::unordered_map<BlockKey, int32_t, BlockKeyHash> prefix;
     std::unordered_map<int32_t, Cached> cached;
     uint64_t tick = 0;
+    // Host swap space: free host block ids, taken from and returned to the back.
+    std::vector<int32_t> host_free;
 };
 
 namespace {
@@ -101,6 +107,18 @@ const pa_pool::Seq *live_seq(const pa_pool *p, int32_t id)
     return live_seq(const_cast<pa_pool *>(p), id);
 }
 
+// A live sequence whose blocks are on the device (not swapped out).
+pa_pool::Seq *resident_seq(pa_pool *p, int32_t id)
+{
+    pa_pool::Seq *s = live_seq(p, id);
+    return (s && !s->swapped) ? s : nullptr;
+}
+
+const pa_pool::Seq *resident_seq(const pa_pool *p, int32_t id)
+{
+    return resident_seq(const_cast<pa_pool *>(p), id);
+}
+
 // Whether an append of ntok tokens to `s` writes into a partly filled last
 // block that another table also maps ([devto] §5 "Zero-Copy Forking": a
 // branch's first new token goes to a private block; copy on write).
@@ -117,7 +135,8 @@ pa_status check_append(const pa_pool *p, const pa_pool::Seq &s, int32_t ntok, in
     int64_t total = (int64_t)s.len + ntok;
     if (total > INT32_MAX)
         return pa::fail(PA_ERR_INVALID_ARG, "sequence length overflows int32");
-    *need = blocks_for(total, bs) - (int32_t)s.blocks.size() + (needs_copy(p, s, ntok) ? 1 : 0);
+    *need = blocks_for(total, bs) - s.dropped - (int32_t)s.blocks.size() +
+            (needs_copy(p, s, ntok) ? 1 : 0);
     return PA_OK;
 }
 
@@ -155,7 +174,8 @@ void do_append(pa_pool *p, pa_pool::Seq &s, int32_t ntok, int32_t *slots)
         p->copies.emplace_back(shared, mine);
         release_block(p, shared); // refcount > 1: never reaches zero here
     }
-    const int32_t need = blocks_for((int64_t)s.len + ntok, bs) - (int32_t)s.blocks.size();
+    const int32_t need =
+        blocks_for((int64_t)s.len + ntok, bs) - s.dropped - (int32_t)s.blocks.size();
     for (int32_t i = 0; i < need; ++i) {
         int32_t b = p->free_list.back();
         p->free_list.pop_back();
@@ -165,7 +185,7 @@ void do_append(pa_pool *p, pa_pool::Seq &s, int32_t ntok, int32_t *slots)
     for (int32_t i = 0; i < ntok; ++i) {
         int32_t pos = s.len + i;
         if (slots)
-            slots[i] = s.blocks[pos / bs] * bs + pos % bs;
+            slots[i] = s.blocks[pos / bs - s.dropped] * bs + pos % bs;
     }
     s.len += ntok;
 }
@@ -180,7 +200,7 @@ pa_status pa_block_pool_init(const pa_pool_config *cfg, pa_pool **out)
         return pa::fail(PA_ERR_INVALID_ARG, "null argument");
     *out = nullptr;
     if (cfg->num_blocks <= 0 || cfg->block_size <= 0 || cfg->num_layers <= 0 ||
-        cfg->num_kv_heads <= 0 || cfg->head_dim <= 0)
+        cfg->num_kv_heads <= 0 || cfg->head_dim <= 0 || cfg->num_host_blocks < 0)
         return pa::fail(PA_ERR_INVALID_ARG, "pool sizes must be positive");
     if (pa::dtype_bytes(cfg->kv_dtype) == 0)
         return pa::fail(PA_ERR_INVALID_ARG, "unknown kv dtype");
@@ -204,6 +224,9 @@ pa_status pa_block_pool_init(const pa_pool_config *cfg, pa_pool **out)
         }
     }
     p->refcount.assign(cfg->num_blocks, 0);
+    p->host_free.resize(cfg->num_host_blocks);
+    for (int32_t i = 0; i < cfg->num_host_blocks; ++i)
+        p->host_free[i] = i;
     *out = p;
     return PA_OK;
 }
@@ -240,9 +263,9 @@ pa_status pa_seq_create(pa_pool *p, int32_t *seq_out)
 
 pa_status pa_seq_append_slots(pa_pool *p, int32_t seq, int32_t ntok, int32_t *slots_out)
 {
-    pa_pool::Seq *s = live_seq(p, seq);
+    pa_pool::Seq *s = resident_seq(p, seq);
     if (!s)
-        return pa::fail(PA_ERR_INVALID_ARG, "unknown or freed sequence id");
+        return pa::fail(PA_ERR_INVALID_ARG, "unknown, freed or swapped-out sequence id");
     if (ntok < 0 || (ntok > 0 && !slots_out))
         return pa::fail(PA_ERR_INVALID_ARG, "bad token count or null slots_out");
     int32_t need = 0;
@@ -266,9 +289,10 @@ pa_status pa_seq_append_slots_batch(pa_pool *p, const int32_t *seqs, int32_t nse
         return pa::fail(PA_ERR_INVALID_ARG, "sequence repeated in batch");
     int64_t total = 0;
     for (int32_t i = 0; i < nseq; ++i) {
-        pa_pool::Seq *s = live_seq(p, seqs[i]);
+        pa_pool::Seq *s = resident_seq(p, seqs[i]);
         if (!s)
-            return pa::fail(PA_ERR_INVALID_ARG, "unknown or freed sequence id in batch");
+            return pa::fail(PA_ERR_INVALID_ARG,
+                            "unknown, freed or swapped-out sequence id in batch");
         int32_t need = 0;
         pa_status st = check_append(p, *s, ntok, &need);
         if (st != PA_OK)
@@ -284,8 +308,8 @@ pa_status pa_seq_append_slots_batch(pa_pool *p, const int32_t *seqs, int32_t nse
 
 pa_status pa_seq_fork(pa_pool *p, int32_t parent, int32_t *child_out)
 {
-    if (!child_out || !live_seq(p, parent))
-        return pa::fail(PA_ERR_INVALID_ARG, "unknown parent or null child_out");
+    if (!child_out || !resident_seq(p, parent))
+        return pa::fail(PA_ERR_INVALID_ARG, "unknown or swapped-out parent, or null child_out");
     int32_t child;
     pa_status st = pa_seq_create(p, &child);
     if (st != PA_OK)
@@ -294,6 +318,8 @@ pa_status pa_seq_fork(pa_pool *p, int32_t parent, int32_t *child_out)
     pa_pool::Seq &c = p->seqs[child];
     c.blocks = par.blocks;
     c.len = par.len;
+    c.start = par.start;
+    c.dropped = par.dropped;
     for (int32_t b : c.blocks)
         ++p->refcount[b];
     *child_out = child;
@@ -305,12 +331,96 @@ pa_status pa_seq_free(pa_pool *p, int32_t seq)
     pa_pool::Seq *s = live_seq(p, seq);
     if (!s)
         return pa::fail(PA_ERR_INVALID_ARG, "unknown or already freed sequence id");
-    for (int32_t b : s->blocks)
-        release_block(p, b);
+    if (s->swapped) {
+        for (int32_t h : s->blocks)
+            p->host_free.push_back(h);
+    } else {
+        for (int32_t b : s->blocks)
+            release_block(p, b);
+    }
     s->blocks.clear();
     s->blocks.shrink_to_fit();
-    s->len = 0;
+    s->len = s->start = s->dropped = 0;
+    s->swapped = false;
     s->live = false;
+    return PA_OK;
+}
+
+pa_status pa_seq_slide_window(pa_pool *p, int32_t seq, int32_t window, int32_t *released_out)
+{
+    pa_pool::Seq *s = resident_seq(p, seq);
+    if (!s || window < 0)
+        return pa::fail(PA_ERR_INVALID_ARG, "unknown or swapped-out sequence, or window < 0");
+    const int32_t bs = p->cfg.block_size;
+    s->start = std::max(s->start, s->len - window);
+    int32_t released = 0;
+    size_t k = 0; // leading blocks wholly before the start
+    while (k < s->blocks.size() && (int64_t)s->start - (int64_t)(s->dropped + k) * bs >= bs)
+        ++k;
+    for (size_t i = 0; i < k; ++i) {
+        release_block(p, s->blocks[i]);
+        ++released;
+    }
+    s->blocks.erase(s->blocks.begin(), s->blocks.begin() + k);
+    s->dropped += (int32_t)k;
+    if (released_out)
+        *released_out = released;
+    return PA_OK;
+}
+
+pa_status pa_seq_swap_out(pa_pool *p, int32_t seq, int32_t *pairs_out, int32_t max_pairs,
+                          int32_t *count_out)
+{
+    pa_pool::Seq *s = resident_seq(p, seq);
+    if (!s || !count_out || max_pairs < 0)
+        return pa::fail(PA_ERR_INVALID_ARG, "unknown or swapped-out sequence, or bad arguments");
+    if (!p->copies.empty())
+        return pa::fail(PA_ERR_INVALID_ARG,
+                        "copy-on-write copies are pending: take and make them first");
+    const size_t n = s->blocks.size();
+    *count_out = (int32_t)n;
+    if (n > p->host_free.size())
+        return pa::fail(PA_ERR_OUT_OF_BLOCKS, "host swap space exhausted");
+    if (n > 0 && (!pairs_out || (size_t)max_pairs < n))
+        return pa::fail(PA_ERR_CAPACITY, "more blocks than max_pairs");
+    std::vector<int32_t> host(n);
+    for (size_t i = 0; i < n; ++i) {
+        host[i] = p->host_free.back();
+        p->host_free.pop_back();
+        pairs_out[2 * i] = s->blocks[i];
+        pairs_out[2 * i + 1] = host[i];
+    }
+    for (int32_t b : s->blocks)
+        release_block(p, b);
+    s->blocks = std::move(host);
+    s->swapped = true;
+    return PA_OK;
+}
+
+pa_status pa_seq_swap_in(pa_pool *p, int32_t seq, int32_t *pairs_out, int32_t max_pairs,
+                         int32_t *count_out)
+{
+    pa_pool::Seq *s = live_seq(p, seq);
+    if (!s || !s->swapped || !count_out || max_pairs < 0)
+        return pa::fail(PA_ERR_INVALID_ARG, "sequence not swapped out, or bad arguments");
+    const size_t n = s->blocks.size();
+    *count_out = (int32_t)n;
+    if (n > p->free_list.size())
+        return pa::fail(PA_ERR_OUT_OF_BLOCKS, "block pool exhausted");
+    if (n > 0 && (!pairs_out || (size_t)max_pairs < n))
+        return pa::fail(PA_ERR_CAPACITY, "more blocks than max_pairs");
+    std::vector<int32_t> dev(n);
+    for (size_t i = 0; i < n; ++i) {
+        dev[i] = p->free_list.back();
+        p->free_list.pop_back();
+        p->refcount[dev[i]] = 1;
+        pairs_out[2 * i] = s->blocks[i];
+        pairs_out[2 * i + 1] = dev[i];
+    }
+    for (int32_t h : s->blocks)
+        p->host_free.push_back(h);
+    s->blocks = std::move(dev);
+    s->swapped = false;
     return PA_OK;
 }
 
@@ -332,14 +442,15 @@ pa_status pa_block_refcount(const pa_pool *p, int32_t block, int32_t *refcount_o
 }
 
 pa_status pa_export_block_tables(const pa_pool *p, const int32_t *seqs, int32_t nseq,
-                                 int32_t max_blocks, int32_t *tables_out, int32_t *lens_out)
+                                 int32_t max_blocks, int32_t *tables_out, int32_t *lens_out,
+                                 int32_t *starts_out)
 {
     if (!p || nseq < 0 || max_blocks < 0 || (nseq > 0 && !seqs))
         return pa::fail(PA_ERR_INVALID_ARG, "bad export arguments");
     for (int32_t i = 0; i < nseq; ++i) {
-        const pa_pool::Seq *s = live_seq(p, seqs[i]);
+        const pa_pool::Seq *s = resident_seq(p, seqs[i]);
         if (!s)
-            return pa::fail(PA_ERR_INVALID_ARG, "unknown sequence id in export");
+            return pa::fail(PA_ERR_INVALID_ARG, "unknown or swapped-out sequence id in export");
         if (tables_out && s->blocks.size() > (size_t)max_blocks)
             return pa::fail(PA_ERR_CAPACITY, "block table longer than max_blocks");
     }
@@ -352,8 +463,11 @@ pa_status pa_export_block_tables(const pa_pool *p, const int32_t *seqs, int32_t 
                 std::memcpy(row, s.blocks.data(), n * sizeof(int32_t));
             std::fill(row + n, row + max_blocks, -1);
         }
+        const int32_t base = s.dropped * p->cfg.block_size; // first kept position
         if (lens_out)
-            lens_out[i] = s.len;
+            lens_out[i] = s.len - base;
+        if (starts_out)
+            starts_out[i] = s.start - base;
     }
     return PA_OK;
 }
@@ -383,11 +497,13 @@ pa_status pa_pool_take_copies(pa_pool *p, int32_t *pairs_out, int32_t max_pairs,
 pa_status pa_prefix_register(pa_pool *p, int32_t seq, const int32_t *tokens, int32_t ntok,
                              int32_t *added_out)
 {
-    pa_pool::Seq *s = live_seq(p, seq);
+    pa_pool::Seq *s = resident_seq(p, seq);
     if (!s)
-        return pa::fail(PA_ERR_INVALID_ARG, "unknown or freed sequence id");
+        return pa::fail(PA_ERR_INVALID_ARG, "unknown, freed or swapped-out sequence id");
     if (ntok < 0 || ntok > s->len || (ntok > 0 && !tokens))
         return pa::fail(PA_ERR_INVALID_ARG, "ntok must be in [0, sequence length]");
+    if (s->start != 0 || s->dropped != 0)
+        return pa::fail(PA_ERR_INVALID_ARG, "the sequence's window has moved: no prefix left");
     const int32_t bs = p->cfg.block_size;
     int32_t added = 0, prev = -1;
     for (int32_t i = 0; i < ntok / bs; ++i) {
@@ -419,7 +535,7 @@ pa_status pa_prefix_register(pa_pool *p, int32_t seq, const int32_t *tokens, int
 pa_status pa_prefix_match(pa_pool *p, int32_t seq, const int32_t *tokens, int32_t ntok,
                           int32_t *matched_out)
 {
-    pa_pool::Seq *s = live_seq(p, seq);
+    pa_pool::Seq *s = resident_seq(p, seq);
     if (!s || !matched_out)
         return pa::fail(PA_ERR_INVALID_ARG, "unknown sequence or null matched_out");
     if (s->len != 0)
@@ -491,13 +607,19 @@ pa_status pa_pool_get_stats(const pa_pool *p, pa_pool_stats *out)
     for (int32_t r : p->refcount)
         st.shared_blocks += (r > 1);
     st.cached_blocks = (int32_t)p->cached.size();
+    st.free_host_blocks = (int32_t)p->host_free.size();
     for (const auto &s : p->seqs) {
         if (!s.live)
             continue;
         ++st.live_seqs;
-        st.logical_tokens += s.len;
+        st.logical_tokens += s.len - s.start;
+        if (s.swapped) {
+            ++st.swapped_seqs;
+            continue;
+        }
         st.mapped_blocks += (int64_t)s.blocks.size();
-        st.tail_slack_tokens += (int64_t)s.blocks.size() * p->cfg.block_size - s.len;
+        st.tail_slack_tokens +=
+            ((int64_t)s.dropped + (int64_t)s.blocks.size()) * p->cfg.block_size - s.len;
     }
     *out = st;
     return PA_OK;

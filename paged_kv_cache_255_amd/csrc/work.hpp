@@ -13,6 +13,7 @@ struct DecodeArgs {
     const void *v_cache;
     const int32_t *block_tables;
     const int32_t *seq_lens;
+    const int32_t *seq_starts; // window starts, or null (every window starts at 0)
     void *out;
     float *ws;                 // partial states (partitioned modes)
     int32_t num_seqs;
@@ -40,6 +41,12 @@ struct DecodeArgs {
 };
 
 constexpr int32_t kPartitionBalanced = -1; // PA_PARTITION_BALANCED
+
+// Starting value of a running max: below every score but finite, so that a
+// tile whose tokens all lie before the window start (scores -inf) gives
+// weights 2^(-inf - m) = 0 rather than NaN.  A real score replaces it at the
+// first rescale, with the same bits as a start from -inf.
+constexpr float kMaxStart = -3.0e38f;
 
 __device__ __forceinline__ bool len_ok(const DecodeArgs &a, int32_t n)
 {

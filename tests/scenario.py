@@ -98,7 +98,7 @@ class GpuStep:
         pa.pa_cache_append(i.k_new, i.v_new, self.k_cache, self.v_cache, slots, self.desc,
                            i.k_scale, i.v_scale)
 
-    def decode_append(self, out=None, slots=None):
+    def decode_append(self, out=None, slots=None, seq_starts=None):
         """pa_decode_append with the step's token: append and decode in one call."""
         i = self.inputs
         out = self.out if out is None else out
@@ -107,16 +107,24 @@ class GpuStep:
         pa.pa_decode_append(i.q, i.k_new, i.v_new, slots, self.k_cache, self.v_cache,
                             self.d_tables, self.d_lens, self.w.max_seq_len(), self.w.scale, out,
                             self.desc, i.k_scale, i.v_scale, workspace=self.workspace,
-                            partition_size=self.partition)
+                            partition_size=self.partition, seq_starts=_dev(seq_starts))
         return out
 
-    def decode(self, out=None):
+    def decode(self, out=None, seq_starts=None):
         i = self.inputs
         out = self.out if out is None else out
         pa.pa_decode(i.q, self.k_cache, self.v_cache, self.d_tables, self.d_lens,
                      self.w.max_seq_len(), self.w.scale, out, self.desc, i.k_scale, i.v_scale,
-                     workspace=self.workspace, partition_size=self.partition)
+                     workspace=self.workspace, partition_size=self.partition,
+                     seq_starts=_dev(seq_starts))
         return out
+
+
+def _dev(a):
+    """An int32 host array as a device tensor (None stays None)."""
+    if a is None:
+        return None
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
 
 
 def _ancestors(ops):
@@ -188,7 +196,7 @@ class OracleStep:
                             self.v_cache, self.step_slots, **common)
         self.inputs = inputs
 
-    def decode(self, rows=None):
+    def decode(self, rows=None, seq_starts=None):
         w, i = self.w, self.inputs
         if rows is None and self.only is not None:
             rows = [(b, h) for b in self.only for h in range(w.num_q_heads)]
@@ -196,7 +204,8 @@ class OracleStep:
                              self.lens, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
                              head_dim=w.head_dim, block_size=w.block_size, num_blocks=w.num_blocks,
                              q_dtype=w.q_dtype, kv_dtype=w.kv_dtype, scale=w.scale,
-                             k_scale=i.k_scale, v_scale=i.v_scale, rows=rows)
+                             k_scale=i.k_scale, v_scale=i.v_scale, rows=rows,
+                             seq_starts=seq_starts)
 
     def block_ids(self):
         """Physical blocks the selected decode positions map."""

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 25, names
+    assert len(names) == 29, names
     lib = ctypes.CDLL(pa.LIB_PATH)
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing, missing
@@ -240,3 +240,89 @@ def test_one_hip_runtime_whatever_the_import_order():
                          timeout=300)
     assert out.returncode == 0, out.stderr
     assert out.stdout.startswith("1 "), out.stdout
+
+
+@pytest.mark.parametrize("bs", [16, 64])
+def test_pool_matches_model_with_windows_and_swaps(bs):
+    """Window slides and swaps out and in, mixed with appends, forks, frees and
+    copies: the library and the model agree on tables, lengths, window
+    starts, refcounts, statistics, copies and swap pairs, and on every error."""
+    rng = np.random.default_rng(23)
+    NB, NH = 160, 90
+    pool = pa.pa_block_pool_init(NB, 2, 64, "bf16", block_size=bs, shuffle_seed=77,
+                                 num_host_blocks=NH)
+    model = am.PoolModel(NB, bs, 77, num_host_blocks=NH)
+    live = []  # (lib id, model id)
+    counts = {"slide": 0, "out": 0, "in": 0}
+
+    def same_error(call, status):
+        with pytest.raises(pa.PaError) as e:
+            call()
+        assert e.value.status == status
+
+    for it in range(2000):
+        op = rng.integers(0, 12)
+        if op < 2 or not live:
+            live.append((pa.pa_seq_create(pool), model.seq_create()))
+        elif op < 5:
+            l, m = live[rng.integers(len(live))]
+            n = int(rng.integers(0, 3 * bs))
+            st, ms = model.append_slots(m, n)
+            if st == am.OK:
+                np.testing.assert_array_equal(pa.pa_seq_append_slots(pool, l, n), ms)
+            else:
+                same_error(lambda: pa.pa_seq_append_slots(pool, l, n), st)
+        elif op < 6:
+            l, m = live[rng.integers(len(live))]
+            st, mc = model.fork(m)
+            if st == am.OK:
+                live.append((pa.pa_seq_fork(pool, l), mc))
+            else:
+                same_error(lambda: pa.pa_seq_fork(pool, l), st)
+        elif op < 7:
+            l, m = live.pop(rng.integers(len(live)))
+            pa.pa_seq_free(pool, l)
+            model.free_seq(m)
+        elif op < 9:
+            l, m = live[rng.integers(len(live))]
+            w = int(rng.integers(0, 4 * bs))
+            st, rel = model.slide_window(m, w)
+            if st == am.OK:
+                assert pa.pa_seq_slide_window(pool, l, w) == rel
+                counts["slide"] += 1
+            else:
+                same_error(lambda: pa.pa_seq_slide_window(pool, l, w), st)
+        elif op < 10:
+            np.testing.assert_array_equal(
+                pa.pa_pool_take_copies(pool),
+                np.array(model.take_copies(), dtype=np.int32).reshape(-1, 2))
+        else:
+            l, m = live[rng.integers(len(live))]
+            if m in model.swapped:
+                st, mp = model.swap_in(m)
+                fn, key = pa.pa_seq_swap_in, "in"
+            else:
+                st, mp = model.swap_out(m)
+                fn, key = pa.pa_seq_swap_out, "out"
+            if st == am.OK:
+                np.testing.assert_array_equal(fn(pool, l),
+                                              np.array(mp, dtype=np.int32).reshape(-1, 2))
+                counts[key] += 1
+            else:
+                same_error(lambda: fn(pool, l), st)
+        if it % 50 == 0:
+            res = [(l, m) for l, m in live if m not in model.swapped]
+            maxb = 64
+            t, n, w = pa.pa_export_block_tables(pool, [l for l, _ in res], maxb,
+                                                with_starts=True)
+            st, mt, mn, mw = model.export([m for _, m in res], maxb, with_starts=True)
+            assert st == am.OK
+            np.testing.assert_array_equal(t, np.array(mt, dtype=np.int32).reshape(t.shape))
+            np.testing.assert_array_equal(n, np.array(mn, dtype=np.int32))
+            np.testing.assert_array_equal(w, np.array(mw, dtype=np.int32))
+            s, ms = pa.pa_pool_get_stats(pool), model.stats()
+            for k in ms:
+                assert s[k] == ms[k], k
+            for b in range(NB):
+                assert pa.pa_block_refcount(pool, b) == model.refcount[b]
+    assert counts["slide"] > 100 and counts["out"] > 30 and counts["in"] > 30, counts
