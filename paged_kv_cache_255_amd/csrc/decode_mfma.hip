@@ -111,6 +111,9 @@ struct MfmaWave {
     static constexpr int PV_TILES = D / 16;
     static constexpr int V_ROW_BYTES = kTile * KE; // one V^T row (16 tokens)
     static constexpr int TILE_BYTES = kTile * D * KE;
+    // Tiles in flight per wave: an FP8 tile is half the bytes of a 16-bit
+    // one, so twice as many keep the same bytes in flight.
+    static constexpr int DEPTH = KE == 1 ? 4 : 2;
     static_assert(CHUNKS % 4 == 0, "row must split into 4 lane groups");
 
     struct Tile {
@@ -240,16 +243,16 @@ struct MfmaWave {
     {
 #pragma unroll
         for (int j = 0; j < CH_PER_LANE; ++j)
-            T.k[j] = load16(kt + col * ROW_BYTES + (grp + 4 * j) * 16);
+            T.k[j] = load16_stream(kt + col * ROW_BYTES + (grp + 4 * j) * 16);
 #pragma unroll
         for (int t = 0; t < PV_TILES; ++t) {
             const char *p = vt + (16 * t + col) * V_ROW_BYTES + grp * 4 * KE;
             if constexpr (KE == 2) {
-                const u32x2 x = *reinterpret_cast<const u32x2 *>(p);
+                const u32x2 x = load8_stream(p);
                 T.v[t][0] = x.x;
                 T.v[t][1] = x.y;
             } else {
-                T.v[t][0] = *reinterpret_cast<const uint32_t *>(p);
+                T.v[t][0] = load4_stream(p);
             }
         }
     }
@@ -367,16 +370,16 @@ struct MfmaWave {
             load_tile(kbase + o, vbase + o, col, grp, T);
         };
 
-        // Two tiles alternate: while one is computed, the next is in flight.
-        // The loop runs over pairs of tiles and has one exit, at the
-        // bottom; the next load is issued on every path (past the end it
-        // re-reads the last tile, an L2 hit).  A load issued on one path
-        // only, or an exit that shares a block with the back edge, would make
-        // the compiler's wait counts assume a shorter queue and wait for the
-        // next tile before the current one is done.  An entry outside the
+        // A ring of DEPTH tiles: while one is computed, the next DEPTH - 1
+        // are in flight.  The loop runs over groups of DEPTH tiles and has one
+        // exit, at the bottom; the next load is issued on every path (past the
+        // end it re-reads the last tile, an L2 hit).  A load issued on one
+        // path only, or an exit that shares a block with the back edge, would
+        // make the compiler's wait counts assume a shorter queue and wait for
+        // the next tile before the current one is done.  An entry outside the
         // pool is recorded and block 0 read in its place (the caller turns
         // the result into NaN), so no early exit is needed either.
-        Tile A, B;
+        Tile T[DEPTH];
         const int32_t n = last - jb0 + 1; // tiles in the range, >= 1
         bool bad = w0 < 0 || w0 > n_seq;
         auto checked = [&](int32_t id) {
@@ -403,28 +406,37 @@ struct MfmaWave {
             if (put)
                 load_new_token(a, b, g, (t1 - 1) % kTile, nt);
         }
-        load(checked(id_of(jb0)), sub_of(jb0), A);
-        int32_t idB = id_of(jb0 + 1);
-        for (int32_t i = 0; i + 1 < n; i = uniform(i + 2)) {
-            const int32_t jb = jb0 + i;
-            const int32_t idA = id_of(jb + 2);
-            load(checked(idB), sub_of(jb + 1), B);
-            __builtin_amdgcn_sched_barrier(0); // B's loads go out before A is waited for
-            compute(A, lo_of(jb), valid_of(jb), sc);
-            idB = id_of(jb + 3);
-            load(checked(idA), sub_of(jb + 2), A);
-            __builtin_amdgcn_sched_barrier(0);
-            if (put && jb + 1 == last)
-                apply_new_token(B, nt);
-            compute(B, lo_of(jb + 1), valid_of(jb + 1), sc);
+        // tile jb0 + k lives in T[k % DEPTH]
+#pragma unroll
+        for (int d = 0; d + 1 < DEPTH; ++d)
+            load(checked(id_of(jb0 + d)), sub_of(jb0 + d), T[d]);
+        int32_t id_next = id_of(jb0 + DEPTH - 1); // block id of the next tile to load
+        int32_t i = 0;
+        for (; i + DEPTH <= n; i = uniform(i + DEPTH)) {
+#pragma unroll
+            for (int d = 0; d < DEPTH; ++d) {
+                const int32_t jb = jb0 + i + d;
+                const int32_t id_after = id_of(jb + DEPTH); // fetched one tile ahead of use
+                load(checked(id_next), sub_of(jb + DEPTH - 1), T[(d + DEPTH - 1) % DEPTH]);
+                __builtin_amdgcn_sched_barrier(0); // that load goes out before T[d] is waited for
+                if (put && jb == last)
+                    apply_new_token(T[d], nt);
+                compute(T[d], lo_of(jb), valid_of(jb), sc);
+                id_next = id_after;
+            }
         }
-        if (n & 1) {
-            if (put)
-                apply_new_token(A, nt);
-            compute(A, lo_of(last), valid_of(last), sc); // A holds the last tile
+        // the last n - i (< DEPTH) tiles, already in T[0 ..]
+#pragma unroll
+        for (int d = 0; d + 1 < DEPTH; ++d) {
+            if (i + d < n) {
+                const int32_t jb = jb0 + i + d;
+                if (put && jb == last)
+                    apply_new_token(T[d], nt);
+                compute(T[d], lo_of(jb), valid_of(jb), sc);
+            }
         }
-        // Drain the re-read issued past the end (n even), so no load into
-        // these registers is in flight when the next range starts.
+        // Drain the re-reads issued past the end, so no load into these
+        // registers is in flight when the next range starts.
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         if (put) {
             const size_t row = ((size_t)b * a.num_kv_heads + g) * D;

@@ -116,14 +116,14 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a, int32_t 
         float kv[S::CH_PER_LANE][S::EPC];
 #pragma unroll
         for (int j = 0; j < S::CH_PER_LANE; ++j) {
-            const u32x4 c = load16(kbase + tile + tq * S::ROW_BYTES + (cq + 4 * j) * 16);
+            const u32x4 c = load16_stream(kbase + tile + tq * S::ROW_BYTES + (cq + 4 * j) * 16);
             Chunk<KT>::unpack(c, kv[j]);
         }
         // V tile: this lane's rows.
         float vv[S::V_INSTR][S::V_TPL];
 #pragma unroll
         for (int i = 0; i < S::V_INSTR; ++i) {
-            const u32x4 c = load16(vbase + tile + i * 1024 + lane * 16);
+            const u32x4 c = load16_stream(vbase + tile + i * 1024 + lane * 16);
             Chunk<KT>::unpack(c, vv[i]);
         }
 
