@@ -71,6 +71,10 @@ def parse():
     ap.add_argument("--upload-per-step", action="store_true",
                     help="run the host allocator and copy the step's metadata inside each "
                          "timed step")
+    ap.add_argument("--feature", choices=["copy", "swap", "window", "prefix"], default=None,
+                    help="measure one of the paths beside the decode step on the workload's "
+                         "shapes (block copies of copy on write, swap transfers, windowed "
+                         "decode, prefix-cache host work) and print one JSON line for it")
     ap.add_argument("--traffic-record", nargs=5, default=None,
                     metavar=("BENCH_LINE", "FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
                              "COPY_WRITE_CSV"),
@@ -99,6 +103,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(torch)
+        return
+    if args.feature:
+        FEATURES[args.feature](args, torch, pa, workloads, execute_plan)
         return
 
     torch.cuda.set_device(0)
@@ -255,7 +262,7 @@ def main():
                                vs, op, None, 0, 0, dref, s_h)
         else:
             rc = lib.pa_decode_partials(qp, kcp, vcp, tables_p, maxb, lens_p, None, B, max_len,
-                                        scale, ks, vs, ws_p, ws_bytes, partition, dref, s_h)
+                                        scale, ks, vs, op, ws_p, ws_bytes, partition, dref, s_h)
         if rc:
             raise RuntimeError("launch failed: " + pa.pa_last_error())
 
@@ -450,6 +457,192 @@ def write_traffic_record(bench_line, fetch_csv, write_csv, copy_fetch_csv, copy_
         f.write("\n")
     print(f"{path}: {rec['hbm_bytes_per_launch']} HBM bytes per launch, "
           f"{rec['hbm_bytes_per_launch'] / rec['algorithmic_bytes_per_launch']:.4f}x algorithmic")
+
+
+def _events(torch):
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def _time_launches(torch, fn, reps):
+    """Mean ms of fn() over reps back-to-back calls between two events."""
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = _events(torch)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def _feature_line(name, value, unit, extra):
+    line = {"metric": name, "value": value, "unit": unit, "n_gpus": 1,
+            "higher_is_better": unit != "us", "data": "synthetic"}
+    line.update(extra)
+    print(json.dumps(line), flush=True)
+
+
+def feature_copy(args, torch, pa, workloads, execute_plan):
+    """Copy-on-write block copies: 4,096 (source, destination) pairs of config-2
+    blocks in one pa_copy_blocks launch.  Bytes = K and V of each block read
+    once and written once."""
+    w = workloads.config(2)
+    NB, npairs = 16384, 4096
+    desc = pa.kv_desc(w.num_q_heads, w.num_kv_heads, w.head_dim, NB, w.q_dtype, w.kv_dtype)
+    elems = NB * w.num_kv_heads * 16 * w.head_dim
+    kc = torch.randn(elems, device="cuda").to(torch.bfloat16)
+    vc = torch.randn(elems, device="cuda").to(torch.bfloat16)
+    perm = np.random.default_rng(7).permutation(NB)
+    pairs = torch.from_numpy(np.stack([perm[:npairs], perm[npairs:2 * npairs]], 1)
+                             .astype(np.int32)).cuda()
+    ms = _time_launches(torch, lambda: pa.pa_copy_blocks(kc, vc, pairs, desc), args.steps)
+    block = 16 * w.num_kv_heads * w.head_dim * 2
+    moved = 2 * 2 * npairs * block  # K and V, read and written
+    _feature_line("copy-on-write block copies: HBM GB/s (read + write)",
+                  round(moved / (ms * 1e-3) / 1e9, 1), "GB/s",
+                  {"us_per_launch": round(ms * 1e3, 2), "pairs": npairs,
+                   "block_bytes_k_and_v": 2 * block, "peak": HBM_PEAK_GBS,
+                   "frac": round(moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                   "config": {"workload": "config-2 blocks (8 KV heads x 16 x 128 bf16)"}})
+
+
+def feature_swap(args, torch, pa, workloads, execute_plan):
+    """Swapping config 2's 32 sequences out to pinned host memory and back in,
+    each direction as one pa_swap_blocks launch over every block of every
+    table (pairs from pa_seq_swap_out / pa_seq_swap_in)."""
+    w = workloads.config(2)
+    Hkv, D = w.num_kv_heads, w.head_dim
+    NB = w.num_blocks
+    pool = pa.pa_block_pool_init(NB, Hkv, D, w.kv_dtype, shuffle_seed=w.shuffle_seeds[0],
+                                 num_host_blocks=NB)
+    ids, pre = execute_plan(pool, w.ops)
+    dec = [ids[s] for s in w.decode_seqs]
+    desc = pa.kv_desc(w.num_q_heads, Hkv, D, NB, w.q_dtype, w.kv_dtype)
+    block = pa.pa_block_bytes(pool)
+    kc = torch.zeros(NB * block, dtype=torch.uint8, device="cuda")
+    vc = torch.zeros_like(kc)
+    hk = torch.zeros(NB * block, dtype=torch.uint8, pin_memory=True)
+    hv = torch.zeros(NB * block, dtype=torch.uint8, pin_memory=True)
+    outs, ins = [], []
+    for cycle in range(args.warmup + args.steps):
+        p_out = np.concatenate([pa.pa_seq_swap_out(pool, s) for s in dec])
+        d_out = torch.from_numpy(p_out).cuda()
+        torch.cuda.synchronize()
+        e0, e1 = _events(torch)
+        e0.record()
+        pa.pa_swap_blocks(kc, vc, hk, hv, d_out, desc, to_host=True)
+        e1.record()
+        p_in = np.concatenate([pa.pa_seq_swap_in(pool, s) for s in dec])
+        d_in = torch.from_numpy(p_in).cuda()
+        torch.cuda.synchronize()
+        e2, e3 = _events(torch)
+        e2.record()
+        pa.pa_swap_blocks(kc, vc, hk, hv, d_in, desc, to_host=False)
+        e3.record()
+        torch.cuda.synchronize()
+        if cycle >= args.warmup:
+            outs.append(e0.elapsed_time(e1))
+            ins.append(e2.elapsed_time(e3))
+    nbytes = 2 * len(p_out) * block  # K and V
+    out_ms, in_ms = float(np.median(outs)), float(np.median(ins))
+    _feature_line("swap to pinned host memory and back: GB/s per direction",
+                  round(nbytes / (out_ms * 1e-3) / 1e9, 2), "GB/s",
+                  {"to_host_gbs": round(nbytes / (out_ms * 1e-3) / 1e9, 2),
+                   "to_device_gbs": round(nbytes / (in_ms * 1e-3) / 1e9, 2),
+                   "to_host_ms": round(out_ms, 3), "to_device_ms": round(in_ms, 3),
+                   "blocks": int(len(p_out)), "bytes_per_direction": int(nbytes),
+                   "cycles": args.steps,
+                   "config": {"workload": "config 2: 32 sequences, every block of every table"}})
+
+
+def feature_window(args, torch, pa, workloads, execute_plan):
+    """Windowed decode at config 2: every sequence keeps its last 1,024 tokens
+    (pa_seq_slide_window releases the blocks before them).  The decode kernel
+    alone, back to back over 4 cache replicas; bytes = the window tokens' K
+    and V."""
+    w = workloads.config(2)
+    Hq, Hkv, D, B = w.num_q_heads, w.num_kv_heads, w.head_dim, w.num_seqs
+    win = 1024
+    NB = w.num_blocks
+    pool = pa.pa_block_pool_init(NB, Hkv, D, w.kv_dtype, shuffle_seed=w.shuffle_seeds[0])
+    ids, pre = execute_plan(pool, w.ops)
+    dec = [ids[s] for s in w.decode_seqs]
+    slots = pa.pa_seq_append_slots_batch(pool, dec, 1)
+    released = sum(pa.pa_seq_slide_window(pool, s, win) for s in dec)
+    maxb = -(-max(w.decode_lengths()) // 16)
+    tables, lens, starts = pa.pa_export_block_tables(pool, dec, maxb, with_starts=True)
+    desc = pa.kv_desc(Hq, Hkv, D, NB, w.q_dtype, w.kv_dtype)
+    k_pre, v_pre = workloads.prefill_tensors(w, 0, "cuda")
+    q, k_new, v_new = workloads.step_tensors(w, 0, "cuda")
+    R = 4
+    caches = []
+    for _ in range(R):
+        kc = torch.zeros(NB * Hkv * 16 * D, dtype=torch.bfloat16, device="cuda")
+        vc = torch.zeros_like(kc)
+        pa.pa_cache_append(k_pre, v_pre, kc, vc, torch.from_numpy(pre).cuda(), desc)
+        pa.pa_cache_append(k_new, v_new, kc, vc, torch.from_numpy(slots).cuda(), desc)
+        caches.append((kc, vc))
+    out = torch.empty_like(q)
+    dt, dl, ds = (torch.from_numpy(a).cuda() for a in (tables, lens, starts))
+    ws = torch.empty(pa.pa_decode_workspace_bytes(desc, B, maxb * 16, pa.PARTITION_BALANCED),
+                     dtype=torch.uint8, device="cuda")
+    it = [0]
+
+    def launch():
+        kc, vc = caches[it[0] % R]
+        it[0] += 1
+        pa.pa_decode_partials(q, kc, vc, dt, dl, maxb * 16, w.scale, out, desc, ws,
+                              pa.PARTITION_BALANCED, seq_starts=ds)
+
+    ms = _time_launches(torch, launch, args.steps)
+    tokens = int((lens - starts).sum())
+    nbytes = tokens * Hkv * D * 2 * 2
+    _feature_line("windowed decode: KV-read HBM GB/s (window tokens)",
+                  round(nbytes / (ms * 1e-3) / 1e9, 1), "GB/s",
+                  {"kernel_us_avg": round(ms * 1e3, 2), "window": win,
+                   "window_tokens": tokens, "blocks_released": int(released),
+                   "frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                   "config": {"workload": "config 2, every sequence slid to its last 1024 "
+                                          "tokens, balanced split, 4 cache replicas"}})
+
+
+def feature_prefix(args, torch, pa, workloads, execute_plan):
+    """Prefix-cache host work at config 4's shape: 256 requests whose prompts
+    start with one 2,048-token system prompt.  Times match + prefill slots +
+    register per request (the host side of admitting a request), and counts
+    the blocks the cache saves against private copies."""
+    import time
+    w = workloads.config(4)
+    rng = np.random.default_rng(4)
+    P = 2048
+    system = [int(x) for x in rng.integers(0, 32000, size=P)]
+    suffixes = [int(n) for n in np.minimum(rng.geometric(1 / 350, size=256), 2048)]
+    prompts = [np.array(system + [int(x) for x in rng.integers(0, 32000, size=n)], np.int32)
+               for n in suffixes]
+    need = sum(-(-len(p) // 16) for p in prompts)
+    pool = pa.pa_block_pool_init(need + 64, w.num_kv_heads, w.head_dim, w.kv_dtype,
+                                 shuffle_seed=1)
+    t0 = time.perf_counter()
+    matched = 0
+    for pr in prompts:
+        s = pa.pa_seq_create(pool)
+        m = pa.pa_prefix_match(pool, s, pr)
+        matched += m
+        pa.pa_seq_append_slots(pool, s, len(pr) - m)
+        pa.pa_prefix_register(pool, s, pr)
+    dt = time.perf_counter() - t0
+    st = pa.pa_pool_get_stats(pool)
+    _feature_line("prefix caching: host time per admitted request", round(dt / 256 * 1e6, 2),
+                  "us", {"requests": 256, "tokens_matched": matched,
+                         "blocks_used": st["used_blocks"], "blocks_without_cache": need,
+                         "blocks_saved_frac": round(1 - st["used_blocks"] / need, 4),
+                         "config": {"workload": "config-4 shape: 256 prompts = 2048-token "
+                                                "system prompt + Geometric(1/350) suffix"}})
+
+
+FEATURES = {"copy": feature_copy, "swap": feature_swap, "window": feature_window,
+            "prefix": feature_prefix}
 
 
 def copy_calibration(torch):

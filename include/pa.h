@@ -398,15 +398,18 @@ pa_status pa_decode_append(const void *q, const void *k_new, const void *v_new,
  * partition_size must not be PA_PARTITION_NONE and `workspace` as for
  * pa_decode).  pa_decode_partials runs the per-partition kernel and leaves
  * each partition's softmax state (running max, sum, unnormalised output) in
- * the workspace; pa_decode_merge combines them into `out`.  Issued in this
- * order on one stream they compute what pa_decode computes, bit for bit (it
- * launches the same two kernels); a caller may time or schedule the two
- * separately. */
+ * the workspace; with PA_PARTITION_BALANCED it also writes to `out` the rows
+ * of every (sequence, KV head) that one work item covers whole.
+ * pa_decode_merge combines the partial states into the other rows of `out`.
+ * Issued in this order on one stream, with the same `out`, they compute what
+ * pa_decode computes, bit for bit (it launches the same two kernels); a caller
+ * may time or schedule the two separately.  `out` must not be NULL
+ * (PA_ERR_INVALID_ARG). */
 pa_status pa_decode_partials(const void *q, const void *k_cache, const void *v_cache,
                              const int32_t *block_tables, int32_t max_blocks_per_seq,
                              const int32_t *seq_lens, const int32_t *seq_starts,
                              int32_t num_seqs, int32_t max_seq_len, float scale, float k_scale,
-                             float v_scale, void *workspace, size_t workspace_bytes,
+                             float v_scale, void *out, void *workspace, size_t workspace_bytes,
                              int32_t partition_size, const pa_kv_desc *desc, void *stream);
 pa_status pa_decode_merge(const int32_t *seq_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
                           int32_t max_seq_len, void *out, const void *workspace,

@@ -100,7 +100,7 @@ _SIGS = {
                                  ctypes.c_float, ctypes.c_float, _P, _P, ctypes.c_size_t, _I32,
                                  ctypes.POINTER(KvDesc), _P]),
     "pa_decode_partials": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _P, _I32, _I32,
-                                          ctypes.c_float, ctypes.c_float, ctypes.c_float, _P,
+                                          ctypes.c_float, ctypes.c_float, ctypes.c_float, _P, _P,
                                           ctypes.c_size_t, _I32, ctypes.POINTER(KvDesc), _P]),
     "pa_decode_merge": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _P, ctypes.c_size_t, _I32,
                                        ctypes.POINTER(KvDesc), _P]),
@@ -456,15 +456,19 @@ def pa_decode_append(q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tabl
                                  _stream(stream)), "pa_decode_append")
 
 
-def pa_decode_partials(q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale, desc,
-                       workspace, partition_size, k_scale=1.0, v_scale=1.0, stream=None,
+def pa_decode_partials(q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale, out,
+                       desc, workspace, partition_size, k_scale=1.0, v_scale=1.0, stream=None,
                        seq_starts=None):
+    """The first launch of a partitioned pa_decode.  In the balanced mode it
+    writes the rows of the (sequence, KV head) segments one work item covers
+    whole to `out`; pa_decode_merge writes the others."""
     B = seq_lens.numel()
     _check_tensor(workspace, "workspace")
+    _check_tensor(out, "out")
     _check(_lib.pa_decode_partials(_addr(q), _addr(k_cache), _addr(v_cache), _addr(block_tables),
                                    block_tables.shape[1], _addr(seq_lens),
                                    _starts(seq_starts, B), B, max_seq_len, scale,
-                                   k_scale, v_scale, _addr(workspace),
+                                   k_scale, v_scale, _addr(out), _addr(workspace),
                                    workspace.numel() * workspace.element_size(), partition_size,
                                    ctypes.byref(desc), _stream(stream)), "pa_decode_partials")
 

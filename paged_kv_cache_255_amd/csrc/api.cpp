@@ -259,7 +259,9 @@ pa_status decode_impl(Phase phase, const void *q, const void *k_cache, const voi
         return fail(PA_ERR_INVALID_ARG, "negative size");
     if (num_seqs == 0)
         return PA_OK;
-    if (!seq_lens || (phase != kPartials && !out))
+    // every phase may write rows of out: the balanced partials kernel writes
+    // the rows one work item covers whole
+    if (!seq_lens || !out)
         return fail(PA_ERR_INVALID_ARG, "null pointer");
     if (phase != kMerge) {
         if (!q || !k_cache || !v_cache || !block_tables)
@@ -421,12 +423,12 @@ pa_status pa_decode_partials(const void *q, const void *k_cache, const void *v_c
                              const int32_t *block_tables, int32_t max_blocks_per_seq,
                              const int32_t *seq_lens, const int32_t *seq_starts,
                              int32_t num_seqs, int32_t max_seq_len, float scale, float k_scale,
-                             float v_scale, void *workspace, size_t workspace_bytes,
+                             float v_scale, void *out, void *workspace, size_t workspace_bytes,
                              int32_t partition_size, const pa_kv_desc *desc, void *stream)
 {
     return decode_impl(kPartials, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
                        seq_lens, seq_starts, num_seqs, max_seq_len, scale, k_scale, v_scale,
-                       nullptr, workspace, workspace_bytes, partition_size, desc, stream);
+                       out, workspace, workspace_bytes, partition_size, desc, stream);
 }
 
 pa_status pa_decode_merge(const int32_t *seq_lens, int32_t num_seqs, int32_t max_blocks_per_seq,

@@ -326,3 +326,15 @@ def test_pool_matches_model_with_windows_and_swaps(bs):
             for b in range(NB):
                 assert pa.pa_block_refcount(pool, b) == model.refcount[b]
     assert counts["slide"] > 100 and counts["out"] > 30 and counts["in"] > 30, counts
+
+
+def test_decode_partials_needs_out():
+    """The balanced partials launch writes whole-segment rows to out, so a
+    NULL out is refused before anything reaches the device."""
+    desc = pa.kv_desc(8, 2, 128, 16, "bf16", "bf16")
+    fake = ctypes.c_void_p(4096)
+    st = pa._lib.pa_decode_partials(fake, fake, fake, fake, 1, fake, None, 1, 16, 0.1, 1.0,
+                                    1.0, None, fake, 1 << 20, pa.PARTITION_BALANCED,
+                                    ctypes.byref(desc), None)
+    assert st == pa.ERR_INVALID_ARG
+    assert "null" in pa.pa_last_error()

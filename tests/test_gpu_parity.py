@@ -260,11 +260,55 @@ def test_two_phase_matches_pa_decode_bits(cid, kernel, part):
     one = g.decode().clone()
     two = torch.full_like(one, 7.0)
     pa.pa_decode_partials(inp.q, g.k_cache, g.v_cache, g.d_tables, g.d_lens, w.max_seq_len(),
-                          w.scale, g.desc, g.workspace, part, inp.k_scale, inp.v_scale)
+                          w.scale, two, g.desc, g.workspace, part, inp.k_scale, inp.v_scale)
     pa.pa_decode_merge(g.d_lens, g.d_tables.shape[1], w.max_seq_len(), two, g.desc, g.workspace,
                        part)
     torch.cuda.synchronize()
     assert torch.equal(one.view(torch.int16), two.view(torch.int16))
+
+
+def _short_workload(lens, seed):
+    w = workloads._independent("short-bf16", 2, lens, 1.25, num_q_heads=32, num_kv_heads=8,
+                               head_dim=128, q_dtype="bf16", kv_dtype="bf16", seed=seed,
+                               block_size=16)
+    w.shuffle_seeds = [seed * 7919 + 1]
+    return w
+
+
+@pytest.mark.parametrize("case", ["one-tile", "few-tiles", "config4-full"])
+def test_two_phase_with_runs_covering_whole_segments(case):
+    """With the balanced split, a work item that covers a whole (sequence, KV
+    head) writes that row itself, in the first launch.  Short sequences make
+    such items common: lengths of 1..15 tokens (one tile per segment, so every
+    item is a whole segment), 300 sequences of 1..47 tokens, and config 4 at
+    full size (segments of 130..256 tiles against items of ~300 tiles).  The
+    two launches, given the output, match pa_decode bit for bit and the
+    oracle on sampled rows."""
+    say(f"[case] two-phase whole segments {case}")
+    rng = np.random.default_rng(91)
+    if case == "one-tile":
+        w = _short_workload(rng.integers(1, 16, size=40), 71)
+    elif case == "few-tiles":
+        w = _short_workload(rng.integers(1, 48, size=300), 72)
+    else:
+        w = workloads.config(4)
+    part = pa.PARTITION_BALANCED
+    inp = Inputs(w)
+    g = GpuStep(w, 0, inp, partition=part, kernel=pa.KERNEL_MFMA)
+    g.append_prefill()
+    g.append_step()
+    one = g.decode().clone()
+    two = torch.full_like(one, 7.0)
+    pa.pa_decode_partials(inp.q, g.k_cache, g.v_cache, g.d_tables, g.d_lens, w.max_seq_len(),
+                          w.scale, two, g.desc, g.workspace, part, inp.k_scale, inp.v_scale)
+    pa.pa_decode_merge(g.d_lens, g.d_tables.shape[1], w.max_seq_len(), two, g.desc, g.workspace,
+                       part)
+    torch.cuda.synchronize()
+    assert torch.equal(one.view(torch.int16), two.view(torch.int16))
+    only = sorted({0, 1, w.num_seqs // 2, w.num_seqs - 1})
+    o = OracleStep(w, 0, inp, only=only)
+    ref = o.decode().reshape(len(only), w.num_q_heads, w.head_dim)
+    check_close(to_f64(two)[only], ref, w.kv_dtype, w.q_dtype)
 
 
 APPEND_CASES = [(2, pa.KERNEL_MFMA, pa.PARTITION_BALANCED), (2, pa.KERNEL_MFMA, 64),
