@@ -154,10 +154,13 @@ class Pool:
     def __init__(self, handle, config):
         self.handle = handle
         self.config = config
+        # held here: module globals may already be None when a pool is
+        # collected at interpreter exit
+        self._destroy = _lib.pa_block_pool_destroy
 
     def __del__(self):
         if getattr(self, "handle", None):
-            _lib.pa_block_pool_destroy(self.handle)
+            self._destroy(self.handle)
             self.handle = None
 
 

@@ -53,39 +53,49 @@ __device__ __forceinline__ void merge_row(const DecodeArgs &a, int32_t b, int32_
         o[i * kWave + lane] = from_f32<QT>(acc[i] * inv);
 }
 
-// Combines the nparts partial states in slots w0 .. w0 + nparts - 1 of
-// segment (b, g) into its G output rows, one wave for the whole segment:
-//   M = max_p m_p,  out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p
-// per query head, the identity the online update inside a work item uses,
-// applied here one batch of parts at a time (in slot order: the result does
-// not depend on which wave merges).  A part's G x D accumulators are
-// contiguous ([h][d]); lane l owns outputs o = 256 s + 4 l + j (s < S = G D /
-// 256, j < 4), so every load instruction reads 1 KiB of one part and no
-// cross-lane reduction is needed.  A NaN partial (a bad block-table entry)
-// makes its rows NaN.
-template <int QT, int D, int S>
-__device__ __forceinline__ void merge_segment_s(const DecodeArgs &a, int32_t b, int32_t g,
-                                                int64_t w0, int64_t nparts, int lane)
-{
-    using TQ = typename Store<QT>::T;
-    constexpr int CH = 16 / S; // parts per batch: 16 x 3 loads in flight per lane
-    int hs[S];
+// Merge state of the outputs one lane owns in a segment (sequence b, KV
+// head g): a part's G x D accumulators are contiguous ([h][d]), and lane l
+// owns outputs o = 256 s + 4 l + j (s < S = G D / 256, j < 4), so every load
+// instruction reads 1 KiB of one part and no cross-lane reduction is needed.
+// Per chunk s: the running max M and sum L of the lane's query head and four
+// unnormalised accumulators.
+template <int S>
+struct MergeState {
     float M[S], L[S];
     f32x4 acc[S];
+    bool nan_seen;
+
+    __device__ __forceinline__ MergeState() : nan_seen(false)
+    {
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-        hs[s] = (256 * s + 4 * lane) / D;
-        M[s] = -INFINITY;
-        L[s] = 0.f;
-        acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < S; ++s) {
+            M[s] = -INFINITY;
+            L[s] = 0.f;
+            acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
     }
-    bool nan_seen = false;
-    for (int64_t p0 = 0; p0 < nparts; p0 += CH) {
+};
+
+// Folds parts [p_begin, p_end) of the segment whose slots start at w0 into
+// st, CH = 16 / S parts per batch (16 x 3 loads in flight per lane), in slot
+// order, with the online rescale between batches:
+//   M = max_p m_p,  out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p
+// per query head, the identity the online update inside a work item uses.
+template <int D, int S>
+__device__ __forceinline__ void merge_fold(const DecodeArgs &a, int64_t w0, int64_t p_begin,
+                                           int64_t p_end, int lane, MergeState<S> &st)
+{
+    constexpr int CH = 16 / S;
+    int hs[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+        hs[s] = (256 * s + 4 * lane) / D;
+    for (int64_t p0 = p_begin; p0 < p_end; p0 += CH) {
         float mp[CH][S], lp[CH][S];
         f32x4 ap[CH][S];
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
-            const bool in = p0 + c < nparts;
+            const bool in = p0 + c < p_end;
             const int64_t w = w0 + p0 + (in ? c : 0);
             const float *base = ws_acc(a, w, 0, D);
 #pragma unroll
@@ -100,35 +110,58 @@ __device__ __forceinline__ void merge_segment_s(const DecodeArgs &a, int32_t b, 
         }
 #pragma unroll
         for (int s = 0; s < S; ++s) {
-            float mb = M[s];
+            float mb = st.M[s];
 #pragma unroll
             for (int c = 0; c < CH; ++c) {
-                nan_seen |= mp[c][s] != mp[c][s];
+                st.nan_seen |= mp[c][s] != mp[c][s];
                 mb = fmaxf(mb, mp[c][s]);
             }
             // every part holds a finite max (a real score, or the finite start
             // value when all its tokens lie before the window), so mb is finite
-            const float alpha = __builtin_amdgcn_exp2f(M[s] - mb); // 0 on the first batch
-            L[s] *= alpha;
-            acc[s] *= alpha;
+            const float alpha = __builtin_amdgcn_exp2f(st.M[s] - mb); // 0 on the first batch
+            st.L[s] *= alpha;
+            st.acc[s] *= alpha;
 #pragma unroll
             for (int c = 0; c < CH; ++c) {
                 const float wgt = __builtin_amdgcn_exp2f(mp[c][s] - mb); // 0 past the end
-                L[s] = fmaf(lp[c][s], wgt, L[s]);
-                acc[s] += ap[c][s] * wgt;
+                st.L[s] = fmaf(lp[c][s], wgt, st.L[s]);
+                st.acc[s] += ap[c][s] * wgt;
             }
-            M[s] = mb;
+            st.M[s] = mb;
         }
     }
+}
+
+// Writes the G output rows of segment (b, g) from a finished state.  A NaN
+// partial (a bad block-table entry) makes its rows NaN; L = 0 (every token
+// before the window start) gives zeros.
+template <int QT, int D, int S>
+__device__ __forceinline__ void merge_store(const DecodeArgs &a, int32_t b, int32_t g,
+                                            const MergeState<S> &st, int lane)
+{
+    using TQ = typename Store<QT>::T;
     TQ *o = static_cast<TQ *>(a.out) + ((size_t)b * a.num_q_heads + (size_t)g * a.group) * D;
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-        const float inv = nan_seen ? NAN : (L[s] == 0.f ? 0.f : 1.f / L[s]); // 0: empty window
-        TQ *r = o + 256 * s + 4 * lane; // row hs[s], dims (256 s + 4 lane) % D ..
+        const float inv = st.nan_seen ? NAN : (st.L[s] == 0.f ? 0.f : 1.f / st.L[s]);
+        TQ *r = o + 256 * s + 4 * lane; // row (256 s + 4 lane) / D
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            r[j] = from_f32<QT>(acc[s][j] * inv);
+            r[j] = from_f32<QT>(st.acc[s][j] * inv);
     }
+}
+
+// Combines the nparts partial states in slots w0 .. w0 + nparts - 1 of
+// segment (b, g) into its G output rows, one wave for the whole segment.
+// Parts are visited in slot order, so the result does not depend on which
+// wave merges.
+template <int QT, int D, int S>
+__device__ __forceinline__ void merge_segment_s(const DecodeArgs &a, int32_t b, int32_t g,
+                                                int64_t w0, int64_t nparts, int lane)
+{
+    MergeState<S> st;
+    merge_fold<D, S>(a, w0, 0, nparts, lane, st);
+    merge_store<QT, D, S>(a, b, g, st, lane);
 }
 
 // G * D / 256 for the shapes merge_segment handles (0: not handled).
@@ -154,6 +187,41 @@ __device__ __forceinline__ void merge_segment(const DecodeArgs &a, int32_t b, in
     }
 }
 
+// Slots w0 .. w0 + nparts - 1 that hold the partial states of segment
+// (sequence b of length n, KV head g).  False when there is nothing to
+// merge: in the balanced split, one run held the whole segment and wrote its
+// rows itself.
+__device__ __forceinline__ bool segment_parts(const DecodeArgs &a, int lane, int32_t b,
+                                              int32_t g, int32_t n, int64_t &w0, int64_t &nparts)
+{
+    if (a.partition == kPartitionBalanced) {
+        const TileCounts tc = tile_counts(a, lane, b);
+        const int64_t T = tc.total;
+        const int32_t R = effective_runs(T, a.waves);
+        const int64_t S0 = tc.before + (int64_t)g * tiles_of(n);
+        const int64_t i0 = run_of_tile(S0, T, R);
+        const int64_t i1 = run_of_tile(S0 + tiles_of(n) - 1, T, R);
+        if (i0 == i1)
+            return false;
+        w0 = i0 + (int64_t)b * a.num_kv_heads + g;
+        nparts = i1 - i0 + 1;
+    } else {
+        w0 = ((int64_t)b * a.num_kv_heads + g) * a.max_parts;
+        nparts = (n + a.partition - 1) / a.partition;
+    }
+    return true;
+}
+
+// The G rows of a segment whose length is out of range (NaN) or zero (0).
+template <int QT, int D>
+__device__ __forceinline__ void merge_fill(const DecodeArgs &a, int32_t b, int32_t g, bool valid,
+                                           int lane)
+{
+    using TQ = typename Store<QT>::T;
+    TQ *o = static_cast<TQ *>(a.out) + ((size_t)b * a.num_q_heads + (size_t)g * a.group) * D;
+    for (int32_t i = lane; i < a.group * D; i += kWave)
+        o[i] = from_f32<QT>(valid ? 0.f : NAN);
+}
 
 template <int QT, int D>
 __global__ __launch_bounds__(64) void merge_kernel(DecodeArgs a)
@@ -176,25 +244,9 @@ __global__ __launch_bounds__(64) void merge_kernel(DecodeArgs a)
             o[i * kWave + lane] = from_f32<QT>(valid ? 0.f : NAN);
         return;
     }
-    // slots w0 .. w0 + nparts - 1 hold this segment's partial states
     int64_t w0, nparts;
-    if (a.partition == kPartitionBalanced) {
-        const TileCounts tc = tile_counts(a, lane, b);
-        const int64_t T = tc.total;
-        const int32_t R = effective_runs(T, a.waves);
-        const int64_t S0 = tc.before + (int64_t)g * tiles_of(n);
-        const int64_t S1 = S0 + tiles_of(n);
-        const int64_t i0 = run_of_tile(S0, T, R);
-        const int64_t i1 = run_of_tile(S1 - 1, T, R);
-        if (i0 == i1)
-            return; // one run held the whole segment and wrote the row itself
-        w0 = i0 + (int64_t)b * a.num_kv_heads + g;
-        nparts = i1 - i0 + 1;
-    } else {
-        w0 = ((int64_t)b * a.num_kv_heads + g) * a.max_parts;
-        nparts = (n + a.partition - 1) / a.partition;
-    }
-    merge_row<QT, D>(a, b, g, h, w0, nparts, lane);
+    if (segment_parts(a, lane, b, g, n, w0, nparts))
+        merge_row<QT, D>(a, b, g, h, w0, nparts, lane);
 }
 
 // One wave per segment (sequence b, KV head g) for the shapes merge_segment
@@ -208,40 +260,122 @@ __global__ __launch_bounds__(64) void merge_segment_kernel(DecodeArgs a)
     const int32_t n = a.seq_lens[b];
     const bool valid = len_ok(a, n);
     if (!valid || n == 0) {
-        using TQ = typename Store<QT>::T;
-        TQ *o = static_cast<TQ *>(a.out) + ((size_t)b * a.num_q_heads + (size_t)g * a.group) * D;
-        for (int32_t i = lane; i < a.group * D; i += kWave)
-            o[i] = from_f32<QT>(valid ? 0.f : NAN);
+        merge_fill<QT, D>(a, b, g, valid, lane);
         return;
     }
     int64_t w0, nparts;
-    if (a.partition == kPartitionBalanced) {
-        const TileCounts tc = tile_counts(a, lane, b);
-        const int64_t T = tc.total;
-        const int32_t R = effective_runs(T, a.waves);
-        const int64_t S0 = tc.before + (int64_t)g * tiles_of(n);
-        const int64_t i0 = run_of_tile(S0, T, R);
-        const int64_t i1 = run_of_tile(S0 + tiles_of(n) - 1, T, R);
-        if (i0 == i1)
-            return; // one run held the whole segment and wrote the rows itself
-        w0 = i0 + (int64_t)b * a.num_kv_heads + g;
-        nparts = i1 - i0 + 1;
-    } else {
-        w0 = ((int64_t)b * a.num_kv_heads + g) * a.max_parts;
-        nparts = (n + a.partition - 1) / a.partition;
+    if (segment_parts(a, lane, b, g, n, w0, nparts))
+        merge_segment<QT, D>(a, b, g, w0, nparts, lane);
+}
+
+// Waves of the wide merge's workgroup: NW x S x 64 lanes x 24 bytes of LDS
+// stays at 48 KiB.
+__host__ __device__ constexpr int wide_merge_waves(int S) { return S >= 8 ? 4 : 8; }
+
+// Segments with many parts (long sequences, few segments): one workgroup of
+// NW waves per segment.  Wave w folds the contiguous parts
+// [w nparts / NW, (w + 1) nparts / NW) like the one-wave merge; wave 0 then
+// combines the NW states from LDS in wave order, with the same identity:
+//   M = max_w M_w,  out = sum_w 2^(M_w - M) acc_w / sum_w 2^(M_w - M) L_w.
+// The grouping is fixed, so the bits do not depend on timing.  A wave with
+// no parts holds M = -inf and L = acc = 0, which weigh 0 (some wave has a
+// part, and every part's max is finite).
+template <int QT, int D, int S>
+__global__ __launch_bounds__(64 * wide_merge_waves(S)) void merge_segment_wide_kernel(DecodeArgs a)
+{
+    constexpr int NW = wide_merge_waves(S);
+    __shared__ float s_m[NW][S][kWave];
+    __shared__ float s_l[NW][S][kWave];
+    __shared__ f32x4 s_acc[NW][S][kWave];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int32_t b = blockIdx.x / a.num_kv_heads;
+    const int32_t g = blockIdx.x % a.num_kv_heads;
+    const int32_t n = a.seq_lens[b];
+    const bool valid = len_ok(a, n);
+    // b, g and n are the same for every wave, so all waves leave together
+    if (!valid || n == 0) {
+        if (wave == 0)
+            merge_fill<QT, D>(a, b, g, valid, lane);
+        return;
     }
-    merge_segment<QT, D>(a, b, g, w0, nparts, lane);
+    int64_t w0, nparts;
+    if (!segment_parts(a, lane, b, g, n, w0, nparts))
+        return;
+    MergeState<S> st;
+    merge_fold<D, S>(a, w0, wave * nparts / NW, (wave + 1) * nparts / NW, lane, st);
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        s_m[wave][s][lane] = st.M[s];
+        s_l[wave][s][lane] = st.nan_seen ? NAN : st.L[s];
+        s_acc[wave][s][lane] = st.acc[s];
+    }
+    __syncthreads();
+    if (wave != 0)
+        return;
+    MergeState<S> tot;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+            M = fmaxf(M, s_m[w][s][lane]);
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const float l = s_l[w][s][lane];
+            tot.nan_seen |= l != l;
+            const float wgt = __builtin_amdgcn_exp2f(s_m[w][s][lane] - M);
+            tot.L[s] = fmaf(l, wgt, tot.L[s]);
+            tot.acc[s] += s_acc[w][s][lane] * wgt;
+        }
+        tot.M[s] = M;
+    }
+    merge_store<QT, D, S>(a, b, g, tot, lane);
+}
+
+// Parts a segment is expected to have: in the balanced split W runs over
+// B * Hkv segments, each segment touching about W / (B * Hkv) + 1 of them;
+// with fixed partitions at most max_parts.
+__host__ __forceinline__ int64_t expected_parts(const DecodeArgs &a)
+{
+    const int64_t segs = (int64_t)a.num_seqs * a.num_kv_heads;
+    if (a.partition == kPartitionBalanced)
+        return (a.waves + segs - 1) / segs + 1;
+    return a.max_parts;
 }
 
 template <int QT, int D>
 hipError_t merge_launch(const DecodeArgs &a, hipStream_t s)
 {
-    if (merge_runs(a.group, D) != 0)
-        hipLaunchKernelGGL((merge_segment_kernel<QT, D>), dim3(a.num_seqs * a.num_kv_heads),
-                           dim3(64), 0, s, a);
-    else
+    const dim3 segs(a.num_seqs * a.num_kv_heads);
+    const int S = merge_runs(a.group, D);
+    // one wave folds 16 / S parts per batch of loads; beyond one batch a
+    // segment gets a workgroup of waves
+    if (S != 0 && expected_parts(a) > 16 / S) {
+        switch (S) {
+        case 1:
+            hipLaunchKernelGGL((merge_segment_wide_kernel<QT, D, 1>), segs,
+                               dim3(64 * wide_merge_waves(1)), 0, s, a);
+            break;
+        case 2:
+            hipLaunchKernelGGL((merge_segment_wide_kernel<QT, D, 2>), segs,
+                               dim3(64 * wide_merge_waves(2)), 0, s, a);
+            break;
+        case 4:
+            hipLaunchKernelGGL((merge_segment_wide_kernel<QT, D, 4>), segs,
+                               dim3(64 * wide_merge_waves(4)), 0, s, a);
+            break;
+        default:
+            hipLaunchKernelGGL((merge_segment_wide_kernel<QT, D, 8>), segs,
+                               dim3(64 * wide_merge_waves(8)), 0, s, a);
+            break;
+        }
+    } else if (S != 0) {
+        hipLaunchKernelGGL((merge_segment_kernel<QT, D>), segs, dim3(64), 0, s, a);
+    } else {
         hipLaunchKernelGGL((merge_kernel<QT, D>), dim3(a.num_seqs * a.num_q_heads), dim3(64), 0,
                            s, a);
+    }
     return hipGetLastError();
 }
 
