@@ -23,14 +23,18 @@
  *   - All arrays are dense, row-major, without padding.
  *
  * Cache layout (per layer, one K and one V tensor, both [num_blocks][Hkv]
- * pieces of one block of one KV head; bs = block_size, o = offset in block):
+ * pieces of one block of one KV head; bs = block_size, o = offset in block,
+ * b = bytes per element, p = 4 / b):
  *   k_cache[block][kv_head][o][dim]                   token-major K
- *   v_cache[block][kv_head][o / 16][dim][o % 16]      V as bs/16 dimension-
- *                                                      major tiles of 16 tokens
- * (at bs = 16: v_cache[block][kv_head][dim][o]).  The pages fix only that a
- * block holds a fixed number of consecutive tokens ([devto] §4); the orders
- * are this library's choice: every 16-token tile of any block size has the
- * layout the decode kernels consume, K rows and V columns contiguous.
+ *   v_cache[block][kv_head][o / 16][vt(o % 16, dim)]  V as bs/16 tiles of 16
+ *                                                      tokens x D dims, with
+ *   vt(u, d) = ((((d / 16p) * 4 + u / 4) * 16 + d % 16) * p + (d / 16) % p) * 4 + u % 4,
+ * so each 16-byte piece of a V tile holds p dims (16 apart) of 4 consecutive
+ * tokens, and a tile is read 1 KiB at a time with 16 bytes per lane.  head_dim
+ * is a multiple of 16p (64 and 128 are).  The pages fix only that a block
+ * holds a fixed number of consecutive tokens ([devto] §4); the orders are
+ * this library's choice: every 16-token tile of any block size has the
+ * layout the decode kernels consume.
  *
  * A token's slot is block * block_size + offset; token t of a sequence lives
  * in block block_tables[seq][t / block_size] at offset t % block_size
@@ -289,7 +293,7 @@ typedef struct {
 /* Writes the K and V of num_tokens new tokens into their cache slots
  * (s = slot_mapping[t], o = s % bs, in the layout above):
  *   k_cache[s / bs][g][o][d] = cvt(k[t][g][d])
- *   v_cache[s / bs][g][o / 16][d][o % 16] = cvt(v[t][g][d])
+ *   v_cache[s / bs][g][o / 16][vt(o % 16, d)] = cvt(v[t][g][d])
  * for every KV head g and dim d ([devto] §1: the new token's K and V are
  * appended to the cache; §4: a slot is a place in a physical block).
  * k, v: device [num_tokens][Hkv][D] in desc->q_dtype.  slot_mapping: device

@@ -121,8 +121,10 @@ def cache_append(k_new, v_new, k_cache, v_cache, slot_mapping, *, num_kv_heads, 
                  block_size, num_blocks, kv_dtype, in_dtype, k_scale=1.0, v_scale=1.0):
     """Writes the new tokens into k_cache / v_cache (numpy storage arrays) in place.
 
-    K cache is [blocks][Hkv][bs][D]; V cache [blocks][Hkv][bs/16][D][16]
-    (16-token dimension-major tiles; bs a multiple of 16); k_new / v_new are
+    K cache is [blocks][Hkv][bs][D]; V cache [blocks][Hkv][bs/16][16 D]: tiles
+    of 16 tokens (bs a multiple of 16) in which, with p = 4 / element bytes,
+    each 16-byte piece holds p dims (16 apart) of 4 consecutive tokens, D a
+    multiple of 16 p (the element index is in pa_oracle.c); k_new / v_new are
     [T][Hkv][D]."""
     _check_storage(k_new, in_dtype)
     _check_storage(v_new, in_dtype)

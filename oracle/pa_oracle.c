@@ -20,10 +20,13 @@
  *   - Query head h reads KV head h / (Hq/Hkv) (consecutive grouping of GQA,
  *     [devto] §2 "Example 2").
  *   - Within one physical block and KV head, K is stored token-major
- *     ([bs][D]) and V as bs/16 dimension-major tiles of 16 consecutive
- *     tokens each ([bs/16][D][16]; one [D][16] tile when bs = 16); bs is a
- *     multiple of 16.  The pages fix only that a block holds a fixed number
- *     of consecutive tokens ([devto] §4).
+ *     ([bs][D]) and V as bs/16 tiles of 16 consecutive tokens each; bs is a
+ *     multiple of 16.  Inside a V tile, with p = 4 / (bytes per element),
+ *     the value of token u and dim d is element
+ *         ((((d / 16p) * 4 + u / 4) * 16 + d % 16) * p + (d / 16) % p) * 4 + u % 4,
+ *     so each 16-byte piece holds p dims (16 apart) of 4 consecutive tokens,
+ *     and D is a multiple of 16p.  The pages fix only that a block holds a
+ *     fixed number of consecutive tokens ([devto] §4).
  *   - The decoded token attends to every cached token including the one just
  *     appended ([devto] §1: append, then attend over the stored history).
  *   - FP8 is OCP E4M3FN (bias 7, max 448, no infinities); the pages only say
@@ -217,10 +220,16 @@ static size_t k_index(const orc_cache_desc *c, int64_t blk, int g, int o, int d)
     return (((size_t)blk * c->num_kv_heads + g) * c->block_size + o) * c->head_dim + d;
 }
 
+/* V: tile o / 16 of (blk, g); inside it, token u = o % 16 and dim d sit in
+ * 16-byte piece (d / 16p) * 64 + (u / 4) * 16 + d % 16, which holds p dims
+ * of 4 tokens, at place ((d / 16) % p) * 4 + u % 4; p = 4 / element bytes. */
 static size_t v_index(const orc_cache_desc *c, int64_t blk, int g, int o, int d)
 {
     const size_t tile = ((size_t)blk * c->num_kv_heads + g) * (c->block_size / 16) + o / 16;
-    return (tile * c->head_dim + d) * 16 + o % 16;
+    const int p = 4 / orc_elem_bytes(c->kv_dtype);
+    const int u = o % 16;
+    const size_t piece = (size_t)(d / (16 * p)) * 64 + (size_t)(u / 4) * 16 + d % 16;
+    return tile * 16 * c->head_dim + piece * 4 * p + (size_t)((d / 16) % p) * 4 + u % 4;
 }
 
 /* Store one value of the new token into the cache slot. */
@@ -276,15 +285,16 @@ static void *append_worker(void *arg)
  * block * block_size + offset, or negative to skip the token.  Tokens are
  * independent (their slots are distinct), so ranges of them are written by
  * separate threads.  Returns 0, or -1 if a slot lies outside the pool, the
- * dtype pair is not one the path defines or block_size is not a positive
- * multiple of 16. */
+ * dtype pair is not one the path defines, block_size is not a positive
+ * multiple of 16 or head_dim not one of 16 p (p = 4 / element bytes). */
 int orc_cache_append(const orc_cache_desc *c, const void *k_new, const void *v_new,
                      void *k_cache, void *v_cache, const int32_t *slot_mapping,
                      int32_t num_tokens, float k_scale, float v_scale)
 {
     if (!(c->kv_dtype == c->in_dtype ||
           (c->kv_dtype == ORC_E4M3 && (c->in_dtype == ORC_BF16 || c->in_dtype == ORC_F16))) ||
-        c->block_size <= 0 || c->block_size % 16 != 0)
+        c->block_size <= 0 || c->block_size % 16 != 0 || c->head_dim <= 0 ||
+        c->head_dim % (64 / orc_elem_bytes(c->kv_dtype)) != 0)
         return -1;
     for (int32_t t = 0; t < num_tokens; ++t)
         if (slot_mapping[t] >= (int64_t)c->num_blocks * c->block_size)
@@ -462,7 +472,8 @@ int orc_decode(const orc_decode_desc *d, const void *q, const void *k_cache,
                int64_t num_rows, double *out, int nthreads)
 {
     if (d->num_kv_heads <= 0 || d->num_q_heads % d->num_kv_heads != 0 || d->head_dim <= 0 ||
-        d->block_size <= 0 || d->block_size % 16 != 0)
+        d->block_size <= 0 || d->block_size % 16 != 0 ||
+        d->head_dim % (64 / orc_elem_bytes(d->kv_dtype)) != 0)
         return -3;
     decode_job J;
     J.d = d;

@@ -10,9 +10,9 @@
 //
 // Lane d writes dims d, d + 64, ...  The K row of a slot is contiguous
 // ([block][head][token][dim]); V is stored per block and head as 16-token
-// dimension-major tiles ([block][head][token / 16][dim][token % 16]), so the
-// V column of a slot is strided by 16.  FP8: the E4M3 code of x * inv
-// (inv = 1/scale in fp32), nearest even, saturating.
+// tiles ([block][head][token / 16][16 D], element order v_tile_index), so
+// the V column of a slot is scattered over the tile.  FP8: the E4M3 code of
+// x * inv (inv = 1/scale in fp32), nearest even, saturating.
 #pragma once
 
 #include "device.hpp"
@@ -30,16 +30,18 @@ __device__ __forceinline__ void store_token(const typename Store<QT>::T *ks,
     // first tile of (blk, g); `off` (0 .. block_size - 1) is in tile off / 16
     const size_t tile0 = ((size_t)blk * num_kv_heads + g) << tile_shift;
     TK *kd = static_cast<TK *>(k_cache) + (tile0 * kTile + off) * D;
-    TK *vd = static_cast<TK *>(v_cache) + (tile0 + off / kTile) * D * kTile + off % kTile;
+    TK *vd = static_cast<TK *>(v_cache) + (tile0 + off / kTile) * D * kTile;
+    const int u = off % kTile;
 #pragma unroll
     for (int i = 0; i < D / kWave; ++i) {
         const int d = i * kWave + lane;
+        const int vi = v_tile_index<Store<KT>::bytes>(u, d);
         if constexpr (KT == PA_FP8_E4M3) {
             kd[d] = f32_to_e4m3(to_f32<QT>(ks[d]) * k_inv);
-            vd[(size_t)d * kTile] = f32_to_e4m3(to_f32<QT>(vs[d]) * v_inv);
+            vd[vi] = f32_to_e4m3(to_f32<QT>(vs[d]) * v_inv);
         } else {
             kd[d] = ks[d];
-            vd[(size_t)d * kTile] = vs[d];
+            vd[vi] = vs[d];
         }
     }
 }

@@ -19,9 +19,10 @@
 // FP8 tiles are widened to the q type with the hardware converter (exact:
 // every E4M3 value is a bf16 and an fp16 value).
 //
-// The next tile's K/V loads are issued before the current tile's math, and
-// the block-table entries are read with scalar loads two tiles ahead, so a
-// wave keeps two tiles of HBM reads in flight.
+// A wave keeps a ring of DEPTH tiles (2 at 16-bit KV, 4 at FP8): the loads of
+// the next DEPTH - 1 tiles are in flight while the current tile's math runs,
+// and each block-table entry is read with a scalar load one tile before the
+// loads that use it.
 //
 // Work split (DecodeArgs::partition):
 //   0   one wave per (sequence, KV head), output written directly;
@@ -109,7 +110,6 @@ struct MfmaWave {
     static constexpr int CH_PER_LANE = CHUNKS / 4;      // chunks per lane per tile
     static constexpr int QK_MMAS = D / 32;
     static constexpr int PV_TILES = D / 16;
-    static constexpr int V_ROW_BYTES = kTile * KE; // one V^T row (16 tokens)
     static constexpr int TILE_BYTES = kTile * D * KE;
     // Tiles in flight per wave: an FP8 tile is half the bytes of a 16-bit
     // one, so twice as many keep the same bytes in flight.
@@ -238,21 +238,29 @@ struct MfmaWave {
 
     // K: token `col`, chunks grp, grp+4, ... (64 contiguous bytes of every row
     // per load instruction).  V^T: dims 16t + col, tokens 4*grp .. 4*grp+3
-    // (512 contiguous bytes per load instruction).
+    // (1 KiB contiguous per load instruction, see v_tile_index).
     __device__ static void load_tile(const char *kt, const char *vt, int col, int grp, Tile &T)
     {
 #pragma unroll
         for (int j = 0; j < CH_PER_LANE; ++j)
             T.k[j] = load16_stream(kt + col * ROW_BYTES + (grp + 4 * j) * 16);
+        // lane L = col + 16 grp takes 16-byte piece 64 q + L of the V tile:
+        // V^T rows 16 t + col, tokens 4 grp .. 4 grp + 3, for the 16 / (4 KE)
+        // values of t that piece holds (v_tile_index)
+        const int L = col + 16 * grp;
 #pragma unroll
-        for (int t = 0; t < PV_TILES; ++t) {
-            const char *p = vt + (16 * t + col) * V_ROW_BYTES + grp * 4 * KE;
+        for (int q = 0; q < PV_TILES * 4 * KE / 16; ++q) {
+            const u32x4 x = load16_stream(vt + q * 1024 + 16 * L);
             if constexpr (KE == 2) {
-                const u32x2 x = load8_stream(p);
-                T.v[t][0] = x.x;
-                T.v[t][1] = x.y;
+                T.v[2 * q][0] = x.x;
+                T.v[2 * q][1] = x.y;
+                T.v[2 * q + 1][0] = x.z;
+                T.v[2 * q + 1][1] = x.w;
             } else {
-                T.v[t][0] = load4_stream(p);
+                T.v[4 * q][0] = x.x;
+                T.v[4 * q + 1][0] = x.y;
+                T.v[4 * q + 2][0] = x.z;
+                T.v[4 * q + 3][0] = x.w;
             }
         }
     }

@@ -14,10 +14,10 @@
 //     chunks c, c+4, c+8, ... of its token's row, so each load instruction
 //     covers 64 contiguous bytes of every row.  Partial dot products are
 //     summed over the quad.
-//   V tile [D][16]: the tile is read as one contiguous run, 16 bytes per lane
-//     per instruction; a lane holds 16/bytes consecutive tokens of one
-//     dimension row and accumulates them, partial sums are combined over the
-//     lanes of a row at the end.
+//   V tile (element order v_tile_index): read 1 KiB per instruction, 16
+//     bytes per lane; lane L holds dims 16 j + L % 16 of tokens
+//     4 (L / 16) .. 4 (L / 16) + 3 and accumulates them; the four lanes of a
+//     dim (L % 16 equal) are combined at the end.
 //   The probabilities move from the K layout to the V layout through LDS.
 #include "device.hpp"
 #include "work.hpp"
@@ -32,14 +32,12 @@ struct ValuShape {
     static constexpr int CHUNKS = ROW_BYTES / 16;     // 16-byte chunks in a K row
     static constexpr int CH_PER_LANE = CHUNKS / 4;
     static constexpr int EPC = 16 / KE;               // elements per chunk
-    static constexpr int V_ROW_BYTES = kTile * KE; // one V^T row (16 tokens)
-    static constexpr int V_LPR = V_ROW_BYTES / 16;    // lanes per V^T row
-    static constexpr int V_TPL = kTile / V_LPR;  // tokens per lane
-    static constexpr int V_RPI = kWave / V_LPR;       // rows per load instruction
-    static constexpr int V_INSTR = D / V_RPI;
+    static constexpr int VP = 4 / KE;                 // dims per 16-byte V piece
+    static constexpr int V_INSTR = D / (16 * VP);     // 1 KiB V loads per tile
+    static constexpr int VD = D / 16;                 // dims per lane
     static constexpr int TILE_BYTES = kTile * D * KE;
     static_assert(CH_PER_LANE >= 1 && CHUNKS % 4 == 0, "K row too short for quad layout");
-    static_assert(V_INSTR >= 1 && D % V_RPI == 0, "V tile layout");
+    static_assert(V_INSTR >= 1 && D % (16 * VP) == 0, "V tile layout");
 };
 
 template <int QT, int KT, int D, int G>
@@ -62,8 +60,8 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a, int32_t 
 
     const int tq = lane >> 2;    // token of this lane in the K layout
     const int cq = lane & 3;     // quad lane
-    const int vrow = lane / S::V_LPR;
-    const int vtok0 = (lane % S::V_LPR) * S::V_TPL;
+    const int vdim = lane & 15;        // V: dims 16 j + vdim
+    const int vtok0 = 4 * (lane >> 4); // of tokens vtok0 .. vtok0 + 3
 
     // q of the G heads, the slice matching this lane's K chunks, in fp32.
     float qv[G][S::CH_PER_LANE][S::EPC];
@@ -79,14 +77,14 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a, int32_t 
                     qv[h][j][e] = to_f32<QT>(qp[h * D + (cq + 4 * j) * S::EPC + e]) * a.score_scale;
     }
 
-    float m[G], l[G], acc[G][S::V_INSTR];
+    float m[G], l[G], acc[G][S::VD];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         m[h] = kMaxStart;
         l[h] = 0.f;
 #pragma unroll
-        for (int i = 0; i < S::V_INSTR; ++i)
-            acc[h][i] = 0.f;
+        for (int j = 0; j < S::VD; ++j)
+            acc[h][j] = 0.f;
     }
 
     // window start: tokens before it are left out (n = 0 rows are not read)
@@ -119,12 +117,19 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a, int32_t 
             const u32x4 c = load16_stream(kbase + tile + tq * S::ROW_BYTES + (cq + 4 * j) * 16);
             Chunk<KT>::unpack(c, kv[j]);
         }
-        // V tile: this lane's rows.
-        float vv[S::V_INSTR][S::V_TPL];
+        // V tile: piece 64 i + lane holds dims 16 (VP i + e) + vdim of this
+        // lane's 4 tokens, at places 4 e .. 4 e + 3
+        float vv[S::VD][4];
 #pragma unroll
         for (int i = 0; i < S::V_INSTR; ++i) {
             const u32x4 c = load16_stream(vbase + tile + i * 1024 + lane * 16);
-            Chunk<KT>::unpack(c, vv[i]);
+            float e[4 * S::VP];
+            Chunk<KT>::unpack(c, e);
+#pragma unroll
+            for (int x = 0; x < S::VP; ++x)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    vv[S::VP * i + x][r] = e[4 * x + r];
         }
 
         // scores of token tq for the G heads (log2 units)
@@ -157,8 +162,8 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a, int32_t 
             pr[h] = __builtin_amdgcn_exp2f(s[h] - mn);
             l[h] = fmaf(l[h], alpha, pr[h]);
 #pragma unroll
-            for (int i = 0; i < S::V_INSTR; ++i)
-                acc[h][i] *= alpha;
+            for (int j = 0; j < S::VD; ++j)
+                acc[h][j] *= alpha;
         }
         // K layout -> V layout for the probabilities
 #pragma unroll
@@ -167,31 +172,32 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a, int32_t 
         wave_lds_sync();
         if (tail) {
 #pragma unroll
-            for (int i = 0; i < S::V_INSTR; ++i)
+            for (int j = 0; j < S::VD; ++j)
 #pragma unroll
-                for (int e = 0; e < S::V_TPL; ++e)
-                    if (tok_base + vtok0 + e >= it.t1 || tok_base + vtok0 + e < w0)
-                        vv[i][e] = 0.f; // slots outside the range may hold anything
+                for (int r = 0; r < 4; ++r)
+                    if (tok_base + vtok0 + r >= it.t1 || tok_base + vtok0 + r < w0)
+                        vv[j][r] = 0.f; // slots outside the range may hold anything
         }
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            float pv[S::V_TPL];
+            float pv[4];
 #pragma unroll
-            for (int e = 0; e < S::V_TPL; ++e)
-                pv[e] = p_lds[wid][h][vtok0 + e];
+            for (int r = 0; r < 4; ++r)
+                pv[r] = p_lds[wid][h][vtok0 + r];
 #pragma unroll
-            for (int i = 0; i < S::V_INSTR; ++i) {
-                float t = acc[h][i];
+            for (int j = 0; j < S::VD; ++j) {
+                float t = acc[h][j];
 #pragma unroll
-                for (int e = 0; e < S::V_TPL; ++e)
-                    t = fmaf(pv[e], vv[i][e], t);
-                acc[h][i] = t;
+                for (int r = 0; r < 4; ++r)
+                    t = fmaf(pv[r], vv[j][r], t);
+                acc[h][j] = t;
             }
         }
         wave_lds_sync();
     }
 
-    // combine lane partials: l over the 16 token quads, acc over a row's lanes
+    // combine lane partials: l over the 16 token quads, acc over the four
+    // lanes of a dim
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         l[h] += shfl_xor(l[h], 4);
@@ -199,14 +205,13 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a, int32_t 
         l[h] += shfl_xor(l[h], 16);
         l[h] += shfl_xor(l[h], 32);
 #pragma unroll
-        for (int i = 0; i < S::V_INSTR; ++i) {
-#pragma unroll
-            for (int x = 1; x < S::V_LPR; x <<= 1)
-                acc[h][i] += shfl_xor(acc[h][i], x);
+        for (int j = 0; j < S::VD; ++j) {
+            acc[h][j] += shfl_xor(acc[h][j], 16);
+            acc[h][j] += shfl_xor(acc[h][j], 32);
         }
     }
 
-    const bool writer = (lane % S::V_LPR) == 0;
+    const bool writer = lane < 16;
     if (a.partition == 0) {
         TQ *o = static_cast<TQ *>(a.out) + ((size_t)it.b * a.num_q_heads + (size_t)it.g * G) * D;
 #pragma unroll
@@ -214,10 +219,10 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a, int32_t 
             // l = 0: no token in the range (n = 0 or an empty window)
             const float inv = (l[h] == 0.f) ? 0.f : a.v_scale / l[h];
 #pragma unroll
-            for (int i = 0; i < S::V_INSTR; ++i) {
-                float r = bad ? NAN : acc[h][i] * inv;
+            for (int j = 0; j < S::VD; ++j) {
+                float r = bad ? NAN : acc[h][j] * inv;
                 if (writer)
-                    o[h * D + i * S::V_RPI + vrow] = from_f32<QT>(r);
+                    o[h * D + 16 * j + vdim] = from_f32<QT>(r);
             }
         }
     } else {
@@ -230,9 +235,9 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a, int32_t 
             }
             float *accp = ws_acc(a, w, h, D);
 #pragma unroll
-            for (int i = 0; i < S::V_INSTR; ++i)
+            for (int j = 0; j < S::VD; ++j)
                 if (writer)
-                    accp[i * S::V_RPI + vrow] = bad ? NAN : acc[h][i] * a.v_scale;
+                    accp[16 * j + vdim] = bad ? NAN : acc[h][j] * a.v_scale;
         }
     }
 }

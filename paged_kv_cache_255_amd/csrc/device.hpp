@@ -16,6 +16,22 @@ constexpr int kWave = 64;     // CDNA wavefront width
 constexpr int kTile = 16;
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Element of token u (0..15) and dim d inside one V tile (16 tokens x D dims,
+// KE bytes per element), p = 4 / KE: each 16-byte piece holds p dims, 16
+// apart, of 4 consecutive tokens.  Piece (d / 16p) * 64 + (u / 4) * 16 + d % 16
+// holds the value at place ((d / 16) % p) * 4 + u % 4.  So one load
+// instruction reads 1 KiB of the tile with lane L taking piece 64 q + L, and
+// lane (col, grp) = (L % 16, L / 16) gets dims 16 (p q + i) + col (i < p) of
+// tokens 4 grp .. 4 grp + 3: the V^T operand of the 16x16x16 MFMA, p
+// products' worth per 16 bytes.  D is a multiple of 16 p.
+template <int KE>
+__host__ __device__ constexpr int v_tile_index(int u, int d)
+{
+    constexpr int p = 4 / KE;
+    const int piece = (d / (16 * p)) * 64 + (u / 4) * 16 + d % 16;
+    return piece * 4 * p + ((d / 16) % p) * 4 + u % 4;
+}
+
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -196,16 +212,6 @@ __device__ __forceinline__ u32x4 load16(const void *p)
 __device__ __forceinline__ u32x4 load16_stream(const void *p)
 {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-}
-
-__device__ __forceinline__ u32x2 load8_stream(const void *p)
-{
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
-}
-
-__device__ __forceinline__ uint32_t load4_stream(const void *p)
-{
-    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p));
 }
 
 } // namespace pa

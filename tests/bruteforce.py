@@ -10,6 +10,8 @@ VRAM...", §1 attention formula; §4 block table).
 import numpy as np
 import torch
 
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "e4m3": 1}
+
 
 def decode_storage(a, dtype):
     """Stored values -> float64, via library conversions."""
@@ -34,11 +36,27 @@ def gather(cache_vals, table, n, bs):
     return np.concatenate(parts, axis=0)[:n]
 
 
-def v_token_major(v_vals, num_kv_heads, head_dim, bs):
-    """The V cache, stored per block and KV head as bs/16 dimension-major
-    tiles of 16 tokens ([bs/16][D][16]), as [blocks][Hkv][bs][D]."""
-    t = v_vals.reshape(-1, num_kv_heads, bs // 16, head_dim, 16)
-    return t.transpose(0, 1, 2, 4, 3).reshape(-1, num_kv_heads, bs, head_dim)
+def v_token_major(v_vals, num_kv_heads, head_dim, bs, elem_bytes):
+    """The V cache as [blocks][Hkv][bs][D].  It is stored per block and KV
+    head as bs/16 tiles of 16 tokens, each tile a run of 16-byte pieces: with
+    p = 4 / elem_bytes, piece (q, a, c) (q < D/16p, a < 4, c < 16) holds the
+    p x 4 values (i, r) of dim 16 (p q + i) + c and token 4 a + r.  Works on
+    any array (storage codes or decoded values)."""
+    p = 4 // elem_bytes
+    t = np.asarray(v_vals).reshape(-1, num_kv_heads, bs // 16, head_dim // (16 * p), 4, 16, p, 4)
+    # axes: block, head, tile, q, a, c, i, r -> block, head, (tile, a, r), (q, i, c)
+    t = t.transpose(0, 1, 2, 4, 7, 3, 6, 5)
+    return t.reshape(-1, num_kv_heads, bs, head_dim)
+
+
+def v_from_token_major(v_tok, elem_bytes):
+    """Inverse of v_token_major: [blocks][Hkv][bs][D] -> V storage order
+    [blocks][Hkv][bs/16][16 D]."""
+    NB, H, bs, D = v_tok.shape
+    p = 4 // elem_bytes
+    t = np.asarray(v_tok).reshape(NB, H, bs // 16, 4, 4, D // (16 * p), p, 16)
+    # axes: block, head, tile, a, r, q, i, c -> block, head, tile, q, a, c, i, r
+    return np.ascontiguousarray(t.transpose(0, 1, 2, 5, 3, 7, 6, 4)).reshape(NB, H, bs // 16, 16 * D)
 
 
 def attention(q, k_cache, v_cache, tables, lens, *, num_q_heads, num_kv_heads, head_dim,
@@ -49,7 +67,8 @@ def attention(q, k_cache, v_cache, tables, lens, *, num_q_heads, num_kv_heads, h
     G = num_q_heads // num_kv_heads
     qv = decode_storage(q, q_dtype).reshape(B, num_q_heads, head_dim)
     kv = decode_storage(k_cache, kv_dtype).reshape(-1, num_kv_heads, block_size, head_dim)
-    vv = v_token_major(decode_storage(v_cache, kv_dtype), num_kv_heads, head_dim, block_size)
+    vv = v_token_major(decode_storage(v_cache, kv_dtype), num_kv_heads, head_dim, block_size,
+                       ELEM_BYTES[kv_dtype])
     out = np.zeros((B, num_q_heads, head_dim))
     for b in range(B):
         n = int(lens[b])

@@ -3,8 +3,8 @@
 Builds storage arrays, block tables (random injective placement of each
 sequence's blocks in the pool) and lengths from a numpy seed.  It contains
 no attention arithmetic.  Cache shapes: K [blocks][Hkv][bs][D]; V
-[blocks][Hkv][D][16] for bs = 16, else [blocks][Hkv][bs/16][D][16] (16-token
-dimension-major tiles).
+[blocks][Hkv][bs/16][16 D] (16-token tiles; the order inside a tile is
+undone by bruteforce.v_token_major).
 """
 import numpy as np
 import torch
@@ -29,7 +29,7 @@ def random_storage(rng, shape, dtype, scale=1.0):
 
 
 def v_shape(NB, Hkv, D, bs):
-    return (NB, Hkv, D, 16) if bs == 16 else (NB, Hkv, bs // 16, D, 16)
+    return (NB, Hkv, bs // 16, 16 * D)
 
 
 def random_case(seed, *, B=3, Hq=4, Hkv=2, D=32, q_dtype="f32", kv_dtype="f32",

@@ -13,6 +13,7 @@ import torch
 import oracle
 import paged_kv_cache_255_amd as pa
 import workloads
+from tests import bruteforce
 from tests.scenario import (GpuStep, Inputs, OracleStep, check_close, compare_cache_blocks,
                             to_f64)
 
@@ -118,11 +119,11 @@ def test_fp8_value_decode_all_codes(kernel):
     say(f"[case] fp8 all codes kernel={kernel}")
     D, NB = 128, 4
     k = torch.zeros(NB * 16 * D, dtype=torch.uint8, device="cuda")
-    v = torch.zeros(NB * D * 16, dtype=torch.uint8, device="cuda")
-    vv = v.view(NB, 1, D, 16)
-    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
-    vv[2, 0, :, 0] = codes[:128].cuda()
-    vv[1, 0, :, 0] = codes[128:].cuda()
+    codes = np.arange(256, dtype=np.uint8)
+    v_tok = np.zeros((NB, 1, 16, D), np.uint8)  # [block][head][token][dim]
+    v_tok[2, 0, 0, :] = codes[:128]
+    v_tok[1, 0, 0, :] = codes[128:]
+    v = torch.from_numpy(bruteforce.v_from_token_major(v_tok, 1).reshape(-1)).cuda()
     tables = torch.tensor([[2], [1]], dtype=torch.int32, device="cuda")
     lens = torch.tensor([1, 1], dtype=torch.int32, device="cuda")
     q = torch.randn(2, 1, D, device="cuda").to(torch.bfloat16)

@@ -16,10 +16,13 @@ SRC = os.path.join(ROOT, "oracle", "pa_oracle.c")
 
 MUTANTS = {
     "gqa_head_mapping": ("int g = h / G;", "int g = h % d->num_kv_heads;"),
-    "k_tile_transposed": ("* c->block_size + o) * c->head_dim + d;\n}\n\nstatic size_t v_index",
-                          "* c->head_dim + d) * c->block_size + o;\n}\n\nstatic size_t v_index"),
-    "v_tile_token_major": ("return (tile * c->head_dim + d) * 16 + o % 16;",
-                           "return (tile * 16 + o % 16) * c->head_dim + d;"),
+    "k_tile_transposed": ("* c->block_size + o) * c->head_dim + d;",
+                          "* c->head_dim + d) * c->block_size + o;"),
+    "v_tile_token_major": ("return tile * 16 * c->head_dim + piece * 4 * p + (size_t)((d / 16) % p) * 4 + u % 4;",
+                           "return (tile * 16 + u) * c->head_dim + d;"),
+    "v_piece_lane_order": ("(size_t)(u / 4) * 16 + d % 16;", "(size_t)(d % 16) * 4 + u / 4;"),
+    "v_piece_dims_adjacent": ("+ (size_t)((d / 16) % p) * 4 + u % 4;",
+                              "+ (size_t)(u % 4) * p + (d / 16) % p;"),
     # the same at 16-token blocks: only the larger-block pins can catch it
     "v_subtile_order": ("* (c->block_size / 16) + o / 16;",
                         "* (c->block_size / 16) + (o / 16 + 1) % (c->block_size / 16);"),

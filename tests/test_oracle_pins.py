@@ -47,7 +47,7 @@ def run_brute(c, **over):
     ("bf16", "bf16", 8, 2, 128),
     ("f16", "f16", 3, 3, 64),
     ("bf16", "e4m3", 8, 1, 64),
-    ("f16", "e4m3", 4, 2, 32),
+    ("f16", "e4m3", 4, 2, 64),
 ])
 def test_oracle_matches_bruteforce(q_dtype, kv_dtype, Hq, Hkv, D):
     for seed in range(3):
@@ -65,12 +65,12 @@ def test_oracle_matches_torch_sdpa():
     o = run_oracle(c)
     G = c["Hq"] // c["Hkv"]
     kv = torch.from_numpy(c["k"]).double()
-    vv = torch.from_numpy(c["v"]).double()
+    vv = torch.from_numpy(bruteforce.v_token_major(c["v"], c["Hkv"], c["D"], BS, 4)).double()
     for b, n in enumerate(c["lens"]):
         n = int(n)
         blocks = c["tables"][b][: -(-n // BS)]
         K = torch.cat([kv[p].permute(1, 0, 2) for p in blocks])[:n]  # [n][Hkv][D]
-        V = torch.cat([vv[p].permute(2, 0, 1) for p in blocks])[:n]
+        V = torch.cat([vv[p].permute(1, 0, 2) for p in blocks])[:n]
         K = K.permute(1, 0, 2).repeat_interleave(G, dim=0)  # [Hq][n][D]
         V = V.permute(1, 0, 2).repeat_interleave(G, dim=0)
         q = torch.from_numpy(c["q"][b]).double()[:, None, :]  # [Hq][1][D]
@@ -80,12 +80,12 @@ def test_oracle_matches_torch_sdpa():
 
 def test_single_token_returns_its_value_row():
     """n = 1: the softmax has one weight, 1, so out = v_scale * V_0 exactly."""
-    c = random_case(3, B=2, Hq=4, Hkv=2, D=32, lens=[1, 1], q_dtype="bf16", kv_dtype="e4m3")
+    c = random_case(3, B=2, Hq=4, Hkv=2, D=64, lens=[1, 1], q_dtype="bf16", kv_dtype="e4m3")
     o = run_oracle(c, k_scale=0.5, v_scale=0.25)
-    vv = bruteforce.decode_storage(c["v"], "e4m3").reshape(c["NB"], 2, 32, BS)
+    vv = bruteforce.v_token_major(bruteforce.decode_storage(c["v"], "e4m3"), 2, 64, BS, 1)
     for b in range(2):
         for h in range(4):
-            np.testing.assert_array_equal(o[b, h], vv[c["tables"][b][0], h // 2, :, 0] * 0.25)
+            np.testing.assert_array_equal(o[b, h], vv[c["tables"][b][0], h // 2, 0, :] * 0.25)
 
 
 def test_zero_query_gives_mean_of_values():
@@ -93,9 +93,9 @@ def test_zero_query_gives_mean_of_values():
     c = random_case(4, B=2, Hq=2, Hkv=2, D=16, lens=[37, 5])
     c["q"][:] = 0.0
     o = run_oracle(c)
-    vv = c["v"].astype(np.float64)
+    vv = bruteforce.v_token_major(c["v"].astype(np.float64), 2, 16, BS, 4)
     for b, n in enumerate(c["lens"]):
-        rows = [vv[c["tables"][b][t // BS], :, :, t % BS] for t in range(n)]
+        rows = [vv[c["tables"][b][t // BS], :, t % BS, :] for t in range(n)]
         np.testing.assert_allclose(o[b], np.mean(rows, axis=0), rtol=1e-13, atol=1e-14)
 
 
@@ -103,17 +103,17 @@ def test_constant_values_and_constant_keys():
     """All V rows equal c => out = c.  All K rows equal => uniform weights."""
     c = random_case(5, B=2, Hq=4, Hkv=1, D=16, lens=[40, 17])
     cvec = np.linspace(-1, 1, 16).astype(np.float32)
-    v_const = np.empty_like(c["v"])
-    v_const[:] = cvec[None, None, :, None]
+    v_const = bruteforce.v_from_token_major(
+        np.broadcast_to(cvec, (c["NB"], 1, BS, 16)).astype(np.float32), 4)
     o = run_oracle(dict(c, v=v_const))
     for b in range(2):
         np.testing.assert_allclose(o[b], np.broadcast_to(cvec, (4, 16)), rtol=1e-13, atol=1e-14)
     k_const = np.empty_like(c["k"])
     k_const[:] = 0.3
     o = run_oracle(dict(c, k=k_const))
-    vv = c["v"].astype(np.float64)
+    vv = bruteforce.v_token_major(c["v"].astype(np.float64), 1, 16, BS, 4)
     for b, n in enumerate(c["lens"]):
-        mean = np.mean([vv[c["tables"][b][t // BS], 0, :, t % BS] for t in range(n)], axis=0)
+        mean = np.mean([vv[c["tables"][b][t // BS], 0, t % BS, :] for t in range(n)], axis=0)
         np.testing.assert_allclose(o[b], np.broadcast_to(mean, (4, 16)), rtol=1e-12, atol=1e-13)
 
 
@@ -181,17 +181,18 @@ def test_page_addressing_example():
     ex = _golden("devto_block_table_example.json")
     table = [e["physical"] for e in ex["logical_blocks"]]
     assert ex["block_size"] == BS
-    NB, Hkv, D, n = 904, 1, 8, 48
+    NB, Hkv, D, n = 904, 1, 16, 48
     rng = np.random.default_rng(5)
     Kc = rng.standard_normal((n, D)).astype(np.float32)
     Vc = rng.standard_normal((n, D)).astype(np.float32)
     q = rng.standard_normal((1, 1, D)).astype(np.float32)
     k = np.full((NB, Hkv, BS, D), np.nan, dtype=np.float32)
-    v = np.full((NB, Hkv, D, BS), np.nan, dtype=np.float32)
+    v_tok = np.full((NB, Hkv, BS, D), np.nan, dtype=np.float32)
     for e in ex["logical_blocks"]:
         for t in range(e["first_token"], e["last_token"] + 1):
             k[e["physical"], 0, t - e["first_token"], :] = Kc[t]
-            v[e["physical"], 0, :, t - e["first_token"]] = Vc[t]
+            v_tok[e["physical"], 0, t - e["first_token"], :] = Vc[t]
+    v = bruteforce.v_from_token_major(v_tok, 4)
     o = oracle.decode(q, k, v, np.array([table]), [n], num_q_heads=1, num_kv_heads=1,
                       head_dim=D, block_size=BS, num_blocks=NB, q_dtype="f32",
                       kv_dtype="f32", scale=0.5)
@@ -281,10 +282,10 @@ def test_f16_and_bf16_decoders_against_library():
 @pytest.mark.parametrize("bs", [16, 64])
 def test_append_writes_exact_slots_only(kv_dtype, in_dtype, bs):
     """Each token lands in its slot and nowhere else.  The V column of offset
-    o is read back as v[blk, :, :, o] (bs = 16) or v[blk, :, o // 16, :, o % 16]
-    (16-token dimension-major tiles)."""
+    o is found through bruteforce.v_token_major applied to the storage
+    positions."""
     rng = np.random.default_rng(21)
-    NB, Hkv, D = 12, 3, 16
+    NB, Hkv, D = 12, 3, 64
     slots = np.array([5, bs * 11 + bs - 1, -1, 33, bs * 4, 2, 100, bs * 7 + bs // 2 + 13],
                      dtype=np.int32)
     T = len(slots)
@@ -293,8 +294,10 @@ def test_append_writes_exact_slots_only(kv_dtype, in_dtype, bs):
     k = np.full((NB, Hkv, bs, D), sentinel)
     v = np.full(v_shape(NB, Hkv, D, bs), sentinel)
 
+    vpos = bruteforce.v_token_major(np.arange(v.size).reshape(v.shape), Hkv, D, bs, eb)
+
     def vcol(a, blk, off):
-        return a[blk, :, :, off] if bs == 16 else a[blk, :, off // 16, :, off % 16]
+        return a.reshape(-1)[vpos[blk, :, off, :]]
 
     k_new = random_storage(rng, (T, Hkv, D), in_dtype)
     v_new = random_storage(rng, (T, Hkv, D), in_dtype)
@@ -311,7 +314,7 @@ def test_append_writes_exact_slots_only(kv_dtype, in_dtype, bs):
             continue
         blk, off = divmod(int(s), bs)
         written_k[blk, :, off, :] = True
-        vcol(written_v, blk, off)[...] = True
+        written_v.reshape(-1)[vpos[blk, :, off, :]] = True
         if kv_dtype == in_dtype:
             np.testing.assert_array_equal(k[blk, :, off, :], k_new[t])
             np.testing.assert_array_equal(vcol(v, blk, off), v_new[t])
@@ -413,7 +416,7 @@ def test_window_matches_bruteforce(bs, q_dtype, kv_dtype):
     whole blocks cut, one token left, nothing left): the oracle against the
     brute force, which slices the gathered rows."""
     for seed in range(3):
-        c = random_case(300 + seed, bs=bs, B=6, Hq=4, Hkv=2, D=32, q_dtype=q_dtype,
+        c = random_case(300 + seed, bs=bs, B=6, Hq=4, Hkv=2, D=64, q_dtype=q_dtype,
                         kv_dtype=kv_dtype, max_len=4 * bs)
         n = c["lens"]
         rng = np.random.default_rng(seed)
@@ -459,7 +462,7 @@ def test_window_closed_forms():
     """One token in the window: its V row exactly.  An empty window: zeros.
     A start outside [0, n]: an error."""
     c = random_case(61, B=2, Hq=2, Hkv=1, D=16, lens=[40, 40])
-    vv = bruteforce.v_token_major(bruteforce.decode_storage(c["v"], "f32"), 1, 16, BS)
+    vv = bruteforce.v_token_major(bruteforce.decode_storage(c["v"], "f32"), 1, 16, BS, 4)
     o = run_oracle(c, seq_starts=[39, 40])
     t = 39
     np.testing.assert_allclose(o[0, 0], vv[c["tables"][0][t // BS], 0, t % BS], rtol=0, atol=0)
