@@ -91,40 +91,54 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a, int32_t 
     const bool windowed = a.seq_starts && it.valid_len && it.n > 0;
     const int32_t w0 = windowed ? __builtin_amdgcn_readfirstlane(a.seq_starts[it.b]) : 0;
     bool bad = !it.valid_len || w0 < 0 || w0 > it.n;
-    const int32_t *table = a.block_tables + (size_t)it.b * a.max_blocks_per_seq;
+    // Block ids come through scalar loads (the table does not change while
+    // the kernel runs), so waiting for one never waits for tile loads.
+    using CI32 = __attribute__((address_space(4))) const int32_t;
+    const CI32 *table = (const CI32 *)(a.block_tables + (size_t)it.b * a.max_blocks_per_seq);
     const char *kbase = static_cast<const char *>(a.k_cache);
     const char *vbase = static_cast<const char *>(a.v_cache);
     const int32_t sh = a.tile_shift; // a block is 1 << sh tiles
-    const int32_t jb0 = it.t0 / kTile;
-    const int32_t jb1 = bad ? jb0 : (it.t1 + kTile - 1) / kTile;
+    const int32_t jb0 = uniform(it.t0 / kTile);
+    const int32_t jb1 = bad ? jb0 : uniform((it.t1 + kTile - 1) / kTile);
 
-    for (int32_t jb = jb0; jb < jb1; ++jb) {
-        const int32_t phys = __builtin_amdgcn_readfirstlane(table[jb >> sh]);
-        if (phys < 0 || phys >= a.num_blocks) {
-            bad = true;
-            break;
-        }
+    // One tile as loaded: this lane's K chunks of token tq, and V pieces
+    // 64 i + lane (dims 16 (VP i + e) + vdim of tokens vtok0 .., places 4 e ..).
+    struct Raw {
+        u32x4 k[S::CH_PER_LANE];
+        u32x4 v[S::V_INSTR];
+    };
+    // Block id of tile jb (clamped to the last tile); an id outside the pool
+    // is recorded and block 0 read in its place.
+    auto id_of = [&](int32_t jb) -> int32_t {
+        const int32_t p = uniform(table[uniform(min(jb, jb1 - 1) >> sh)]);
+        const bool out = (uint32_t)p >= (uint32_t)a.num_blocks;
+        bad |= out;
+        return out ? 0 : p;
+    };
+    auto load = [&](int32_t jb, int32_t phys, Raw &R) {
+        jb = min(jb, jb1 - 1);
         const size_t tile =
             ((((size_t)phys * a.num_kv_heads + it.g) << sh) + (jb & ((1 << sh) - 1))) *
             S::TILE_BYTES;
+#pragma unroll
+        for (int j = 0; j < S::CH_PER_LANE; ++j)
+            R.k[j] = load16_stream(kbase + tile + tq * S::ROW_BYTES + (cq + 4 * j) * 16);
+#pragma unroll
+        for (int i = 0; i < S::V_INSTR; ++i)
+            R.v[i] = load16_stream(vbase + tile + i * 1024 + lane * 16);
+    };
+    auto compute = [&](const Raw &R, int32_t jb) {
         const int32_t tok_base = jb * kTile;
         const bool tail = tok_base + kTile > it.t1 || tok_base < w0;
-
-        // K tile: this lane's chunks of token tq.
         float kv[S::CH_PER_LANE][S::EPC];
 #pragma unroll
-        for (int j = 0; j < S::CH_PER_LANE; ++j) {
-            const u32x4 c = load16_stream(kbase + tile + tq * S::ROW_BYTES + (cq + 4 * j) * 16);
-            Chunk<KT>::unpack(c, kv[j]);
-        }
-        // V tile: piece 64 i + lane holds dims 16 (VP i + e) + vdim of this
-        // lane's 4 tokens, at places 4 e .. 4 e + 3
+        for (int j = 0; j < S::CH_PER_LANE; ++j)
+            Chunk<KT>::unpack(R.k[j], kv[j]);
         float vv[S::VD][4];
 #pragma unroll
         for (int i = 0; i < S::V_INSTR; ++i) {
-            const u32x4 c = load16_stream(vbase + tile + i * 1024 + lane * 16);
             float e[4 * S::VP];
-            Chunk<KT>::unpack(c, e);
+            Chunk<KT>::unpack(R.v[i], e);
 #pragma unroll
             for (int x = 0; x < S::VP; ++x)
 #pragma unroll
@@ -194,6 +208,33 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a, int32_t 
             }
         }
         wave_lds_sync();
+    };
+
+    // A ring of two tiles: the next tile's loads go out before the current
+    // tile's math.  The loop handles tiles in pairs and has one exit, at the
+    // bottom, and the next load is issued on every path (past the end it
+    // re-reads the last tile), so the compiler's wait before the math covers
+    // the current tile only.
+    if (jb1 > jb0) {
+        const int32_t n = jb1 - jb0;
+        Raw R[2];
+        load(jb0, id_of(jb0), R[0]);
+        int32_t id_next = id_of(jb0 + 1);
+        int32_t i = 0;
+        for (; i + 2 <= n; i = uniform(i + 2)) {
+#pragma unroll
+            for (int d = 0; d < 2; ++d) {
+                const int32_t jb = jb0 + i + d;
+                const int32_t id_after = id_of(jb + 2);
+                load(jb + 1, id_next, R[(d + 1) % 2]);
+                compute(R[d], jb);
+                id_next = id_after;
+            }
+        }
+        if (i < n)
+            compute(R[0], jb0 + i); // the last tile of an odd count
+        // no load into these registers is left in flight
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     }
 
     // combine lane partials: l over the 16 token quads, acc over the four
