@@ -65,6 +65,8 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain device-to-device copies of 1 GiB (calibrates the HBM "
                          "byte counters a profiler reports) and exit")
+    ap.add_argument("--no-reuse-hint", action="store_true",
+                    help="pass no seq_shared hint: every block is read with streaming loads")
     ap.add_argument("--separate-append", action="store_true",
                     help="a step calls pa_cache_append then pa_decode instead of "
                          "pa_decode_append")
@@ -166,7 +168,7 @@ def main():
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
 
     # Per-step metadata (slots, tables, lengths), one row per step.
-    meta_words = B + B * maxb + B  # slots, tables, lens
+    meta_words = B + B * maxb + B + B  # slots, tables, lens, leading shared blocks
     lib = pa._lib
     pool_h = pool.handle
     dec_p = dec.ctypes.data
@@ -174,7 +176,8 @@ def main():
     def host_step(dst_ptr):
         rc = lib.pa_seq_append_slots_batch(pool_h, dec_p, B, 1, dst_ptr)
         rc |= lib.pa_export_block_tables(pool_h, dec_p, B, maxb, dst_ptr + 4 * B,
-                                         dst_ptr + 4 * (B + B * maxb), None)
+                                         dst_ptr + 4 * (B + B * maxb), None,
+                                         dst_ptr + 4 * (2 * B + B * maxb))
         if rc:
             raise RuntimeError("host step failed: " + pa.pa_last_error())
 
@@ -204,6 +207,18 @@ def main():
     meta_base = d_meta.data_ptr()
 
     separate = args.separate_append
+    # the sharing hint goes with the launches when some sequence of the batch
+    # shares blocks with another (all-zero counts would add a read for nothing)
+    if upload:
+        first_row = np.zeros(meta_words, np.int32)
+        rc = lib.pa_export_block_tables(pool_h, dec_p, B, maxb, None, None, None,
+                                        first_row.ctypes.data + 4 * (2 * B + B * maxb))
+        if rc:
+            raise RuntimeError("export failed: " + pa.pa_last_error())
+    else:
+        first_row = h_meta[0].numpy()
+    any_shared = bool((first_row[2 * B + B * maxb:] > 0).any())
+    no_hint = args.no_reuse_hint or not any_shared
 
     def step(i):
         if upload:
@@ -217,17 +232,19 @@ def main():
         else:
             row = meta_base + i * meta_row
         slots_p, tables_p, lens_p = row, row + 4 * B, row + 4 * (B + B * maxb)
+        shared_p = None if no_hint else row + 4 * (2 * B + B * maxb)
         r = i % R
         for layer in range(L):
             kcp, vcp = kc_p[layer * R + r]
             if separate:
                 rc = lib.pa_cache_append(kn, vn, kcp, vcp, slots_p, B, dref, ks, vs, s_h)
-                rc |= lib.pa_decode(qp, kcp, vcp, tables_p, maxb, lens_p, None, B, max_len,
-                                    scale, ks, vs, op, ws_p, ws_bytes, partition, dref, s_h)
+                rc |= lib.pa_decode(qp, kcp, vcp, tables_p, maxb, lens_p, None, shared_p, B,
+                                    max_len, scale, ks, vs, op, ws_p, ws_bytes, partition, dref,
+                                    s_h)
             else:
                 rc = lib.pa_decode_append(qp, kn, vn, slots_p, kcp, vcp, tables_p, maxb, lens_p,
-                                          None, B, max_len, scale, ks, vs, op, ws_p, ws_bytes,
-                                          partition, dref, s_h)
+                                          None, shared_p, B, max_len, scale, ks, vs, op, ws_p,
+                                          ws_bytes, partition, dref, s_h)
             if rc:
                 raise RuntimeError("launch failed: " + pa.pa_last_error())
 
@@ -254,15 +271,17 @@ def main():
     # queue's dispatch latency to every sample.
     row = meta_base if upload else meta_base + last * meta_row
     tables_p, lens_p = row + 4 * B, row + 4 * (B + B * maxb)
+    shared_p = None if no_hint else row + 4 * (2 * B + B * maxb)
 
     def decode_kernel(r, layer):
         kcp, vcp = kc_p[layer * R + r]
         if partition == 0:
-            rc = lib.pa_decode(qp, kcp, vcp, tables_p, maxb, lens_p, None, B, max_len, scale, ks,
-                               vs, op, None, 0, 0, dref, s_h)
+            rc = lib.pa_decode(qp, kcp, vcp, tables_p, maxb, lens_p, None, shared_p, B, max_len,
+                               scale, ks, vs, op, None, 0, 0, dref, s_h)
         else:
-            rc = lib.pa_decode_partials(qp, kcp, vcp, tables_p, maxb, lens_p, None, B, max_len,
-                                        scale, ks, vs, op, ws_p, ws_bytes, partition, dref, s_h)
+            rc = lib.pa_decode_partials(qp, kcp, vcp, tables_p, maxb, lens_p, None, shared_p, B,
+                                        max_len, scale, ks, vs, op, ws_p, ws_bytes, partition,
+                                        dref, s_h)
         if rc:
             raise RuntimeError("launch failed: " + pa.pa_last_error())
 
@@ -291,7 +310,7 @@ def main():
         f"of HBM peak")
     final_meta = (staging[last % NBUF] if upload else h_meta[last]).numpy()
     final_tables = final_meta[B:B + B * maxb].reshape(B, maxb).copy()
-    final_lens = final_meta[B + B * maxb:].copy()
+    final_lens = final_meta[B + B * maxb:2 * B + B * maxb].copy()
     last_r = last % R
 
     cpu = None
@@ -332,6 +351,7 @@ def main():
             "kernel": kname,
             "cache_replicas": R,
             "metadata": "uploaded per step" if upload else "resident (all steps)",
+            "reuse_hint": not no_hint,
             "step_calls": ("pa_cache_append + pa_decode" if separate else "pa_decode_append"),
             "parallelism": "none (1 GPU)",
         },
@@ -689,8 +709,17 @@ def cpu_baseline(w, k_cache, v_cache, q, tables, lens, nblocks, ks, vs, target_s
         t += run(nseq)
         reps += 1
     nbytes = reps * int(lens[:nseq].sum()) * w.num_kv_heads * w.head_dim * 2 * eb
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": round(nbytes / t / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model,
             "sample": f"{nseq} of {len(lens)} sequences ({int(lens[:nseq].sum())} tokens, all "
                       f"{w.num_q_heads} q heads) of the last timed step, {reps} pass(es), fp64 C "
                       f"oracle, {t:.1f} s"}

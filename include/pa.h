@@ -214,13 +214,19 @@ pa_status pa_block_refcount(const pa_pool *pool, int32_t block, int32_t *refcoun
 
 /* Writes the block tables of nseq resident sequences into tables_out
  * [nseq][max_blocks] (int32, entries past a table's end set to -1), their
- * lengths into lens_out[nseq] and their window starts into starts_out[nseq]
- * (any output may be NULL).  Lengths and starts count from the first kept
- * block (see pa_seq_slide_window); without a window they are the length and
- * 0.  PA_ERR_CAPACITY if a table has more than max_blocks entries. */
+ * lengths into lens_out[nseq], their window starts into starts_out[nseq] and
+ * into shared_out[nseq] how many leading entries of each table hold a block
+ * that another of these nseq tables also holds (any output may be NULL).
+ * Lengths and starts count from the first kept block (see
+ * pa_seq_slide_window); without a window they are the length and 0.  The
+ * shared counts are a hint for the decode calls' seq_shared: blocks shared
+ * through a common prefix ([devto] §5 "Automatic Prefix Caching"; [hi]
+ * "Prefix caching: share the system prompt") are read once per sequence
+ * that holds them, so they are worth keeping in the GPU caches.
+ * PA_ERR_CAPACITY if a table has more than max_blocks entries. */
 pa_status pa_export_block_tables(const pa_pool *pool, const int32_t *seqs, int32_t nseq,
                                  int32_t max_blocks, int32_t *tables_out, int32_t *lens_out,
-                                 int32_t *starts_out);
+                                 int32_t *starts_out, int32_t *shared_out);
 
 pa_status pa_pool_get_stats(const pa_pool *pool, pa_pool_stats *out);
 
@@ -335,6 +341,12 @@ size_t pa_decode_workspace_bytes(const pa_kv_desc *desc, int32_t num_seqs, int32
  *     block ids are out of range is written as NaN instead of being read.
  *   seq_starts: device int32 [num_seqs] or NULL; each in [0, seq_lens[b]]
  *     (not read for zero-length rows).  pa_export_block_tables gives them.
+ *   seq_shared: device int32 [num_seqs] or NULL, a hint: the first
+ *     seq_shared[b] entries of table b hold blocks that other sequences of
+ *     the batch also read (pa_export_block_tables gives the counts).  The
+ *     MFMA kernel reads those blocks with loads that keep them in the GPU
+ *     caches and all others with streaming loads (read once); the VALU
+ *     kernel streams every block.  The result does not depend on the hint.
  *   partition_size: PA_PARTITION_NONE, PA_PARTITION_BALANCED, or a positive
  *     multiple of block_size: each (sequence, KV head) is split into chunks
  *     of that many tokens whose partial softmax states are merged by a second
@@ -344,8 +356,9 @@ size_t pa_decode_workspace_bytes(const pa_kv_desc *desc, int32_t num_seqs, int32
  * Accumulation is fp32; out is rounded to nearest even. */
 pa_status pa_decode(const void *q, const void *k_cache, const void *v_cache,
                     const int32_t *block_tables, int32_t max_blocks_per_seq,
-                    const int32_t *seq_lens, const int32_t *seq_starts, int32_t num_seqs,
-                    int32_t max_seq_len, float scale, float k_scale, float v_scale, void *out,
+                    const int32_t *seq_lens, const int32_t *seq_starts,
+                    const int32_t *seq_shared, int32_t num_seqs, int32_t max_seq_len,
+                    float scale, float k_scale, float v_scale, void *out,
                     void *workspace, size_t workspace_bytes, int32_t partition_size,
                     const pa_kv_desc *desc, void *stream);
 
@@ -393,8 +406,9 @@ pa_status pa_swap_blocks(void *k_cache, void *v_cache, void *host_k, void *host_
 pa_status pa_decode_append(const void *q, const void *k_new, const void *v_new,
                            const int32_t *slot_mapping, void *k_cache, void *v_cache,
                            const int32_t *block_tables, int32_t max_blocks_per_seq,
-                           const int32_t *seq_lens, const int32_t *seq_starts, int32_t num_seqs,
-                           int32_t max_seq_len, float scale, float k_scale, float v_scale,
+                           const int32_t *seq_lens, const int32_t *seq_starts,
+                           const int32_t *seq_shared, int32_t num_seqs, int32_t max_seq_len,
+                           float scale, float k_scale, float v_scale,
                            void *out, void *workspace, size_t workspace_bytes,
                            int32_t partition_size, const pa_kv_desc *desc, void *stream);
 
@@ -412,9 +426,10 @@ pa_status pa_decode_append(const void *q, const void *k_new, const void *v_new,
 pa_status pa_decode_partials(const void *q, const void *k_cache, const void *v_cache,
                              const int32_t *block_tables, int32_t max_blocks_per_seq,
                              const int32_t *seq_lens, const int32_t *seq_starts,
-                             int32_t num_seqs, int32_t max_seq_len, float scale, float k_scale,
-                             float v_scale, void *out, void *workspace, size_t workspace_bytes,
-                             int32_t partition_size, const pa_kv_desc *desc, void *stream);
+                             const int32_t *seq_shared, int32_t num_seqs, int32_t max_seq_len,
+                             float scale, float k_scale, float v_scale, void *out,
+                             void *workspace, size_t workspace_bytes, int32_t partition_size,
+                             const pa_kv_desc *desc, void *stream);
 pa_status pa_decode_merge(const int32_t *seq_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
                           int32_t max_seq_len, void *out, const void *workspace,
                           size_t workspace_bytes, int32_t partition_size, const pa_kv_desc *desc,

@@ -368,22 +368,38 @@ class PoolModel:
         return n
 
     # -- export ----------------------------------------------------------
-    def export(self, sids, max_blocks, with_starts=False):
-        """(status, tables[nseq][max_blocks] padded with -1, lens) and, with
-        with_starts, the window starts as a fourth item; lengths and starts
-        count from the first kept block."""
+    def export(self, sids, max_blocks, with_starts=False, with_shared=False):
+        """(status, tables[nseq][max_blocks] padded with -1, lens), then with
+        with_starts the window starts, then with with_shared, per sequence,
+        how many leading entries of its table name a block that another of
+        the exported tables also names; lengths and starts count from the
+        first kept block."""
+        extra = ((None,) if with_starts else ()) + ((None,) if with_shared else ())
         tables, lens, starts = [], [], []
         for sid in sids:
             if not self._resident(sid):
-                return (ERR_INVALID_ARG, None, None) + ((None,) if with_starts else ())
+                return (ERR_INVALID_ARG, None, None) + extra
             t = self.tables[sid]
             if len(t) > max_blocks:
-                return (ERR_CAPACITY, None, None) + ((None,) if with_starts else ())
+                return (ERR_CAPACITY, None, None) + extra
             tables.append(t + [-1] * (max_blocks - len(t)))
             base = self.dropped[sid] * self.block_size
             lens.append(self.lens[sid] - base)
             starts.append(self.starts[sid] - base)
-        return (OK, tables, lens) + ((starts,) if with_starts else ())
+        out = (OK, tables, lens) + ((starts,) if with_starts else ())
+        if with_shared:
+            shared = []
+            for i, sid in enumerate(sids):
+                others = set()
+                for j, other in enumerate(sids):
+                    if j != i:
+                        others.update(self.tables[other])
+                k = 0
+                while k < len(self.tables[sid]) and self.tables[sid][k] in others:
+                    k += 1
+                shared.append(k)
+            out += (shared,)
+        return out
 
     def stats(self):
         used = self.num_blocks - len(self.free)

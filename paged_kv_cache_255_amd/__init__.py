@@ -86,7 +86,7 @@ _SIGS = {
     "pa_seq_free": (ctypes.c_int, [_P, _I32]),
     "pa_seq_length": (ctypes.c_int, [_P, _I32, _PI32]),
     "pa_block_refcount": (ctypes.c_int, [_P, _I32, _PI32]),
-    "pa_export_block_tables": (ctypes.c_int, [_P, _P, _I32, _I32, _P, _P, _P]),
+    "pa_export_block_tables": (ctypes.c_int, [_P, _P, _I32, _I32, _P, _P, _P, _P]),
     "pa_seq_slide_window": (ctypes.c_int, [_P, _I32, _I32, _P]),
     "pa_seq_swap_out": (ctypes.c_int, [_P, _I32, _P, _I32, _P]),
     "pa_seq_swap_in": (ctypes.c_int, [_P, _I32, _P, _I32, _P]),
@@ -96,15 +96,15 @@ _SIGS = {
     "pa_cache_append": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, ctypes.POINTER(KvDesc),
                                        ctypes.c_float, ctypes.c_float, _P]),
     "pa_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(KvDesc), _I32, _I32, _I32]),
-    "pa_decode": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _P, _I32, _I32, ctypes.c_float,
+    "pa_decode": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _P, _P, _I32, _I32, ctypes.c_float,
                                  ctypes.c_float, ctypes.c_float, _P, _P, ctypes.c_size_t, _I32,
                                  ctypes.POINTER(KvDesc), _P]),
-    "pa_decode_partials": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _P, _I32, _I32,
+    "pa_decode_partials": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _P, _P, _I32, _I32,
                                           ctypes.c_float, ctypes.c_float, ctypes.c_float, _P, _P,
                                           ctypes.c_size_t, _I32, ctypes.POINTER(KvDesc), _P]),
     "pa_decode_merge": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _P, ctypes.c_size_t, _I32,
                                        ctypes.POINTER(KvDesc), _P]),
-    "pa_decode_append": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _I32, _I32,
+    "pa_decode_append": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _I32, _I32,
                                         ctypes.c_float, ctypes.c_float, ctypes.c_float, _P, _P,
                                         ctypes.c_size_t, _I32, _P, _P]),
     "pa_pool_take_copies": (ctypes.c_int, [_P, _P, _I32, _P]),
@@ -232,19 +232,30 @@ def pa_block_refcount(pool, block):
 
 
 def pa_export_block_tables(pool, seqs, max_blocks, tables_out=None, lens_out=None,
-                           starts_out=None, with_starts=False):
-    """Returns (tables [nseq][max_blocks] int32, lens [nseq] int32), and the
-    window starts [nseq] as a third item with with_starts (or starts_out);
-    pass preallocated buffers (numpy or pinned tensors) to fill them in place."""
+                           starts_out=None, with_starts=False, shared_out=None,
+                           with_shared=False):
+    """Returns (tables [nseq][max_blocks] int32, lens [nseq] int32), then the
+    window starts [nseq] with with_starts (or starts_out), then the leading
+    shared-block counts [nseq] with with_shared (or shared_out); pass
+    preallocated buffers (numpy or pinned tensors) to fill them in place."""
     seqs = _i32_array(seqs)
     t = tables_out if tables_out is not None else np.empty((len(seqs), max_blocks), np.int32)
     n = lens_out if lens_out is not None else np.empty(len(seqs), np.int32)
     w = starts_out
     if w is None and with_starts:
         w = np.empty(len(seqs), np.int32)
+    sh = shared_out
+    if sh is None and with_shared:
+        sh = np.empty(len(seqs), np.int32)
     _check(_lib.pa_export_block_tables(pool.handle, seqs.ctypes.data, len(seqs), max_blocks,
-                                       _addr(t), _addr(n), _addr(w)), "pa_export_block_tables")
-    return (t, n, w) if w is not None else (t, n)
+                                       _addr(t), _addr(n), _addr(w), _addr(sh)),
+           "pa_export_block_tables")
+    out = (t, n)
+    if w is not None:
+        out += (w,)
+    if sh is not None:
+        out += (sh,)
+    return out
 
 
 def pa_seq_slide_window(pool, seq, window):
@@ -395,16 +406,20 @@ def pa_decode_workspace_bytes(desc, num_seqs, max_seq_len, partition_size):
                                               partition_size))
 
 
-def _starts(seq_starts, B):
-    if seq_starts is None:
+def _per_seq(x, name, B):
+    if x is None:
         return None
-    _check_tensor(seq_starts, "seq_starts", B * 4)
-    return _addr(seq_starts)
+    _check_tensor(x, name, B * 4)
+    return _addr(x)
+
+
+def _starts(seq_starts, B):
+    return _per_seq(seq_starts, "seq_starts", B)
 
 
 def pa_decode(q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale, out, desc,
               k_scale=1.0, v_scale=1.0, workspace=None, partition_size=PARTITION_NONE,
-              stream=None, seq_starts=None):
+              stream=None, seq_starts=None, seq_shared=None):
     B = seq_lens.numel()
     qb, kb = DTYPE_BYTES[desc.q_dtype], DTYPE_BYTES[desc.kv_dtype]
     qrow = desc.num_q_heads * desc.head_dim
@@ -422,15 +437,16 @@ def pa_decode(q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale, o
         _check_tensor(workspace, "workspace")
         ws_bytes = workspace.numel() * workspace.element_size()
     _check(_lib.pa_decode(_addr(q), _addr(k_cache), _addr(v_cache), _addr(block_tables),
-                          block_tables.shape[1], _addr(seq_lens), _starts(seq_starts, B), B,
-                          max_seq_len, scale, k_scale, v_scale, _addr(out), _addr(workspace),
+                          block_tables.shape[1], _addr(seq_lens), _starts(seq_starts, B),
+                          _per_seq(seq_shared, "seq_shared", B), B, max_seq_len, scale, k_scale, v_scale, _addr(out), _addr(workspace),
                           ws_bytes, partition_size, ctypes.byref(desc), _stream(stream)),
            "pa_decode")
 
 
 def pa_decode_append(q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables, seq_lens,
                      max_seq_len, scale, out, desc, k_scale=1.0, v_scale=1.0, workspace=None,
-                     partition_size=PARTITION_NONE, stream=None, seq_starts=None):
+                     partition_size=PARTITION_NONE, stream=None, seq_starts=None,
+                     seq_shared=None):
     B = seq_lens.numel()
     qb, kb = DTYPE_BYTES[desc.q_dtype], DTYPE_BYTES[desc.kv_dtype]
     qrow = desc.num_q_heads * desc.head_dim
@@ -454,14 +470,14 @@ def pa_decode_append(q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tabl
     _check(_lib.pa_decode_append(_addr(q), _addr(k_new), _addr(v_new), _addr(slot_mapping),
                                  _addr(k_cache), _addr(v_cache), _addr(block_tables),
                                  block_tables.shape[1], _addr(seq_lens), _starts(seq_starts, B),
-                                 B, max_seq_len, scale, k_scale, v_scale, _addr(out),
+                                 _per_seq(seq_shared, "seq_shared", B), B, max_seq_len, scale, k_scale, v_scale, _addr(out),
                                  _addr(workspace), ws_bytes, partition_size, ctypes.byref(desc),
                                  _stream(stream)), "pa_decode_append")
 
 
 def pa_decode_partials(q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale, out,
                        desc, workspace, partition_size, k_scale=1.0, v_scale=1.0, stream=None,
-                       seq_starts=None):
+                       seq_starts=None, seq_shared=None):
     """The first launch of a partitioned pa_decode.  In the balanced mode it
     writes the rows of the (sequence, KV head) segments one work item covers
     whole to `out`; pa_decode_merge writes the others."""
@@ -470,7 +486,8 @@ def pa_decode_partials(q, k_cache, v_cache, block_tables, seq_lens, max_seq_len,
     _check_tensor(out, "out")
     _check(_lib.pa_decode_partials(_addr(q), _addr(k_cache), _addr(v_cache), _addr(block_tables),
                                    block_tables.shape[1], _addr(seq_lens),
-                                   _starts(seq_starts, B), B, max_seq_len, scale,
+                                   _starts(seq_starts, B), _per_seq(seq_shared, "seq_shared", B),
+                                   B, max_seq_len, scale,
                                    k_scale, v_scale, _addr(out), _addr(workspace),
                                    workspace.numel() * workspace.element_size(), partition_size,
                                    ctypes.byref(desc), _stream(stream)), "pa_decode_partials")

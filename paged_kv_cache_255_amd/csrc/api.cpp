@@ -247,7 +247,8 @@ struct NewTokens {
 
 pa_status decode_impl(Phase phase, const void *q, const void *k_cache, const void *v_cache,
                       const int32_t *block_tables, int32_t max_blocks_per_seq,
-                      const int32_t *seq_lens, const int32_t *seq_starts, int32_t num_seqs,
+                      const int32_t *seq_lens, const int32_t *seq_starts,
+                      const int32_t *seq_shared, int32_t num_seqs,
                       int32_t max_seq_len, float scale, float k_scale, float v_scale, void *out,
                       void *workspace, size_t workspace_bytes, int32_t partition_size,
                       const pa_kv_desc *desc, void *stream, const NewTokens &nt = NewTokens{})
@@ -289,6 +290,7 @@ pa_status decode_impl(Phase phase, const void *q, const void *k_cache, const voi
     a.block_tables = block_tables;
     a.seq_lens = seq_lens;
     a.seq_starts = seq_starts;
+    a.seq_shared = seq_shared;
     a.out = out;
     a.ws = static_cast<float *>(workspace);
     a.num_seqs = num_seqs;
@@ -390,21 +392,23 @@ extern "C" {
 
 pa_status pa_decode(const void *q, const void *k_cache, const void *v_cache,
                     const int32_t *block_tables, int32_t max_blocks_per_seq,
-                    const int32_t *seq_lens, const int32_t *seq_starts, int32_t num_seqs,
-                    int32_t max_seq_len, float scale, float k_scale, float v_scale, void *out,
+                    const int32_t *seq_lens, const int32_t *seq_starts,
+                    const int32_t *seq_shared, int32_t num_seqs, int32_t max_seq_len,
+                    float scale, float k_scale, float v_scale, void *out,
                     void *workspace, size_t workspace_bytes, int32_t partition_size,
                     const pa_kv_desc *desc, void *stream)
 {
     return decode_impl(kAll, q, k_cache, v_cache, block_tables, max_blocks_per_seq, seq_lens,
-                       seq_starts, num_seqs, max_seq_len, scale, k_scale, v_scale, out,
-                       workspace, workspace_bytes, partition_size, desc, stream);
+                       seq_starts, seq_shared, num_seqs, max_seq_len, scale, k_scale, v_scale,
+                       out, workspace, workspace_bytes, partition_size, desc, stream);
 }
 
 pa_status pa_decode_append(const void *q, const void *k_new, const void *v_new,
                            const int32_t *slot_mapping, void *k_cache, void *v_cache,
                            const int32_t *block_tables, int32_t max_blocks_per_seq,
-                           const int32_t *seq_lens, const int32_t *seq_starts, int32_t num_seqs,
-                           int32_t max_seq_len, float scale, float k_scale, float v_scale,
+                           const int32_t *seq_lens, const int32_t *seq_starts,
+                           const int32_t *seq_shared, int32_t num_seqs, int32_t max_seq_len,
+                           float scale, float k_scale, float v_scale,
                            void *out, void *workspace, size_t workspace_bytes,
                            int32_t partition_size, const pa_kv_desc *desc, void *stream)
 {
@@ -415,20 +419,21 @@ pa_status pa_decode_append(const void *q, const void *k_new, const void *v_new,
     nt.v = v_new;
     nt.slots = slot_mapping;
     return decode_impl(kAll, q, k_cache, v_cache, block_tables, max_blocks_per_seq, seq_lens,
-                       seq_starts, num_seqs, max_seq_len, scale, k_scale, v_scale, out,
-                       workspace, workspace_bytes, partition_size, desc, stream, nt);
+                       seq_starts, seq_shared, num_seqs, max_seq_len, scale, k_scale, v_scale,
+                       out, workspace, workspace_bytes, partition_size, desc, stream, nt);
 }
 
 pa_status pa_decode_partials(const void *q, const void *k_cache, const void *v_cache,
                              const int32_t *block_tables, int32_t max_blocks_per_seq,
                              const int32_t *seq_lens, const int32_t *seq_starts,
-                             int32_t num_seqs, int32_t max_seq_len, float scale, float k_scale,
-                             float v_scale, void *out, void *workspace, size_t workspace_bytes,
-                             int32_t partition_size, const pa_kv_desc *desc, void *stream)
+                             const int32_t *seq_shared, int32_t num_seqs, int32_t max_seq_len,
+                             float scale, float k_scale, float v_scale, void *out,
+                             void *workspace, size_t workspace_bytes, int32_t partition_size,
+                             const pa_kv_desc *desc, void *stream)
 {
     return decode_impl(kPartials, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
-                       seq_lens, seq_starts, num_seqs, max_seq_len, scale, k_scale, v_scale,
-                       out, workspace, workspace_bytes, partition_size, desc, stream);
+                       seq_lens, seq_starts, seq_shared, num_seqs, max_seq_len, scale, k_scale,
+                       v_scale, out, workspace, workspace_bytes, partition_size, desc, stream);
 }
 
 pa_status pa_decode_merge(const int32_t *seq_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
@@ -437,7 +442,7 @@ pa_status pa_decode_merge(const int32_t *seq_lens, int32_t num_seqs, int32_t max
                           void *stream)
 {
     return decode_impl(kMerge, nullptr, nullptr, nullptr, nullptr, max_blocks_per_seq, seq_lens,
-                       nullptr, num_seqs, max_seq_len, 1.f, 1.f, 1.f, out,
+                       nullptr, nullptr, num_seqs, max_seq_len, 1.f, 1.f, 1.f, out,
                        const_cast<void *>(workspace), workspace_bytes, partition_size, desc,
                        stream);
 }

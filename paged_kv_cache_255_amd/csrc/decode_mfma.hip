@@ -34,6 +34,7 @@
 //       others leave partial states that merge.hip combines.
 #include <map>
 #include <mutex>
+#include <type_traits>
 
 #include "append.hpp"
 #include "device.hpp"
@@ -238,19 +239,32 @@ struct MfmaWave {
 
     // K: token `col`, chunks grp, grp+4, ... (64 contiguous bytes of every row
     // per load instruction).  V^T: dims 16t + col, tokens 4*grp .. 4*grp+3
-    // (1 KiB contiguous per load instruction, see v_tile_index).
+    // (1 KiB contiguous per load instruction, see v_tile_index).  kt and vt
+    // are wave-uniform.  STREAM: loads for data read once (the nontemporal
+    // hint); otherwise loads that keep the tile in the caches, for blocks
+    // other sequences also read.
+    template <bool STREAM>
+    __device__ static u32x4 load16_policy(const char *p)
+    {
+        if constexpr (STREAM)
+            return load16_stream(p);
+        else
+            return load16(p);
+    }
+
+    template <bool STREAM>
     __device__ static void load_tile(const char *kt, const char *vt, int col, int grp, Tile &T)
     {
 #pragma unroll
         for (int j = 0; j < CH_PER_LANE; ++j)
-            T.k[j] = load16_stream(kt + col * ROW_BYTES + (grp + 4 * j) * 16);
+            T.k[j] = load16_policy<STREAM>(kt + col * ROW_BYTES + (grp + 4 * j) * 16);
         // lane L = col + 16 grp takes 16-byte piece 64 q + L of the V tile:
         // V^T rows 16 t + col, tokens 4 grp .. 4 grp + 3, for the 16 / (4 KE)
         // values of t that piece holds (v_tile_index)
         const int L = col + 16 * grp;
 #pragma unroll
         for (int q = 0; q < PV_TILES * 4 * KE / 16; ++q) {
-            const u32x4 x = load16_stream(vt + q * 1024 + 16 * L);
+            const u32x4 x = load16_policy<STREAM>(vt + q * 1024 + 16 * L);
             if constexpr (KE == 2) {
                 T.v[2 * q][0] = x.x;
                 T.v[2 * q][1] = x.y;
@@ -339,13 +353,16 @@ struct MfmaWave {
     // not read), if the window start is outside [0, n], or if the step's
     // token is to be appended here (a.append and t1 == n) and its slot is not
     // the cache slot of position n - 1.
+    // HINT: a.seq_shared is set (the launch reads it once per range and
+    // picks the cache policy per tile); without it every tile streams.
+    template <bool HINT>
     __device__ bool run(const DecodeArgs &a, int32_t b, int32_t g, int32_t t0, int32_t t1,
                         int32_t n_seq)
     {
         // The block table does not change while the kernel runs: its entries
         // are read with scalar loads (one wave-uniform id per tile, fetched
-        // two tiles ahead), which keeps them out of the vector-load queue
-        // the tiles stream through.
+        // one tile before its loads), which keeps them out of the vector-load
+        // queue the tiles stream through.
         using CI32 = __attribute__((address_space(4))) const int32_t;
         b = uniform(b);
         g = uniform(g);
@@ -366,29 +383,22 @@ struct MfmaWave {
         auto id_of = [&](int32_t jb) -> int32_t {
             return uniform(table[uniform(min(jb, last) >> sh)]);
         };
-        auto sub_of = [&](int32_t jb) -> size_t {
-            return (size_t)(min(jb, last) & mask) * TILE_BYTES;
-        };
         auto valid_of = [&](int32_t jb) { return min(kTile, t1 - jb * kTile); };
         const int32_t w0 = a.seq_starts ? uniform(((const CI32 *)a.seq_starts)[b]) : 0;
         auto lo_of = [&](int32_t jb) { return min(kTile, max(0, w0 - jb * kTile)); };
         const bool append_here = a.append && t1 == uniform(n_seq);
-        auto load = [&](int32_t phys, size_t sub, Tile &T) {
-            const size_t o = (size_t)phys * bstride + sub;
-            load_tile(kbase + o, vbase + o, col, grp, T);
-        };
 
-        // A ring of DEPTH tiles: while one is computed, the next DEPTH - 1
-        // are in flight.  The loop runs over groups of DEPTH tiles and has one
-        // exit, at the bottom; the next load is issued on every path (past the
-        // end it re-reads the last tile, an L2 hit).  A load issued on one
-        // path only, or an exit that shares a block with the back edge, would
-        // make the compiler's wait counts assume a shorter queue and wait for
-        // the next tile before the current one is done.  An entry outside the
-        // pool is recorded and block 0 read in its place (the caller turns
-        // the result into NaN), so no early exit is needed either.
-        Tile T[DEPTH];
-        const int32_t n = last - jb0 + 1; // tiles in the range, >= 1
+        // A ring of DEPTH tiles over tiles [s0, s1] (s0 <= s1), all read with
+        // one cache policy: while one is computed, the next DEPTH - 1 are in
+        // flight.  The loop runs over groups of DEPTH tiles and has one exit,
+        // at the bottom; the next load is issued on every path (past s1 it
+        // re-reads tile s1, an L2 hit).  A load issued on one path only, or an
+        // exit that shares a block with the back edge, would make the
+        // compiler's wait counts assume a shorter queue and wait for the next
+        // tile before the current one is done; so would a branch between the
+        // two policies inside the loop.  An entry outside the pool is
+        // recorded and block 0 read in its place (the caller turns the result
+        // into NaN), so no early exit is needed either.
         bool bad = w0 < 0 || w0 > n_seq;
         auto checked = [&](int32_t id) {
             const bool out = (uint32_t)id >= nblocks;
@@ -414,38 +424,78 @@ struct MfmaWave {
             if (put)
                 load_new_token(a, b, g, (t1 - 1) % kTile, nt);
         }
-        // tile jb0 + k lives in T[k % DEPTH]
+        // With the hint, the block ids of the first DEPTH tiles are fetched
+        // before the split below is known (every range starts with a ring at
+        // jb0), so that reading the hint adds no step to the chain before
+        // the first tile loads.
+        int32_t id0[DEPTH];
+        if constexpr (HINT) {
 #pragma unroll
-        for (int d = 0; d + 1 < DEPTH; ++d)
-            load(checked(id_of(jb0 + d)), sub_of(jb0 + d), T[d]);
-        int32_t id_next = id_of(jb0 + DEPTH - 1); // block id of the next tile to load
-        int32_t i = 0;
-        for (; i + DEPTH <= n; i = uniform(i + DEPTH)) {
-#pragma unroll
-            for (int d = 0; d < DEPTH; ++d) {
-                const int32_t jb = jb0 + i + d;
-                const int32_t id_after = id_of(jb + DEPTH); // fetched one tile ahead of use
-                load(checked(id_next), sub_of(jb + DEPTH - 1), T[(d + DEPTH - 1) % DEPTH]);
-                __builtin_amdgcn_sched_barrier(0); // that load goes out before T[d] is waited for
-                if (put && jb == last)
-                    apply_new_token(T[d], nt);
-                compute(T[d], lo_of(jb), valid_of(jb), sc);
-                id_next = id_after;
-            }
+            for (int d = 0; d < DEPTH; ++d)
+                id0[d] = id_of(jb0 + d);
         }
-        // the last n - i (< DEPTH) tiles, already in T[0 ..]
+        auto ring = [&](auto stream, int32_t s0, int32_t s1, bool first) {
+            constexpr bool STREAM = decltype(stream)::value;
+            auto id_at = [&](int32_t jb) -> int32_t {
+                return uniform(table[uniform(min(jb, s1) >> sh)]);
+            };
+            auto load = [&](int32_t phys, int32_t jb, Tile &T) {
+                jb = min(jb, s1);
+                const size_t o = (size_t)phys * bstride + (size_t)(jb & mask) * TILE_BYTES;
+                load_tile<STREAM>(kbase + o, vbase + o, col, grp, T);
+            };
+            Tile T[DEPTH];
+            const int32_t n = s1 - s0 + 1;
+            // tile s0 + k lives in T[k % DEPTH]
+            // (with `first`, s0 = jb0 and the ids past s1 are those of tiles
+            // of the range past s1: valid blocks, read and not used)
 #pragma unroll
-        for (int d = 0; d + 1 < DEPTH; ++d) {
-            if (i + d < n) {
-                const int32_t jb = jb0 + i + d;
-                if (put && jb == last)
-                    apply_new_token(T[d], nt);
-                compute(T[d], lo_of(jb), valid_of(jb), sc);
+            for (int d = 0; d + 1 < DEPTH; ++d)
+                load(checked(HINT && first ? id0[d] : id_at(s0 + d)), s0 + d, T[d]);
+            // block id of the next tile to load
+            int32_t id_next = HINT && first ? id0[DEPTH - 1] : id_at(s0 + DEPTH - 1);
+            int32_t i = 0;
+            for (; i + DEPTH <= n; i = uniform(i + DEPTH)) {
+#pragma unroll
+                for (int d = 0; d < DEPTH; ++d) {
+                    const int32_t jb = s0 + i + d;
+                    const int32_t id_after = id_at(jb + DEPTH); // one tile ahead of use
+                    load(checked(id_next), jb + DEPTH - 1, T[(d + DEPTH - 1) % DEPTH]);
+                    __builtin_amdgcn_sched_barrier(0); // that load goes out before T[d] is waited for
+                    if (put && jb == last)
+                        apply_new_token(T[d], nt);
+                    compute(T[d], lo_of(jb), valid_of(jb), sc);
+                    id_next = id_after;
+                }
             }
+            // the last n - i (< DEPTH) tiles, already in T[0 ..]
+#pragma unroll
+            for (int d = 0; d + 1 < DEPTH; ++d) {
+                if (i + d < n) {
+                    const int32_t jb = s0 + i + d;
+                    if (put && jb == last)
+                        apply_new_token(T[d], nt);
+                    compute(T[d], lo_of(jb), valid_of(jb), sc);
+                }
+            }
+            // Drain the re-reads issued past s1, so no load into these
+            // registers is in flight when the next ring starts.
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        };
+        // The first `shared` blocks of the table are also read by other
+        // sequences of the batch: their tiles go through a ring of caching
+        // loads, the rest through a ring of streaming loads.
+        if constexpr (HINT) {
+            int32_t shared = uniform(((const CI32 *)a.seq_shared)[b]);
+            shared = min(max(shared, 0), a.max_blocks_per_seq);
+            const int32_t split = uniform(min(max(shared << sh, jb0), last + 1));
+            if (split > jb0)
+                ring(std::integral_constant<bool, false>{}, jb0, split - 1, true);
+            if (split <= last)
+                ring(std::integral_constant<bool, true>{}, split, last, split == jb0);
+        } else {
+            ring(std::integral_constant<bool, true>{}, jb0, last, false);
         }
-        // Drain the re-reads issued past the end, so no load into these
-        // registers is in flight when the next range starts.
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         if (put) {
             const size_t row = ((size_t)b * a.num_kv_heads + g) * D;
             store_token<QT, KT, D>(static_cast<const TQ *>(a.k_new) + row,
@@ -494,8 +544,10 @@ struct MfmaWave {
     }
 };
 
-// partition == 0 or > 0: one wave per work item (see work.hpp).
-template <int QT, int KT, int D>
+// partition == 0 or > 0: one wave per work item (see work.hpp).  HINT:
+// a.seq_shared is set; each kernel is built with and without it, so the
+// launches without the hint run the same code as before it existed.
+template <int QT, int KT, int D, bool HINT>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a, int32_t num_items)
 {
     const int lane = threadIdx.x & 63;
@@ -511,7 +563,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a, int32_t 
     wv.start(a, it.b, it.g);
     bool ok = it.valid_len;
     if (ok && it.t1 > it.t0)
-        ok = wv.run(a, it.b, it.g, it.t0, it.t1, it.n);
+        ok = wv.template run<HINT>(a, it.b, it.g, it.t0, it.t1, it.n);
     wv.finish();
     if (a.partition == 0)
         wv.write_out(a, it.b, it.g, it.n, ok);
@@ -521,7 +573,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a, int32_t 
 
 // Balanced split: wave i of W takes tiles [i*T/W, (i+1)*T/W) of the list of
 // all (sequence, KV head, 16-token tile) tiles in that order, T tiles in total.
-template <int QT, int KT, int D>
+// HINT as for decode_mfma_kernel.
+template <int QT, int KT, int D, bool HINT>
 __global__ __launch_bounds__(256)
 void decode_mfma_balanced_kernel(DecodeArgs a, int32_t W)
 {
@@ -550,7 +603,8 @@ void decode_mfma_balanced_kernel(DecodeArgs a, int32_t W)
         const int64_t stop = min(x1, seg_end);
         const int32_t je = j + (int32_t)(stop - x);
         wv.start(a, pos.b, g);
-        const bool ok = wv.run(a, pos.b, g, j * kTile, min(je * kTile, pos.n), pos.n);
+        const bool ok =
+            wv.template run<HINT>(a, pos.b, g, j * kTile, min(je * kTile, pos.n), pos.n);
         wv.finish();
         if (j == 0 && je == nb) {
             wv.write_out(a, pos.b, g, pos.n, ok);
@@ -600,12 +654,17 @@ template <int QT, int KT, int D>
 hipError_t launch_mfma(const DecodeArgs &a, int32_t num_items, hipStream_t stream)
 {
     const int grid = (num_items + 3) / 4;
-    if (a.partition == kPartitionBalanced)
-        hipLaunchKernelGGL((decode_mfma_balanced_kernel<QT, KT, D>), dim3(grid), dim3(256),
-                           balanced_lds_bytes(), stream, a, num_items);
-    else
-        hipLaunchKernelGGL((decode_mfma_kernel<QT, KT, D>), dim3(grid), dim3(256), 0, stream, a,
+    const bool hint = a.seq_shared != nullptr;
+    if (a.partition == kPartitionBalanced) {
+        auto kern = hint ? &decode_mfma_balanced_kernel<QT, KT, D, true>
+                         : &decode_mfma_balanced_kernel<QT, KT, D, false>;
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(256), balanced_lds_bytes(), stream, a,
                            num_items);
+    } else {
+        auto kern =
+            hint ? &decode_mfma_kernel<QT, KT, D, true> : &decode_mfma_kernel<QT, KT, D, false>;
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, stream, a, num_items);
+    }
     return hipGetLastError();
 }
 
@@ -615,7 +674,8 @@ int mfma_balanced_waves_per_cu()
 {
     int blocks = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &blocks, reinterpret_cast<const void *>(&decode_mfma_balanced_kernel<QT, KT, D>), 256,
+            &blocks,
+            reinterpret_cast<const void *>(&decode_mfma_balanced_kernel<QT, KT, D, false>), 256,
             balanced_lds_bytes()) != hipSuccess)
         return 0;
     return blocks * 4;

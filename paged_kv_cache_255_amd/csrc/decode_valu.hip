@@ -115,17 +115,21 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a, int32_t 
         bad |= out;
         return out ? 0 : p;
     };
+    // every tile with the streaming (read-once) hint; this kernel does not
+    // use the seq_shared hint
     auto load = [&](int32_t jb, int32_t phys, Raw &R) {
         jb = min(jb, jb1 - 1);
         const size_t tile =
             ((((size_t)phys * a.num_kv_heads + it.g) << sh) + (jb & ((1 << sh) - 1))) *
             S::TILE_BYTES;
+        const char *kp = kbase + tile + tq * S::ROW_BYTES + cq * 16;
+        const char *vp = vbase + tile + lane * 16;
 #pragma unroll
         for (int j = 0; j < S::CH_PER_LANE; ++j)
-            R.k[j] = load16_stream(kbase + tile + tq * S::ROW_BYTES + (cq + 4 * j) * 16);
+            R.k[j] = load16_stream(kp + 64 * j);
 #pragma unroll
         for (int i = 0; i < S::V_INSTR; ++i)
-            R.v[i] = load16_stream(vbase + tile + i * 1024 + lane * 16);
+            R.v[i] = load16_stream(vp + i * 1024);
     };
     auto compute = [&](const Raw &R, int32_t jb) {
         const int32_t tok_base = jb * kTile;

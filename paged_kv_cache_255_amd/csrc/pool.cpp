@@ -47,6 +47,9 @@ struct pa_pool {
     pa_pool_config cfg{};
     std::vector<int32_t> free_list; // taken from and returned to the back
     std::vector<int32_t> refcount;  // per physical block
+    // Export scratch: per block, how many of the exported tables hold it
+    // (all zero between calls).
+    mutable std::vector<int32_t> batch_count;
     struct Seq {
         bool live = false;
         bool swapped = false; // blocks holds host block ids
@@ -443,7 +446,7 @@ pa_status pa_block_refcount(const pa_pool *p, int32_t block, int32_t *refcount_o
 
 pa_status pa_export_block_tables(const pa_pool *p, const int32_t *seqs, int32_t nseq,
                                  int32_t max_blocks, int32_t *tables_out, int32_t *lens_out,
-                                 int32_t *starts_out)
+                                 int32_t *starts_out, int32_t *shared_out)
 {
     if (!p || nseq < 0 || max_blocks < 0 || (nseq > 0 && !seqs))
         return pa::fail(PA_ERR_INVALID_ARG, "bad export arguments");
@@ -468,6 +471,25 @@ pa_status pa_export_block_tables(const pa_pool *p, const int32_t *seqs, int32_t 
             lens_out[i] = s.len - base;
         if (starts_out)
             starts_out[i] = s.start - base;
+    }
+    if (shared_out) {
+        // leading table entries whose block another exported table also holds
+        std::vector<int32_t> &cnt = p->batch_count;
+        if (cnt.size() != (size_t)p->cfg.num_blocks)
+            cnt.assign(p->cfg.num_blocks, 0);
+        for (int32_t i = 0; i < nseq; ++i)
+            for (int32_t b : p->seqs[seqs[i]].blocks)
+                ++cnt[b];
+        for (int32_t i = 0; i < nseq; ++i) {
+            const std::vector<int32_t> &bl = p->seqs[seqs[i]].blocks;
+            size_t k = 0;
+            while (k < bl.size() && cnt[bl[k]] > 1)
+                ++k;
+            shared_out[i] = (int32_t)k;
+        }
+        for (int32_t i = 0; i < nseq; ++i)
+            for (int32_t b : p->seqs[seqs[i]].blocks)
+                cnt[b] = 0;
     }
     return PA_OK;
 }

@@ -14,6 +14,8 @@ struct DecodeArgs {
     const int32_t *block_tables;
     const int32_t *seq_lens;
     const int32_t *seq_starts; // window starts, or null (every window starts at 0)
+    const int32_t *seq_shared; // leading table entries shared within the batch
+                               // (read with caching loads), or null
     void *out;
     float *ws;                 // partial states (partitioned modes)
     int32_t num_seqs;

@@ -98,7 +98,7 @@ class GpuStep:
         pa.pa_cache_append(i.k_new, i.v_new, self.k_cache, self.v_cache, slots, self.desc,
                            i.k_scale, i.v_scale)
 
-    def decode_append(self, out=None, slots=None, seq_starts=None):
+    def decode_append(self, out=None, slots=None, seq_starts=None, seq_shared=None):
         """pa_decode_append with the step's token: append and decode in one call."""
         i = self.inputs
         out = self.out if out is None else out
@@ -107,16 +107,17 @@ class GpuStep:
         pa.pa_decode_append(i.q, i.k_new, i.v_new, slots, self.k_cache, self.v_cache,
                             self.d_tables, self.d_lens, self.w.max_seq_len(), self.w.scale, out,
                             self.desc, i.k_scale, i.v_scale, workspace=self.workspace,
-                            partition_size=self.partition, seq_starts=_dev(seq_starts))
+                            partition_size=self.partition, seq_starts=_dev(seq_starts),
+                            seq_shared=_dev(seq_shared))
         return out
 
-    def decode(self, out=None, seq_starts=None):
+    def decode(self, out=None, seq_starts=None, seq_shared=None):
         i = self.inputs
         out = self.out if out is None else out
         pa.pa_decode(i.q, self.k_cache, self.v_cache, self.d_tables, self.d_lens,
                      self.w.max_seq_len(), self.w.scale, out, self.desc, i.k_scale, i.v_scale,
                      workspace=self.workspace, partition_size=self.partition,
-                     seq_starts=_dev(seq_starts))
+                     seq_starts=_dev(seq_starts), seq_shared=_dev(seq_shared))
         return out
 
 

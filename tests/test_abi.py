@@ -313,13 +313,15 @@ def test_pool_matches_model_with_windows_and_swaps(bs):
         if it % 50 == 0:
             res = [(l, m) for l, m in live if m not in model.swapped]
             maxb = 64
-            t, n, w = pa.pa_export_block_tables(pool, [l for l, _ in res], maxb,
-                                                with_starts=True)
-            st, mt, mn, mw = model.export([m for _, m in res], maxb, with_starts=True)
+            t, n, w, sh = pa.pa_export_block_tables(pool, [l for l, _ in res], maxb,
+                                                    with_starts=True, with_shared=True)
+            st, mt, mn, mw, msh = model.export([m for _, m in res], maxb, with_starts=True,
+                                               with_shared=True)
             assert st == am.OK
             np.testing.assert_array_equal(t, np.array(mt, dtype=np.int32).reshape(t.shape))
             np.testing.assert_array_equal(n, np.array(mn, dtype=np.int32))
             np.testing.assert_array_equal(w, np.array(mw, dtype=np.int32))
+            np.testing.assert_array_equal(sh, np.array(msh, dtype=np.int32))
             s, ms = pa.pa_pool_get_stats(pool), model.stats()
             for k in ms:
                 assert s[k] == ms[k], k
@@ -333,8 +335,8 @@ def test_decode_partials_needs_out():
     NULL out is refused before anything reaches the device."""
     desc = pa.kv_desc(8, 2, 128, 16, "bf16", "bf16")
     fake = ctypes.c_void_p(4096)
-    st = pa._lib.pa_decode_partials(fake, fake, fake, fake, 1, fake, None, 1, 16, 0.1, 1.0,
-                                    1.0, None, fake, 1 << 20, pa.PARTITION_BALANCED,
+    st = pa._lib.pa_decode_partials(fake, fake, fake, fake, 1, fake, None, None, 1, 16, 0.1,
+                                    1.0, 1.0, None, fake, 1 << 20, pa.PARTITION_BALANCED,
                                     ctypes.byref(desc), None)
     assert st == pa.ERR_INVALID_ARG
     assert "null" in pa.pa_last_error()
