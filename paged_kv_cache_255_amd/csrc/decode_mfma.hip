@@ -571,18 +571,19 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a, int32_t 
         wv.write_partial(a, w, ok);
 }
 
-// Balanced split: wave i of W takes tiles [i*T/W, (i+1)*T/W) of the list of
-// all (sequence, KV head, 16-token tile) tiles in that order, T tiles in total.
-// HINT as for decode_mfma_kernel.
+// Balanced split: run i of W takes tiles [i*T/W, (i+1)*T/W) of the list of
+// all tiles in head-major order ((KV head, sequence, 16-token tile), see
+// work.hpp), T tiles in total; balanced_run places each XCD's runs on that
+// XCD's workgroups.  HINT as for decode_mfma_kernel.
 template <int QT, int KT, int D, bool HINT>
 __global__ __launch_bounds__(256)
 void decode_mfma_balanced_kernel(DecodeArgs a, int32_t W)
 {
     const int lane = threadIdx.x & 63;
-    const int32_t i = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int32_t i =
+        balanced_run(blockIdx.x, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), W);
     if (i >= W)
         return;
-    const int32_t H = a.num_kv_heads;
 
     // T, the number of runs (never more than tiles, so no run is empty), and
     // the first segment of this wave's run
@@ -590,30 +591,26 @@ void decode_mfma_balanced_kernel(DecodeArgs a, int32_t W)
     if (i >= rs.runs)
         return;
     const int64_t x1 = rs.x1;
-    SeqPos pos = rs.pos;
+    SegPos pos = rs.pos;
 
     MfmaWave<QT, KT, D> wv(lane);
     int64_t x = rs.x0;
     while (x < x1) {
         const int32_t nb = tiles_of(pos.n);
-        const int64_t local = x - pos.first_tile;
-        const int32_t g = (int32_t)(local / nb);
-        const int32_t j = (int32_t)(local % nb);
-        const int64_t seg_end = pos.first_tile + (int64_t)(g + 1) * nb;
-        const int64_t stop = min(x1, seg_end);
+        const int32_t j = (int32_t)(x - pos.first_tile);
+        const int64_t stop = min(x1, pos.first_tile + nb);
         const int32_t je = j + (int32_t)(stop - x);
-        wv.start(a, pos.b, g);
-        const bool ok =
-            wv.template run<HINT>(a, pos.b, g, j * kTile, min(je * kTile, pos.n), pos.n);
+        wv.start(a, pos.b, pos.g);
+        const bool ok = wv.template run<HINT>(a, pos.b, pos.g, j * kTile,
+                                              min(je * kTile, pos.n), pos.n);
         wv.finish();
-        if (j == 0 && je == nb) {
-            wv.write_out(a, pos.b, g, pos.n, ok);
-        } else {
-            wv.write_partial(a, (int64_t)i + (int64_t)pos.b * H + g, ok);
-        }
+        if (j == 0 && je == nb)
+            wv.write_out(a, pos.b, pos.g, pos.n, ok);
+        else
+            wv.write_partial(a, balanced_slot(a, i, pos.g, pos.b), ok);
         x = stop;
-        if (x < x1 && g == H - 1)
-            pos = next_sequence(a, pos);
+        if (x < x1)
+            pos = next_segment(a, pos);
     }
 }
 

@@ -195,15 +195,16 @@ __device__ __forceinline__ bool segment_parts(const DecodeArgs &a, int lane, int
                                               int32_t g, int32_t n, int64_t &w0, int64_t &nparts)
 {
     if (a.partition == kPartitionBalanced) {
-        const TileCounts tc = tile_counts(a, lane, b);
-        const int64_t T = tc.total;
+        // segment (g, b) starts at tile g * Th + (tiles of sequences [0, b))
+        const HeadTiles ht = head_tiles(a, lane, b);
+        const int64_t T = ht.per_head * a.num_kv_heads;
         const int32_t R = effective_runs(T, a.waves);
-        const int64_t S0 = tc.before + (int64_t)g * tiles_of(n);
+        const int64_t S0 = (int64_t)g * ht.per_head + ht.before;
         const int64_t i0 = run_of_tile(S0, T, R);
         const int64_t i1 = run_of_tile(S0 + tiles_of(n) - 1, T, R);
         if (i0 == i1)
             return false;
-        w0 = i0 + (int64_t)b * a.num_kv_heads + g;
+        w0 = balanced_slot(a, i0, g, b);
         nparts = i1 - i0 + 1;
     } else {
         w0 = ((int64_t)b * a.num_kv_heads + g) * a.max_parts;

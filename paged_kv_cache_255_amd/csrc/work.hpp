@@ -91,26 +91,20 @@ __device__ __forceinline__ int64_t readlane64(int64_t v, int l)
     return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-// Tiles (KV head x 16-token tile) of sequences [0, upto), summed by one wave.
-__device__ __forceinline__ int64_t tiles_before(const DecodeArgs &a, int lane, int32_t upto)
-{
-    int64_t t = 0;
-    for (int32_t c = 0; c < upto; c += kWave) {
-        const int32_t b = c + lane;
-        t += (b < upto) ? split_tiles(a, a.seq_lens[b]) : 0;
-    }
-    return wave_sum(t) * a.num_kv_heads;
-}
+// The balanced split orders the segments head-major: (KV head g, sequence
+// b) for g = 0 .. Hkv-1 and, within a head, b = 0 .. B-1.  Every head has
+// the same Th tiles (the sequences' tiles summed), so T = Hkv * Th and
+// segment (g, b) starts at tile g * Th + (tiles of sequences [0, b)).
 
-// Tiles of sequences [0, b) and of all sequences, from one pass over the
-// lengths (each lane sums its own sequences; the two sums are wave
-// reductions).
-struct TileCounts {
-    int64_t before; // tiles of sequences [0, b)
-    int64_t total;  // T
+// Tiles of sequences [0, b) and of all sequences (one head's share, Th),
+// from one pass over the lengths (each lane sums its own sequences; the two
+// sums are wave reductions).
+struct HeadTiles {
+    int64_t before;   // tiles of sequences [0, b)
+    int64_t per_head; // Th
 };
 
-__device__ __forceinline__ TileCounts tile_counts(const DecodeArgs &a, int lane, int32_t b)
+__device__ __forceinline__ HeadTiles head_tiles(const DecodeArgs &a, int lane, int32_t b)
 {
     int64_t before = 0, total = 0;
     for (int32_t c = 0; c < a.num_seqs; c += kWave) {
@@ -119,37 +113,42 @@ __device__ __forceinline__ TileCounts tile_counts(const DecodeArgs &a, int lane,
         total += t;
         before += (s < b) ? t : 0;
     }
-    return TileCounts{wave_sum(before) * a.num_kv_heads, wave_sum(total) * a.num_kv_heads};
+    return HeadTiles{wave_sum(before), wave_sum(total)};
 }
 
-struct SeqPos {
+struct SegPos {
+    int32_t g;          // KV head
     int32_t b;          // sequence
     int32_t n;          // its length
-    int64_t first_tile; // index of its first tile in the balanced order
+    int64_t first_tile; // index of the segment's first tile in the balanced order
 };
 
-// The sequence holding tile x (x < total tiles), found one 64-sequence chunk
-// at a time with a wave scan and a ballot.
-__device__ __forceinline__ SeqPos locate_tile(const DecodeArgs &a, int lane, int64_t x)
+// The segment holding tile x (x < T = Hkv * Th): head x / Th, then the
+// sequence holding tile x % Th of that head, found one 64-sequence chunk at
+// a time with a wave scan and a ballot.
+__device__ __forceinline__ SegPos locate_tile(const DecodeArgs &a, int lane, int64_t x,
+                                              int64_t Th)
 {
+    const int32_t g = (int32_t)(x / Th);
+    const int64_t y = x - (int64_t)g * Th;
     int64_t carry = 0;
     for (int32_t c = 0; c < a.num_seqs; c += kWave) {
         const int32_t b = c + lane;
-        const int64_t tiles =
-            (b < a.num_seqs) ? (int64_t)split_tiles(a, a.seq_lens[b]) * a.num_kv_heads : 0;
+        const int64_t tiles = (b < a.num_seqs) ? (int64_t)split_tiles(a, a.seq_lens[b]) : 0;
         const int64_t incl = wave_incl_scan(tiles, lane);
-        const uint64_t hit = __ballot(b < a.num_seqs && carry + incl > x);
+        const uint64_t hit = __ballot(b < a.num_seqs && carry + incl > y);
         if (hit) {
             const int k = __ffsll((unsigned long long)hit) - 1;
-            SeqPos p;
+            SegPos p;
+            p.g = g;
             p.b = c + k;
             p.n = uniform_load(a.seq_lens + p.b);
-            p.first_tile = carry + readlane64(incl - tiles, k);
+            p.first_tile = (int64_t)g * Th + carry + readlane64(incl - tiles, k);
             return p;
         }
         carry += readlane64(incl, kWave - 1);
     }
-    return SeqPos{a.num_seqs, 0, carry};
+    return SegPos{g, a.num_seqs, 0, (int64_t)g * Th + carry};
 }
 
 // Runs the balanced split cuts T tiles into: the launch's W waves, but no
@@ -159,15 +158,30 @@ __device__ __forceinline__ int32_t effective_runs(int64_t T, int32_t W)
     return (int32_t)(T < (int64_t)W ? T : (int64_t)W);
 }
 
-// Where run i of the balanced split starts: T, the number of runs, the run's
-// tiles [x0, x1) and the sequence holding x0.  Up to 64 sequences this is one
-// pass over the lengths (one load per lane, one scan, one ballot); beyond,
-// the chunked count and search above.
+// XCDs of the GPU; the dispatcher hands workgroups to them in turn
+// (workgroup w runs on XCD w mod 8).
+constexpr int32_t kXcds = 8;
+
+// Run of wave v (0..3) of workgroup w among W waves.  Each XCD gets one
+// eighth of the runs, in order: with the head-major order and 8 KV heads,
+// the tiles of one head, so a prefix that the head's sequences share is read
+// through one XCD's L2.  (Falls back to run 4 w + v when W is not a
+// multiple of 32.)
+__device__ __forceinline__ int32_t balanced_run(int32_t w, int32_t v, int32_t W)
+{
+    if (W % (4 * kXcds) != 0)
+        return 4 * w + v;
+    return (w % kXcds) * (W / kXcds) + (w / kXcds) * 4 + v;
+}
+
+// Where run i of the balanced split starts: Th, T, the number of runs, the
+// run's tiles [x0, x1) and the segment holding x0.  Up to 64 sequences the
+// tile count is one load per lane and one reduction; beyond, chunked.
 struct RunStart {
-    int64_t T;
+    int64_t Th, T;
     int32_t runs;
     int64_t x0, x1;
-    SeqPos pos;
+    SegPos pos;
 };
 
 __device__ __forceinline__ RunStart run_start(const DecodeArgs &a, int lane, int32_t i,
@@ -175,43 +189,66 @@ __device__ __forceinline__ RunStart run_start(const DecodeArgs &a, int lane, int
 {
     RunStart r;
     if (a.num_seqs <= kWave) {
+        // one length per lane: the scan gives Th and the segment together
         const bool in = lane < a.num_seqs;
         const int32_t n = in ? a.seq_lens[lane] : 0;
-        const int64_t tiles = in ? (int64_t)split_tiles(a, n) * a.num_kv_heads : 0;
+        const int64_t tiles = in ? (int64_t)split_tiles(a, n) : 0;
         const int64_t incl = wave_incl_scan(tiles, lane);
-        r.T = readlane64(incl, kWave - 1);
+        r.Th = readlane64(incl, kWave - 1);
+        r.T = r.Th * a.num_kv_heads;
         r.runs = effective_runs(r.T, W);
         if (i >= r.runs)
             return r;
         r.x0 = (int64_t)i * r.T / r.runs;
         r.x1 = (int64_t)(i + 1) * r.T / r.runs;
-        const uint64_t hit = __ballot(in && incl > r.x0);
-        const int k = __ffsll((unsigned long long)hit) - 1; // x0 < T: some lane hits
+        const int32_t g = (int32_t)(r.x0 / r.Th);
+        const int64_t y = r.x0 - (int64_t)g * r.Th;
+        const uint64_t hit = __ballot(in && incl > y);
+        const int k = __ffsll((unsigned long long)hit) - 1; // y < Th: some lane hits
+        r.pos.g = g;
         r.pos.b = k;
         r.pos.n = __builtin_amdgcn_readlane(n, k);
-        r.pos.first_tile = readlane64(incl - tiles, k);
+        r.pos.first_tile = (int64_t)g * r.Th + readlane64(incl - tiles, k);
         return r;
     }
-    r.T = tiles_before(a, lane, a.num_seqs);
+    r.Th = head_tiles(a, lane, 0).per_head;
+    r.T = r.Th * a.num_kv_heads;
     r.runs = effective_runs(r.T, W);
     if (i >= r.runs)
         return r;
     r.x0 = (int64_t)i * r.T / r.runs;
     r.x1 = (int64_t)(i + 1) * r.T / r.runs;
-    r.pos = locate_tile(a, lane, r.x0);
+    r.pos = locate_tile(a, lane, r.x0, r.Th);
     return r;
 }
 
-// The next sequence after p that has tiles.
-__device__ __forceinline__ SeqPos next_sequence(const DecodeArgs &a, SeqPos p)
+// The segment after p that has tiles: the next sequence of the head with
+// tiles, else the first such sequence of the next head.
+__device__ __forceinline__ SegPos next_segment(const DecodeArgs &a, SegPos p)
 {
-    SeqPos q;
-    q.first_tile = p.first_tile + (int64_t)tiles_of(p.n) * a.num_kv_heads;
+    SegPos q;
+    q.first_tile = p.first_tile + tiles_of(p.n);
+    q.g = p.g;
     q.b = p.b + 1;
-    while (q.b < a.num_seqs && split_tiles(a, uniform_load(a.seq_lens + q.b)) == 0)
-        ++q.b;
+    for (;;) {
+        while (q.b < a.num_seqs && split_tiles(a, uniform_load(a.seq_lens + q.b)) == 0)
+            ++q.b;
+        if (q.b < a.num_seqs || q.g + 1 >= a.num_kv_heads)
+            break;
+        ++q.g; // every head has the same sequences with tiles
+        q.b = 0;
+    }
     q.n = q.b < a.num_seqs ? uniform_load(a.seq_lens + q.b) : 0;
     return q;
+}
+
+// Partial-state slot of run i's piece of segment (g, b): i + g * B + b.  The
+// runs touching one segment are consecutive, and a run's segments follow
+// each other, so no two (run, segment) pairs share a slot.
+__device__ __forceinline__ int64_t balanced_slot(const DecodeArgs &a, int64_t i, int32_t g,
+                                                 int32_t b)
+{
+    return i + (int64_t)g * a.num_seqs + b;
 }
 
 // Run holding tile x when T tiles are cut into R runs [i*T/R, (i+1)*T/R)
