@@ -457,7 +457,7 @@ def write_traffic_record(bench_line, fetch_csv, write_csv, copy_fetch_csv, copy_
         "partition": cfg["partition"],
         "steps": steps,
         "warmup": warmup,
-        "launches": f"the {steps} back-to-back decode launches bench.py times "
+        "launches": f"the last {steps} of the back-to-back decode launches bench.py times "
                     "(last step's metadata)",
         "kernel_sources": TRAFFIC_SOURCES,
         "kernel_sources_sha256": h.hexdigest(),
