@@ -36,7 +36,6 @@
 #include <mutex>
 #include <type_traits>
 
-#include "append.hpp"
 #include "device.hpp"
 #include "work.hpp"
 
@@ -168,22 +167,47 @@ struct MfmaWave {
         l_run = 0.f;
     }
 
-    // Row (b, g) of k_new / v_new into `nt`, converted as the append does.
-    __device__ void load_new_token(const DecodeArgs &a, int32_t b, int32_t g, int tok,
-                                   NewToken &nt) const
+    // Row (b, g) of k_new / v_new as loaded (q dtype), in tile layout: the
+    // K chunks of the token's row that lane (col, grp) would hold (16-bit
+    // KV: chunk grp + 4 j, 8 dims; FP8: chunk grp + 4 j, 16 dims, as two
+    // 16-byte halves) and the V value of dim 16 t + col.
+    struct RawToken {
+        u32x4 k[KE == 2 ? CH_PER_LANE : 2 * CH_PER_LANE];
+        TQ v[PV_TILES];
+    };
+
+    __device__ void load_token_raw(const DecodeArgs &a, int32_t b, int32_t g, RawToken &rt) const
     {
         const size_t row = ((size_t)b * a.num_kv_heads + g) * D;
         const TQ *kr = static_cast<const TQ *>(a.k_new) + row;
         const TQ *vr = static_cast<const TQ *>(a.v_new) + row;
-        nt.tok = tok;
 #pragma unroll
         for (int j = 0; j < CH_PER_LANE; ++j) {
             const int c = grp + 4 * j; // chunk of the K row this lane holds
             if constexpr (KE == 2) {
-                nt.k[j] = load16(kr + c * 8);
+                rt.k[j] = load16(kr + c * 8);
             } else {
-                const u32x4 lo = load16(kr + c * 16);
-                const u32x4 hi = load16(kr + c * 16 + 8);
+                rt.k[2 * j] = load16(kr + c * 16);
+                rt.k[2 * j + 1] = load16(kr + c * 16 + 8);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < PV_TILES; ++t)
+            rt.v[t] = vr[16 * t + col];
+    }
+
+    // The raw token in the cache's storage format, converted as the append
+    // does (FP8: e4m3 of x * inv, nearest even, saturating).
+    __device__ void finish_token(const DecodeArgs &a, const RawToken &rt, int tok,
+                                 NewToken &nt) const
+    {
+        nt.tok = tok;
+#pragma unroll
+        for (int j = 0; j < CH_PER_LANE; ++j) {
+            if constexpr (KE == 2) {
+                nt.k[j] = rt.k[j];
+            } else {
+                const u32x4 lo = rt.k[2 * j], hi = rt.k[2 * j + 1];
                 const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
                 uint32_t q[4];
 #pragma unroll
@@ -203,11 +227,41 @@ struct MfmaWave {
         }
 #pragma unroll
         for (int t = 0; t < PV_TILES; ++t) {
-            const TQ x = vr[16 * t + col];
             if constexpr (KE == 2)
-                nt.v[t] = __builtin_bit_cast(uint16_t, x);
+                nt.v[t] = __builtin_bit_cast(uint16_t, rt.v[t]);
             else
-                nt.v[t] = f32_to_e4m3(to_f32<QT>(x) * a.v_inv);
+                nt.v[t] = f32_to_e4m3(to_f32<QT>(rt.v[t]) * a.v_inv);
+        }
+    }
+
+    // Stores the token from its tile-layout registers into cache slot
+    // (block blk, offset off): the lanes of column 0 write the K row (chunk
+    // grp + 4 j each), the lanes of group 0 the V values of dims 16 t + col.
+    // The same bytes as store_token writes for the append kernel.
+    __device__ void store_new_token(const DecodeArgs &a, const NewToken &nt, int32_t blk,
+                                    int32_t off, int32_t sh, int32_t g) const
+    {
+        using TK = typename Store<KT>::T;
+        const size_t tile0 = ((size_t)blk * a.num_kv_heads + g) << sh;
+        if (col == 0) {
+            char *kd = reinterpret_cast<char *>(static_cast<TK *>(const_cast<void *>(a.k_cache)) +
+                                                (tile0 * kTile + off) * D);
+#pragma unroll
+            for (int j = 0; j < CH_PER_LANE; ++j)
+                *reinterpret_cast<u32x4 *>(kd + (grp + 4 * j) * 16) = nt.k[j];
+        }
+        if (grp == 0) {
+            TK *vd = static_cast<TK *>(const_cast<void *>(a.v_cache)) +
+                     (tile0 + off / kTile) * D * kTile;
+            const int u = off % kTile;
+#pragma unroll
+            for (int t = 0; t < PV_TILES; ++t) {
+                const int vi = v_tile_index<KE>(u, 16 * t + col);
+                if constexpr (KE == 2)
+                    reinterpret_cast<uint16_t *>(vd)[vi] = (uint16_t)nt.v[t];
+                else
+                    reinterpret_cast<uint8_t *>(vd)[vi] = (uint8_t)nt.v[t];
+            }
         }
     }
 
@@ -406,24 +460,32 @@ struct MfmaWave {
             return out ? 0 : id;
         };
         // The step's token (position t1 - 1) when this range ends the
-        // sequence: checked against its slot, put into the last tile's
-        // registers when that tile is computed, stored after the loop.
+        // sequence.  Its row is loaded before any tile (the addresses need
+        // nothing but b and g); after the first ring has issued its first
+        // tiles' loads, the slot is checked, the token converted and stored
+        // to the cache, so none of this delays the tile stream; when the last
+        // tile is computed the token replaces its slot in the registers.
         bool put = false;
         NewToken nt;
-        int32_t id_last = 0;
+        RawToken rt;
+        int32_t slot = -1, id_last = 0;
         const int32_t off_last = (t1 - 1) & ((kTile << sh) - 1); // in its block
         if (append_here) {
-            const int32_t slot = uniform(((const CI32 *)a.slots)[b]);
+            slot = uniform(((const CI32 *)a.slots)[b]);
             id_last = id_of(last);
-            if (slot >= 0) {
-                if ((uint32_t)id_last >= nblocks || slot != (id_last << sh) * kTile + off_last)
-                    bad = true;
-                else
-                    put = true;
-            }
-            if (put)
-                load_new_token(a, b, g, (t1 - 1) % kTile, nt);
+            load_token_raw(a, b, g, rt);
         }
+        auto after_first_loads = [&]() {
+            if (!append_here || slot < 0)
+                return;
+            if ((uint32_t)id_last >= nblocks || slot != (id_last << sh) * kTile + off_last) {
+                bad = true;
+                return;
+            }
+            put = true;
+            finish_token(a, rt, (t1 - 1) % kTile, nt);
+            store_new_token(a, nt, id_last, off_last, sh, g);
+        };
         // With the hint, the block ids of the first DEPTH tiles are fetched
         // before the split below is known (every range starts with a ring at
         // jb0), so that reading the hint adds no step to the chain before
@@ -434,7 +496,7 @@ struct MfmaWave {
             for (int d = 0; d < DEPTH; ++d)
                 id0[d] = id_of(jb0 + d);
         }
-        auto ring = [&](auto stream, int32_t s0, int32_t s1, bool first) {
+        auto ring = [&](auto stream, int32_t s0, int32_t s1, bool first, bool hook) {
             constexpr bool STREAM = decltype(stream)::value;
             auto id_at = [&](int32_t jb) -> int32_t {
                 return uniform(table[uniform(min(jb, s1) >> sh)]);
@@ -454,6 +516,8 @@ struct MfmaWave {
                 load(checked(HINT && first ? id0[d] : id_at(s0 + d)), s0 + d, T[d]);
             // block id of the next tile to load
             int32_t id_next = HINT && first ? id0[DEPTH - 1] : id_at(s0 + DEPTH - 1);
+            if (hook)
+                after_first_loads();
             int32_t i = 0;
             for (; i + DEPTH <= n; i = uniform(i + DEPTH)) {
 #pragma unroll
@@ -490,19 +554,12 @@ struct MfmaWave {
             shared = min(max(shared, 0), a.max_blocks_per_seq);
             const int32_t split = uniform(min(max(shared << sh, jb0), last + 1));
             if (split > jb0)
-                ring(std::integral_constant<bool, false>{}, jb0, split - 1, true);
+                ring(std::integral_constant<bool, false>{}, jb0, split - 1, true, true);
             if (split <= last)
-                ring(std::integral_constant<bool, true>{}, split, last, split == jb0);
+                ring(std::integral_constant<bool, true>{}, split, last, split == jb0,
+                     split == jb0);
         } else {
-            ring(std::integral_constant<bool, true>{}, jb0, last, false);
-        }
-        if (put) {
-            const size_t row = ((size_t)b * a.num_kv_heads + g) * D;
-            store_token<QT, KT, D>(static_cast<const TQ *>(a.k_new) + row,
-                                   static_cast<const TQ *>(a.v_new) + row,
-                                   const_cast<void *>(a.k_cache), const_cast<void *>(a.v_cache),
-                                   id_last, off_last, sh, g, a.num_kv_heads, a.k_inv, a.v_inv,
-                                   col + 16 * grp);
+            ring(std::integral_constant<bool, true>{}, jb0, last, false, true);
         }
         return !bad;
     }
