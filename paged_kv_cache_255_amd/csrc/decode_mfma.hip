@@ -28,10 +28,11 @@
 //   0   one wave per (sequence, KV head), output written directly;
 //   > 0 one wave per (sequence, KV head, partition of that many tokens),
 //       partial states merged by merge.hip;
-//   balanced: the tiles of all (sequence, KV head) pairs, in order, are cut
-//       into W equal runs, one per wave (W = the waves the GPU holds at
-//       once); a run that covers a whole segment writes the output, the
-//       others leave partial states that merge.hip combines.
+//   balanced: the tiles of all (KV head, sequence) segments, head-major,
+//       are cut into W equal runs, one per wave (W = the waves the GPU holds
+//       at once), each XCD taking one eighth of them in order; a run that
+//       covers a whole segment writes the output, the others leave partial
+//       states that merge.hip combines.
 #include <map>
 #include <mutex>
 #include <type_traits>
