@@ -55,7 +55,7 @@ typedef enum {
     PA_ERR_INVALID_ARG = 1,   /* bad pointer, shape, id or size */
     PA_ERR_OUT_OF_BLOCKS = 2, /* the pool cannot supply the blocks asked for */
     PA_ERR_CAPACITY = 3,      /* a caller-sized buffer is too small */
-    PA_ERR_UNSUPPORTED = 4,   /* valid request this build does not implement */
+    PA_ERR_UNSUPPORTED = 4,   /* valid request the library does not implement */
     PA_ERR_HIP = 5            /* a HIP runtime call or launch failed */
 } pa_status;
 
