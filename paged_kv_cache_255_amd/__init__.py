@@ -353,9 +353,36 @@ def _check_tensor(t, name, nbytes=None):
         raise ValueError(f"{name}: expected {nbytes} bytes, got {t.numel() * t.element_size()}")
 
 
+def _check_i32(t, name, numel=None):
+    """An int32 device tensor (the library reads these as int32_t arrays: a
+    wider integer type would be misread, not rejected, on the device)."""
+    import torch
+    if t.dtype != torch.int32:
+        raise ValueError(f"{name} must be torch.int32, got {t.dtype}")
+    _check_tensor(t, name, None if numel is None else numel * 4)
+
+
+def _check_tables(block_tables, B):
+    """block_tables: int32 [num_seqs][max_blocks_per_seq], contiguous."""
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [num_seqs][max_blocks_per_seq]")
+    _check_i32(block_tables, "block_tables", B * block_tables.shape[1])
+
+
+def _check_lens_tables(seq_lens, block_tables, B):
+    """Types and shapes of both first, then where they live."""
+    import torch
+    for t, nm in [(seq_lens, "seq_lens"), (block_tables, "block_tables")]:
+        if t.dtype != torch.int32:
+            raise ValueError(f"{nm} must be torch.int32, got {t.dtype}")
+    _check_tables(block_tables, B)
+    _check_i32(seq_lens, "seq_lens", B)
+
+
 def pa_cache_append(k, v, k_cache, v_cache, slot_mapping, desc, k_scale=1.0, v_scale=1.0,
                     stream=None):
     T = slot_mapping.numel()
+    _check_i32(slot_mapping, "slot_mapping", T)
     qb, kb = DTYPE_BYTES[desc.q_dtype], DTYPE_BYTES[desc.kv_dtype]
     row = desc.num_kv_heads * desc.head_dim
     cache_bytes = desc.num_blocks * desc.block_size * row * kb
@@ -363,7 +390,6 @@ def pa_cache_append(k, v, k_cache, v_cache, slot_mapping, desc, k_scale=1.0, v_s
         _check_tensor(t, nm, T * row * qb)
     for t, nm in [(k_cache, "k_cache"), (v_cache, "v_cache")]:
         _check_tensor(t, nm, cache_bytes)
-    _check_tensor(slot_mapping, "slot_mapping", T * 4)
     _check(_lib.pa_cache_append(_addr(k), _addr(v), _addr(k_cache), _addr(v_cache),
                                 _addr(slot_mapping), T, ctypes.byref(desc), k_scale, v_scale,
                                 _stream(stream)), "pa_cache_append")
@@ -377,7 +403,7 @@ def pa_copy_blocks(k_cache, v_cache, pairs, desc, stream=None):
         _check_tensor(t, nm, cache_bytes)
     n = pairs.shape[0] if pairs.dim() == 2 else 0
     if n:
-        _check_tensor(pairs, "pairs", n * 8)
+        _check_i32(pairs, "pairs", n * 2)
     _check(_lib.pa_copy_blocks(_addr(k_cache), _addr(v_cache), _addr(pairs) if n else None, n,
                                ctypes.byref(desc), _stream(stream)), "pa_copy_blocks")
 
@@ -395,7 +421,7 @@ def pa_swap_blocks(k_cache, v_cache, host_k, host_v, pairs, desc, to_host, strea
         raise ValueError("host_k / host_v must be pinned host tensors of whole blocks")
     n = pairs.shape[0] if pairs.dim() == 2 else 0
     if n:
-        _check_tensor(pairs, "pairs", n * 8)
+        _check_i32(pairs, "pairs", n * 2)
     _check(_lib.pa_swap_blocks(_addr(k_cache), _addr(v_cache), _addr(host_k), _addr(host_v),
                                hb // block, _addr(pairs) if n else None, n, int(bool(to_host)),
                                ctypes.byref(desc), _stream(stream)), "pa_swap_blocks")
@@ -409,7 +435,7 @@ def pa_decode_workspace_bytes(desc, num_seqs, max_seq_len, partition_size):
 def _per_seq(x, name, B):
     if x is None:
         return None
-    _check_tensor(x, name, B * 4)
+    _check_i32(x, name, B)
     return _addr(x)
 
 
@@ -421,6 +447,7 @@ def pa_decode(q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale, o
               k_scale=1.0, v_scale=1.0, workspace=None, partition_size=PARTITION_NONE,
               stream=None, seq_starts=None, seq_shared=None):
     B = seq_lens.numel()
+    _check_lens_tables(seq_lens, block_tables, B)
     qb, kb = DTYPE_BYTES[desc.q_dtype], DTYPE_BYTES[desc.kv_dtype]
     qrow = desc.num_q_heads * desc.head_dim
     cache_bytes = desc.num_blocks * desc.block_size * desc.num_kv_heads * desc.head_dim * kb
@@ -428,10 +455,6 @@ def pa_decode(q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale, o
     _check_tensor(out, "out", B * qrow * qb)
     for t, nm in [(k_cache, "k_cache"), (v_cache, "v_cache")]:
         _check_tensor(t, nm, cache_bytes)
-    _check_tensor(seq_lens, "seq_lens", B * 4)
-    if block_tables.dim() != 2 or block_tables.shape[0] != B:
-        raise ValueError("block_tables must be [num_seqs][max_blocks_per_seq]")
-    _check_tensor(block_tables, "block_tables")
     ws_bytes = 0
     if workspace is not None:
         _check_tensor(workspace, "workspace")
@@ -448,6 +471,7 @@ def pa_decode_append(q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tabl
                      partition_size=PARTITION_NONE, stream=None, seq_starts=None,
                      seq_shared=None):
     B = seq_lens.numel()
+    _check_lens_tables(seq_lens, block_tables, B)
     qb, kb = DTYPE_BYTES[desc.q_dtype], DTYPE_BYTES[desc.kv_dtype]
     qrow = desc.num_q_heads * desc.head_dim
     krow = desc.num_kv_heads * desc.head_dim
@@ -456,13 +480,9 @@ def pa_decode_append(q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tabl
     _check_tensor(out, "out", B * qrow * qb)
     _check_tensor(k_new, "k_new", B * krow * qb)
     _check_tensor(v_new, "v_new", B * krow * qb)
-    _check_tensor(slot_mapping, "slot_mapping", B * 4)
+    _check_i32(slot_mapping, "slot_mapping", B)
     for t, nm in [(k_cache, "k_cache"), (v_cache, "v_cache")]:
         _check_tensor(t, nm, cache_bytes)
-    _check_tensor(seq_lens, "seq_lens", B * 4)
-    if block_tables.dim() != 2 or block_tables.shape[0] != B:
-        raise ValueError("block_tables must be [num_seqs][max_blocks_per_seq]")
-    _check_tensor(block_tables, "block_tables")
     ws_bytes = 0
     if workspace is not None:
         _check_tensor(workspace, "workspace")
@@ -482,8 +502,15 @@ def pa_decode_partials(q, k_cache, v_cache, block_tables, seq_lens, max_seq_len,
     writes the rows of the (sequence, KV head) segments one work item covers
     whole to `out`; pa_decode_merge writes the others."""
     B = seq_lens.numel()
+    _check_lens_tables(seq_lens, block_tables, B)
+    qb, kb = DTYPE_BYTES[desc.q_dtype], DTYPE_BYTES[desc.kv_dtype]
+    qrow = desc.num_q_heads * desc.head_dim
+    cache_bytes = desc.num_blocks * desc.block_size * desc.num_kv_heads * desc.head_dim * kb
+    _check_tensor(q, "q", B * qrow * qb)
+    _check_tensor(out, "out", B * qrow * qb)
+    for t, nm in [(k_cache, "k_cache"), (v_cache, "v_cache")]:
+        _check_tensor(t, nm, cache_bytes)
     _check_tensor(workspace, "workspace")
-    _check_tensor(out, "out")
     _check(_lib.pa_decode_partials(_addr(q), _addr(k_cache), _addr(v_cache), _addr(block_tables),
                                    block_tables.shape[1], _addr(seq_lens),
                                    _starts(seq_starts, B), _per_seq(seq_shared, "seq_shared", B),
@@ -496,8 +523,10 @@ def pa_decode_partials(q, k_cache, v_cache, block_tables, seq_lens, max_seq_len,
 def pa_decode_merge(seq_lens, max_blocks_per_seq, max_seq_len, out, desc, workspace,
                     partition_size, stream=None):
     B = seq_lens.numel()
+    qrow = desc.num_q_heads * desc.head_dim
+    _check_i32(seq_lens, "seq_lens", B)
     _check_tensor(workspace, "workspace")
-    _check_tensor(out, "out")
+    _check_tensor(out, "out", B * qrow * DTYPE_BYTES[desc.q_dtype])
     _check(_lib.pa_decode_merge(_addr(seq_lens), B, max_blocks_per_seq, max_seq_len, _addr(out),
                                 _addr(workspace), workspace.numel() * workspace.element_size(),
                                 partition_size, ctypes.byref(desc), _stream(stream)),

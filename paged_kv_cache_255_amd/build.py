@@ -31,7 +31,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC, "-Wall"]
 # VALU ops, which cannot read AGPRs, so AGPR accumulators cost a copy of
 # every accumulator per block.
 DEVICE_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
-                "-packed-fp32-ops", "-munsafe-fp-atomics", "-mllvm", "-amdgpu-mfma-vgpr-form"]
+                "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def _hipcc():

@@ -158,8 +158,12 @@ __device__ __forceinline__ int32_t effective_runs(int64_t T, int32_t W)
     return (int32_t)(T < (int64_t)W ? T : (int64_t)W);
 }
 
-// XCDs of the GPU; the dispatcher hands workgroups to them in turn
-// (workgroup w runs on XCD w mod 8).
+// XCDs (accelerator complex dies) of an MI355X.  The hardware dispatcher
+// hands a launch's workgroups to the XCDs round-robin, so workgroup w runs on
+// XCD w mod 8.  That order is how the dispatcher behaves, not something HIP
+// promises: the run placement below relies on it for speed only (which L2
+// holds which tiles).  If the order differed, every run would still be done
+// once by one wave, and the results would not change.
 constexpr int32_t kXcds = 8;
 
 // Run of wave v (0..3) of workgroup w among W waves.  Each XCD gets one

@@ -340,3 +340,31 @@ def test_decode_partials_needs_out():
                                     ctypes.byref(desc), None)
     assert st == pa.ERR_INVALID_ARG
     assert "null" in pa.pa_last_error()
+
+
+def test_binding_refuses_wide_integer_metadata():
+    """The library reads block tables, lengths and slots as int32_t arrays;
+    an int64 tensor (torch's default for integer lists) would be misread on
+    the device, so the binding refuses it before any pointer is passed."""
+    import torch
+    desc = pa.kv_desc(8, 2, 128, 16, "bf16", "bf16")
+    B = 2
+    q = torch.zeros(B, 8, 128, dtype=torch.bfloat16)
+    kc = torch.zeros(16 * 2 * 16 * 128, dtype=torch.bfloat16)
+    lens32 = torch.tensor([3, 5], dtype=torch.int32)
+    wide = torch.tensor([[0, 1], [2, 3]], dtype=torch.int64)
+    ws = torch.zeros(1 << 20, dtype=torch.uint8)
+    for call in (
+        lambda t, n: pa.pa_decode(q, kc, kc, t, n, 32, 0.1, q, desc),
+        lambda t, n: pa.pa_decode_partials(q, kc, kc, t, n, 32, 0.1, q, desc, ws,
+                                           pa.PARTITION_BALANCED),
+        lambda t, n: pa.pa_decode_append(q, q, q, lens32, kc, kc, t, n, 32, 0.1, q, desc),
+    ):
+        with pytest.raises(ValueError, match="int32"):
+            call(wide, lens32)
+        with pytest.raises(ValueError, match="int32"):
+            call(wide.to(torch.int32), lens32.to(torch.int64))
+        with pytest.raises(ValueError, match=r"\[num_seqs\]\[max_blocks_per_seq\]"):
+            call(wide.to(torch.int32).reshape(-1), lens32)
+    with pytest.raises(ValueError, match="int32"):
+        pa.pa_cache_append(q, q, kc, kc, torch.tensor([1, 2]), desc)
