@@ -85,29 +85,55 @@ def test_parity_config1_tiny_fp32():
 
 
 # -- full sizes, in the launch configuration the benchmark times --------------
+# Every output row is compared with the oracle, and every cache block byte for
+# byte (the oracle's fp64 work at full size: config 2 about 1.3 GFLOP, config
+# 4 about 10, config 5 about 17, two layers of config 3 about 1.3).
 def test_parity_config2_full():
     w = workloads.config(2)
     run_and_check(w)
 
 
-def test_parity_config4_full_sampled():
+def test_parity_config4_full():
     w = workloads.config(4)
-    rng = np.random.default_rng(4)
-    only = sorted(set(rng.choice(w.num_seqs, size=6, replace=False).tolist()) | {0, w.num_seqs - 1})
-    run_and_check(w, only=only)
+    run_and_check(w)
 
 
-def test_parity_config5_full_sampled():
+def test_parity_config5_full():
     w = workloads.config(5)
-    rows = [(b, h) for b in (1, 3) for h in (0, 7, 8, 33, 63)]
-    run_and_check(w, only=[1, 3], rows=rows)
+    run_and_check(w)
 
 
-def test_parity_config3_full_sampled_layers():
+def test_parity_config3_full_two_layers():
+    """Two of the 40 layers (the first and the last, each with its own block
+    permutation): every row, and the whole pool of each."""
     w = workloads.config(3)
     for layer in (0, w.num_layers - 1):
-        rows = [(b, h) for b in (0, 5) for h in (0, 19, 39)]
-        run_and_check(w, layer, only=[0, 5], rows=rows)
+        run_and_check(w, layer)
+
+
+@pytest.mark.parametrize("cid", [2, 5])
+def test_decode_append_full_against_oracle(cid):
+    """The call bench.py times, in its launch: pa_decode_append with the
+    balanced split on the MFMA kernel and no sharing hint, at full size
+    (config 2: about 41 tiles per run; config 5: about 260), where runs span
+    several segments and the appended token's tile sits deep inside a run's
+    main loop.  Every output row against the oracle, and the whole pool byte
+    for byte against the oracle's append."""
+    w = workloads.config(cid)
+    say(f"[case] decode_append full {w.name}")
+    inp = Inputs(w, 0)
+    g = GpuStep(w, 0, inp, partition=pa.PARTITION_BALANCED, kernel=pa.KERNEL_MFMA)
+    o = OracleStep(w, 0, inp)
+    np.testing.assert_array_equal(g.tables, o.tables)
+    np.testing.assert_array_equal(g.lens, o.lens)
+    np.testing.assert_array_equal(g.step_slots, o.step_slots)
+    g.append_prefill()
+    out = g.decode_append(out=torch.full_like(inp.q, 7.0))
+    torch.cuda.synchronize()
+    compare_cache_blocks(g.k_cache, o.k_cache, w, None)
+    compare_cache_blocks(g.v_cache, o.v_cache, w, None)
+    err = check_close(to_f64(out), o.decode(), w.kv_dtype, w.q_dtype)
+    say(f"[ok] {w.name} decode_append err={err:.3g}")
 
 
 # -- exhaustive FP8 decode through the decode path ----------------------------

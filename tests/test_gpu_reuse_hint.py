@@ -77,13 +77,9 @@ def test_hint_keeps_every_bit(size, kernel, part):
     assert torch.equal(a.k_cache.view(torch.uint8), b.k_cache.view(torch.uint8))
     assert torch.equal(a.v_cache.view(torch.uint8), b.v_cache.view(torch.uint8))
     if size == "full":
-        only = [0, 77, 255]
-        o = OracleStep(w, 0, inp, only=only)
-        rows = [(bb, h) for bb in only for h in (0, 13, 31)]
-        out = to_f64(got)
-        err = check_close(np.stack([out[bb, h] for (bb, h) in rows]), o.decode(rows=rows),
-                          w.kv_dtype, w.q_dtype)
-        say(f"[ok] sampled rows err={err:.3g}")
+        o = OracleStep(w, 0, inp)
+        err = check_close(to_f64(got2), o.decode(), w.kv_dtype, w.q_dtype)
+        say(f"[ok] every row err={err:.3g}")
 
 
 def test_hint_counts_out_of_range_are_clamped():
