@@ -62,6 +62,12 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--read-ceiling", action="store_true",
+                    help="only sweep the read-ceiling probe (pa_read_probe: loads in flight, "
+                         "workgroups, nontemporal hint) over a 4 GiB buffer, print one JSON "
+                         "line per setting and exit")
+    ap.add_argument("--no-probe", action="store_true",
+                    help="skip the read-ceiling probe in a decode run")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain device-to-device copies of 1 GiB (calibrates the HBM "
                          "byte counters a profiler reports) and exit")
@@ -105,6 +111,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(torch)
+        return
+    if args.read_ceiling:
+        read_ceiling_sweep(torch, pa, args)
         return
     if args.feature:
         FEATURES[args.feature](args, torch, pa, workloads, execute_plan)
@@ -265,6 +274,17 @@ def main():
     ms_per_step = ms_total / K
     last = W + K - 1
 
+    # pass 1b: the same K steps again, an event recorded after each one, for
+    # the spread of per-step times (the events themselves may add a little
+    # to each step, so the headline stays pass 1's)
+    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    step_ev[0].record()
+    for j, i in enumerate(range(W, W + K)):
+        step(i)
+        step_ev[j + 1].record()
+    torch.cuda.synchronize()
+    step_us = np.array([step_ev[j].elapsed_time(step_ev[j + 1]) * 1e3 for j in range(K)])
+
     # pass 2: the decode kernel alone (no append, no merge), K * L launches back
     # to back on the last step's metadata, rotating over the replicas, between
     # two events: an event pair around each single launch would add the
@@ -297,6 +317,7 @@ def main():
     k_end.record()
     torch.cuda.synchronize()
     kern_us = k_start.elapsed_time(k_end) * 1e3 / (K * L)
+    probe = None if args.no_probe else read_probe(torch, pa, dev, reps=max(K, 10))
 
     # algorithmic KV bytes: step i decodes lens0 + i + 1 tokens per sequence
     tokens = np.array([int((lens0 + i + 1).sum()) for i in range(W, W + K)], dtype=np.float64)
@@ -304,6 +325,9 @@ def main():
     gbs = bytes_steps.sum() / (ms_total * 1e-3) / 1e9
     launch_bytes = int((lens0 + last + 1).sum()) * step_bytes_1 / L  # one layer, last step
     kern_gbs = launch_bytes / (kern_us * 1e-6) / 1e9
+    p10, p50, p90 = (float(np.percentile(step_us, x)) for x in (10, 50, 90))
+    log(f"[bench] per-step (events after each step): median {p50:.2f} us, p10 {p10:.2f}, "
+        f"p90 {p90:.2f}")
     log(f"[bench] {K} steps: {ms_per_step * 1e3:.2f} us/step (wall {wall / K * 1e6:.2f} us), "
         f"{gbs:.1f} GB/s over whole steps; decode kernel {kern_us:.2f} us per launch "
         f"({K * L} back to back), {kern_gbs:.1f} GB/s = {kern_gbs / HBM_PEAK_GBS * 100:.1f}% "
@@ -331,6 +355,10 @@ def main():
         "warmup": W,
         "ms_per_step": round(ms_per_step, 5),
         "us_per_step": round(ms_per_step * 1e3, 2),
+        "us_per_step_dist": {"median": round(p50, 2), "p10": round(p10, 2),
+                             "p90": round(p90, 2),
+                             "how": "second pass of the same K steps, an event after each"},
+        "gbs_at_median_step": round(float(bytes_steps.mean()) / (p50 * 1e-6) / 1e9, 1),
         "steps_per_s": round(1e3 / ms_per_step, 1),
         "pct_of_peak": round(gbs / HBM_PEAK_GBS * 100, 2),
         "higher_is_better": True,
@@ -361,7 +389,11 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(w.name, partition, K, W) if bs == 16 else None,
+            "probe_gbs": None if probe is None else probe["gbs"],
+            "frac_of_probe": None if probe is None else round(kern_gbs / probe["gbs"], 4),
+            "probe": probe,
+            "traffic": (measured_traffic(w.name, partition, int(launch_bytes), no_hint)
+                        if bs == 16 else None),
             "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE x1)",
             "algorithmic_bytes": int(launch_bytes),
             "kernel": ("decode_valu_kernel" if "valu" in kname else
@@ -374,11 +406,12 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def measured_traffic(workload, partition, steps, warmup):
+def measured_traffic(workload, partition, launch_bytes, no_hint):
     """HBM bytes per decode launch from the committed rocprofv3 counter runs
-    (profiles/decode_mfma_balanced_<workload>.traffic.json), if they were taken
-    for this launch configuration and the kernel's sources have not changed
-    since; else None."""
+    (profiles/decode_mfma_balanced_<workload>.traffic.json), if they were
+    taken for this launch (same workload, launch mode, hint and algorithmic
+    bytes per launch, which fixes every sequence length) and the kernel's
+    sources have not changed since; else None."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"decode_mfma_balanced_{workload}.traffic.json")
     try:
@@ -391,7 +424,8 @@ def measured_traffic(workload, partition, steps, warmup):
     except (OSError, ValueError, KeyError):
         return None
     same = (rec.get("workload") == workload and rec.get("partition") == partition and
-            rec.get("steps") == steps and rec.get("warmup") == warmup and
+            rec.get("algorithmic_bytes_per_launch") == launch_bytes and
+            rec.get("reuse_hint", False) == (not no_hint) and
             rec.get("kernel_sources_sha256") == h.hexdigest())
     return rec["hbm_bytes_per_launch"] if same else None
 
@@ -455,6 +489,7 @@ def write_traffic_record(bench_line, fetch_csv, write_csv, copy_fetch_csv, copy_
         "kernel": roof["kernel"],
         "workload": cfg["workload_name"],
         "partition": cfg["partition"],
+        "reuse_hint": cfg.get("reuse_hint", False),
         "steps": steps,
         "warmup": warmup,
         "launches": f"the last {steps} of the back-to-back decode launches bench.py times "
@@ -680,35 +715,42 @@ def copy_calibration(torch):
 
 
 def cpu_baseline(w, k_cache, v_cache, q, tables, lens, nblocks, ks, vs, target_s):
-    """The CPU oracle (fp64 C, all host threads up to 16) on the first sequences
-    of the last timed step, sized to about `target_s` seconds."""
+    """The CPU oracle (fp64 C) on the last timed step's sequences, sized to
+    about `target_s` seconds, with one thread per core this process may run
+    on (os.sched_getaffinity), then with one thread on about a third of that
+    time."""
     import oracle
     import workloads
-    threads = min(16, len(os.sched_getaffinity(0)))
     kh = workloads.storage(k_cache)
     vh = workloads.storage(v_cache)
     qh = workloads.storage(q)
     eb = {"f32": 4, "f16": 2, "bf16": 2, "e4m3": 1}[w.kv_dtype]
     args = dict(num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
                 block_size=w.block_size, num_blocks=nblocks, q_dtype=w.q_dtype,
-                kv_dtype=w.kv_dtype, scale=w.scale, k_scale=ks, v_scale=vs, nthreads=threads)
+                kv_dtype=w.kv_dtype, scale=w.scale, k_scale=ks, v_scale=vs)
 
-    def run(nseq):
+    def run(nseq, threads):
         rows = [(b, h) for b in range(nseq) for h in range(w.num_q_heads)]
         t0 = time.perf_counter()
-        oracle.decode(qh, kh, vh, tables, lens, rows=rows, **args)
+        oracle.decode(qh, kh, vh, tables, lens, rows=rows, nthreads=threads, **args)
         return time.perf_counter() - t0
 
-    # as many sequences as fit in target_s; if the whole batch is faster than
-    # that, the whole batch repeated until about target_s have passed
-    t1 = run(1)
-    nseq = int(max(1, min(len(lens), target_s / max(t1, 1e-6))))
-    t = run(nseq)
-    reps = 1
-    while t < 0.8 * target_s:
-        t += run(nseq)
-        reps += 1
-    nbytes = reps * int(lens[:nseq].sum()) * w.num_kv_heads * w.head_dim * 2 * eb
+    def timed(threads, budget):
+        # as many sequences as fit in the budget; if the whole batch is faster
+        # than that, the whole batch repeated until about the budget has passed
+        t1 = run(1, threads)
+        nseq = int(max(1, min(len(lens), budget / max(t1, 1e-6))))
+        t = run(nseq, threads)
+        reps = 1
+        while t < 0.8 * budget:
+            t += run(nseq, threads)
+            reps += 1
+        nbytes = reps * int(lens[:nseq].sum()) * w.num_kv_heads * w.head_dim * 2 * eb
+        return nbytes / t / 1e9, nseq, reps, t
+
+    cores = len(os.sched_getaffinity(0))
+    gbs, nseq, reps, t = timed(cores, target_s)
+    gbs1, nseq1, reps1, t_1 = timed(1, target_s / 3)
     model = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
@@ -718,11 +760,46 @@ def cpu_baseline(w, k_cache, v_cache, q, tables, lens, nblocks, ks, vs, target_s
                     break
     except OSError:
         pass
-    return {"value": round(nbytes / t / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle", "cpu_model": model,
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores,
+            "value_1_thread": round(gbs1, 4), "kind": "oracle", "cpu_model": model,
             "sample": f"{nseq} of {len(lens)} sequences ({int(lens[:nseq].sum())} tokens, all "
                       f"{w.num_q_heads} q heads) of the last timed step, {reps} pass(es), fp64 C "
-                      f"oracle, {t:.1f} s"}
+                      f"oracle, {cores} threads, {t:.1f} s; one thread: {nseq1} sequences, "
+                      f"{reps1} pass(es), {t_1:.1f} s"}
+
+
+def read_probe(torch, pa, dev, reps, loads=8, wgs=None, nontemporal=True, one_per_cu=True,
+               nbytes=4 << 30):
+    """GB/s of pa_read_probe over a buffer of nbytes: `reps` launches back to
+    back between two events.  Defaults: the setting that reads fastest on
+    MI355X (8 loads in flight per lane, one workgroup per CU, nontemporal)."""
+    if wgs is None:
+        wgs = torch.cuda.get_device_properties(dev).multi_processor_count
+    buf = torch.ones(nbytes // 2, dtype=torch.int16, device=dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    ms = _time_launches(torch, lambda: pa.pa_read_probe(buf, loads, wgs, sink, nontemporal,
+                                                         one_per_cu), reps)
+    del buf
+    return {"gbs": round(nbytes / (ms * 1e-3) / 1e9, 1), "loads_in_flight": loads,
+            "workgroups": wgs, "nontemporal": nontemporal, "one_wg_per_cu": one_per_cu,
+            "bytes": nbytes, "us": round(ms * 1e3, 1)}
+
+
+def read_ceiling_sweep(torch, pa, args):
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    best = None
+    for nt in (True, False):
+        for loads in (4, 8, 16):
+            for mult, one in ((1, True), (2, False), (4, False), (16, False)):
+                r = read_probe(torch, pa, dev, reps=20, loads=loads, wgs=cus * mult,
+                               nontemporal=nt, one_per_cu=one)
+                r["frac_of_peak"] = round(r["gbs"] / HBM_PEAK_GBS, 4)
+                print(json.dumps({"read_probe": r}), flush=True)
+                if best is None or r["gbs"] > best["gbs"]:
+                    best = r
+    print(json.dumps({"read_ceiling_best": best}), flush=True)
 
 
 if __name__ == "__main__":

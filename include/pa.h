@@ -436,6 +436,27 @@ pa_status pa_decode_merge(const int32_t *seq_lens, int32_t num_seqs, int32_t max
                           void *stream);
 
 /* Message describing the last failure on this thread ("" if none). */
+/* ------------------------------------------------------------------------ */
+/* Measurement.                                                             */
+/* ------------------------------------------------------------------------ */
+
+/* Read ceiling of the device: one launch that reads the `bytes` bytes at buf
+ * (device memory, 16-byte aligned, a multiple of 16 bytes) once, 16 bytes per
+ * lane per load, `loads_in_flight` (4, 8 or 16) loads issued before their
+ * values are used, over `workgroups` workgroups of 256 threads, with the
+ * nontemporal hint when `nontemporal` is non-zero, and, when `one_per_cu` is
+ * non-zero, an LDS request that lets a compute unit hold one workgroup (one
+ * wave per SIMD, as the balanced decode launch runs).  The values are folded
+ * and nothing is written except, at most, one word at `sink` (device memory,
+ * 4 bytes).  The rate it reaches is the practical roof of a kernel whose time
+ * is its reads: decode is bound by how fast the cache is read (vaibhawkumar.in,
+ * "Why fragmentation matters more than bandwidth").  Asynchronous on
+ * `stream`; PA_ERR_INVALID_ARG for the shapes above, PA_ERR_HIP if the launch
+ * fails. */
+pa_status pa_read_probe(const void *buf, size_t bytes, int32_t loads_in_flight,
+                        int32_t workgroups, int32_t nontemporal, int32_t one_per_cu, void *sink,
+                        void *stream);
+
 const char *pa_last_error(void);
 
 #ifdef __cplusplus

@@ -112,6 +112,7 @@ _SIGS = {
     "pa_prefix_match": (ctypes.c_int, [_P, _I32, _P, _I32, _P]),
     "pa_prefix_evict": (ctypes.c_int, [_P, _I32, _P]),
     "pa_copy_blocks": (ctypes.c_int, [_P, _P, _P, _I32, _P, _P]),
+    "pa_read_probe": (ctypes.c_int, [_P, ctypes.c_size_t, _I32, _I32, _I32, _I32, _P, _P]),
     "pa_last_error": (ctypes.c_char_p, []),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -531,6 +532,19 @@ def pa_decode_merge(seq_lens, max_blocks_per_seq, max_seq_len, out, desc, worksp
                                 _addr(workspace), workspace.numel() * workspace.element_size(),
                                 partition_size, ctypes.byref(desc), _stream(stream)),
            "pa_decode_merge")
+
+
+def pa_read_probe(buf, loads_in_flight, workgroups, sink, nontemporal=True, one_per_cu=True,
+                  stream=None):
+    """One read of the whole device tensor `buf` (see pa.h); sink: a device
+    tensor of at least 4 bytes."""
+    _check_tensor(buf, "buf")
+    _check_tensor(sink, "sink")
+    if sink.numel() * sink.element_size() < 4:
+        raise ValueError("sink must hold at least 4 bytes")
+    _check(_lib.pa_read_probe(_addr(buf), buf.numel() * buf.element_size(), loads_in_flight,
+                              workgroups, int(bool(nontemporal)), int(bool(one_per_cu)),
+                              _addr(sink), _stream(stream)), "pa_read_probe")
 
 
 def pa_last_error():

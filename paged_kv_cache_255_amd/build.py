@@ -21,7 +21,7 @@ OBJDIR = os.path.join(ROOT, "_build", "libpa")
 LIB = os.path.join(HERE, "libpa.so")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["append.hip", "decode_valu.hip", "decode_mfma.hip", "merge.hip"]
+HIP_SOURCES = ["append.hip", "decode_valu.hip", "decode_mfma.hip", "merge.hip", "probe.hip"]
 HOST_HIP_API = ["api.cpp"]           # host code that calls the HIP runtime
 HOST_ONLY = ["pool.cpp", "errors.cpp"]
 

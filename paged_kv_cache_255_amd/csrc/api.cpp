@@ -33,6 +33,8 @@ hipError_t launch_swap_blocks(const void *src_k, const void *src_v, void *dst_k,
 hipError_t launch_copy_blocks(void *k_cache, void *v_cache, const int32_t *pairs,
                               int32_t num_pairs, int64_t block_bytes, int32_t num_blocks,
                               hipStream_t s);
+hipError_t launch_read_probe(const void *buf, int64_t pieces, int32_t loads, int32_t wgs,
+                             bool stream, bool one_per_cu, uint32_t *sink, hipStream_t s);
 
 namespace {
 
@@ -213,6 +215,29 @@ pa_status pa_swap_blocks(void *k_cache, void *v_cache, void *host_k, void *host_
                                                 static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return hip_fail(e, "swap launch");
+    return PA_OK;
+}
+
+pa_status pa_read_probe(const void *buf, size_t bytes, int32_t loads_in_flight,
+                        int32_t workgroups, int32_t nontemporal, int32_t one_per_cu, void *sink,
+                        void *stream)
+{
+    if (!buf || !sink)
+        return fail(PA_ERR_INVALID_ARG, "null pointer");
+    if (bytes == 0 || bytes % 16 != 0 || reinterpret_cast<uintptr_t>(buf) % 16 != 0)
+        return fail(PA_ERR_INVALID_ARG, "buffer must be 16-byte aligned, a positive multiple "
+                                        "of 16 bytes");
+    if (loads_in_flight != 4 && loads_in_flight != 8 && loads_in_flight != 16)
+        return fail(PA_ERR_INVALID_ARG, "loads_in_flight must be 4, 8 or 16");
+    if (workgroups < 1 || workgroups > (1 << 20))
+        return fail(PA_ERR_INVALID_ARG, "workgroups must be in [1, 2^20]");
+    clear_stale_hip_error();
+    hipError_t e = launch_read_probe(buf, (int64_t)(bytes / 16), loads_in_flight, workgroups,
+                                     nontemporal != 0, one_per_cu != 0,
+                                     static_cast<uint32_t *>(sink),
+                                     static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "read probe launch");
     return PA_OK;
 }
 
