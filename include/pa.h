@@ -435,7 +435,6 @@ pa_status pa_decode_merge(const int32_t *seq_lens, int32_t num_seqs, int32_t max
                           size_t workspace_bytes, int32_t partition_size, const pa_kv_desc *desc,
                           void *stream);
 
-/* Message describing the last failure on this thread ("" if none). */
 /* ------------------------------------------------------------------------ */
 /* Measurement.                                                             */
 /* ------------------------------------------------------------------------ */
@@ -457,6 +456,44 @@ pa_status pa_read_probe(const void *buf, size_t bytes, int32_t loads_in_flight,
                         int32_t workgroups, int32_t nontemporal, int32_t one_per_cu, void *sink,
                         void *stream);
 
+/* ------------------------------------------------------------------------ */
+/* Allocation-free decode step.                                             */
+/* ------------------------------------------------------------------------ */
+
+/* Scratch the library holds on each GPU for pa_decode_append_noalloc. */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/* For callers that cannot allocate device memory at the time of the call:
+ * code being captured into a HIP graph, tight serving loops, or harnesses
+ * that forbid hipMalloc.  The same step as pa_decode_append, with the same
+ * arguments except the workspace: the partial softmax states of the
+ * partitioned modes go to a scratch array of PA_NOALLOC_SCRATCH_BYTES that the
+ * library holds in each GPU's memory from its first use on that GPU until the
+ * process ends.  The call allocates and frees nothing (no hipMalloc, hipFree
+ * or allocating library routine); the caller still passes every input and
+ * output.  The scratch needs no initial contents.
+ *   Limit: PA_ERR_CAPACITY, before anything is launched, when
+ *   pa_decode_workspace_bytes(desc, num_seqs, max_seq_len, partition_size)
+ *   exceeds PA_NOALLOC_SCRATCH_BYTES (with PA_PARTITION_BALANCED that holds
+ *   up to about 7,000 (sequence, KV head) pairs at group 4 and head_dim 128);
+ *   PA_PARTITION_NONE needs no scratch.
+ *   Sharing: every call on one GPU uses that GPU's one scratch array, and it
+ *   keeps the last call's contents.  Calls that may overlap on one GPU (on
+ *   different streams, or from different threads) race on it and give wrong
+ *   results; issue them on one stream, or use pa_decode_append with a
+ *   workspace of their own.
+ * Errors otherwise as for pa_decode_append, plus PA_ERR_HIP if the scratch's
+ * device address cannot be found. */
+pa_status pa_decode_append_noalloc(const void *q, const void *k_new, const void *v_new,
+                                   const int32_t *slot_mapping, void *k_cache, void *v_cache,
+                                   const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t *seq_lens, const int32_t *seq_starts,
+                                   const int32_t *seq_shared, int32_t num_seqs,
+                                   int32_t max_seq_len, float scale, float k_scale, float v_scale,
+                                   void *out, int32_t partition_size, const pa_kv_desc *desc,
+                                   void *stream);
+
+/* Message describing the last failure on this thread ("" if none). */
 const char *pa_last_error(void);
 
 #ifdef __cplusplus

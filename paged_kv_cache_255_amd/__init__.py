@@ -39,6 +39,7 @@ DTYPE_BYTES = {F32: 4, F16: 2, BF16: 2, FP8_E4M3: 1}
 # kernel choice and partitioning
 KERNEL_AUTO, KERNEL_VALU, KERNEL_MFMA = 0, 1, 2
 PARTITION_NONE, PARTITION_BALANCED = 0, -1
+NOALLOC_SCRATCH_BYTES = 16 << 20  # PA_NOALLOC_SCRATCH_BYTES
 
 
 class PaError(RuntimeError):
@@ -112,6 +113,9 @@ _SIGS = {
     "pa_prefix_match": (ctypes.c_int, [_P, _I32, _P, _I32, _P]),
     "pa_prefix_evict": (ctypes.c_int, [_P, _I32, _P]),
     "pa_copy_blocks": (ctypes.c_int, [_P, _P, _P, _I32, _P, _P]),
+    "pa_decode_append_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P,
+                                                _I32, _I32, ctypes.c_float, ctypes.c_float,
+                                                ctypes.c_float, _P, _I32, _P, _P]),
     "pa_read_probe": (ctypes.c_int, [_P, ctypes.c_size_t, _I32, _I32, _I32, _I32, _P, _P]),
     "pa_last_error": (ctypes.c_char_p, []),
 }
@@ -494,6 +498,33 @@ def pa_decode_append(q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tabl
                                  _per_seq(seq_shared, "seq_shared", B), B, max_seq_len, scale, k_scale, v_scale, _addr(out),
                                  _addr(workspace), ws_bytes, partition_size, ctypes.byref(desc),
                                  _stream(stream)), "pa_decode_append")
+
+
+def pa_decode_append_noalloc(q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables,
+                             seq_lens, max_seq_len, scale, out, desc, k_scale=1.0, v_scale=1.0,
+                             partition_size=PARTITION_NONE, stream=None, seq_starts=None,
+                             seq_shared=None):
+    """pa_decode_append with the partial states in the library's per-GPU
+    scratch instead of a caller workspace (see pa.h)."""
+    B = seq_lens.numel()
+    _check_lens_tables(seq_lens, block_tables, B)
+    qb, kb = DTYPE_BYTES[desc.q_dtype], DTYPE_BYTES[desc.kv_dtype]
+    qrow = desc.num_q_heads * desc.head_dim
+    krow = desc.num_kv_heads * desc.head_dim
+    cache_bytes = desc.num_blocks * desc.block_size * desc.num_kv_heads * desc.head_dim * kb
+    _check_tensor(q, "q", B * qrow * qb)
+    _check_tensor(out, "out", B * qrow * qb)
+    _check_tensor(k_new, "k_new", B * krow * qb)
+    _check_tensor(v_new, "v_new", B * krow * qb)
+    _check_i32(slot_mapping, "slot_mapping", B)
+    for t, nm in [(k_cache, "k_cache"), (v_cache, "v_cache")]:
+        _check_tensor(t, nm, cache_bytes)
+    _check(_lib.pa_decode_append_noalloc(
+        _addr(q), _addr(k_new), _addr(v_new), _addr(slot_mapping), _addr(k_cache),
+        _addr(v_cache), _addr(block_tables), block_tables.shape[1], _addr(seq_lens),
+        _starts(seq_starts, B), _per_seq(seq_shared, "seq_shared", B), B, max_seq_len, scale,
+        k_scale, v_scale, _addr(out), partition_size, ctypes.byref(desc), _stream(stream)),
+        "pa_decode_append_noalloc")
 
 
 def pa_decode_partials(q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale, out,

@@ -261,6 +261,38 @@ size_t pa_decode_workspace_bytes(const pa_kv_desc *desc, int32_t num_seqs, int32
 
 namespace {
 
+// Partial-state scratch of pa_decode_append_noalloc: one array in each GPU's
+// memory, for the life of the process.  In host code `scratch` names a host
+// stand-in, never the device memory: the device address comes from
+// hipGetSymbolAddress, once per device (with that device current), and only
+// that address is passed on.
+constexpr size_t kNoallocScratchBytes = PA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+pa_status noalloc_scratch(void **out)
+{
+    static std::mutex mu;
+    static std::map<int, void *> addr; // device -> address of its scratch
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "no current device for the allocation-free scratch");
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = addr.find(dev);
+    if (it == addr.end()) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr) {
+            (void)hipGetLastError();
+            return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                            "device address of the allocation-free scratch");
+        }
+        it = addr.emplace(dev, p).first;
+    }
+    *out = it->second;
+    return PA_OK;
+}
+
 enum Phase { kAll, kPartials, kMerge };
 
 // The step's new tokens when pa_decode_append is the caller (else all null).
@@ -446,6 +478,50 @@ pa_status pa_decode_append(const void *q, const void *k_new, const void *v_new,
     return decode_impl(kAll, q, k_cache, v_cache, block_tables, max_blocks_per_seq, seq_lens,
                        seq_starts, seq_shared, num_seqs, max_seq_len, scale, k_scale, v_scale,
                        out, workspace, workspace_bytes, partition_size, desc, stream, nt);
+}
+
+pa_status pa_decode_append_noalloc(const void *q, const void *k_new, const void *v_new,
+                                   const int32_t *slot_mapping, void *k_cache, void *v_cache,
+                                   const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t *seq_lens, const int32_t *seq_starts,
+                                   const int32_t *seq_shared, int32_t num_seqs,
+                                   int32_t max_seq_len, float scale, float k_scale, float v_scale,
+                                   void *out, int32_t partition_size, const pa_kv_desc *desc,
+                                   void *stream)
+{
+    pa_status st = check_desc(desc);
+    if (st != PA_OK)
+        return st;
+    if (num_seqs > 0 && !slot_mapping)
+        return fail(PA_ERR_INVALID_ARG, "null pointer");
+    void *ws = nullptr;
+    size_t ws_bytes = 0;
+    if (num_seqs > 0 && partition_size != PA_PARTITION_NONE) {
+        const size_t need =
+            pa_decode_workspace_bytes(desc, num_seqs, max_seq_len, partition_size);
+        if (need == 0)
+            return fail(PA_ERR_INVALID_ARG, "bad partition_size or shape (or no device to size "
+                                            "the balanced split for)");
+        if (need > kNoallocScratchBytes) {
+            char m[160];
+            std::snprintf(m, sizeof m,
+                          "this call needs %zu bytes of partial states; the allocation-free "
+                          "entry point holds %zu",
+                          need, (size_t)kNoallocScratchBytes);
+            return fail(PA_ERR_CAPACITY, m);
+        }
+        st = noalloc_scratch(&ws);
+        if (st != PA_OK)
+            return st;
+        ws_bytes = need;
+    }
+    NewTokens nt;
+    nt.k = k_new;
+    nt.v = v_new;
+    nt.slots = slot_mapping;
+    return decode_impl(kAll, q, k_cache, v_cache, block_tables, max_blocks_per_seq, seq_lens,
+                       seq_starts, seq_shared, num_seqs, max_seq_len, scale, k_scale, v_scale,
+                       out, ws, ws_bytes, partition_size, desc, stream, nt);
 }
 
 pa_status pa_decode_partials(const void *q, const void *k_cache, const void *v_cache,
