@@ -629,44 +629,77 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a, int32_t 
         wv.write_partial(a, w, ok);
 }
 
+// Bytes of the block tables each wave touches at launch (two 1 KiB loads):
+// the waves of one XCD together cover the first W/8 * 2 KiB of the tables.
+constexpr int kTablePrefetchLoads = 2;
+
 // Balanced split: run i of W takes tiles [i*T/W, (i+1)*T/W) of the list of
-// all tiles in head-major order ((KV head, sequence, 16-token tile), see
-// work.hpp), T tiles in total; balanced_run places each XCD's runs on that
-// XCD's workgroups.  HINT as for decode_mfma_kernel.
+// all tiles in head-major order ((KV head, sequence, 16-token tile), each
+// segment preceded by its start charge, see work.hpp), T tiles in total;
+// balanced_run places each XCD's runs on that XCD's workgroups.  HINT as for
+// decode_mfma_kernel.
 template <int QT, int KT, int D, bool HINT>
 __global__ __launch_bounds__(256)
 void decode_mfma_balanced_kernel(DecodeArgs a, int32_t W)
 {
+    __shared__ u32x4 table_sink[4][kWave]; // receives the prefetch, never read
     const int lane = threadIdx.x & 63;
-    const int32_t i =
-        balanced_run(blockIdx.x, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), W);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int32_t i = balanced_run(blockIdx.x, wave, W);
     if (i >= W)
         return;
 
-    // T, the number of runs (never more than tiles, so no run is empty), and
-    // the first segment of this wave's run
+    // A decode step's tables are cold (the host wrote them for this step),
+    // and the scalar loads of each run's first block ids would wait a full
+    // HBM round trip after the lengths have been read.  So while the lengths
+    // load, the waves of each XCD touch the tables, 1 KiB per wave and load,
+    // and those block-id loads find them in the XCD's L2.  (Wave k of an XCD
+    // covers bytes [1 KiB (k + r W / 8), +1 KiB); placement as balanced_run.)
+    {
+        const int64_t tbytes = (int64_t)a.num_seqs * a.max_blocks_per_seq * 4;
+        const int32_t per_xcd = W % (4 * kXcds) == 0 ? W / kXcds : W;
+        const int32_t k = W % (4 * kXcds) == 0 ? (blockIdx.x / kXcds) * 4 + wave : i;
+        const char *tb = reinterpret_cast<const char *>(a.block_tables);
+        // (a hint only: skipped for a table that is not 16-byte aligned)
+        const int64_t tbytes_in = (reinterpret_cast<uintptr_t>(tb) & 15) == 0 ? tbytes : 0;
+#pragma unroll
+        for (int r = 0; r < kTablePrefetchLoads; ++r) {
+            const int64_t off = ((int64_t)k + (int64_t)r * per_xcd) * 1024 + 16 * lane;
+            if (uniform((int32_t)(((int64_t)k + (int64_t)r * per_xcd) * 1024 < tbytes_in)) &&
+                off + 16 <= tbytes_in)
+                load16_to_lds(tb + off, &table_sink[wave][0]);
+        }
+    }
+
+    // T, the number of runs (never more than tiles), and the segment holding
+    // this wave's first tile
     const RunStart rs = run_start(a, lane, i, W);
     if (i >= rs.runs)
         return;
     const int64_t x1 = rs.x1;
     SegPos pos = rs.pos;
 
+    // The run's virtual tiles [x0, x1) meet each segment's start charge and
+    // real tiles in turn; a piece of real tiles is a range to decode (a run
+    // may begin or end inside a start charge, which holds nothing to read).
     MfmaWave<QT, KT, D> wv(lane);
     int64_t x = rs.x0;
     while (x < x1) {
         const int32_t nb = tiles_of(pos.n);
-        const int32_t j = (int32_t)(x - pos.first_tile);
-        const int64_t stop = min(x1, pos.first_tile + nb);
-        const int32_t je = j + (int32_t)(stop - x);
-        wv.start(a, pos.b, pos.g);
-        const bool ok = wv.template run<HINT>(a, pos.b, pos.g, j * kTile,
-                                              min(je * kTile, pos.n), pos.n);
-        wv.finish();
-        if (j == 0 && je == nb)
-            wv.write_out(a, pos.b, pos.g, pos.n, ok);
-        else
-            wv.write_partial(a, balanced_slot(a, i, pos.g, pos.b), ok);
-        x = stop;
+        const int64_t r0 = pos.first_tile + kSegmentCost; // the segment's tile 0
+        const int64_t lo = max(x, r0), hi = min(x1, r0 + nb);
+        if (hi > lo) {
+            const int32_t j = (int32_t)(lo - r0), je = (int32_t)(hi - r0);
+            wv.start(a, pos.b, pos.g);
+            const bool ok = wv.template run<HINT>(a, pos.b, pos.g, j * kTile,
+                                                  min(je * kTile, pos.n), pos.n);
+            wv.finish();
+            if (j == 0 && je == nb)
+                wv.write_out(a, pos.b, pos.g, pos.n, ok);
+            else
+                wv.write_partial(a, balanced_slot(a, i, pos.g, pos.b), ok);
+        }
+        x = r0 + nb;
         if (x < x1)
             pos = next_segment(a, pos);
     }

@@ -214,4 +214,15 @@ __device__ __forceinline__ u32x4 load16_stream(const void *p)
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
 }
 
+// Loads 16 bytes per lane from global memory straight into LDS (lane l's
+// bytes land at lds + 16 l): a load the compiler keeps although no register
+// receives it, used to bring data into the caches ahead of the loads that
+// need it.  lds must be wave-uniform and hold 1 KiB.
+__device__ __forceinline__ void load16_to_lds(const void *src, void *lds)
+{
+    __builtin_amdgcn_global_load_lds(
+        (const __attribute__((address_space(1))) void *)src,
+        (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
+
 } // namespace pa

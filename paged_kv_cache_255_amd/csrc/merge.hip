@@ -191,21 +191,57 @@ __device__ __forceinline__ void merge_segment(const DecodeArgs &a, int32_t b, in
 // (sequence b of length n, KV head g).  False when there is nothing to
 // merge: in the balanced split, one run held the whole segment and wrote its
 // rows itself.
+// The balanced split's run bounds for segment (g, b), whose real tiles (nt
+// of them) follow its start charge at g * Th + before: the runs that decode
+// some of them.  False when one run holds them all.
+__device__ __forceinline__ bool balanced_parts(const DecodeArgs &a, int32_t b, int32_t g,
+                                               int64_t Th, int64_t before, int32_t nt,
+                                               int64_t &w0, int64_t &nparts)
+{
+    const int64_t T = Th * a.num_kv_heads;
+    const int32_t R = effective_runs(T, a.waves);
+    const int64_t S0 = (int64_t)g * Th + before + kSegmentCost;
+    const int64_t i0 = run_of_tile(S0, T, R);
+    const int64_t i1 = run_of_tile(S0 + nt - 1, T, R);
+    if (i0 == i1)
+        return false;
+    w0 = balanced_slot(a, i0, g, b);
+    nparts = i1 - i0 + 1;
+    return true;
+}
+
+// What the merge does with segment (g, b) of a balanced launch over at most
+// 64 sequences of lengths below kScan32MaxLen: every length comes in with one
+// load per lane, issued before anything else (the segment's own length, the
+// tiles before it and the head's total all follow from it).
+enum SegAction { kSegFillZero, kSegFillNan, kSegWritten, kSegMerge };
+
+__device__ __forceinline__ SegAction balanced_segment_fast(const DecodeArgs &a, int lane,
+                                                           int32_t b, int32_t g, int64_t &w0,
+                                                           int64_t &nparts)
+{
+    const bool in = lane < a.num_seqs;
+    const int32_t len = in ? a.seq_lens[lane] : 0;
+    const int32_t n = __builtin_amdgcn_readlane(len, b);
+    const int32_t tiles = in ? split_tiles(a, len) : 0;
+    const int32_t incl = wave_incl_scan32(tiles);
+    if (!len_ok(a, n))
+        return kSegFillNan;
+    if (n == 0)
+        return kSegFillZero;
+    const int32_t Th = __builtin_amdgcn_readlane(incl, kWave - 1);
+    const int32_t before = __builtin_amdgcn_readlane(incl - tiles, b);
+    return balanced_parts(a, b, g, Th, before, tiles_of(n), w0, nparts) ? kSegMerge
+                                                                         : kSegWritten;
+}
+
 __device__ __forceinline__ bool segment_parts(const DecodeArgs &a, int lane, int32_t b,
                                               int32_t g, int32_t n, int64_t &w0, int64_t &nparts)
 {
     if (a.partition == kPartitionBalanced) {
-        // segment (g, b) starts at tile g * Th + (tiles of sequences [0, b))
+        // segment (g, b) starts at g * Th + (split_tiles of sequences [0, b))
         const HeadTiles ht = head_tiles(a, lane, b);
-        const int64_t T = ht.per_head * a.num_kv_heads;
-        const int32_t R = effective_runs(T, a.waves);
-        const int64_t S0 = (int64_t)g * ht.per_head + ht.before;
-        const int64_t i0 = run_of_tile(S0, T, R);
-        const int64_t i1 = run_of_tile(S0 + tiles_of(n) - 1, T, R);
-        if (i0 == i1)
-            return false;
-        w0 = balanced_slot(a, i0, g, b);
-        nparts = i1 - i0 + 1;
+        return balanced_parts(a, b, g, ht.per_head, ht.before, tiles_of(n), w0, nparts);
     } else {
         w0 = ((int64_t)b * a.num_kv_heads + g) * a.max_parts;
         nparts = (n + a.partition - 1) / a.partition;
@@ -252,12 +288,28 @@ __global__ __launch_bounds__(64) void merge_kernel(DecodeArgs a)
 
 // One wave per segment (sequence b, KV head g) for the shapes merge_segment
 // handles; one workgroup per output row (merge_row) for the others.
+// True when balanced_segment_fast applies to the launch.
+__device__ __forceinline__ bool segment_fast_path(const DecodeArgs &a)
+{
+    return a.partition == kPartitionBalanced && a.num_seqs <= kWave &&
+           a.max_seq_len < kScan32MaxLen;
+}
+
 template <int QT, int D>
 __global__ __launch_bounds__(64) void merge_segment_kernel(DecodeArgs a)
 {
     const int lane = threadIdx.x;
     const int32_t b = blockIdx.x / a.num_kv_heads;
     const int32_t g = blockIdx.x % a.num_kv_heads;
+    if (segment_fast_path(a)) {
+        int64_t w0 = 0, nparts = 0;
+        switch (balanced_segment_fast(a, lane, b, g, w0, nparts)) {
+        case kSegFillNan: merge_fill<QT, D>(a, b, g, false, lane); return;
+        case kSegFillZero: merge_fill<QT, D>(a, b, g, true, lane); return;
+        case kSegWritten: return;
+        default: merge_segment<QT, D>(a, b, g, w0, nparts, lane); return;
+        }
+    }
     const int32_t n = a.seq_lens[b];
     const bool valid = len_ok(a, n);
     if (!valid || n == 0) {
@@ -292,17 +344,29 @@ __global__ __launch_bounds__(64 * wide_merge_waves(S)) void merge_segment_wide_k
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int32_t b = blockIdx.x / a.num_kv_heads;
     const int32_t g = blockIdx.x % a.num_kv_heads;
-    const int32_t n = a.seq_lens[b];
-    const bool valid = len_ok(a, n);
-    // b, g and n are the same for every wave, so all waves leave together
-    if (!valid || n == 0) {
-        if (wave == 0)
-            merge_fill<QT, D>(a, b, g, valid, lane);
-        return;
+    int64_t w0 = 0, nparts = 0;
+    // b, g and the lengths are the same for every wave, so all waves take the
+    // same branch and leave together
+    if (segment_fast_path(a)) {
+        const SegAction act = balanced_segment_fast(a, lane, b, g, w0, nparts);
+        if (act == kSegFillNan || act == kSegFillZero) {
+            if (wave == 0)
+                merge_fill<QT, D>(a, b, g, act == kSegFillZero, lane);
+            return;
+        }
+        if (act == kSegWritten)
+            return;
+    } else {
+        const int32_t n = a.seq_lens[b];
+        const bool valid = len_ok(a, n);
+        if (!valid || n == 0) {
+            if (wave == 0)
+                merge_fill<QT, D>(a, b, g, valid, lane);
+            return;
+        }
+        if (!segment_parts(a, lane, b, g, n, w0, nparts))
+            return;
     }
-    int64_t w0, nparts;
-    if (!segment_parts(a, lane, b, g, n, w0, nparts))
-        return;
     MergeState<S> st;
     merge_fold<D, S>(a, w0, wave * nparts / NW, (wave + 1) * nparts / NW, lane, st);
 #pragma unroll

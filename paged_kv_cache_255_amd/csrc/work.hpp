@@ -58,11 +58,24 @@ __device__ __forceinline__ bool len_ok(const DecodeArgs &a, int32_t n)
 
 __device__ __forceinline__ int32_t tiles_of(int32_t n) { return (n + kTile - 1) / kTile; }
 
-// Tiles a sequence contributes to the balanced split; a length out of range
-// contributes none (the merge kernel writes that row as NaN).
+// Tiles the balanced split charges a segment for starting, on top of its own:
+// a wave that moves on to a new (sequence, KV head) inside its run restarts
+// its tile pipeline (the lengths, q and the block ids of the new segment, then
+// the first tiles' loads).  Measured on MI355X (Llama-3-8B layer, 32
+// sequences): with no charge, runs holding two segments ended 3.9 us after
+// the others (a tile takes a wave about 1.2 us); whole decode steps took
+// 58.1, 57.5, 57.0, 57.1, 57.3, 57.5 and 58.1 us on average (runs of three,
+// two sweeps) with charges of 0, 3, 5, 7, 9, 12 and 16 tiles.  In the
+// balanced order a segment is kSegmentCost virtual tiles, then its real
+// tiles.
+constexpr int32_t kSegmentCost = 5;
+
+// Tiles a sequence contributes to the balanced split (its real tiles plus the
+// start charge); an empty sequence or a length out of range contributes none
+// (the merge kernel writes that row as 0 or NaN).
 __device__ __forceinline__ int32_t split_tiles(const DecodeArgs &a, int32_t n)
 {
-    return len_ok(a, n) ? tiles_of(n) : 0;
+    return (len_ok(a, n) && n > 0) ? tiles_of(n) + kSegmentCost : 0;
 }
 
 __device__ __forceinline__ int64_t wave_sum(int64_t v)
@@ -84,6 +97,24 @@ __device__ __forceinline__ int64_t wave_incl_scan(int64_t v, int lane)
     return v;
 }
 
+// Inclusive prefix sum of a 32-bit value over the 64 lanes of a wave, with
+// DPP moves (row shifts within each 16-lane row, then the row broadcasts of
+// lanes 15 and 31): six VALU adds, no LDS-queue round trips.
+__device__ __forceinline__ int32_t wave_incl_scan32(int32_t v)
+{
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false); // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false); // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false); // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false); // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false); // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false); // row_bcast:31
+    return v;
+}
+
+// Lengths below this keep every per-wave tile sum of up to 64 sequences
+// inside 32 bits (64 * 2^21 tiles), so the split can use wave_incl_scan32.
+constexpr int32_t kScan32MaxLen = 1 << 25;
+
 __device__ __forceinline__ int64_t readlane64(int64_t v, int l)
 {
     const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, l);
@@ -93,8 +124,9 @@ __device__ __forceinline__ int64_t readlane64(int64_t v, int l)
 
 // The balanced split orders the segments head-major: (KV head g, sequence
 // b) for g = 0 .. Hkv-1 and, within a head, b = 0 .. B-1.  Every head has
-// the same Th tiles (the sequences' tiles summed), so T = Hkv * Th and
-// segment (g, b) starts at tile g * Th + (tiles of sequences [0, b)).
+// the same Th tiles (the sequences' split_tiles summed: real tiles and start
+// charges), so T = Hkv * Th and segment (g, b) starts at tile
+// g * Th + (split_tiles of sequences [0, b)).
 
 // Tiles of sequences [0, b) and of all sequences (one head's share, Th),
 // from one pass over the lengths (each lane sums its own sequences; the two
@@ -120,7 +152,8 @@ struct SegPos {
     int32_t g;          // KV head
     int32_t b;          // sequence
     int32_t n;          // its length
-    int64_t first_tile; // index of the segment's first tile in the balanced order
+    int64_t first_tile; // where the segment starts in the balanced order; its
+                        // tile j is at first_tile + kSegmentCost + j
 };
 
 // The segment holding tile x (x < T = Hkv * Th): head x / Th, then the
@@ -152,7 +185,8 @@ __device__ __forceinline__ SegPos locate_tile(const DecodeArgs &a, int lane, int
 }
 
 // Runs the balanced split cuts T tiles into: the launch's W waves, but no
-// more than T so that every run holds at least one tile.
+// more than T so that every run holds at least one tile (which may be a start
+// charge only: such a run decodes nothing and leaves no partial state).
 __device__ __forceinline__ int32_t effective_runs(int64_t T, int32_t W)
 {
     return (int32_t)(T < (int64_t)W ? T : (int64_t)W);
@@ -192,6 +226,29 @@ __device__ __forceinline__ RunStart run_start(const DecodeArgs &a, int lane, int
                                               int32_t W)
 {
     RunStart r;
+    if (a.num_seqs <= kWave && a.max_seq_len < kScan32MaxLen) {
+        // one length per lane: the scan gives Th and the segment together
+        const bool in = lane < a.num_seqs;
+        const int32_t n = in ? a.seq_lens[lane] : 0;
+        const int32_t tiles = in ? split_tiles(a, n) : 0;
+        const int32_t incl = wave_incl_scan32(tiles);
+        r.Th = __builtin_amdgcn_readlane(incl, kWave - 1);
+        r.T = r.Th * a.num_kv_heads;
+        r.runs = effective_runs(r.T, W);
+        if (i >= r.runs)
+            return r;
+        r.x0 = (int64_t)i * r.T / r.runs;
+        r.x1 = (int64_t)(i + 1) * r.T / r.runs;
+        const int32_t g = (int32_t)(r.x0 / r.Th);
+        const int32_t y = (int32_t)(r.x0 - (int64_t)g * r.Th);
+        const uint64_t hit = __ballot(in && incl > y);
+        const int k = __ffsll((unsigned long long)hit) - 1; // y < Th: some lane hits
+        r.pos.g = g;
+        r.pos.b = k;
+        r.pos.n = __builtin_amdgcn_readlane(n, k);
+        r.pos.first_tile = (int64_t)g * r.Th + __builtin_amdgcn_readlane(incl - tiles, k);
+        return r;
+    }
     if (a.num_seqs <= kWave) {
         // one length per lane: the scan gives Th and the segment together
         const bool in = lane < a.num_seqs;
@@ -231,7 +288,7 @@ __device__ __forceinline__ RunStart run_start(const DecodeArgs &a, int lane, int
 __device__ __forceinline__ SegPos next_segment(const DecodeArgs &a, SegPos p)
 {
     SegPos q;
-    q.first_tile = p.first_tile + tiles_of(p.n);
+    q.first_tile = p.first_tile + split_tiles(a, p.n);
     q.g = p.g;
     q.b = p.b + 1;
     for (;;) {

@@ -90,6 +90,24 @@ inline SimPair __builtin_amdgcn_permlane16_swap(uint32_t a, uint32_t, bool, bool
 inline SimPair __builtin_amdgcn_permlane32_swap(uint32_t a, uint32_t, bool, bool) {
   uint32_t o = sim_exchange(a, sim_lane() ^ 32); return SimPair{{a, o}};
 }
+// DPP moves used by the wave scan: row_shr:k (0x110 + k, k < 16) reads lane
+// - k of the same 16-lane row; row_bcast:15 (0x142) and row_bcast:31 (0x143)
+// read lane 15 of the previous row and lane 31.  Rows outside row_mask, and
+// lanes whose source is outside the row, return `old`.
+inline int __builtin_amdgcn_update_dpp(int old, int src, int ctrl, int row_mask, int, bool) {
+  const int l = sim_lane(), row = l / 16;
+  int from = -1;
+  if (ctrl > 0x110 && ctrl < 0x120) { const int k = ctrl - 0x110; if (l % 16 >= k) from = l - k; }
+  else if (ctrl == 0x142) from = row > 0 ? row * 16 - 1 : -1;
+  else if (ctrl == 0x143) from = 31;
+  else { fprintf(stderr, "update_dpp: control %#x not simulated\n", ctrl); abort(); }
+  const int v = sim_exchange(src, from < 0 ? l : from);
+  return ((row_mask >> row) & 1) && from >= 0 ? v : old;
+}
+// Global-to-LDS load: lane l's `size` bytes land at lds + size * l.
+inline void __builtin_amdgcn_global_load_lds(const void *src, void *lds, unsigned size, int, int) {
+  memcpy(static_cast<char *>(lds) + size * sim_lane(), src, size);
+}
 enum { hipDeviceAttributeMaxSharedMemoryPerMultiprocessor = 1, hipDeviceAttributeMaxSharedMemoryPerBlock = 2,
        hipDeviceAttributeMultiprocessorCount = 3 };
 inline hipError_t hipGetDevice(int *d) { *d = 0; return 0; }

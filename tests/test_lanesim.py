@@ -34,7 +34,9 @@ def sim(tmp_path_factory):
     src.mkdir()
     for f in ("device.hpp", "work.hpp", "merge.hip", "decode_mfma.hip", "append.hpp"):
         text = open(os.path.join(CSRC, f)).read()
-        (src / f).write_text(text.replace("__attribute__((address_space(4)))", ""))
+        for space in (1, 3, 4):
+            text = text.replace(f"__attribute__((address_space({space})))", "")
+        (src / f).write_text(text)
     exe = d / "sim"
     subprocess.check_call([CLANG, "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
                            "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer",

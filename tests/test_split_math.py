@@ -1,14 +1,17 @@
 """The integer arithmetic of the balanced work split, checked on the CPU.
 
 The decode kernel cuts the T tiles of all (sequence, KV head) segments, in
-order, into R = min(T, W) runs [i*T/R, (i+1)*T/R); the merge finds the run of
+order, into R = min(T, W) runs [i*T/R, (i+1)*T/R); each segment is charged
+kSegmentCost virtual tiles before its real ones (a wave that starts a new
+segment inside its run pays a pipeline restart).  The merge finds the run of
 a tile as ((x + 1) * R - 1) // T, and a run's partial state for a segment
-goes to slot run + segment.  These tests restate those three formulas and
-check the properties the kernels rely on: every run is non-empty, the runs
-tile [0, T) exactly, run_of_tile inverts the cut, and no two (run, segment)
-pairs share a slot.  (The device code is checked end to end by the GPU
-parity tests; this pins the arithmetic itself, including sizes no GPU test
-reaches.)
+goes to slot run + segment.  These tests restate those formulas and check the
+properties the kernels rely on: every run is non-empty, the runs tile [0, T)
+exactly, run_of_tile inverts the cut, the runs the decode gives a piece of a
+segment are exactly the ones the merge reads, every real tile is decoded
+once, and no two (run, segment) pairs share a slot.  (The device code is
+checked end to end by the GPU parity tests; this pins the arithmetic itself,
+including sizes no GPU test reaches.)
 """
 import random
 
@@ -57,26 +60,55 @@ def test_run_of_tile_exhaustive_small():
             assert [run_of_tile(x, T, R) for x in range(T)] == owner
 
 
-@pytest.mark.parametrize("seed", range(20))
-def test_partial_slots_are_unique(seed):
+SEGMENT_COST = 5  # kSegmentCost in work.hpp
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_decode_pieces_match_merge_parts(seed):
+    """The decode's walk (a run's virtual tiles meet each segment's start
+    charge, then its real tiles) against the merge's run bounds."""
     rng = random.Random(seed)
     nseg = rng.randint(1, 300)
-    seg_tiles = [rng.choice([0, 1, 2, rng.randint(1, 400)]) for _ in range(nseg)]
-    T = sum(seg_tiles)
+    real = [rng.choice([0, 1, 2, rng.randint(1, 400)]) for _ in range(nseg)]
+    virt = [n + SEGMENT_COST if n > 0 else 0 for n in real]
+    T = sum(virt)
     if T == 0:
         return
-    W = rng.choice([1, 7, 256, 3072, T, 2 * T])
+    W = rng.choice([1, 7, 256, 1024, 3072, T, 2 * T])
     R = runs(T, W)
+    starts = [sum(virt[:s]) for s in range(nseg)]
+    # decode side: run i walks [x0, x1)
+    pieces = {}  # segment -> list of (run, j, je)
+    for i in range(R):
+        x0, x1 = run_bounds(i, T, R)
+        s = next(k for k in range(nseg) if starts[k] + virt[k] > x0)  # segment holding x0
+        x = x0
+        while x < x1:
+            r0 = starts[s] + SEGMENT_COST
+            lo, hi = max(x, r0), min(x1, r0 + real[s])
+            if hi > lo:
+                pieces.setdefault(s, []).append((i, lo - r0, hi - r0))
+            x = r0 + real[s]
+            if x < x1:
+                s = next(k for k in range(s + 1, nseg) if virt[k] > 0)
     used = set()
-    start = 0
-    for s, n in enumerate(seg_tiles):
-        if n == 0:
+    for s in range(nseg):
+        if real[s] == 0:
+            assert s not in pieces
             continue
-        i0, i1 = run_of_tile(start, T, R), run_of_tile(start + n - 1, T, R)
-        if i0 != i1:  # split segment: runs i0..i1 each leave a partial state
+        got = pieces[s]
+        # every real tile once, in order
+        assert got[0][1] == 0 and got[-1][2] == real[s]
+        assert all(got[k][2] == got[k + 1][1] for k in range(len(got) - 1))
+        # merge side
+        S0 = starts[s] + SEGMENT_COST
+        i0, i1 = run_of_tile(S0, T, R), run_of_tile(S0 + real[s] - 1, T, R)
+        assert [p[0] for p in got] == list(range(i0, i1 + 1))
+        # one run holds it all exactly when the merge finds i0 == i1
+        assert (len(got) == 1) == (i0 == i1)
+        if i0 != i1:
             for i in range(i0, i1 + 1):
                 slot = i + s
                 assert slot not in used
                 assert slot < R + nseg  # within the workspace's W + B*Hkv slots
                 used.add(slot)
-        start += n
