@@ -72,7 +72,8 @@ def parse():
                     help="only run plain device-to-device copies of 1 GiB (calibrates the HBM "
                          "byte counters a profiler reports) and exit")
     ap.add_argument("--no-reuse-hint", action="store_true",
-                    help="pass no seq_shared hint: every block is read with streaming loads")
+                    help="pass no share plan (seq_shared): every block is read with streaming "
+                         "loads and every sequence reads its shared blocks itself")
     ap.add_argument("--separate-append", action="store_true",
                     help="a step calls pa_cache_append then pa_decode instead of "
                          "pa_decode_append")
@@ -176,8 +177,9 @@ def main():
         ws_bytes = pa.pa_decode_workspace_bytes(desc, B, max_len, partition)
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
 
-    # Per-step metadata (slots, tables, lengths), one row per step.
-    meta_words = B + B * maxb + B + B  # slots, tables, lens, leading shared blocks
+    # Per-step metadata (slots, tables, lengths, share plan), one row per step.
+    plan_off = 4 * (2 * B + B * maxb)  # byte offset of the share plan in a row
+    meta_words = B + B * maxb + B + pa.share_plan_words(B)
     lib = pa._lib
     pool_h = pool.handle
     dec_p = dec.ctypes.data
@@ -185,8 +187,8 @@ def main():
     def host_step(dst_ptr):
         rc = lib.pa_seq_append_slots_batch(pool_h, dec_p, B, 1, dst_ptr)
         rc |= lib.pa_export_block_tables(pool_h, dec_p, B, maxb, dst_ptr + 4 * B,
-                                         dst_ptr + 4 * (B + B * maxb), None,
-                                         dst_ptr + 4 * (2 * B + B * maxb))
+                                         dst_ptr + 4 * (B + B * maxb), None, None)
+        rc |= lib.pa_export_share_plan(pool_h, dec_p, B, dst_ptr + plan_off)
         if rc:
             raise RuntimeError("host step failed: " + pa.pa_last_error())
 
@@ -216,17 +218,14 @@ def main():
     meta_base = d_meta.data_ptr()
 
     separate = args.separate_append
-    # the sharing hint goes with the launches when some sequence of the batch
-    # shares blocks with another (all-zero counts would add a read for nothing)
+    # the share plan goes with the launches when some sequence of the batch
+    # shares blocks with another (a plan of zero counts and no groups would
+    # add a read for nothing)
     if upload:
-        first_row = np.zeros(meta_words, np.int32)
-        rc = lib.pa_export_block_tables(pool_h, dec_p, B, maxb, None, None, None,
-                                        first_row.ctypes.data + 4 * (2 * B + B * maxb))
-        if rc:
-            raise RuntimeError("export failed: " + pa.pa_last_error())
+        first_plan = pa.pa_export_share_plan(pool, dec)
     else:
-        first_row = h_meta[0].numpy()
-    any_shared = bool((first_row[2 * B + B * maxb:] > 0).any())
+        first_plan = h_meta[0].numpy()[plan_off // 4:]
+    any_shared = bool(first_plan[1] > 0 or (first_plan[2:2 + B] > 0).any())
     no_hint = args.no_reuse_hint or not any_shared
 
     def step(i):
@@ -241,7 +240,7 @@ def main():
         else:
             row = meta_base + i * meta_row
         slots_p, tables_p, lens_p = row, row + 4 * B, row + 4 * (B + B * maxb)
-        shared_p = None if no_hint else row + 4 * (2 * B + B * maxb)
+        shared_p = None if no_hint else row + plan_off
         r = i % R
         for layer in range(L):
             kcp, vcp = kc_p[layer * R + r]
@@ -291,7 +290,7 @@ def main():
     # queue's dispatch latency to every sample.
     row = meta_base if upload else meta_base + last * meta_row
     tables_p, lens_p = row + 4 * B, row + 4 * (B + B * maxb)
-    shared_p = None if no_hint else row + 4 * (2 * B + B * maxb)
+    shared_p = None if no_hint else row + plan_off
 
     def decode_kernel(r, layer):
         kcp, vcp = kc_p[layer * R + r]
@@ -336,6 +335,23 @@ def main():
     final_tables = final_meta[B:B + B * maxb].reshape(B, maxb).copy()
     final_lens = final_meta[B + B * maxb:2 * B + B * maxb].copy()
     last_r = last % R
+    # bytes of the distinct cache slots the last step reads (shared blocks
+    # once): below the algorithmic bytes when sequences share blocks
+    used = {}
+    for b in range(B):
+        n = int(final_lens[b])
+        for j in range(-(-n // bs)):
+            blk = int(final_tables[b, j])
+            used[blk] = max(used.get(blk, 0), min(bs, n - j * bs))
+    unique_bytes = sum(used.values()) * step_bytes_1 // L
+    unique = None
+    if unique_bytes < int(launch_bytes):
+        ugbs = unique_bytes / (kern_us * 1e-6) / 1e9
+        unique = {"bytes": int(unique_bytes), "achieved": round(ugbs, 1),
+                  "frac": round(ugbs / HBM_PEAK_GBS, 4),
+                  "how": "distinct cache slots of the last step's tables, per launch"}
+        log(f"[bench] distinct KV bytes per launch {unique_bytes / 1e6:.1f} MB "
+            f"({ugbs:.1f} GB/s, {ugbs / HBM_PEAK_GBS * 100:.1f}% of HBM peak)")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -379,7 +395,7 @@ def main():
             "kernel": kname,
             "cache_replicas": R,
             "metadata": "uploaded per step" if upload else "resident (all steps)",
-            "reuse_hint": not no_hint,
+            "share_plan": not no_hint,
             "step_calls": ("pa_cache_append + pa_decode" if separate else "pa_decode_append"),
             "parallelism": "none (1 GPU)",
         },
@@ -400,6 +416,7 @@ def main():
                        "decode_mfma_balanced_kernel" if partition == -1 else
                        "decode_mfma_kernel"),
             "kernel_us_avg": round(kern_us, 2),
+            "unique": unique,
         },
         "cpu_baseline": cpu,
     }
@@ -425,7 +442,7 @@ def measured_traffic(workload, partition, launch_bytes, no_hint):
         return None
     same = (rec.get("workload") == workload and rec.get("partition") == partition and
             rec.get("algorithmic_bytes_per_launch") == launch_bytes and
-            rec.get("reuse_hint", False) == (not no_hint) and
+            rec.get("share_plan", False) == (not no_hint) and
             rec.get("kernel_sources_sha256") == h.hexdigest())
     return rec["hbm_bytes_per_launch"] if same else None
 
@@ -489,7 +506,7 @@ def write_traffic_record(bench_line, fetch_csv, write_csv, copy_fetch_csv, copy_
         "kernel": roof["kernel"],
         "workload": cfg["workload_name"],
         "partition": cfg["partition"],
-        "reuse_hint": cfg.get("reuse_hint", False),
+        "share_plan": cfg.get("share_plan", False),
         "steps": steps,
         "warmup": warmup,
         "launches": f"the last {steps} of the back-to-back decode launches bench.py times "

@@ -228,6 +228,39 @@ pa_status pa_export_block_tables(const pa_pool *pool, const int32_t *seqs, int32
                                  int32_t max_blocks, int32_t *tables_out, int32_t *lens_out,
                                  int32_t *starts_out, int32_t *shared_out);
 
+/* Share plan of a decode batch: which sequences hold the same leading blocks,
+ * so that a decode launch can read those blocks once per KV head for all of
+ * them ([devto] §5 "Zero-Copy Forking" and "Automatic Prefix Caching": the
+ * sharers' tables point at one copy of the prompt's blocks; [hi] "Prefix
+ * caching: share the system prompt": one copy of the prefix KV serves every
+ * request).  int32 words, for a batch of B sequences in export order:
+ *   [0]                  PA_SHARE_PLAN_MAGIC
+ *   [1]                  number of groups, ng
+ *   [2 + b]              leading table entries of b whose block another of the
+ *                        B tables also holds (the hint of pa_export_block_tables)
+ *   [2 + B + b]          group of b, or -1
+ *   [2 + 2B + b]         rank of b in its group (0 when none)
+ *   [2 + 3B + b]         leading blocks of b its group shares (0 when none)
+ *   [2 + 4B + g]         members of group g (g < ng)
+ *   [2 + 5B + g]         leading blocks group g shares
+ *   [2 + 6B + i]         members, group by group, each in rank order
+ *   [2 + 7B + g]         index in that list of group g's first member
+ * A group: at least two sequences without a slid window whose tables begin
+ * with the same block; it shares the longest run of leading entries all its
+ * members hold alike, counting only blocks before each member's last token
+ * (so the shared tokens are the same for all, and the block a step appends
+ * to stays the member's own).  Groups are numbered by their first member and
+ * members are in batch order.  A plan is valid for the tables and lengths
+ * it was exported with. */
+#define PA_SHARE_PLAN_MAGIC 0x31534150
+#define PA_SHARE_PLAN_WORDS(nseq) (2 + 8 * (size_t)(nseq))
+
+/* Writes the share plan of nseq resident sequences (as listed for
+ * pa_export_block_tables) into plan_out[PA_SHARE_PLAN_WORDS(nseq)].
+ * PA_ERR_INVALID_ARG for an unknown or swapped-out sequence. */
+pa_status pa_export_share_plan(const pa_pool *pool, const int32_t *seqs, int32_t nseq,
+                               int32_t *plan_out);
+
 pa_status pa_pool_get_stats(const pa_pool *pool, pa_pool_stats *out);
 
 /* Hands out the block copies the appends since the last call queued (copy on
@@ -319,9 +352,21 @@ pa_status pa_cache_append(const void *k, const void *v, void *k_cache, void *v_c
 #define PA_PARTITION_BALANCED (-1) /* tokens split evenly over the GPU's waves */
 
 /* Workspace bytes pa_decode needs for this shape and partitioning (0 for
- * PA_PARTITION_NONE).  partition_size > 0 must be a multiple of 16. */
+ * PA_PARTITION_NONE).  partition_size > 0 must be a multiple of 16.  For
+ * PA_PARTITION_BALANCED with the MFMA kernel and a shape that can read a
+ * share plan's groups once per KV head (see seq_shared), this includes the
+ * room for those reads' partial states, (W + Hkv x num_seqs / 2) x
+ * 4 x 16 / G slots of G x (head_dim + 2) floats (W: the launch's waves); a
+ * launch given less, but no less than the size without that room, reads
+ * every sequence's blocks itself. */
 size_t pa_decode_workspace_bytes(const pa_kv_desc *desc, int32_t num_seqs, int32_t max_seq_len,
                                  int32_t partition_size);
+
+/* Runs W of a PA_PARTITION_BALANCED launch of this shape on the current
+ * device: the waves of the balanced kernel the GPU holds at once (CUs x
+ * resident waves per CU; 1,024 on an MI355X).  0 for a shape the balanced
+ * mode does not take, or when the device cannot be queried. */
+int32_t pa_decode_balanced_waves(const pa_kv_desc *desc);
 
 /* Single-query attention for each sequence b and query head h
  * ([devto] §1, Attention(Q,K,V) = softmax(QK^T / sqrt(d_k)) V; §4 "The
@@ -341,12 +386,21 @@ size_t pa_decode_workspace_bytes(const pa_kv_desc *desc, int32_t num_seqs, int32
  *     block ids are out of range is written as NaN instead of being read.
  *   seq_starts: device int32 [num_seqs] or NULL; each in [0, seq_lens[b]]
  *     (not read for zero-length rows).  pa_export_block_tables gives them.
- *   seq_shared: device int32 [num_seqs] or NULL, a hint: the first
- *     seq_shared[b] entries of table b hold blocks that other sequences of
- *     the batch also read (pa_export_block_tables gives the counts).  The
- *     MFMA kernel reads those blocks with loads that keep them in the GPU
- *     caches and all others with streaming loads (read once); the VALU
- *     kernel streams every block.  The result does not depend on the hint.
+ *   seq_shared: device int32 [PA_SHARE_PLAN_WORDS(num_seqs)] or NULL: the
+ *     batch's share plan (pa_export_share_plan, for these tables and
+ *     lengths; with any other plan the outputs are unspecified, though
+ *     every access stays inside the buffers).  With the MFMA kernel, the
+ *     leading entries other tables also hold are read with loads that keep
+ *     them in the GPU caches (all others with streaming loads, read once).
+ *     With PA_PARTITION_BALANCED, 16 % G == 0, G x head_dim
+ *     a power-of-two multiple of 256 up to 2048, and a workspace of
+ *     pa_decode_workspace_bytes(), the blocks a group shares are read once
+ *     per KV head for all its members: the group is cut into rows of
+ *     4 x 16 / G members, whose query heads fill four 16-column MFMA tiles,
+ *     and the launch's waves take pieces of those rows as they take pieces
+ *     of sequences; the merge folds each member's row state in with its own
+ *     pieces.  The VALU kernel ignores the plan.  The result does not depend
+ *     on the plan beyond rounding (tokens are summed in another order).
  *   partition_size: PA_PARTITION_NONE, PA_PARTITION_BALANCED, or a positive
  *     multiple of block_size: each (sequence, KV head) is split into chunks
  *     of that many tokens whose partial softmax states are merged by a second
@@ -418,7 +472,9 @@ pa_status pa_decode_append(const void *q, const void *k_new, const void *v_new,
  * each partition's softmax state (running max, sum, unnormalised output) in
  * the workspace; with PA_PARTITION_BALANCED it also writes to `out` the rows
  * of every (sequence, KV head) that one work item covers whole.
- * pa_decode_merge combines the partial states into the other rows of `out`.
+ * pa_decode_merge combines the partial states into the other rows of `out`;
+ * it takes the same seq_shared (the share plan, or NULL), since where the
+ * partial states lie depends on it.
  * Issued in this order on one stream, with the same `out`, they compute what
  * pa_decode computes, bit for bit (it launches the same two kernels); a caller
  * may time or schedule the two separately.  `out` must not be NULL
@@ -430,10 +486,10 @@ pa_status pa_decode_partials(const void *q, const void *k_cache, const void *v_c
                              float scale, float k_scale, float v_scale, void *out,
                              void *workspace, size_t workspace_bytes, int32_t partition_size,
                              const pa_kv_desc *desc, void *stream);
-pa_status pa_decode_merge(const int32_t *seq_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
-                          int32_t max_seq_len, void *out, const void *workspace,
-                          size_t workspace_bytes, int32_t partition_size, const pa_kv_desc *desc,
-                          void *stream);
+pa_status pa_decode_merge(const int32_t *seq_lens, const int32_t *seq_shared, int32_t num_seqs,
+                          int32_t max_blocks_per_seq, int32_t max_seq_len, void *out,
+                          const void *workspace, size_t workspace_bytes, int32_t partition_size,
+                          const pa_kv_desc *desc, void *stream);
 
 /* ------------------------------------------------------------------------ */
 /* Measurement.                                                             */
@@ -472,11 +528,14 @@ pa_status pa_read_probe(const void *buf, size_t bytes, int32_t loads_in_flight,
  * process ends.  The call allocates and frees nothing (no hipMalloc, hipFree
  * or allocating library routine); the caller still passes every input and
  * output.  The scratch needs no initial contents.
- *   Limit: PA_ERR_CAPACITY, before anything is launched, when
- *   pa_decode_workspace_bytes(desc, num_seqs, max_seq_len, partition_size)
- *   exceeds PA_NOALLOC_SCRATCH_BYTES (with PA_PARTITION_BALANCED that holds
- *   up to about 7,000 (sequence, KV head) pairs at group 4 and head_dim 128);
- *   PA_PARTITION_NONE needs no scratch.
+ *   Limit: PA_ERR_CAPACITY, before anything is launched, when the partial
+ *   states exceed PA_NOALLOC_SCRATCH_BYTES: those of
+ *   pa_decode_workspace_bytes(desc, num_seqs, max_seq_len, partition_size),
+ *   or with PA_PARTITION_BALANCED those of a launch without a share plan's
+ *   rows (that holds up to about 7,000 (sequence, KV head) pairs at group 4
+ *   and head_dim 128); a share plan's rows are read once per KV head only
+ *   when their room fits in the scratch as well.  PA_PARTITION_NONE needs no
+ *   scratch.
  *   Sharing: every call on one GPU uses that GPU's one scratch array, and it
  *   keeps the last call's contents.  Calls that may overlap on one GPU (on
  *   different streams, or from different threads) race on it and give wrong

@@ -40,6 +40,12 @@ DTYPE_BYTES = {F32: 4, F16: 2, BF16: 2, FP8_E4M3: 1}
 KERNEL_AUTO, KERNEL_VALU, KERNEL_MFMA = 0, 1, 2
 PARTITION_NONE, PARTITION_BALANCED = 0, -1
 NOALLOC_SCRATCH_BYTES = 16 << 20  # PA_NOALLOC_SCRATCH_BYTES
+SHARE_PLAN_MAGIC = 0x31534150      # PA_SHARE_PLAN_MAGIC
+
+
+def share_plan_words(nseq):
+    """PA_SHARE_PLAN_WORDS: int32 words of a share plan for nseq sequences."""
+    return 2 + 8 * nseq
 
 
 class PaError(RuntimeError):
@@ -97,14 +103,16 @@ _SIGS = {
     "pa_cache_append": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, ctypes.POINTER(KvDesc),
                                        ctypes.c_float, ctypes.c_float, _P]),
     "pa_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(KvDesc), _I32, _I32, _I32]),
+    "pa_decode_balanced_waves": (_I32, [ctypes.POINTER(KvDesc)]),
     "pa_decode": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _P, _P, _I32, _I32, ctypes.c_float,
                                  ctypes.c_float, ctypes.c_float, _P, _P, ctypes.c_size_t, _I32,
                                  ctypes.POINTER(KvDesc), _P]),
     "pa_decode_partials": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _P, _P, _I32, _I32,
                                           ctypes.c_float, ctypes.c_float, ctypes.c_float, _P, _P,
                                           ctypes.c_size_t, _I32, ctypes.POINTER(KvDesc), _P]),
-    "pa_decode_merge": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _P, ctypes.c_size_t, _I32,
+    "pa_decode_merge": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P, _P, ctypes.c_size_t, _I32,
                                        ctypes.POINTER(KvDesc), _P]),
+    "pa_export_share_plan": (ctypes.c_int, [_P, _P, _I32, _P]),
     "pa_decode_append": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _I32, _I32,
                                         ctypes.c_float, ctypes.c_float, ctypes.c_float, _P, _P,
                                         ctypes.c_size_t, _I32, _P, _P]),
@@ -261,6 +269,26 @@ def pa_export_block_tables(pool, seqs, max_blocks, tables_out=None, lens_out=Non
     if sh is not None:
         out += (sh,)
     return out
+
+
+def pa_export_share_plan(pool, seqs, out=None):
+    """The share plan of resident sequences `seqs` (pa.h layout): int32
+    [share_plan_words(len(seqs))], into `out` (numpy or pinned tensor) when
+    given.  Pass it to the decode calls as seq_shared, on the device."""
+    seqs = _i32_array(seqs)
+    words = share_plan_words(len(seqs))
+    plan = out if out is not None else np.empty(words, np.int32)
+    if isinstance(plan, np.ndarray):
+        ok = plan.dtype == np.int32 and plan.flags.c_contiguous and plan.size >= words
+    else:
+        import torch
+        ok = (plan.dtype == torch.int32 and plan.device.type == "cpu" and plan.is_contiguous()
+              and plan.numel() >= words)
+    if not ok:
+        raise ValueError(f"out must be a contiguous host int32 buffer of >= {words} words")
+    _check(_lib.pa_export_share_plan(pool.handle, seqs.ctypes.data, len(seqs), _addr(plan)),
+           "pa_export_share_plan")
+    return plan
 
 
 def pa_seq_slide_window(pool, seq, window):
@@ -432,6 +460,12 @@ def pa_swap_blocks(k_cache, v_cache, host_k, host_v, pairs, desc, to_host, strea
                                ctypes.byref(desc), _stream(stream)), "pa_swap_blocks")
 
 
+def pa_decode_balanced_waves(desc):
+    """Runs of a balanced launch of this shape on the current device (0 if
+    the shape does not take the balanced mode)."""
+    return int(_lib.pa_decode_balanced_waves(ctypes.byref(desc)))
+
+
 def pa_decode_workspace_bytes(desc, num_seqs, max_seq_len, partition_size):
     return int(_lib.pa_decode_workspace_bytes(ctypes.byref(desc), num_seqs, max_seq_len,
                                               partition_size))
@@ -446,6 +480,15 @@ def _per_seq(x, name, B):
 
 def _starts(seq_starts, B):
     return _per_seq(seq_starts, "seq_starts", B)
+
+
+def _plan(seq_shared, B):
+    """seq_shared: the batch's share plan (pa_export_share_plan), an int32
+    device tensor of share_plan_words(B) words, or None."""
+    if seq_shared is None:
+        return None
+    _check_i32(seq_shared, "seq_shared", share_plan_words(B))
+    return _addr(seq_shared)
 
 
 def pa_decode(q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale, out, desc,
@@ -466,7 +509,7 @@ def pa_decode(q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale, o
         ws_bytes = workspace.numel() * workspace.element_size()
     _check(_lib.pa_decode(_addr(q), _addr(k_cache), _addr(v_cache), _addr(block_tables),
                           block_tables.shape[1], _addr(seq_lens), _starts(seq_starts, B),
-                          _per_seq(seq_shared, "seq_shared", B), B, max_seq_len, scale, k_scale, v_scale, _addr(out), _addr(workspace),
+                          _plan(seq_shared, B), B, max_seq_len, scale, k_scale, v_scale, _addr(out), _addr(workspace),
                           ws_bytes, partition_size, ctypes.byref(desc), _stream(stream)),
            "pa_decode")
 
@@ -495,7 +538,7 @@ def pa_decode_append(q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tabl
     _check(_lib.pa_decode_append(_addr(q), _addr(k_new), _addr(v_new), _addr(slot_mapping),
                                  _addr(k_cache), _addr(v_cache), _addr(block_tables),
                                  block_tables.shape[1], _addr(seq_lens), _starts(seq_starts, B),
-                                 _per_seq(seq_shared, "seq_shared", B), B, max_seq_len, scale, k_scale, v_scale, _addr(out),
+                                 _plan(seq_shared, B), B, max_seq_len, scale, k_scale, v_scale, _addr(out),
                                  _addr(workspace), ws_bytes, partition_size, ctypes.byref(desc),
                                  _stream(stream)), "pa_decode_append")
 
@@ -522,7 +565,7 @@ def pa_decode_append_noalloc(q, k_new, v_new, slot_mapping, k_cache, v_cache, bl
     _check(_lib.pa_decode_append_noalloc(
         _addr(q), _addr(k_new), _addr(v_new), _addr(slot_mapping), _addr(k_cache),
         _addr(v_cache), _addr(block_tables), block_tables.shape[1], _addr(seq_lens),
-        _starts(seq_starts, B), _per_seq(seq_shared, "seq_shared", B), B, max_seq_len, scale,
+        _starts(seq_starts, B), _plan(seq_shared, B), B, max_seq_len, scale,
         k_scale, v_scale, _addr(out), partition_size, ctypes.byref(desc), _stream(stream)),
         "pa_decode_append_noalloc")
 
@@ -545,7 +588,7 @@ def pa_decode_partials(q, k_cache, v_cache, block_tables, seq_lens, max_seq_len,
     _check_tensor(workspace, "workspace")
     _check(_lib.pa_decode_partials(_addr(q), _addr(k_cache), _addr(v_cache), _addr(block_tables),
                                    block_tables.shape[1], _addr(seq_lens),
-                                   _starts(seq_starts, B), _per_seq(seq_shared, "seq_shared", B),
+                                   _starts(seq_starts, B), _plan(seq_shared, B),
                                    B, max_seq_len, scale,
                                    k_scale, v_scale, _addr(out), _addr(workspace),
                                    workspace.numel() * workspace.element_size(), partition_size,
@@ -553,13 +596,14 @@ def pa_decode_partials(q, k_cache, v_cache, block_tables, seq_lens, max_seq_len,
 
 
 def pa_decode_merge(seq_lens, max_blocks_per_seq, max_seq_len, out, desc, workspace,
-                    partition_size, stream=None):
+                    partition_size, stream=None, seq_shared=None):
     B = seq_lens.numel()
     qrow = desc.num_q_heads * desc.head_dim
     _check_i32(seq_lens, "seq_lens", B)
     _check_tensor(workspace, "workspace")
     _check_tensor(out, "out", B * qrow * DTYPE_BYTES[desc.q_dtype])
-    _check(_lib.pa_decode_merge(_addr(seq_lens), B, max_blocks_per_seq, max_seq_len, _addr(out),
+    _check(_lib.pa_decode_merge(_addr(seq_lens), _plan(seq_shared, B), B, max_blocks_per_seq,
+                                max_seq_len, _addr(out),
                                 _addr(workspace), workspace.numel() * workspace.element_size(),
                                 partition_size, ctypes.byref(desc), _stream(stream)),
            "pa_decode_merge")

@@ -115,6 +115,47 @@ int32_t balanced_waves(const pa_kv_desc *d)
     return w;
 }
 
+// The kernel a launch runs: PA_KERNEL_AUTO takes MFMA where it applies.
+int resolved_kernel(const pa_kv_desc *d)
+{
+    const int G = d->num_q_heads / d->num_kv_heads;
+    if (d->kernel != PA_KERNEL_AUTO)
+        return d->kernel;
+    return mfma_supports(d->q_dtype, d->kv_dtype, d->head_dim, G) ? PA_KERNEL_MFMA
+                                                                    : PA_KERNEL_VALU;
+}
+
+// Whether a balanced launch of this shape can read a share plan's groups once
+// per KV head: the MFMA kernel, 16 / G members per 16-column tile, and a
+// G x D the one-wave segment merge handles (a power-of-two multiple of 256 up
+// to 2048).
+bool prefix_capable(const pa_kv_desc *d)
+{
+    const int G = d->num_q_heads / d->num_kv_heads;
+    const int gd = G * d->head_dim;
+    return resolved_kernel(d) == PA_KERNEL_MFMA &&
+           mfma_supports(d->q_dtype, d->kv_dtype, d->head_dim, G) && 16 % G == 0 &&
+           gd % 256 == 0 && (gd / 256 == 1 || gd / 256 == 2 || gd / 256 == 4 || gd / 256 == 8);
+}
+
+// Partial-state slots of a balanced launch with W waves: one per (run,
+// sequence segment) pair, W + B Hkv; with prefix rows, (W + Hkv B / 2) row
+// pieces of 4 x 16 / G member slots each on top.
+int64_t balanced_seq_slots(const pa_kv_desc *d, int32_t W, int32_t num_seqs)
+{
+    return (int64_t)W + (int64_t)num_seqs * d->num_kv_heads;
+}
+int64_t balanced_row_slots(const pa_kv_desc *d, int32_t W, int32_t num_seqs)
+{
+    const int G = d->num_q_heads / d->num_kv_heads;
+    return ((int64_t)W + (int64_t)d->num_kv_heads * (num_seqs / 2)) * (4 * (16 / G));
+}
+size_t slot_bytes(const pa_kv_desc *d, int64_t slots)
+{
+    const int64_t G = d->num_q_heads / d->num_kv_heads;
+    return (size_t)(slots * G * (2 + d->head_dim) * (int64_t)sizeof(float));
+}
+
 int32_t parts_for(int32_t max_seq_len, int32_t partition)
 {
     if (partition <= 0)
@@ -248,13 +289,28 @@ size_t pa_decode_workspace_bytes(const pa_kv_desc *desc, int32_t num_seqs, int32
         partition_size < PA_PARTITION_BALANCED || desc->num_kv_heads <= 0 ||
         desc->num_q_heads <= 0 || desc->head_dim <= 0)
         return 0;
-    const int64_t G = desc->num_q_heads / desc->num_kv_heads;
     int64_t slots;
-    if (partition_size == PA_PARTITION_BALANCED)
-        slots = (int64_t)balanced_waves(desc) + (int64_t)num_seqs * desc->num_kv_heads;
-    else
+    if (partition_size == PA_PARTITION_BALANCED) {
+        const int32_t W = balanced_waves(desc);
+        if (W <= 0)
+            return 0;
+        slots = balanced_seq_slots(desc, W, num_seqs);
+        if (prefix_capable(desc))
+            slots += balanced_row_slots(desc, W, num_seqs);
+    } else {
         slots = (int64_t)num_seqs * desc->num_kv_heads * parts_for(max_seq_len, partition_size);
-    return (size_t)(slots * G * (2 + desc->head_dim) * (int64_t)sizeof(float));
+    }
+    return slot_bytes(desc, slots);
+}
+
+int32_t pa_decode_balanced_waves(const pa_kv_desc *desc)
+{
+    if (check_desc(desc) != PA_OK || resolved_kernel(desc) != PA_KERNEL_MFMA)
+        return 0;
+    const int G = desc->num_q_heads / desc->num_kv_heads;
+    if (!mfma_supports(desc->q_dtype, desc->kv_dtype, desc->head_dim, G))
+        return 0;
+    return balanced_waves(desc);
 }
 
 } // extern "C"
@@ -347,7 +403,7 @@ pa_status decode_impl(Phase phase, const void *q, const void *k_cache, const voi
     a.block_tables = block_tables;
     a.seq_lens = seq_lens;
     a.seq_starts = seq_starts;
-    a.seq_shared = seq_shared;
+    a.share = seq_shared;
     a.out = out;
     a.ws = static_cast<float *>(workspace);
     a.num_seqs = num_seqs;
@@ -375,11 +431,9 @@ pa_status decode_impl(Phase phase, const void *q, const void *k_cache, const voi
         a.v_inv = desc->kv_dtype == PA_FP8_E4M3 ? 1.0f / v_scale : 1.f;
     }
 
-    int kernel = desc->kernel;
-    if (kernel == PA_KERNEL_AUTO)
-        kernel = mfma_supports(desc->q_dtype, desc->kv_dtype, D, G) ? PA_KERNEL_MFMA
-                                                                      : PA_KERNEL_VALU;
+    const int kernel = resolved_kernel(desc);
     int64_t items64;
+    size_t need = 0;
     if (balanced) {
         if (kernel != PA_KERNEL_MFMA)
             return fail(PA_ERR_UNSUPPORTED, "balanced partitioning needs the MFMA kernel");
@@ -387,20 +441,31 @@ pa_status decode_impl(Phase phase, const void *q, const void *k_cache, const voi
         if (a.waves <= 0)
             return fail(PA_ERR_HIP, "could not query the device for the balanced split");
         items64 = a.waves;
-        a.num_slots = (int64_t)a.waves + (int64_t)num_seqs * desc->num_kv_heads;
+        a.num_slots = balanced_seq_slots(desc, a.waves, num_seqs);
+        need = slot_bytes(desc, a.num_slots);
+        // prefix rows: with a plan, a capable shape and room for their
+        // partial states after the sequences' slots (the same decision for
+        // the partials and the merge launch; a plan groups no sequence with
+        // a slid window)
+        const int64_t with_rows = a.num_slots + balanced_row_slots(desc, a.waves, num_seqs);
+        if (seq_shared && prefix_capable(desc) &&
+            workspace_bytes >= slot_bytes(desc, with_rows)) {
+            a.prefix = 1;
+            a.prefix_base = a.num_slots;
+            a.num_slots = with_rows;
+        }
     } else {
         items64 = (int64_t)num_seqs * desc->num_kv_heads * a.max_parts;
         a.waves = 0;
         a.num_slots = items64;
+        if (partition_size != 0)
+            need = pa_decode_workspace_bytes(desc, num_seqs, max_seq_len, partition_size);
     }
     if (items64 > (int64_t)1 << 30)
         return fail(PA_ERR_INVALID_ARG, "too many work items");
     const int32_t items = (int32_t)items64;
-    if (partition_size != 0) {
-        const size_t need = pa_decode_workspace_bytes(desc, num_seqs, max_seq_len, partition_size);
-        if (!workspace || need == 0 || workspace_bytes < need)
-            return fail(PA_ERR_CAPACITY, "workspace smaller than pa_decode_workspace_bytes()");
-    }
+    if (partition_size != 0 && (!workspace || need == 0 || workspace_bytes < need))
+        return fail(PA_ERR_CAPACITY, "workspace smaller than pa_decode_workspace_bytes()");
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
@@ -497,8 +562,11 @@ pa_status pa_decode_append_noalloc(const void *q, const void *k_new, const void 
     void *ws = nullptr;
     size_t ws_bytes = 0;
     if (num_seqs > 0 && partition_size != PA_PARTITION_NONE) {
-        const size_t need =
-            pa_decode_workspace_bytes(desc, num_seqs, max_seq_len, partition_size);
+        // the room without prefix rows; the scratch is offered whole, so a
+        // plan's rows are read when their room fits as well
+        size_t need = pa_decode_workspace_bytes(desc, num_seqs, max_seq_len, partition_size);
+        if (need != 0 && partition_size == PA_PARTITION_BALANCED)
+            need = slot_bytes(desc, balanced_seq_slots(desc, balanced_waves(desc), num_seqs));
         if (need == 0)
             return fail(PA_ERR_INVALID_ARG, "bad partition_size or shape (or no device to size "
                                             "the balanced split for)");
@@ -513,7 +581,7 @@ pa_status pa_decode_append_noalloc(const void *q, const void *k_new, const void 
         st = noalloc_scratch(&ws);
         if (st != PA_OK)
             return st;
-        ws_bytes = need;
+        ws_bytes = kNoallocScratchBytes;
     }
     NewTokens nt;
     nt.k = k_new;
@@ -537,13 +605,13 @@ pa_status pa_decode_partials(const void *q, const void *k_cache, const void *v_c
                        v_scale, out, workspace, workspace_bytes, partition_size, desc, stream);
 }
 
-pa_status pa_decode_merge(const int32_t *seq_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
-                          int32_t max_seq_len, void *out, const void *workspace,
-                          size_t workspace_bytes, int32_t partition_size, const pa_kv_desc *desc,
-                          void *stream)
+pa_status pa_decode_merge(const int32_t *seq_lens, const int32_t *seq_shared, int32_t num_seqs,
+                          int32_t max_blocks_per_seq, int32_t max_seq_len, void *out,
+                          const void *workspace, size_t workspace_bytes, int32_t partition_size,
+                          const pa_kv_desc *desc, void *stream)
 {
     return decode_impl(kMerge, nullptr, nullptr, nullptr, nullptr, max_blocks_per_seq, seq_lens,
-                       nullptr, nullptr, num_seqs, max_seq_len, 1.f, 1.f, 1.f, out,
+                       nullptr, seq_shared, num_seqs, max_seq_len, 1.f, 1.f, 1.f, out,
                        const_cast<void *>(workspace), workspace_bytes, partition_size, desc,
                        stream);
 }

@@ -408,7 +408,7 @@ struct MfmaWave {
     // not read), if the window start is outside [0, n], or if the step's
     // token is to be appended here (a.append and t1 == n) and its slot is not
     // the cache slot of position n - 1.
-    // HINT: a.seq_shared is set (the launch reads it once per range and
+    // HINT: a.share is set (the launch reads its hint once per range and
     // picks the cache policy per tile); without it every tile streams.
     template <bool HINT>
     __device__ bool run(const DecodeArgs &a, int32_t b, int32_t g, int32_t t0, int32_t t1,
@@ -462,22 +462,37 @@ struct MfmaWave {
         };
         // The step's token (position t1 - 1) when this range ends the
         // sequence.  Its row is loaded before any tile (the addresses need
-        // nothing but b and g); after the first ring has issued its first
-        // tiles' loads, the slot is checked, the token converted and stored
-        // to the cache, so none of this delays the tile stream; when the last
-        // tile is computed the token replaces its slot in the registers.
+        // nothing but b and g).  The slot is checked and the token converted
+        // (prepare_token): for FP8, whose ring holds three tiles in flight,
+        // once those are issued (keeping the raw FP8 row live through the
+        // ring would spill); for 16-bit KV, whose ring holds one, just
+        // before the last tile is computed (a wait after the first tile's
+        // loads would hold back the second's).  The token replaces its slot
+        // in the last tile's registers, and once every tile is in, it is
+        // stored to the cache: no store precedes a tile's loads (the vector
+        // memory counter covers stores too, so the wait for that tile would
+        // wait for the store's acknowledgement as well).
+        constexpr bool kPrepareEarly = KE == 1;
         bool put = false;
         NewToken nt;
         RawToken rt;
-        int32_t slot = -1, id_last = 0;
+        // The token's slot and the block id of the last tile come in with
+        // vector loads: scalar loads may complete out of order, so the
+        // first tile's block id (a scalar load) would wait for these too,
+        // and the slots are cold at launch.
+        int32_t slot_v = -1, id_last_v = 0, slot = -1, id_last = 0;
         const int32_t off_last = (t1 - 1) & ((kTile << sh) - 1); // in its block
         if (append_here) {
-            slot = uniform(((const CI32 *)a.slots)[b]);
-            id_last = id_of(last);
+            using GI32 = __attribute__((address_space(1))) const int32_t;
+            slot_v = __builtin_nontemporal_load((GI32 *)(a.slots + b));
+            id_last_v = __builtin_nontemporal_load(
+                (GI32 *)(a.block_tables + (size_t)b * a.max_blocks_per_seq + (last >> sh)));
             load_token_raw(a, b, g, rt);
         }
-        auto after_first_loads = [&]() {
-            if (!append_here || slot < 0)
+        auto prepare_token = [&]() {
+            slot = uniform(slot_v);
+            id_last = uniform(id_last_v);
+            if (slot < 0)
                 return;
             if ((uint32_t)id_last >= nblocks || slot != (id_last << sh) * kTile + off_last) {
                 bad = true;
@@ -485,7 +500,6 @@ struct MfmaWave {
             }
             put = true;
             finish_token(a, rt, (t1 - 1) % kTile, nt);
-            store_new_token(a, nt, id_last, off_last, sh, g);
         };
         // With the hint, the block ids of the first DEPTH tiles are fetched
         // before the split below is known (every range starts with a ring at
@@ -517,8 +531,8 @@ struct MfmaWave {
                 load(checked(HINT && first ? id0[d] : id_at(s0 + d)), s0 + d, T[d]);
             // block id of the next tile to load
             int32_t id_next = HINT && first ? id0[DEPTH - 1] : id_at(s0 + DEPTH - 1);
-            if (hook)
-                after_first_loads();
+            if (kPrepareEarly && append_here && hook)
+                prepare_token();
             int32_t i = 0;
             for (; i + DEPTH <= n; i = uniform(i + DEPTH)) {
 #pragma unroll
@@ -527,8 +541,12 @@ struct MfmaWave {
                     const int32_t id_after = id_at(jb + DEPTH); // one tile ahead of use
                     load(checked(id_next), jb + DEPTH - 1, T[(d + DEPTH - 1) % DEPTH]);
                     __builtin_amdgcn_sched_barrier(0); // that load goes out before T[d] is waited for
-                    if (put && jb == last)
-                        apply_new_token(T[d], nt);
+                    if (append_here && jb == last) {
+                        if (!kPrepareEarly)
+                            prepare_token();
+                        if (put)
+                            apply_new_token(T[d], nt);
+                    }
                     compute(T[d], lo_of(jb), valid_of(jb), sc);
                     id_next = id_after;
                 }
@@ -538,8 +556,12 @@ struct MfmaWave {
             for (int d = 0; d + 1 < DEPTH; ++d) {
                 if (i + d < n) {
                     const int32_t jb = s0 + i + d;
-                    if (put && jb == last)
-                        apply_new_token(T[d], nt);
+                    if (append_here && jb == last) {
+                        if (!kPrepareEarly)
+                            prepare_token();
+                        if (put)
+                            apply_new_token(T[d], nt);
+                    }
                     compute(T[d], lo_of(jb), valid_of(jb), sc);
                 }
             }
@@ -551,7 +573,7 @@ struct MfmaWave {
         // sequences of the batch: their tiles go through a ring of caching
         // loads, the rest through a ring of streaming loads.
         if constexpr (HINT) {
-            int32_t shared = uniform(((const CI32 *)a.seq_shared)[b]);
+            int32_t shared = uniform(((const CI32 *)plan_shared(a))[b]);
             shared = min(max(shared, 0), a.max_blocks_per_seq);
             const int32_t split = uniform(min(max(shared << sh, jb0), last + 1));
             if (split > jb0)
@@ -562,6 +584,8 @@ struct MfmaWave {
         } else {
             ring(std::integral_constant<bool, true>{}, jb0, last, false, true);
         }
+        if (put)
+            store_new_token(a, nt, id_last, off_last, sh, g);
         return !bad;
     }
 
@@ -603,7 +627,7 @@ struct MfmaWave {
 };
 
 // partition == 0 or > 0: one wave per work item (see work.hpp).  HINT:
-// a.seq_shared is set; each kernel is built with and without it, so the
+// a.share is set; each kernel is built with and without it, so the
 // launches without the hint run the same code as before it existed.
 template <int QT, int KT, int D, bool HINT>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a, int32_t num_items)
@@ -629,6 +653,166 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a, int32_t 
         wv.write_partial(a, w, ok);
 }
 
+// Tiles [j, je) of prefix row `pos` (head pos.g; members [chunk SPR,
+// (chunk + 1) SPR) of group pos.gi in rank order, SPR = kPrefixColGroups *
+// 16 / G).  The group's shared tiles are read once, through its first
+// member's table, with loads that keep them in the caches (the head's other
+// rows read the same tiles), and applied to kPrefixColGroups column groups
+// of 16 MFMA columns: 16 / G members times G query heads each, so one tile
+// load serves SPR sequences.  Per member and query head, the partial state
+// (m, l, acc) goes to slot slot0 + (rank - chunk SPR); the merge folds it with
+// the member's other parts.  A block id outside the pool makes the piece's
+// states NaN.
+template <int QT, int KT, int D>
+__device__ void prefix_piece(const DecodeArgs &a, int lane, const SegPos &pos, int32_t j,
+                             int32_t je, int64_t slot0)
+{
+    using Wv = MfmaWave<QT, KT, D>;
+    using Tile = typename Wv::Tile;
+    using A8 = typename Wv::A8;
+    using TQ = typename Store<QT>::T;
+    using CI32 = __attribute__((address_space(4))) const int32_t;
+    constexpr int CG = kPrefixColGroups;
+    // One more tile in flight than a sequence's ring: a row tile comes from
+    // L2 and its loads must land while the tile before is computed for
+    // every column group.
+    constexpr int DEPTH = Wv::DEPTH + 1;
+    static_assert(CG == 4, "four column groups");
+    const int32_t G = a.group, spc = 16 / G;
+    const int32_t gi = uniform(pos.gi), g = uniform(pos.g);
+    const int32_t count = uniform(group_count(a, gi));
+    const int32_t first = uniform(min(max(plan_gfirst(a)[gi], 0), a.num_seqs - count));
+    const int32_t lead = uniform(min(max(plan_members(a)[first], 0), a.num_seqs - 1));
+    const int32_t rank0 = uniform(pos.chunk * prefix_row_seqs(G));
+
+    // column col of group cg: member rank0 + cg spc + col / G, query head col % G
+    const int col = lane & 15, grp = lane >> 4;
+    const int32_t mcol = col / G, h = col % G;
+    Wv wv[CG] = {Wv(lane), Wv(lane), Wv(lane), Wv(lane)};
+    bool real[CG];
+#pragma unroll
+    for (int cg = 0; cg < CG; ++cg) {
+        const int32_t k = cg * spc + mcol;
+        real[cg] = mcol < spc && rank0 + k < count;
+        const int32_t b =
+            real[cg] ? min(max(plan_members(a)[first + rank0 + k], 0), a.num_seqs - 1) : 0;
+        const TQ *qp = static_cast<const TQ *>(a.q) +
+                       ((size_t)b * a.num_q_heads + (size_t)g * G + h) * D;
+#pragma unroll
+        for (int m = 0; m < Wv::QK_MMAS; ++m) {
+            int d0;
+            if constexpr (Store<KT>::bytes == 2)
+                d0 = (grp + 4 * m) * 8;
+            else
+                d0 = (grp + 4 * (m / 2)) * 16 + 8 * (m % 2);
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (real[cg])
+                v = load16(qp + d0);
+            wv[cg].qop[m] = __builtin_bit_cast(A8, v);
+        }
+#pragma unroll
+        for (int t = 0; t < Wv::PV_TILES; ++t)
+            wv[cg].acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        wv[cg].m_run = kMaxStart;
+        wv[cg].l_run = 0.f;
+    }
+
+    // tiles [j, je) of the lead's table, DEPTH - 1 in flight while one is
+    // computed
+    const int32_t sh = a.tile_shift;
+    const int32_t mask = (1 << sh) - 1;
+    const CI32 *table = (const CI32 *)(a.block_tables + (size_t)lead * a.max_blocks_per_seq);
+    const char *kbase = static_cast<const char *>(a.k_cache) + ((size_t)g << sh) * Wv::TILE_BYTES;
+    const char *vbase = static_cast<const char *>(a.v_cache) + ((size_t)g << sh) * Wv::TILE_BYTES;
+    const size_t bstride = ((size_t)a.num_kv_heads << sh) * Wv::TILE_BYTES;
+    const uint32_t nblocks = (uint32_t)a.num_blocks;
+    const float sc = a.score_scale;
+    const int32_t s0 = uniform(j), s1 = uniform(je - 1);
+    bool bad = false;
+    auto id_at = [&](int32_t jb) -> int32_t { return uniform(table[uniform(min(jb, s1) >> sh)]); };
+    auto load = [&](int32_t id, int32_t jb, Tile &T) {
+        const bool out = (uint32_t)id >= nblocks;
+        bad |= out;
+        jb = min(jb, s1);
+        const size_t o = (size_t)(out ? 0 : id) * bstride + (size_t)(jb & mask) * Wv::TILE_BYTES;
+        Wv::template load_tile<false>(kbase + o, vbase + o, col, grp, T);
+    };
+    Tile T[DEPTH];
+    const int32_t n = s1 - s0 + 1;
+#pragma unroll
+    for (int d = 0; d + 1 < DEPTH; ++d)
+        load(id_at(s0 + d), s0 + d, T[d]);
+    int32_t id_next = id_at(s0 + DEPTH - 1);
+    int32_t i = 0;
+    for (; i + DEPTH <= n; i = uniform(i + DEPTH)) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+            const int32_t jb = s0 + i + d;
+            const int32_t id_after = id_at(jb + DEPTH);
+            load(id_next, jb + DEPTH - 1, T[(d + DEPTH - 1) % DEPTH]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int cg = 0; cg < CG; ++cg)
+                wv[cg].compute(T[d], 0, kTile, sc);
+            id_next = id_after;
+        }
+    }
+#pragma unroll
+    for (int d = 0; d + 1 < DEPTH; ++d) {
+        if (i + d < n) {
+#pragma unroll
+            for (int cg = 0; cg < CG; ++cg)
+                wv[cg].compute(T[d], 0, kTile, sc);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+
+#pragma unroll
+    for (int cg = 0; cg < CG; ++cg) {
+        wv[cg].finish();
+        if (!real[cg])
+            continue;
+        const int64_t slot = slot0 + cg * spc + mcol;
+        if (grp == 0) {
+            float *ml = ws_ml(a, slot, h);
+            ml[0] = bad ? NAN : wv[cg].m_run;
+            ml[1] = bad ? NAN : wv[cg].l_run;
+        }
+        float *accp = ws_acc(a, slot, h, D);
+        const float f = bad ? NAN : a.v_scale;
+#pragma unroll
+        for (int t = 0; t < Wv::PV_TILES; ++t)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                accp[16 * t + 4 * grp + q] = wv[cg].acc[t][q] * f;
+    }
+}
+
+// Run r of Wr in the rows' split: the row pieces its units [x0, x1) meet.
+template <int QT, int KT, int D>
+__device__ void decode_rows(const DecodeArgs &a, int lane, int32_t r, int32_t Wr,
+                            const PrefixHead &P)
+{
+    const RunStart rs = row_run_start(a, lane, r, Wr, P);
+    if (r >= rs.runs)
+        return;
+    SegPos pos = rs.pos;
+    int64_t x = rs.x0;
+    while (x < rs.x1) {
+        const int64_t r0 = pos.first_tile + kSegmentCost; // the row's tile 0
+        const int64_t end = r0 + row_body(pos.n);
+        const int64_t lo = max(x, r0), hi = min(rs.x1, end);
+        if (hi > lo) {
+            const int32_t j = row_tile_at(lo - r0), je = min(pos.n, row_tile_at(hi - r0));
+            if (je > j)
+                prefix_piece<QT, KT, D>(a, lane, pos, j, je, row_slot(a, r, pos.g, pos.row, P));
+        }
+        x = end;
+        if (x < rs.x1)
+            pos = next_row(a, lane, pos, P);
+    }
+}
+
 // Bytes of the block tables each wave touches at launch (two 1 KiB loads):
 // the waves of one XCD together cover the first W/8 * 2 KiB of the tables.
 constexpr int kTablePrefetchLoads = 2;
@@ -645,8 +829,8 @@ void decode_mfma_balanced_kernel(DecodeArgs a, int32_t W)
     __shared__ u32x4 table_sink[4][kWave]; // receives the prefetch, never read
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int32_t i = balanced_run(blockIdx.x, wave, W);
-    if (i >= W)
+    const int32_t i0 = balanced_run(blockIdx.x, wave, W);
+    if (i0 >= W)
         return;
 
     // A decode step's tables are cold (the host wrote them for this step),
@@ -658,7 +842,7 @@ void decode_mfma_balanced_kernel(DecodeArgs a, int32_t W)
     {
         const int64_t tbytes = (int64_t)a.num_seqs * a.max_blocks_per_seq * 4;
         const int32_t per_xcd = W % (4 * kXcds) == 0 ? W / kXcds : W;
-        const int32_t k = W % (4 * kXcds) == 0 ? (blockIdx.x / kXcds) * 4 + wave : i;
+        const int32_t k = W % (4 * kXcds) == 0 ? (blockIdx.x / kXcds) * 4 + wave : i0;
         const char *tb = reinterpret_cast<const char *>(a.block_tables);
         // (a hint only: skipped for a table that is not 16-byte aligned)
         const int64_t tbytes_in = (reinterpret_cast<uintptr_t>(tb) & 15) == 0 ? tbytes : 0;
@@ -671,37 +855,58 @@ void decode_mfma_balanced_kernel(DecodeArgs a, int32_t W)
         }
     }
 
-    // T, the number of runs (never more than tiles), and the segment holding
-    // this wave's first tile
-    const RunStart rs = run_start(a, lane, i, W);
+    // Prefix rows only come with a share plan, which also turns on HINT: the
+    // launches without one run the code they ran before rows existed.
+    PrefixHead P{false, 0, 0, 0};
+    if constexpr (HINT)
+        P = prefix_head(a, lane);
+    int32_t i = i0, Wseq = W;
+    if (HINT && P.on) {
+        // this wave's run in the rows' split or in the sequences'
+        const int32_t Wr = row_runs(a, P, head_tiles(a, lane, 0, P).per_head, W);
+        const int32_t per = W / kXcds, rx = Wr / kXcds;
+        const int32_t x = i0 / per, loc = i0 - x * per;
+        if (loc < rx) {
+            decode_rows<QT, KT, D>(a, lane, x * rx + loc, Wr, P);
+            return;
+        }
+        i = x * (per - rx) + (loc - rx);
+        Wseq = W - Wr;
+    }
+
+    // T, the number of runs (never more than units), and the segment holding
+    // this wave's first unit
+    const RunStart rs = run_start(a, lane, i, Wseq, P);
     if (i >= rs.runs)
         return;
     const int64_t x1 = rs.x1;
     SegPos pos = rs.pos;
 
-    // The run's virtual tiles [x0, x1) meet each segment's start charge and
-    // real tiles in turn; a piece of real tiles is a range to decode (a run
-    // may begin or end inside a start charge, which holds nothing to read).
+    // The run's units [x0, x1) meet each segment's start charge and tiles in
+    // turn; a piece of tiles is a range to decode (a run may begin or end
+    // inside a start charge, which holds nothing to read).
     MfmaWave<QT, KT, D> wv(lane);
     int64_t x = rs.x0;
     while (x < x1) {
-        const int32_t nb = tiles_of(pos.n);
-        const int64_t r0 = pos.first_tile + kSegmentCost; // the segment's tile 0
+        // the sequence's tiles past the ones its prefix row reads
+        const int32_t nb = tiles_of(pos.n) - pos.own;
+        const int64_t r0 = pos.first_tile + kSegmentCost; // tile pos.own
         const int64_t lo = max(x, r0), hi = min(x1, r0 + nb);
         if (hi > lo) {
-            const int32_t j = (int32_t)(lo - r0), je = (int32_t)(hi - r0);
+            const int32_t j = (int32_t)(lo - r0) + pos.own;
+            const int32_t je = (int32_t)(hi - r0) + pos.own;
             wv.start(a, pos.b, pos.g);
             const bool ok = wv.template run<HINT>(a, pos.b, pos.g, j * kTile,
                                                   min(je * kTile, pos.n), pos.n);
             wv.finish();
-            if (j == 0 && je == nb)
+            if (j == 0 && je == tiles_of(pos.n))
                 wv.write_out(a, pos.b, pos.g, pos.n, ok);
             else
                 wv.write_partial(a, balanced_slot(a, i, pos.g, pos.b), ok);
         }
         x = r0 + nb;
         if (x < x1)
-            pos = next_segment(a, pos);
+            pos = next_segment(a, pos, P);
     }
 }
 
@@ -742,7 +947,7 @@ template <int QT, int KT, int D>
 hipError_t launch_mfma(const DecodeArgs &a, int32_t num_items, hipStream_t stream)
 {
     const int grid = (num_items + 3) / 4;
-    const bool hint = a.seq_shared != nullptr;
+    const bool hint = a.share != nullptr;
     if (a.partition == kPartitionBalanced) {
         auto kern = hint ? &decode_mfma_balanced_kernel<QT, KT, D, true>
                          : &decode_mfma_balanced_kernel<QT, KT, D, false>;

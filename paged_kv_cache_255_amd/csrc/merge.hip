@@ -76,14 +76,15 @@ struct MergeState {
     }
 };
 
-// Folds parts [p_begin, p_end) of the segment whose slots start at w0 into
-// st, CH = 16 / S parts per batch (16 x 3 loads in flight per lane), in slot
-// order, with the online rescale between batches:
+// Folds parts [p_begin, p_end) of a segment into st, part p in slot
+// w0 + p stride, CH = 16 / S parts per batch (16 x 3 loads in flight per
+// lane), in part order, with the online rescale between batches:
 //   M = max_p m_p,  out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p
 // per query head, the identity the online update inside a work item uses.
 template <int D, int S>
-__device__ __forceinline__ void merge_fold(const DecodeArgs &a, int64_t w0, int64_t p_begin,
-                                           int64_t p_end, int lane, MergeState<S> &st)
+__device__ __forceinline__ void merge_fold(const DecodeArgs &a, int64_t w0, int64_t stride,
+                                           int64_t p_begin, int64_t p_end, int lane,
+                                           MergeState<S> &st)
 {
     constexpr int CH = 16 / S;
     int hs[S];
@@ -96,7 +97,7 @@ __device__ __forceinline__ void merge_fold(const DecodeArgs &a, int64_t w0, int6
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const bool in = p0 + c < p_end;
-            const int64_t w = w0 + p0 + (in ? c : 0);
+            const int64_t w = w0 + (p0 + (in ? c : 0)) * stride;
             const float *base = ws_acc(a, w, 0, D);
 #pragma unroll
             for (int s = 0; s < S; ++s) {
@@ -160,7 +161,7 @@ __device__ __forceinline__ void merge_segment_s(const DecodeArgs &a, int32_t b, 
                                                 int64_t w0, int64_t nparts, int lane)
 {
     MergeState<S> st;
-    merge_fold<D, S>(a, w0, 0, nparts, lane, st);
+    merge_fold<D, S>(a, w0, 1, 0, nparts, lane, st);
     merge_store<QT, D, S>(a, b, g, st, lane);
 }
 
@@ -240,13 +241,88 @@ __device__ __forceinline__ bool segment_parts(const DecodeArgs &a, int lane, int
 {
     if (a.partition == kPartitionBalanced) {
         // segment (g, b) starts at g * Th + (split_tiles of sequences [0, b))
-        const HeadTiles ht = head_tiles(a, lane, b);
+        const HeadTiles ht = head_tiles(a, lane, b, PrefixHead{false, 0, 0, 0});
         return balanced_parts(a, b, g, ht.per_head, ht.before, tiles_of(n), w0, nparts);
     } else {
         w0 = ((int64_t)b * a.num_kv_heads + g) * a.max_parts;
         nparts = (n + a.partition - 1) / a.partition;
     }
     return true;
+}
+
+// Slots holding parts of a segment: w0 + p stride for p < n.
+struct PartList {
+    int64_t w0, n, stride;
+};
+
+// The parts of segment (sequence b of n tokens, KV head g) of a balanced
+// launch with prefix rows: the pieces of its own tiles in the sequences'
+// split (seq) and, when its prefix row reads its leading tiles, the pieces
+// of that row in the rows' split, one slot per piece at the member's place
+// in the row (row).  False when one run held
+// all the sequence's tiles, none was left to a row, and that run wrote the
+// rows itself.
+__device__ __forceinline__ bool prefix_segment_parts(const DecodeArgs &a, int lane, int32_t b,
+                                                     int32_t g, int32_t n, const PrefixHead &P,
+                                                     PartList &seq, PartList &row)
+{
+    const int32_t spr = prefix_row_seqs(a.group);
+    const HeadTiles ht = head_tiles(a, lane, b, P);
+    const int64_t T = ht.per_head * a.num_kv_heads;
+    const int32_t Wr = P.on ? row_runs(a, P, ht.per_head, a.waves) : 0;
+    const int32_t R = effective_runs(T, a.waves - Wr);
+    const int32_t own = uniform(own_tiles(a, P, b, n));
+    seq = PartList{0, 0, 1};
+    row = PartList{0, 0, spr};
+    const int32_t nt = tiles_of(n) - own;
+    if (nt > 0) {
+        const int64_t S0 = (int64_t)g * ht.per_head + ht.before + kSegmentCost;
+        const int64_t i0 = run_of_tile(S0, T, R);
+        const int64_t i1 = run_of_tile(S0 + nt - 1, T, R);
+        if (own == 0 && i0 == i1)
+            return false;
+        seq = PartList{balanced_slot(a, i0, g, b), i1 - i0 + 1, 1};
+    }
+    if (own > 0) {
+        const int32_t gi = uniform(min(max(plan_group(a)[b], 0), P.ng - 1));
+        const int32_t count = uniform(group_count(a, gi));
+        const int32_t rank = uniform(min(max(plan_rank(a)[b], 0), max(count - 1, 0)));
+        const RowPos r = row_of_group(a, lane, gi, rank / spr, P);
+        if (count > 0 && r.nt > 0) {
+            // the rows' own split: Hkv * P.units units over Wr runs
+            const int64_t Tr = P.units * a.num_kv_heads;
+            const int32_t Rr = effective_runs(Tr, Wr);
+            const int64_t S0 = (int64_t)g * P.units + r.before + kSegmentCost;
+            const int64_t i0 = run_of_tile(S0, Tr, Rr);
+            const int64_t i1 = run_of_tile(S0 + row_body(r.nt) - 1, Tr, Rr);
+            row = PartList{row_slot(a, i0, g, r.row, P) + rank % spr, i1 - i0 + 1, spr};
+        }
+    }
+    return true;
+}
+
+// Combines the segment's parts, its own pieces first, then its row's.
+template <int QT, int D, int S>
+__device__ __forceinline__ void merge_lists_s(const DecodeArgs &a, int32_t b, int32_t g,
+                                              const PartList &seq, const PartList &row, int lane)
+{
+    MergeState<S> st;
+    merge_fold<D, S>(a, seq.w0, seq.stride, 0, seq.n, lane, st);
+    merge_fold<D, S>(a, row.w0, row.stride, 0, row.n, lane, st);
+    merge_store<QT, D, S>(a, b, g, st, lane);
+}
+
+template <int QT, int D>
+__device__ __forceinline__ void merge_lists(const DecodeArgs &a, int32_t b, int32_t g,
+                                            const PartList &seq, const PartList &row, int lane)
+{
+    switch (merge_runs(a.group, D)) {
+    case 1: merge_lists_s<QT, D, 1>(a, b, g, seq, row, lane); break;
+    case 2: merge_lists_s<QT, D, 2>(a, b, g, seq, row, lane); break;
+    case 4: merge_lists_s<QT, D, 4>(a, b, g, seq, row, lane); break;
+    case 8: merge_lists_s<QT, D, 8>(a, b, g, seq, row, lane); break;
+    default: break;
+    }
 }
 
 // The G rows of a segment whose length is out of range (NaN) or zero (0).
@@ -291,7 +367,7 @@ __global__ __launch_bounds__(64) void merge_kernel(DecodeArgs a)
 // True when balanced_segment_fast applies to the launch.
 __device__ __forceinline__ bool segment_fast_path(const DecodeArgs &a)
 {
-    return a.partition == kPartitionBalanced && a.num_seqs <= kWave &&
+    return a.partition == kPartitionBalanced && !a.prefix && a.num_seqs <= kWave &&
            a.max_seq_len < kScan32MaxLen;
 }
 
@@ -314,6 +390,12 @@ __global__ __launch_bounds__(64) void merge_segment_kernel(DecodeArgs a)
     const bool valid = len_ok(a, n);
     if (!valid || n == 0) {
         merge_fill<QT, D>(a, b, g, valid, lane);
+        return;
+    }
+    if (a.prefix) {
+        PartList seq, row;
+        if (prefix_segment_parts(a, lane, b, g, n, prefix_head(a, lane), seq, row))
+            merge_lists<QT, D>(a, b, g, seq, row, lane);
         return;
     }
     int64_t w0, nparts;
@@ -345,6 +427,7 @@ __global__ __launch_bounds__(64 * wide_merge_waves(S)) void merge_segment_wide_k
     const int32_t b = blockIdx.x / a.num_kv_heads;
     const int32_t g = blockIdx.x % a.num_kv_heads;
     int64_t w0 = 0, nparts = 0;
+    PartList row{0, 0, 1};
     // b, g and the lengths are the same for every wave, so all waves take the
     // same branch and leave together
     if (segment_fast_path(a)) {
@@ -364,11 +447,20 @@ __global__ __launch_bounds__(64 * wide_merge_waves(S)) void merge_segment_wide_k
                 merge_fill<QT, D>(a, b, g, valid, lane);
             return;
         }
-        if (!segment_parts(a, lane, b, g, n, w0, nparts))
+        if (a.prefix) {
+            PartList seq;
+            if (!prefix_segment_parts(a, lane, b, g, n, prefix_head(a, lane), seq, row))
+                return;
+            w0 = seq.w0;
+            nparts = seq.n;
+        } else if (!segment_parts(a, lane, b, g, n, w0, nparts)) {
             return;
+        }
     }
+    // wave w folds its share of the segment's own pieces, then of its row's
     MergeState<S> st;
-    merge_fold<D, S>(a, w0, wave * nparts / NW, (wave + 1) * nparts / NW, lane, st);
+    merge_fold<D, S>(a, w0, 1, wave * nparts / NW, (wave + 1) * nparts / NW, lane, st);
+    merge_fold<D, S>(a, row.w0, row.stride, wave * row.n / NW, (wave + 1) * row.n / NW, lane, st);
 #pragma unroll
     for (int s = 0; s < S; ++s) {
         s_m[wave][s][lane] = st.M[s];

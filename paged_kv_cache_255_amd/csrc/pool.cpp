@@ -494,6 +494,83 @@ pa_status pa_export_block_tables(const pa_pool *p, const int32_t *seqs, int32_t 
     return PA_OK;
 }
 
+pa_status pa_export_share_plan(const pa_pool *p, const int32_t *seqs, int32_t nseq,
+                               int32_t *plan_out)
+{
+    if (!p || nseq < 0 || (nseq > 0 && (!seqs || !plan_out)))
+        return pa::fail(PA_ERR_INVALID_ARG, "bad share-plan arguments");
+    for (int32_t i = 0; i < nseq; ++i)
+        if (!resident_seq(p, seqs[i]))
+            return pa::fail(PA_ERR_INVALID_ARG, "unknown or swapped-out sequence id in export");
+    if (nseq == 0)
+        return PA_OK;
+    const int32_t B = nseq;
+    const int32_t bs = p->cfg.block_size;
+    int32_t *shared = plan_out + 2;
+    int32_t *group_of = plan_out + 2 + B;
+    int32_t *rank = plan_out + 2 + 2 * B;
+    int32_t *own = plan_out + 2 + 3 * B;
+    int32_t *gcount = plan_out + 2 + 4 * B;
+    int32_t *gblocks = plan_out + 2 + 5 * B;
+    int32_t *members = plan_out + 2 + 6 * B;
+    int32_t *gfirst = plan_out + 2 + 7 * B;
+    std::fill(plan_out, plan_out + PA_SHARE_PLAN_WORDS(B), 0);
+    plan_out[0] = PA_SHARE_PLAN_MAGIC;
+    // the hint: leading entries whose block another exported table holds
+    pa_status st = pa_export_block_tables(p, seqs, nseq, 0, nullptr, nullptr, nullptr, shared);
+    if (st != PA_OK)
+        return st;
+    std::fill(group_of, group_of + B, -1);
+    // candidates: no window, first entry shared; keyed by the first block,
+    // in order of their first member
+    std::vector<int32_t> first_of_key(p->cfg.num_blocks, -1);
+    std::vector<std::vector<int32_t>> sets;
+    for (int32_t i = 0; i < B; ++i) {
+        const pa_pool::Seq &q = p->seqs[seqs[i]];
+        if (q.dropped != 0 || q.start != 0 || q.blocks.empty() || shared[i] < 1 || q.len <= bs)
+            continue;
+        const int32_t key = q.blocks[0];
+        if (first_of_key[key] < 0) {
+            first_of_key[key] = (int32_t)sets.size();
+            sets.emplace_back();
+        }
+        sets[first_of_key[key]].push_back(i);
+    }
+    int32_t ngroups = 0, placed = 0;
+    for (const std::vector<int32_t> &m : sets) {
+        if (m.size() < 2)
+            continue;
+        // the longest run of leading entries every member holds alike, all
+        // before each member's last token (its block stays its own)
+        size_t k = SIZE_MAX;
+        for (int32_t i : m)
+            k = std::min(k, (size_t)((p->seqs[seqs[i]].len - 1) / bs));
+        const std::vector<int32_t> &lead = p->seqs[seqs[m[0]]].blocks;
+        size_t j = 0;
+        for (; j < k; ++j) {
+            bool same = true;
+            for (int32_t i : m)
+                same = same && p->seqs[seqs[i]].blocks[j] == lead[j];
+            if (!same)
+                break;
+        }
+        if (j == 0)
+            continue;
+        gcount[ngroups] = (int32_t)m.size();
+        gblocks[ngroups] = (int32_t)j;
+        gfirst[ngroups] = placed;
+        for (size_t r = 0; r < m.size(); ++r) {
+            group_of[m[r]] = ngroups;
+            rank[m[r]] = (int32_t)r;
+            own[m[r]] = (int32_t)j;
+            members[placed++] = m[r];
+        }
+        ++ngroups;
+    }
+    plan_out[1] = ngroups;
+    return PA_OK;
+}
+
 pa_status pa_pool_take_copies(pa_pool *p, int32_t *pairs_out, int32_t max_pairs,
                               int32_t *count_out)
 {

@@ -14,8 +14,10 @@ struct DecodeArgs {
     const int32_t *block_tables;
     const int32_t *seq_lens;
     const int32_t *seq_starts; // window starts, or null (every window starts at 0)
-    const int32_t *seq_shared; // leading table entries shared within the batch
-                               // (read with caching loads), or null
+    const int32_t *share;      // the batch's share plan (pa.h), or null
+    int32_t prefix;            // balanced launch that may read the plan's groups once
+                               // per KV head (the launch decides with prefix_layout)
+    int64_t prefix_base;       // first partial-state slot of those reads
     void *out;
     float *ws;                 // partial states (partitioned modes)
     int32_t num_seqs;
@@ -70,12 +72,83 @@ __device__ __forceinline__ int32_t tiles_of(int32_t n) { return (n + kTile - 1) 
 // tiles.
 constexpr int32_t kSegmentCost = 5;
 
-// Tiles a sequence contributes to the balanced split (its real tiles plus the
-// start charge); an empty sequence or a length out of range contributes none
-// (the merge kernel writes that row as 0 or NaN).
-__device__ __forceinline__ int32_t split_tiles(const DecodeArgs &a, int32_t n)
+// XCDs (accelerator complex dies) of an MI355X.  The hardware dispatcher
+// hands a launch's workgroups to the XCDs round-robin, so workgroup w runs on
+// XCD w mod 8.  That order is how the dispatcher behaves, not something HIP
+// promises: the run placement below relies on it for speed only (which L2
+// holds which tiles).  If the order differed, every run would still be done
+// once by one wave, and the results would not change.
+constexpr int32_t kXcds = 8;
+
+// ---- the share plan (layout in pa.h) ---------------------------------------
+__device__ __forceinline__ const int32_t *plan_shared(const DecodeArgs &a) { return a.share + 2; }
+__device__ __forceinline__ const int32_t *plan_group(const DecodeArgs &a)
 {
-    return (len_ok(a, n) && n > 0) ? tiles_of(n) + kSegmentCost : 0;
+    return a.share + 2 + a.num_seqs;
+}
+__device__ __forceinline__ const int32_t *plan_rank(const DecodeArgs &a)
+{
+    return a.share + 2 + 2 * (size_t)a.num_seqs;
+}
+__device__ __forceinline__ const int32_t *plan_own(const DecodeArgs &a)
+{
+    return a.share + 2 + 3 * (size_t)a.num_seqs;
+}
+__device__ __forceinline__ const int32_t *plan_gcount(const DecodeArgs &a)
+{
+    return a.share + 2 + 4 * (size_t)a.num_seqs;
+}
+__device__ __forceinline__ const int32_t *plan_gblocks(const DecodeArgs &a)
+{
+    return a.share + 2 + 5 * (size_t)a.num_seqs;
+}
+__device__ __forceinline__ const int32_t *plan_members(const DecodeArgs &a)
+{
+    return a.share + 2 + 6 * (size_t)a.num_seqs;
+}
+__device__ __forceinline__ const int32_t *plan_gfirst(const DecodeArgs &a)
+{
+    return a.share + 2 + 7 * (size_t)a.num_seqs;
+}
+
+// Column groups a prefix row keeps (each 16 MFMA columns: 16 / G sequences
+// times G query heads), and the sequences of one prefix row.
+constexpr int32_t kPrefixColGroups = 4;
+__host__ __device__ __forceinline__ int32_t prefix_row_seqs(int32_t G)
+{
+    return kPrefixColGroups * (16 / G);
+}
+
+// What a tile of a prefix row costs in the balanced split, as the fraction
+// kRowUnitNum / kRowUnitDen of a sequence tile (one unit).  A row's tiles
+// come mostly from L2 (the head's other rows read the same blocks) and feed
+// kPrefixColGroups MFMA column groups.  Measured on MI355X (Llama-3-8B layer,
+// 256 sequences on a 2048-token prompt, per-wave clocks): 0.78 us per row
+// tile against 1.14 us per sequence tile.
+constexpr int32_t kRowUnitNum = 11;
+constexpr int32_t kRowUnitDen = 16;
+
+// Units a row of nt tiles takes after its start charge: its tile j starts at
+// unit floor(j num / den).
+__device__ __forceinline__ int32_t row_body(int32_t nt)
+{
+    return nt > 0 ? (int32_t)((int64_t)(nt - 1) * kRowUnitNum / kRowUnitDen) + 1 : 0;
+}
+
+// The first tile of a row that starts at unit u or later (u >= 0).
+__device__ __forceinline__ int32_t row_tile_at(int64_t u)
+{
+    return (int32_t)((u * kRowUnitDen + kRowUnitNum - 1) / kRowUnitNum);
+}
+
+// Units a sequence of n tokens contributes to the balanced split: its tiles
+// past the own_t its prefix row reads, plus the start charge; none when that
+// leaves nothing, or for a length out of range (the merge kernel writes that
+// row as 0 or NaN, or from its prefix row's state alone).
+__device__ __forceinline__ int32_t split_tiles(const DecodeArgs &a, int32_t n, int32_t own_t = 0)
+{
+    const int32_t t = tiles_of(n) - own_t;
+    return (len_ok(a, n) && t > 0) ? t + kSegmentCost : 0;
 }
 
 __device__ __forceinline__ int64_t wave_sum(int64_t v)
@@ -122,66 +195,249 @@ __device__ __forceinline__ int64_t readlane64(int64_t v, int l)
     return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-// The balanced split orders the segments head-major: (KV head g, sequence
-// b) for g = 0 .. Hkv-1 and, within a head, b = 0 .. B-1.  Every head has
-// the same Th tiles (the sequences' split_tiles summed: real tiles and start
-// charges), so T = Hkv * Th and segment (g, b) starts at tile
-// g * Th + (split_tiles of sequences [0, b)).
+// ---- prefix rows of a share plan -------------------------------------------
+// With a plan, every group of sequences that map the same leading blocks
+// (gblocks of them, the plan's groups) is cut into rows of
+// prefix_row_seqs(G) members in rank order, ceil(gcount / SPR) rows per group,
+// and every KV head gets the same rows.  A row's tiles are those leading
+// blocks, read once for all its members; the members' own segments then
+// cover only their tiles past them.  Groups with no blocks get no rows.
+struct PrefixHead {
+    bool on;
+    int32_t ng;    // groups of the plan
+    int32_t rows;  // rows per KV head
+    int64_t units; // the rows' units per head, start charges included
+};
 
-// Tiles of sequences [0, b) and of all sequences (one head's share, Th),
-// from one pass over the lengths (each lane sums its own sequences; the two
-// sums are wave reductions).
+// Group gi's members, clamped into the batch, and its tiles, clamped into a
+// table row.
+__device__ __forceinline__ int32_t group_count(const DecodeArgs &a, int32_t gi)
+{
+    return min(max(plan_gcount(a)[gi], 0), a.num_seqs);
+}
+__device__ __forceinline__ int32_t group_tiles(const DecodeArgs &a, int32_t gi)
+{
+    return min(max(plan_gblocks(a)[gi], 0), a.max_blocks_per_seq) << a.tile_shift;
+}
+__device__ __forceinline__ int32_t group_rows(const DecodeArgs &a, int32_t cnt, int32_t nt)
+{
+    const int32_t spr = prefix_row_seqs(a.group);
+    return nt > 0 ? (cnt + spr - 1) / spr : 0;
+}
+__device__ __forceinline__ int64_t row_units(int32_t nt)
+{
+    return nt > 0 ? kSegmentCost + row_body(nt) : 0;
+}
+
+// The launch's rows, the same in every wave of the decode and of the merge.
+// Off without a plan, or when the plan holds more groups or rows than B / 2
+// (a plan from pa_export_share_plan never does: every group has two members
+// or more).
+__device__ __forceinline__ PrefixHead prefix_head(const DecodeArgs &a, int lane)
+{
+    PrefixHead P{false, 0, 0, 0};
+    // rows take whole workgroups of each XCD's runs: 4 or more of W / 8
+    if (!a.prefix || a.waves % (4 * kXcds) != 0 || a.waves / kXcds < 8)
+        return P;
+    const int32_t ng = uniform(a.share[1]);
+    if (ng <= 0 || ng > a.num_seqs / 2)
+        return P;
+    int64_t rows = 0, units = 0;
+    for (int32_t c = 0; c < ng; c += kWave) {
+        const int32_t gi = c + lane;
+        int64_t r = 0, u = 0;
+        if (gi < ng) {
+            const int32_t nt = group_tiles(a, gi);
+            r = group_rows(a, group_count(a, gi), nt);
+            u = r * row_units(nt);
+        }
+        rows += wave_sum(r);
+        units += wave_sum(u);
+    }
+    if (rows == 0 || rows > a.num_seqs / 2)
+        return P;
+    P.on = true;
+    P.ng = ng;
+    P.rows = (int32_t)rows;
+    P.units = units;
+    return P;
+}
+
+// Leading tiles of sequence b (of n tokens) that its prefix row reads: none
+// without rows, for a sequence in no group, or when they would reach the
+// sequence's last token (that tile stays with the sequence, so the step's
+// token is appended and every tile the row reads is full).
+__device__ __forceinline__ int32_t own_tiles(const DecodeArgs &a, const PrefixHead &P, int32_t b,
+                                             int32_t n)
+{
+    if (!P.on)
+        return 0;
+    const int32_t t = min(max(plan_own(a)[b], 0), a.max_blocks_per_seq) << a.tile_shift;
+    return (int64_t)t * kTile < (int64_t)n ? t : 0;
+}
+
+// A row of a head: the plan's group gi, rows chunk of it (members
+// [chunk SPR, (chunk + 1) SPR) of its rank order), its tiles, its index
+// among the head's rows and the units of the head's rows before it.
+struct RowPos {
+    int32_t gi, chunk, nt, row;
+    int64_t before;
+};
+
+// The row holding unit y (< P.units) of a head's rows (by_unit), or row
+// number y (!by_unit): a scan over the groups, 64 at a time.
+__device__ __forceinline__ RowPos locate_row(const DecodeArgs &a, int lane, int64_t y,
+                                             bool by_unit, const PrefixHead &P)
+{
+    int64_t rows_c = 0, units_c = 0;
+    for (int32_t c = 0; c < P.ng; c += kWave) {
+        const int32_t gi = c + lane;
+        int64_t r = 0, u = 0;
+        int32_t nt = 0;
+        if (gi < P.ng) {
+            nt = group_tiles(a, gi);
+            r = group_rows(a, group_count(a, gi), nt);
+            u = row_units(nt);
+        }
+        const int64_t ri = wave_incl_scan(r, lane), ui = wave_incl_scan(r * u, lane);
+        const uint64_t hit = __ballot(gi < P.ng && (by_unit ? units_c + ui : rows_c + ri) > y);
+        if (hit) {
+            const int k = __ffsll((unsigned long long)hit) - 1;
+            RowPos q;
+            q.gi = c + k;
+            q.nt = __builtin_amdgcn_readlane(nt, k);
+            const int64_t u_k = readlane64(u, k);
+            const int64_t rows_b = rows_c + readlane64(ri - r, k);
+            const int64_t units_b = units_c + readlane64(ui - r * u, k);
+            q.chunk = (int32_t)(by_unit ? (y - units_b) / u_k : y - rows_b);
+            q.row = (int32_t)rows_b + q.chunk;
+            q.before = units_b + (int64_t)q.chunk * u_k;
+            return q;
+        }
+        rows_c += readlane64(ri, kWave - 1);
+        units_c += readlane64(ui, kWave - 1);
+    }
+    return RowPos{0, 0, 0, P.rows, P.units}; // not reached for y inside the rows
+}
+
+// Row `chunk` of group gi: its index among the head's rows and the units
+// before it.
+__device__ __forceinline__ RowPos row_of_group(const DecodeArgs &a, int lane, int32_t gi,
+                                               int32_t chunk, const PrefixHead &P)
+{
+    int64_t rows_c = 0, units_c = 0;
+    for (int32_t c = 0; c < P.ng; c += kWave) {
+        const int32_t x = c + lane;
+        int64_t r = 0, u = 0;
+        if (x < P.ng) {
+            const int32_t nt = group_tiles(a, x);
+            r = group_rows(a, group_count(a, x), nt);
+            u = row_units(nt);
+        }
+        const int64_t ri = wave_incl_scan(r, lane), ui = wave_incl_scan(r * u, lane);
+        if (gi < c + kWave) {
+            const int k = gi - c;
+            RowPos q;
+            q.gi = gi;
+            q.chunk = chunk;
+            q.nt = group_tiles(a, gi);
+            q.row = (int32_t)(rows_c + readlane64(ri - r, k)) + chunk;
+            q.before = units_c + readlane64(ui - r * u, k) + (int64_t)chunk * readlane64(u, k);
+            return q;
+        }
+        rows_c += readlane64(ri, kWave - 1);
+        units_c += readlane64(ui, kWave - 1);
+    }
+    return RowPos{gi, chunk, 0, P.rows, P.units}; // gi >= P.ng: not called so
+}
+
+// ---- the balanced order ------------------------------------------------------
+// The balanced split orders the sequence segments head-major: (KV head g,
+// sequence b) for g = 0 .. Hkv-1 and, within a head, b = 0 .. B-1.  Every
+// head has the same Th units (the sequences' split_tiles summed: tiles and
+// start charges), so T = Hkv * Th and segment (g, b) starts at unit
+// g * Th + (split_tiles of sequences [0, b)).  A launch with prefix rows cuts
+// the rows (head-major too: head g's rows fill units [g P.units,
+// (g + 1) P.units)) in a second balanced split over runs of their own.
+
+// Units of sequences [0, b) (`before`) and of all sequences (one head's
+// share, Th), from one pass over the lengths (each lane sums its own
+// sequences; the two sums are wave reductions).
 struct HeadTiles {
-    int64_t before;   // tiles of sequences [0, b)
+    int64_t before;   // units of sequences [0, b)
     int64_t per_head; // Th
 };
 
-__device__ __forceinline__ HeadTiles head_tiles(const DecodeArgs &a, int lane, int32_t b)
+__device__ __forceinline__ HeadTiles head_tiles(const DecodeArgs &a, int lane, int32_t b,
+                                                const PrefixHead &P)
 {
     int64_t before = 0, total = 0;
     for (int32_t c = 0; c < a.num_seqs; c += kWave) {
         const int32_t s = c + lane;
-        const int64_t t = (s < a.num_seqs) ? split_tiles(a, a.seq_lens[s]) : 0;
+        int64_t t = 0;
+        if (s < a.num_seqs) {
+            const int32_t n = a.seq_lens[s];
+            t = split_tiles(a, n, own_tiles(a, P, s, n));
+        }
         total += t;
         before += (s < b) ? t : 0;
     }
     return HeadTiles{wave_sum(before), wave_sum(total)};
 }
 
+// A segment of a balanced split: a sequence (row < 0) or a prefix row.
 struct SegPos {
     int32_t g;          // KV head
-    int32_t b;          // sequence
-    int32_t n;          // its length
-    int64_t first_tile; // where the segment starts in the balanced order; its
-                        // tile j is at first_tile + kSegmentCost + j
+    int32_t b;          // sequence (B past the last one)
+    int32_t n;          // its length; for a row, the row's tiles
+    int32_t own;        // the sequence's leading tiles its prefix row reads
+    int32_t row;        // -1, or the row's index among the head's rows
+    int32_t gi, chunk;  // a row's group and chunk
+    int64_t first_tile; // where the segment starts in its split; its first
+                        // tile (a sequence's tile own, a row's tile 0) is at
+                        // first_tile + kSegmentCost
 };
 
-// The segment holding tile x (x < T = Hkv * Th): head x / Th, then the
-// sequence holding tile x % Th of that head, found one 64-sequence chunk at
-// a time with a wave scan and a ballot.
+__device__ __forceinline__ SegPos seq_segment(int32_t g, int32_t b, int32_t n, int32_t own,
+                                              int64_t first)
+{
+    return SegPos{g, b, n, own, -1, 0, 0, first};
+}
+
+__device__ __forceinline__ SegPos row_segment(int32_t g, const RowPos &r, int64_t head0)
+{
+    return SegPos{g, 0, r.nt, 0, r.row, r.gi, r.chunk, head0 + r.before};
+}
+
+// The sequence segment holding unit x (x < T = Hkv * Th): head x / Th, then
+// the sequence holding unit x % Th of that head, found one 64-sequence chunk
+// at a time with a wave scan and a ballot.
 __device__ __forceinline__ SegPos locate_tile(const DecodeArgs &a, int lane, int64_t x,
-                                              int64_t Th)
+                                              int64_t Th, const PrefixHead &P)
 {
     const int32_t g = (int32_t)(x / Th);
     const int64_t y = x - (int64_t)g * Th;
     int64_t carry = 0;
     for (int32_t c = 0; c < a.num_seqs; c += kWave) {
         const int32_t b = c + lane;
-        const int64_t tiles = (b < a.num_seqs) ? (int64_t)split_tiles(a, a.seq_lens[b]) : 0;
+        int32_t n = 0, own = 0;
+        int64_t tiles = 0;
+        if (b < a.num_seqs) {
+            n = a.seq_lens[b];
+            own = own_tiles(a, P, b, n);
+            tiles = split_tiles(a, n, own);
+        }
         const int64_t incl = wave_incl_scan(tiles, lane);
         const uint64_t hit = __ballot(b < a.num_seqs && carry + incl > y);
         if (hit) {
             const int k = __ffsll((unsigned long long)hit) - 1;
-            SegPos p;
-            p.g = g;
-            p.b = c + k;
-            p.n = uniform_load(a.seq_lens + p.b);
-            p.first_tile = (int64_t)g * Th + carry + readlane64(incl - tiles, k);
-            return p;
+            return seq_segment(g, c + k, __builtin_amdgcn_readlane(n, k),
+                               __builtin_amdgcn_readlane(own, k),
+                               (int64_t)g * Th + carry + readlane64(incl - tiles, k));
         }
         carry += readlane64(incl, kWave - 1);
     }
-    return SegPos{g, a.num_seqs, 0, (int64_t)g * Th + carry};
+    return seq_segment(g, a.num_seqs, 0, 0, (int64_t)g * Th + carry);
 }
 
 // Runs the balanced split cuts T tiles into: the launch's W waves, but no
@@ -191,14 +447,6 @@ __device__ __forceinline__ int32_t effective_runs(int64_t T, int32_t W)
 {
     return (int32_t)(T < (int64_t)W ? T : (int64_t)W);
 }
-
-// XCDs (accelerator complex dies) of an MI355X.  The hardware dispatcher
-// hands a launch's workgroups to the XCDs round-robin, so workgroup w runs on
-// XCD w mod 8.  That order is how the dispatcher behaves, not something HIP
-// promises: the run placement below relies on it for speed only (which L2
-// holds which tiles).  If the order differed, every run would still be done
-// once by one wave, and the results would not change.
-constexpr int32_t kXcds = 8;
 
 // Run of wave v (0..3) of workgroup w among W waves.  Each XCD gets one
 // eighth of the runs, in order: with the head-major order and 8 KV heads,
@@ -212,9 +460,8 @@ __device__ __forceinline__ int32_t balanced_run(int32_t w, int32_t v, int32_t W)
     return (w % kXcds) * (W / kXcds) + (w / kXcds) * 4 + v;
 }
 
-// Where run i of the balanced split starts: Th, T, the number of runs, the
-// run's tiles [x0, x1) and the segment holding x0.  Up to 64 sequences the
-// tile count is one load per lane and one reduction; beyond, chunked.
+// Where run i of a balanced split starts: Th, T, the number of runs, the
+// run's units [x0, x1) and the segment holding x0.
 struct RunStart {
     int64_t Th, T;
     int32_t runs;
@@ -222,15 +469,19 @@ struct RunStart {
     SegPos pos;
 };
 
+// Run i of W over the sequence segments.  Up to 64 sequences the unit count
+// is one load per lane (two with prefix rows) and one reduction; beyond,
+// chunked.
 __device__ __forceinline__ RunStart run_start(const DecodeArgs &a, int lane, int32_t i,
-                                              int32_t W)
+                                              int32_t W, const PrefixHead &P)
 {
     RunStart r;
     if (a.num_seqs <= kWave && a.max_seq_len < kScan32MaxLen) {
         // one length per lane: the scan gives Th and the segment together
         const bool in = lane < a.num_seqs;
         const int32_t n = in ? a.seq_lens[lane] : 0;
-        const int32_t tiles = in ? split_tiles(a, n) : 0;
+        const int32_t own = in ? own_tiles(a, P, lane, n) : 0;
+        const int32_t tiles = in ? split_tiles(a, n, own) : 0;
         const int32_t incl = wave_incl_scan32(tiles);
         r.Th = __builtin_amdgcn_readlane(incl, kWave - 1);
         r.T = r.Th * a.num_kv_heads;
@@ -243,17 +494,17 @@ __device__ __forceinline__ RunStart run_start(const DecodeArgs &a, int lane, int
         const int32_t y = (int32_t)(r.x0 - (int64_t)g * r.Th);
         const uint64_t hit = __ballot(in && incl > y);
         const int k = __ffsll((unsigned long long)hit) - 1; // y < Th: some lane hits
-        r.pos.g = g;
-        r.pos.b = k;
-        r.pos.n = __builtin_amdgcn_readlane(n, k);
-        r.pos.first_tile = (int64_t)g * r.Th + __builtin_amdgcn_readlane(incl - tiles, k);
+        r.pos = seq_segment(g, k, __builtin_amdgcn_readlane(n, k),
+                            __builtin_amdgcn_readlane(own, k),
+                            (int64_t)g * r.Th + __builtin_amdgcn_readlane(incl - tiles, k));
         return r;
     }
     if (a.num_seqs <= kWave) {
         // one length per lane: the scan gives Th and the segment together
         const bool in = lane < a.num_seqs;
         const int32_t n = in ? a.seq_lens[lane] : 0;
-        const int64_t tiles = in ? (int64_t)split_tiles(a, n) : 0;
+        const int32_t own = in ? own_tiles(a, P, lane, n) : 0;
+        const int64_t tiles = in ? (int64_t)split_tiles(a, n, own) : 0;
         const int64_t incl = wave_incl_scan(tiles, lane);
         r.Th = readlane64(incl, kWave - 1);
         r.T = r.Th * a.num_kv_heads;
@@ -266,50 +517,111 @@ __device__ __forceinline__ RunStart run_start(const DecodeArgs &a, int lane, int
         const int64_t y = r.x0 - (int64_t)g * r.Th;
         const uint64_t hit = __ballot(in && incl > y);
         const int k = __ffsll((unsigned long long)hit) - 1; // y < Th: some lane hits
-        r.pos.g = g;
-        r.pos.b = k;
-        r.pos.n = __builtin_amdgcn_readlane(n, k);
-        r.pos.first_tile = (int64_t)g * r.Th + readlane64(incl - tiles, k);
+        r.pos = seq_segment(g, k, __builtin_amdgcn_readlane(n, k),
+                            __builtin_amdgcn_readlane(own, k),
+                            (int64_t)g * r.Th + readlane64(incl - tiles, k));
         return r;
     }
-    r.Th = head_tiles(a, lane, 0).per_head;
+    r.Th = head_tiles(a, lane, 0, P).per_head;
     r.T = r.Th * a.num_kv_heads;
     r.runs = effective_runs(r.T, W);
     if (i >= r.runs)
         return r;
     r.x0 = (int64_t)i * r.T / r.runs;
     r.x1 = (int64_t)(i + 1) * r.T / r.runs;
-    r.pos = locate_tile(a, lane, r.x0, r.Th);
+    r.pos = locate_tile(a, lane, r.x0, r.Th, P);
     return r;
 }
 
-// The segment after p that has tiles: the next sequence of the head with
-// tiles, else the first such sequence of the next head.
-__device__ __forceinline__ SegPos next_segment(const DecodeArgs &a, SegPos p)
+// The sequence segment after p that has tiles: the next sequence of the
+// head with tiles, else the first such sequence of the next head.
+__device__ __forceinline__ SegPos next_segment(const DecodeArgs &a, const SegPos &p,
+                                               const PrefixHead &P)
 {
-    SegPos q;
-    q.first_tile = p.first_tile + split_tiles(a, p.n);
-    q.g = p.g;
-    q.b = p.b + 1;
+    const int64_t first = p.first_tile + split_tiles(a, p.n, p.own);
+    int32_t g = p.g, b = p.b + 1;
     for (;;) {
-        while (q.b < a.num_seqs && split_tiles(a, uniform_load(a.seq_lens + q.b)) == 0)
-            ++q.b;
-        if (q.b < a.num_seqs || q.g + 1 >= a.num_kv_heads)
-            break;
-        ++q.g; // every head has the same sequences with tiles
-        q.b = 0;
+        while (b < a.num_seqs) {
+            const int32_t n = uniform_load(a.seq_lens + b);
+            const int32_t own = uniform(own_tiles(a, P, b, n));
+            if (split_tiles(a, n, own) > 0)
+                return seq_segment(g, b, n, own, first);
+            ++b;
+        }
+        if (g + 1 >= a.num_kv_heads)
+            return seq_segment(g, b, 0, 0, first);
+        ++g; // every head has the same sequences with tiles
+        b = 0;
     }
-    q.n = q.b < a.num_seqs ? uniform_load(a.seq_lens + q.b) : 0;
-    return q;
 }
 
-// Partial-state slot of run i's piece of segment (g, b): i + g * B + b.  The
-// runs touching one segment are consecutive, and a run's segments follow
-// each other, so no two (run, segment) pairs share a slot.
+// ---- the rows' split -----------------------------------------------------------
+// With prefix rows, each XCD's block of W / 8 runs gives its first R (a
+// multiple of 4: whole workgroups) to the rows and the others to the
+// sequences, so that no CU runs both (a CU serves its waves' loads in order,
+// and a row's L2 hits would wait behind the sequences' HBM reads).  R is the
+// multiple of 4 that best evens the units per run of the two splits; run r
+// of the rows' split (r < Wr = 8 R) and run s of the sequences' (s < W - Wr)
+// take XCD x's share when r / R == x, s / (W / 8 - R) == x.
+__device__ __forceinline__ int32_t row_runs(const DecodeArgs &a, const PrefixHead &P, int64_t Th,
+                                            int32_t W)
+{
+    const int32_t per = W / kXcds;
+    const double ur = (double)P.units * a.num_kv_heads, us = (double)Th * a.num_kv_heads;
+    const double ideal = per * ur / (ur + us);
+    int32_t lo = (int32_t)(ideal / 4) * 4;
+    lo = max(4, min(lo, per - 4));
+    const int32_t hi = min(lo + 4, per - 4);
+    auto cost = [&](int32_t R) { return fmax(ur / (kXcds * R), us / (W - kXcds * R)); };
+    return kXcds * (cost(hi) < cost(lo) ? hi : lo);
+}
+
+// Run r of Wr over the rows: units [x0, x1) of T = Hkv * P.units and the row
+// holding x0.
+__device__ __forceinline__ RunStart row_run_start(const DecodeArgs &a, int lane, int32_t r,
+                                                  int32_t Wr, const PrefixHead &P)
+{
+    RunStart s;
+    s.Th = P.units;
+    s.T = P.units * a.num_kv_heads;
+    s.runs = effective_runs(s.T, Wr);
+    if (r >= s.runs)
+        return s;
+    s.x0 = (int64_t)r * s.T / s.runs;
+    s.x1 = (int64_t)(r + 1) * s.T / s.runs;
+    const int32_t g = (int32_t)(s.x0 / s.Th);
+    s.pos = row_segment(g, locate_row(a, lane, s.x0 - (int64_t)g * s.Th, true, P),
+                        (int64_t)g * s.Th);
+    return s;
+}
+
+// The row after p: the head's next row, else the next head's first.
+__device__ __forceinline__ SegPos next_row(const DecodeArgs &a, int lane, const SegPos &p,
+                                           const PrefixHead &P)
+{
+    const int64_t first = p.first_tile + row_units(p.n);
+    const bool wrap = p.row + 1 >= P.rows;
+    const int32_t g = wrap ? p.g + 1 : p.g;
+    const RowPos r = locate_row(a, lane, wrap ? 0 : p.row + 1, false, P);
+    return SegPos{g, 0, r.nt, 0, r.row, r.gi, r.chunk, first};
+}
+
+// Partial-state slot of run i's piece of sequence segment (g, b):
+// i + g * B + b.  The runs touching one segment are consecutive, and a run's
+// segments follow each other, so no two (run, segment) pairs share a slot.
 __device__ __forceinline__ int64_t balanced_slot(const DecodeArgs &a, int64_t i, int32_t g,
                                                  int32_t b)
 {
     return i + (int64_t)g * a.num_seqs + b;
+}
+
+// First slot of row run r's piece of row `row` of head g: prefix_base +
+// (r + g rows + row) SPR, then one slot per member of the row (by the same
+// argument, over the rows, no two pieces share one).
+__device__ __forceinline__ int64_t row_slot(const DecodeArgs &a, int64_t r, int32_t g,
+                                            int32_t row, const PrefixHead &P)
+{
+    return a.prefix_base + (r + (int64_t)g * P.rows + row) * prefix_row_seqs(a.group);
 }
 
 // Run holding tile x when T tiles are cut into R runs [i*T/R, (i+1)*T/R)

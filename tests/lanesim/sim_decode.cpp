@@ -7,13 +7,16 @@
 // load and store stays inside its buffer, that every cross-lane operation is
 // reached by all lanes, and that every output element is written.
 // Input file: int32 header B maxb NB Hkv G D W max_len, then lens[B],
-// tables[B][maxb], slots[B].  argv: input, hint (0 or the largest count).
+// tables[B][maxb], slots[B], then a share plan of 2 + 8 B words (pa.h
+// layout).  argv: input, mode: 0 no plan, 1 the plan as a cache-policy hint
+// only, 2 the plan with prefix rows.
 #include <hip/hip_runtime.h>
 thread_local dim3 threadIdx, blockIdx;
 thread_local SimWave *g_wave;
 SimBlock *g_block;
 #include "decode_mfma.hip"
 #include "merge.hip"
+#include <cmath>
 #include <thread>
 #include <vector>
 using namespace pa;
@@ -48,15 +51,17 @@ int main(int argc, char **argv)
         return 2;
     const int B = hdr[0], maxb = hdr[1], NB = hdr[2], H = hdr[3], G = hdr[4], D = hdr[5],
               W = hdr[6], maxlen = hdr[7];
-    std::vector<int32_t> lens(B), tables((size_t)B * maxb), slots(B);
+    std::vector<int32_t> lens(B), tables((size_t)B * maxb), slots(B), plan(2 + 8 * (size_t)B);
     if (fread(lens.data(), 4, B, fp) != (size_t)B ||
         fread(tables.data(), 4, tables.size(), fp) != tables.size() ||
-        fread(slots.data(), 4, B, fp) != (size_t)B)
+        fread(slots.data(), 4, B, fp) != (size_t)B ||
+        fread(plan.data(), 4, plan.size(), fp) != plan.size())
         return 2;
     fclose(fp);
     if (D != 128)
         return 2;
-    const int hint = atoi(argv[2]);
+    const int mode = atoi(argv[2]);
+    const bool hint = mode > 0;
     // exact-size buffers, so that any access past them is reported
     const size_t cache_elems = (size_t)NB * H * 16 * D;
     std::vector<__bf16> k(cache_elems, (__bf16)0.f), v(cache_elems, (__bf16)0.f);
@@ -64,16 +69,18 @@ int main(int argc, char **argv)
     std::vector<__bf16> q(q_elems, (__bf16)0.f), out(q_elems);
     std::memset(out.data(), 0xFF, 2 * q_elems);
     std::vector<__bf16> kn((size_t)B * H * D, (__bf16)0.f), vn((size_t)B * H * D, (__bf16)0.f);
-    const int64_t nslots = (int64_t)W + (int64_t)B * H;
+    // the library's sizing: W + B Hkv sequence slots, then with prefix rows
+    // (W + Hkv B / 2) pieces of 4 x 16 / G member slots
+    const int64_t seq_slots = (int64_t)W + (int64_t)B * H;
+    const int64_t nslots =
+        seq_slots + (mode == 2 ? ((int64_t)W + (int64_t)H * (B / 2)) * prefix_row_seqs(G) : 0);
     // NaN in every slot: a merge that reads a slot no run wrote gives NaN
     std::vector<float> ws((size_t)nslots * G * (2 + D), __builtin_nanf(""));
-    std::vector<int32_t> shared(B);
-    for (int i = 0; i < B; ++i)
-        shared[i] = hint > 0 ? (i * 37) % (hint + 1) : 0;
 
     DecodeArgs a{};
     a.q = q.data(); a.k_cache = k.data(); a.v_cache = v.data(); a.block_tables = tables.data();
-    a.seq_lens = lens.data(); a.seq_starts = nullptr; a.seq_shared = hint > 0 ? shared.data() : nullptr;
+    a.seq_lens = lens.data(); a.seq_starts = nullptr; a.share = hint ? plan.data() : nullptr;
+    a.prefix = mode == 2; a.prefix_base = seq_slots;
     a.out = out.data(); a.ws = ws.data(); a.num_seqs = B; a.num_q_heads = H * G;
     a.num_kv_heads = H; a.group = G; a.num_blocks = NB; a.tile_shift = 0;
     a.max_blocks_per_seq = maxb; a.max_seq_len = maxlen; a.partition = kPartitionBalanced;
@@ -81,11 +88,15 @@ int main(int argc, char **argv)
     a.append = 1; a.k_new = kn.data(); a.v_new = vn.data(); a.slots = slots.data();
     a.k_inv = a.v_inv = 1.f;
     for (int wave = 0; wave < W; ++wave) {
-        if (hint > 0)
+        if (hint)
             run_wave(wave / 4, wave % 4, [&] { decode_mfma_balanced_kernel<PA_BF16, PA_BF16, 128, true>(a, W); });
         else
             run_wave(wave / 4, wave % 4, [&] { decode_mfma_balanced_kernel<PA_BF16, PA_BF16, 128, false>(a, W); });
     }
+    // prefix-row member slots the decode wrote (their m values)
+    size_t row_slots = 0;
+    for (int64_t w = seq_slots; w < nslots; ++w)
+        row_slots += !std::isnan(ws[(size_t)w * G * 2]);
     for (int seg = 0; seg < B * H; ++seg)
         run_wave(seg, 0, [&] { merge_segment_kernel<PA_BF16, 128>(a); });
     // every element written, and none NaN: with the placeholder arithmetic
@@ -97,6 +108,6 @@ int main(int argc, char **argv)
         unwritten += (o16[e] == 0xFFFF);
         nan += ((o16[e] & 0x7F80) == 0x7F80 && (o16[e] & 0x7F) != 0);
     }
-    printf("unwritten %zu of %zu, NaN %zu\n", unwritten, q_elems, nan);
+    printf("unwritten %zu of %zu, NaN %zu, row slots %zu\n", unwritten, q_elems, nan, row_slots);
     return (unwritten || nan) ? 3 : 0;
 }

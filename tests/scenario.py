@@ -86,6 +86,10 @@ class GpuStep:
                                               self.partition)
             self.workspace = torch.empty(nb, dtype=torch.uint8, device="cuda")
 
+    def plan(self):
+        """The batch's share plan (pa_export_share_plan), on the host."""
+        return pa.pa_export_share_plan(self.pool, self.dec)
+
     def append_prefill(self):
         i = self.inputs
         slots = torch.from_numpy(self.pre_slots).cuda()

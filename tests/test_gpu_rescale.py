@@ -53,14 +53,12 @@ def _workload(q_dtype, kv_dtype):
 
 
 def _device_waves(w):
-    """Runs of the balanced split on this device, from the workspace size
-    (one partial state per run plus one per (sequence, KV head))."""
+    """Runs of the balanced split on this device."""
     desc = pa.kv_desc(w.num_q_heads, w.num_kv_heads, w.head_dim, w.num_blocks, w.q_dtype,
                       w.kv_dtype)
-    nb = pa.pa_decode_workspace_bytes(desc, w.num_seqs, w.max_seq_len(), pa.PARTITION_BALANCED)
-    per_slot = w.group * (w.head_dim + 2) * 4
-    assert nb % per_slot == 0
-    return nb // per_slot - w.num_seqs * w.num_kv_heads
+    W = pa.pa_decode_balanced_waves(desc)
+    assert 0 < W <= 1 << 16, W
+    return W
 
 
 @pytest.fixture(scope="module", params=[("bf16", "bf16"), ("f16", "f16"), ("bf16", "e4m3")],

@@ -46,13 +46,62 @@ def sim(tmp_path_factory):
     return d, exe
 
 
-def _case(path, B, H, G, W, max_len, seed):
+def _plan(tables, lens, bs=16):
+    """A share plan in the layout pa.h gives: groups of two or more sequences
+    whose tables begin with the same block, sharing the longest run of
+    leading entries they hold alike before each member's last token."""
+    B, maxb = tables.shape
+    plan = np.zeros(2 + 8 * B, np.int32)
+    plan[0] = 0x31534150
+    nblk = [-(-int(n) // bs) for n in lens]
+    for b in range(B):  # the cache-policy hint: entries another table holds
+        others = {int(x) for c in range(B) if c != b for x in tables[c, :nblk[c]]}
+        k = 0
+        while k < nblk[b] and int(tables[b, k]) in others:
+            k += 1
+        plan[2 + b] = k
+    plan[2 + B:2 + 2 * B] = -1
+    keys = {}
+    for b in range(B):
+        if lens[b] > bs and plan[2 + b] >= 1:
+            keys.setdefault(int(tables[b, 0]), []).append(b)
+    ng = placed = 0
+    for members in keys.values():
+        if len(members) < 2:
+            continue
+        k = min((int(lens[b]) - 1) // bs for b in members)
+        j = 0
+        while j < k and all(tables[b, j] == tables[members[0], j] for b in members):
+            j += 1
+        if j == 0:
+            continue
+        plan[2 + 4 * B + ng] = len(members)
+        plan[2 + 5 * B + ng] = j
+        plan[2 + 7 * B + ng] = placed
+        for r, b in enumerate(members):
+            plan[2 + B + b] = ng
+            plan[2 + 2 * B + b] = r
+            plan[2 + 3 * B + b] = j
+            plan[2 + 6 * B + placed] = b
+            placed += 1
+        ng += 1
+    plan[1] = ng
+    return plan
+
+
+def _case(path, B, H, G, W, max_len, seed, groups=(), plan_kind="real"):
     """Seeded lengths (zero and one-token sequences included) and tables that
-    place every sequence's blocks at random in a pool with spare blocks."""
+    place every sequence's blocks at random in a pool with spare blocks.
+    groups: (first, count, blocks) runs of sequences whose tables begin with
+    the same `blocks` blocks (their lengths past them).  plan_kind: "real"
+    (the plan of those tables), "hint" (cache-policy counts only, some past
+    the tables, no groups) or "garbage" (every word but the magic random)."""
     rng = np.random.default_rng(seed)
     lens = rng.integers(1, max_len + 1, size=B).astype(np.int32)
     lens[0] = 0
     lens[-1] = 1
+    for first, count, blocks in groups:
+        lens[first:first + count] = np.maximum(lens[first:first + count], blocks * 16 + 1)
     nblk = [-(-int(n) // 16) for n in lens]
     maxb = max(max(nblk), 1)
     NB = sum(nblk) + 7
@@ -63,29 +112,94 @@ def _case(path, B, H, G, W, max_len, seed):
     for b, k in enumerate(nblk):
         tables[b, :k] = perm[pos:pos + k]
         pos += k
+    for first, count, blocks in groups:
+        tables[first + 1:first + count, :blocks] = tables[first, :blocks]
+    for b in range(B):
         if lens[b] > 0:
             t = lens[b] - 1
             slots[b] = tables[b, t // 16] * 16 + t % 16
+    if plan_kind == "garbage":
+        plan = rng.integers(-5, B + 6, size=2 + 8 * B).astype(np.int32)
+        plan[0] = 0x31534150
+        plan[1] = rng.integers(0, B // 2 + 1)
+    else:
+        plan = _plan(tables, lens)
+        if plan_kind == "hint":
+            plan[1] = 0
+            plan[2:2 + B] = [(i * 37) % 41 for i in range(B)]
     with open(path, "wb") as f:
         f.write(np.array([B, maxb, NB, H, G, 128, W, maxb * 16], np.int32).tobytes())
         f.write(lens.tobytes())
         f.write(tables.tobytes())
         f.write(slots.tobytes())
+        f.write(plan.tobytes())
+    return plan
 
 
-@pytest.mark.parametrize("B,H,G,W,hint", [
+def _run(exe, path, mode):
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0",
+               UBSAN_OPTIONS="halt_on_error=1")
+    return subprocess.run([str(exe), str(path), str(mode)], capture_output=True, text=True,
+                          timeout=900, env=env)
+
+
+@pytest.mark.parametrize("B,H,G,W,mode", [
     (9, 8, 4, 64, 0),      # W a multiple of 32: the per-XCD run placement
-    (9, 8, 4, 64, 40),     # the hint, counts past the tables included
+    (9, 8, 4, 64, 1),      # the hint, counts past the tables included
     (70, 2, 2, 60, 0),     # more than 64 sequences; W not a multiple of 32
     (5, 4, 8, 1000, 0),    # more waves than tiles: idle runs
 ])
-def test_kernels_stay_in_bounds(sim, B, H, G, W, hint):
+def test_kernels_stay_in_bounds(sim, B, H, G, W, mode):
     d, exe = sim
-    path = d / f"case_{B}_{H}_{G}_{W}_{hint}.bin"
-    _case(path, B, H, G, W, max_len=300, seed=B * 1000 + W)
-    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0",
-               UBSAN_OPTIONS="halt_on_error=1")
-    r = subprocess.run([str(exe), str(path), str(hint)], capture_output=True, text=True,
-                       timeout=600, env=env)
+    path = d / f"case_{B}_{H}_{G}_{W}_{mode}.bin"
+    _case(path, B, H, G, W, max_len=300, seed=B * 1000 + W,
+          plan_kind="hint" if mode else "real")
+    r = _run(exe, path, mode)
     assert r.returncode == 0, (r.stdout + r.stderr)[-3000:]
     assert "unwritten 0 of" in r.stdout and "NaN 0" in r.stdout
+
+
+@pytest.mark.parametrize("B,H,G,W,groups,rows", [
+    # two groups, one cut into two rows (SPR = 16 at G = 4), and loners;
+    # 8 runs per XCD: 4 to the rows, 4 to the sequences
+    (40, 2, 4, 64, ((1, 20, 5), (21, 10, 3)), True),
+    # more than 64 sequences, G = 8 (8 members a row)
+    (70, 2, 8, 96, ((0, 30, 4), (40, 12, 2)), True),
+    # a group whose shared blocks are most of each member; more waves than units
+    (12, 2, 16, 512, ((0, 12, 12),), True),
+    # W not a multiple of 32: no rows, the plan only hints (the merge takes
+    # the plan's branch all the same)
+    (70, 2, 8, 60, ((0, 30, 4), (40, 12, 2)), False),
+])
+def test_prefix_rows_stay_in_bounds(sim, B, H, G, W, groups, rows):
+    """Prefix rows in the balanced split: every piece of a row and of the
+    members' own tiles stays in its buffers, every output is written, and
+    the merge reads only slots some run wrote."""
+    d, exe = sim
+    path = d / f"prefix_{B}_{H}_{G}_{W}.bin"
+    plan = _case(path, B, H, G, W, max_len=300, seed=B * 7 + W, groups=groups)
+    assert plan[1] == len(groups)
+    r = _run(exe, path, 2)
+    assert r.returncode == 0, (r.stdout + r.stderr)[-3000:]
+    assert "unwritten 0 of" in r.stdout and "NaN 0" in r.stdout
+    # with rows, every member of every group has a slot per row piece, on
+    # every head
+    members = sum(c for _, c, _ in groups)
+    written = int(r.stdout.split("row slots")[1])
+    if rows:
+        assert written >= members * H, r.stdout
+    else:
+        assert written == 0, r.stdout
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_garbage_plan_stays_in_bounds(sim, seed):
+    """A plan that does not belong to the tables gives unspecified outputs,
+    but no access outside the buffers (AddressSanitizer would stop the run)."""
+    d, exe = sim
+    path = d / f"garbage_{seed}.bin"
+    _case(path, 40, 2, 4, 64, max_len=300, seed=seed, groups=((0, 20, 5),),
+          plan_kind="garbage")
+    r = _run(exe, path, 2)
+    assert r.returncode in (0, 3), (r.stdout + r.stderr)[-3000:]
+    assert "unwritten 0 of" in r.stdout, r.stdout
