@@ -191,11 +191,21 @@ __device__ __forceinline__ void wave_lds_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// A value every lane of the wave reads from the same address, marked
-// wave-uniform so control flow that depends on it stays scalar.
+// A value every lane of the wave reads from the same address, in memory the
+// launch does not write (lengths, tables, plans), read with a scalar load.
+// Its wait is on the scalar counter: a vector load's wait would also wait
+// for every vector store the wave issued before it (the vector memory
+// counter covers stores), such as the partial states a piece just wrote.
+// The address goes through readfirstlane: computed from an index the
+// compiler keeps in a vector register, it would otherwise become a vector
+// load after all.
 __device__ __forceinline__ int32_t uniform_load(const int32_t *p)
 {
-    return __builtin_amdgcn_readfirstlane(*p);
+    using CI32 = __attribute__((address_space(4))) const int32_t;
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    return __builtin_amdgcn_readfirstlane(*(const CI32 *)((hi << 32) | lo));
 }
 
 __device__ __forceinline__ int32_t uniform(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }

@@ -151,12 +151,18 @@ __device__ __forceinline__ int32_t split_tiles(const DecodeArgs &a, int32_t n, i
     return (len_ok(a, n) && t > 0) ? t + kSegmentCost : 0;
 }
 
+// The sum over the wave's lanes, returned as a wave-uniform value (through
+// readfirstlane, so the compiler keeps what depends on it, such as the
+// run's bounds and its walk over segments, in scalar registers and uniform
+// branches).
 __device__ __forceinline__ int64_t wave_sum(int64_t v)
 {
 #pragma unroll
     for (int x = 1; x < kWave; x <<= 1)
         v += __shfl_xor(v, x, kWave);
-    return v;
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)((hi << 32) | lo);
 }
 
 __device__ __forceinline__ int64_t wave_incl_scan(int64_t v, int lane)
@@ -273,6 +279,17 @@ __device__ __forceinline__ int32_t own_tiles(const DecodeArgs &a, const PrefixHe
     if (!P.on)
         return 0;
     const int32_t t = min(max(plan_own(a)[b], 0), a.max_blocks_per_seq) << a.tile_shift;
+    return (int64_t)t * kTile < (int64_t)n ? t : 0;
+}
+
+// The same for a wave-uniform b, with a scalar load (see uniform_load).
+__device__ __forceinline__ int32_t own_tiles_uniform(const DecodeArgs &a, const PrefixHead &P,
+                                                     int32_t b, int32_t n)
+{
+    if (!P.on)
+        return 0;
+    const int32_t t = min(max(uniform_load(plan_own(a) + b), 0), a.max_blocks_per_seq)
+                      << a.tile_shift;
     return (int64_t)t * kTile < (int64_t)n ? t : 0;
 }
 
@@ -535,22 +552,25 @@ __device__ __forceinline__ RunStart run_start(const DecodeArgs &a, int lane, int
 
 // The sequence segment after p that has tiles: the next sequence of the
 // head with tiles, else the first such sequence of the next head.
+// (b and g pass through uniform() so that the compiler keeps the walk in
+// scalar registers: as a divergent loop it would wait for the wave's
+// outstanding vector stores at its head.)
 __device__ __forceinline__ SegPos next_segment(const DecodeArgs &a, const SegPos &p,
                                                const PrefixHead &P)
 {
     const int64_t first = p.first_tile + split_tiles(a, p.n, p.own);
-    int32_t g = p.g, b = p.b + 1;
+    int32_t g = uniform(p.g), b = uniform(p.b + 1);
     for (;;) {
         while (b < a.num_seqs) {
             const int32_t n = uniform_load(a.seq_lens + b);
-            const int32_t own = uniform(own_tiles(a, P, b, n));
+            const int32_t own = own_tiles_uniform(a, P, b, n);
             if (split_tiles(a, n, own) > 0)
                 return seq_segment(g, b, n, own, first);
-            ++b;
+            b = uniform(b + 1);
         }
         if (g + 1 >= a.num_kv_heads)
             return seq_segment(g, b, 0, 0, first);
-        ++g; // every head has the same sequences with tiles
+        g = uniform(g + 1); // every head has the same sequences with tiles
         b = 0;
     }
 }
