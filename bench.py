@@ -80,10 +80,12 @@ def parse():
     ap.add_argument("--upload-per-step", action="store_true",
                     help="run the host allocator and copy the step's metadata inside each "
                          "timed step")
-    ap.add_argument("--feature", choices=["copy", "swap", "window", "prefix"], default=None,
+    ap.add_argument("--feature", choices=["copy", "swap", "window", "prefix", "prefill"],
+                    default=None,
                     help="measure one of the paths beside the decode step on the workload's "
                          "shapes (block copies of copy on write, swap transfers, windowed "
-                         "decode, prefix-cache host work) and print one JSON line for it")
+                         "decode, prefix-cache host work, the prefill append of --config) "
+                         "and print one JSON line for it")
     ap.add_argument("--traffic-record", nargs=5, default=None,
                     metavar=("BENCH_LINE", "FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
                              "COPY_WRITE_CSV"),
@@ -713,8 +715,49 @@ def feature_prefix(args, torch, pa, workloads, execute_plan):
                                                 "system prompt + Geometric(1/350) suffix"}})
 
 
+def feature_prefill(args, torch, pa, workloads, execute_plan):
+    """The prefill append of one layer of --config (3: 8 x 4,095 tokens, 40 KV
+    heads, fp16; 5: 4 x 131,071 tokens, 8 KV heads, bf16 into FP8): one
+    pa_cache_append of every prefill token, timed over back-to-back launches.
+    Bytes = the K and V rows read (activation dtype) plus those written (cache
+    dtype)."""
+    w = workloads.config(args.config)
+    pool = pa.pa_block_pool_init(w.num_blocks, w.num_kv_heads, w.head_dim, w.kv_dtype,
+                                 block_size=w.block_size, shuffle_seed=w.shuffle_seeds[0])
+    _, pre = execute_plan(pool, w.ops)
+    T = len(pre)
+    desc = pa.kv_desc(w.num_q_heads, w.num_kv_heads, w.head_dim, w.num_blocks, w.q_dtype,
+                      w.kv_dtype, block_size=w.block_size)
+    k_pre, v_pre = workloads.prefill_tensors(w, 0, "cuda")
+    ks = vs = 1.0
+    if w.kv_dtype == "e4m3":
+        ks, vs = workloads.fp8_scale(k_pre), workloads.fp8_scale(v_pre)
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "e4m3": torch.uint8}[w.kv_dtype]
+    nelem = w.num_blocks * w.num_kv_heads * w.block_size * w.head_dim
+    kc = torch.zeros(nelem, dtype=tdt, device="cuda")
+    vc = torch.zeros(nelem, dtype=tdt, device="cuda")
+    slots = torch.from_numpy(pre).cuda()
+    ms = _time_launches(torch, lambda: pa.pa_cache_append(k_pre, v_pre, kc, vc, slots, desc,
+                                                          ks, vs), args.steps)
+    qb = {"f32": 4, "f16": 2, "bf16": 2}[w.q_dtype]
+    kb = {"f32": 4, "f16": 2, "bf16": 2, "e4m3": 1}[w.kv_dtype]
+    row = w.num_kv_heads * w.head_dim
+    moved = 2 * T * row * (qb + kb)
+    gbs = moved / (ms * 1e-3) / 1e9
+    log(f"[bench] prefill append {w.name}: {T} tokens, {ms * 1e3:.1f} us per launch, "
+        f"{gbs:.1f} GB/s = {gbs / HBM_PEAK_GBS * 100:.1f}% of HBM peak")
+    _feature_line("prefill cache append: HBM GB/s (K and V read + written)",
+                  round(gbs, 1), "GB/s",
+                  {"us_per_launch": round(ms * 1e3, 2), "tokens": T, "bytes_per_launch": moved,
+                   "peak": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4),
+                   "kernel": "append_tiles_kernel",
+                   "config": {"workload": f"{w.name}: prefill of one layer, {T} tokens, "
+                                          f"{w.num_kv_heads} KV heads x {w.head_dim}, "
+                                          f"{w.q_dtype} into {w.kv_dtype}"}})
+
+
 FEATURES = {"copy": feature_copy, "swap": feature_swap, "window": feature_window,
-            "prefix": feature_prefix}
+            "prefix": feature_prefix, "prefill": feature_prefill}
 
 
 def copy_calibration(torch):

@@ -31,6 +31,181 @@ __global__ __launch_bounds__(256) void append_kernel(const void *k, const void *
                            num_kv_heads, k_inv, v_inv, lane);
 }
 
+// Value of the low (hi = false) or high half of a word of two 16-bit
+// activations.
+template <int QT>
+__device__ __forceinline__ float half_f32(uint32_t w, bool hi)
+{
+    using TQ = typename Store<QT>::T;
+    return to_f32<QT>(__builtin_bit_cast(TQ, (uint16_t)(hi ? w >> 16 : w & 0xFFFFu)));
+}
+
+// The same append for calls that write whole 16-token tiles (a prefill): wave
+// (w, g) takes window w of the token array (entries [16 w, 16 w + 16)) for KV
+// head g.  From the slots of entries [16 w - 16, 16 w + 32), one per lane, it
+// finds the complete tiles: 16 entries in a row whose slots run from a
+// multiple of 16 to 15 past it, all inside the pool.  At most one starts in
+// the window; the wave writes it whole, its 16 K rows with 16-byte loads
+// and stores, its V tile through LDS: the 16 V rows are staged dim-major,
+// and each lane then gathers the 16-byte pieces of the tile layout
+// (v_tile_index) it stores.  A window entry inside a complete tile that
+// starts in the window before is that window's wave's; any other entry is
+// written on its own as by append_kernel.  The bytes are those append_kernel
+// writes.
+template <int QT, int KT, int D>
+__global__ __launch_bounds__(256) void append_tiles_kernel(const void *k, const void *v,
+                                                           void *k_cache, void *v_cache,
+                                                           const int32_t *slots,
+                                                           int32_t num_tokens,
+                                                           int32_t num_kv_heads,
+                                                           int32_t num_blocks, int32_t tile_shift,
+                                                           float k_inv, float v_inv)
+{
+    using TQ = typename Store<QT>::T;
+    using TK = typename Store<KT>::T;
+    constexpr int QB = Store<QT>::bytes, KE = Store<KT>::bytes;
+    // LDS row of one dim: 16 tokens plus 4 of padding (fewer bank
+    // conflicts; keeps each 4-token group aligned for its read)
+    constexpr int ROW = 20 * KE;
+    __shared__ __align__(16) uint8_t stage[4][D * ROW];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t wid = (int64_t)blockIdx.x * 4 + wave;
+    const int64_t windows = ((int64_t)num_tokens + kTile - 1) / kTile;
+    if (wid >= windows * num_kv_heads)
+        return;
+    const int64_t w = wid / num_kv_heads;
+    const int32_t g = (int32_t)(wid % num_kv_heads);
+    const int32_t bs = kTile << tile_shift;
+    const int64_t cap = (int64_t)num_blocks * bs;
+
+    // lane i: slot of entry 16 w - 16 + i (i < 48), -1 outside the array or
+    // the pool
+    const int64_t e = kTile * w - kTile + lane;
+    int32_t s = -1;
+    if (lane < 3 * kTile && e >= 0 && e < num_tokens) {
+        s = slots[e];
+        if (s < 0 || (int64_t)s >= cap)
+            s = -1;
+    }
+    const int32_t s_next = __shfl_down(s, 1, kWave);
+    const uint64_t links = __ballot(s >= 0 && lane + 1 < 3 * kTile && s_next == s + 1);
+    const bool starts_here = s >= 0 && s % kTile == 0 && lane + kTile <= 3 * kTile &&
+                             ((links >> lane) & 0x7FFFull) == 0x7FFFull;
+    const uint64_t starts = __ballot(starts_here);
+
+    const uint64_t mine = (starts >> kTile) & 0xFFFFull;
+    if (mine) {
+        const int p = kTile + __ffsll((unsigned long long)mine) - 1;
+        const int64_t t0 = kTile * w - kTile + p;
+        const int32_t s0 = __builtin_amdgcn_readlane(s, p);
+        const size_t tile = (((size_t)(s0 / bs) * num_kv_heads + g) << tile_shift) +
+                            (size_t)((s0 % bs) / kTile);
+        TK *kd = static_cast<TK *>(k_cache) + tile * kTile * D;
+        uint8_t *vd = reinterpret_cast<uint8_t *>(static_cast<TK *>(v_cache) + tile * kTile * D);
+        const size_t row = (size_t)num_kv_heads * D; // source stride between tokens
+        const TQ *ks = static_cast<const TQ *>(k) + ((size_t)t0 * num_kv_heads + g) * D;
+        const TQ *vs = static_cast<const TQ *>(v) + ((size_t)t0 * num_kv_heads + g) * D;
+
+        // K: the tile's 16 rows are contiguous in the cache; chunk c holds
+        // cache elements [16 c / KE, 16 (c + 1) / KE)
+#pragma unroll
+        for (int c = lane; c < D * KE; c += kWave) {
+            const int el0 = c * (16 / KE);
+            const TQ *src = ks + (size_t)(el0 / D) * row + el0 % D;
+            if constexpr (KE == QB) {
+                *reinterpret_cast<u32x4 *>(kd + el0) = load16(src);
+            } else {
+                // FP8 from 16-bit activations: 16 values from two loads
+                const u32x4 a = load16(src), b = load16(src + 8);
+                const uint32_t wd[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+                uint32_t out[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    out[i] = e4m3x4(half_f32<QT>(wd[2 * i], false) * k_inv,
+                                    half_f32<QT>(wd[2 * i], true) * k_inv,
+                                    half_f32<QT>(wd[2 * i + 1], false) * k_inv,
+                                    half_f32<QT>(wd[2 * i + 1], true) * k_inv);
+                *reinterpret_cast<u32x4 *>(kd + el0) = u32x4{out[0], out[1], out[2], out[3]};
+            }
+        }
+
+        // V: stage the 16 rows dim-major (token u of dim d at byte
+        // d ROW + u KE), converted to the cache format
+        uint8_t *st = stage[wave];
+#pragma unroll
+        for (int c = lane; c < D * QB; c += kWave) {
+            const int el0 = c * (16 / QB);
+            const int u = el0 / D, d0 = el0 % D;
+            const u32x4 x = load16(vs + (size_t)u * row + d0);
+            if constexpr (KT == PA_FP8_E4M3) {
+                // 8 values of 16 bits: two words of four codes
+                const uint32_t c0 = e4m3x4(half_f32<QT>(x.x, false) * v_inv,
+                                           half_f32<QT>(x.x, true) * v_inv,
+                                           half_f32<QT>(x.y, false) * v_inv,
+                                           half_f32<QT>(x.y, true) * v_inv);
+                const uint32_t c1 = e4m3x4(half_f32<QT>(x.z, false) * v_inv,
+                                           half_f32<QT>(x.z, true) * v_inv,
+                                           half_f32<QT>(x.w, false) * v_inv,
+                                           half_f32<QT>(x.w, true) * v_inv);
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    st[(d0 + i) * ROW + u] = (uint8_t)((i < 4 ? c0 : c1) >> (8 * (i % 4)));
+            } else {
+                const TQ *xe = reinterpret_cast<const TQ *>(&x);
+#pragma unroll
+                for (int i = 0; i < 16 / QB; ++i)
+                    *reinterpret_cast<TK *>(st + (d0 + i) * ROW + u * KE) = xe[i];
+            }
+        }
+        wave_lds_sync();
+        // piece 64 q + L (L = col + 16 grp) holds, for i < 4 / KE, dim
+        // 16 ((4 / KE) q + i) + col of tokens 4 grp .. 4 grp + 3
+        const int col = lane & 15, grp = lane >> 4;
+        constexpr int PD = 4 / KE;
+#pragma unroll
+        for (int q = 0; q < D * KE / kWave; ++q) {
+            uint32_t wds[4];
+#pragma unroll
+            for (int i = 0; i < PD; ++i) {
+                const uint8_t *src = st + (16 * (PD * q + i) + col) * ROW + 4 * grp * KE;
+                if constexpr (KE == 1) {
+                    wds[i] = *reinterpret_cast<const uint32_t *>(src);
+                } else if constexpr (KE == 2) {
+                    const u32x2 two = *reinterpret_cast<const u32x2 *>(src);
+                    wds[2 * i] = two.x;
+                    wds[2 * i + 1] = two.y;
+                } else {
+                    const u32x4 four = *reinterpret_cast<const u32x4 *>(src);
+                    wds[0] = four.x;
+                    wds[1] = four.y;
+                    wds[2] = four.z;
+                    wds[3] = four.w;
+                }
+            }
+            *reinterpret_cast<u32x4 *>(vd + (size_t)(kWave * q + lane) * 16) =
+                u32x4{wds[0], wds[1], wds[2], wds[3]};
+        }
+    }
+
+    // the window's other entries, one token at a time
+#pragma unroll 1
+    for (int j = 0; j < kTile; ++j) {
+        const int p = kTile + j;
+        const int32_t sj = __builtin_amdgcn_readlane(s, p);
+        if (sj < 0)
+            continue;
+        const int q = p - sj % kTile;
+        if (q >= 0 && ((starts >> q) & 1ull))
+            continue;
+        const int64_t t = kTile * w + j;
+        const TQ *ksj = static_cast<const TQ *>(k) + ((size_t)t * num_kv_heads + g) * D;
+        const TQ *vsj = static_cast<const TQ *>(v) + ((size_t)t * num_kv_heads + g) * D;
+        store_token<QT, KT, D>(ksj, vsj, k_cache, v_cache, sj / bs, sj % bs, tile_shift, g,
+                               num_kv_heads, k_inv, v_inv, lane);
+    }
+}
+
 // Block copies for copy on write: for each pair (src, dst), the K and V of
 // block dst (all KV heads, block_bytes each) become those of block src.
 // blockIdx.y picks the pair; the threads of a row of workgroups stride over
@@ -115,16 +290,31 @@ hipError_t append_by_dim(const void *k, const void *v, void *kc, void *vc, const
                          int32_t T, int32_t H, int32_t NB, int32_t TS, int D, float ki,
                          float vi, hipStream_t s)
 {
+    if (D != 64 && D != 128)
+        return hipErrorInvalidValue;
+    // Calls of kTilesFrom tokens or more (prefills) go to the tile kernel,
+    // shorter ones (decode steps: one token per sequence, no whole tile) to
+    // one wave per (token, KV head).
+    constexpr int32_t kTilesFrom = 64;
+    if (T >= kTilesFrom) {
+        const int64_t waves = ((int64_t)T + kTile - 1) / kTile * H;
+        const int grid = (int)((waves + 3) / 4);
+        if (D == 64)
+            hipLaunchKernelGGL((append_tiles_kernel<QT, KT, 64>), dim3(grid), dim3(256), 0, s, k,
+                               v, kc, vc, slots, T, H, NB, TS, ki, vi);
+        else
+            hipLaunchKernelGGL((append_tiles_kernel<QT, KT, 128>), dim3(grid), dim3(256), 0, s,
+                               k, v, kc, vc, slots, T, H, NB, TS, ki, vi);
+        return hipGetLastError();
+    }
     const int64_t waves = (int64_t)T * H;
     const int grid = (int)((waves + 3) / 4);
     if (D == 64)
         hipLaunchKernelGGL((append_kernel<QT, KT, 64>), dim3(grid), dim3(256), 0, s, k, v, kc, vc,
                            slots, T, H, NB, TS, ki, vi);
-    else if (D == 128)
+    else
         hipLaunchKernelGGL((append_kernel<QT, KT, 128>), dim3(grid), dim3(256), 0, s, k, v, kc,
                            vc, slots, T, H, NB, TS, ki, vi);
-    else
-        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

@@ -210,19 +210,15 @@ struct MfmaWave {
             } else {
                 const u32x4 lo = rt.k[2 * j], hi = rt.k[2 * j + 1];
                 const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+                auto half = [](uint32_t x, bool high) {
+                    return to_f32<QT>(__builtin_bit_cast(TQ, (uint16_t)(high ? x >> 16 : x & 0xFFFFu)));
+                };
                 uint32_t q[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    uint32_t word = 0;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const uint32_t src = w[(4 * i + e) / 2];
-                        const uint16_t h = (uint16_t)((e & 1) ? (src >> 16) : (src & 0xFFFFu));
-                        const float x = to_f32<QT>(__builtin_bit_cast(TQ, h));
-                        word |= (uint32_t)f32_to_e4m3(x * a.k_inv) << (8 * e);
-                    }
-                    q[i] = word;
-                }
+                for (int i = 0; i < 4; ++i)
+                    q[i] = e4m3x4(half(w[2 * i], false) * a.k_inv, half(w[2 * i], true) * a.k_inv,
+                                  half(w[2 * i + 1], false) * a.k_inv,
+                                  half(w[2 * i + 1], true) * a.k_inv);
                 nt.k[j] = u32x4{q[0], q[1], q[2], q[3]};
             }
         }

@@ -123,32 +123,46 @@ template <> __device__ __forceinline__ _Float16 from_f32<PA_F16>(float x) { retu
 template <> __device__ __forceinline__ __bf16 from_f32<PA_BF16>(float x) { return (__bf16)x; }
 
 // fp32 -> E4M3FN, nearest value with ties to the even code, saturating at
-// +-448, NaN -> 0x7F with the sign kept.  Works on the fp32 bit pattern: the
-// normal range keeps the top 3 mantissa bits with round-half-even on the
-// dropped 20, and the exponent carry of a round-up falls into place because
-// (exponent, mantissa) are adjacent fields; below 2^-6 the value is scaled
-// by 2^9 (exact) and rounded to an integer count of the 2^-9 quantum.
+// +-448, NaN -> 0x7F with the sign kept.  The conversion instruction
+// (v_cvt_pk_fp8_f32) rounds to nearest even but neither saturates (an input
+// past the largest code becomes NaN) nor keeps a NaN through the clamp that
+// would make it saturate; so the input is clamped to +-448 (v_med3_f32) and
+// a NaN input is encoded by hand.  Measured on MI355X over all 2^32 fp32 bit
+// patterns: identical to a bit-level definition (keep the top 3 mantissa
+// bits with round-half-even on the dropped ones, subnormals below 2^-6 as
+// integer counts of 2^-9, saturation at 448), and clamp without the NaN case
+// differs on every NaN, no clamp on every input past 464.
+__device__ __forceinline__ float e4m3_clamp(float x)
+{
+    return __builtin_amdgcn_fmed3f(x, -448.0f, 448.0f);
+}
+
+__device__ __forceinline__ uint32_t e4m3_nan_code(float x)
+{
+    return ((__float_as_uint(x) >> 24) & 0x80u) | 0x7Fu;
+}
+
+// Four values, packed low byte first.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d)
+{
+    uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(a), e4m3_clamp(b), 0, false);
+    w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(c), e4m3_clamp(d), (int)w, true);
+    if (__builtin_isnan(a) || __builtin_isnan(b) || __builtin_isnan(c) || __builtin_isnan(d)) {
+        const float x[4] = {a, b, c, d};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (__builtin_isnan(x[i]))
+                w = (w & ~(0xFFu << (8 * i))) | (e4m3_nan_code(x[i]) << (8 * i));
+    }
+    return w;
+}
+
 __device__ __forceinline__ uint8_t f32_to_e4m3(float x)
 {
-    const uint32_t u = __float_as_uint(x);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const uint32_t a = u & 0x7FFFFFFFu;
-    if (a > 0x7F800000u)
-        return (uint8_t)(sign | 0x7Fu);
-    if (a >= 0x43E00000u) // 448.0f and above (including inf)
-        return (uint8_t)(sign | 0x7Eu);
-    if (a < 0x3C800000u) { // below 2^-6: subnormal E4M3 (or zero)
-        const float q = __builtin_rintf(__uint_as_float(a) * 512.0f); // 0..8
-        return (uint8_t)(sign | (uint32_t)q);
-    }
-    uint32_t r = a >> 20;           // biased fp32 exponent : top 3 mantissa bits
-    const uint32_t rest = a & 0xFFFFFu;
-    if (rest > 0x80000u || (rest == 0x80000u && (r & 1u)))
-        ++r;
-    r -= (127u - 7u) << 3;          // rebias exponent 127 -> 7
-    if (r > 0x7Eu)
-        r = 0x7Eu;
-    return (uint8_t)(sign | r);
+    if (__builtin_isnan(x))
+        return (uint8_t)e4m3_nan_code(x);
+    const float c = e4m3_clamp(x);
+    return (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xFF);
 }
 
 // s_waitcnt operand that waits for vmcnt == 0 and leaves the expcnt and

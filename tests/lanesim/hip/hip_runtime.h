@@ -56,6 +56,7 @@ template <class T> inline T sim_exchange(T v, int src) {
 }
 template <class T> inline T __shfl_xor(T v, int mask, int w = 64) { return sim_exchange(v, sim_lane() ^ mask); }
 template <class T> inline T __shfl_up(T v, unsigned d, int w = 64) { int s = sim_lane() - (int)d; return sim_exchange(v, s < 0 ? sim_lane() : s); }
+template <class T> inline T __shfl_down(T v, unsigned d, int w = 64) { int s = sim_lane() + (int)d; return sim_exchange(v, s > 63 ? sim_lane() : s); }
 inline unsigned long long __ballot(int p) {
   g_wave->buf[sim_lane()] = p ? 1 : 0; g_wave->sync();
   unsigned long long r = 0; for (int i = 0; i < 64; ++i) if (g_wave->buf[i]) r |= 1ull << i;
@@ -70,7 +71,9 @@ inline int __builtin_amdgcn_readlane(int v, int l) {
 }
 inline float __builtin_amdgcn_exp2f(float x) { return exp2f(x); }
 #define __builtin_amdgcn_fence(a, b) (void)0
-#define __builtin_amdgcn_wave_barrier() (void)0
+// a wave's lanes run in lockstep on the GPU: here they meet at a barrier, so
+// LDS written by some lanes is read by the others only after every write
+#define __builtin_amdgcn_wave_barrier() g_wave->sync()
 // math ops whose values do not steer control flow: stubbed
 #define __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, x, y, z) (c)
 #define __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, x, y, z) (c)
@@ -113,8 +116,29 @@ enum { hipDeviceAttributeMaxSharedMemoryPerMultiprocessor = 1, hipDeviceAttribut
 inline hipError_t hipGetDevice(int *d) { *d = 0; return 0; }
 inline hipError_t hipDeviceGetAttribute(int *v, int a, int) { *v = a == 3 ? 256 : 163840; return 0; }
 
+// E4M3 conversion (v_cvt_pk_fp8_f32: nearest even, no saturation) and the
+// clamp used before it, in software
+inline float __builtin_amdgcn_fmed3f(float a, float b, float c) {
+  return std::max(std::min(a, std::max(b, c)), std::min(b, c));
+}
+inline uint32_t sim_e4m3(float x) {
+  uint32_t u; memcpy(&u, &x, 4);
+  const uint32_t sign = (u >> 24) & 0x80u, a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u || a >= 0x43F00000u) return sign | 0x7Fu;  // NaN, or past 480
+  if (a < 0x3C800000u) { float m; memcpy(&m, &a, 4); return sign | (uint32_t)std::nearbyint(m * 512.0f); }
+  uint32_t r = a >> 20; const uint32_t rest = a & 0xFFFFFu;
+  if (rest > 0x80000u || (rest == 0x80000u && (r & 1u))) ++r;
+  r -= (127u - 7u) << 3;
+  return sign | (r > 0x7Eu ? 0x7Fu : r);
+}
+inline int __builtin_amdgcn_cvt_pk_fp8_f32(float a, float b, int old, bool hi) {
+  const uint32_t pair = sim_e4m3(a) | (sim_e4m3(b) << 8);
+  return hi ? (int)(((uint32_t)old & 0xFFFFu) | (pair << 16)) : (int)(((uint32_t)old & 0xFFFF0000u) | pair);
+}
+
 // ---- workgroup shims: one block at a time, all its waves as threads ----------
 #define __shared__ static
+#define __align__(n) __attribute__((aligned(n)))
 struct SimBlock {
   std::mutex mu; std::condition_variable cv; int arrived = 0, total = 0; unsigned gen = 0;
   void sync() {

@@ -203,3 +203,71 @@ def test_garbage_plan_stays_in_bounds(sim, seed):
     r = _run(exe, path, 2)
     assert r.returncode in (0, 3), (r.stdout + r.stderr)[-3000:]
     assert "unwritten 0 of" in r.stdout, r.stdout
+
+
+@pytest.fixture(scope="module")
+def sim_append(tmp_path_factory):
+    if not os.path.exists(CLANG):
+        pytest.skip("no ROCm clang++ to build the lane simulator")
+    d = tmp_path_factory.mktemp("lanesim_append")
+    src = d / "src"
+    src.mkdir()
+    for f in ("device.hpp", "append.hpp", "append.hip"):
+        text = open(os.path.join(CSRC, f)).read()
+        for space in (1, 3, 4):
+            text = text.replace(f"__attribute__((address_space({space})))", "")
+        (src / f).write_text(text)
+    exe = d / "sim_append"
+    subprocess.check_call([CLANG, "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
+                           "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer",
+                           "-I", SIM, "-I", str(src), "-I", os.path.join(ROOT, "include"),
+                           "-x", "c++", os.path.join(SIM, "sim_append.cpp"), "-o", str(exe),
+                           "-lpthread"])
+    return d, exe
+
+
+def _prefill_slots(lens, held, tile_shift, seed, spoil=0):
+    """Slots of one append call that writes lens[i] tokens to sequence i,
+    which already holds held[i] tokens, the sequences' blocks placed at
+    random in a pool with spare blocks; `spoil` entries are then set to -1 or
+    past the pool (skipped by the kernels)."""
+    rng = np.random.default_rng(seed)
+    bs = 16 << tile_shift
+    need = [-(-(h + n) // bs) for h, n in zip(held, lens)]
+    NB = sum(need) + 5
+    perm = rng.permutation(NB)
+    slots, pos = [], 0
+    for h, n, k in zip(held, lens, need):
+        blocks = perm[pos:pos + k]
+        pos += k
+        slots += [int(blocks[t // bs]) * bs + t % bs for t in range(h, h + n)]
+    slots = np.array(slots, np.int32)
+    for i in rng.choice(len(slots), size=spoil, replace=False):
+        slots[i] = -1 if rng.random() < 0.5 else NB * bs + int(rng.integers(0, 50))
+    return slots, NB
+
+
+@pytest.mark.parametrize("kv,tile_shift,case", [
+    (0, 0, "fresh"), (0, 0, "continued"), (0, 1, "spoiled"),
+    (1, 1, "fresh"), (1, 0, "continued"),
+])
+def test_tile_append_matches_token_append(sim_append, kv, tile_shift, case):
+    """The whole-tile append writes exactly the bytes of the per-token one:
+    ragged sequences, so complete tiles start at any place in the token
+    array and cross 16-entry windows; sequences that continue mid-tile (their
+    first tile is partial and goes token by token); entries skipped for a
+    slot outside the pool, which break the tile they fall in."""
+    d, exe = sim_append
+    lens = [17, 70, 3, 64, 33, 20]
+    held = [0] * len(lens) if case != "continued" else [5, 16, 31, 7, 0, 12]
+    slots, NB = _prefill_slots(lens, held, tile_shift, seed=tile_shift * 10 + kv,
+                               spoil=5 if case == "spoiled" else 0)
+    path = d / f"app_{kv}_{tile_shift}_{case}.bin"
+    with open(path, "wb") as f:
+        f.write(np.array([len(slots), 2, NB, tile_shift, kv], np.int32).tobytes())
+        f.write(slots.tobytes())
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0",
+               UBSAN_OPTIONS="halt_on_error=1")
+    r = subprocess.run([str(exe), str(path)], capture_output=True, text=True, timeout=900, env=env)
+    assert r.returncode == 0, (r.stdout + r.stderr)[-3000:]
+    assert "differing 0 " in r.stdout
