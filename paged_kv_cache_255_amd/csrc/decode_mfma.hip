@@ -787,9 +787,9 @@ __device__ void prefix_piece(const DecodeArgs &a, int lane, const SegPos &pos, i
 // Run r of Wr in the rows' split: the row pieces its units [x0, x1) meet.
 template <int QT, int KT, int D>
 __device__ void decode_rows(const DecodeArgs &a, int lane, int32_t r, int32_t Wr,
-                            const PrefixHead &P)
+                            const PrefixHead &P, const LaunchRegs &R)
 {
-    const RunStart rs = row_run_start(a, lane, r, Wr, P);
+    const RunStart rs = row_run_start(a, lane, r, Wr, P, R);
     if (r >= rs.runs)
         return;
     SegPos pos = rs.pos;
@@ -805,7 +805,7 @@ __device__ void decode_rows(const DecodeArgs &a, int lane, int32_t r, int32_t Wr
         }
         x = end;
         if (x < rs.x1)
-            pos = next_row(a, lane, pos, P);
+            pos = next_row(a, lane, pos, P, R);
     }
 }
 
@@ -854,16 +854,21 @@ void decode_mfma_balanced_kernel(DecodeArgs a, int32_t W)
     // Prefix rows only come with a share plan, which also turns on HINT: the
     // launches without one run the code they ran before rows existed.
     PrefixHead P{false, 0, 0, 0};
-    if constexpr (HINT)
-        P = prefix_head(a, lane);
+    LaunchRegs R;
+    R.ok = false;
+    if constexpr (HINT) {
+        R = launch_regs(a, lane);
+        P = R.ok ? R.P : prefix_head(a, lane);
+    }
     int32_t i = i0, Wseq = W;
     if (HINT && P.on) {
         // this wave's run in the rows' split or in the sequences'
-        const int32_t Wr = row_runs(a, P, head_tiles(a, lane, 0, P).per_head, W);
+        const int64_t Th = R.ok ? (int64_t)R.Th : head_tiles(a, lane, 0, P).per_head;
+        const int32_t Wr = row_runs(a, P, Th, W);
         const int32_t per = W / kXcds, rx = Wr / kXcds;
         const int32_t x = i0 / per, loc = i0 - x * per;
         if (loc < rx) {
-            decode_rows<QT, KT, D>(a, lane, x * rx + loc, Wr, P);
+            decode_rows<QT, KT, D>(a, lane, x * rx + loc, Wr, P, R);
             return;
         }
         i = x * (per - rx) + (loc - rx);
@@ -872,7 +877,7 @@ void decode_mfma_balanced_kernel(DecodeArgs a, int32_t W)
 
     // T, the number of runs (never more than units), and the segment holding
     // this wave's first unit
-    const RunStart rs = run_start(a, lane, i, Wseq, P);
+    const RunStart rs = HINT && R.ok ? run_start_regs(a, R, i, Wseq) : run_start(a, lane, i, Wseq, P);
     if (i >= rs.runs)
         return;
     const int64_t x1 = rs.x1;

@@ -263,15 +263,29 @@ struct PartList {
 // all the sequence's tiles, none was left to a row, and that run wrote the
 // rows itself.
 __device__ __forceinline__ bool prefix_segment_parts(const DecodeArgs &a, int lane, int32_t b,
-                                                     int32_t g, int32_t n, const PrefixHead &P,
-                                                     PartList &seq, PartList &row)
+                                                     int32_t g, int32_t n, PartList &seq,
+                                                     PartList &row)
 {
     const int32_t spr = prefix_row_seqs(a.group);
-    const HeadTiles ht = head_tiles(a, lane, b, P);
+    const LaunchRegs L = launch_regs(a, lane);
+    const PrefixHead P = L.ok ? L.P : prefix_head(a, lane);
+    HeadTiles ht;
+    int32_t own;
+    if (L.ok) {
+        ht = HeadTiles{L.before(b), L.Th};
+        int32_t o = 0;
+#pragma unroll
+        for (int c = 0; c < kRegChunks; ++c)
+            if (b >= c * kWave && b < (c + 1) * kWave)
+                o = __builtin_amdgcn_readlane(L.own[c], b - c * kWave);
+        own = uniform(o);
+    } else {
+        ht = head_tiles(a, lane, b, P);
+        own = uniform(own_tiles(a, P, b, n));
+    }
     const int64_t T = ht.per_head * a.num_kv_heads;
     const int32_t Wr = P.on ? row_runs(a, P, ht.per_head, a.waves) : 0;
     const int32_t R = effective_runs(T, a.waves - Wr);
-    const int32_t own = uniform(own_tiles(a, P, b, n));
     seq = PartList{0, 0, 1};
     row = PartList{0, 0, spr};
     const int32_t nt = tiles_of(n) - own;
@@ -287,7 +301,7 @@ __device__ __forceinline__ bool prefix_segment_parts(const DecodeArgs &a, int la
         const int32_t gi = uniform(min(max(plan_group(a)[b], 0), P.ng - 1));
         const int32_t count = uniform(group_count(a, gi));
         const int32_t rank = uniform(min(max(plan_rank(a)[b], 0), max(count - 1, 0)));
-        const RowPos r = row_of_group(a, lane, gi, rank / spr, P);
+        const RowPos r = L.ok ? L.row_of_group(gi, rank / spr) : row_of_group(a, lane, gi, rank / spr, P);
         if (count > 0 && r.nt > 0) {
             // the rows' own split: Hkv * P.units units over Wr runs
             const int64_t Tr = P.units * a.num_kv_heads;
@@ -394,7 +408,7 @@ __global__ __launch_bounds__(64) void merge_segment_kernel(DecodeArgs a)
     }
     if (a.prefix) {
         PartList seq, row;
-        if (prefix_segment_parts(a, lane, b, g, n, prefix_head(a, lane), seq, row))
+        if (prefix_segment_parts(a, lane, b, g, n, seq, row))
             merge_lists<QT, D>(a, b, g, seq, row, lane);
         return;
     }
@@ -449,7 +463,7 @@ __global__ __launch_bounds__(64 * wide_merge_waves(S)) void merge_segment_wide_k
         }
         if (a.prefix) {
             PartList seq;
-            if (!prefix_segment_parts(a, lane, b, g, n, prefix_head(a, lane), seq, row))
+            if (!prefix_segment_parts(a, lane, b, g, n, seq, row))
                 return;
             w0 = seq.w0;
             nparts = seq.n;

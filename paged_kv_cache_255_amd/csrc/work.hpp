@@ -575,6 +575,163 @@ __device__ __forceinline__ SegPos next_segment(const DecodeArgs &a, const SegPos
     }
 }
 
+// ---- one round of loads for a launch with prefix rows -----------------------
+// A launch with a plan splits on every sequence's length and shared tiles and
+// on every group's size; read in loops, those take a round trip per 64
+// entries and per lookup.  For up to kRegChunks x 64 sequences and 64
+// groups, LaunchRegs loads them all in one round, one entry per lane and
+// chunk, and answers the split's lookups from registers (the same answers as
+// head_tiles, locate_tile, prefix_head, locate_row and row_of_group).
+constexpr int32_t kRegChunks = 4;
+
+struct LaunchRegs {
+    bool ok; // the batch and the plan fit (else use the loops)
+    PrefixHead P;
+    int32_t n[kRegChunks], own[kRegChunks], units[kRegChunks], incl[kRegChunks];
+    int32_t carry[kRegChunks]; // units of the chunks before (wave-uniform)
+    int32_t Th;                // units of all sequences (wave-uniform)
+    int32_t g_nt, g_rows, g_unit; // group `lane`: tiles, rows, units a row
+    int32_t g_rows_incl;          // rows of groups 0 .. lane
+    int64_t g_units_incl;         // units of groups 0 .. lane
+
+    // units of sequences [0, b)
+    __device__ __forceinline__ int64_t before(int32_t b) const
+    {
+        int64_t v = 0;
+#pragma unroll
+        for (int c = 0; c < kRegChunks; ++c)
+            if (b >= c * kWave && b < (c + 1) * kWave) {
+                const int k = b - c * kWave;
+                v = carry[c] + (k > 0 ? __builtin_amdgcn_readlane(incl[c], k - 1) : 0);
+            }
+        return uniform((int32_t)v);
+    }
+
+    // the sequence segment holding unit x of the sequences' split
+    __device__ __forceinline__ SegPos locate_seq(int64_t x) const
+    {
+        const int32_t g = (int32_t)(x / Th);
+        const int32_t y = (int32_t)(x - (int64_t)g * Th);
+        SegPos p{g, 0, 0, 0, -1, 0, 0, 0};
+        bool found = false;
+#pragma unroll
+        for (int c = 0; c < kRegChunks; ++c) {
+            const uint64_t hit = __ballot(carry[c] + incl[c] > y && units[c] > 0);
+            if (!found && hit) {
+                const int k = __ffsll((unsigned long long)hit) - 1;
+                p = SegPos{g, c * kWave + k, __builtin_amdgcn_readlane(n[c], k),
+                           __builtin_amdgcn_readlane(own[c], k), -1, 0, 0,
+                           (int64_t)g * Th + carry[c] +
+                               __builtin_amdgcn_readlane(incl[c] - units[c], k)};
+                found = true;
+            }
+        }
+        return p; // y < Th: some chunk hits
+    }
+
+    // the row holding unit y of a head's rows (by_unit), or row number y
+    __device__ __forceinline__ RowPos locate_row(int64_t y, bool by_unit) const
+    {
+        const uint64_t hit = __ballot(g_rows > 0 &&
+                                      (by_unit ? g_units_incl > y : (int64_t)g_rows_incl > y));
+        const int k = __ffsll((unsigned long long)hit) - 1; // y inside the rows: some group hits
+        const int32_t unit = __builtin_amdgcn_readlane(g_unit, k);
+        const int32_t rows_b = __builtin_amdgcn_readlane(g_rows_incl - g_rows, k);
+        const int64_t units_b = readlane64(g_units_incl - (int64_t)g_rows * g_unit, k);
+        RowPos q;
+        q.gi = k;
+        q.nt = __builtin_amdgcn_readlane(g_nt, k);
+        q.chunk = (int32_t)(by_unit ? (y - units_b) / unit : y - rows_b);
+        q.row = rows_b + q.chunk;
+        q.before = units_b + (int64_t)q.chunk * unit;
+        return q;
+    }
+
+    // row `chunk` of group gi (gi < P.ng)
+    __device__ __forceinline__ RowPos row_of_group(int32_t gi, int32_t chunk) const
+    {
+        RowPos q;
+        q.gi = gi;
+        q.chunk = chunk;
+        q.nt = __builtin_amdgcn_readlane(g_nt, gi);
+        q.row = __builtin_amdgcn_readlane(g_rows_incl - g_rows, gi) + chunk;
+        q.before = readlane64(g_units_incl - (int64_t)g_rows * g_unit, gi) +
+                   (int64_t)chunk * __builtin_amdgcn_readlane(g_unit, gi);
+        return q;
+    }
+};
+
+__device__ __forceinline__ LaunchRegs launch_regs(const DecodeArgs &a, int lane)
+{
+    LaunchRegs R;
+    R.P = PrefixHead{false, 0, 0, 0};
+    R.ok = a.prefix && a.num_seqs <= kRegChunks * kWave && a.max_seq_len < kScan32MaxLen &&
+           a.waves % (4 * kXcds) == 0 && a.waves / kXcds >= 8;
+    if (!R.ok)
+        return R;
+    // every load first, then the arithmetic
+    const int32_t ng = uniform_load(a.share + 1);
+    int32_t raw_own[kRegChunks];
+#pragma unroll
+    for (int c = 0; c < kRegChunks; ++c) {
+        const int32_t b = c * kWave + lane;
+        R.n[c] = b < a.num_seqs ? a.seq_lens[b] : 0;
+        raw_own[c] = b < a.num_seqs ? plan_own(a)[b] : 0;
+    }
+    const bool gin = lane < a.num_seqs;
+    const int32_t gcnt = gin ? plan_gcount(a)[lane] : 0;
+    const int32_t gblk = gin ? plan_gblocks(a)[lane] : 0;
+    if (ng <= 0 || ng > a.num_seqs / 2 || ng > kWave) {
+        R.ok = ng <= 0 || ng > a.num_seqs / 2; // no rows (P off) is fine; too many groups: loops
+        R.P = PrefixHead{false, 0, 0, 0};
+        R.g_nt = R.g_rows = R.g_unit = R.g_rows_incl = 0;
+        R.g_units_incl = 0;
+    } else {
+        const bool in = lane < ng;
+        R.g_nt = in ? min(max(gblk, 0), a.max_blocks_per_seq) << a.tile_shift : 0;
+        R.g_rows = in ? group_rows(a, min(max(gcnt, 0), a.num_seqs), R.g_nt) : 0;
+        R.g_unit = (int32_t)row_units(R.g_nt);
+        R.g_rows_incl = wave_incl_scan32(R.g_rows);
+        R.g_units_incl = wave_incl_scan((int64_t)R.g_rows * R.g_unit, lane);
+        const int32_t rows = __builtin_amdgcn_readlane(R.g_rows_incl, kWave - 1);
+        if (rows > 0 && rows <= a.num_seqs / 2)
+            R.P = PrefixHead{true, ng, rows, readlane64(R.g_units_incl, kWave - 1)};
+    }
+    int32_t carry = 0;
+#pragma unroll
+    for (int c = 0; c < kRegChunks; ++c) {
+        const int32_t b = c * kWave + lane;
+        int32_t t = 0;
+        if (R.P.on && b < a.num_seqs) {
+            t = min(max(raw_own[c], 0), a.max_blocks_per_seq) << a.tile_shift;
+            t = (int64_t)t * kTile < (int64_t)R.n[c] ? t : 0;
+        }
+        R.own[c] = t;
+        R.units[c] = b < a.num_seqs ? split_tiles(a, R.n[c], t) : 0;
+        R.incl[c] = wave_incl_scan32(R.units[c]);
+        R.carry[c] = carry;
+        carry += __builtin_amdgcn_readlane(R.incl[c], kWave - 1);
+    }
+    R.Th = uniform(carry);
+    return R;
+}
+
+// run_start from the registers (the sequences' split, W runs)
+__device__ __forceinline__ RunStart run_start_regs(const DecodeArgs &a, const LaunchRegs &R,
+                                                   int32_t i, int32_t W)
+{
+    RunStart r;
+    r.Th = R.Th;
+    r.T = r.Th * a.num_kv_heads;
+    r.runs = effective_runs(r.T, W);
+    if (i >= r.runs)
+        return r;
+    r.x0 = (int64_t)i * r.T / r.runs;
+    r.x1 = (int64_t)(i + 1) * r.T / r.runs;
+    r.pos = R.locate_seq(r.x0);
+    return r;
+}
+
 // ---- the rows' split -----------------------------------------------------------
 // With prefix rows, each XCD's block of W / 8 runs gives its first R (a
 // multiple of 4: whole workgroups) to the rows and the others to the
@@ -598,8 +755,10 @@ __device__ __forceinline__ int32_t row_runs(const DecodeArgs &a, const PrefixHea
 
 // Run r of Wr over the rows: units [x0, x1) of T = Hkv * P.units and the row
 // holding x0.
+// (R: the launch's registers when R.ok, else the loops look the rows up)
 __device__ __forceinline__ RunStart row_run_start(const DecodeArgs &a, int lane, int32_t r,
-                                                  int32_t Wr, const PrefixHead &P)
+                                                  int32_t Wr, const PrefixHead &P,
+                                                  const LaunchRegs &R)
 {
     RunStart s;
     s.Th = P.units;
@@ -610,19 +769,21 @@ __device__ __forceinline__ RunStart row_run_start(const DecodeArgs &a, int lane,
     s.x0 = (int64_t)r * s.T / s.runs;
     s.x1 = (int64_t)(r + 1) * s.T / s.runs;
     const int32_t g = (int32_t)(s.x0 / s.Th);
-    s.pos = row_segment(g, locate_row(a, lane, s.x0 - (int64_t)g * s.Th, true, P),
+    const int64_t y = s.x0 - (int64_t)g * s.Th;
+    s.pos = row_segment(g, R.ok ? R.locate_row(y, true) : locate_row(a, lane, y, true, P),
                         (int64_t)g * s.Th);
     return s;
 }
 
 // The row after p: the head's next row, else the next head's first.
 __device__ __forceinline__ SegPos next_row(const DecodeArgs &a, int lane, const SegPos &p,
-                                           const PrefixHead &P)
+                                           const PrefixHead &P, const LaunchRegs &R)
 {
     const int64_t first = p.first_tile + row_units(p.n);
     const bool wrap = p.row + 1 >= P.rows;
     const int32_t g = wrap ? p.g + 1 : p.g;
-    const RowPos r = locate_row(a, lane, wrap ? 0 : p.row + 1, false, P);
+    const int32_t y = wrap ? 0 : p.row + 1;
+    const RowPos r = R.ok ? R.locate_row(y, false) : locate_row(a, lane, y, false, P);
     return SegPos{g, 0, r.nt, 0, r.row, r.gi, r.chunk, first};
 }
 

@@ -170,6 +170,10 @@ def test_kernels_stay_in_bounds(sim, B, H, G, W, mode):
     # W not a multiple of 32: no rows, the plan only hints (the merge takes
     # the plan's branch all the same)
     (70, 2, 8, 60, ((0, 30, 4), (40, 12, 2)), False),
+    # more than 256 sequences: the split's lookups loop over the tables
+    (300, 2, 4, 64, ((3, 100, 3), (150, 40, 2)), True),
+    # more than 64 groups: the same
+    (140, 1, 4, 64, tuple((2 * i, 2, 1 + i % 3) for i in range(66)), True),
 ])
 def test_prefix_rows_stay_in_bounds(sim, B, H, G, W, groups, rows):
     """Prefix rows in the balanced split: every piece of a row and of the
