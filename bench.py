@@ -434,19 +434,22 @@ def measured_traffic(workload, partition, launch_bytes, no_hint):
     import hashlib
     path = os.path.join(ROOT, "profiles", f"decode_mfma_balanced_{workload}.traffic.json")
     try:
-        rec = json.load(open(path))
+        recs = json.load(open(path))
+        recs = recs if isinstance(recs, list) else [recs]
         h = hashlib.sha256()
-        if rec["kernel_sources"] != TRAFFIC_SOURCES:
-            return None
-        for f in rec["kernel_sources"]:
+        for f in TRAFFIC_SOURCES:
             h.update(open(os.path.join(ROOT, f), "rb").read())
-    except (OSError, ValueError, KeyError):
+    except (OSError, ValueError):
         return None
-    same = (rec.get("workload") == workload and rec.get("partition") == partition and
-            rec.get("algorithmic_bytes_per_launch") == launch_bytes and
-            rec.get("share_plan", False) == (not no_hint) and
-            rec.get("kernel_sources_sha256") == h.hexdigest())
-    return rec["hbm_bytes_per_launch"] if same else None
+    for rec in recs:
+        same = (rec.get("kernel_sources") == TRAFFIC_SOURCES and
+                rec.get("workload") == workload and rec.get("partition") == partition and
+                rec.get("algorithmic_bytes_per_launch") == launch_bytes and
+                rec.get("share_plan", False) == (not no_hint) and
+                rec.get("kernel_sources_sha256") == h.hexdigest())
+        if same:
+            return rec["hbm_bytes_per_launch"]
+    return None
 
 
 TRAFFIC_SOURCES = [
@@ -524,10 +527,20 @@ def write_traffic_record(bench_line, fetch_csv, write_csv, copy_fetch_csv, copy_
         "hbm_bytes_per_launch": int(round(fk * 1024 * fetch_scale + wk * 1024 * write_scale)),
         "algorithmic_bytes_per_launch": roof["algorithmic_bytes"],
     }
+    # one record per launch (steps and warmup fix the last step's lengths): a
+    # record for the same launch is replaced, others are kept
     path = os.path.join(ROOT, "profiles",
                         f"decode_mfma_balanced_{cfg['workload_name']}.traffic.json")
+    try:
+        old = json.load(open(path))
+        old = old if isinstance(old, list) else [old]
+    except (OSError, ValueError):
+        old = []
+    keep = [r for r in old if not (r.get("steps") == steps and r.get("warmup") == warmup and
+                                   r.get("partition") == rec["partition"] and
+                                   r.get("share_plan") == rec["share_plan"])]
     with open(path, "w") as f:
-        json.dump(rec, f, indent=1)
+        json.dump(keep + [rec], f, indent=1)
         f.write("\n")
     print(f"{path}: {rec['hbm_bytes_per_launch']} HBM bytes per launch, "
           f"{rec['hbm_bytes_per_launch'] / rec['algorithmic_bytes_per_launch']:.4f}x algorithmic")
