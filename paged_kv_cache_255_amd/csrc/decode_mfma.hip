@@ -330,36 +330,48 @@ struct MfmaWave {
         }
     }
 
-    // One tile: its tokens lo .. valid - 1 (0 <= lo, valid <= 16) belong to
-    // the range; lo > 0 only in a tile that holds the window start.
-    __device__ void compute(const Tile &T, int lo, int valid, float sc)
+    // K operand of QK product m: 8 dims of the lane's token row (FP8 widened
+    // to the q type).
+    __device__ static A8 k_operand(const Tile &T, int m)
     {
-        f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m = 0; m < QK_MMAS; ++m) {
-            A8 kop;
-            if constexpr (KE == 2) {
-                kop = __builtin_bit_cast(A8, T.k[m]);
-            } else {
-                const u32x4 c = T.k[m / 2];
-                const uint32_t w0 = (m % 2) ? c.z : c.x;
-                const uint32_t w1 = (m % 2) ? c.w : c.y;
-                u32x4 e = {M::fp8x2(w0, false), M::fp8x2(w0, true), M::fp8x2(w1, false),
-                           M::fp8x2(w1, true)};
-                kop = __builtin_bit_cast(A8, e);
-            }
-            s = M::qk(kop, qop[m], s);
+        if constexpr (KE == 2) {
+            return __builtin_bit_cast(A8, T.k[m]);
+        } else {
+            const u32x4 c = T.k[m / 2];
+            const uint32_t w0 = (m % 2) ? c.z : c.x;
+            const uint32_t w1 = (m % 2) ? c.w : c.y;
+            u32x4 e = {M::fp8x2(w0, false), M::fp8x2(w0, true), M::fp8x2(w1, false),
+                       M::fp8x2(w1, true)};
+            return __builtin_bit_cast(A8, e);
         }
-        float x[4];
+    }
+
+    // V^T operand of PV product t: the lane's 4 tokens of dim 16 t + col.
+    __device__ static u32x2 v_operand(const Tile &T, int t)
+    {
+        if constexpr (KE == 2)
+            return u32x2{T.v[t][0], T.v[t][1]};
+        else
+            return u32x2{M::fp8x2(T.v[t][0], false), M::fp8x2(T.v[t][0], true)};
+    }
+
+    // Scaled scores of S^T (tokens lo .. valid - 1 of the tile, -inf for the
+    // others) and the tile's max over them, per query head.
+    __device__ float scores(const f32x4 &s, int lo, int valid, float sc, float (&x)[4]) const
+    {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             x[r] = (4 * grp + r < valid && 4 * grp + r >= lo) ? s[r] * sc : -INFINITY;
-        float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-        bm = max_xor32(max_xor16(bm));
-        // The reference max m_run moves only when a tile's max exceeds it by
-        // more than kLazyRescale (log2 units); until then the weights
-        // 2^(s - m_run) stay below 2^kLazyRescale and acc, l need no rescale.
-        // Any reference gives the same softmax: acc and l share it.
+        const float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        return max_xor32(max_xor16(bm));
+    }
+
+    // The reference max m_run moves only when a tile's max exceeds it by
+    // more than kLazyRescale (log2 units); until then the weights
+    // 2^(s - m_run) stay below 2^kLazyRescale and acc, l need no rescale.
+    // Any reference gives the same softmax: acc and l share it.
+    __device__ void rescale_if(float bm)
+    {
         if (__any(bm > m_run + kLazyRescale)) {
             const float mn = fmaxf(m_run, bm);
             const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
@@ -369,13 +381,32 @@ struct MfmaWave {
             for (int t = 0; t < PV_TILES; ++t)
                 acc[t] *= alpha;
         }
+    }
+
+    // The tile's softmax weights 2^(x - m_run), added to l, as the B operand
+    // of the PV products.
+    __device__ A4 weights(const float (&x)[4])
+    {
         float p[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             p[r] = __builtin_amdgcn_exp2f(x[r] - m_run);
         l_run += (p[0] + p[1]) + (p[2] + p[3]);
         const u32x2 pp = {M::pack2(p[0], p[1]), M::pack2(p[2], p[3])};
-        const A4 pop = __builtin_bit_cast(A4, pp);
+        return __builtin_bit_cast(A4, pp);
+    }
+
+    // One tile: its tokens lo .. valid - 1 (0 <= lo, valid <= 16) belong to
+    // the range; lo > 0 only in a tile that holds the window start.
+    __device__ void compute(const Tile &T, int lo, int valid, float sc)
+    {
+        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < QK_MMAS; ++m)
+            s = M::qk(k_operand(T, m), qop[m], s);
+        float x[4];
+        rescale_if(scores(s, lo, valid, sc, x));
+        const A4 pop = weights(x);
         // Slots past the end or before the window start may hold anything
         // (NaN included): their V values are zeroed, without a branch, so
         // 0 * garbage never reaches acc.  This lane's tokens r = 0..3 are in
@@ -387,14 +418,53 @@ struct MfmaWave {
                                 (klo <= 3 && khi > 3 ? 0xFFFF0000u : 0u);
 #pragma unroll
         for (int t = 0; t < PV_TILES; ++t) {
-            u32x2 vw;
-            if constexpr (KE == 2)
-                vw = u32x2{T.v[t][0], T.v[t][1]};
-            else
-                vw = u32x2{M::fp8x2(T.v[t][0], false), M::fp8x2(T.v[t][0], true)};
+            u32x2 vw = v_operand(T, t);
             vw.x &= keep_x;
             vw.y &= keep_y;
             acc[t] = M::pv(__builtin_bit_cast(A4, vw), pop, acc[t]);
+        }
+    }
+
+    // A whole tile (all 16 tokens in range) for CG states at once, each
+    // with the arithmetic of compute(T, 0, 16, sc): the K and V operands are
+    // formed once, and the groups' products and softmax steps are issued
+    // side by side instead of one group after another.
+    template <int CG>
+    __device__ static void compute_groups(MfmaWave (&w)[CG], const Tile &T, float sc)
+    {
+        f32x4 s[CG];
+#pragma unroll
+        for (int c = 0; c < CG; ++c)
+            s[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < QK_MMAS; ++m) {
+            const A8 kop = k_operand(T, m);
+#pragma unroll
+            for (int c = 0; c < CG; ++c)
+                s[c] = M::qk(kop, w[c].qop[m], s[c]);
+        }
+        float x[CG][4], bm[CG];
+        bool move = false;
+#pragma unroll
+        for (int c = 0; c < CG; ++c) {
+            bm[c] = w[c].scores(s[c], 0, kTile, sc, x[c]);
+            move |= bm[c] > w[c].m_run + kLazyRescale;
+        }
+        if (__any(move)) {
+#pragma unroll
+            for (int c = 0; c < CG; ++c)
+                w[c].rescale_if(bm[c]);
+        }
+        A4 pop[CG];
+#pragma unroll
+        for (int c = 0; c < CG; ++c)
+            pop[c] = w[c].weights(x[c]);
+#pragma unroll
+        for (int t = 0; t < PV_TILES; ++t) {
+            const A4 vop = __builtin_bit_cast(A4, v_operand(T, t));
+#pragma unroll
+            for (int c = 0; c < CG; ++c)
+                w[c].acc[t] = M::pv(vop, pop[c], w[c].acc[t]);
         }
     }
 
@@ -747,19 +817,14 @@ __device__ void prefix_piece(const DecodeArgs &a, int lane, const SegPos &pos, i
             const int32_t id_after = id_at(jb + DEPTH);
             load(id_next, jb + DEPTH - 1, T[(d + DEPTH - 1) % DEPTH]);
             __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int cg = 0; cg < CG; ++cg)
-                wv[cg].compute(T[d], 0, kTile, sc);
+            Wv::compute_groups(wv, T[d], sc);
             id_next = id_after;
         }
     }
 #pragma unroll
     for (int d = 0; d + 1 < DEPTH; ++d) {
-        if (i + d < n) {
-#pragma unroll
-            for (int cg = 0; cg < CG; ++cg)
-                wv[cg].compute(T[d], 0, kTile, sc);
-        }
+        if (i + d < n)
+            Wv::compute_groups(wv, T[d], sc);
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 

@@ -67,10 +67,12 @@ __device__ __forceinline__ int32_t tiles_of(int32_t n) { return (n + kTile - 1) 
 // sequences): with no charge, runs holding two segments ended 3.9 us after
 // the others (a tile takes a wave about 1.2 us); whole decode steps took
 // 58.1, 57.5, 57.0, 57.1, 57.3, 57.5 and 58.1 us on average (runs of three,
-// two sweeps) with charges of 0, 3, 5, 7, 9, 12 and 16 tiles.  In the
-// balanced order a segment is kSegmentCost virtual tiles, then its real
-// tiles.
-constexpr int32_t kSegmentCost = 5;
+// two sweeps) with charges of 0, 3, 5, 7, 9, 12 and 16 tiles.  Per-wave
+// clocks later put a piece's fixed cost at 3.6 (32 sequences) and 4.2 (256
+// sequences sharing a prompt) tiles, and a charge of 4 ran both launches
+// 1 - 1.5% faster than 5 (3 gave back most of it).  In the balanced order a
+// segment is kSegmentCost virtual tiles, then its real tiles.
+constexpr int32_t kSegmentCost = 4;
 
 // XCDs (accelerator complex dies) of an MI355X.  The hardware dispatcher
 // hands a launch's workgroups to the XCDs round-robin, so workgroup w runs on

@@ -13,7 +13,9 @@ once, and no two (run, segment) pairs share a slot.  (The device code is
 checked end to end by the GPU parity tests; this pins the arithmetic itself,
 including sizes no GPU test reaches.)
 """
+import os
 import random
+import re
 
 import pytest
 
@@ -60,7 +62,15 @@ def test_run_of_tile_exhaustive_small():
             assert [run_of_tile(x, T, R) for x in range(T)] == owner
 
 
-SEGMENT_COST = 5  # kSegmentCost in work.hpp
+def _segment_cost():
+    """kSegmentCost as work.hpp defines it (read from the header, so the
+    model below cannot drift from the kernels)."""
+    here = os.path.dirname(os.path.abspath(__file__))
+    text = open(os.path.join(here, "..", "paged_kv_cache_255_amd", "csrc", "work.hpp")).read()
+    return int(re.search(r"constexpr int32_t kSegmentCost = (\d+);", text).group(1))
+
+
+SEGMENT_COST = _segment_cost()
 
 
 @pytest.mark.parametrize("seed", range(40))
