@@ -356,9 +356,11 @@ pa_status pa_cache_append(const void *k, const void *v, void *k_cache, void *v_c
  * PA_PARTITION_BALANCED with the MFMA kernel and a shape that can read a
  * share plan's groups once per KV head (see seq_shared), this includes the
  * room for those reads' partial states, (W + Hkv x num_seqs / 2) x
- * 4 x 16 / G slots of G x (head_dim + 2) floats (W: the launch's waves); a
- * launch given less, but no less than the size without that room, reads
- * every sequence's blocks itself. */
+ * 4 x 16 / G slots of G x (head_dim + 2) floats (W: the launch's waves),
+ * and, from the next 256-byte boundary, 16 bytes per (sequence, KV head) in
+ * which the decode records where the merge finds that pair's partial
+ * states; a launch given less, but no less than the size without that room,
+ * reads every sequence's blocks itself. */
 size_t pa_decode_workspace_bytes(const pa_kv_desc *desc, int32_t num_seqs, int32_t max_seq_len,
                                  int32_t partition_size);
 
@@ -404,9 +406,10 @@ int32_t pa_decode_balanced_waves(const pa_kv_desc *desc);
  *   partition_size: PA_PARTITION_NONE, PA_PARTITION_BALANCED, or a positive
  *     multiple of block_size: each (sequence, KV head) is split into chunks
  *     of that many tokens whose partial softmax states are merged by a second
- *     kernel.  The partitioned modes need `workspace` (device, at least
- *     pa_decode_workspace_bytes(...) bytes, no initial contents required;
- *     two launches that may run at the same time must not share one).
+ *     kernel.  The partitioned modes need `workspace` (device, 16-byte
+ *     aligned, at least pa_decode_workspace_bytes(...) bytes, no initial
+ *     contents required; two launches that may run at the same time must
+ *     not share one).
  * Accumulation is fp32; out is rounded to nearest even. */
 pa_status pa_decode(const void *q, const void *k_cache, const void *v_cache,
                     const int32_t *block_tables, int32_t max_blocks_per_seq,

@@ -155,6 +155,17 @@ size_t slot_bytes(const pa_kv_desc *d, int64_t slots)
     const int64_t G = d->num_q_heads / d->num_kv_heads;
     return (size_t)(slots * G * (2 + d->head_dim) * (int64_t)sizeof(float));
 }
+// With prefix rows the workspace also holds, after the slots (at a 256-byte
+// boundary), the decode's record of where each segment's parts are: four
+// int32 per (KV head, sequence).
+size_t seg_dir_offset(const pa_kv_desc *d, int64_t slots)
+{
+    return (slot_bytes(d, slots) + 255) / 256 * 256;
+}
+size_t prefix_bytes(const pa_kv_desc *d, int64_t slots, int32_t num_seqs)
+{
+    return seg_dir_offset(d, slots) + (size_t)num_seqs * d->num_kv_heads * 4 * sizeof(int32_t);
+}
 
 int32_t parts_for(int32_t max_seq_len, int32_t partition)
 {
@@ -296,7 +307,7 @@ size_t pa_decode_workspace_bytes(const pa_kv_desc *desc, int32_t num_seqs, int32
             return 0;
         slots = balanced_seq_slots(desc, W, num_seqs);
         if (prefix_capable(desc))
-            slots += balanced_row_slots(desc, W, num_seqs);
+            return prefix_bytes(desc, slots + balanced_row_slots(desc, W, num_seqs), num_seqs);
     } else {
         slots = (int64_t)num_seqs * desc->num_kv_heads * parts_for(max_seq_len, partition_size);
     }
@@ -448,11 +459,13 @@ pa_status decode_impl(Phase phase, const void *q, const void *k_cache, const voi
         // the partials and the merge launch; a plan groups no sequence with
         // a slid window)
         const int64_t with_rows = a.num_slots + balanced_row_slots(desc, a.waves, num_seqs);
-        if (seq_shared && prefix_capable(desc) &&
-            workspace_bytes >= slot_bytes(desc, with_rows)) {
+        if (seq_shared && prefix_capable(desc) && with_rows < ((int64_t)1 << 31) &&
+            workspace_bytes >= prefix_bytes(desc, with_rows, num_seqs)) {
             a.prefix = 1;
             a.prefix_base = a.num_slots;
             a.num_slots = with_rows;
+            a.seg_dir = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) +
+                                                    seg_dir_offset(desc, with_rows));
         }
     } else {
         items64 = (int64_t)num_seqs * desc->num_kv_heads * a.max_parts;
@@ -466,6 +479,8 @@ pa_status decode_impl(Phase phase, const void *q, const void *k_cache, const voi
     const int32_t items = (int32_t)items64;
     if (partition_size != 0 && (!workspace || need == 0 || workspace_bytes < need))
         return fail(PA_ERR_CAPACITY, "workspace smaller than pa_decode_workspace_bytes()");
+    if (partition_size != 0 && (reinterpret_cast<uintptr_t>(workspace) & 15) != 0)
+        return fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;

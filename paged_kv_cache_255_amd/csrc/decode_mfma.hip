@@ -925,11 +925,11 @@ void decode_mfma_balanced_kernel(DecodeArgs a, int32_t W)
         R = launch_regs(a, lane);
         P = R.ok ? R.P : prefix_head(a, lane);
     }
-    int32_t i = i0, Wseq = W;
+    int32_t i = i0, Wseq = W, Wr = 0;
     if (HINT && P.on) {
         // this wave's run in the rows' split or in the sequences'
         const int64_t Th = R.ok ? (int64_t)R.Th : head_tiles(a, lane, 0, P).per_head;
-        const int32_t Wr = row_runs(a, P, Th, W);
+        Wr = row_runs(a, P, Th, W);
         const int32_t per = W / kXcds, rx = Wr / kXcds;
         const int32_t x = i0 / per, loc = i0 - x * per;
         if (loc < rx) {
@@ -961,6 +961,15 @@ void decode_mfma_balanced_kernel(DecodeArgs a, int32_t W)
         if (hi > lo) {
             const int32_t j = (int32_t)(lo - r0) + pos.own;
             const int32_t je = (int32_t)(hi - r0) + pos.own;
+            // with prefix rows, the run holding the segment's first own tile
+            // records where the merge finds all its parts; the plan entries
+            // that takes load here, while the piece's tiles do
+            const bool record = HINT && a.prefix && j == pos.own;
+            int32_t grp_raw = 0, rank_raw = 0;
+            if (record && pos.own > 0) {
+                grp_raw = uniform_load(plan_group(a) + pos.b);
+                rank_raw = uniform_load(plan_rank(a) + pos.b);
+            }
             wv.start(a, pos.b, pos.g);
             const bool ok = wv.template run<HINT>(a, pos.b, pos.g, j * kTile,
                                                   min(je * kTile, pos.n), pos.n);
@@ -969,6 +978,14 @@ void decode_mfma_balanced_kernel(DecodeArgs a, int32_t W)
                 wv.write_out(a, pos.b, pos.g, pos.n, ok);
             else
                 wv.write_partial(a, balanced_slot(a, i, pos.g, pos.b), ok);
+            if (record) {
+                const SegLists e = segment_lists(a, lane, pos.b, pos.g, pos.n, pos.own, r0,
+                                                 rs.T, rs.runs, Wr, P, R, grp_raw, rank_raw);
+                if (lane == 0)
+                    *reinterpret_cast<u32x4 *>(seg_dir_entry(a, pos.g, pos.b)) =
+                        u32x4{(uint32_t)e.seq_w0, (uint32_t)e.seq_n, (uint32_t)e.row_w0,
+                              (uint32_t)e.row_n};
+            }
         }
         x = r0 + nb;
         if (x < x1)

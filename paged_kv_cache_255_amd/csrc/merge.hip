@@ -76,15 +76,22 @@ struct MergeState {
     }
 };
 
-// Folds parts [p_begin, p_end) of a segment into st, part p in slot
-// w0 + p stride, CH = 16 / S parts per batch (16 x 3 loads in flight per
-// lane), in part order, with the online rescale between batches:
+// Slots holding parts of a segment: w0 + p stride for p < n.
+struct PartList {
+    int64_t w0, n, stride;
+};
+
+// Folds parts [p_begin, p_end) of the list `first` followed by the list
+// `then` (part p < first.n in slot first.w0 + p first.stride, part
+// first.n + k in slot then.w0 + k then.stride) into st, CH = 16 / S parts
+// per batch (16 x 3 loads in flight per lane), in part order, with the
+// online rescale between batches:
 //   M = max_p m_p,  out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p
 // per query head, the identity the online update inside a work item uses.
 template <int D, int S>
-__device__ __forceinline__ void merge_fold(const DecodeArgs &a, int64_t w0, int64_t stride,
-                                           int64_t p_begin, int64_t p_end, int lane,
-                                           MergeState<S> &st)
+__device__ __forceinline__ void merge_fold(const DecodeArgs &a, const PartList &first,
+                                           const PartList &then, int64_t p_begin,
+                                           int64_t p_end, int lane, MergeState<S> &st)
 {
     constexpr int CH = 16 / S;
     int hs[S];
@@ -97,7 +104,9 @@ __device__ __forceinline__ void merge_fold(const DecodeArgs &a, int64_t w0, int6
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const bool in = p0 + c < p_end;
-            const int64_t w = w0 + (p0 + (in ? c : 0)) * stride;
+            const int64_t p = p0 + (in ? c : 0);
+            const int64_t w = p < first.n ? first.w0 + p * first.stride
+                                          : then.w0 + (p - first.n) * then.stride;
             const float *base = ws_acc(a, w, 0, D);
 #pragma unroll
             for (int s = 0; s < S; ++s) {
@@ -161,7 +170,7 @@ __device__ __forceinline__ void merge_segment_s(const DecodeArgs &a, int32_t b, 
                                                 int64_t w0, int64_t nparts, int lane)
 {
     MergeState<S> st;
-    merge_fold<D, S>(a, w0, 1, 0, nparts, lane, st);
+    merge_fold<D, S>(a, PartList{w0, nparts, 1}, PartList{0, 0, 1}, 0, nparts, lane, st);
     merge_store<QT, D, S>(a, b, g, st, lane);
 }
 
@@ -250,69 +259,23 @@ __device__ __forceinline__ bool segment_parts(const DecodeArgs &a, int lane, int
     return true;
 }
 
-// Slots holding parts of a segment: w0 + p stride for p < n.
-struct PartList {
-    int64_t w0, n, stride;
-};
-
-// The parts of segment (sequence b of n tokens, KV head g) of a balanced
-// launch with prefix rows: the pieces of its own tiles in the sequences'
-// split (seq) and, when its prefix row reads its leading tiles, the pieces
-// of that row in the rows' split, one slot per piece at the member's place
-// in the row (row).  False when one run held
-// all the sequence's tiles, none was left to a row, and that run wrote the
-// rows itself.
-__device__ __forceinline__ bool prefix_segment_parts(const DecodeArgs &a, int lane, int32_t b,
-                                                     int32_t g, int32_t n, PartList &seq,
-                                                     PartList &row)
+// The parts of segment (g, b) of a launch with prefix rows, as the decode
+// recorded them (SegLists): its own pieces, then its row's.  Slots are
+// clamped into the workspace, so an entry the decode did not write (a
+// length that changed between the two phases) cannot send the merge outside
+// it.  False when one run wrote the rows itself.
+__device__ __forceinline__ bool prefix_lists(const DecodeArgs &a, const u32x4 &e, PartList &seq,
+                                             PartList &row)
 {
-    const int32_t spr = prefix_row_seqs(a.group);
-    const LaunchRegs L = launch_regs(a, lane);
-    const PrefixHead P = L.ok ? L.P : prefix_head(a, lane);
-    HeadTiles ht;
-    int32_t own;
-    if (L.ok) {
-        ht = HeadTiles{L.before(b), L.Th};
-        int32_t o = 0;
-#pragma unroll
-        for (int c = 0; c < kRegChunks; ++c)
-            if (b >= c * kWave && b < (c + 1) * kWave)
-                o = __builtin_amdgcn_readlane(L.own[c], b - c * kWave);
-        own = uniform(o);
-    } else {
-        ht = head_tiles(a, lane, b, P);
-        own = uniform(own_tiles(a, P, b, n));
-    }
-    const int64_t T = ht.per_head * a.num_kv_heads;
-    const int32_t Wr = P.on ? row_runs(a, P, ht.per_head, a.waves) : 0;
-    const int32_t R = effective_runs(T, a.waves - Wr);
-    seq = PartList{0, 0, 1};
-    row = PartList{0, 0, spr};
-    const int32_t nt = tiles_of(n) - own;
-    if (nt > 0) {
-        const int64_t S0 = (int64_t)g * ht.per_head + ht.before + kSegmentCost;
-        const int64_t i0 = run_of_tile(S0, T, R);
-        const int64_t i1 = run_of_tile(S0 + nt - 1, T, R);
-        if (own == 0 && i0 == i1)
-            return false;
-        seq = PartList{balanced_slot(a, i0, g, b), i1 - i0 + 1, 1};
-    }
-    if (own > 0) {
-        const int32_t gi = uniform(min(max(plan_group(a)[b], 0), P.ng - 1));
-        const int32_t count = uniform(group_count(a, gi));
-        const int32_t rank = uniform(min(max(plan_rank(a)[b], 0), max(count - 1, 0)));
-        const RowPos r = L.ok ? L.row_of_group(gi, rank / spr) : row_of_group(a, lane, gi, rank / spr, P);
-        if (count > 0 && r.nt > 0) {
-            // the rows' own split: Hkv * P.units units over Wr runs
-            const int64_t Tr = P.units * a.num_kv_heads;
-            const int32_t Rr = effective_runs(Tr, Wr);
-            const int64_t S0 = (int64_t)g * P.units + r.before + kSegmentCost;
-            const int64_t i0 = run_of_tile(S0, Tr, Rr);
-            const int64_t i1 = run_of_tile(S0 + row_body(r.nt) - 1, Tr, Rr);
-            row = PartList{row_slot(a, i0, g, r.row, P) + rank % spr, i1 - i0 + 1, spr};
-        }
-    }
-    return true;
+    const int64_t S = a.num_slots;
+    const int64_t sw = min(max((int64_t)(int32_t)e.x, (int64_t)0), S - 1);
+    const int64_t sn = min(max((int64_t)(int32_t)e.y, (int64_t)0), S - sw);
+    const int64_t stride = prefix_row_seqs(a.group);
+    const int64_t rw = min(max((int64_t)(int32_t)e.z, (int64_t)0), S - 1);
+    const int64_t rn = min(max((int64_t)(int32_t)e.w, (int64_t)0), (S - 1 - rw) / stride + 1);
+    seq = PartList{sw, sn, 1};
+    row = PartList{rw, rn, stride};
+    return sn > 0;
 }
 
 // Combines the segment's parts, its own pieces first, then its row's.
@@ -321,8 +284,7 @@ __device__ __forceinline__ void merge_lists_s(const DecodeArgs &a, int32_t b, in
                                               const PartList &seq, const PartList &row, int lane)
 {
     MergeState<S> st;
-    merge_fold<D, S>(a, seq.w0, seq.stride, 0, seq.n, lane, st);
-    merge_fold<D, S>(a, row.w0, row.stride, 0, row.n, lane, st);
+    merge_fold<D, S>(a, seq, row, 0, seq.n + row.n, lane, st);
     merge_store<QT, D, S>(a, b, g, st, lane);
 }
 
@@ -401,6 +363,9 @@ __global__ __launch_bounds__(64) void merge_segment_kernel(DecodeArgs a)
         }
     }
     const int32_t n = a.seq_lens[b];
+    // with prefix rows, the decode's record of the segment's parts comes in
+    // with the length
+    const u32x4 e = a.prefix ? load16(seg_dir_entry(a, g, b)) : u32x4{0u, 0u, 0u, 0u};
     const bool valid = len_ok(a, n);
     if (!valid || n == 0) {
         merge_fill<QT, D>(a, b, g, valid, lane);
@@ -408,7 +373,7 @@ __global__ __launch_bounds__(64) void merge_segment_kernel(DecodeArgs a)
     }
     if (a.prefix) {
         PartList seq, row;
-        if (prefix_segment_parts(a, lane, b, g, n, seq, row))
+        if (prefix_lists(a, e, seq, row))
             merge_lists<QT, D>(a, b, g, seq, row, lane);
         return;
     }
@@ -455,6 +420,7 @@ __global__ __launch_bounds__(64 * wide_merge_waves(S)) void merge_segment_wide_k
             return;
     } else {
         const int32_t n = a.seq_lens[b];
+        const u32x4 e = a.prefix ? load16(seg_dir_entry(a, g, b)) : u32x4{0u, 0u, 0u, 0u};
         const bool valid = len_ok(a, n);
         if (!valid || n == 0) {
             if (wave == 0)
@@ -463,7 +429,7 @@ __global__ __launch_bounds__(64 * wide_merge_waves(S)) void merge_segment_wide_k
         }
         if (a.prefix) {
             PartList seq;
-            if (!prefix_segment_parts(a, lane, b, g, n, seq, row))
+            if (!prefix_lists(a, e, seq, row))
                 return;
             w0 = seq.w0;
             nparts = seq.n;
@@ -471,10 +437,12 @@ __global__ __launch_bounds__(64 * wide_merge_waves(S)) void merge_segment_wide_k
             return;
         }
     }
-    // wave w folds its share of the segment's own pieces, then of its row's
+    // wave w folds its share of the segment's parts: its own pieces, then
+    // its row's
+    const int64_t total = nparts + row.n;
     MergeState<S> st;
-    merge_fold<D, S>(a, w0, 1, wave * nparts / NW, (wave + 1) * nparts / NW, lane, st);
-    merge_fold<D, S>(a, row.w0, row.stride, wave * row.n / NW, (wave + 1) * row.n / NW, lane, st);
+    merge_fold<D, S>(a, PartList{w0, nparts, 1}, row, wave * total / NW,
+                     (wave + 1) * total / NW, lane, st);
 #pragma unroll
     for (int s = 0; s < S; ++s) {
         s_m[wave][s][lane] = st.M[s];

@@ -18,6 +18,8 @@ struct DecodeArgs {
     int32_t prefix;            // balanced launch that may read the plan's groups once
                                // per KV head (the launch decides with prefix_layout)
     int64_t prefix_base;       // first partial-state slot of those reads
+    int32_t *seg_dir;          // with prefix: per (KV head, sequence), the slots the
+                               // merge folds (SegLists), written by the decode
     void *out;
     float *ws;                 // partial states (partitioned modes)
     int32_t num_seqs;
@@ -593,6 +595,7 @@ struct LaunchRegs {
     int32_t carry[kRegChunks]; // units of the chunks before (wave-uniform)
     int32_t Th;                // units of all sequences (wave-uniform)
     int32_t g_nt, g_rows, g_unit; // group `lane`: tiles, rows, units a row
+    int32_t g_count;              // group `lane`: members (as group_count)
     int32_t g_rows_incl;          // rows of groups 0 .. lane
     int64_t g_units_incl;         // units of groups 0 .. lane
 
@@ -686,12 +689,13 @@ __device__ __forceinline__ LaunchRegs launch_regs(const DecodeArgs &a, int lane)
     if (ng <= 0 || ng > a.num_seqs / 2 || ng > kWave) {
         R.ok = ng <= 0 || ng > a.num_seqs / 2; // no rows (P off) is fine; too many groups: loops
         R.P = PrefixHead{false, 0, 0, 0};
-        R.g_nt = R.g_rows = R.g_unit = R.g_rows_incl = 0;
+        R.g_nt = R.g_rows = R.g_unit = R.g_rows_incl = R.g_count = 0;
         R.g_units_incl = 0;
     } else {
         const bool in = lane < ng;
         R.g_nt = in ? min(max(gblk, 0), a.max_blocks_per_seq) << a.tile_shift : 0;
-        R.g_rows = in ? group_rows(a, min(max(gcnt, 0), a.num_seqs), R.g_nt) : 0;
+        R.g_count = in ? min(max(gcnt, 0), a.num_seqs) : 0;
+        R.g_rows = in ? group_rows(a, R.g_count, R.g_nt) : 0;
         R.g_unit = (int32_t)row_units(R.g_nt);
         R.g_rows_incl = wave_incl_scan32(R.g_rows);
         R.g_units_incl = wave_incl_scan((int64_t)R.g_rows * R.g_unit, lane);
@@ -811,7 +815,65 @@ __device__ __forceinline__ int64_t row_slot(const DecodeArgs &a, int64_t r, int3
 // (R <= T, so runs are never empty and consecutive runs are adjacent).
 __device__ __forceinline__ int64_t run_of_tile(int64_t x, int64_t T, int32_t R)
 {
+    // x < T: with T R below 2^32 the quotient is a 32-bit division (a 64-bit
+    // one is a long emulated sequence)
+    if (T * R < ((int64_t)1 << 32))
+        return (int64_t)(((uint32_t)(x + 1) * (uint32_t)R - 1u) / (uint32_t)T);
     return ((x + 1) * R - 1) / T;
+}
+
+// The partial states of segment (sequence b of n tokens, KV head g) of a
+// balanced launch with prefix rows, in the order the merge folds them: the
+// pieces of its own tiles in the sequences' split, slots seq_w0 .. seq_w0 +
+// seq_n - 1, then, when its prefix row reads its leading tiles, one slot per
+// piece of that row at the member's place in it, row_w0 + k SPR for k <
+// row_n.  seq_n = 0 when one run held all the sequence's tiles, no row read
+// any, and that run wrote the rows itself.  The run that decodes the
+// segment's first own tile (unit S0 of the sequences' split of T units over
+// R runs) writes them to seg_dir for the merge.
+struct SegLists {
+    int32_t seq_w0, seq_n, row_w0, row_n;
+};
+
+__device__ __forceinline__ int32_t *seg_dir_entry(const DecodeArgs &a, int32_t g, int32_t b)
+{
+    return a.seg_dir + 4 * ((int64_t)g * a.num_seqs + b);
+}
+
+// (grp_raw, rank_raw: plan_group(a)[b] and plan_rank(a)[b] as loaded, so
+// that the caller can issue those loads early)
+__device__ __forceinline__ SegLists segment_lists(const DecodeArgs &a, int lane, int32_t b,
+                                                  int32_t g, int32_t n, int32_t own, int64_t S0,
+                                                  int64_t T, int32_t R, int32_t Wr,
+                                                  const PrefixHead &P, const LaunchRegs &L,
+                                                  int32_t grp_raw, int32_t rank_raw)
+{
+    SegLists e{0, 0, 0, 0};
+    const int32_t nt = tiles_of(n) - own; // >= 1: a member's own tiles hold its last token
+    const int64_t i0 = run_of_tile(S0, T, R);
+    const int64_t i1 = run_of_tile(S0 + nt - 1, T, R);
+    e.seq_w0 = (int32_t)balanced_slot(a, i0, g, b);
+    e.seq_n = own == 0 && i0 == i1 ? 0 : (int32_t)(i1 - i0 + 1);
+    if (own > 0 && P.on) {
+        const int32_t spr = prefix_row_seqs(a.group);
+        const int32_t gi = uniform(min(max(grp_raw, 0), P.ng - 1));
+        const int32_t count =
+            uniform(L.ok ? __builtin_amdgcn_readlane(L.g_count, gi) : group_count(a, gi));
+        const int32_t rank = uniform(min(max(rank_raw, 0), max(count - 1, 0)));
+        const RowPos r = L.ok ? L.row_of_group(gi, rank / spr)
+                              : row_of_group(a, lane, gi, rank / spr, P);
+        if (count > 0 && r.nt > 0) {
+            // the rows' own split: Hkv * P.units units over Wr runs
+            const int64_t Tr = P.units * a.num_kv_heads;
+            const int32_t Rr = effective_runs(Tr, Wr);
+            const int64_t S0r = (int64_t)g * P.units + r.before + kSegmentCost;
+            const int64_t j0 = run_of_tile(S0r, Tr, Rr);
+            const int64_t j1 = run_of_tile(S0r + row_body(r.nt) - 1, Tr, Rr);
+            e.row_w0 = (int32_t)(row_slot(a, j0, g, r.row, P) + rank % spr);
+            e.row_n = (int32_t)(j1 - j0 + 1);
+        }
+    }
+    return e;
 }
 
 // Work item w covers (sequence b, KV head g, part p) with

@@ -76,11 +76,15 @@ int main(int argc, char **argv)
         seq_slots + (mode == 2 ? ((int64_t)W + (int64_t)H * (B / 2)) * prefix_row_seqs(G) : 0);
     // NaN in every slot: a merge that reads a slot no run wrote gives NaN
     std::vector<float> ws((size_t)nslots * G * (2 + D), __builtin_nanf(""));
+    // the decode's record of each segment's parts (prefix rows): garbage
+    // until written, so a merge that reads an entry no run wrote reads
+    // the last slot (NaN) after clamping
+    std::vector<int32_t> dir((size_t)B * H * 4, 0x7F7F7F7F);
 
     DecodeArgs a{};
     a.q = q.data(); a.k_cache = k.data(); a.v_cache = v.data(); a.block_tables = tables.data();
     a.seq_lens = lens.data(); a.seq_starts = nullptr; a.share = hint ? plan.data() : nullptr;
-    a.prefix = mode == 2; a.prefix_base = seq_slots;
+    a.prefix = mode == 2; a.prefix_base = seq_slots; a.seg_dir = mode == 2 ? dir.data() : nullptr;
     a.out = out.data(); a.ws = ws.data(); a.num_seqs = B; a.num_q_heads = H * G;
     a.num_kv_heads = H; a.group = G; a.num_blocks = NB; a.tile_shift = 0;
     a.max_blocks_per_seq = maxb; a.max_seq_len = maxlen; a.partition = kPartitionBalanced;
