@@ -459,11 +459,12 @@ def measured_traffic(workload, partition, launch_bytes, no_hint):
     return None
 
 
+# The decode kernel's translation unit and what it includes, and the build's
+# flags: a traffic record holds only while these are unchanged.
 TRAFFIC_SOURCES = [
     "paged_kv_cache_255_amd/csrc/decode_mfma.hip",
     "paged_kv_cache_255_amd/csrc/work.hpp",
     "paged_kv_cache_255_amd/csrc/device.hpp",
-    "paged_kv_cache_255_amd/csrc/append.hpp",
     "paged_kv_cache_255_amd/build.py",
 ]
 

@@ -19,12 +19,31 @@
 
 namespace pa {
 
+// One token's K row and V column values for one KV head as lane `lane`
+// holds them: dims lane, lane + 64, ...
+template <int QT, int D>
+struct TokenVals {
+    typename Store<QT>::T k[D / kWave], v[D / kWave];
+};
+
+template <int QT, int D>
+__device__ __forceinline__ TokenVals<QT, D> load_token(const typename Store<QT>::T *ks,
+                                                       const typename Store<QT>::T *vs, int lane)
+{
+    TokenVals<QT, D> x;
+#pragma unroll
+    for (int i = 0; i < D / kWave; ++i) {
+        x.k[i] = ks[i * kWave + lane];
+        x.v[i] = vs[i * kWave + lane];
+    }
+    return x;
+}
+
 template <int QT, int KT, int D>
-__device__ __forceinline__ void store_token(const typename Store<QT>::T *ks,
-                                            const typename Store<QT>::T *vs, void *k_cache,
-                                            void *v_cache, int32_t blk, int32_t off,
-                                            int32_t tile_shift, int32_t g, int32_t num_kv_heads,
-                                            float k_inv, float v_inv, int lane)
+__device__ __forceinline__ void put_token(const TokenVals<QT, D> &x, void *k_cache,
+                                          void *v_cache, int32_t blk, int32_t off,
+                                          int32_t tile_shift, int32_t g, int32_t num_kv_heads,
+                                          float k_inv, float v_inv, int lane)
 {
     using TK = typename Store<KT>::T;
     // first tile of (blk, g); `off` (0 .. block_size - 1) is in tile off / 16
@@ -37,13 +56,24 @@ __device__ __forceinline__ void store_token(const typename Store<QT>::T *ks,
         const int d = i * kWave + lane;
         const int vi = v_tile_index<Store<KT>::bytes>(u, d);
         if constexpr (KT == PA_FP8_E4M3) {
-            kd[d] = f32_to_e4m3(to_f32<QT>(ks[d]) * k_inv);
-            vd[vi] = f32_to_e4m3(to_f32<QT>(vs[d]) * v_inv);
+            kd[d] = f32_to_e4m3(to_f32<QT>(x.k[i]) * k_inv);
+            vd[vi] = f32_to_e4m3(to_f32<QT>(x.v[i]) * v_inv);
         } else {
-            kd[d] = ks[d];
-            vd[vi] = vs[d];
+            kd[d] = x.k[i];
+            vd[vi] = x.v[i];
         }
     }
+}
+
+template <int QT, int KT, int D>
+__device__ __forceinline__ void store_token(const typename Store<QT>::T *ks,
+                                            const typename Store<QT>::T *vs, void *k_cache,
+                                            void *v_cache, int32_t blk, int32_t off,
+                                            int32_t tile_shift, int32_t g, int32_t num_kv_heads,
+                                            float k_inv, float v_inv, int lane)
+{
+    put_token<QT, KT, D>(load_token<QT, D>(ks, vs, lane), k_cache, v_cache, blk, off, tile_shift,
+                         g, num_kv_heads, k_inv, v_inv, lane);
 }
 
 } // namespace pa

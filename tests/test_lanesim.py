@@ -253,17 +253,24 @@ def _prefill_slots(lens, held, tile_shift, seed, spoil=0):
 
 @pytest.mark.parametrize("kv,tile_shift,case", [
     (0, 0, "fresh"), (0, 0, "continued"), (0, 1, "spoiled"),
-    (1, 1, "fresh"), (1, 0, "continued"),
+    (1, 1, "fresh"), (1, 0, "continued"), (0, 0, "step"), (1, 1, "step"),
 ])
 def test_tile_append_matches_token_append(sim_append, kv, tile_shift, case):
     """The whole-tile append writes exactly the bytes of the per-token one:
     ragged sequences, so complete tiles start at any place in the token
     array and cross 16-entry windows; sequences that continue mid-tile (their
     first tile is partial and goes token by token); entries skipped for a
-    slot outside the pool, which break the tile they fall in."""
+    slot outside the pool, which break the tile they fall in; a decode step
+    (one token for each of 70 sequences: no complete tile, every entry
+    written on its own)."""
     d, exe = sim_append
-    lens = [17, 70, 3, 64, 33, 20]
-    held = [0] * len(lens) if case != "continued" else [5, 16, 31, 7, 0, 12]
+    if case == "step":
+        rng = np.random.default_rng(7 + kv)
+        lens = [1] * 70
+        held = [int(h) for h in rng.integers(0, 300, size=70)]
+    else:
+        lens = [17, 70, 3, 64, 33, 20]
+        held = [0] * len(lens) if case != "continued" else [5, 16, 31, 7, 0, 12]
     slots, NB = _prefill_slots(lens, held, tile_shift, seed=tile_shift * 10 + kv,
                                spoil=5 if case == "spoiled" else 0)
     path = d / f"app_{kv}_{tile_shift}_{case}.bin"
