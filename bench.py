@@ -789,10 +789,17 @@ def copy_calibration(torch):
     dst = torch.empty(n, dtype=torch.uint8, device="cuda")
     src.fill_(1)
     torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
     for _ in range(3):
         dst.copy_(src)
+    e1.record()
     torch.cuda.synchronize()
-    print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
+    us = e0.elapsed_time(e1) * 1e3 / 3
+    # also the rate of a plain device copy (read + write), the ceiling a
+    # copy-shaped kernel such as the prefill append can be measured against
+    print(json.dumps({"copy_calibration_bytes": n, "copies": 3, "us_per_copy": round(us, 1),
+                      "gbs_read_plus_write": round(2 * n / (us * 1e-6) / 1e9, 1)}), flush=True)
 
 
 def cpu_baseline(w, k_cache, v_cache, q, tables, lens, nblocks, ks, vs, target_s):

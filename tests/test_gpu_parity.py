@@ -448,3 +448,34 @@ def test_zero_length_rows_mfma(part):
                         num_kv_heads=Hkv, head_dim=D, block_size=16, num_blocks=NB,
                         q_dtype="bf16", kv_dtype="bf16", scale=float(np.float32(0.088)))
     check_close(to_f64(out), ref, "bf16", "bf16")
+
+
+@pytest.mark.parametrize("part", [16, pa.PARTITION_BALANCED])
+def test_misaligned_workspace_is_refused(part):
+    """A partitioned launch given a workspace that is not 16-byte aligned
+    (pa.h: the partial states and the segments' records are read 16 bytes
+    at a time) fails with PA_ERR_INVALID_ARG before anything is launched:
+    the output keeps its contents.  The same launch on an aligned view of
+    the same buffer runs."""
+    say(f"[case] misaligned workspace partition={part}")
+    D, NB, Hq, Hkv = 128, 6, 8, 2
+    g = torch.Generator().manual_seed(5)
+    k = torch.randn(NB * Hkv * 16 * D, generator=g).to(torch.bfloat16).cuda()
+    v = torch.randn(NB * Hkv * 16 * D, generator=g).to(torch.bfloat16).cuda()
+    tables = torch.tensor([[0, 3], [2, 1], [4, 5]], dtype=torch.int32, device="cuda")
+    lens = torch.tensor([30, 20, 17], dtype=torch.int32, device="cuda")
+    q = torch.randn(3, Hq, D, generator=g).to(torch.bfloat16).cuda()
+    desc = pa.kv_desc(Hq, Hkv, D, NB, "bf16", "bf16", kernel=pa.KERNEL_MFMA)
+    nb = pa.pa_decode_workspace_bytes(desc, 3, 32, part)
+    buf = torch.empty(nb + 256, dtype=torch.uint8, device="cuda")
+    out = torch.full_like(q, 7.0)
+    with pytest.raises(pa.PaError) as err:
+        pa.pa_decode(q, k, v, tables, lens, 32, 0.088, out, desc, workspace=buf[4:4 + nb],
+                     partition_size=part)
+    assert err.value.status == pa.ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
+    pa.pa_decode(q, k, v, tables, lens, 32, 0.088, out, desc, workspace=buf[16:16 + nb],
+                 partition_size=part)
+    torch.cuda.synchronize()
+    assert not torch.any(out == 7.0)
