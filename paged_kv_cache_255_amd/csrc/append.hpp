@@ -1,6 +1,8 @@
 // One token's K row and V column for one KV head, written into its cache slot
-// by one wave: the cache append, shared by the append kernel and the decode
-// launch that appends the step's token itself (so both write the same bytes).
+// by one wave: the cache append of append_kernel and of the entries of
+// append_tiles_kernel outside complete tiles.  (The decode launch that
+// appends the step's token itself writes the same bytes from its own
+// registers, MfmaWave::store_new_token; the GPU tests compare the caches.)
 //
 // dev.to, "Why LLMs Run Out of VRAM: KV Cache Fragmentation and How
 // PagedAttention Fixes It", §1: every step appends the new token's K and V to
