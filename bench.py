@@ -415,7 +415,7 @@ def main():
             "probe_gbs": None if probe is None else probe["gbs"],
             "frac_of_probe": None if probe is None else round(roof_gbs / probe["gbs"], 4),
             "probe": probe,
-            "traffic": (measured_traffic(w.name, partition, int(launch_bytes), no_hint)
+            "traffic": (measured_traffic(w.name, partition, int(roof_bytes), no_hint)
                         if bs == 16 else None),
             "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE x1)",
             "algorithmic_bytes": int(roof_bytes),
