@@ -83,3 +83,41 @@ def test_noalloc_refuses_more_than_its_scratch():
                                           ctypes.byref(desc), None)
     assert st == pa.ERR_CAPACITY
     assert "allocation-free" in pa.pa_last_error()
+
+
+def test_noalloc_with_a_share_plan():
+    """A batch whose sequences share a prompt, with its share plan: the
+    scratch has no room for the plan's prefix rows (their room is sized for
+    W x 16 member slots, about 34 MB), so the allocation-free step reads the
+    shared blocks with the plan's caching hint and gives the bits of
+    pa_decode_append with the same plan and a workspace holding only the
+    sequences' room; both match the oracle."""
+    w = workloads.config(4, "small")
+    say(f"[case] noalloc with a share plan {w.name}")
+    inp = Inputs(w, 0)
+    part = pa.PARTITION_BALANCED
+    ref = GpuStep(w, 0, inp, partition=part, kernel=pa.KERNEL_MFMA)
+    plan = ref.plan()
+    assert plan[1] >= 1  # the batch has a group
+    W = pa.pa_decode_balanced_waves(ref.desc)
+    G = w.num_q_heads // w.num_kv_heads
+    seq_room = (W + w.num_seqs * w.num_kv_heads) * G * (w.head_dim + 2) * 4
+    assert seq_room < pa.pa_decode_workspace_bytes(ref.desc, w.num_seqs, w.max_seq_len(), part)
+    ref.workspace = torch.empty(seq_room, dtype=torch.uint8, device="cuda")
+    ref.append_prefill()
+    want = ref.decode_append(out=torch.full_like(inp.q, 7.0), seq_shared=plan).clone()
+    g = GpuStep(w, 0, inp, partition=part, kernel=pa.KERNEL_MFMA)
+    g.append_prefill()
+    i = g.inputs
+    slots = torch.from_numpy(np.ascontiguousarray(g.step_slots)).cuda()
+    got = torch.full_like(inp.q, 3.0)
+    pa.pa_decode_append_noalloc(i.q, i.k_new, i.v_new, slots, g.k_cache, g.v_cache, g.d_tables,
+                                g.d_lens, w.max_seq_len(), w.scale, got, g.desc, i.k_scale,
+                                i.v_scale, partition_size=part,
+                                seq_shared=torch.from_numpy(plan).cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(want.view(torch.int16), got.view(torch.int16))
+    assert torch.equal(ref.k_cache.view(torch.uint8), g.k_cache.view(torch.uint8))
+    assert torch.equal(ref.v_cache.view(torch.uint8), g.v_cache.view(torch.uint8))
+    err = check_close(to_f64(got), OracleStep(w, 0, inp).decode(), w.kv_dtype, w.q_dtype)
+    say(f"[ok] oracle err={err:.3g}")
