@@ -658,12 +658,18 @@ struct MfmaWave {
     // The lane groups hold disjoint tokens: sum their shares of l.
     __device__ void finish() { l_run = sum_xor32(sum_xor16(l_run)); }
 
-    __device__ void write_out(const DecodeArgs &a, int32_t b, int32_t g, int32_t n, bool ok)
+    // Output rows G g .. G g + G - 1 of sequence b (G = group): [G][D].
+    __device__ static TQ *out_rows(const DecodeArgs &a, int32_t b, int32_t g)
+    {
+        return static_cast<TQ *>(a.out) + ((size_t)b * a.num_q_heads + (size_t)g * a.group) * D;
+    }
+
+    // The G output rows from o: the output tensor's, or an LDS image of them.
+    __device__ void put_out(TQ *o, const DecodeArgs &a, bool ok) const
     {
         if (col >= a.group)
             return;
-        TQ *o = static_cast<TQ *>(a.out) +
-                ((size_t)b * a.num_q_heads + (size_t)g * a.group + col) * D;
+        o += col * D;
         // l = 0: no token in the range (n = 0 or an empty window)
         const float inv = !ok ? NAN : (l_run == 0.f ? 0.f : a.v_scale / l_run);
 #pragma unroll
@@ -673,16 +679,21 @@ struct MfmaWave {
                 o[16 * t + 4 * grp + r] = from_f32<QT>(acc[t][r] * inv);
     }
 
-    __device__ void write_partial(const DecodeArgs &a, int64_t slot, bool ok)
+    // A partial state in the workspace layout: m, l of the G heads ([G][2])
+    // from ml, acc ([G][D]) from accp (the workspace's, or LDS images).
+    __device__ void put_ml(float *ml, const DecodeArgs &a, bool ok) const
+    {
+        if (col >= a.group || grp != 0)
+            return;
+        ml[2 * col] = ok ? m_run : NAN;
+        ml[2 * col + 1] = ok ? l_run : NAN;
+    }
+
+    __device__ void put_acc(float *accp, const DecodeArgs &a, bool ok) const
     {
         if (col >= a.group)
             return;
-        if (grp == 0) {
-            float *ml = ws_ml(a, slot, col);
-            ml[0] = ok ? m_run : NAN;
-            ml[1] = ok ? l_run : NAN;
-        }
-        float *accp = ws_acc(a, slot, col, D);
+        accp += col * D;
         const float f = ok ? a.v_scale : NAN;
 #pragma unroll
         for (int t = 0; t < PV_TILES; ++t)
@@ -690,7 +701,98 @@ struct MfmaWave {
             for (int r = 0; r < 4; ++r)
                 accp[16 * t + 4 * grp + r] = acc[t][r] * f;
     }
+
+    __device__ void write_out(const DecodeArgs &a, int32_t b, int32_t g, int32_t n, bool ok)
+    {
+        put_out(out_rows(a, b, g), a, ok);
+    }
+
+    __device__ void write_partial(const DecodeArgs &a, int64_t slot, bool ok)
+    {
+        put_ml(ws_ml(a, slot, 0), a, ok);
+        put_acc(ws_acc(a, slot, 0, D), a, ok);
+    }
 };
+
+// A run's results (outputs, partial states, the merge's records of
+// segments), held in the wave's LDS area and stored when the run ends.  The
+// tile loads and the stores count in one in-order counter, so the wait for
+// a tile loaded after a store also waits for that store's acknowledgement;
+// held to the run's end, the stores keep no tile waiting.  Each record is an
+// image of its destination's bytes (a multiple of 8); one that does not fit
+// beside those held stores them first, and one larger than the whole area
+// (or an area of no bytes) is stored directly by the caller.  Headers (the
+// destination, bytes, image offset) take the area's first kRecs quads.
+// `used` and `nrec` are the same in every lane.
+struct Stage {
+    static constexpr int kRecs = 16;
+    u32x4 *area;
+    int32_t cap; // image bytes
+    int32_t used, nrec;
+
+    __device__ Stage(u32x4 *q, int32_t bytes)
+        : area(q), cap(max(0, (bytes & ~15) - kRecs * 16)), used(0), nrec(0)
+    {
+    }
+
+    // Whether a record of `bytes` can be held (storing those held if it
+    // needs their room).  Then image() gives its LDS image.
+    __device__ bool fits(int lane, int32_t bytes)
+    {
+        const int32_t need = (bytes + 15) & ~15;
+        if (need > cap)
+            return false;
+        if (used + need > cap || nrec == kRecs)
+            flush(lane);
+        return true;
+    }
+
+    __device__ char *image(int lane, const void *dst, int32_t bytes)
+    {
+        char *img = reinterpret_cast<char *>(area + kRecs) + used;
+        if (lane == 0) {
+            const uint64_t d = reinterpret_cast<uint64_t>(dst);
+            area[nrec] = u32x4{(uint32_t)d, (uint32_t)(d >> 32), (uint32_t)bytes, (uint32_t)used};
+        }
+        used += (bytes + 15) & ~15;
+        nrec += 1;
+        return img;
+    }
+
+    // Records from here on are stored directly by the caller.
+    __device__ void close() { cap = 0; }
+
+    // Stores every record held: 16 bytes per lane and instruction when the
+    // destination and size allow, else 8.
+    __device__ void flush(int lane)
+    {
+        if (nrec == 0)
+            return;
+        using GU4 = __attribute__((address_space(1))) u32x4;
+        using GU2 = __attribute__((address_space(1))) u32x2;
+        wave_lds_sync();
+        for (int32_t r = 0; r < nrec; ++r) {
+            const u32x4 h = area[r];
+            const uint64_t d = ((uint64_t)(uint32_t)uniform((int32_t)h.y) << 32) |
+                               (uint32_t)uniform((int32_t)h.x);
+            const int32_t bytes = uniform((int32_t)h.z);
+            const char *src = reinterpret_cast<const char *>(area + kRecs) + uniform((int32_t)h.w);
+            if (((bytes | (int32_t)d) & 15) == 0) {
+                for (int32_t o = 16 * lane; o < bytes; o += 16 * kWave)
+                    *reinterpret_cast<GU4 *>(d + o) = *reinterpret_cast<const u32x4 *>(src + o);
+            } else {
+                for (int32_t o = 8 * lane; o < bytes; o += 8 * kWave)
+                    *reinterpret_cast<GU2 *>(d + o) = *reinterpret_cast<const u32x2 *>(src + o);
+            }
+        }
+        wave_lds_sync();
+        used = 0;
+        nrec = 0;
+    }
+};
+
+// LDS quads of one wave's Stage area (16 KiB).
+constexpr int kStageQuads = 1024;
 
 // partition == 0 or > 0: one wave per work item (see work.hpp).  HINT:
 // a.share is set; each kernel is built with and without it, so the
@@ -888,6 +990,10 @@ __global__ __launch_bounds__(256)
 void decode_mfma_balanced_kernel(DecodeArgs a, int32_t W)
 {
     __shared__ u32x4 table_sink[4][kWave]; // receives the prefetch, never read
+    // the waves' Stage areas: launches with a share plan only (their runs
+    // hold several pieces; without one, a run rarely ends a piece before its
+    // last, and the area cost config 2's step 0.4 us)
+    __shared__ u32x4 stage_lds[4][HINT ? kStageQuads : 1];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int32_t i0 = balanced_run(blockIdx.x, wave, W);
@@ -951,7 +1057,9 @@ void decode_mfma_balanced_kernel(DecodeArgs a, int32_t W)
     // The run's units [x0, x1) meet each segment's start charge and tiles in
     // turn; a piece of tiles is a range to decode (a run may begin or end
     // inside a start charge, which holds nothing to read).
-    MfmaWave<QT, KT, D> wv(lane);
+    using Wv = MfmaWave<QT, KT, D>;
+    Wv wv(lane);
+    Stage st(&stage_lds[wave][0], a.stage_bytes);
     int64_t x = rs.x0;
     while (x < x1) {
         // the sequence's tiles past the ones its prefix row reads
@@ -974,44 +1082,82 @@ void decode_mfma_balanced_kernel(DecodeArgs a, int32_t W)
             const bool ok = wv.template run<HINT>(a, pos.b, pos.g, j * kTile,
                                                   min(je * kTile, pos.n), pos.n);
             wv.finish();
-            if (j == 0 && je == tiles_of(pos.n))
-                wv.write_out(a, pos.b, pos.g, pos.n, ok);
-            else
-                wv.write_partial(a, balanced_slot(a, i, pos.g, pos.b), ok);
+            // The results of every piece but the run's last go to the run's
+            // Stage when they fit (no tile comes after the last piece to wait
+            // for its stores); the branches keep every pointer's address
+            // space known.
+            if (HINT && r0 + nb >= x1)
+                st.close();
+            if (j == 0 && je == tiles_of(pos.n)) {
+                typename Wv::TQ *o = Wv::out_rows(a, pos.b, pos.g);
+                const int32_t bytes = a.group * D * (int32_t)sizeof(typename Wv::TQ);
+                if (HINT && st.fits(lane, bytes))
+                    wv.put_out(reinterpret_cast<typename Wv::TQ *>(st.image(lane, o, bytes)), a, ok);
+                else
+                    wv.put_out(o, a, ok);
+            } else {
+                const int64_t slot = balanced_slot(a, i, pos.g, pos.b);
+                float *ml = ws_ml(a, slot, 0), *accp = ws_acc(a, slot, 0, D);
+                if (HINT && st.fits(lane, 8 * a.group))
+                    wv.put_ml(reinterpret_cast<float *>(st.image(lane, ml, 8 * a.group)), a, ok);
+                else
+                    wv.put_ml(ml, a, ok);
+                if (HINT && st.fits(lane, 4 * D * a.group))
+                    wv.put_acc(reinterpret_cast<float *>(st.image(lane, accp, 4 * D * a.group)), a,
+                               ok);
+                else
+                    wv.put_acc(accp, a, ok);
+            }
             if (record) {
                 const SegLists e = segment_lists(a, lane, pos.b, pos.g, pos.n, pos.own, r0,
                                                  rs.T, rs.runs, Wr, P, R, grp_raw, rank_raw);
-                if (lane == 0)
-                    *reinterpret_cast<u32x4 *>(seg_dir_entry(a, pos.g, pos.b)) =
-                        u32x4{(uint32_t)e.seq_w0, (uint32_t)e.seq_n, (uint32_t)e.row_w0,
-                              (uint32_t)e.row_n};
+                const u32x4 ev = {(uint32_t)e.seq_w0, (uint32_t)e.seq_n, (uint32_t)e.row_w0,
+                                  (uint32_t)e.row_n};
+                int32_t *dst = seg_dir_entry(a, pos.g, pos.b);
+                if (HINT && st.fits(lane, 16)) {
+                    u32x4 *img = reinterpret_cast<u32x4 *>(st.image(lane, dst, 16));
+                    if (lane == 0)
+                        *img = ev;
+                } else if (lane == 0) {
+                    *reinterpret_cast<u32x4 *>(dst) = ev;
+                }
             }
         }
         x = r0 + nb;
         if (x < x1)
             pos = next_segment(a, pos, P);
     }
+    if constexpr (HINT)
+        st.flush(lane);
 }
 
-// LDS bytes the balanced kernel's launch asks for and never uses: just over
-// half of a CU's LDS, so that a CU holds one 256-thread workgroup, one wave
-// per SIMD (0 if the device cannot grant that much to one workgroup).
+// Static LDS of the balanced kernel: the table prefetch's sink and, with a
+// share plan, the four waves' Stage areas.
+constexpr int balanced_static_lds(bool hint)
+{
+    return (int)sizeof(u32x4) * 4 * (kWave + (hint ? kStageQuads : 1));
+}
+
+// LDS bytes the balanced kernel's launch asks for beyond its static arrays,
+// and never uses: enough that the workgroup holds just over half of a CU's
+// LDS, so that a CU holds one 256-thread workgroup, one wave per SIMD (0 if
+// the device cannot grant that much to one workgroup).
 // Measured on MI355X: a CU's memory requests are served oldest wave first, so
 // a second or third wave per SIMD adds no bandwidth; it only waits, then
 // runs as a later generation, which lengthens the tail and cuts the tiles
 // into more runs (more partial states to merge).  With one wave per SIMD the
 // config-2 step went from 72.0 to 69.9 us, the config-5 one from 236.7 to
 // 219.1 us.
-static int balanced_lds_bytes()
+static int balanced_lds_bytes(bool hint)
 {
     static std::mutex mu;
-    static std::map<int, int> cache;
+    static std::map<int, int> cache[2];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess)
         return 0;
     std::lock_guard<std::mutex> lock(mu);
-    auto it = cache.find(dev);
-    if (it != cache.end())
+    auto it = cache[hint].find(dev);
+    if (it != cache[hint].end())
         return it->second;
     int per_cu = 0, per_block = 0;
     if (hipDeviceGetAttribute(&per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
@@ -1020,9 +1166,8 @@ static int balanced_lds_bytes()
             hipSuccess)
         return 0;
     int want = per_cu / 2 + 1024;
-    if (want > per_block)
-        want = 0;
-    cache[dev] = want;
+    want = want > per_block ? 0 : max(0, want - balanced_static_lds(hint));
+    cache[hint][dev] = want;
     return want;
 }
 
@@ -1034,7 +1179,9 @@ hipError_t launch_mfma(const DecodeArgs &a, int32_t num_items, hipStream_t strea
     if (a.partition == kPartitionBalanced) {
         auto kern = hint ? &decode_mfma_balanced_kernel<QT, KT, D, true>
                          : &decode_mfma_balanced_kernel<QT, KT, D, false>;
-        hipLaunchKernelGGL(kern, dim3(grid), dim3(256), balanced_lds_bytes(), stream, a,
+        DecodeArgs b = a;
+        b.stage_bytes = hint ? (int32_t)sizeof(u32x4) * kStageQuads : 0;
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(256), balanced_lds_bytes(hint), stream, b,
                            num_items);
     } else {
         auto kern =
@@ -1052,7 +1199,7 @@ int mfma_balanced_waves_per_cu()
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
             &blocks,
             reinterpret_cast<const void *>(&decode_mfma_balanced_kernel<QT, KT, D, false>), 256,
-            balanced_lds_bytes()) != hipSuccess)
+            balanced_lds_bytes(false)) != hipSuccess)
         return 0;
     return blocks * 4;
 }

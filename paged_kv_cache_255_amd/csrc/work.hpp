@@ -44,6 +44,8 @@ struct DecodeArgs {
     const void *v_new;
     const int32_t *slots;
     float k_inv, v_inv;        // FP8 cache: 1 / k_scale, 1 / v_scale
+    int32_t stage_bytes;       // balanced launch: LDS bytes per wave that hold a run's
+                               // results until it ends (0: stored at once)
 };
 
 constexpr int32_t kPartitionBalanced = -1; // PA_PARTITION_BALANCED

@@ -9,7 +9,9 @@
 // Input file: int32 header B maxb NB Hkv G D W max_len, then lens[B],
 // tables[B][maxb], slots[B], then a share plan of 2 + 8 B words (pa.h
 // layout).  argv: input, mode: 0 no plan, 1 the plan as a cache-policy hint
-// only, 2 the plan with prefix rows.
+// only, 2 the plan with prefix rows; optional: LDS bytes per wave that hold
+// a run's results until it ends (default: what the launch gives; 0 stores
+// them at once).
 #include <hip/hip_runtime.h>
 thread_local dim3 threadIdx, blockIdx;
 thread_local SimWave *g_wave;
@@ -91,6 +93,9 @@ int main(int argc, char **argv)
     a.max_parts = 1; a.waves = W; a.num_slots = nslots; a.score_scale = 0.1f; a.v_scale = 1.f;
     a.append = 1; a.k_new = kn.data(); a.v_new = vn.data(); a.slots = slots.data();
     a.k_inv = a.v_inv = 1.f;
+    a.stage_bytes = argc > 3 ? atoi(argv[3]) : (int32_t)sizeof(u32x4) * kStageQuads;
+    if (a.stage_bytes < 0 || a.stage_bytes > (int32_t)sizeof(u32x4) * kStageQuads)
+        return 2;
     for (int wave = 0; wave < W; ++wave) {
         if (hint)
             run_wave(wave / 4, wave % 4, [&] { decode_mfma_balanced_kernel<PA_BF16, PA_BF16, 128, true>(a, W); });

@@ -9,8 +9,8 @@ merge, on seeded tables, and checks that every output element is written
 and that the merge reads only slots the decode runs wrote (the workspace
 starts as NaN).
 The arithmetic is not checked here (the GPU parity tests do that): this pins
-the work split, the run placement, the slot arithmetic and the token store to
-stay inside their buffers for shapes the GPU tests do not reach, such as a
+the work split, the run placement, the slot arithmetic, the token store and
+the LDS area that holds a run's results to stay inside their buffers for shapes the GPU tests do not reach, such as a
 wave count that is not a multiple of 32.
 """
 import os
@@ -136,11 +136,11 @@ def _case(path, B, H, G, W, max_len, seed, groups=(), plan_kind="real"):
     return plan
 
 
-def _run(exe, path, mode):
+def _run(exe, path, mode, stage=None):
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0",
                UBSAN_OPTIONS="halt_on_error=1")
-    return subprocess.run([str(exe), str(path), str(mode)], capture_output=True, text=True,
-                          timeout=900, env=env)
+    args = [str(exe), str(path), str(mode)] + ([] if stage is None else [str(stage)])
+    return subprocess.run(args, capture_output=True, text=True, timeout=900, env=env)
 
 
 @pytest.mark.parametrize("B,H,G,W,mode", [
@@ -155,6 +155,28 @@ def test_kernels_stay_in_bounds(sim, B, H, G, W, mode):
     _case(path, B, H, G, W, max_len=300, seed=B * 1000 + W,
           plan_kind="hint" if mode else "real")
     r = _run(exe, path, mode)
+    assert r.returncode == 0, (r.stdout + r.stderr)[-3000:]
+    assert "unwritten 0 of" in r.stdout and "NaN 0" in r.stdout
+
+
+@pytest.mark.parametrize("stage", [
+    0,      # every result stored at once
+    2352,   # room for one partial state and its records: stored often before the end
+    1200,   # an acc image does not fit: stored at once beside held m, l and records
+])
+@pytest.mark.parametrize("mode", [1, 2])
+def test_held_results_are_all_stored(sim, stage, mode):
+    """With a share plan, a run's outputs, partial states and segment records
+    go through the wave's LDS area until the run ends (or until it is full):
+    with areas too small for some records and too small for more than one
+    piece, every output is still written and the merge still reads only
+    written slots."""
+    d, exe = sim
+    path = d / f"stage_{stage}_{mode}.bin"
+    groups = ((1, 20, 5), (21, 10, 3)) if mode == 2 else ()
+    _case(path, 40, 2, 4, 64, max_len=300, seed=40 * 7 + 64, groups=groups,
+          plan_kind="real" if mode == 2 else "hint")
+    r = _run(exe, path, mode, stage)
     assert r.returncode == 0, (r.stdout + r.stderr)[-3000:]
     assert "unwritten 0 of" in r.stdout and "NaN 0" in r.stdout
 
