@@ -468,6 +468,15 @@ struct MfmaWave {
         }
     }
 
+    // The step's token as run() leaves it (pa_decode_append): in the cache's
+    // storage format, bound for offset `off` of block `blk`; put is false
+    // when the range does not end the sequence or the slot is refused.
+    struct PendingToken {
+        bool put;
+        NewToken nt;
+        int32_t blk, off;
+    };
+
     // Tokens [t0, t1) of (b, g), of a sequence of n tokens; t0 is a multiple
     // of 16.  Tokens before the window start (seq_starts[b]) are left out.
     // Returns false if a block-table entry is outside the pool (that block is
@@ -476,9 +485,11 @@ struct MfmaWave {
     // the cache slot of position n - 1.
     // HINT: a.share is set (the launch reads its hint once per range and
     // picks the cache policy per tile); without it every tile streams.
+    // The appended token is not stored here: it comes back in `tok` for the
+    // caller to store (store_pending) or hold.
     template <bool HINT>
     __device__ bool run(const DecodeArgs &a, int32_t b, int32_t g, int32_t t0, int32_t t1,
-                        int32_t n_seq)
+                        int32_t n_seq, PendingToken &tok)
     {
         // The block table does not change while the kernel runs: its entries
         // are read with scalar loads (one wave-uniform id per tile, fetched
@@ -650,9 +661,56 @@ struct MfmaWave {
         } else {
             ring(std::integral_constant<bool, true>{}, jb0, last, false, true);
         }
-        if (put)
-            store_new_token(a, nt, id_last, off_last, sh, g);
+        tok.put = put;
+        tok.nt = nt;
+        tok.blk = id_last;
+        tok.off = off_last;
         return !bad;
+    }
+
+    __device__ void store_pending(const DecodeArgs &a, const PendingToken &tok, int32_t g) const
+    {
+        if (tok.put)
+            store_new_token(a, tok.nt, tok.blk, tok.off, a.tile_shift, g);
+    }
+
+    // The bytes store_new_token writes, as two images: the K row (ROW_BYTES,
+    // contiguous at k_row) and the V values in dim order (D * KE bytes,
+    // scattered over the V tile at v_tile, token u: Stage::image_v).
+    __device__ static char *token_k_row(const DecodeArgs &a, const PendingToken &tok, int32_t g)
+    {
+        const size_t tile0 = ((size_t)tok.blk * a.num_kv_heads + g) << a.tile_shift;
+        return static_cast<char *>(const_cast<void *>(a.k_cache)) +
+               (tile0 * kTile + tok.off) * ROW_BYTES;
+    }
+
+    __device__ static char *token_v_tile(const DecodeArgs &a, const PendingToken &tok, int32_t g)
+    {
+        const size_t tile0 = ((size_t)tok.blk * a.num_kv_heads + g) << a.tile_shift;
+        return static_cast<char *>(const_cast<void *>(a.v_cache)) +
+               (tile0 + tok.off / kTile) * TILE_BYTES;
+    }
+
+    __device__ void put_token_k(char *img, const NewToken &nt) const
+    {
+        if (col != 0)
+            return;
+#pragma unroll
+        for (int j = 0; j < CH_PER_LANE; ++j)
+            *reinterpret_cast<u32x4 *>(img + (grp + 4 * j) * 16) = nt.k[j];
+    }
+
+    __device__ void put_token_v(char *img, const NewToken &nt) const
+    {
+        if (grp != 0)
+            return;
+#pragma unroll
+        for (int t = 0; t < PV_TILES; ++t) {
+            if constexpr (KE == 2)
+                reinterpret_cast<uint16_t *>(img)[16 * t + col] = (uint16_t)nt.v[t];
+            else
+                reinterpret_cast<uint8_t *>(img)[16 * t + col] = (uint8_t)nt.v[t];
+        }
     }
 
     // The lane groups hold disjoint tokens: sum their shares of l.
@@ -715,11 +773,13 @@ struct MfmaWave {
 };
 
 // A run's results (outputs, partial states, the merge's records of
-// segments), held in the wave's LDS area and stored when the run ends.  The
+// segments, appended tokens), held in the wave's LDS area and stored when
+// the run ends.  The
 // tile loads and the stores count in one in-order counter, so the wait for
 // a tile loaded after a store also waits for that store's acknowledgement;
 // held to the run's end, the stores keep no tile waiting.  Each record is an
-// image of its destination's bytes (a multiple of 8); one that does not fit
+// image of its destination's bytes (a multiple of 8), or, for a token's V
+// values, of the values to scatter over their tile; one that does not fit
 // beside those held stores them first, and one larger than the whole area
 // (or an area of no bytes) is stored directly by the caller.  Headers (the
 // destination, bytes, image offset) take the area's first kRecs quads.
@@ -735,24 +795,42 @@ struct Stage {
     {
     }
 
-    // Whether a record of `bytes` can be held (storing those held if it
-    // needs their room).  Then image() gives its LDS image.
-    __device__ bool fits(int lane, int32_t bytes)
+    // Whether a record of `bytes` (or two, of `bytes` and `bytes2`) can be
+    // held, storing those held if it needs their room.  Then image() /
+    // image_v() give the LDS images, in that order.
+    __device__ bool fits(int lane, int32_t bytes, int32_t bytes2 = -1)
     {
-        const int32_t need = (bytes + 15) & ~15;
+        const int32_t need = ((bytes + 15) & ~15) + (bytes2 < 0 ? 0 : (bytes2 + 15) & ~15);
+        const int32_t recs = bytes2 < 0 ? 1 : 2;
         if (need > cap)
             return false;
-        if (used + need > cap || nrec == kRecs)
+        if (used + need > cap || nrec + recs > kRecs)
             flush(lane);
         return true;
     }
 
     __device__ char *image(int lane, const void *dst, int32_t bytes)
     {
+        return take(lane, dst, (uint32_t)bytes, bytes);
+    }
+
+    // One token's V values in dim order (ke bytes each), bound for its V
+    // tile at vt: stored one value per 16-byte piece, at v_tile_index(u, d),
+    // not copied.
+    __device__ char *image_v(int lane, const void *vt, int ke, int u, int32_t bytes)
+    {
+        return take(lane, vt, kScatter | (uint32_t)ke << 24 | (uint32_t)u << 16 | (uint32_t)bytes,
+                    bytes);
+    }
+
+    static constexpr uint32_t kScatter = 0x80000000u; // header kind bit (bytes < 2^16)
+
+    __device__ char *take(int lane, const void *dst, uint32_t word, int32_t bytes)
+    {
         char *img = reinterpret_cast<char *>(area + kRecs) + used;
         if (lane == 0) {
             const uint64_t d = reinterpret_cast<uint64_t>(dst);
-            area[nrec] = u32x4{(uint32_t)d, (uint32_t)(d >> 32), (uint32_t)bytes, (uint32_t)used};
+            area[nrec] = u32x4{(uint32_t)d, (uint32_t)(d >> 32), word, (uint32_t)used};
         }
         used += (bytes + 15) & ~15;
         nrec += 1;
@@ -775,9 +853,22 @@ struct Stage {
             const u32x4 h = area[r];
             const uint64_t d = ((uint64_t)(uint32_t)uniform((int32_t)h.y) << 32) |
                                (uint32_t)uniform((int32_t)h.x);
-            const int32_t bytes = uniform((int32_t)h.z);
+            const uint32_t word = (uint32_t)uniform((int32_t)h.z);
+            const int32_t bytes = (int32_t)(word & 0xFFFFu);
             const char *src = reinterpret_cast<const char *>(area + kRecs) + uniform((int32_t)h.w);
-            if (((bytes | (int32_t)d) & 15) == 0) {
+            if (word & kScatter) {
+                using GU16 = __attribute__((address_space(1))) uint16_t;
+                using GU8 = __attribute__((address_space(1))) uint8_t;
+                const int ke = (int)(word >> 24) & 0x7F, u = (int)(word >> 16) & 0xFF;
+                for (int32_t dd = lane; dd * ke < bytes; dd += kWave) {
+                    if (ke == 2)
+                        *reinterpret_cast<GU16 *>(d + 2 * v_tile_index<2>(u, dd)) =
+                            reinterpret_cast<const uint16_t *>(src)[dd];
+                    else
+                        *reinterpret_cast<GU8 *>(d + v_tile_index<1>(u, dd)) =
+                            reinterpret_cast<const uint8_t *>(src)[dd];
+                }
+            } else if (((bytes | (int32_t)d) & 15) == 0) {
                 for (int32_t o = 16 * lane; o < bytes; o += 16 * kWave)
                     *reinterpret_cast<GU4 *>(d + o) = *reinterpret_cast<const u32x4 *>(src + o);
             } else {
@@ -812,8 +903,11 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a, int32_t 
     MfmaWave<QT, KT, D> wv(lane);
     wv.start(a, it.b, it.g);
     bool ok = it.valid_len;
-    if (ok && it.t1 > it.t0)
-        ok = wv.template run<HINT>(a, it.b, it.g, it.t0, it.t1, it.n);
+    if (ok && it.t1 > it.t0) {
+        typename MfmaWave<QT, KT, D>::PendingToken tok;
+        ok = wv.template run<HINT>(a, it.b, it.g, it.t0, it.t1, it.n, tok);
+        wv.store_pending(a, tok, it.g);
+    }
     wv.finish();
     if (a.partition == 0)
         wv.write_out(a, it.b, it.g, it.n, ok);
@@ -1079,15 +1173,25 @@ void decode_mfma_balanced_kernel(DecodeArgs a, int32_t W)
                 rank_raw = uniform_load(plan_rank(a) + pos.b);
             }
             wv.start(a, pos.b, pos.g);
+            typename Wv::PendingToken tok;
             const bool ok = wv.template run<HINT>(a, pos.b, pos.g, j * kTile,
-                                                  min(je * kTile, pos.n), pos.n);
-            wv.finish();
+                                                  min(je * kTile, pos.n), pos.n, tok);
             // The results of every piece but the run's last go to the run's
             // Stage when they fit (no tile comes after the last piece to wait
             // for its stores); the branches keep every pointer's address
             // space known.
             if (HINT && r0 + nb >= x1)
                 st.close();
+            if (HINT && tok.put && st.fits(lane, Wv::ROW_BYTES, D * Wv::KE)) {
+                wv.put_token_k(st.image(lane, Wv::token_k_row(a, tok, pos.g), Wv::ROW_BYTES),
+                               tok.nt);
+                wv.put_token_v(st.image_v(lane, Wv::token_v_tile(a, tok, pos.g), Wv::KE,
+                                          tok.off % kTile, D * Wv::KE),
+                               tok.nt);
+            } else {
+                wv.store_pending(a, tok, pos.g);
+            }
+            wv.finish();
             if (j == 0 && je == tiles_of(pos.n)) {
                 typename Wv::TQ *o = Wv::out_rows(a, pos.b, pos.g);
                 const int32_t bytes = a.group * D * (int32_t)sizeof(typename Wv::TQ);

@@ -166,11 +166,12 @@ def test_kernels_stay_in_bounds(sim, B, H, G, W, mode):
 ])
 @pytest.mark.parametrize("mode", [1, 2])
 def test_held_results_are_all_stored(sim, stage, mode):
-    """With a share plan, a run's outputs, partial states and segment records
-    go through the wave's LDS area until the run ends (or until it is full):
-    with areas too small for some records and too small for more than one
-    piece, every output is still written and the merge still reads only
-    written slots."""
+    """With a share plan, a run's outputs, partial states, segment records
+    and appended tokens go through the wave's LDS area until the run ends (or
+    until it is full): with areas too small for some records and too small
+    for more than one piece, every output is still written, the merge still
+    reads only written slots, and every store (the token's scattered V
+    values included) stays inside its buffer."""
     d, exe = sim
     path = d / f"stage_{stage}_{mode}.bin"
     groups = ((1, 20, 5), (21, 10, 3)) if mode == 2 else ()
