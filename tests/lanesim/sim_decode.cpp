@@ -1,7 +1,8 @@
 // Runs the balanced MFMA decode kernel (with the step's append folded in,
 // with and without the shared-block hint) and the segment merge of the
 // library's own device sources on the CPU: every lane is a thread, a wave is
-// 64 of them, cross-lane operations and barriers are emulated, and the MFMA
+// 64 of them, the decode's workgroups run their four waves at once,
+// cross-lane operations and barriers are emulated, and the MFMA
 // and conversion builtins return placeholders, so the values are not checked
 // here, only the indexing.  Built with AddressSanitizer, it shows that every
 // load and store stays inside its buffer, that every cross-lane operation is
@@ -22,6 +23,28 @@ SimBlock *g_block;
 #include <thread>
 #include <vector>
 using namespace pa;
+
+// All four waves of a workgroup at once (256 threads): __syncthreads waits
+// for all of them, so a barrier that some wave of the workgroup misses, or
+// reaches a different number of times, stops the run (DEADLOCK) instead of
+// passing.
+template <class F> static void run_block(unsigned block, F f)
+{
+    SimWave w[4];
+    SimBlock blk;
+    blk.total = 256;
+    g_block = &blk;
+    std::vector<std::thread> th;
+    for (int t = 0; t < 256; ++t)
+        th.emplace_back([&, t] {
+            g_wave = &w[t / 64];
+            threadIdx = dim3(t);
+            blockIdx = dim3(block);
+            f();
+        });
+    for (auto &x : th)
+        x.join();
+}
 
 template <class F> static void run_wave(unsigned block, unsigned wave_in_block, F f)
 {
@@ -96,11 +119,11 @@ int main(int argc, char **argv)
     a.stage_bytes = argc > 3 ? atoi(argv[3]) : (int32_t)sizeof(u32x4) * kStageQuads;
     if (a.stage_bytes < 0 || a.stage_bytes > (int32_t)sizeof(u32x4) * kStageQuads)
         return 2;
-    for (int wave = 0; wave < W; ++wave) {
+    for (int wave = 0; wave < W; wave += 4) {
         if (hint)
-            run_wave(wave / 4, wave % 4, [&] { decode_mfma_balanced_kernel<PA_BF16, PA_BF16, 128, true>(a, W); });
+            run_block(wave / 4, [&] { decode_mfma_balanced_kernel<PA_BF16, PA_BF16, 128, true>(a, W); });
         else
-            run_wave(wave / 4, wave % 4, [&] { decode_mfma_balanced_kernel<PA_BF16, PA_BF16, 128, false>(a, W); });
+            run_block(wave / 4, [&] { decode_mfma_balanced_kernel<PA_BF16, PA_BF16, 128, false>(a, W); });
     }
     // prefix-row member slots the decode wrote (their m values)
     size_t row_slots = 0;
