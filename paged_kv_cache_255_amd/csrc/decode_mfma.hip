@@ -1056,7 +1056,7 @@ __device__ void decode_rows(const DecodeArgs &a, int lane, int32_t r, int32_t Wr
     SegPos pos = rs.pos;
     int64_t x = rs.x0;
     while (x < rs.x1) {
-        const int64_t r0 = pos.first_tile + kSegmentCost; // the row's tile 0
+        const int64_t r0 = pos.first_tile + kSegmentCostShared; // the row's tile 0
         const int64_t end = r0 + row_body(pos.n);
         const int64_t lo = max(x, r0), hi = min(rs.x1, end);
         if (hi > lo) {
@@ -1158,7 +1158,7 @@ void decode_mfma_balanced_kernel(DecodeArgs a, int32_t W)
     while (x < x1) {
         // the sequence's tiles past the ones its prefix row reads
         const int32_t nb = tiles_of(pos.n) - pos.own;
-        const int64_t r0 = pos.first_tile + kSegmentCost; // tile pos.own
+        const int64_t r0 = pos.first_tile + seq_cost(P); // tile pos.own
         const int64_t lo = max(x, r0), hi = min(x1, r0 + nb);
         if (hi > lo) {
             const int32_t j = (int32_t)(lo - r0) + pos.own;

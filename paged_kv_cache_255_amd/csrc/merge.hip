@@ -210,7 +210,7 @@ __device__ __forceinline__ bool balanced_parts(const DecodeArgs &a, int32_t b, i
 {
     const int64_t T = Th * a.num_kv_heads;
     const int32_t R = effective_runs(T, a.waves);
-    const int64_t S0 = (int64_t)g * Th + before + kSegmentCost;
+    const int64_t S0 = (int64_t)g * Th + before + kSegmentCost; // no prefix rows here
     const int64_t i0 = run_of_tile(S0, T, R);
     const int64_t i1 = run_of_tile(S0 + nt - 1, T, R);
     if (i0 == i1)
@@ -233,7 +233,7 @@ __device__ __forceinline__ SegAction balanced_segment_fast(const DecodeArgs &a, 
     const bool in = lane < a.num_seqs;
     const int32_t len = in ? a.seq_lens[lane] : 0;
     const int32_t n = __builtin_amdgcn_readlane(len, b);
-    const int32_t tiles = in ? split_tiles(a, len) : 0;
+    const int32_t tiles = in ? split_tiles(a, len, 0, kSegmentCost) : 0;
     const int32_t incl = wave_incl_scan32(tiles);
     if (!len_ok(a, n))
         return kSegFillNan;

@@ -74,9 +74,16 @@ __device__ __forceinline__ int32_t tiles_of(int32_t n) { return (n + kTile - 1) 
 // two sweeps) with charges of 0, 3, 5, 7, 9, 12 and 16 tiles.  Per-wave
 // clocks later put a piece's fixed cost at 3.6 (32 sequences) and 4.2 (256
 // sequences sharing a prompt) tiles, and a charge of 4 ran both launches
-// 1 - 1.5% faster than 5 (3 gave back most of it).  In the balanced order a
-// segment is kSegmentCost virtual tiles, then its real tiles.
+// 1 - 1.5% faster than 5 (3 gave back most of it).  Once a run's results
+// were held in LDS until it ends (launches with a share plan), the 256
+// sequences ran about 1.5% faster with a charge of 5 or 6 than with 4, while
+// 5 cost the 32-sequence launch (no plan) 1%; so in a launch with prefix rows
+// (seq_cost) every segment is charged kSegmentCostShared, and in any other
+// kSegmentCost (a plan that only marks shared blocks leaves the split, and so
+// every bit, as without it).  In the balanced order a segment is that many
+// virtual tiles, then its real tiles.
 constexpr int32_t kSegmentCost = 4;
+constexpr int32_t kSegmentCostShared = 6;
 
 // XCDs (accelerator complex dies) of an MI355X.  The hardware dispatcher
 // hands a launch's workgroups to the XCDs round-robin, so workgroup w runs on
@@ -151,10 +158,11 @@ __device__ __forceinline__ int32_t row_tile_at(int64_t u)
 // past the own_t its prefix row reads, plus the start charge; none when that
 // leaves nothing, or for a length out of range (the merge kernel writes that
 // row as 0 or NaN, or from its prefix row's state alone).
-__device__ __forceinline__ int32_t split_tiles(const DecodeArgs &a, int32_t n, int32_t own_t = 0)
+__device__ __forceinline__ int32_t split_tiles(const DecodeArgs &a, int32_t n, int32_t own_t,
+                                              int32_t cost)
 {
     const int32_t t = tiles_of(n) - own_t;
-    return (len_ok(a, n) && t > 0) ? t + kSegmentCost : 0;
+    return (len_ok(a, n) && t > 0) ? t + cost : 0;
 }
 
 // The sum over the wave's lanes, returned as a wave-uniform value (through
@@ -221,6 +229,13 @@ struct PrefixHead {
     int64_t units; // the rows' units per head, start charges included
 };
 
+// The start charge of a sequence segment: kSegmentCostShared in a launch with
+// prefix rows (a row always pays it), else kSegmentCost.
+__device__ __forceinline__ int32_t seq_cost(const PrefixHead &P)
+{
+    return P.on ? kSegmentCostShared : kSegmentCost;
+}
+
 // Group gi's members, clamped into the batch, and its tiles, clamped into a
 // table row.
 __device__ __forceinline__ int32_t group_count(const DecodeArgs &a, int32_t gi)
@@ -238,7 +253,7 @@ __device__ __forceinline__ int32_t group_rows(const DecodeArgs &a, int32_t cnt, 
 }
 __device__ __forceinline__ int64_t row_units(int32_t nt)
 {
-    return nt > 0 ? kSegmentCost + row_body(nt) : 0;
+    return nt > 0 ? kSegmentCostShared + row_body(nt) : 0;
 }
 
 // The launch's rows, the same in every wave of the decode and of the merge.
@@ -400,7 +415,7 @@ __device__ __forceinline__ HeadTiles head_tiles(const DecodeArgs &a, int lane, i
         int64_t t = 0;
         if (s < a.num_seqs) {
             const int32_t n = a.seq_lens[s];
-            t = split_tiles(a, n, own_tiles(a, P, s, n));
+            t = split_tiles(a, n, own_tiles(a, P, s, n), seq_cost(P));
         }
         total += t;
         before += (s < b) ? t : 0;
@@ -418,7 +433,7 @@ struct SegPos {
     int32_t gi, chunk;  // a row's group and chunk
     int64_t first_tile; // where the segment starts in its split; its first
                         // tile (a sequence's tile own, a row's tile 0) is at
-                        // first_tile + kSegmentCost
+                        // first_tile + its start charge
 };
 
 __device__ __forceinline__ SegPos seq_segment(int32_t g, int32_t b, int32_t n, int32_t own,
@@ -448,7 +463,7 @@ __device__ __forceinline__ SegPos locate_tile(const DecodeArgs &a, int lane, int
         if (b < a.num_seqs) {
             n = a.seq_lens[b];
             own = own_tiles(a, P, b, n);
-            tiles = split_tiles(a, n, own);
+            tiles = split_tiles(a, n, own, seq_cost(P));
         }
         const int64_t incl = wave_incl_scan(tiles, lane);
         const uint64_t hit = __ballot(b < a.num_seqs && carry + incl > y);
@@ -504,7 +519,7 @@ __device__ __forceinline__ RunStart run_start(const DecodeArgs &a, int lane, int
         const bool in = lane < a.num_seqs;
         const int32_t n = in ? a.seq_lens[lane] : 0;
         const int32_t own = in ? own_tiles(a, P, lane, n) : 0;
-        const int32_t tiles = in ? split_tiles(a, n, own) : 0;
+        const int32_t tiles = in ? split_tiles(a, n, own, seq_cost(P)) : 0;
         const int32_t incl = wave_incl_scan32(tiles);
         r.Th = __builtin_amdgcn_readlane(incl, kWave - 1);
         r.T = r.Th * a.num_kv_heads;
@@ -527,7 +542,7 @@ __device__ __forceinline__ RunStart run_start(const DecodeArgs &a, int lane, int
         const bool in = lane < a.num_seqs;
         const int32_t n = in ? a.seq_lens[lane] : 0;
         const int32_t own = in ? own_tiles(a, P, lane, n) : 0;
-        const int64_t tiles = in ? (int64_t)split_tiles(a, n, own) : 0;
+        const int64_t tiles = in ? (int64_t)split_tiles(a, n, own, seq_cost(P)) : 0;
         const int64_t incl = wave_incl_scan(tiles, lane);
         r.Th = readlane64(incl, kWave - 1);
         r.T = r.Th * a.num_kv_heads;
@@ -564,13 +579,13 @@ __device__ __forceinline__ RunStart run_start(const DecodeArgs &a, int lane, int
 __device__ __forceinline__ SegPos next_segment(const DecodeArgs &a, const SegPos &p,
                                                const PrefixHead &P)
 {
-    const int64_t first = p.first_tile + split_tiles(a, p.n, p.own);
+    const int64_t first = p.first_tile + split_tiles(a, p.n, p.own, seq_cost(P));
     int32_t g = uniform(p.g), b = uniform(p.b + 1);
     for (;;) {
         while (b < a.num_seqs) {
             const int32_t n = uniform_load(a.seq_lens + b);
             const int32_t own = own_tiles_uniform(a, P, b, n);
-            if (split_tiles(a, n, own) > 0)
+            if (split_tiles(a, n, own, seq_cost(P)) > 0)
                 return seq_segment(g, b, n, own, first);
             b = uniform(b + 1);
         }
@@ -715,7 +730,7 @@ __device__ __forceinline__ LaunchRegs launch_regs(const DecodeArgs &a, int lane)
             t = (int64_t)t * kTile < (int64_t)R.n[c] ? t : 0;
         }
         R.own[c] = t;
-        R.units[c] = b < a.num_seqs ? split_tiles(a, R.n[c], t) : 0;
+        R.units[c] = b < a.num_seqs ? split_tiles(a, R.n[c], t, seq_cost(R.P)) : 0;
         R.incl[c] = wave_incl_scan32(R.units[c]);
         R.carry[c] = carry;
         carry += __builtin_amdgcn_readlane(R.incl[c], kWave - 1);
@@ -868,7 +883,7 @@ __device__ __forceinline__ SegLists segment_lists(const DecodeArgs &a, int lane,
             // the rows' own split: Hkv * P.units units over Wr runs
             const int64_t Tr = P.units * a.num_kv_heads;
             const int32_t Rr = effective_runs(Tr, Wr);
-            const int64_t S0r = (int64_t)g * P.units + r.before + kSegmentCost;
+            const int64_t S0r = (int64_t)g * P.units + r.before + kSegmentCostShared;
             const int64_t j0 = run_of_tile(S0r, Tr, Rr);
             const int64_t j1 = run_of_tile(S0r + row_body(r.nt) - 1, Tr, Rr);
             e.row_w0 = (int32_t)(row_slot(a, j0, g, r.row, P) + rank % spr);

@@ -2,7 +2,8 @@
 
 The decode kernel cuts the T tiles of all (sequence, KV head) segments, in
 order, into R = min(T, W) runs [i*T/R, (i+1)*T/R); each segment is charged
-kSegmentCost virtual tiles before its real ones (a wave that starts a new
+seg_cost virtual tiles before its real ones (kSegmentCostShared in a launch
+that reads prefix rows, kSegmentCost in any other) (a wave that starts a new
 segment inside its run pays a pipeline restart).  The merge finds the run of
 a tile as ((x + 1) * R - 1) // T, and a run's partial state for a segment
 goes to slot run + segment.  These tests restate those formulas and check the
@@ -62,19 +63,25 @@ def test_run_of_tile_exhaustive_small():
             assert [run_of_tile(x, T, R) for x in range(T)] == owner
 
 
-def _segment_cost():
-    """kSegmentCost as work.hpp defines it (read from the header, so the
-    model below cannot drift from the kernels)."""
+def _segment_costs():
+    """kSegmentCost and kSegmentCostShared as work.hpp defines them (read
+    from the header, so the model below cannot drift from the kernels)."""
     here = os.path.dirname(os.path.abspath(__file__))
     text = open(os.path.join(here, "..", "paged_kv_cache_255_amd", "csrc", "work.hpp")).read()
-    return int(re.search(r"constexpr int32_t kSegmentCost = (\d+);", text).group(1))
+    return [int(re.search(r"constexpr int32_t %s = (\d+);" % name, text).group(1))
+            for name in ("kSegmentCost", "kSegmentCostShared")]
 
 
-SEGMENT_COST = _segment_cost()
+SEGMENT_COSTS = _segment_costs()
 
 
+def test_segment_costs_are_positive():
+    assert all(c > 0 for c in SEGMENT_COSTS)
+
+
+@pytest.mark.parametrize("SEGMENT_COST", SEGMENT_COSTS)
 @pytest.mark.parametrize("seed", range(40))
-def test_decode_pieces_match_merge_parts(seed):
+def test_decode_pieces_match_merge_parts(seed, SEGMENT_COST):
     """The decode's walk (a run's virtual tiles meet each segment's start
     charge, then its real tiles) against the merge's run bounds."""
     rng = random.Random(seed)
